@@ -1,0 +1,145 @@
+"""Selective-scan oracle: plain sequential float64 evaluation on the CPU.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` import this package. The product path (the
+HIP library and its Python binding) never imports it, and the two share no
+code: the only module both sides use is the seeded input generator, which holds
+none of the method's arithmetic.
+
+The arithmetic lives in ``ssm_oracle.c`` (C, libm, OpenMP over independent
+rows); this module compiles it with gcc, widens inputs to float64 and calls it.
+Every input is widened exactly (bf16 bit patterns and float32 both convert to
+float64 without rounding), so the oracle sees the same values the GPU sees.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+MAX_N = 1024
+
+
+def build(force: bool = False) -> str:
+    """Compile ssm_oracle.c into liboracle.so with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99", "-Wall", "-Wextra",
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_scan_rows.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                         ctypes.c_int]
+        lib.oracle_scan_rows.restype = None
+        lib.oracle_state_update.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p,
+                                            ctypes.c_int]
+        lib.oracle_state_update.restype = None
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan_rows(rows_b, rows_d, u_rows, dt_rows, A, Bm, Cm, *, z_rows=None, dt_bias=None,
+              Dskip=None, reset=None, h0_rows=None, want_h_last=False, nthreads=0):
+    """Run the recurrence on selected (b, d) rows over the full sequence.
+
+    rows_b, rows_d : (R,) int   batch and channel of each row
+    u_rows, dt_rows, z_rows : (R, L) values of that row (any float dtype)
+    A : (D, N); Bm, Cm : (B, L, N); dt_bias, Dskip : (D,) or None
+    reset : (B, L) bool/uint8 or None; h0_rows : (R, N) or None
+    Returns out (R, L) float64 and, if asked, h_last (R, N).
+    """
+    lib = _load()
+    rows_b = np.ascontiguousarray(np.asarray(rows_b, dtype=np.int64))
+    rows_d = np.ascontiguousarray(np.asarray(rows_d, dtype=np.int64))
+    u_rows, dt_rows, z_rows = _f64(u_rows), _f64(dt_rows), _f64(z_rows)
+    A, Bm, Cm = _f64(A), _f64(Bm), _f64(Cm)
+    dt_bias, Dskip, h0_rows = _f64(dt_bias), _f64(Dskip), _f64(h0_rows)
+    R, L = u_rows.shape
+    N = A.shape[1]
+    if N > MAX_N:
+        raise ValueError("oracle supports N <= %d" % MAX_N)
+    Bt = Bm.shape[0]
+    assert dt_rows.shape == (R, L) and Bm.shape == (Bt, L, N) and Cm.shape == (Bt, L, N)
+    assert rows_b.shape == (R,) and rows_d.shape == (R,)
+    if z_rows is not None:
+        assert z_rows.shape == (R, L)
+    if h0_rows is not None:
+        assert h0_rows.shape == (R, N)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+        assert reset.shape == (Bt, L)
+    out = np.empty((R, L), dtype=np.float64)
+    h_last = np.empty((R, N), dtype=np.float64) if want_h_last else None
+    lib.oracle_scan_rows(R, L, N, _ptr(rows_b), _ptr(rows_d), _ptr(u_rows), _ptr(dt_rows),
+                         _ptr(z_rows), _ptr(dt_bias), _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm),
+                         _ptr(reset), _ptr(h0_rows), _ptr(out), _ptr(h_last), int(nthreads))
+    return (out, h_last) if want_h_last else out
+
+
+def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
+         want_h_last=False, nthreads=0):
+    """Full scan. u, dt_raw, z: (B, D, L); h0: (B, D, N). Returns out (B, D, L)."""
+    u = np.asarray(u)
+    Bt, D, L = u.shape
+    N = np.asarray(A).shape[1]
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    res = scan_rows(rb, rd, u.reshape(Bt * D, L), np.asarray(dt_raw).reshape(Bt * D, L), A, Bm, Cm,
+                    z_rows=None if z is None else np.asarray(z).reshape(Bt * D, L),
+                    dt_bias=dt_bias, Dskip=Dskip, reset=reset,
+                    h0_rows=None if h0 is None else np.asarray(h0).reshape(Bt * D, N),
+                    want_h_last=want_h_last, nthreads=nthreads)
+    if want_h_last:
+        out, hl = res
+        return out.reshape(Bt, D, L), hl.reshape(Bt, D, N)
+    return res.reshape(Bt, D, L)
+
+
+def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, nthreads=0):
+    """Decode step. h: (B, D, N); u, dt_raw, z: (B, D); Bm, Cm: (B, N).
+
+    Returns (out (B, D), h_new (B, D, N)); the input h is not modified.
+    """
+    lib = _load()
+    h_new = np.array(h, dtype=np.float64, copy=True, order="C")
+    u, dt_raw, z = _f64(u), _f64(dt_raw), _f64(z)
+    A, Bm, Cm, dt_bias, Dskip = _f64(A), _f64(Bm), _f64(Cm), _f64(dt_bias), _f64(Dskip)
+    Bt, D, N = h_new.shape
+    if N > MAX_N:
+        raise ValueError("oracle supports N <= %d" % MAX_N)
+    assert u.shape == (Bt, D) and dt_raw.shape == (Bt, D) and A.shape == (D, N)
+    assert Bm.shape == (Bt, N) and Cm.shape == (Bt, N)
+    out = np.empty((Bt, D), dtype=np.float64)
+    lib.oracle_state_update(Bt, D, N, _ptr(h_new), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
+                            _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(out), int(nthreads))
+    return out, h_new
