@@ -1,0 +1,180 @@
+/*
+ * ssm_scan.h - C ABI of the MI355X (gfx950) selective-scan library libssmscan.so.
+ *
+ * The library computes the Mamba selective state-space scan. For every batch
+ * row b, channel d and step t:
+ *
+ *   delta_t = softplus(dt_raw[b,d,t] + dt_bias[d])              (beta = 1)
+ *   h_t[n]  = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B[b,t,n] * u[b,d,t]
+ *   y_t     = sum_n C[b,t,n] * h_t[n] + D[d] * u[b,d,t]
+ *   out     = y_t * silu(z[b,d,t])                               (y_t without z)
+ *
+ * with h_{-1} = h0 (zeros when absent) and, where reset[b,t] != 0, h_{t-1}
+ * taken as zero before step t.
+ *
+ * Where each piece is defined (page titles; section names as on the pages):
+ *  - the discrete recurrence h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t with
+ *    Abar = exp(delta A), and the small-delta input matrix Bbar = delta B:
+ *    "Illustrated Mamba state space model" (blog.luzhipeng.com), sections
+ *    "Mathematical basis: structured SSM" and step 1 (discretisation);
+ *  - delta = softplus(linear(x)) with B, C chosen per step: same page,
+ *    "Mamba's innovation: the selection mechanism";
+ *  - diagonal A, the per-step update state = A_t*state + B_t*u_t, the read-out
+ *    with + D*u and the SiLU-gated block: "Mamba SSM core theory and
+ *    Keras/TensorFlow implementation" (highthink.cn), SelectiveSSM layer;
+ *  - the fused single kernel that loads parameters into on-chip memory,
+ *    discretises and recurs there and writes back only the result:
+ *    "Technical analysis: Mamba selective state spaces" (codechina.net),
+ *    section 1 (hardware-aware algorithm) and 2.2 (kernel fusion);
+ *  - document isolation by resetting the hidden state: same page, 3.2;
+ *  - the single-token recurrent (RNN-style) inference step: "Reproducing
+ *    Mamba's SSM core in Python" (mhpn.cn), section 3.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major in the layouts given below, each aligned to its element size.
+ *    The library never allocates, frees or keeps them beyond the call.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *    and runs asynchronously; the call returns once it is enqueued.
+ *  - Every argument check runs on the host before anything is enqueued, so a
+ *    non-OK status means no device work was issued and no output was touched.
+ *    Only SSM_ERR_HIP can follow a partial launch; ssm_last_error() then holds
+ *    the HIP error text. Faults during execution surface at the caller's next
+ *    synchronisation of the stream.
+ *  - NaN/Inf inputs propagate by IEEE rules; they are not trapped.
+ *  - The library is re-entrant; its only global mutable state is the
+ *    thread-local text returned by ssm_last_error().
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define SSM_MAX_DSTATE 256     /* largest supported N */
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL_POINTER = 1, /* a required pointer (or params itself) is NULL   */
+  SSM_ERR_BAD_SHAPE = 2,    /* a size is < 1 (decode: < 1), N > SSM_MAX_DSTATE, or
+                               an element count overflows int64                */
+  SSM_ERR_BAD_DTYPE = 3,    /* in_dtype / out_dtype is not an ssm_dtype         */
+  SSM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size    */
+  SSM_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement   */
+  SSM_ERR_WORKSPACE = 6,    /* workspace smaller than ssm_scan_workspace_size() */
+  SSM_ERR_ALIAS = 7,        /* out (or h_last) overlaps an input tensor         */
+  SSM_ERR_HIP = 8           /* the HIP runtime refused a call; see ssm_last_error */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/*
+ * Full-sequence scan (prefill / training forward).
+ *
+ *   batch, dim, seqlen, dstate : B, D, L, N;  B, D, L >= 1, 1 <= N <= 256
+ *   in_dtype  : element type of u, dt_raw, z, Bm, Cm (SSM_F32 or SSM_BF16)
+ *   out_dtype : element type of out (SSM_F32 or SSM_BF16)
+ *   u        (B,D,L)  required; the SSM input x (L contiguous)
+ *   dt_raw   (B,D,L)  required; pre-softplus step size
+ *   dt_bias  (D)      float32, NULL => 0
+ *   A        (D,N)    float32, required; the diagonal of the state matrix.
+ *                     Any real value is accepted; stable models have A <= 0.
+ *   Bm, Cm   (B,L,N)  required; input and output matrices per step (N contiguous)
+ *   Dskip    (D)      float32, NULL => no skip term
+ *   z        (B,D,L)  NULL => no gate (out = y)
+ *   reset    (B,L)    uint8, NULL => none; nonzero at t clears the state before step t
+ *   h0       (B,D,N)  float32, NULL => zero initial state
+ *   out      (B,D,L)  required; written once per element; must not overlap inputs
+ *   h_last   (B,D,N)  float32, NULL => not written; the state after step L-1
+ *   workspace, workspace_bytes : scratch for scans that split the sequence
+ *                     across workgroups; at least ssm_scan_workspace_size()
+ *                     bytes (may be NULL when that size is 0). Its contents on
+ *                     entry are ignored; callers may reuse it between calls on
+ *                     the same stream.
+ *   num_segments : 0 = the library chooses how many pieces to split L into;
+ *                  k >= 1 asks for k pieces (clamped to what L allows).
+ */
+typedef struct {
+  int64_t batch, dim, seqlen, dstate;
+  int32_t in_dtype, out_dtype;
+  const void* u;
+  const void* dt_raw;
+  const float* dt_bias;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const uint8_t* reset;
+  const float* h0;
+  void* out;
+  float* h_last;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t num_segments;
+  int32_t reserved0;
+} ssm_scan_params;
+
+/* Bytes of workspace ssm_scan_fwd needs for these parameters (0 when the scan
+ * does not split the sequence). Only the sizes, dtypes and num_segments of
+ * `p` are read. */
+ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes);
+
+/* Enqueue the scan described by `p` on `hip_stream`. */
+ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream);
+
+/*
+ * Single-token decode step: one application of the recurrence to a stored
+ * state, in place.
+ *
+ *   batch, dim, dstate : B, D, N;  B, D >= 1, 1 <= N <= 256
+ *   h        (B,D,N)  float32, required; read as h_{t-1}, overwritten with h_t.
+ *                     To start a new sequence the caller zeroes that row.
+ *   u, dt_raw (B,D)   required; z (B,D) NULL => no gate
+ *   dt_bias  (D), Dskip (D) float32, NULL => 0 / no skip term; A (D,N) float32
+ *   Bm, Cm   (B,N)    required
+ *   out      (B,D)    required; must not overlap h or any input
+ */
+typedef struct {
+  int64_t batch, dim, dstate;
+  int32_t in_dtype, out_dtype;
+  float* h;
+  const void* u;
+  const void* dt_raw;
+  const void* z;
+  const float* dt_bias;
+  const float* A;
+  const float* Dskip;
+  const void* Bm;
+  const void* Cm;
+  void* out;
+} ssm_update_params;
+
+/* Enqueue the decode step described by `p` on `hip_stream`. */
+ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* ssm_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on this thread (static storage,
+ * valid until the next library call on this thread). */
+const char* ssm_last_error(void);
+
+/* SSM_SCAN_VERSION of the loaded library. */
+int32_t ssm_version(void);
+
+/* sizeof of the parameter structs as compiled into the library:
+ * which = 0 -> ssm_scan_params, 1 -> ssm_update_params; 0 for anything else.
+ * Bindings compare these with their own layouts at load time. */
+size_t ssm_abi_struct_size(int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,16 @@
+"""MI355X-native selective-scan forward (Mamba SSM) behind a C-ABI HIP library.
+
+The public entry points mirror the C functions of ``include/ssm_scan.h``:
+``ssm_scan_fwd``, ``ssm_scan_workspace_size`` and ``ssm_state_update``. They
+take torch tensors only as carriers of device pointers and the current stream;
+every step of the computation runs in the HIP kernels of ``libssmscan.so``.
+The library is loaded on first use and a missing build raises at that point.
+"""
+from .binding import (  # noqa: F401
+    SsmError,
+    library_path,
+    load_library,
+    ssm_scan_fwd,
+    ssm_scan_workspace_size,
+    ssm_state_update,
+)

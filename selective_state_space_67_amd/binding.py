@@ -1,0 +1,245 @@
+"""ctypes binding of libssmscan.so (declared in include/ssm_scan.h).
+
+Argument marshalling only: the functions below read shapes, dtypes, device
+pointers and the current HIP stream from torch tensors, fill the C parameter
+structs and call the library. Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind. If the library is
+missing (not built) the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libssmscan.so"
+
+SSM_F32 = 0
+SSM_BF16 = 1
+
+STATUS_NAMES = {
+    0: "SSM_OK", 1: "SSM_ERR_NULL_POINTER", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
+    4: "SSM_ERR_MISALIGNED", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_ALIAS",
+    8: "SSM_ERR_HIP",
+}
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), detail))
+
+
+class ScanParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("u", ctypes.c_void_p), ("dt_raw", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("A", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
+        ("Dskip", ctypes.c_void_p), ("z", ctypes.c_void_p), ("reset", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("out", ctypes.c_void_p), ("h_last", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_segments", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    ]
+
+
+class UpdateParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("h", ctypes.c_void_p), ("u", ctypes.c_void_p), ("dt_raw", ctypes.c_void_p),
+        ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("Dskip", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_status_string",
+           "ssm_last_error", "ssm_version", "ssm_abi_struct_size")
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("SSM_SCAN_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libssmscan.so (once) and check the struct layouts against it."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError("libssmscan.so is not built (%s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanParams), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssm_scan_workspace_size.restype = ctypes.c_int
+    lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), vp]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_state_update.argtypes = [ctypes.POINTER(UpdateParams), vp]
+    lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_status_string.argtypes = [ctypes.c_int32]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_version.argtypes = []
+    lib.ssm_version.restype = ctypes.c_int32
+    lib.ssm_abi_struct_size.argtypes = [ctypes.c_int32]
+    lib.ssm_abi_struct_size.restype = ctypes.c_size_t
+    if lib.ssm_abi_struct_size(0) != ctypes.sizeof(ScanParams) or \
+            lib.ssm_abi_struct_size(1) != ctypes.sizeof(UpdateParams):
+        raise ImportError("libssmscan.so struct layout does not match this binding")
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise SsmError(status, _lib.ssm_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, shape, name, dtype=None):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
+                 num_segments):
+    import torch
+
+    Bt, D, L = u.shape
+    N = A.shape[1]
+    _need(u, (Bt, D, L), "u")
+    _need(dt_raw, (Bt, D, L), "dt_raw", u.dtype)
+    _need(A, (D, N), "A", torch.float32)
+    _need(Bm, (Bt, L, N), "Bm", u.dtype)
+    _need(Cm, (Bt, L, N), "Cm", u.dtype)
+    if dt_bias is not None:
+        _need(dt_bias, (D,), "dt_bias", torch.float32)
+    if Dskip is not None:
+        _need(Dskip, (D,), "Dskip", torch.float32)
+    if z is not None:
+        _need(z, (Bt, D, L), "z", u.dtype)
+    if reset is not None:
+        _need(reset, (Bt, L), "reset", torch.uint8)
+    if h0 is not None:
+        _need(h0, (Bt, D, N), "h0", torch.float32)
+    if out is not None:
+        _need(out, (Bt, D, L), "out")
+    if h_last is not None:
+        _need(h_last, (Bt, D, N), "h_last", torch.float32)
+    p = ScanParams()
+    p.batch, p.dim, p.seqlen, p.dstate = Bt, D, L, N
+    p.in_dtype = _dtype_code(u)
+    p.out_dtype = _dtype_code(out) if out is not None else (SSM_F32 if out_dtype is None
+                                                            else _dtype_code(torch.empty(0, dtype=out_dtype)))
+    p.u, p.dt_raw, p.dt_bias, p.A = _ptr(u), _ptr(dt_raw), _ptr(dt_bias), _ptr(A)
+    p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
+    p.reset, p.h0, p.out, p.h_last = _ptr(reset), _ptr(h0), _ptr(out), _ptr(h_last)
+    p.num_segments = int(num_segments)
+    return p
+
+
+def ssm_scan_workspace_size(u, A, *, num_segments=0, out_dtype=None):
+    """Workspace bytes ssm_scan_fwd needs for inputs shaped like u (B,D,L) and A (D,N)."""
+    import torch
+
+    lib = load_library()
+    p = ScanParams()
+    p.batch, p.dim, p.seqlen = u.shape
+    p.dstate = A.shape[1]
+    p.in_dtype = _dtype_code(u)
+    p.out_dtype = SSM_F32 if out_dtype in (None, torch.float32) else SSM_BF16
+    p.num_segments = int(num_segments)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
+                 out=None, h_last=None, out_dtype=None, workspace=None, num_segments=0, stream=None):
+    """Selective scan over the whole sequence; returns ``out`` (B, D, L).
+
+    u, dt_raw, z: (B, D, L) float32 or bfloat16; A: (D, N) float32;
+    Bm, Cm: (B, L, N) same dtype as u; dt_bias, Dskip: (D,) float32;
+    reset: (B, L) uint8; h0, h_last: (B, D, N) float32. ``out`` is allocated
+    (float32 unless ``out_dtype`` says bfloat16) when not given, and so is the
+    workspace the library asks for. Runs on ``stream`` (default: the current
+    torch stream of u's device).
+    """
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
+    p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
+                     num_segments)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    if n.value:
+        if workspace is None or workspace.numel() * workspace.element_size() < n.value:
+            workspace = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
+        p.workspace = _ptr(workspace)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssm_scan_fwd(ctypes.byref(p), _stream(stream, u.device)))
+    return out
+
+
+def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
+                     out_dtype=None, stream=None):
+    """Decode step: updates h (B, D, N) float32 in place and returns out (B, D)."""
+    import torch
+
+    lib = load_library()
+    Bt, D, N = h.shape
+    _need(h, (Bt, D, N), "h", torch.float32)
+    _need(u, (Bt, D), "u")
+    _need(dt_raw, (Bt, D), "dt_raw", u.dtype)
+    _need(A, (D, N), "A", torch.float32)
+    _need(Bm, (Bt, N), "Bm", u.dtype)
+    _need(Cm, (Bt, N), "Cm", u.dtype)
+    if z is not None:
+        _need(z, (Bt, D), "z", u.dtype)
+    if dt_bias is not None:
+        _need(dt_bias, (D,), "dt_bias", torch.float32)
+    if Dskip is not None:
+        _need(Dskip, (D,), "Dskip", torch.float32)
+    if out is None:
+        out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
+    _need(out, (Bt, D), "out")
+    p = UpdateParams()
+    p.batch, p.dim, p.dstate = Bt, D, N
+    p.in_dtype, p.out_dtype = _dtype_code(u), _dtype_code(out)
+    p.h, p.u, p.dt_raw, p.z = _ptr(h), _ptr(u), _ptr(dt_raw), _ptr(z)
+    p.dt_bias, p.A, p.Dskip = _ptr(dt_bias), _ptr(A), _ptr(Dskip)
+    p.Bm, p.Cm, p.out = _ptr(Bm), _ptr(Cm), _ptr(out)
+    _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
+    return out

@@ -1,0 +1,293 @@
+// C-ABI front end of libssmscan.so (include/ssm_scan.h).
+//
+// Every check here is plain host arithmetic on the parameter struct; nothing
+// touches the HIP runtime until all checks have passed, so invalid calls
+// return their status with no device-side effect (and can be exercised on a
+// machine without a GPU). The launches themselves live in scan_fwd.hip and
+// state_update.hip.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ssm_status ok() {
+  g_last_error[0] = '\0';
+  return SSM_OK;
+}
+
+bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
+size_t dtype_size(int32_t t) { return t == SSM_BF16 ? 2 : 4; }
+
+// a * b without overflow for non-negative operands.
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// A byte range [p, p + n) of one tensor; empty when p is null.
+struct Range {
+  const char* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  return a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+Range range(const void* p, int64_t count, size_t esize, const char* name) {
+  return Range{static_cast<const char*>(p), p ? static_cast<size_t>(count) * esize : 0, name};
+}
+
+// Sizes of a scan, checked for range and overflow.
+struct ScanSizes {
+  int64_t bdl, bln, dn, bdn, bl;
+};
+
+ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
+  if (p->batch < 1 || p->dim < 1 || p->seqlen < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "batch, dim and seqlen must be >= 1 (got %lld, %lld, %lld)",
+                (long long)p->batch, (long long)p->dim, (long long)p->seqlen);
+  if (p->dstate < 1 || p->dstate > SSM_MAX_DSTATE)
+    return fail(SSM_ERR_BAD_SHAPE, "dstate must be in [1, %d] (got %lld)", SSM_MAX_DSTATE,
+                (long long)p->dstate);
+  if (p->seqlen > std::numeric_limits<int32_t>::max() / 2)
+    return fail(SSM_ERR_BAD_SHAPE, "seqlen %lld is too large", (long long)p->seqlen);
+  int64_t bd;
+  const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
+  if (!mul_ok(p->batch, p->dim, &bd) || !mul_ok(bd, p->seqlen, &sz->bdl) ||
+      !mul_ok(p->batch, p->seqlen, &sz->bl) || !mul_ok(sz->bl, p->dstate, &sz->bln) ||
+      !mul_ok(p->dim, p->dstate, &sz->dn) || !mul_ok(bd, p->dstate, &sz->bdn) || sz->bdl > lim ||
+      sz->bln > lim || sz->bdn > lim)
+    return fail(SSM_ERR_BAD_SHAPE, "element count overflows");
+  return SSM_OK;
+}
+
+ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
+  if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
+  ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+  if (ssm::scan_grid_blocks(p->batch, p->dim, *nseg) > std::numeric_limits<int32_t>::max())
+    return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  *ws = ssm::scan_workspace_bytes(p->batch, p->dim, p->dstate, *nseg);
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
+  if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");
+  ScanSizes sz;
+  ssm_status s = check_scan_sizes(p, &sz);
+  if (s != SSM_OK) return s;
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
+  int nseg;
+  int64_t seg_len;
+  size_t ws;
+  if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  *bytes = ws;
+  return ok();
+}
+
+ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
+  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
+  ScanSizes sz;
+  ssm_status s = check_scan_sizes(p, &sz);
+  if (s != SSM_OK) return s;
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
+  const struct {
+    const void* ptr;
+    const char* name;
+  } required[] = {{p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"}, {p->Bm, "Bm"}, {p->Cm, "Cm"},
+                  {p->out, "out"}};
+  for (const auto& r : required)
+    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+
+  const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
+  const Range inputs[] = {
+      range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
+      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln, si, "Bm"),
+      range(p->Cm, sz.bln, si, "Cm"),        range(p->A, sz.dn, 4, "A"),
+      range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
+      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
+  };
+  const struct {
+    const void* ptr;
+    size_t align;
+    const char* name;
+  } aligns[] = {{p->u, si, "u"},           {p->dt_raw, si, "dt_raw"}, {p->z, si, "z"},
+                {p->Bm, si, "Bm"},         {p->Cm, si, "Cm"},         {p->A, 4, "A"},
+                {p->dt_bias, 4, "dt_bias"}, {p->Dskip, 4, "Dskip"},   {p->h0, 4, "h0"},
+                {p->out, so, "out"},       {p->h_last, 4, "h_last"},  {p->workspace, 4, "workspace"}};
+  for (const auto& a : aligns)
+    if (a.ptr && !aligned(a.ptr, a.align))
+      return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
+
+  const Range out = range(p->out, sz.bdl, so, "out");
+  const Range hl = range(p->h_last, sz.bdn, 4, "h_last");
+  for (const Range& r : inputs) {
+    if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+    if (overlaps(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps %s", r.name);
+  }
+  if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
+
+  int nseg;
+  int64_t seg_len;
+  size_t ws;
+  if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  if (ws > 0) {
+    if (!p->workspace || p->workspace_bytes < ws)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws,
+                  p->workspace ? p->workspace_bytes : static_cast<size_t>(0));
+    const Range w{static_cast<const char*>(p->workspace), ws, "workspace"};
+    for (const Range& r : inputs)
+      if (overlaps(w, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+    if (overlaps(w, out) || overlaps(w, hl)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+  }
+
+  ssm::ScanPlan plan{};
+  plan.B = p->batch;
+  plan.D = p->dim;
+  plan.L = p->seqlen;
+  plan.N = p->dstate;
+  plan.in_bf16 = p->in_dtype == SSM_BF16;
+  plan.out_bf16 = p->out_dtype == SSM_BF16;
+  plan.u = p->u;
+  plan.dt = p->dt_raw;
+  plan.z = p->z;
+  plan.Bm = p->Bm;
+  plan.Cm = p->Cm;
+  plan.dt_bias = p->dt_bias;
+  plan.A = p->A;
+  plan.Dskip = p->Dskip;
+  plan.h0 = p->h0;
+  plan.reset = p->reset;
+  plan.out = p->out;
+  plan.h_last = p->h_last;
+  plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  plan.nseg = nseg;
+  plan.seg_len = seg_len;
+  hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
+  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
+  if (p->batch < 1 || p->dim < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "batch and dim must be >= 1 (got %lld, %lld)", (long long)p->batch,
+                (long long)p->dim);
+  if (p->dstate < 1 || p->dstate > SSM_MAX_DSTATE)
+    return fail(SSM_ERR_BAD_SHAPE, "dstate must be in [1, %d] (got %lld)", SSM_MAX_DSTATE,
+                (long long)p->dstate);
+  int64_t bd, bdn, bn, dn;
+  if (!mul_ok(p->batch, p->dim, &bd) || !mul_ok(bd, p->dstate, &bdn) || !mul_ok(p->batch, p->dstate, &bn) ||
+      !mul_ok(p->dim, p->dstate, &dn) || bdn > std::numeric_limits<int64_t>::max() / 8)
+    return fail(SSM_ERR_BAD_SHAPE, "element count overflows");
+  if ((bd + 3) / 4 > std::numeric_limits<int32_t>::max())
+    return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
+  const struct {
+    const void* ptr;
+    const char* name;
+  } required[] = {{p->h, "h"}, {p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"},
+                  {p->Bm, "Bm"}, {p->Cm, "Cm"}, {p->out, "out"}};
+  for (const auto& r : required)
+    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+  const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
+  const struct {
+    const void* ptr;
+    size_t align;
+    const char* name;
+  } aligns[] = {{p->h, 4, "h"},   {p->u, si, "u"},   {p->dt_raw, si, "dt_raw"}, {p->z, si, "z"},
+                {p->dt_bias, 4, "dt_bias"}, {p->A, 4, "A"}, {p->Dskip, 4, "Dskip"}, {p->Bm, si, "Bm"},
+                {p->Cm, si, "Cm"}, {p->out, so, "out"}};
+  for (const auto& a : aligns)
+    if (a.ptr && !aligned(a.ptr, a.align))
+      return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
+  const Range inputs[] = {range(p->u, bd, si, "u"),         range(p->dt_raw, bd, si, "dt_raw"),
+                          range(p->z, bd, si, "z"),         range(p->dt_bias, p->dim, 4, "dt_bias"),
+                          range(p->A, dn, 4, "A"),          range(p->Dskip, p->dim, 4, "Dskip"),
+                          range(p->Bm, bn, si, "Bm"),       range(p->Cm, bn, si, "Cm")};
+  const Range h = range(p->h, bdn, 4, "h");
+  const Range out = range(p->out, bd, so, "out");
+  for (const Range& r : inputs) {
+    if (overlaps(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps %s", r.name);
+    if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+  }
+  if (overlaps(out, h)) return fail(SSM_ERR_ALIAS, "out overlaps h");
+
+  ssm::UpdatePlan plan{};
+  plan.B = p->batch;
+  plan.D = p->dim;
+  plan.N = p->dstate;
+  plan.in_bf16 = p->in_dtype == SSM_BF16;
+  plan.out_bf16 = p->out_dtype == SSM_BF16;
+  plan.h = p->h;
+  plan.u = p->u;
+  plan.dt = p->dt_raw;
+  plan.z = p->z;
+  plan.dt_bias = p->dt_bias;
+  plan.A = p->A;
+  plan.Dskip = p->Dskip;
+  plan.Bm = p->Bm;
+  plan.Cm = p->Cm;
+  plan.out = p->out;
+  hipError_t e = ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "state update launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* ssm_status_string(int32_t status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_NULL_POINTER: return "SSM_ERR_NULL_POINTER";
+    case SSM_ERR_BAD_SHAPE: return "SSM_ERR_BAD_SHAPE";
+    case SSM_ERR_BAD_DTYPE: return "SSM_ERR_BAD_DTYPE";
+    case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
+    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* ssm_last_error(void) { return g_last_error; }
+
+int32_t ssm_version(void) { return SSM_SCAN_VERSION; }
+
+size_t ssm_abi_struct_size(int32_t which) {
+  if (which == 0) return sizeof(ssm_scan_params);
+  if (which == 1) return sizeof(ssm_update_params);
+  return 0;
+}
+
+}  // extern "C"

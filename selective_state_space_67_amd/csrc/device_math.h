@@ -1,0 +1,63 @@
+// Device-side helpers shared by the scan and decode kernels (gfx950).
+//
+// Element access for the two input formats (float32 and bfloat16 bit
+// patterns), the float32 step-size and gate functions, and the DPP lane shift
+// the scan's cross-lane accumulation uses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bfloat16 is stored as its 16-bit pattern; widening to float is a shift.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const bf16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i].bits) << 16);
+}
+
+__device__ __forceinline__ void store_elem(float* p, int64_t i, float v) { p[i] = v; }
+// float -> bfloat16, round to nearest, ties to even.
+__device__ __forceinline__ void store_elem(bf16_t* p, int64_t i, float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  p[i].bits = static_cast<uint16_t>(b >> 16);
+}
+
+// 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32); both
+// are within ~2 ulp of the correctly rounded value on gfx950.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) with beta 1, evaluated as max(x, 0) + log1p(e^-|x|).
+// log1p(e) for e in (0, 1] is log(1 + e) plus the rounding error of the sum
+// 1 + e (recovered exactly by Sterbenz subtraction); without that term the
+// result loses relative accuracy once e is small (x below about -3).
+__device__ __forceinline__ float softplus_f32(float x) {
+  const float e = fast_exp2(-fabsf(x) * kLog2e);
+  const float s = 1.0f + e;
+  const float lost = e - (s - 1.0f);
+  return fmaxf(x, 0.0f) + __builtin_fmaf(fast_log2(s), kLn2, lost);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z). For z -> -inf, e^-z -> inf and
+// the reciprocal gives 0, so the result is a signed zero rather than NaN.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// Value of the lane one below within the same row of 16 lanes (DPP
+// row_shr:1); lane 0 of each row reads 0.
+__device__ __forceinline__ float row_shr1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+}
+
+}  // namespace ssm

@@ -159,6 +159,8 @@ def to_torch(x, device):
     if x is None:
         return None
     x = np.ascontiguousarray(x)
+    if not x.flags.writeable:
+        x = x.copy()
     if x.dtype == np.uint16:
         return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(x).to(device)
