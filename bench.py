@@ -1,0 +1,262 @@
+"""Benchmark of the selective-scan forward on one MI355X.
+
+One step = one ssm_scan_fwd call over the Mamba-130M-shaped layer workload
+(batch 8, 1536 channels, 2048 steps, N = 16; bf16 inputs, float32 state,
+arithmetic and output), inputs resident in HBM. Prints one JSON line:
+
+  value        whole-job throughput in scan elements (B*D*L*N) per second over
+               the K timed steps (wall clock, synchronised on both sides)
+  hbm_gbps     algorithmic HBM bytes per step / time per step
+  roofline     the scan kernel against the bound that limits it (the vector
+               ALU; see the design doc for the peak), measured with HIP events on
+               the launch stream; `traffic` is the HBM byte count from the
+               rocprofv3 counter runs recorded under profiles/ (null when the
+               kernel source changed since they were taken)
+  cold_cache   the same launch after a 1 GiB write that evicts L2 and MALL
+  decode       the single-token decode step (batch 64, 2048 channels, N = 128)
+  cpu_baseline the float64 oracle on the host cores over the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# Vector ALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic ALU work of the scan in fp32 lane-operations (an FMA is one; a
+# transcendental counts the two issue slots it occupies):
+#   per (b, d, t, n): exp(delta*A) (2) + delta*A (1) + B*delta*u (1)
+#                     + state FMA (1) + C.h FMA (1)                     = 6
+#   per (b, d, t):    softplus = exp, log (4) + 5 ops; silu = exp, rcp (4)
+#                     + 2 ops; delta*u, D*u + y, gate (3)               = 18
+OPS_PER_ELEMENT = 6.0
+OPS_PER_ROW_STEP = 18.0
+SCAN_SOURCES = ["selective_state_space_67_amd/csrc/scan_fwd.hip",
+                "selective_state_space_67_amd/csrc/device_math.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_counters_mamba130m.md")
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in SCAN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed counter summary, if still valid."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != scan_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def algorithmic_bytes(B, D, L, N, s_in, s_out, reset=False, h0=False, h_last=False):
+    """HBM bytes the scan must move: u, dt_raw, z, B, C, A, D, dt_bias, [reset], out, [h0, h_last]."""
+    b = 3 * B * D * L * s_in + 2 * B * L * N * s_in + 4 * D * N + 8 * D + B * D * L * s_out
+    if reset:
+        b += B * L
+    if h0:
+        b += 4 * B * D * N
+    if h_last:
+        b += 4 * B * D * N
+    return b
+
+
+def decode_bytes(B, D, N, s_in, s_out):
+    return 8 * B * D * N + 3 * B * D * s_in + 2 * B * N * s_in + 4 * D * N + 8 * D + B * D * s_out
+
+
+def percentile(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (for counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_67_amd import load_library, ssm_state_update
+    from selective_state_space_67_amd import binding
+    from selective_state_space_67_amd import workloads as wl
+
+    load_library()
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[1]
+    B, D, L, N = cfg["B"], cfg["D"], cfg["L"], cfg["N"]
+    x = wl.config_inputs(1)
+    t = {k: wl.to_torch(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    out = torch.empty((B, D, L), dtype=torch.float32, device=dev)
+    call = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                                Dskip=t["Dskip"], z=t["z"], out=out)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # K timed steps, back to back.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    # Per-launch kernel time with HIP events on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    launch_s = float(np.mean(launch_ms)) / 1e3
+
+    # Cold caches: a 1 GiB write before each launch, outside the timed events.
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(min(args.steps, 50)):
+        scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    elements = B * D * L * N
+    abytes = algorithmic_bytes(B, D, L, N, 2, 4)
+    ops = OPS_PER_ELEMENT * elements + OPS_PER_ROW_STEP * B * D * L
+    achieved = ops / launch_s / 1e12
+    traffic = recorded_traffic()
+
+    # Decode step at its workload size.
+    y = wl.decode_inputs()
+    td = {k: wl.to_torch(y[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    hd = torch.from_numpy(y["h"]).to(dev)
+    od = torch.empty((y["h"].shape[0], y["h"].shape[1]), dtype=torch.float32, device=dev)
+
+    def dec():
+        ssm_state_update(hd, td["u"], td["dt_raw"], td["A"], td["Bm"], td["Cm"], dt_bias=td["dt_bias"],
+                         Dskip=td["Dskip"], z=td["z"], out=od)
+
+    for _ in range(5):
+        dec()
+    dms = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dec()
+        e1.record(stream)
+        e1.synchronize()
+        dms.append(e0.elapsed_time(e1))
+    Bd, Dd, Nd = y["h"].shape
+    dbytes = decode_bytes(Bd, Dd, Nd, 2, 4)
+    dsec = float(np.median(dms)) / 1e3
+
+    result = {
+        "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
+        "value": elements / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mamba130m-layer scan: B=8 D=1536 L=2048 N=16, bf16 u/dt/z/B/C, "
+                               "fp32 A/D/dt_bias/state/out, silu gate, no reset",
+                   "global_batch": B, "seq_len": L, "d_inner": D, "d_state": N, "parallelism": "none"},
+        "hbm_gbps": abytes / wall / 1e9,
+        "hbm_frac_of_peak": abytes / wall / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {
+            "kernel": "scan_kernel<NPL=1, bf16, no reset, full>",
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": ALU_PEAK_TOPS,
+            "unit": "TOP/s (fp32 VALU lane-ops; transcendental = 2)",
+            "frac": achieved / ALU_PEAK_TOPS,
+            "traffic": traffic,
+            "launch_ms_mean": launch_s * 1e3,
+            "algorithmic_bytes": abytes,
+            "algorithmic_ops": ops,
+            "hbm_gbps_at_launch_time": abytes / launch_s / 1e9,
+        },
+        "cold_cache": {"launch_ms_median": float(np.median(cold)), "launch_ms_p10": percentile(cold, 10),
+                       "launch_ms_p90": percentile(cold, 90),
+                       "hbm_gbps": abytes / (float(np.median(cold)) / 1e3) / 1e9},
+        "decode": {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
+                   "launch_ms_median": dsec * 1e3, "algorithmic_bytes": dbytes,
+                   "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS},
+    }
+
+    if not args.no_cpu:
+        import oracle
+
+        # The whole workload, every row, through the oracle (inputs widened to
+        # float64 before the clock starts).
+        w = wl.widen
+        rows = np.arange(B * D)
+        rb, rd = rows // D, rows % D
+        u64, dt64, z64 = (w(x[k]).reshape(B * D, L) for k in ("u", "dt_raw", "z"))
+        Bm64, Cm64 = w(x["Bm"]), w(x["Cm"])
+        threads = oracle.max_threads()
+        c0 = time.perf_counter()
+        ref = oracle.scan_rows(rb, rd, u64, dt64, x["A"], Bm64, Cm64, z_rows=z64, dt_bias=x["dt_bias"],
+                               Dskip=x["Dskip"])
+        csec = time.perf_counter() - c0
+        got = out.reshape(B * D, L).cpu().numpy().astype(np.float64)
+        margin = float(np.max(np.abs(got - ref) / (2e-3 * (1.0 + np.abs(ref)))))
+        result["cpu_baseline"] = {"value": elements / csec, "unit": "elements/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": "the full workload (all 12288 rows x 2048 steps x 16 states), "
+                                            "float64, OpenMP over rows; %.1f s" % csec}
+        result["parity_vs_oracle"] = {"rows": int(B * D), "max_err_over_bound": margin,
+                                      "bound": "2e-3*(1+|ref|)"}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

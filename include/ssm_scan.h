@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL_POINTER = 1, /* a required pointer (or params itself) is NULL   */
-  SSM_ERR_BAD_SHAPE = 2,    /* a size is < 1 (decode: < 1), N > SSM_MAX_DSTATE, or
+  SSM_ERR_BAD_SHAPE = 2,    /* a size is < 1, N > SSM_MAX_DSTATE, L >= 2^27, or
                                an element count overflows int64                */
   SSM_ERR_BAD_DTYPE = 3,    /* in_dtype / out_dtype is not an ssm_dtype         */
   SSM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size    */
@@ -76,7 +76,7 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 /*
  * Full-sequence scan (prefill / training forward).
  *
- *   batch, dim, seqlen, dstate : B, D, L, N;  B, D, L >= 1, 1 <= N <= 256
+ *   batch, dim, seqlen, dstate : B, D, L, N;  B, D >= 1, 1 <= L < 2^27, 1 <= N <= 256
  *   in_dtype  : element type of u, dt_raw, z, Bm, Cm (SSM_F32 or SSM_BF16)
  *   out_dtype : element type of out (SSM_F32 or SSM_BF16)
  *   u        (B,D,L)  required; the SSM input x (L contiguous)

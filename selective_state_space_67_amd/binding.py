@@ -213,6 +213,38 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     return out
 
 
+def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None, out=None,
+                 h_last=None, out_dtype=None, num_segments=0, stream=None):
+    """Marshal the arguments of ssm_scan_fwd once; returns a no-argument callable
+    that enqueues the same scan again (same tensors, same stream) each time it is
+    called. The tensors must stay alive and unchanged in shape while it is used."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
+    p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
+                     num_segments)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last]
+    if n.value:
+        ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
+        keep.append(ws)
+        p.workspace = _ptr(ws)
+        p.workspace_bytes = int(n.value)
+    st = _stream(stream, u.device)
+    fn = lib.ssm_scan_fwd
+    pref = ctypes.byref(p)
+
+    def call():
+        _check(fn(pref, st))
+        return out
+
+    call.keep = (keep, p)
+    return call
+
+
 def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
                      out_dtype=None, stream=None):
     """Decode step: updates h (B, D, N) float32 in place and returns out (B, D)."""

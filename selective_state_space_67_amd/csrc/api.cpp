@@ -74,8 +74,8 @@ ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
   if (p->dstate < 1 || p->dstate > SSM_MAX_DSTATE)
     return fail(SSM_ERR_BAD_SHAPE, "dstate must be in [1, %d] (got %lld)", SSM_MAX_DSTATE,
                 (long long)p->dstate);
-  if (p->seqlen > std::numeric_limits<int32_t>::max() / 2)
-    return fail(SSM_ERR_BAD_SHAPE, "seqlen %lld is too large", (long long)p->seqlen);
+  if (p->seqlen >= (int64_t{1} << 27))
+    return fail(SSM_ERR_BAD_SHAPE, "seqlen must be below 2^27 (got %lld)", (long long)p->seqlen);
   int64_t bd;
   const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
   if (!mul_ok(p->batch, p->dim, &bd) || !mul_ok(bd, p->seqlen, &sz->bdl) ||

@@ -104,21 +104,26 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   using TL = Tile<NPL>;
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
   constexpr int MASK = RING - 1;
-  // (delta, delta*u) rows carry a 16-entry mirror of their first 16 slots so a
-  // lane's 16-step window never wraps; (B, C) windows start at multiples of 16
-  // and cannot wrap.
-  constexpr int DU_STRIDE = RING + 16 + 2;
-  constexpr int BC_STRIDE = RING + 2;
   constexpr bool FULL = MODE == kFull;
-  constexpr int BC_ITEMS = T * NPAD / kThreads;       // (step, state) items per thread per chunk
-  constexpr int ROW_ITEMS = kChannels * T / kThreads; // (channel, step) items per thread per chunk
+  // LDS geometry, in float2 units.
+  //  (delta, delta*u): two copies x 16 channel rows. Each row carries a
+  //  16-entry mirror of its first 16 slots so a lane's 16-step window never
+  //  wraps. Row stride and copy offset were chosen by measurement on gfx950:
+  //  with a row stride of RING + 16 float2 and copy 1 offset by 16 float2
+  //  beyond copy 0's rows, the skewed 16-byte window reads of a wave are free
+  //  of bank conflicts.
+  constexpr int DU_STRIDE = RING + 16;
+  constexpr int DU_COPY = kChannels * DU_STRIDE + 16;
+  //  (B, C): one row per state; windows start at multiples of 16 and never wrap.
+  constexpr int BC_STRIDE = RING + 2;
+  constexpr int RI = kChannels * T / kThreads;   // consecutive steps per thread in row staging
+  constexpr int BC_ITEMS = T * NPAD / kThreads;  // (step, state) items per thread per chunk
+  static_assert(RI == 1 || RI == 2, "row staging handles one or two steps per thread");
   static_assert(BC_ITEMS >= 1 && (T * NPAD) % kThreads == 0, "B/C staging split");
-  static_assert(ROW_ITEMS >= 1 && (kChannels * T) % kThreads == 0, "row staging split");
 
-  __shared__ __align__(16) float2 s_du[2][kChannels][DU_STRIDE];   // (delta, delta*u), two shifted copies
-  __shared__ __align__(16) float2 s_bc[NPAD][BC_STRIDE];           // (B, C) per state, diagonal layout
-  __shared__ __align__(16) float s_y[FULL ? kChannels : 1][RING];  // finished sum_n C h per step
-  __shared__ __align__(16) float2 s_g[FULL ? kChannels : 1][RING]; // (D*u, silu(z)) per step
+  __shared__ __align__(16) float2 s_du[DU_COPY + kChannels * DU_STRIDE];
+  __shared__ __align__(16) float2 s_bc[NPAD * BC_STRIDE];
+  __shared__ __align__(16) float s_y[FULL ? kChannels * RING : 4];  // finished sum_n C h per step
 
   // Workgroup -> (piece, batch row, channel group). Consecutive logical tiles
   // share a batch row and therefore B and C; hardware dispatches consecutive
@@ -132,17 +137,27 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   const int s = rest / static_cast<int>(a.B);
   const int64_t t_seg = static_cast<int64_t>(s) * a.seg_len;
   const int Lseg = static_cast<int>(min(a.seg_len, a.L - t_seg));
-  const InT* __restrict__ u_in = static_cast<const InT*>(a.u);
-  const InT* __restrict__ dt_in = static_cast<const InT*>(a.dt);
-  const InT* __restrict__ z_in = static_cast<const InT*>(a.z);
-  const InT* __restrict__ B_in = static_cast<const InT*>(a.Bm);
-  const InT* __restrict__ C_in = static_cast<const InT*>(a.Cm);
+  const int L = static_cast<int>(a.L);
+  const int N = static_cast<int>(a.N);
+  const int64_t d0 = static_cast<int64_t>(g) * kChannels;
+  const bool group_full = d0 + kChannels <= a.D;
+
+  // Workgroup-uniform bases; per-thread offsets below stay in 32 bits
+  // (channel * L + step < 16 L, and L < 2^27 is checked by the front end).
+  const int64_t row0 = (static_cast<int64_t>(b) * a.D + d0) * a.L + t_seg;
+  const InT* __restrict__ u_wg = static_cast<const InT*>(a.u) + row0;
+  const InT* __restrict__ dt_wg = static_cast<const InT*>(a.dt) + row0;
+  const InT* __restrict__ z_wg = a.z ? static_cast<const InT*>(a.z) + row0 : nullptr;
+  const int64_t bc0 = (static_cast<int64_t>(b) * a.L + t_seg) * a.N;
+  const InT* __restrict__ B_wg = static_cast<const InT*>(a.Bm) + bc0;
+  const InT* __restrict__ C_wg = static_cast<const InT*>(a.Cm) + bc0;
+  const uint8_t* __restrict__ rs_wg = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L + t_seg : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int k = lane & 15;                        // lane within the channel's row
   const int c = (tid >> 6) * 4 + (lane >> 4);     // channel within the workgroup
-  const int64_t d = static_cast<int64_t>(g) * kChannels + c;
+  const int64_t d = d0 + c;
   const bool dvalid = d < a.D;
 
   // Per-lane parameters and state.
@@ -150,15 +165,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = k * NPL + j;
-    const bool ok = dvalid && n < a.N;
-    A2[j] = ok ? a.A[d * a.N + n] * kLog2e : 0.0f;
+    const bool ok = dvalid && n < N;
+    A2[j] = ok ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = 0.0f;
     if (FULL && ok) {
-      const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * a.N + n;
+      const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + n;
       float hv = a.h0 ? a.h0[hi] : 0.0f;
       // Fold the aggregates of the preceding pieces: h <- P h + H.
       for (int sp = 0; sp < s; ++sp) {
-        const int64_t wi = (static_cast<int64_t>(sp) * a.B + b) * a.D * a.N + d * a.N + n;
+        const int64_t wi = (static_cast<int64_t>(sp) * a.B + b) * a.D * N + d * N + n;
         hv = __builtin_fmaf(a.ws_P[wi], hv, a.ws_H[wi]);
       }
       h[j] = hv;
@@ -167,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
 
   // Empty rings: steps before the start (read by lagging lanes) are identity
   // steps (delta = 0, delta*u = 0, B = C = 0).
-  for (int i = tid; i < 2 * kChannels * DU_STRIDE; i += kThreads) (&s_du[0][0][0])[i] = make_float2(0.f, 0.f);
-  for (int i = tid; i < NPAD * BC_STRIDE; i += kThreads) (&s_bc[0][0])[i] = make_float2(0.f, 0.f);
+  for (int i = tid; i < DU_COPY + kChannels * DU_STRIDE; i += kThreads) s_du[i] = make_float2(0.f, 0.f);
+  for (int i = tid; i < NPAD * BC_STRIDE; i += kThreads) s_bc[i] = make_float2(0.f, 0.f);
 
   const int nchunks = (Lseg + 18 + T - 1) / T;  // lane 15 finishes step L-1 by iteration L+17
   const int p = k & 1;
@@ -179,106 +194,141 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   float sum_delta = 0.0f;
   bool cleared = false;
 
-  // Channel parameters of this thread's staging items (the channel of an item
-  // does not change from chunk to chunk).
-  float bias_r[ROW_ITEMS], dskip_r[ROW_ITEMS];
+  // Row-staging items of this thread: RI consecutive steps of one channel.
+  const int sc = tid / 16;              // channel
+  const int stl = (tid % 16) * RI;      // first step within the chunk
+  const unsigned srow = static_cast<unsigned>(sc * L + stl);  // offset from the workgroup base
+  const bool sc_valid = d0 + sc < a.D;
+  const float s_bias = sc_valid && a.dt_bias ? a.dt_bias[d0 + sc] : 0.0f;
+  const float s_dskip = sc_valid && a.Dskip ? a.Dskip[d0 + sc] : 0.0f;
+
+  // (step, state) staging items of this thread; offsets are chunk-invariant.
+  unsigned bc_off[BC_ITEMS];
+  int bc_tl[BC_ITEMS];
+  bool bc_ok[BC_ITEMS];
 #pragma unroll
-  for (int r = 0; r < ROW_ITEMS; ++r) {
-    const int64_t dd = static_cast<int64_t>(g) * kChannels + (tid + r * kThreads) / T;
-    const bool ok = dd < a.D;
-    bias_r[r] = ok && a.dt_bias ? a.dt_bias[dd] : 0.0f;
-    dskip_r[r] = ok && a.Dskip ? a.Dskip[dd] : 0.0f;
+  for (int r = 0; r < BC_ITEMS; ++r) {
+    const int q = tid + r * kThreads;
+    bc_tl[r] = q / NPAD;
+    bc_ok[r] = q % NPAD < N;
+    bc_off[r] = static_cast<unsigned>(bc_tl[r] * N + q % NPAD);
   }
 
-  // ---- raw inputs of one chunk, loaded a chunk ahead of their use ----
-  InT pb[BC_ITEMS], pc[BC_ITEMS], pu[ROW_ITEMS], pdt[ROW_ITEMS], pz[ROW_ITEMS];
-  uint8_t prs[ROW_ITEMS];
-  auto load_chunk = [&](int J) {
+  // Raw inputs of one chunk (loaded two chunks ahead of their use) and the
+  // per-step output factors D*u and silu(z) kept until the chunk is finished.
+  struct Raw {
+    InT b[BC_ITEMS], c[BC_ITEMS], u[RI], dt[RI], z[RI];
+    uint8_t rs[RI];
+  };
+  struct Out {
+    float dsk[RI], gate[RI];
+  };
+
+  // Interior chunks of a full channel group take the unmasked path; the last
+  // chunks and partial groups mask each item (masked items load nothing and
+  // stay zero).
+  auto load_chunk = [&](int J, Raw& r) {
     const int tau0 = J * T;
+    const InT* __restrict__ Bj = B_wg + static_cast<int64_t>(tau0) * N;
+    const InT* __restrict__ Cj = C_wg + static_cast<int64_t>(tau0) * N;
+    const InT* __restrict__ uj = u_wg + tau0;
+    const InT* __restrict__ dtj = dt_wg + tau0;
+    const InT* __restrict__ zj = z_wg ? z_wg + tau0 : nullptr;
+    const uint8_t* __restrict__ rsj = HAS_RESET ? rs_wg + tau0 : nullptr;
+    if (group_full && tau0 + T <= Lseg) {
 #pragma unroll
-    for (int r = 0; r < BC_ITEMS; ++r) {
-      const int q = tid + r * kThreads;
-      const int tau = tau0 + q / NPAD, n = q % NPAD;
-      pb[r] = InT{};
-      pc[r] = InT{};
-      if (tau < Lseg && n < a.N) {
-        const int64_t gi = (static_cast<int64_t>(b) * a.L + t_seg + tau) * a.N + n;
-        pb[r] = B_in[gi];
-        if (FULL) pc[r] = C_in[gi];
+      for (int q = 0; q < BC_ITEMS; ++q) {
+        r.b[q] = bc_ok[q] ? Bj[bc_off[q]] : InT{};
+        r.c[q] = FULL && bc_ok[q] ? Cj[bc_off[q]] : InT{};
       }
-    }
 #pragma unroll
-    for (int r = 0; r < ROW_ITEMS; ++r) {
-      const int q = tid + r * kThreads;
-      const int tau = tau0 + q % T;
-      const int64_t dd = static_cast<int64_t>(g) * kChannels + q / T;
-      pu[r] = InT{};
-      pdt[r] = InT{};
-      pz[r] = InT{};
-      prs[r] = 0;
-      if (tau < Lseg && dd < a.D) {
-        const int64_t t = t_seg + tau;
-        const int64_t gi = (static_cast<int64_t>(b) * a.D + dd) * a.L + t;
-        pu[r] = u_in[gi];
-        pdt[r] = dt_in[gi];
-        if (FULL && z_in) pz[r] = z_in[gi];
-        if (HAS_RESET) prs[r] = a.reset[static_cast<int64_t>(b) * a.L + t];
+      for (int i = 0; i < RI; ++i) {
+        r.u[i] = uj[srow + i];
+        r.dt[i] = dtj[srow + i];
+        r.z[i] = FULL && zj ? zj[srow + i] : InT{};
+        r.rs[i] = HAS_RESET ? rsj[stl + i] : 0;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < BC_ITEMS; ++q) {
+        const bool ok = bc_ok[q] && tau0 + bc_tl[q] < Lseg;
+        r.b[q] = ok ? Bj[bc_off[q]] : InT{};
+        r.c[q] = FULL && ok ? Cj[bc_off[q]] : InT{};
+      }
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        const bool ok = sc_valid && tau0 + stl + i < Lseg;
+        r.u[i] = ok ? uj[srow + i] : InT{};
+        r.dt[i] = ok ? dtj[srow + i] : InT{};
+        r.z[i] = FULL && zj && ok ? zj[srow + i] : InT{};
+        r.rs[i] = HAS_RESET && ok ? rsj[stl + i] : 0;
       }
     }
   };
 
-  // ---- chunk J into the rings: per-step parameters computed once ----
-  auto store_chunk = [&](int J) {
+  // ---- chunk J (ring half `par` = J & 1) into LDS: per-step parameters computed once ----
+  auto store_chunk = [&](int J, const int par, const Raw& r, Out& o) {
     const int tau0 = J * T;
 #pragma unroll
-    for (int r = 0; r < BC_ITEMS; ++r) {
-      const int q = tid + r * kThreads;
-      const int tau = tau0 + q / NPAD, n = q % NPAD;
-      s_bc[n][(tau + n / NPL) & MASK] = make_float2(load_elem(&pb[r], 0), FULL ? load_elem(&pc[r], 0) : 0.0f);
+    for (int q = 0; q < BC_ITEMS; ++q) {
+      const int n = (tid + q * kThreads) % NPAD;
+      s_bc[n * BC_STRIDE + ((par * T + bc_tl[q] + n / NPL) & MASK)] =
+          make_float2(load_elem(&r.b[q], 0), FULL ? load_elem(&r.c[q], 0) : 0.0f);
+    }
+    float dl[RI], dv[RI];
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+      // Items past the end carry zeros, which make identity steps (delta = 0).
+      const float uu = load_elem(&r.u[i], 0);
+      dl[i] = softplus_f32(load_elem(&r.dt[i], 0) + s_bias);
+      if (!sc_valid || tau0 + stl + i >= Lseg) dl[i] = 0.0f;
+      dv[i] = dl[i] * uu;
+      if (FULL) {
+        o.dsk[i] = s_dskip * uu;
+        o.gate[i] = z_wg ? silu_f32(load_elem(&r.z[i], 0)) : 1.0f;
+      }
+      if (HAS_RESET && r.rs[i]) dl[i] = -dl[i];  // sign bit: clear the state before this step
+    }
+    const int s0 = par * T + stl;                       // ring slot of this thread's first step
+    float2* du0 = s_du + sc * DU_STRIDE;                // copy 0: step tau at slot tau
+    float2* du1 = s_du + DU_COPY + sc * DU_STRIDE;      // copy 1: step tau at slot tau + 1
+    if (RI == 2) {
+      const float4 v = make_float4(dl[0], dv[0], dl[RI - 1], dv[RI - 1]);
+      *reinterpret_cast<float4*>(du0 + s0) = v;
+      if (s0 < 16) *reinterpret_cast<float4*>(du0 + s0 + RING) = v;
+    } else {
+      du0[s0] = make_float2(dl[0], dv[0]);
+      if (s0 < 16) du0[s0 + RING] = make_float2(dl[0], dv[0]);
     }
 #pragma unroll
-    for (int r = 0; r < ROW_ITEMS; ++r) {
-      const int q = tid + r * kThreads;
-      const int cc = q / T;
-      const int tau = tau0 + q % T;
-      const int64_t dd = static_cast<int64_t>(g) * kChannels + cc;
-      float dl = 0.0f, dv = 0.0f, dskip = 0.0f, gate = 1.0f;
-      if (tau < Lseg && dd < a.D) {
-        const float uu = load_elem(&pu[r], 0);
-        dl = softplus_f32(load_elem(&pdt[r], 0) + bias_r[r]);
-        dv = dl * uu;
-        if (FULL) {
-          dskip = dskip_r[r] * uu;
-          if (z_in) gate = silu_f32(load_elem(&pz[r], 0));
-        }
-        if (HAS_RESET && prs[r]) dl = -dl;  // sign bit: clear the state before this step
-      }
-      const float2 v = make_float2(dl, dv);
-      const int s0 = tau & MASK, s1 = (tau + 1) & MASK;
-      s_du[0][cc][s0] = v;
-      if (s0 < 16) s_du[0][cc][s0 + RING] = v;
-      s_du[1][cc][s1] = v;
-      if (s1 < 16) s_du[1][cc][s1 + RING] = v;
-      if (FULL) s_g[cc][s0] = make_float2(dskip, gate);
+    for (int i = 0; i < RI; ++i) {
+      const int s1 = (s0 + 1 + i) & MASK;
+      du1[s1] = make_float2(dl[i], dv[i]);
+      if (s1 < 16) du1[s1 + RING] = make_float2(dl[i], dv[i]);
     }
   };
 
   // ---- the finished outputs of chunk J: out = (y + D u) silu(z) ----
-  auto finalize = [&](int J) {
+  auto finalize = [&](int J, const int par, const Out& o) {
+    const int tau0 = J * T;
+    const int s0 = par * T + stl;
+    float y[RI];
+    if (RI == 2) {
+      const float2 yy = *reinterpret_cast<const float2*>(s_y + sc * RING + s0);
+      y[0] = yy.x;
+      y[RI - 1] = yy.y;
+    } else {
+      y[0] = s_y[sc * RING + s0];
+    }
+    const int64_t o0 = row0 + tau0 + srow;  // element index of this thread's first output
 #pragma unroll
-    for (int r = 0; r < ROW_ITEMS; ++r) {
-      const int q = tid + r * kThreads;
-      const int cc = q / T;
-      const int tau = J * T + q % T;
-      const int64_t dd = static_cast<int64_t>(g) * kChannels + cc;
-      if (tau < Lseg && dd < a.D) {
-        const float2 gg = s_g[cc][tau & MASK];
-        const float o = (s_y[cc][tau & MASK] + gg.x) * gg.y;
-        const int64_t gi = (static_cast<int64_t>(b) * a.D + dd) * a.L + t_seg + tau;
+    for (int i = 0; i < RI; ++i) {
+      if (sc_valid && tau0 + stl + i < Lseg) {
+        const float v = (y[i] + o.dsk[i]) * o.gate[i];
         if (a.out_bf16)
-          store_elem(static_cast<bf16_t*>(a.out), gi, o);
+          store_elem(static_cast<bf16_t*>(a.out), o0 + i, v);
         else
-          store_elem(static_cast<float*>(a.out), gi, o);
+          store_elem(static_cast<float*>(a.out), o0 + i, v);
       }
     }
   };
@@ -306,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
       yreg[i] = row_shr1(yreg[(i + 15) & 15]) + part;
       if ((i & 3) == 2 && k == 15) {
         // steps m0+i-18 .. m0+i-15 are complete in this row: one aligned 16-byte store
-        *reinterpret_cast<float4*>(&s_y[c][(m0 + i - 18) & MASK]) =
+        *reinterpret_cast<float4*>(s_y + c * RING + ((m0 + i - 18) & MASK)) =
             make_float4(yreg[(i - 3) & 15], yreg[(i - 2) & 15], yreg[(i - 1) & 15], yreg[i]);
       }
     } else {
@@ -314,47 +364,81 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
     }
   };
 
-  load_chunk(0);
-  __syncthreads();  // rings are empty before the first chunk is stored
-  for (int J = 0; J < nchunks; ++J) {
-    store_chunk(J);
-    if (J + 1 < nchunks) load_chunk(J + 1);  // in flight during this chunk's recurrence
-    __syncthreads();
+  const float2* du_row = s_du + p * DU_COPY + c * DU_STRIDE;
+  const float2* bc_row = s_bc + (k * NPL) * BC_STRIDE;
+
+  // ---- the recurrence over chunk J (ring half `par`) ----
+  auto compute = [&](const int par) {
+#pragma unroll 1
     for (int blk = 0; blk < T / 16; ++blk) {
-      const int m0 = J * T + blk * 16;
+      const int m0 = par * T + blk * 16;  // ring position of the block (step offsets cancel mod RING)
       // This lane's 16-step window of (delta, delta*u) pairs, pair-aligned in copy p.
-      const float2* du_win = &s_du[p][c][(m0 - k + p) & MASK];
-      const float2* bc_win = &s_bc[k * NPL][m0 & MASK];
+      const float2* du_win = du_row + ((m0 - k + p) & MASK);
+      const float2* bc_win = bc_row + m0;
+      float4 dd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dd[i] = *reinterpret_cast<const float4*>(du_win + 2 * i);
+      float4 bcb[NPL == 1 ? 8 : 1];
+      if (NPL == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bcb[NPL == 1 ? i : 0] = *reinterpret_cast<const float4*>(bc_win + 2 * i);
+      }
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float4 dd = *reinterpret_cast<const float4*>(du_win + i);
         float B0[NPL], C0[NPL], B1[NPL], C1[NPL];
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          const float4 v = *reinterpret_cast<const float4*>(bc_win + j * BC_STRIDE + i);
+          const float4 v = NPL == 1 ? bcb[NPL == 1 ? i / 2 : 0]
+                                    : *reinterpret_cast<const float4*>(bc_win + j * BC_STRIDE + i);
           B0[j] = v.x;
           C0[j] = v.y;
           B1[j] = v.z;
           C1[j] = v.w;
         }
-        step(i, m0, dd.x, dd.y, B0, C0);
-        step(i + 1, m0, dd.z, dd.w, B1, C1);
+        step(i, m0, dd[i / 2].x, dd[i / 2].y, B0, C0);
+        step(i + 1, m0, dd[i / 2].z, dd[i / 2].w, B1, C1);
       }
     }
+  };
+
+  Raw r0, r1;
+  Out o0, o1;
+  load_chunk(0, r0);
+  if (nchunks > 1) load_chunk(1, r1);
+  __syncthreads();  // rings are empty before the first chunk is stored
+  for (int J = 0; J < nchunks; J += 2) {
+    // even chunk: ring half 0, register sets r0 / o0
+    store_chunk(J, 0, r0, o0);
+    if (J + 2 < nchunks) load_chunk(J + 2, r0);
     __syncthreads();
-    if (FULL && J >= 1) finalize(J - 1);
+    compute(0);
+    __syncthreads();
+    if (FULL && J >= 1) finalize(J - 1, 1, o1);
+    if (J + 1 >= nchunks) break;
+    // odd chunk: ring half 1, register sets r1 / o1
+    store_chunk(J + 1, 1, r1, o1);
+    if (J + 3 < nchunks) load_chunk(J + 3, r1);
+    __syncthreads();
+    compute(1);
+    __syncthreads();
+    if (FULL) finalize(J, 0, o0);
   }
-  if (FULL && (nchunks - 1) * T < Lseg) finalize(nchunks - 1);
+  if (FULL && (nchunks - 1) * T < Lseg) {
+    if ((nchunks - 1) & 1)
+      finalize(nchunks - 1, 1, o1);
+    else
+      finalize(nchunks - 1, 0, o0);
+  }
 
   // ---- results that leave the workgroup ----
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = k * NPL + j;
-    if (!dvalid || n >= a.N) continue;
+    if (!dvalid || n >= N) continue;
     if (FULL) {
-      if (a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * a.N + n] = h[j];
+      if (a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * N + n] = h[j];
     } else {
-      const int64_t wi = (static_cast<int64_t>(s) * a.B + b) * a.D * a.N + d * a.N + n;
+      const int64_t wi = (static_cast<int64_t>(s) * a.B + b) * a.D * N + d * N + n;
       a.ws_H[wi] = h[j];
       a.ws_P[wi] = cleared ? 0.0f : fast_exp2(A2[j] * sum_delta);
     }
