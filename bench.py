@@ -47,7 +47,7 @@ OPS_PER_ELEMENT = 6.0
 OPS_PER_ROW_STEP = 18.0
 SCAN_SOURCES = ["selective_state_space_67_amd/csrc/scan_fwd.hip",
                 "selective_state_space_67_amd/csrc/device_math.h"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_counters_mamba130m.md")
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
 def scan_source_hash() -> str:
@@ -58,11 +58,13 @@ def scan_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed counter summary, if still valid."""
-    if not os.path.exists(COUNTERS_FILE):
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, if the kernel source is unchanged since it was taken."""
+    path = os.path.join(COUNTERS_DIR, "scan_counters_%s.md" % workload)
+    if not os.path.exists(path):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != scan_source_hash():
@@ -96,6 +98,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index (1 = Mamba-130M layer, the default and the headline; 0, 2, 3, 4 "
+                         "print their own line for reference)")
+    ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL-evicting write")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (for counter calibration runs)")
     args = ap.parse_args()
@@ -112,13 +118,14 @@ def main():
 
     load_library()
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS[1]
+    cfg = wl.CONFIGS[args.config]
     B, D, L, N = cfg["B"], cfg["D"], cfg["L"], cfg["N"]
-    x = wl.config_inputs(1)
-    t = {k: wl.to_torch(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    x = wl.config_inputs(args.config)
+    t = {k: wl.to_torch(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
     out = torch.empty((B, D, L), dtype=torch.float32, device=dev)
     call = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
-                                Dskip=t["Dskip"], z=t["z"], out=out)
+                                Dskip=t["Dskip"], z=t["z"], reset=t["reset"], out=out)
+    s_in = 4 if cfg["dtype"] == wl.F32 else 2
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
@@ -144,17 +151,18 @@ def main():
     launch_s = float(np.mean(launch_ms)) / 1e3
 
     # Cold caches: a 1 GiB write before each launch, outside the timed events.
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold = []
-    for i in range(min(args.steps, 50)):
-        scratch.fill_(float(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        call()
-        e1.record(stream)
-        e1.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del scratch
+    if args.cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for i in range(min(args.steps, 50)):
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del scratch
 
     if args.copy_calibration:
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
@@ -164,10 +172,10 @@ def main():
         del src, dst
 
     elements = B * D * L * N
-    abytes = algorithmic_bytes(B, D, L, N, 2, 4)
+    abytes = algorithmic_bytes(B, D, L, N, s_in, 4, reset=x["reset"] is not None)
     ops = OPS_PER_ELEMENT * elements + OPS_PER_ROW_STEP * B * D * L
     achieved = ops / launch_s / 1e12
-    traffic = recorded_traffic()
+    traffic = recorded_traffic(cfg["name"])
 
     # Decode step at its workload size.
     y = wl.decode_inputs()
@@ -206,13 +214,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "mamba130m-layer scan: B=8 D=1536 L=2048 N=16, bf16 u/dt/z/B/C, "
-                               "fp32 A/D/dt_bias/state/out, silu gate, no reset",
+        "config": {"workload": "%s scan: B=%d D=%d L=%d N=%d, %s u/dt/z/B/C, fp32 A/D/dt_bias/state/out, "
+                               "silu gate, %s" % (cfg["name"], B, D, L, N, cfg["dtype"],
+                                                  "document resets" if cfg["packed"] else "no reset"),
                    "global_batch": B, "seq_len": L, "d_inner": D, "d_state": N, "parallelism": "none"},
         "hbm_gbps": abytes / wall / 1e9,
         "hbm_frac_of_peak": abytes / wall / 1e9 / HBM_PEAK_GBPS,
         "roofline": {
-            "kernel": "scan_kernel<NPL=1, bf16, no reset, full>",
+            "kernel": "scan_kernel<NPL=%d, %s, %s>" % (max(1, (N + 15) // 16), cfg["dtype"],
+                                                       "reset" if cfg["packed"] else "no reset"),
             "bound": "alu",
             "achieved": achieved,
             "peak": ALU_PEAK_TOPS,
@@ -224,9 +234,9 @@ def main():
             "algorithmic_ops": ops,
             "hbm_gbps_at_launch_time": abytes / launch_s / 1e9,
         },
-        "cold_cache": {"launch_ms_median": float(np.median(cold)), "launch_ms_p10": percentile(cold, 10),
-                       "launch_ms_p90": percentile(cold, 90),
-                       "hbm_gbps": abytes / (float(np.median(cold)) / 1e3) / 1e9},
+        "cold_cache": None if not cold else {
+            "launch_ms_median": float(np.median(cold)), "launch_ms_p10": percentile(cold, 10),
+            "launch_ms_p90": percentile(cold, 90), "hbm_gbps": abytes / (float(np.median(cold)) / 1e3) / 1e9},
         "decode": {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
                    "launch_ms_median": dsec * 1e3, "algorithmic_bytes": dbytes,
                    "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS},
@@ -245,16 +255,17 @@ def main():
         threads = oracle.max_threads()
         c0 = time.perf_counter()
         ref = oracle.scan_rows(rb, rd, u64, dt64, x["A"], Bm64, Cm64, z_rows=z64, dt_bias=x["dt_bias"],
-                               Dskip=x["Dskip"])
+                               Dskip=x["Dskip"], reset=x["reset"])
         csec = time.perf_counter() - c0
         got = out.reshape(B * D, L).cpu().numpy().astype(np.float64)
-        margin = float(np.max(np.abs(got - ref) / (2e-3 * (1.0 + np.abs(ref)))))
+        tol = 1e-5 if cfg["dtype"] == wl.F32 else 2e-3
+        margin = float(np.max(np.abs(got - ref) / (tol * (1.0 + np.abs(ref)))))
         result["cpu_baseline"] = {"value": elements / csec, "unit": "elements/s", "cores": threads,
                                   "kind": "oracle",
-                                  "sample": "the full workload (all 12288 rows x 2048 steps x 16 states), "
-                                            "float64, OpenMP over rows; %.1f s" % csec}
+                                  "sample": "the full workload (all %d rows x %d steps x %d states), "
+                                            "float64, OpenMP over rows; %.2f s" % (B * D, L, N, csec)}
         result["parity_vs_oracle"] = {"rows": int(B * D), "max_err_over_bound": margin,
-                                      "bound": "2e-3*(1+|ref|)"}
+                                      "bound": "%g*(1+|ref|)" % tol}
     print(json.dumps(result))
 
 

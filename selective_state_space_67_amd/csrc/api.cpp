@@ -89,7 +89,7 @@ ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
 ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
   if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
   ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
-  if (ssm::scan_grid_blocks(p->batch, p->dim, *nseg) > std::numeric_limits<int32_t>::max())
+  if (ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg) > std::numeric_limits<int32_t>::max())
     return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
   *ws = ssm::scan_workspace_bytes(p->batch, p->dim, p->dstate, *nseg);
   return SSM_OK;

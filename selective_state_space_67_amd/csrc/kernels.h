@@ -45,8 +45,7 @@ struct UpdatePlan {
   void* out;
 };
 
-// Channels per workgroup of the scan kernels and the largest state size.
-constexpr int kScanChannelsPerBlock = 16;
+// Largest supported state size.
 constexpr int kMaxState = 256;
 
 // How many pieces the sequence is split into (requested = 0: automatic) and
@@ -59,7 +58,7 @@ void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, in
 size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg);
 
 // Number of workgroups the scan launches use (for grid-limit checks).
-int64_t scan_grid_blocks(int64_t B, int64_t D, int nseg);
+int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg);
 
 hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
 hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);

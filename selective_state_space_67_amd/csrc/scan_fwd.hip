@@ -16,18 +16,20 @@
 // float32 operations per (b, d, t, n), while it moves well under one byte of
 // HBM traffic per element, so the vector ALU -- not HBM -- is the limit.
 //
-// Mapping. A workgroup owns 16 channels of one batch row (4 waves, 4 channels
-// per wave). Within a wave each channel occupies one DPP row of 16 lanes and
-// lane k of that row holds states n = k*NPL .. k*NPL+NPL-1 in registers. Every
-// lane runs the recurrence sequentially in time for its own states, so no
-// per-element work is spent on a parallel scan; the (b, d, n) recurrences
-// already give each launch thousands of waves.
+// Mapping. A workgroup owns CPW channels of one batch row. Each channel
+// occupies RPC DPP rows of 16 lanes (RPC = 1, 2 or 4 by state size, so that
+// even N = 128 launches four waves per SIMD), and lane k of slice s holds
+// states n = (16 s + k) * NPL .. + NPL - 1 in registers. Every lane runs the
+// recurrence sequentially in time for its own states, so no per-element work
+// is spent on a parallel scan; the (b, d, n) recurrences already give each
+// launch thousands of waves.
 //
 // Skewed pipeline. Lane k processes step t at iteration m = t + k. The partial
 // output sum_n C h of lane k is added to the running sum that lane k-1
 // produced for the same step one iteration earlier (one DPP row_shr:1 add), so
-// after lane 15 the row holds the full dot product over n. This costs one add
-// per lane-step instead of a log2(16)-level reduction.
+// after lane 15 the row holds the dot product over its slice of n. This costs
+// one add per lane-step instead of a log2(16)-level reduction; the RPC slice
+// sums of a channel are added when the output is written.
 //
 // Staging. Per chunk of T steps the workgroup
 //  - loads dt_raw, u, z along L (consecutive threads read consecutive steps)
@@ -40,8 +42,9 @@
 //    reads the copy that aligns its window (k odd or even);
 //  - (B, C) of state n is stored in row n at column t + n/NPL, which cancels
 //    the lane's skew, so lane k's window starts at a multiple of 16.
-// Lane 15 of each row writes the finished sums into an LDS ring; after the
-// next chunk the workgroup applies D*u and the gate and stores `out` along L.
+// Lane 15 of each row writes the finished slice sums into an LDS ring; after
+// the next chunk the workgroup adds the slices, applies D*u and the gate and
+// stores `out` along L.
 //
 // Long sequences with few channels (L split into pieces): a first launch
 // computes each piece's affine aggregate (product of the decays and the end
@@ -61,16 +64,21 @@
 namespace ssm {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChannels = kScanChannelsPerBlock;  // 16 = 4 waves x 4 rows
-
 enum Mode { kFull = 0, kAggregate = 1 };
 
-template <int NPL>
+// Work layout of one kernel instance, fixed at compile time.
+template <int NPL_, int RPC_>
 struct Tile {
-  static constexpr int NPAD = 16 * NPL;          // states covered by one row
-  static constexpr int T = NPL <= 2 ? 32 : 16;   // steps per chunk
-  static constexpr int RING = 2 * T;             // steps kept in LDS
+  static constexpr int NPL = NPL_;                  // states per lane
+  static constexpr int RPC = RPC_;                  // DPP rows (slices) per channel
+  static constexpr int WAVES = RPC >= 4 ? 8 : 4;    // waves per workgroup
+  static constexpr int THREADS = 64 * WAVES;
+  // Register budget for the occupancy the layout relies on (waves per SIMD).
+  static constexpr int MIN_WAVES_PER_SIMD = NPL >= 4 ? 2 : RPC >= 4 ? 4 : 3;
+  static constexpr int CPW = WAVES * 4 / RPC;       // channels per workgroup
+  static constexpr int NPAD = 16 * NPL * RPC;       // states covered per channel
+  static constexpr int T = NPAD <= 32 ? 32 : 16;    // steps per chunk
+  static constexpr int RING = 2 * T;                // steps kept in LDS
   static_assert((RING & (RING - 1)) == 0, "ring length must be a power of two");
   static_assert(T % 16 == 0 && T >= 16, "chunk must hold whole 16-step blocks");
 };
@@ -99,31 +107,35 @@ struct ScanArgs {
   float* ws_H;  // end states of pieces 0..nseg-2 from a zero start
 };
 
-template <int NPL, typename InT, bool HAS_RESET, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
-  using TL = Tile<NPL>;
+template <typename TL, typename InT, bool HAS_RESET, int MODE>
+__global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kernel(const ScanArgs a) {
+  constexpr int NPL = TL::NPL, RPC = TL::RPC, CPW = TL::CPW, THREADS = TL::THREADS;
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
   constexpr int MASK = RING - 1;
   constexpr bool FULL = MODE == kFull;
   // LDS geometry, in float2 units.
-  //  (delta, delta*u): two copies x 16 channel rows. Each row carries a
+  //  (delta, delta*u): two copies x CPW channel rows. Each row carries a
   //  16-entry mirror of its first 16 slots so a lane's 16-step window never
   //  wraps. Row stride and copy offset were chosen by measurement on gfx950:
   //  with a row stride of RING + 16 float2 and copy 1 offset by 16 float2
   //  beyond copy 0's rows, the skewed 16-byte window reads of a wave are free
   //  of bank conflicts.
   constexpr int DU_STRIDE = RING + 16;
-  constexpr int DU_COPY = kChannels * DU_STRIDE + 16;
+  constexpr int DU_COPY = CPW * DU_STRIDE + 16;
   //  (B, C): one row per state; windows start at multiples of 16 and never wrap.
   constexpr int BC_STRIDE = RING + 2;
-  constexpr int RI = kChannels * T / kThreads;   // consecutive steps per thread in row staging
-  constexpr int BC_ITEMS = T * NPAD / kThreads;  // (step, state) items per thread per chunk
-  static_assert(RI == 1 || RI == 2, "row staging handles one or two steps per thread");
-  static_assert(BC_ITEMS >= 1 && (T * NPAD) % kThreads == 0, "B/C staging split");
+  // Row staging: CPW x T (channel, step) items per chunk, RI consecutive steps
+  // per thread, handled by the first ROW_THREADS threads.
+  constexpr int ROW_ITEMS = CPW * T;
+  constexpr int RI = ROW_ITEMS >= 2 * THREADS ? 2 : 1;
+  constexpr int ROW_THREADS = ROW_ITEMS / RI;
+  constexpr int BC_ITEMS = T * NPAD / THREADS;  // (step, state) items per thread per chunk
+  static_assert(ROW_THREADS <= THREADS && ROW_ITEMS % RI == 0, "row staging split");
+  static_assert(BC_ITEMS >= 1 && (T * NPAD) % THREADS == 0, "B/C staging split");
 
-  __shared__ __align__(16) float2 s_du[DU_COPY + kChannels * DU_STRIDE];
+  __shared__ __align__(16) float2 s_du[DU_COPY + CPW * DU_STRIDE];
   __shared__ __align__(16) float2 s_bc[NPAD * BC_STRIDE];
-  __shared__ __align__(16) float s_y[FULL ? kChannels * RING : 4];  // finished sum_n C h per step
+  __shared__ __align__(16) float s_y[FULL ? CPW * RPC * RING : 4];  // finished slice sums per step
 
   // Workgroup -> (piece, batch row, channel group). Consecutive logical tiles
   // share a batch row and therefore B and C; hardware dispatches consecutive
@@ -139,11 +151,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   const int Lseg = static_cast<int>(min(a.seg_len, a.L - t_seg));
   const int L = static_cast<int>(a.L);
   const int N = static_cast<int>(a.N);
-  const int64_t d0 = static_cast<int64_t>(g) * kChannels;
-  const bool group_full = d0 + kChannels <= a.D;
+  const int64_t d0 = static_cast<int64_t>(g) * CPW;
+  const bool group_full = d0 + CPW <= a.D;
 
   // Workgroup-uniform bases; per-thread offsets below stay in 32 bits
-  // (channel * L + step < 16 L, and L < 2^27 is checked by the front end).
+  // (channel * L + step < CPW L <= 16 L, and L < 2^27 is checked by the front end).
   const int64_t row0 = (static_cast<int64_t>(b) * a.D + d0) * a.L + t_seg;
   const InT* __restrict__ u_wg = static_cast<const InT*>(a.u) + row0;
   const InT* __restrict__ dt_wg = static_cast<const InT*>(a.dt) + row0;
@@ -155,16 +167,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int k = lane & 15;                        // lane within the channel's row
-  const int c = (tid >> 6) * 4 + (lane >> 4);     // channel within the workgroup
+  const int k = lane & 15;                          // lane within its DPP row
+  const int grow = (tid >> 6) * 4 + (lane >> 4);    // DPP row within the workgroup
+  const int c = grow / RPC;                         // channel within the workgroup
+  const int slice = grow % RPC;                     // slice of the channel's states
   const int64_t d = d0 + c;
   const bool dvalid = d < a.D;
+  const int nbase = (slice * 16 + k) * NPL;         // first state of this lane
 
   // Per-lane parameters and state.
   float A2[NPL], h[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const int n = k * NPL + j;
+    const int n = nbase + j;
     const bool ok = dvalid && n < N;
     A2[j] = ok ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = 0.0f;
@@ -182,8 +197,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
 
   // Empty rings: steps before the start (read by lagging lanes) are identity
   // steps (delta = 0, delta*u = 0, B = C = 0).
-  for (int i = tid; i < DU_COPY + kChannels * DU_STRIDE; i += kThreads) s_du[i] = make_float2(0.f, 0.f);
-  for (int i = tid; i < NPAD * BC_STRIDE; i += kThreads) s_bc[i] = make_float2(0.f, 0.f);
+  for (int i = tid; i < DU_COPY + CPW * DU_STRIDE; i += THREADS) s_du[i] = make_float2(0.f, 0.f);
+  for (int i = tid; i < NPAD * BC_STRIDE; i += THREADS) s_bc[i] = make_float2(0.f, 0.f);
 
   const int nchunks = (Lseg + 18 + T - 1) / T;  // lane 15 finishes step L-1 by iteration L+17
   const int p = k & 1;
@@ -195,24 +210,18 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   bool cleared = false;
 
   // Row-staging items of this thread: RI consecutive steps of one channel.
-  const int sc = tid / 16;              // channel
-  const int stl = (tid % 16) * RI;      // first step within the chunk
+  const bool row_thread = tid < ROW_THREADS;
+  const int sc = (tid / (T / RI)) % CPW;   // channel (threads past ROW_THREADS repeat, unused)
+  const int stl = (tid % (T / RI)) * RI;   // first step within the chunk
   const unsigned srow = static_cast<unsigned>(sc * L + stl);  // offset from the workgroup base
-  const bool sc_valid = d0 + sc < a.D;
+  const bool sc_valid = row_thread && d0 + sc < a.D;
   const float s_bias = sc_valid && a.dt_bias ? a.dt_bias[d0 + sc] : 0.0f;
   const float s_dskip = sc_valid && a.Dskip ? a.Dskip[d0 + sc] : 0.0f;
 
-  // (step, state) staging items of this thread; offsets are chunk-invariant.
-  unsigned bc_off[BC_ITEMS];
-  int bc_tl[BC_ITEMS];
-  bool bc_ok[BC_ITEMS];
-#pragma unroll
-  for (int r = 0; r < BC_ITEMS; ++r) {
-    const int q = tid + r * kThreads;
-    bc_tl[r] = q / NPAD;
-    bc_ok[r] = q % NPAD < N;
-    bc_off[r] = static_cast<unsigned>(bc_tl[r] * N + q % NPAD);
-  }
+  // (step, state) staging item q of this thread: step q_tl within the chunk,
+  // state q_n (NPAD is a power of two, so these are a shift and a mask).
+  auto bc_tl = [&](int q) { return (tid + q * THREADS) / NPAD; };
+  auto bc_n = [&](int q) { return (tid + q * THREADS) % NPAD; };
 
   // Raw inputs of one chunk (loaded two chunks ahead of their use) and the
   // per-step output factors D*u and silu(z) kept until the chunk is finished.
@@ -238,22 +247,25 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
     if (group_full && tau0 + T <= Lseg) {
 #pragma unroll
       for (int q = 0; q < BC_ITEMS; ++q) {
-        r.b[q] = bc_ok[q] ? Bj[bc_off[q]] : InT{};
-        r.c[q] = FULL && bc_ok[q] ? Cj[bc_off[q]] : InT{};
+        const bool ok = bc_n(q) < N;
+        const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
+        r.b[q] = ok ? Bj[off] : InT{};
+        r.c[q] = FULL && ok ? Cj[off] : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
-        r.u[i] = uj[srow + i];
-        r.dt[i] = dtj[srow + i];
-        r.z[i] = FULL && zj ? zj[srow + i] : InT{};
-        r.rs[i] = HAS_RESET ? rsj[stl + i] : 0;
+        r.u[i] = row_thread ? uj[srow + i] : InT{};
+        r.dt[i] = row_thread ? dtj[srow + i] : InT{};
+        r.z[i] = FULL && zj && row_thread ? zj[srow + i] : InT{};
+        r.rs[i] = HAS_RESET && row_thread ? rsj[stl + i] : 0;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < BC_ITEMS; ++q) {
-        const bool ok = bc_ok[q] && tau0 + bc_tl[q] < Lseg;
-        r.b[q] = ok ? Bj[bc_off[q]] : InT{};
-        r.c[q] = FULL && ok ? Cj[bc_off[q]] : InT{};
+        const bool ok = bc_n(q) < N && tau0 + bc_tl(q) < Lseg;
+        const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
+        r.b[q] = ok ? Bj[off] : InT{};
+        r.c[q] = FULL && ok ? Cj[off] : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
@@ -271,10 +283,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
     const int tau0 = J * T;
 #pragma unroll
     for (int q = 0; q < BC_ITEMS; ++q) {
-      const int n = (tid + q * kThreads) % NPAD;
-      s_bc[n * BC_STRIDE + ((par * T + bc_tl[q] + n / NPL) & MASK)] =
+      const int n = bc_n(q);
+      s_bc[n * BC_STRIDE + ((par * T + bc_tl(q) + (n / NPL) % 16) & MASK)] =
           make_float2(load_elem(&r.b[q], 0), FULL ? load_elem(&r.c[q], 0) : 0.0f);
     }
+    if (!row_thread) return;
     float dl[RI], dv[RI];
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
@@ -308,17 +321,24 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
     }
   };
 
-  // ---- the finished outputs of chunk J: out = (y + D u) silu(z) ----
+  // ---- the finished outputs of chunk J: out = (sum of slices + D u) silu(z) ----
   auto finalize = [&](int J, const int par, const Out& o) {
+    if (!row_thread) return;
     const int tau0 = J * T;
     const int s0 = par * T + stl;
     float y[RI];
-    if (RI == 2) {
-      const float2 yy = *reinterpret_cast<const float2*>(s_y + sc * RING + s0);
-      y[0] = yy.x;
-      y[RI - 1] = yy.y;
-    } else {
-      y[0] = s_y[sc * RING + s0];
+#pragma unroll
+    for (int i = 0; i < RI; ++i) y[i] = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < RPC; ++sl) {
+      const float* yrow = s_y + (sc * RPC + sl) * RING + s0;
+      if (RI == 2) {
+        const float2 yy = *reinterpret_cast<const float2*>(yrow);
+        y[0] += yy.x;
+        y[RI - 1] += yy.y;
+      } else {
+        y[0] += yrow[0];
+      }
     }
     const int64_t o0 = row0 + tau0 + srow;  // element index of this thread's first output
 #pragma unroll
@@ -334,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   };
 
   // ---- one recurrence step of this lane (unrolled position i in a 16-step block) ----
+  float* const yslot = s_y + grow * RING;  // this row's slice sums
   auto step = [&](const int i, const int m0, float dl, const float dv, const float (&Bv)[NPL],
                   const float (&Cv)[NPL]) {
     if (HAS_RESET) {
@@ -356,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
       yreg[i] = row_shr1(yreg[(i + 15) & 15]) + part;
       if ((i & 3) == 2 && k == 15) {
         // steps m0+i-18 .. m0+i-15 are complete in this row: one aligned 16-byte store
-        *reinterpret_cast<float4*>(s_y + c * RING + ((m0 + i - 18) & MASK)) =
+        *reinterpret_cast<float4*>(yslot + ((m0 + i - 18) & MASK)) =
             make_float4(yreg[(i - 3) & 15], yreg[(i - 2) & 15], yreg[(i - 1) & 15], yreg[i]);
       }
     } else {
@@ -365,38 +386,75 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   };
 
   const float2* du_row = s_du + p * DU_COPY + c * DU_STRIDE;
-  const float2* bc_row = s_bc + (k * NPL) * BC_STRIDE;
+  const float2* bc_row = s_bc + nbase * BC_STRIDE;
 
   // ---- the recurrence over chunk J (ring half `par`) ----
+  // One lane-step reads one (delta, delta*u) pair and NPL (B, C) pairs. With
+  // one state per lane and up to three waves per SIMD (the register budget
+  // allows it), the reads of each 8-step half block are issued while the
+  // previous half block computes (two register sets, alternating statically).
   auto compute = [&](const int par) {
-#pragma unroll 1
-    for (int blk = 0; blk < T / 16; ++blk) {
-      const int m0 = par * T + blk * 16;  // ring position of the block (step offsets cancel mod RING)
-      // This lane's 16-step window of (delta, delta*u) pairs, pair-aligned in copy p.
-      const float2* du_win = du_row + ((m0 - k + p) & MASK);
-      const float2* bc_win = bc_row + m0;
-      float4 dd[8];
+    if constexpr (NPL == 1 && RPC <= 2) {
+      constexpr int HB = T / 8;
+      float4 dA[4], bA[NPL][4], dB[4], bB[NPL][4];
+      auto fetch = [&](const int hb, float4 (&dd)[4], float4 (&bb)[NPL][4]) {
+        const int m0 = par * T + (hb >> 1) * 16;
+        const float2* du_win = du_row + ((m0 - k + p) & MASK) + (hb & 1) * 8;
+        const float2* bc_win = bc_row + m0 + (hb & 1) * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dd[i] = *reinterpret_cast<const float4*>(du_win + 2 * i);
-      float4 bcb[NPL == 1 ? 8 : 1];
-      if (NPL == 1) {
+        for (int i = 0; i < 4; ++i) {
+          dd[i] = *reinterpret_cast<const float4*>(du_win + 2 * i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bcb[NPL == 1 ? i : 0] = *reinterpret_cast<const float4*>(bc_win + 2 * i);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float B0[NPL], C0[NPL], B1[NPL], C1[NPL];
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-          const float4 v = NPL == 1 ? bcb[NPL == 1 ? i / 2 : 0]
-                                    : *reinterpret_cast<const float4*>(bc_win + j * BC_STRIDE + i);
-          B0[j] = v.x;
-          C0[j] = v.y;
-          B1[j] = v.z;
-          C1[j] = v.w;
+          for (int j = 0; j < NPL; ++j) bb[j][i] = *reinterpret_cast<const float4*>(bc_win + j * BC_STRIDE + 2 * i);
         }
-        step(i, m0, dd[i / 2].x, dd[i / 2].y, B0, C0);
-        step(i + 1, m0, dd[i / 2].z, dd[i / 2].w, B1, C1);
+      };
+      auto run = [&](const int hb, const float4 (&dd)[4], const float4 (&bb)[NPL][4]) {
+        const int m0 = par * T + (hb >> 1) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int st = (hb & 1) * 8 + 2 * i;
+          float B0[NPL], C0[NPL], B1[NPL], C1[NPL];
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) {
+            B0[j] = bb[j][i].x;
+            C0[j] = bb[j][i].y;
+            B1[j] = bb[j][i].z;
+            C1[j] = bb[j][i].w;
+          }
+          step(st, m0, dd[i].x, dd[i].y, B0, C0);
+          step(st + 1, m0, dd[i].z, dd[i].w, B1, C1);
+        }
+      };
+      fetch(0, dA, bA);
+#pragma unroll
+      for (int hb = 0; hb < HB; hb += 2) {
+        fetch(hb + 1, dB, bB);
+        run(hb, dA, bA);
+        if (hb + 2 < HB) fetch(hb + 2, dA, bA);
+        run(hb + 1, dB, bB);
+      }
+    } else {
+#pragma unroll 1
+      for (int blk = 0; blk < T / 16; ++blk) {
+        const int m0 = par * T + blk * 16;  // ring position of the block
+        // This lane's 16-step window of (delta, delta*u) pairs, pair-aligned in copy p.
+        const float2* du_win = du_row + ((m0 - k + p) & MASK);
+        const float2* bc_win = bc_row + m0;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float4 dd = *reinterpret_cast<const float4*>(du_win + i);
+          float B0[NPL], C0[NPL], B1[NPL], C1[NPL];
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(bc_win + j * BC_STRIDE + i);
+            B0[j] = v.x;
+            C0[j] = v.y;
+            B1[j] = v.z;
+            C1[j] = v.w;
+          }
+          step(i, m0, dd.x, dd.y, B0, C0);
+          step(i + 1, m0, dd.z, dd.w, B1, C1);
+        }
       }
     }
   };
@@ -433,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   // ---- results that leave the workgroup ----
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const int n = k * NPL + j;
+    const int n = nbase + j;
     if (!dvalid || n >= N) continue;
     if (FULL) {
       if (a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * N + n] = h[j];
@@ -445,44 +503,47 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanArgs a) {
   }
 }
 
-template <int NPL, typename InT, bool HAS_RESET>
+template <typename TL, typename InT, bool HAS_RESET>
 hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, hipStream_t stream) {
   if (args.nseg > 1) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
-    hipLaunchKernelGGL((scan_kernel<NPL, InT, HAS_RESET, kAggregate>), dim3(nblocks_agg), dim3(kThreads), 0,
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate>), dim3(nblocks_agg), dim3(TL::THREADS), 0,
                        stream, agg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
-  hipLaunchKernelGGL((scan_kernel<NPL, InT, HAS_RESET, kFull>), dim3(nblocks_full), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull>), dim3(nblocks_full), dim3(TL::THREADS), 0, stream,
                      full);
   return hipGetLastError();
 }
 
-template <typename InT, bool HAS_RESET>
-hipError_t launch_npl(int npl, const ScanArgs& args, int nf, int na, hipStream_t stream) {
-  switch (npl) {
-    case 1: return launch_tile<1, InT, HAS_RESET>(args, nf, na, stream);
-    case 2: return launch_tile<2, InT, HAS_RESET>(args, nf, na, stream);
-    case 4: return launch_tile<4, InT, HAS_RESET>(args, nf, na, stream);
-    case 8: return launch_tile<8, InT, HAS_RESET>(args, nf, na, stream);
-    default: return launch_tile<16, InT, HAS_RESET>(args, nf, na, stream);
-  }
+// Layout by state size: (states per lane, rows per channel).
+//   N <= 16: (1, 1)   N <= 32: (1, 2)   N <= 64: (1, 4)   N <= 128: (2, 4)   N <= 256: (4, 4)
+template <typename Fn>
+hipError_t with_tile(int64_t N, Fn&& fn) {
+  if (N <= 16) return fn(Tile<1, 1>{});
+  if (N <= 32) return fn(Tile<1, 2>{});
+  if (N <= 64) return fn(Tile<1, 4>{});
+  if (N <= 128) return fn(Tile<2, 4>{});
+  return fn(Tile<4, 4>{});
 }
 
-template <typename InT>
-hipError_t launch_dtype(int npl, bool reset, const ScanArgs& args, int nf, int na, hipStream_t stream) {
-  return reset ? launch_npl<InT, true>(npl, args, nf, na, stream) : launch_npl<InT, false>(npl, args, nf, na, stream);
+int channels_per_block(int64_t N) {
+  int cpw = 0;
+  (void)with_tile(N, [&](auto tile) {
+    cpw = decltype(tile)::CPW;
+    return hipSuccess;
+  });
+  return cpw;
 }
 
 }  // namespace
 
 void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg,
                    int64_t* seg_len) {
-  (void)N;
   int64_t want;
   if (requested > 0) {
     want = requested;
@@ -490,7 +551,8 @@ void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, in
     // About four workgroups per CU (256 CUs) keeps every SIMD busy; split the
     // sequence only when the channels alone give far fewer, and keep pieces
     // long enough (>= 512 steps) that the extra aggregate pass stays small.
-    const int64_t blocks = B * ((D + kChannels - 1) / kChannels);
+    const int cpw = channels_per_block(N);
+    const int64_t blocks = B * ((D + cpw - 1) / cpw);
     want = blocks >= 512 ? 1 : (1024 + blocks - 1) / blocks;
     want = std::min<int64_t>(want, std::max<int64_t>(1, L / 512));
   }
@@ -507,8 +569,9 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg) {
          static_cast<size_t>(D) * static_cast<size_t>(N) * sizeof(float);
 }
 
-int64_t scan_grid_blocks(int64_t B, int64_t D, int nseg) {
-  return static_cast<int64_t>(nseg) * B * ((D + kChannels - 1) / kChannels);
+int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg) {
+  const int cpw = channels_per_block(N);
+  return static_cast<int64_t>(nseg) * B * ((D + cpw - 1) / cpw);
 }
 
 hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
@@ -519,7 +582,8 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.N = pl.N;
   a.seg_len = pl.seg_len;
   a.nseg = pl.nseg;
-  a.n_dgroups = static_cast<int>((pl.D + kChannels - 1) / kChannels);
+  const int cpw = channels_per_block(pl.N);
+  a.n_dgroups = static_cast<int>((pl.D + cpw - 1) / cpw);
   a.in_bf16 = pl.in_bf16;
   a.out_bf16 = pl.out_bf16;
   a.u = pl.u;
@@ -540,10 +604,13 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
   const int nf = per_piece * pl.nseg;
   const int na = per_piece * (pl.nseg - 1);
-  int npl = 1;
-  while (npl * 16 < pl.N) npl *= 2;
-  return pl.in_bf16 ? launch_dtype<bf16_t>(npl, pl.reset != nullptr, a, nf, na, stream)
-                    : launch_dtype<float>(npl, pl.reset != nullptr, a, nf, na, stream);
+  const bool reset = pl.reset != nullptr;
+  return with_tile(pl.N, [&](auto tile) {
+    using TL = decltype(tile);
+    if (pl.in_bf16)
+      return reset ? launch_tile<TL, bf16_t, true>(a, nf, na, stream) : launch_tile<TL, bf16_t, false>(a, nf, na, stream);
+    return reset ? launch_tile<TL, float, true>(a, nf, na, stream) : launch_tile<TL, float, false>(a, nf, na, stream);
+  });
 }
 
 }  // namespace ssm

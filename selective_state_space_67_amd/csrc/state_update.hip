@@ -10,12 +10,14 @@
 //   out   = y * silu(z)
 //
 // The step reads and rewrites the whole (B, D, N) float32 state, which is
-// nearly all of its HBM traffic, so it is laid out for streaming: LR
-// consecutive lanes own one (b, d) row and walk its N contiguous states,
-// each wave instruction touching 64 consecutive floats. The step-size and gate
-// (a handful of transcendentals per row) are recomputed by every lane of the
-// row, which is cheaper than broadcasting them; the dot product over n is a
-// butterfly of cross-lane adds.
+// nearly all of its HBM traffic, so the kernel is built to keep many bytes of
+// state in flight: LR consecutive lanes own one (b, d) row, each lane holding
+// four consecutive states (one 16-byte load and store), and every thread
+// handles RPT rows whose loads are all issued before any arithmetic. The
+// step size and gate (a few transcendentals per row) are recomputed by each
+// lane of the row, which is cheaper than broadcasting them; the dot product
+// over n is a butterfly of cross-lane adds. Shapes whose N is not a multiple
+// of four take a scalar variant (one state per lane per pass).
 #include "device_math.h"
 #include "kernels.h"
 
@@ -39,47 +41,158 @@ struct UpdateArgs {
   void* out;
 };
 
-__device__ __forceinline__ float load_in(const void* p, int64_t i, int bf16) {
-  return bf16 ? load_elem(static_cast<const bf16_t*>(p), i) : load_elem(static_cast<const float*>(p), i);
+template <typename InT>
+__device__ __forceinline__ float4 load4(const InT* p, int64_t i);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p, int64_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p, int64_t i) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
 }
 
 template <int LR>
-__global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs a) {
+__device__ __forceinline__ float row_sum(float y) {
+#pragma unroll
+  for (int off = LR / 2; off >= 1; off >>= 1) y += __shfl_xor(y, off, LR);
+  return y;
+}
+
+__device__ __forceinline__ void store_out(const UpdateArgs& a, int64_t row, float v) {
+  if (a.out_bf16)
+    store_elem(static_cast<bf16_t*>(a.out), row, v);
+  else
+    store_elem(static_cast<float*>(a.out), row, v);
+}
+
+// Vector variant: N % 4 == 0, LR = N / 4 lanes per row (a power of two <= 64).
+template <typename InT, int LR, int RPT>
+__global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a) {
+  constexpr int ROWS_PER_PASS = kThreads / LR;
+  const int li = threadIdx.x % LR;
+  const int64_t first = (static_cast<int64_t>(blockIdx.x) * RPT) * ROWS_PER_PASS + threadIdx.x / LR;
+  const InT* u_in = static_cast<const InT*>(a.u);
+  const InT* dt_in = static_cast<const InT*>(a.dt);
+  const InT* z_in = static_cast<const InT*>(a.z);
+  const InT* B_in = static_cast<const InT*>(a.Bm);
+  const InT* C_in = static_cast<const InT*>(a.Cm);
+  const int n0 = li * 4;
+
+  // Issue every load of this thread's rows first.
+  float4 hv[RPT], Av[RPT], Bv[RPT], Cv[RPT];
+  float uu[RPT], xx[RPT], zz[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int64_t row = first + static_cast<int64_t>(r) * ROWS_PER_PASS;
+    if (row < a.rows) {
+      const int64_t b = row / a.D, d = row - b * a.D;
+      hv[r] = *reinterpret_cast<const float4*>(a.h + row * a.N + n0);
+      Av[r] = *reinterpret_cast<const float4*>(a.A + d * a.N + n0);
+      Bv[r] = load4(B_in, b * a.N + n0);
+      Cv[r] = load4(C_in, b * a.N + n0);
+      uu[r] = load_elem(u_in, row);
+      xx[r] = load_elem(dt_in, row) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
+      zz[r] = z_in ? load_elem(z_in, row) : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int64_t row = first + static_cast<int64_t>(r) * ROWS_PER_PASS;
+    // Rows never straddle a wave (LR divides 64), so a row past the end is
+    // inactive as a whole and its lanes take no part in the cross-lane adds.
+    if (row >= a.rows) continue;
+    const int64_t d = row % a.D;
+    const float delta = softplus_f32(xx[r]);
+    const float du = delta * uu[r];
+    float4 hn;
+    hn.x = __builtin_fmaf(fast_exp2(delta * (Av[r].x * kLog2e)), hv[r].x, Bv[r].x * du);
+    hn.y = __builtin_fmaf(fast_exp2(delta * (Av[r].y * kLog2e)), hv[r].y, Bv[r].y * du);
+    hn.z = __builtin_fmaf(fast_exp2(delta * (Av[r].z * kLog2e)), hv[r].z, Bv[r].z * du);
+    hn.w = __builtin_fmaf(fast_exp2(delta * (Av[r].w * kLog2e)), hv[r].w, Bv[r].w * du);
+    *reinterpret_cast<float4*>(a.h + row * a.N + n0) = hn;
+    float y = Cv[r].x * hn.x;
+    y = __builtin_fmaf(Cv[r].y, hn.y, y);
+    y = __builtin_fmaf(Cv[r].z, hn.z, y);
+    y = __builtin_fmaf(Cv[r].w, hn.w, y);
+    y = row_sum<LR>(y);
+    if (li == 0) {
+      float o = y + (a.Dskip ? a.Dskip[d] * uu[r] : 0.0f);
+      if (z_in) o *= silu_f32(zz[r]);
+      store_out(a, row, o);
+    }
+  }
+}
+
+// Scalar variant for any N: LR lanes per row, states n = li, li + LR, ...
+template <typename InT, int LR>
+__global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs a) {
   const int li = threadIdx.x % LR;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / LR) + threadIdx.x / LR;
-  // Rows never straddle a wave (LR divides 64), so a row past the end is
-  // inactive as a whole and its lanes take no part in the cross-lane adds.
-  if (row >= a.rows) return;
+  if (row >= a.rows) return;  // whole rows only (LR divides 64)
+  const InT* B_in = static_cast<const InT*>(a.Bm);
+  const InT* C_in = static_cast<const InT*>(a.Cm);
   const int64_t b = row / a.D, d = row % a.D;
-  const float uu = load_in(a.u, row, a.in_bf16);
-  const float delta = softplus_f32(load_in(a.dt, row, a.in_bf16) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
+  const float uu = load_elem(static_cast<const InT*>(a.u), row);
+  const float delta =
+      softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
   const float du = delta * uu;
   float y = 0.0f;
   float* hrow = a.h + row * a.N;
   for (int64_t n = li; n < a.N; n += LR) {
     const float abar = fast_exp2(delta * (a.A[d * a.N + n] * kLog2e));
-    const float hn = __builtin_fmaf(abar, hrow[n], load_in(a.Bm, b * a.N + n, a.in_bf16) * du);
+    const float hn = __builtin_fmaf(abar, hrow[n], load_elem(B_in, b * a.N + n) * du);
     hrow[n] = hn;
-    y = __builtin_fmaf(load_in(a.Cm, b * a.N + n, a.in_bf16), hn, y);
+    y = __builtin_fmaf(load_elem(C_in, b * a.N + n), hn, y);
   }
-#pragma unroll
-  for (int off = LR / 2; off >= 1; off >>= 1) y += __shfl_xor(y, off, LR);
+  y = row_sum<LR>(y);
   if (li == 0) {
     float o = y + (a.Dskip ? a.Dskip[d] * uu : 0.0f);
-    if (a.z) o *= silu_f32(load_in(a.z, row, a.in_bf16));
-    if (a.out_bf16)
-      store_elem(static_cast<bf16_t*>(a.out), row, o);
-    else
-      store_elem(static_cast<float*>(a.out), row, o);
+    if (a.z) o *= silu_f32(load_elem(static_cast<const InT*>(a.z), row));
+    store_out(a, row, o);
   }
 }
 
-template <int LR>
-hipError_t launch_lr(const UpdateArgs& a, hipStream_t stream) {
+template <typename InT, int LR>
+hipError_t launch_vec(const UpdateArgs& a, hipStream_t stream) {
+  constexpr int RPT = 4;
+  const int64_t rows_per_block = static_cast<int64_t>(kThreads / LR) * RPT;
+  const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <typename InT, int LR>
+hipError_t launch_scalar(const UpdateArgs& a, hipStream_t stream) {
   const int64_t rows_per_block = kThreads / LR;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(state_update_kernel<LR>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((state_update_scalar<InT, LR>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+template <typename InT>
+hipError_t launch_dtype(const UpdateArgs& a, hipStream_t stream) {
+  // 16-byte state rows need N % 4 == 0, a power-of-two lane count N / 4 and
+  // base pointers aligned to a 4-state group.
+  const bool vec_ok = aligned_to(a.h, 16) && aligned_to(a.A, 16) && aligned_to(a.Bm, 4 * sizeof(InT)) &&
+                      aligned_to(a.Cm, 4 * sizeof(InT));
+  if (vec_ok) switch (a.N) {
+    case 16: return launch_vec<InT, 4>(a, stream);
+    case 32: return launch_vec<InT, 8>(a, stream);
+    case 64: return launch_vec<InT, 16>(a, stream);
+    case 128: return launch_vec<InT, 32>(a, stream);
+    case 256: return launch_vec<InT, 64>(a, stream);
+    default: break;
+  }
+  if (a.N <= 16) return launch_scalar<InT, 16>(a, stream);
+  if (a.N <= 32) return launch_scalar<InT, 32>(a, stream);
+  return launch_scalar<InT, 64>(a, stream);
 }
 
 }  // namespace
@@ -102,9 +215,7 @@ hipError_t launch_state_update(const UpdatePlan& pl, hipStream_t stream) {
   a.Bm = pl.Bm;
   a.Cm = pl.Cm;
   a.out = pl.out;
-  if (pl.N <= 16) return launch_lr<16>(a, stream);
-  if (pl.N <= 32) return launch_lr<32>(a, stream);
-  return launch_lr<64>(a, stream);
+  return pl.in_bf16 ? launch_dtype<bf16_t>(a, stream) : launch_dtype<float>(a, stream);
 }
 
 }  // namespace ssm

@@ -195,6 +195,27 @@ def test_decode_small(dtype, B, D, N):
     assert_close(h, rh, dtype, what="h")
 
 
+def test_decode_unaligned_state_takes_scalar_path():
+    # h offset by one float inside a larger buffer: not 16-byte aligned
+    import torch
+
+    from selective_state_space_67_amd import ssm_state_update
+
+    x = wl.make_decode_inputs(3, 10, 128, dtype=wl.BF16, seed=77)
+    dev = torch.device("cuda:0")
+    t = {k: wl.to_torch(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    big = torch.zeros(x["h"].size + 1, dtype=torch.float32, device=dev)
+    ht = big[1:].view(x["h"].shape)
+    ht.copy_(torch.from_numpy(x["h"]).to(dev))
+    out = ssm_state_update(ht, t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                           Dskip=t["Dskip"], z=t["z"])
+    torch.cuda.synchronize()
+    ro, rh = oracle_update(x, x["h"])
+    assert_close(out.cpu().numpy(), ro, wl.BF16)
+    assert_close(ht.cpu().numpy(), rh, wl.BF16, what="h")
+    assert big[0].item() == 0.0
+
+
 def test_decode_config_full_size():
     x = wl.decode_inputs()
     log("decode config %s" % (x["h"].shape,))
