@@ -245,12 +245,33 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     return call
 
 
-def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                     out_dtype=None, stream=None):
-    """Decode step: updates h (B, D, N) float32 in place and returns out (B, D)."""
+def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
+                         out_dtype=None, stream=None):
+    """Marshal the arguments of ssm_state_update once; returns a no-argument
+    callable that enqueues the same decode step again each time it is called
+    (updating h in place every time)."""
     import torch
 
     lib = load_library()
+    Bt, D, N = h.shape
+    if out is None:
+        out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out)
+    st = _stream(stream, u.device)
+    fn = lib.ssm_state_update
+    pref = ctypes.byref(p)
+
+    def call():
+        _check(fn(pref, st))
+        return out
+
+    call.keep = ((h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out), p)
+    return call
+
+
+def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out):
+    import torch
+
     Bt, D, N = h.shape
     _need(h, (Bt, D, N), "h", torch.float32)
     _need(u, (Bt, D), "u")
@@ -264,8 +285,6 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
         _need(dt_bias, (D,), "dt_bias", torch.float32)
     if Dskip is not None:
         _need(Dskip, (D,), "Dskip", torch.float32)
-    if out is None:
-        out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
     _need(out, (Bt, D), "out")
     p = UpdateParams()
     p.batch, p.dim, p.dstate = Bt, D, N
@@ -273,5 +292,18 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     p.h, p.u, p.dt_raw, p.z = _ptr(h), _ptr(u), _ptr(dt_raw), _ptr(z)
     p.dt_bias, p.A, p.Dskip = _ptr(dt_bias), _ptr(A), _ptr(Dskip)
     p.Bm, p.Cm, p.out = _ptr(Bm), _ptr(Cm), _ptr(out)
+    return p
+
+
+def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
+                     out_dtype=None, stream=None):
+    """Decode step: updates h (B, D, N) float32 in place and returns out (B, D)."""
+    import torch
+
+    lib = load_library()
+    Bt, D, N = h.shape
+    if out is None:
+        out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out)
     _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
     return out
