@@ -540,6 +540,18 @@ int channels_per_block(int64_t N) {
   return cpw;
 }
 
+// Workgroups of the full pass that are resident at once on the whole chip
+// (256 CUs x 4 SIMDs x the layout's waves per SIMD / waves per workgroup).
+int resident_blocks(int64_t N) {
+  int r = 0;
+  (void)with_tile(N, [&](auto tile) {
+    using TL = decltype(tile);
+    r = 256 * 4 * TL::MIN_WAVES_PER_SIMD / TL::WAVES;
+    return hipSuccess;
+  });
+  return r;
+}
+
 }  // namespace
 
 void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg,
@@ -548,12 +560,14 @@ void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, in
   if (requested > 0) {
     want = requested;
   } else {
-    // About four workgroups per CU (256 CUs) keeps every SIMD busy; split the
-    // sequence only when the channels alone give far fewer, and keep pieces
-    // long enough (>= 512 steps) that the extra aggregate pass stays small.
+    // Split the sequence only when the channels alone fill less than half of
+    // one resident round of workgroups (the aggregate pass costs about half a
+    // full pass over the data it covers); then aim for exactly one round, with
+    // pieces long enough (>= 512 steps) that per-piece overheads stay small.
     const int cpw = channels_per_block(N);
     const int64_t blocks = B * ((D + cpw - 1) / cpw);
-    want = blocks >= 512 ? 1 : (1024 + blocks - 1) / blocks;
+    const int64_t round = resident_blocks(N);
+    want = 2 * blocks >= round ? 1 : round / blocks;
     want = std::min<int64_t>(want, std::max<int64_t>(1, L / 512));
   }
   want = std::max<int64_t>(1, std::min<int64_t>(want, (L + 15) / 16));
