@@ -51,7 +51,10 @@
 // state from a zero start); the second launch folds the aggregates of the
 // preceding pieces into the starting state of each piece and runs the full
 // recurrence. The two-level composition is the associative combine of affine
-// maps (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2).
+// maps (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2). The aggregate launch writes
+// no output, so its lanes run in lockstep without the skew (one copy of the
+// (delta, delta*u) ring, broadcast reads), and the sum of delta that gives the
+// decay product is taken by the staging threads, once per (channel, step).
 //
 // Resets: the step's delta is stored with its sign bit set; the lane clears
 // its states before that step (a wave-uniform branch, taken only when some
@@ -119,11 +122,18 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   //  wraps. Row stride and copy offset were chosen by measurement on gfx950:
   //  with a row stride of RING + 16 float2 and copy 1 offset by 16 float2
   //  beyond copy 0's rows, the skewed 16-byte window reads of a wave are free
-  //  of bank conflicts.
-  constexpr int DU_STRIDE = RING + 16;
+  //  of bank conflicts. The lockstep aggregate pass reads one address per row;
+  //  a row stride of RING + 8 float2 (144 dwords at RING = 64) puts the four
+  //  rows of a wave in different banks.
+  constexpr int DU_STRIDE = FULL ? RING + 16 : RING + 8;
   constexpr int DU_COPY = CPW * DU_STRIDE + 16;
   //  (B, C): one row per state; windows start at multiples of 16 and never wrap.
   constexpr int BC_STRIDE = RING + 2;
+  //  The aggregate pass needs B only: one float per (state, step), row stride
+  //  RING + 4 floats, so that a 16-byte read covers four steps and the 16
+  //  rows read by a DPP row fall in different banks.
+  constexpr int B_STRIDE = RING + 4;
+  static_assert(B_STRIDE <= 2 * BC_STRIDE, "B rows fit the (B, C) area");
   // Row staging: CPW x T (channel, step) items per chunk, RI consecutive steps
   // per thread, handled by the first ROW_THREADS threads.
   constexpr int ROW_ITEMS = CPW * T;
@@ -136,6 +146,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   __shared__ __align__(16) float2 s_du[DU_COPY + CPW * DU_STRIDE];
   __shared__ __align__(16) float2 s_bc[NPAD * BC_STRIDE];
   __shared__ __align__(16) float s_y[FULL ? CPW * RPC * RING : 4];  // finished slice sums per step
+  __shared__ float s_sum[FULL ? 1 : CPW];                              // aggregate pass: sum of delta
 
   // Workgroup -> (piece, batch row, channel group). Consecutive logical tiles
   // share a batch row and therefore B and C; hardware dispatches consecutive
@@ -200,12 +211,16 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   for (int i = tid; i < DU_COPY + CPW * DU_STRIDE; i += THREADS) s_du[i] = make_float2(0.f, 0.f);
   for (int i = tid; i < NPAD * BC_STRIDE; i += THREADS) s_bc[i] = make_float2(0.f, 0.f);
 
-  const int nchunks = (Lseg + 18 + T - 1) / T;  // lane 15 finishes step L-1 by iteration L+17
-  const int p = k & 1;
+  // Full pass: lane 15 finishes step L-1 by iteration L+17. The aggregate pass
+  // needs no cross-lane sum, so its lanes run in lockstep without the skew.
+  const int nchunks = FULL ? (Lseg + 18 + T - 1) / T : (Lseg + T - 1) / T;
+  const int p = FULL ? k & 1 : 0;
 
   float yreg[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) yreg[i] = 0.0f;
+  // Aggregate pass: sum of delta over this staging thread's steps, and whether
+  // one of them resets (then the piece's decay product is 0).
   float sum_delta = 0.0f;
   bool cleared = false;
 
@@ -284,8 +299,11 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
 #pragma unroll
     for (int q = 0; q < BC_ITEMS; ++q) {
       const int n = bc_n(q);
-      s_bc[n * BC_STRIDE + ((par * T + bc_tl(q) + (n / NPL) % 16) & MASK)] =
-          make_float2(load_elem(&r.b[q], 0), FULL ? load_elem(&r.c[q], 0) : 0.0f);
+      if (FULL)
+        s_bc[n * BC_STRIDE + ((par * T + bc_tl(q) + (n / NPL) % 16) & MASK)] =
+            make_float2(load_elem(&r.b[q], 0), load_elem(&r.c[q], 0));
+      else
+        reinterpret_cast<float*>(s_bc)[n * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.b[q], 0);
     }
     if (!row_thread) return;
     float dl[RI], dv[RI];
@@ -300,9 +318,22 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         o.dsk[i] = s_dskip * uu;
         o.gate[i] = z_wg ? silu_f32(load_elem(&r.z[i], 0)) : 1.0f;
       }
+      if (!FULL) {
+        sum_delta += dl[i];
+        cleared = cleared || (HAS_RESET && r.rs[i]);
+      }
       if (HAS_RESET && r.rs[i]) dl[i] = -dl[i];  // sign bit: clear the state before this step
     }
     const int s0 = par * T + stl;                       // ring slot of this thread's first step
+    if (!FULL) {
+      // Lockstep lanes read slot tau itself: one copy, no mirror.
+      float2* du = s_du + sc * DU_STRIDE + s0;
+      if (RI == 2)
+        *reinterpret_cast<float4*>(du) = make_float4(dl[0], dv[0], dl[RI - 1], dv[RI - 1]);
+      else
+        du[0] = make_float2(dl[0], dv[0]);
+      return;
+    }
     float2* du0 = s_du + sc * DU_STRIDE;                // copy 0: step tau at slot tau
     float2* du1 = s_du + DU_COPY + sc * DU_STRIDE;      // copy 1: step tau at slot tau + 1
     if (RI == 2) {
@@ -363,7 +394,6 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
 #pragma unroll
         for (int j = 0; j < NPL; ++j) h[j] = rs ? 0.0f : h[j];
       }
-      if (!FULL) cleared = cleared || rs;
       dl = fabsf(dl);
     }
     float part = 0.0f;
@@ -380,8 +410,6 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         *reinterpret_cast<float4*>(yslot + ((m0 + i - 18) & MASK)) =
             make_float4(yreg[(i - 3) & 15], yreg[(i - 2) & 15], yreg[(i - 1) & 15], yreg[i]);
       }
-    } else {
-      sum_delta += dl;
     }
   };
 
@@ -394,7 +422,32 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   // allows it), the reads of each 8-step half block are issued while the
   // previous half block computes (two register sets, alternating statically).
   auto compute = [&](const int par) {
-    if constexpr (NPL == 1 && RPC <= 2) {
+    if constexpr (!FULL) {
+      // Lockstep: every lane is at step m. Per four steps a lane reads two
+      // (delta, delta*u) float4s (broadcast within its DPP row) and one B
+      // float4 per state (shared by the rows of a wave). Nothing is stored,
+      // so the compiler may issue the reads of the whole chunk early.
+      const float* b_row = reinterpret_cast<const float*>(s_bc) + nbase * B_STRIDE;
+#pragma unroll
+      for (int i = 0; i < T; i += 4) {
+        const int m = par * T + i;
+        const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
+        const float4 d23 = *reinterpret_cast<const float4*>(du_row + m + 2);
+        float B0[NPL], B1[NPL], B2[NPL], B3[NPL];
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const float4 v = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
+          B0[j] = v.x;
+          B1[j] = v.y;
+          B2[j] = v.z;
+          B3[j] = v.w;
+        }
+        step(i, m, d01.x, d01.y, B0, B0);  // C is not used by the aggregate pass
+        step(i + 1, m, d01.z, d01.w, B1, B1);
+        step(i + 2, m, d23.x, d23.y, B2, B2);
+        step(i + 3, m, d23.z, d23.w, B3, B3);
+      }
+    } else if constexpr (NPL == 1 && RPC <= 2) {
       constexpr int HB = T / 8;
       float4 dA[4], bA[NPL][4], dB[4], bB[NPL][4];
       auto fetch = [&](const int hb, float4 (&dd)[4], float4 (&bb)[NPL][4]) {
@@ -489,6 +542,20 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   }
 
   // ---- results that leave the workgroup ----
+  if (!FULL) {
+    // Per-channel totals from the T / RI staging threads of each channel
+    // (consecutive threads within one wave).
+    constexpr int G = T / RI;
+    int clr = cleared ? 1 : 0;
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+      sum_delta += __shfl_xor(sum_delta, off, G);
+      clr |= __shfl_xor(clr, off, G);
+    }
+    if (row_thread && stl == 0) s_sum[sc] = clr ? -1.0f : sum_delta;  // delta >= 0, so -1 marks a reset
+    __syncthreads();
+    sum_delta = s_sum[c];
+  }
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = nbase + j;
@@ -498,7 +565,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     } else {
       const int64_t wi = (static_cast<int64_t>(s) * a.B + b) * a.D * N + d * N + n;
       a.ws_H[wi] = h[j];
-      a.ws_P[wi] = cleared ? 0.0f : fast_exp2(A2[j] * sum_delta);
+      a.ws_P[wi] = sum_delta < 0.0f ? 0.0f : fast_exp2(A2[j] * sum_delta);
     }
   }
 }
