@@ -51,6 +51,8 @@ def _load():
                                             ctypes.c_int]
         lib.oracle_state_update.restype = None
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
+        lib.oracle_scan_bwd_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -143,3 +145,43 @@ def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, n
     lib.oracle_state_update(Bt, D, N, _ptr(h_new), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
                             _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(out), int(nthreads))
     return out, h_new
+
+
+def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
+             dh_last=None, nthreads=0):
+    """Gradients of sum(dout * out) + sum(dh_last * h_last) for the full scan.
+
+    u, dt_raw, z, dout: (B, D, L); A: (D, N); Bm, Cm: (B, L, N); dt_bias, Dskip: (D,);
+    reset: (B, L); h0, dh_last: (B, D, N). Returns a dict of float64 arrays:
+    du, d_dt_raw (B, D, L), dz (B, D, L) or None, dA (D, N), dD, d_dt_bias (D,),
+    dB, dC (B, L, N) and dh0 (B, D, N). dD and d_dt_bias are the gradients with
+    respect to those parameters whether or not they were given (None acts as 0).
+    """
+    lib = _load()
+    u, dt_raw, z, dout = _f64(u), _f64(dt_raw), _f64(z), _f64(dout)
+    A, Bm, Cm = _f64(A), _f64(Bm), _f64(Cm)
+    dt_bias, Dskip, h0, dh_last = _f64(dt_bias), _f64(Dskip), _f64(h0), _f64(dh_last)
+    Bt, D, L = u.shape
+    N = A.shape[1]
+    assert dt_raw.shape == (Bt, D, L) and dout.shape == (Bt, D, L) and A.shape == (D, N)
+    assert Bm.shape == (Bt, L, N) and Cm.shape == (Bt, L, N)
+    for x in (z,):
+        assert x is None or x.shape == (Bt, D, L)
+    for x in (h0, dh_last):
+        assert x is None or x.shape == (Bt, D, N)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+        assert reset.shape == (Bt, L)
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    out = dict(du=np.empty((Bt, D, L)), d_dt_raw=np.empty((Bt, D, L)),
+               dz=None if z is None else np.empty((Bt, D, L)), dA=np.empty((D, N)),
+               dD=np.empty(D), d_dt_bias=np.empty(D), dB=np.empty((Bt, L, N)),
+               dC=np.empty((Bt, L, N)), dh0=np.empty((Bt, D, N)))
+    rc = lib.oracle_scan_bwd_rows(
+        Bt * D, L, N, Bt, D, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
+        _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last),
+        _ptr(out["du"]), _ptr(out["d_dt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dD"]),
+        _ptr(out["d_dt_bias"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle backward: scratch allocation failed")
+    return out

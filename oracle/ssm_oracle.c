@@ -43,6 +43,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -160,4 +161,170 @@ int oracle_max_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/*
+ * Backward pass: gradients of the scalar
+ *
+ *   loss = sum_{b,d,t} dout[b,d,t] * out[b,d,t] + sum_{b,d,n} dh_last[b,d,n] * h_last[b,d,n]
+ *
+ * with respect to every input of the scan above. Gradient recomputation is the
+ * pages' own account of the backward ("Technical analysis: Mamba selective
+ * state spaces", section 2.2, item 3: the forward keeps no intermediate states
+ * and the backward recomputes them); no page writes the gradients out, so this
+ * is the chain rule applied to the recurrence, step by step in reverse:
+ *
+ *   forward (kept per row): delta_t, x_t = dt_raw_t + dt_bias, y_t (before the
+ *   gate) and h_t; hp_t = 0 if reset[b,t] else h_{t-1} (h_{-1} = h0)
+ *   g[n] = dh_last[n]                      (adjoint of h_{L-1})
+ *   for t = L-1 .. 0:
+ *     dy      = dout_t * silu(z_t)         (dout_t without a gate)
+ *     dz_t    = dout_t * y_t * silu'(z_t), silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *     dD     += dy * u_t;  du_t = dy * D
+ *     for n:  g[n] += dy * C_t[n]          (now the adjoint of h_t)
+ *             a = exp(delta_t A[n])
+ *             dC[b,t,n] += dy * h_t[n];    dB[b,t,n] += g[n] * delta_t * u_t
+ *             dA[d,n]   += g[n] * hp_t[n] * a * delta_t
+ *             ddelta    += g[n] * (hp_t[n] * a * A[n] + B_t[n] * u_t)
+ *             du_t      += g[n] * delta_t * B_t[n]
+ *             g[n]       = reset[b,t] ? 0 : g[n] * a   (adjoint of h_{t-1})
+ *     d dt_raw_t = ddelta * sigmoid(x_t)   (softplus' = sigmoid);  d dt_bias += the same
+ *   dh0 = g
+ *
+ * Shared gradients (dA, dD, d dt_bias, dB, dC) are summed over rows in a fixed
+ * order for a given thread count.
+ *
+ *   dout    : (R, L);  dh_last : (R, N) or NULL
+ *   du, d_dt_raw : (R, L); dz : (R, L) or NULL (required when z is given)
+ *   dA : (Dtot, N); dD, d_dt_bias : (Dtot); dB, dC : (Btot, L, N); dh0 : (R, N) or NULL
+ *   The shared outputs are overwritten (zeroed first). Rows must be distinct.
+ * Returns 0, or -1 when scratch memory could not be allocated.
+ */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t Dtot,
+                         const int64_t* row_b, const int64_t* row_d, const double* u,
+                         const double* dt_raw, const double* z, const double* dt_bias,
+                         const double* A, const double* Dskip, const double* Bm, const double* Cm,
+                         const uint8_t* reset, const double* h0, const double* dout,
+                         const double* dh_last, double* du, double* d_dt_raw, double* dz,
+                         double* dA, double* dD, double* d_dt_bias, double* dB, double* dC,
+                         double* dh0, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int T = omp_get_max_threads();
+#else
+  (void)nthreads;
+  const int T = 1;
+#endif
+  /* Per-thread accumulators for the shared gradients, summed at the end. */
+  const int64_t nA = Dtot * N, nBC = Btot * L * N;
+  const int64_t per = nA + 2 * Dtot + 2 * nBC;
+  double* acc = (double*)calloc((size_t)T * (size_t)per, sizeof(double));
+  if (!acc) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+    const int tid = omp_get_thread_num();
+#else
+    const int tid = 0;
+#endif
+    double* my = acc + (int64_t)tid * per;
+    double *mA = my, *mD = my + nA, *mbias = my + nA + Dtot, *mB = my + nA + 2 * Dtot,
+           *mC = mB + nBC;
+    /* h_t for t = -1 .. L-1 (row t+1), delta_t, x_t, y_t of the current row */
+    double* hist = (double*)malloc((size_t)(L + 1) * (size_t)N * sizeof(double));
+    double* dl = (double*)malloc((size_t)L * 3 * sizeof(double));
+    double* g = (double*)malloc((size_t)N * sizeof(double));
+    if (!hist || !dl || !g) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t b = row_b[r], d = row_d[r];
+        const double bias = dt_bias ? dt_bias[d] : 0.0;
+        const double dsk = Dskip ? Dskip[d] : 0.0;
+        const double* Ad = A + d * N;
+        double *xs = dl + L, *ys = dl + 2 * L;
+        /* forward, keeping every state */
+        for (int64_t n = 0; n < N; ++n) hist[n] = h0 ? h0[r * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+          const int64_t bt = b * L + t;
+          const double x = dt_raw[r * L + t] + bias;
+          const double delta = softplus(x);
+          const int rs = reset ? reset[bt] != 0 : 0;
+          const double uu = u[r * L + t];
+          double y = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double hp = rs ? 0.0 : hist[t * N + n];
+            const double h = exp(delta * Ad[n]) * hp + delta * Bm[bt * N + n] * uu;
+            hist[(t + 1) * N + n] = h;
+            y += Cm[bt * N + n] * h;
+          }
+          dl[t] = delta;
+          xs[t] = x;
+          ys[t] = y + dsk * uu;
+        }
+        /* reverse */
+        for (int64_t n = 0; n < N; ++n) g[n] = dh_last ? dh_last[r * N + n] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          const int64_t bt = b * L + t;
+          const double delta = dl[t], uu = u[r * L + t], go = dout[r * L + t];
+          const int rs = reset ? reset[bt] != 0 : 0;
+          double dy = go;
+          if (z) {
+            const double zz = z[r * L + t], s = sigmoid(zz);
+            dy = go * zz * s;
+            dz[r * L + t] = go * ys[t] * s * (1.0 + zz * (1.0 - s));
+          }
+          mD[d] += dy * uu;
+          double du_t = dy * dsk, ddelta = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double Bn = Bm[bt * N + n], Cn = Cm[bt * N + n];
+            const double hp = rs ? 0.0 : hist[t * N + n];
+            const double a = exp(delta * Ad[n]);
+            g[n] += dy * Cn;
+            mC[bt * N + n] += dy * hist[(t + 1) * N + n];
+            mB[bt * N + n] += g[n] * delta * uu;
+            mA[d * N + n] += g[n] * hp * a * delta;
+            ddelta += g[n] * (hp * a * Ad[n] + Bn * uu);
+            du_t += g[n] * delta * Bn;
+            g[n] = rs ? 0.0 : g[n] * a;
+          }
+          du[r * L + t] = du_t;
+          const double dx = ddelta * sigmoid(xs[t]);
+          d_dt_raw[r * L + t] = dx;
+          mbias[d] += dx;
+        }
+        if (dh0)
+          for (int64_t n = 0; n < N; ++n) dh0[r * N + n] = g[n];
+      }
+    }
+    free(hist);
+    free(dl);
+    free(g);
+  }
+  if (failed) {
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < nA; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < Dtot; ++i) dD[i] = d_dt_bias[i] = 0.0;
+  for (int64_t i = 0; i < nBC; ++i) dB[i] = dC[i] = 0.0;
+  for (int t = 0; t < T; ++t) {
+    const double* my = acc + (int64_t)t * per;
+    for (int64_t i = 0; i < nA; ++i) dA[i] += my[i];
+    for (int64_t i = 0; i < Dtot; ++i) {
+      dD[i] += my[nA + i];
+      d_dt_bias[i] += my[nA + Dtot + i];
+    }
+    for (int64_t i = 0; i < nBC; ++i) {
+      dB[i] += my[nA + 2 * Dtot + i];
+      dC[i] += my[nA + 2 * Dtot + nBC + i];
+    }
+  }
+  free(acc);
+  return 0;
 }
