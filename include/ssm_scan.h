@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10100 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -67,7 +67,8 @@ typedef enum {
   SSM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size    */
   SSM_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement   */
   SSM_ERR_WORKSPACE = 6,    /* workspace smaller than ssm_scan_workspace_size() */
-  SSM_ERR_ALIAS = 7,        /* out (or h_last) overlaps an input tensor         */
+  SSM_ERR_ALIAS = 7,        /* an output overlaps an input, another output or
+                               the workspace                                   */
   SSM_ERR_HIP = 8           /* the HIP runtime refused a call; see ssm_last_error */
 } ssm_status;
 
@@ -158,6 +159,80 @@ typedef struct {
 /* Enqueue the decode step described by `p` on `hip_stream`. */
 ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
 
+/*
+ * Backward pass of the full-sequence scan: the gradients of
+ *
+ *   loss = sum_{b,d,t} dout[b,d,t] * out[b,d,t] + sum_{b,d,n} dh_last[b,d,n] * h_last[b,d,n]
+ *
+ * with respect to every input of ssm_scan_fwd, for the same inputs. The
+ * forward keeps no intermediate states; the backward recomputes them
+ * ("Technical analysis: Mamba selective state spaces", section 2.2, item 3:
+ * gradient recomputation). The gradients are the chain rule through the
+ * recurrence above, run in reverse time:
+ *
+ *   g_t     = adjoint of h_t = a_{t+1} g_{t+1} + dy_t C_t,  dy_t = dout_t silu(z_t)
+ *   dB[b,t,n] = sum_d g_t[n] delta_t u_t          dC[b,t,n] = sum_d dy_t h_t[n]
+ *   dA[d,n]   = sum_{b,t} g_t[n] a_t[n] h_{t-1}[n] delta_t
+ *   du_t      = dy_t D + delta_t sum_n g_t[n] B_t[n]
+ *   d dt_raw_t = (sum_n g_t[n] (A[n] a_t[n] h_{t-1}[n] + B_t[n] u_t)) sigmoid(dt_raw_t + dt_bias)
+ *   dz_t      = dout_t y_t silu'(z_t);  dD = sum dy u;  d dt_bias = sum d dt_raw
+ *   dh0       = a_0 g_0
+ *
+ * with a_t = exp(delta_t A) (0 where reset[b,t] clears the state) and h_{-1} = h0.
+ *
+ *   batch .. h0 : as in ssm_scan_params (the forward's inputs, unchanged)
+ *   in_dtype   : element type of u, dt_raw, z, Bm, Cm and dout
+ *   grad_dtype : element type of du, d_dt_raw and dz (SSM_F32 or SSM_BF16)
+ *   dout     (B,D,L)  required; gradient of the loss with respect to out
+ *   dh_last  (B,D,N)  float32, NULL => 0
+ *   du, d_dt_raw (B,D,L) required outputs
+ *   dz       (B,D,L)  required when z is given, must be NULL otherwise
+ *   dA       (D,N)    float32, required output
+ *   dBm, dCm (B,L,N)  float32, required outputs
+ *   dDskip, d_dt_bias (D) float32 outputs, NULL => not written. They are the
+ *                     gradients with respect to D and dt_bias whether or not
+ *                     those inputs are given (an absent input acts as 0).
+ *   dh0      (B,D,N)  float32 output, NULL => not written
+ *   workspace, workspace_bytes : at least ssm_scan_bwd_workspace_size() bytes
+ *                     (never 0 for the backward); contents on entry ignored.
+ * Outputs must not overlap each other, the inputs or the workspace. Shared
+ * gradients (dA, dBm, dCm, dDskip, d_dt_bias) are sums in a fixed order, so
+ * repeated calls give identical bits.
+ */
+typedef struct {
+  int64_t batch, dim, seqlen, dstate;
+  int32_t in_dtype, grad_dtype;
+  const void* u;
+  const void* dt_raw;
+  const float* dt_bias;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const uint8_t* reset;
+  const float* h0;
+  const void* dout;
+  const float* dh_last;
+  void* du;
+  void* d_dt_raw;
+  void* dz;
+  float* dA;
+  float* dBm;
+  float* dCm;
+  float* dDskip;
+  float* d_dt_bias;
+  float* dh0;
+  void* workspace;
+  size_t workspace_bytes;
+} ssm_scan_bwd_params;
+
+/* Bytes of workspace ssm_scan_bwd needs (only sizes and dtypes of `p` are read). */
+ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params* p, size_t* bytes);
+
+/* Enqueue the backward pass described by `p` on `hip_stream`. */
+ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ssm_status_string(int32_t status);
 
@@ -169,7 +244,8 @@ const char* ssm_last_error(void);
 int32_t ssm_version(void);
 
 /* sizeof of the parameter structs as compiled into the library:
- * which = 0 -> ssm_scan_params, 1 -> ssm_update_params; 0 for anything else.
+ * which = 0 -> ssm_scan_params, 1 -> ssm_update_params,
+ * 2 -> ssm_scan_bwd_params; 0 for anything else.
  * Bindings compare these with their own layouts at load time. */
 size_t ssm_abi_struct_size(int32_t which);
 

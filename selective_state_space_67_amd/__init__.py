@@ -1,7 +1,8 @@
-"""MI355X-native selective-scan forward (Mamba SSM) behind a C-ABI HIP library.
+"""MI355X-native selective scan (Mamba SSM) behind a C-ABI HIP library.
 
 The public entry points mirror the C functions of ``include/ssm_scan.h``:
-``ssm_scan_fwd``, ``ssm_scan_workspace_size`` and ``ssm_state_update``. They
+``ssm_scan_fwd``, ``ssm_scan_workspace_size``, ``ssm_state_update`` and the
+backward pass ``ssm_scan_bwd``. They
 take torch tensors only as carriers of device pointers and the current stream;
 every step of the computation runs in the HIP kernels of ``libssmscan.so``.
 The library is loaded on first use and a missing build raises at that point.
@@ -10,6 +11,7 @@ from .binding import (  # noqa: F401
     SsmError,
     library_path,
     load_library,
+    ssm_scan_bwd,
     ssm_scan_fwd,
     ssm_scan_workspace_size,
     ssm_state_update,

@@ -54,8 +54,23 @@ class UpdateParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_status_string",
-           "ssm_last_error", "ssm_version", "ssm_abi_struct_size")
+class BwdParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+        ("u", ctypes.c_void_p), ("dt_raw", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("A", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
+        ("Dskip", ctypes.c_void_p), ("z", ctypes.c_void_p), ("reset", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("dh_last", ctypes.c_void_p),
+        ("du", ctypes.c_void_p), ("d_dt_raw", ctypes.c_void_p), ("dz", ctypes.c_void_p),
+        ("dA", ctypes.c_void_p), ("dBm", ctypes.c_void_p), ("dCm", ctypes.c_void_p),
+        ("dDskip", ctypes.c_void_p), ("d_dt_bias", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_scan_bwd_workspace_size",
+           "ssm_scan_bwd", "ssm_status_string", "ssm_last_error", "ssm_version", "ssm_abi_struct_size")
 
 _lib = None
 
@@ -80,6 +95,10 @@ def load_library():
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [ctypes.POINTER(UpdateParams), vp]
     lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_int
+    lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(BwdParams), vp]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_last_error.argtypes = []
@@ -89,7 +108,8 @@ def load_library():
     lib.ssm_abi_struct_size.argtypes = [ctypes.c_int32]
     lib.ssm_abi_struct_size.restype = ctypes.c_size_t
     if lib.ssm_abi_struct_size(0) != ctypes.sizeof(ScanParams) or \
-            lib.ssm_abi_struct_size(1) != ctypes.sizeof(UpdateParams):
+            lib.ssm_abi_struct_size(1) != ctypes.sizeof(UpdateParams) or \
+            lib.ssm_abi_struct_size(2) != ctypes.sizeof(BwdParams):
         raise ImportError("libssmscan.so struct layout does not match this binding")
     _lib = lib
     return lib
@@ -307,3 +327,101 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out)
     _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
     return out
+
+
+def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads):
+    import torch
+
+    Bt, D, L = u.shape
+    N = A.shape[1]
+    _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, None, None, None, 0)  # input checks
+    _need(dout, (Bt, D, L), "dout", u.dtype)
+    if dh_last is not None:
+        _need(dh_last, (Bt, D, N), "dh_last", torch.float32)
+    shapes = dict(du=(Bt, D, L), d_dt_raw=(Bt, D, L), dz=(Bt, D, L), dA=(D, N), dBm=(Bt, L, N), dCm=(Bt, L, N),
+                  dDskip=(D,), d_dt_bias=(D,), dh0=(Bt, D, N))
+    for k, t in grads.items():
+        if t is not None:
+            _need(t, shapes[k], k)
+    p = BwdParams()
+    p.batch, p.dim, p.seqlen, p.dstate = Bt, D, L, N
+    p.in_dtype = _dtype_code(u)
+    p.grad_dtype = _dtype_code(grads["du"])
+    p.u, p.dt_raw, p.dt_bias, p.A = _ptr(u), _ptr(dt_raw), _ptr(dt_bias), _ptr(A)
+    p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
+    p.reset, p.h0, p.dout, p.dh_last = _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last)
+    for k, t in grads.items():
+        setattr(p, k, _ptr(t))
+    return p
+
+
+def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0):
+    import torch
+
+    Bt, D, L = u.shape
+    N = A.shape[1]
+    dev = u.device
+    gd = grad_dtype or torch.float32
+    f32 = torch.float32
+    return dict(du=torch.empty((Bt, D, L), dtype=gd, device=dev),
+                d_dt_raw=torch.empty((Bt, D, L), dtype=gd, device=dev),
+                dz=torch.empty((Bt, D, L), dtype=gd, device=dev) if z is not None else None,
+                dA=torch.empty((D, N), dtype=f32, device=dev),
+                dBm=torch.empty((Bt, L, N), dtype=f32, device=dev),
+                dCm=torch.empty((Bt, L, N), dtype=f32, device=dev),
+                dDskip=torch.empty((D,), dtype=f32, device=dev) if want_dD else None,
+                d_dt_bias=torch.empty((D,), dtype=f32, device=dev) if want_dbias else None,
+                dh0=torch.empty((Bt, D, N), dtype=f32, device=dev) if want_dh0 else None)
+
+
+def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
+                 dh_last=None, grad_dtype=None, want_dDskip=True, want_d_dt_bias=True, want_dh0=True,
+                 workspace=None, stream=None):
+    """Backward pass of ssm_scan_fwd for the same inputs and the output gradient dout.
+
+    Returns a dict with du, d_dt_raw, dz (None without z) in ``grad_dtype``
+    (float32 by default), and float32 dA, dBm, dCm, dDskip, d_dt_bias, dh0
+    (the last three None when not asked for). dh_last (B, D, N) float32 is the
+    gradient reaching h_last (None = 0). The workspace is allocated when not
+    given or too small.
+    """
+    import torch
+
+    lib = load_library()
+    grads = _bwd_grads(u, A, Bm, z, grad_dtype, want_dDskip, want_d_dt_bias, want_dh0)
+    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    if workspace is None or workspace.numel() * workspace.element_size() < n.value:
+        workspace = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssm_scan_bwd(ctypes.byref(p), _stream(stream, u.device)))
+    return grads
+
+
+def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
+                     dh_last=None, grad_dtype=None, stream=None):
+    """Marshal the arguments of ssm_scan_bwd once; returns a no-argument callable
+    that enqueues the same backward pass again each time it is called and
+    returns the gradient dict (the same tensors every time)."""
+    import torch
+
+    lib = load_library()
+    grads = _bwd_grads(u, A, Bm, z, grad_dtype, True, True, True)
+    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
+    p.workspace = _ptr(ws)
+    p.workspace_bytes = int(n.value)
+    st = _stream(stream, u.device)
+    fn = lib.ssm_scan_bwd
+    pref = ctypes.byref(p)
+
+    def call():
+        _check(fn(pref, st))
+        return grads
+
+    call.keep = ((u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, ws), p)
+    return call

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.cpp", "scan_fwd.hip", "state_update.hip"]
+SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bwd.hip", "state_update.hip"]
 OUT = os.path.join(HERE, "libssmscan.so")
 ARCH = "gfx950"
 

@@ -3,8 +3,8 @@
 // Every check here is plain host arithmetic on the parameter struct; nothing
 // touches the HIP runtime until all checks have passed, so invalid calls
 // return their status with no device-side effect (and can be exercised on a
-// machine without a GPU). The launches themselves live in scan_fwd.hip and
-// state_update.hip.
+// machine without a GPU). The launches themselves live in scan_fwd.hip,
+// scan_bwd.hip and state_update.hip.
 #include "ssm_scan.h"
 
 #include <hip/hip_runtime.h>
@@ -95,9 +95,211 @@ ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size
   return SSM_OK;
 }
 
+// Workspace layout of the backward pass (byte offsets, each 256-aligned).
+struct BwdLayout {
+  int nseg;           // pieces of the checkpoint sweep (forward split)
+  int64_t seg_len;
+  int nsegb;          // segments of the reverse sweep
+  int64_t seg_steps;
+  int64_t n_ck;       // 16-step checkpoints
+  size_t off_agg, off_ckpt, off_segP, off_segG, off_part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+ssm_status check_bwd_sizes(const ssm_scan_bwd_params* p, ScanSizes* sz) {
+  ssm_scan_params f{};
+  f.batch = p->batch;
+  f.dim = p->dim;
+  f.seqlen = p->seqlen;
+  f.dstate = p->dstate;
+  return check_scan_sizes(&f, sz);
+}
+
+ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout* lay) {
+  const int64_t B = p->batch, D = p->dim, L = p->seqlen, N = p->dstate;
+  ssm::plan_bwd_segments(B, D, L, N, &lay->nsegb, &lay->seg_steps);
+  int nseg;
+  int64_t seg_len;
+  ssm::plan_segments(B, D, L, N, 0, &nseg, &seg_len);
+  seg_len = (seg_len + lay->seg_steps - 1) / lay->seg_steps * lay->seg_steps;
+  lay->seg_len = seg_len;
+  lay->nseg = static_cast<int>((L + seg_len - 1) / seg_len);
+  lay->n_ck = (L + 15) / 16;
+  if (ssm::scan_grid_blocks(B, D, N, lay->nseg) > std::numeric_limits<int32_t>::max() ||
+      ssm::bwd_grid_blocks(B, D, N, lay->nsegb) > std::numeric_limits<int32_t>::max())
+    return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  int64_t ck, seg, part;
+  const int64_t groups = (D + ssm::bwd_channels_per_block(N) - 1) / ssm::bwd_channels_per_block(N);
+  if (!mul_ok(sz.bdn, lay->n_ck, &ck) || !mul_ok(sz.bdn, lay->nsegb, &seg) || !mul_ok(sz.bln, 2 * groups, &part) ||
+      ck > (int64_t{1} << 58) || seg > (int64_t{1} << 58) || part > (int64_t{1} << 58))
+    return fail(SSM_ERR_BAD_SHAPE, "backward workspace size overflows");
+  size_t off = 0;
+  lay->off_agg = off;
+  off += align256(ssm::scan_workspace_bytes(B, D, N, lay->nseg));
+  lay->off_ckpt = off;
+  off += align256(static_cast<size_t>(ck) * 4);
+  lay->off_segP = off;
+  off += align256(static_cast<size_t>(seg) * 4);
+  lay->off_segG = off;
+  off += align256(static_cast<size_t>(seg) * 4);
+  lay->off_part = off;
+  off += align256(ssm::bwd_partial_floats(B, D, L, N, lay->nsegb) * 4);
+  lay->total = off;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params* p, size_t* bytes) {
+  if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");
+  ScanSizes sz;
+  ssm_status s = check_bwd_sizes(p, &sz);
+  if (s != SSM_OK) return s;
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->grad_dtype))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
+  BwdLayout lay;
+  if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
+  *bytes = lay.total;
+  return ok();
+}
+
+ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
+  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
+  ScanSizes sz;
+  ssm_status s = check_bwd_sizes(p, &sz);
+  if (s != SSM_OK) return s;
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->grad_dtype))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
+  const struct {
+    const void* ptr;
+    const char* name;
+  } required[] = {{p->u, "u"},     {p->dt_raw, "dt_raw"},     {p->A, "A"},        {p->Bm, "Bm"},
+                  {p->Cm, "Cm"},   {p->dout, "dout"},         {p->du, "du"},      {p->d_dt_raw, "d_dt_raw"},
+                  {p->dA, "dA"},   {p->dBm, "dBm"},           {p->dCm, "dCm"},    {p->workspace, "workspace"}};
+  for (const auto& r : required)
+    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+  if (p->z && !p->dz) return fail(SSM_ERR_NULL_POINTER, "dz is NULL although z is given");
+  if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
+
+  const size_t si = dtype_size(p->in_dtype), sg = dtype_size(p->grad_dtype);
+  const struct {
+    const void* ptr;
+    size_t align;
+    const char* name;
+  } aligns[] = {{p->u, si, "u"},           {p->dt_raw, si, "dt_raw"},   {p->z, si, "z"},
+                {p->Bm, si, "Bm"},         {p->Cm, si, "Cm"},           {p->dout, si, "dout"},
+                {p->A, 4, "A"},            {p->dt_bias, 4, "dt_bias"},  {p->Dskip, 4, "Dskip"},
+                {p->h0, 4, "h0"},          {p->dh_last, 4, "dh_last"},  {p->du, sg, "du"},
+                {p->d_dt_raw, sg, "d_dt_raw"}, {p->dz, sg, "dz"},       {p->dA, 4, "dA"},
+                {p->dBm, 4, "dBm"},        {p->dCm, 4, "dCm"},          {p->dDskip, 4, "dDskip"},
+                {p->d_dt_bias, 4, "d_dt_bias"}, {p->dh0, 4, "dh0"},     {p->workspace, 16, "workspace"}};
+  for (const auto& a : aligns)
+    if (a.ptr && !aligned(a.ptr, a.align))
+      return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
+
+  BwdLayout lay;
+  if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
+  if (p->workspace_bytes < lay.total)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, p->workspace_bytes);
+
+  const Range inputs[] = {
+      range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
+      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln, si, "Bm"),
+      range(p->Cm, sz.bln, si, "Cm"),        range(p->A, sz.dn, 4, "A"),
+      range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
+      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
+      range(p->dout, sz.bdl, si, "dout"),    range(p->dh_last, sz.bdn, 4, "dh_last"),
+  };
+  const Range outputs[] = {
+      range(p->du, sz.bdl, sg, "du"),        range(p->d_dt_raw, sz.bdl, sg, "d_dt_raw"),
+      range(p->dz, sz.bdl, sg, "dz"),        range(p->dA, sz.dn, 4, "dA"),
+      range(p->dBm, sz.bln, 4, "dBm"),       range(p->dCm, sz.bln, 4, "dCm"),
+      range(p->dDskip, p->dim, 4, "dDskip"), range(p->d_dt_bias, p->dim, 4, "d_dt_bias"),
+      range(p->dh0, sz.bdn, 4, "dh0"),
+      Range{static_cast<const char*>(p->workspace), lay.total, "workspace"},
+  };
+  constexpr int n_out = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& r : inputs)
+      if (overlaps(outputs[i], r)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outputs[i].name, r.name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outputs[i], outputs[j]))
+        return fail(SSM_ERR_ALIAS, "%s overlaps %s", outputs[i].name, outputs[j].name);
+  }
+
+  char* ws = static_cast<char*>(p->workspace);
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  ssm::ScanPlan sp{};
+  sp.B = p->batch;
+  sp.D = p->dim;
+  sp.L = p->seqlen;
+  sp.N = p->dstate;
+  sp.in_bf16 = p->in_dtype == SSM_BF16;
+  sp.u = p->u;
+  sp.dt = p->dt_raw;
+  sp.z = p->z;
+  sp.Bm = p->Bm;
+  sp.Cm = p->Cm;
+  sp.dt_bias = p->dt_bias;
+  sp.A = p->A;
+  sp.Dskip = p->Dskip;
+  sp.h0 = p->h0;
+  sp.reset = p->reset;
+  sp.ws = lay.nseg > 1 ? reinterpret_cast<float*>(ws + lay.off_agg) : nullptr;
+  sp.nseg = lay.nseg;
+  sp.seg_len = lay.seg_len;
+  sp.checkpoint = 1;
+  sp.dout = p->dout;
+  sp.ckpt = reinterpret_cast<float*>(ws + lay.off_ckpt);
+  sp.seg_P = reinterpret_cast<float*>(ws + lay.off_segP);
+  sp.seg_G = reinterpret_cast<float*>(ws + lay.off_segG);
+  sp.seg_steps = lay.seg_steps;
+  sp.n_ck = lay.n_ck;
+  sp.nsegb = lay.nsegb;
+  hipError_t e = ssm::launch_scan(sp, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint sweep launch failed: %s", hipGetErrorString(e));
+
+  ssm::BwdPlan bp{};
+  bp.B = p->batch;
+  bp.D = p->dim;
+  bp.L = p->seqlen;
+  bp.N = p->dstate;
+  bp.in_bf16 = p->in_dtype == SSM_BF16;
+  bp.grad_bf16 = p->grad_dtype == SSM_BF16;
+  bp.u = p->u;
+  bp.dt = p->dt_raw;
+  bp.z = p->z;
+  bp.Bm = p->Bm;
+  bp.Cm = p->Cm;
+  bp.dout = p->dout;
+  bp.dt_bias = p->dt_bias;
+  bp.A = p->A;
+  bp.Dskip = p->Dskip;
+  bp.reset = p->reset;
+  bp.dh_last = p->dh_last;
+  bp.ckpt = sp.ckpt;
+  bp.seg_P = sp.seg_P;
+  bp.seg_G = sp.seg_G;
+  bp.du = p->du;
+  bp.ddt = p->d_dt_raw;
+  bp.dz = p->dz;
+  bp.dA = p->dA;
+  bp.dB = p->dBm;
+  bp.dC = p->dCm;
+  bp.dD = p->dDskip;
+  bp.dbias = p->d_dt_bias;
+  bp.dh0 = p->dh0;
+  bp.part = reinterpret_cast<float*>(ws + lay.off_part);
+  bp.seg_steps = lay.seg_steps;
+  bp.n_ck = lay.n_ck;
+  bp.nsegb = lay.nsegb;
+  e = ssm::launch_scan_bwd(bp, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "reverse sweep launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");
@@ -287,6 +489,7 @@ int32_t ssm_version(void) { return SSM_SCAN_VERSION; }
 size_t ssm_abi_struct_size(int32_t which) {
   if (which == 0) return sizeof(ssm_scan_params);
   if (which == 1) return sizeof(ssm_update_params);
+  if (which == 2) return sizeof(ssm_scan_bwd_params);
   return 0;
 }
 

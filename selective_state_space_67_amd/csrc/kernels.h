@@ -28,6 +28,18 @@ struct ScanPlan {
   float* ws;
   int nseg;         // pieces L is split into (1 = no split)
   int64_t seg_len;  // steps per piece (the last may be shorter)
+  // Backward forward-sweep (checkpoint != 0): instead of `out`, write the state
+  // entering every 16-step chunk to ckpt (B, n_ck, D, N) and each backward
+  // segment's adjoint aggregate to seg_P / seg_G (B, nsegb, D, N). seg_len is
+  // then a multiple of seg_steps.
+  int checkpoint;
+  const void* dout;
+  float* ckpt;
+  float* seg_P;
+  float* seg_G;
+  int64_t seg_steps;
+  int64_t n_ck;
+  int nsegb;
 };
 
 struct UpdatePlan {
@@ -62,5 +74,51 @@ int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg);
 
 hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
 hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);
+
+// Backward pass (scan_bwd.hip). The checkpoint sweep runs through launch_scan
+// with ScanPlan::checkpoint set; BwdPlan describes the reverse sweep and the
+// final reduction.
+struct BwdPlan {
+  int64_t B, D, L, N;
+  int in_bf16, grad_bf16;
+  const void* u;
+  const void* dt;
+  const void* z;
+  const void* Bm;
+  const void* Cm;
+  const void* dout;
+  const float* dt_bias;
+  const float* A;
+  const float* Dskip;
+  const uint8_t* reset;
+  const float* dh_last;
+  const float* ckpt;   // from the checkpoint sweep
+  const float* seg_P;
+  const float* seg_G;
+  void* du;
+  void* ddt;
+  void* dz;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* dbias;
+  float* dh0;
+  float* part;  // partial sums, bwd_partial_floats() floats
+  int64_t seg_steps;
+  int64_t n_ck;
+  int nsegb;
+};
+
+// Backward segments: how many pieces the reverse sweep splits L into and
+// their length (a multiple of 16). Pure host arithmetic.
+void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps);
+// Channels one reverse-sweep workgroup covers.
+int bwd_channels_per_block(int64_t N);
+// Floats of partial sums the reverse sweep writes and the reduction reads.
+size_t bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb);
+// Workgroups of the reverse sweep.
+int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb);
+hipError_t launch_scan_bwd(const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace ssm

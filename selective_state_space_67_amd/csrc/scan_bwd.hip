@@ -1,0 +1,597 @@
+// Backward pass of the selective scan for gfx950 (MI355X): the reverse sweep
+// and the final reduction.
+//
+// The forward keeps no intermediate states and the backward recomputes them
+// ("Technical analysis: Mamba selective state spaces", section 2.2, item 3,
+// gradient recomputation). The gradients are the chain rule through the
+// recurrence of the forward kernel (softplus step, h_t = a_t h_{t-1} +
+// delta_t B_t u_t with a_t = exp(delta_t A), y_t = C_t h_t + D u_t, SiLU gate),
+// run in reverse time with the adjoint g_t of h_t:
+//
+//   g_t  = a_{t+1} g_{t+1} + dy_t C_t,   dy_t = dout_t silu(z_t)
+//   dB[t,n] += g_t[n] delta_t u_t          dC[t,n] += dy_t h_t[n]
+//   dA[n]   += g_t[n] a_t[n] h_{t-1}[n] delta_t
+//   du_t     = dy_t D + delta_t S1_t,      S1_t = sum_n g_t[n] B_t[n]
+//   d dt_t   = (S2_t + u_t S1_t) sigmoid(x_t),  S2_t = sum_n A[n] g_t[n] a_t[n] h_{t-1}[n]
+//   dz_t     = dout_t (Y_t + D u_t) silu'(z_t),  Y_t = sum_n C_t[n] h_t[n]
+//
+// Three launches make up the pass:
+//  1. the checkpoint sweep (scan_fwd.hip, kCheckpoint): the forward recurrence
+//     in lockstep, writing the state entering every 16-step chunk, and for
+//     every backward segment the product of its a_t and its adjoint from a
+//     zero start (accumulated in forward order as sum (prod a) dy C);
+//  2. the reverse sweep (this file): one workgroup per (batch row, channel
+//     group, segment). It folds the later segments' aggregates into the
+//     adjoint entering its segment, then walks the segment's 16-step chunks
+//     backwards: recompute the chunk's states from its checkpoint (kept in
+//     registers), then run the adjoint through the chunk;
+//  3. the reduction (this file): the shared gradients summed over channel
+//     groups (dB, dC) and over batch rows and segments (dA, dD, d dt_bias).
+//
+// Layout of the reverse sweep. Each lane holds four consecutive states of one
+// channel; a channel spans LPC lanes (LPC = N/4 rounded up to a power of two,
+// at least 4). The sums over n (S1, S2, Y) are butterflies of DPP adds over
+// those LPC lanes (two for N <= 16), so four states share every cross-lane
+// operation. Lanes step in lockstep. After each step the lane whose index
+// matches the step (mod 4) keeps the three sums; every four steps those lanes
+// compute du, d dt_raw and dz for four steps at once. The sums over channels
+// (dB, dC) go through a per-wave LDS buffer (a wave adds up its channels for
+// two steps at a time into its own totals); the waves' totals are added in a
+// fixed order and written as one partial per channel group, so every sum has
+// a fixed order and repeated calls give identical bits.
+#include <algorithm>
+
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kK = 16;                 // steps per chunk (the checkpoint spacing)
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNPL = 4;                // states per lane
+
+template <int LPC_>
+struct BwdTile {
+  static constexpr int LPC = LPC_;               // lanes per channel
+  static constexpr int NPADC = LPC * kNPL;       // states covered per channel
+  static constexpr int CPWAVE = 64 / LPC;        // channels per wave
+  static constexpr int CPW = kWaves * CPWAVE;    // channels per workgroup
+  // Per-wave buffer for the channel sums: [type][channel][step parity][state],
+  // padded so that the 16-byte writes and the 4-byte reads spread over banks.
+  static constexpr int QS = 2 * NPADC + 4;
+  static constexpr int TS = CPWAVE * QS + 32;
+  // Steps per flush of the dB / dC totals: each wave keeps its own totals
+  // (2 x FP x NPADC floats) and the flush adds the waves in a fixed order, so
+  // the result does not depend on timing. FP x NPADC <= 1024 bounds the LDS.
+  static constexpr int FP = NPADC <= 64 ? 16 : 1024 / NPADC;
+};
+
+struct BwdArgs {
+  int64_t B, D, L, N, seg_steps, n_ck;
+  int nsegb, n_dgroups, nblocks, grad_bf16;
+  const void* u;
+  const void* dt;
+  const void* z;
+  const void* Bm;
+  const void* Cm;
+  const void* dout;
+  const float* dt_bias;
+  const float* A;
+  const float* Dskip;
+  const uint8_t* reset;
+  const float* dh_last;
+  const float* ckpt;
+  const float* seg_P;
+  const float* seg_G;
+  void* du;
+  void* ddt;
+  void* dz;
+  float* dh0;
+  float* partB;     // (G, B, L, N)
+  float* partC;     // (G, B, L, N)
+  float* partA;     // (B, nsegb, D, N)
+  float* partD;     // (B, nsegb, D)
+  float* partBias;  // (B, nsegb, D)
+};
+
+// DPP lane permutation within rows of 16 (control word CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPC lanes of a channel; every lane of the group gets the total.
+template <int LPC>
+__device__ __forceinline__ float chan_sum(float v) {
+  if constexpr (LPC >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (LPC >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LPC >= 8) v += dpp_f<0x141>(v);   // row_half_mirror: the other quad of each 8
+  if constexpr (LPC >= 16) v += dpp_f<0x140>(v);  // row_mirror: the other 8 of each row
+  if constexpr (LPC >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPC >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ void store_grad(const BwdArgs& a, void* p, int64_t i, float v) {
+  if (a.grad_bf16)
+    store_elem(static_cast<bf16_t*>(p), i, v);
+  else
+    store_elem(static_cast<float*>(p), i, v);
+}
+
+template <typename TL, typename InT, bool HAS_RESET>
+__global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) {
+  constexpr int LPC = TL::LPC, NPADC = TL::NPADC, CPWAVE = TL::CPWAVE, CPW = TL::CPW;
+  constexpr int QS = TL::QS, TS = TL::TS, FP = TL::FP;
+  static_assert(kK % FP == 0 && FP % 2 == 0, "flush period");
+  constexpr int BCI = kK * NPADC / kThreads;  // (step, state) staging items per thread
+  static_assert(BCI >= 1 && (kK * NPADC) % kThreads == 0, "B/C staging split");
+
+  __shared__ __align__(16) float4 s_rec[CPW * kK];  // (delta, delta*u, dy, 0); delta negated on a reset
+  __shared__ __align__(16) float s_B[kK * NPADC];
+  __shared__ __align__(16) float s_C[kK * NPADC];
+  __shared__ __align__(16) float s_w[kWaves * 2 * TS];
+  __shared__ float s_acc[kWaves * 2 * FP * NPADC];  // per-wave totals of the dB and dC terms
+
+  int idx = blockIdx.x;
+  if ((a.nblocks & 7) == 0) idx = (idx & 7) * (a.nblocks >> 3) + (idx >> 3);
+  const int g = idx % a.n_dgroups;
+  const int rest = idx / a.n_dgroups;
+  const int b = rest % static_cast<int>(a.B);
+  const int s = rest / static_cast<int>(a.B);
+  const int64_t t_seg = static_cast<int64_t>(s) * a.seg_steps;
+  const int64_t pend = min(t_seg + a.seg_steps, a.L);
+  const int nchunks = static_cast<int>((pend - t_seg + kK - 1) / kK);
+  const int N = static_cast<int>(a.N);
+  const int64_t d0 = static_cast<int64_t>(g) * CPW;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int cw = lane / LPC;       // channel within the wave
+  const int c = w * CPWAVE + cw;   // channel within the workgroup
+  const int l = lane % LPC;        // lane within the channel
+  const int64_t d = d0 + c;
+  const bool dvalid = d < a.D;
+  const int n0 = l * kNPL;
+  const bool fin = l < 4;          // finalize / staging lane: owns steps l, l+4, l+8, l+12 of a chunk
+
+  const InT* __restrict__ u_in = static_cast<const InT*>(a.u);
+  const InT* __restrict__ dt_in = static_cast<const InT*>(a.dt);
+  const InT* __restrict__ z_in = static_cast<const InT*>(a.z);
+  const InT* __restrict__ go_in = static_cast<const InT*>(a.dout);
+  const InT* __restrict__ B_in = static_cast<const InT*>(a.Bm);
+  const InT* __restrict__ C_in = static_cast<const InT*>(a.Cm);
+  const int64_t rowbase = (static_cast<int64_t>(b) * a.D + (dvalid ? d : 0)) * a.L;
+  const int64_t bdn = (static_cast<int64_t>(b) * a.D + d) * N;
+
+  // Per-lane parameters, gradient accumulators and the adjoint entering this
+  // segment: dh_last folded through the aggregates of every later segment,
+  // g <- P g + G (the later segments' affine maps, last one first).
+  float Av[kNPL], A2[kNPL], gv[kNPL], dA[kNPL];
+#pragma unroll
+  for (int j = 0; j < kNPL; ++j) {
+    const int n = n0 + j;
+    const bool ok = dvalid && n < N;
+    Av[j] = ok ? a.A[d * N + n] : 0.0f;
+    A2[j] = Av[j] * kLog2e;
+    dA[j] = 0.0f;
+    float gg = ok && a.dh_last ? a.dh_last[bdn + n] : 0.0f;
+    if (ok) {
+      for (int sp = a.nsegb - 1; sp > s; --sp) {
+        const int64_t wi = ((static_cast<int64_t>(b) * a.nsegb + sp) * a.D + d) * N + n;
+        gg = __builtin_fmaf(a.seg_P[wi], gg, a.seg_G[wi]);
+      }
+    }
+    gv[j] = gg;
+  }
+  const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
+  const float dsk = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+
+  struct Raw {
+    InT b[BCI], c[BCI], u[4], dt[4], z[4], go[4];
+    uint8_t rs[4];
+  };
+  struct Out {
+    float u[4], sig[4], gz[4];
+  };
+
+  auto load = [&](int J, Raw& r) {
+    const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
+#pragma unroll
+    for (int q = 0; q < BCI; ++q) {
+      const int it = tid + q * kThreads;
+      const int t = it / NPADC, n = it % NPADC;
+      const bool ok = n < N && tc + t < pend;
+      const int64_t off = (static_cast<int64_t>(b) * a.L + tc + t) * N + n;
+      r.b[q] = ok ? B_in[off] : InT{};
+      r.c[q] = ok ? C_in[off] : InT{};
+    }
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int t = l + 4 * G;
+      const bool ok = fin && dvalid && tc + t < pend;
+      const int64_t off = rowbase + tc + t;
+      r.u[G] = ok ? u_in[off] : InT{};
+      r.dt[G] = ok ? dt_in[off] : InT{};
+      r.z[G] = ok && z_in ? z_in[off] : InT{};
+      r.go[G] = ok ? go_in[off] : InT{};
+      r.rs[G] = HAS_RESET && ok ? a.reset[static_cast<int64_t>(b) * a.L + tc + t] : 0;
+    }
+  };
+
+  // Per-step parameters of chunk J into LDS; the finalize factors stay in the
+  // staging lane's registers (it finalizes the same steps).
+  auto store = [&](int J, const Raw& r, Out& o) {
+    const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
+#pragma unroll
+    for (int q = 0; q < BCI; ++q) {
+      const int it = tid + q * kThreads;
+      s_B[it] = load_elem(&r.b[q], 0);
+      s_C[it] = load_elem(&r.c[q], 0);
+    }
+    if (!fin) return;
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int t = l + 4 * G;
+      const bool ok = dvalid && tc + t < pend;
+      const float x = load_elem(&r.dt[G], 0) + bias;
+      float dl = ok ? softplus_f32(x) : 0.0f;
+      const float uu = load_elem(&r.u[G], 0);
+      const float go = load_elem(&r.go[G], 0);
+      float dy = go, gz = 0.0f;
+      if (z_in) {
+        const float zz = load_elem(&r.z[G], 0);
+        const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+        dy = go * (zz * sg);
+        gz = go * (sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
+      }
+      const float dv = dl * uu;
+      if (HAS_RESET && r.rs[G]) dl = -dl;  // sign bit: the state is cleared before this step
+      s_rec[c * kK + t] = make_float4(dl, dv, dy, 0.0f);
+      o.u[G] = uu;
+      o.sig[G] = fast_rcp(1.0f + fast_exp2(-x * kLog2e));
+      o.gz[G] = gz;
+    }
+  };
+
+  float* const wbuf = s_w + w * 2 * TS;
+  float* const wacc = s_acc + w * 2 * FP * NPADC;
+
+  // The workgroup's dB / dC terms of steps [t0, t0 + FP) of the chunk at tc:
+  // the waves' totals added in order, one partial per channel group.
+  auto flush = [&](int64_t tc, int t0) {
+    for (int i = tid; i < 2 * FP * NPADC; i += kThreads) {
+      const int type = i / (FP * NPADC);
+      const int tt = (i / NPADC) % FP;
+      const int n = i % NPADC;
+      const int64_t tg = tc + t0 + tt;
+      if (n < N && tg < pend) {
+        float sum = s_acc[i];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) sum += s_acc[ww * 2 * FP * NPADC + i];
+        float* dst = type ? a.partC : a.partB;
+        dst[((static_cast<int64_t>(g) * a.B + b) * a.L + tg) * N + n] = sum;
+      }
+    }
+  };
+
+  // Chunk J: recompute its states from the checkpoint, then the adjoint
+  // backwards through it.
+  auto chunk = [&](int J, const Out& o) {
+    const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
+    float hs[kNPL], hist[kK][kNPL];
+    {
+      const int64_t ci = ((static_cast<int64_t>(b) * a.n_ck + tc / kK) * a.D + d) * N;
+#pragma unroll
+      for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? a.ckpt[ci + n0 + j] : 0.0f;
+    }
+    __syncthreads();  // this chunk's LDS parameters are complete
+
+    float h[kNPL];
+#pragma unroll
+    for (int j = 0; j < kNPL; ++j) h[j] = hs[j];
+#pragma unroll
+    for (int t = 0; t < kK; ++t) {
+      const float4 r = s_rec[c * kK + t];
+      const float4 bv = *reinterpret_cast<const float4*>(s_B + t * NPADC + n0);
+      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+      float dl = r.x;
+      if (HAS_RESET) {
+        const bool rs = __float_as_int(dl) < 0;
+        if (__builtin_amdgcn_ballot_w64(rs)) {
+#pragma unroll
+          for (int j = 0; j < kNPL; ++j) h[j] = rs ? 0.0f : h[j];
+        }
+        dl = fabsf(dl);
+      }
+#pragma unroll
+      for (int j = 0; j < kNPL; ++j) {
+        h[j] = __builtin_fmaf(fast_exp2(dl * A2[j]), h[j], bb[j] * r.y);
+        hist[t][j] = h[j];
+      }
+    }
+
+    float F1 = 0.0f, F2 = 0.0f, FY = 0.0f;  // this lane's step sums in the current group of four
+#pragma unroll
+    for (int t = kK - 1; t >= 0; --t) {
+      const float4 r = s_rec[c * kK + t];
+      const float4 bv = *reinterpret_cast<const float4*>(s_B + t * NPADC + n0);
+      const float4 cv = *reinterpret_cast<const float4*>(s_C + t * NPADC + n0);
+      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+      const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+      const bool rs = HAS_RESET && __float_as_int(r.x) < 0;
+      const float dl = fabsf(r.x), dv = r.y, dy = r.z;
+      float s1 = 0.0f, s2 = 0.0f, yy = 0.0f, p3[kNPL], p4[kNPL];
+#pragma unroll
+      for (int j = 0; j < kNPL; ++j) {
+        const float hp = t > 0 ? hist[t - 1][j] : hs[j];
+        const float av = rs ? 0.0f : fast_exp2(dl * A2[j]);
+        gv[j] = __builtin_fmaf(dy, cc[j], gv[j]);  // adjoint of h_t
+        const float gq = gv[j] * (av * hp);
+        s1 = __builtin_fmaf(gv[j], bb[j], s1);
+        s2 = __builtin_fmaf(gq, Av[j], s2);
+        dA[j] = __builtin_fmaf(gq, dl, dA[j]);
+        yy = __builtin_fmaf(cc[j], hist[t][j], yy);
+        p3[j] = gv[j] * dv;
+        p4[j] = dy * hist[t][j];
+        gv[j] = av * gv[j];  // carried to step t-1
+      }
+      s1 = chan_sum<LPC>(s1);
+      s2 = chan_sum<LPC>(s2);
+      yy = chan_sum<LPC>(yy);
+      const bool mine = (l & 3) == (t & 3);
+      F1 = mine ? s1 : F1;
+      F2 = mine ? s2 : F2;
+      FY = mine ? yy : FY;
+
+      // dB / dC terms of this step into the wave buffer (slot t & 1).
+      *reinterpret_cast<float4*>(wbuf + cw * QS + (t & 1) * NPADC + n0) = make_float4(p3[0], p3[1], p3[2], p3[3]);
+      *reinterpret_cast<float4*>(wbuf + TS + cw * QS + (t & 1) * NPADC + n0) =
+          make_float4(p4[0], p4[1], p4[2], p4[3]);
+      if ((t & 1) == 0) {
+        // Steps t and t+1 are in the buffer: add up the wave's channels into
+        // the wave's totals.
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < 4 * NPADC / 64; ++it) {
+          const int item = lane + 64 * it;
+          const int type = item / (2 * NPADC);
+          const int par = (item / NPADC) & 1;
+          const int n = item % NPADC;
+          const float* src = wbuf + type * TS + par * NPADC + n;
+          float sum = src[0];
+#pragma unroll
+          for (int q = 1; q < CPWAVE; ++q) sum += src[q * QS];
+          wacc[(type * FP + (t + par) % FP) * NPADC + n] = sum;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (t % FP == 0 && t > 0) {
+          __syncthreads();  // every wave's totals of steps [t, t + FP) are in LDS
+          flush(tc, t);
+          __syncthreads();  // read before the next period overwrites them
+        }
+      }
+
+      if ((t & 3) == 0 && fin) {
+        // Steps t .. t+3 are complete: lane l finalizes step t + l.
+        const int G = t / 4;
+        const int tf = t + l;
+        const int64_t tg = tc + tf;
+        const float4 rf = s_rec[c * kK + tf];
+        if (dvalid && tg < pend) {
+          const float dlf = fabsf(rf.x), dyf = rf.z;
+          const float du = __builtin_fmaf(dyf, dsk, dlf * F1);
+          const float dx = __builtin_fmaf(o.u[G], F1, F2) * o.sig[G];
+          const float dz = o.gz[G] * __builtin_fmaf(dsk, o.u[G], FY);
+          store_grad(a, a.du, rowbase + tg, du);
+          store_grad(a, a.ddt, rowbase + tg, dx);
+          if (a.dz) store_grad(a, a.dz, rowbase + tg, dz);
+          dD_acc = __builtin_fmaf(dyf, o.u[G], dD_acc);
+          dbias_acc += dx;
+        }
+      }
+    }
+    __syncthreads();  // totals of the chunk's first period complete; LDS parameters free
+    flush(tc, 0);
+  };
+
+  Raw r;
+  Out o;
+  load(nchunks - 1, r);
+  for (int J = nchunks - 1; J >= 0; --J) {
+    store(J, r, o);
+    if (J > 0) load(J - 1, r);
+    chunk(J, o);
+  }
+
+  // Per-(b, segment) partials of dA, dD and d dt_bias; dh0 from the first segment.
+#pragma unroll
+  for (int j = 0; j < kNPL; ++j) {
+    const int n = n0 + j;
+    if (!dvalid || n >= N) continue;
+    a.partA[((static_cast<int64_t>(b) * a.nsegb + s) * a.D + d) * N + n] = dA[j];
+    if (s == 0 && a.dh0) a.dh0[bdn + n] = gv[j];
+  }
+  dD_acc = chan_sum<4>(dD_acc);
+  dbias_acc = chan_sum<4>(dbias_acc);
+  if (l == 0 && dvalid) {
+    const int64_t pi = (static_cast<int64_t>(b) * a.nsegb + s) * a.D + d;
+    a.partD[pi] = dD_acc;
+    a.partBias[pi] = dbias_acc;
+  }
+}
+
+struct RedArgs {
+  int64_t bln, dn, D, groups, bs;  // groups: channel groups; bs: batch rows x segments
+  const float* partB;
+  const float* partC;
+  const float* partA;
+  const float* partD;
+  const float* partBias;
+  float* dB;
+  float* dC;
+  float* dA;
+  float* dD;
+  float* dbias;
+};
+
+// Shared gradients: sums of the partials in a fixed order.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const RedArgs r) {
+  const int64_t total = 2 * r.bln + r.dn + 2 * r.D;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (i < 2 * r.bln) {
+      const bool isC = i >= r.bln;
+      const int64_t e = isC ? i - r.bln : i;
+      const float* src = isC ? r.partC : r.partB;
+      float acc = 0.0f;
+      for (int64_t q = 0; q < r.groups; ++q) acc += src[q * r.bln + e];
+      (isC ? r.dC : r.dB)[e] = acc;
+    } else if (i < 2 * r.bln + r.dn) {
+      const int64_t e = i - 2 * r.bln;
+      float acc = 0.0f;
+      for (int64_t q = 0; q < r.bs; ++q) acc += r.partA[q * r.dn + e];
+      r.dA[e] = acc;
+    } else {
+      const int64_t e = i - 2 * r.bln - r.dn;
+      const bool isBias = e >= r.D;
+      const int64_t dd = isBias ? e - r.D : e;
+      float* dst = isBias ? r.dbias : r.dD;
+      if (!dst) continue;
+      const float* src = isBias ? r.partBias : r.partD;
+      float acc = 0.0f;
+      for (int64_t q = 0; q < r.bs; ++q) acc += src[q * r.D + dd];
+      dst[dd] = acc;
+    }
+  }
+}
+
+int bwd_lpc(int64_t N) {
+  if (N <= 16) return 4;
+  if (N <= 32) return 8;
+  if (N <= 64) return 16;
+  if (N <= 128) return 32;
+  return 64;
+}
+
+template <typename Fn>
+hipError_t with_bwd_tile(int64_t N, Fn&& fn) {
+  switch (bwd_lpc(N)) {
+    case 4: return fn(BwdTile<4>{});
+    case 8: return fn(BwdTile<8>{});
+    case 16: return fn(BwdTile<16>{});
+    case 32: return fn(BwdTile<32>{});
+    default: return fn(BwdTile<64>{});
+  }
+}
+
+}  // namespace
+
+int bwd_channels_per_block(int64_t N) { return kWaves * 64 / bwd_lpc(N); }
+
+void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps) {
+  // Enough segments that the reverse sweep launches about three resident
+  // workgroups per compute unit (256 CUs), each segment a whole number of
+  // 16-step chunks.
+  const int64_t groups = B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N));
+  const int64_t chunks = (L + kK - 1) / kK;
+  int64_t want = (3 * 256 + groups - 1) / groups;
+  want = std::max<int64_t>(1, std::min<int64_t>(want, chunks));
+  const int64_t per = (chunks + want - 1) / want;  // chunks per segment
+  *seg_steps = per * kK;
+  *nsegb = static_cast<int>((chunks + per - 1) / per);
+}
+
+size_t bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb) {
+  const int64_t groups = (D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N);
+  return static_cast<size_t>(2 * groups * B * L * N + B * nsegb * D * N + 2 * B * nsegb * D);
+}
+
+int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb) {
+  return B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N)) * nsegb;
+}
+
+hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
+  const int cpw = bwd_channels_per_block(pl.N);
+  const int64_t groups = (pl.D + cpw - 1) / cpw;
+  BwdArgs a{};
+  a.B = pl.B;
+  a.D = pl.D;
+  a.L = pl.L;
+  a.N = pl.N;
+  a.seg_steps = pl.seg_steps;
+  a.n_ck = pl.n_ck;
+  a.nsegb = pl.nsegb;
+  a.n_dgroups = static_cast<int>(groups);
+  a.nblocks = static_cast<int>(pl.B * groups * pl.nsegb);
+  a.grad_bf16 = pl.grad_bf16;
+  a.u = pl.u;
+  a.dt = pl.dt;
+  a.z = pl.z;
+  a.Bm = pl.Bm;
+  a.Cm = pl.Cm;
+  a.dout = pl.dout;
+  a.dt_bias = pl.dt_bias;
+  a.A = pl.A;
+  a.Dskip = pl.Dskip;
+  a.reset = pl.reset;
+  a.dh_last = pl.dh_last;
+  a.ckpt = pl.ckpt;
+  a.seg_P = pl.seg_P;
+  a.seg_G = pl.seg_G;
+  a.du = pl.du;
+  a.ddt = pl.ddt;
+  a.dz = pl.dz;
+  a.dh0 = pl.dh0;
+  const int64_t bln = pl.B * pl.L * pl.N;
+  a.partB = pl.part;
+  a.partC = pl.part + groups * bln;
+  a.partA = pl.part + 2 * groups * bln;
+  a.partD = a.partA + pl.B * pl.nsegb * pl.D * pl.N;
+  a.partBias = a.partD + pl.B * pl.nsegb * pl.D;
+  const bool reset = pl.reset != nullptr;
+  hipError_t e = with_bwd_tile(pl.N, [&](auto tile) {
+    using TL = decltype(tile);
+    const dim3 grid(static_cast<unsigned>(a.nblocks)), block(kThreads);
+    if (pl.in_bf16) {
+      if (reset)
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, false>), grid, block, 0, stream, a);
+    } else {
+      if (reset)
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+
+  RedArgs r{};
+  r.bln = bln;
+  r.dn = pl.D * pl.N;
+  r.D = pl.D;
+  r.groups = groups;
+  r.bs = pl.B * pl.nsegb;
+  r.partB = a.partB;
+  r.partC = a.partC;
+  r.partA = a.partA;
+  r.partD = a.partD;
+  r.partBias = a.partBias;
+  r.dB = pl.dB;
+  r.dC = pl.dC;
+  r.dA = pl.dA;
+  r.dD = pl.dD;
+  r.dbias = pl.dbias;
+  const int64_t total = 2 * r.bln + r.dn + 2 * r.D;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

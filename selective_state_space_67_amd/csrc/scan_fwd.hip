@@ -67,7 +67,10 @@
 namespace ssm {
 namespace {
 
-enum Mode { kFull = 0, kAggregate = 1 };
+// kFull: the scan itself. kAggregate: per-piece affine aggregates of a split
+// scan. kCheckpoint: the forward sweep of the backward pass (states every 16
+// steps and per-segment adjoint aggregates; see the kernel).
+enum Mode { kFull = 0, kAggregate = 1, kCheckpoint = 2 };
 
 // Work layout of one kernel instance, fixed at compile time.
 template <int NPL_, int RPC_>
@@ -108,6 +111,14 @@ struct ScanArgs {
   float* h_last;
   float* ws_P;  // decay products of pieces 0..nseg-2, (nseg-1, B, D, N)
   float* ws_H;  // end states of pieces 0..nseg-2 from a zero start
+  // kCheckpoint only
+  const void* dout;   // (B, D, L), the gradient of out
+  float* ckpt;        // (B, n_ck, D, N): the state entering every 16-step chunk
+  float* seg_P;       // (B, nsegb, D, N): product of a_t over each backward segment
+  float* seg_G;       // (B, nsegb, D, N): sum of (prod a) dy C over each segment
+  int64_t seg_steps;  // backward segment length (a multiple of 16 dividing seg_len)
+  int64_t n_ck;
+  int nsegb;
 };
 
 template <typename TL, typename InT, bool HAS_RESET, int MODE>
@@ -116,6 +127,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
   constexpr int MASK = RING - 1;
   constexpr bool FULL = MODE == kFull;
+  constexpr bool CKPT = MODE == kCheckpoint;
   // LDS geometry, in float2 units.
   //  (delta, delta*u): two copies x CPW channel rows. Each row carries a
   //  16-entry mirror of its first 16 slots so a lane's 16-step window never
@@ -133,7 +145,10 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   //  RING + 4 floats, so that a 16-byte read covers four steps and the 16
   //  rows read by a DPP row fall in different banks.
   constexpr int B_STRIDE = RING + 4;
-  static_assert(B_STRIDE <= 2 * BC_STRIDE, "B rows fit the (B, C) area");
+  //  The checkpoint sweep stages B and C as two such float arrays, and dy (the
+  //  gate-weighted output gradient) per (channel, step) with the same stride.
+  constexpr int BC_FLOATS = CKPT ? 2 * NPAD * B_STRIDE : 2 * NPAD * BC_STRIDE;
+  constexpr int DY_STRIDE = RING + 4;
   // Row staging: CPW x T (channel, step) items per chunk, RI consecutive steps
   // per thread, handled by the first ROW_THREADS threads.
   constexpr int ROW_ITEMS = CPW * T;
@@ -144,7 +159,9 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   static_assert(BC_ITEMS >= 1 && (T * NPAD) % THREADS == 0, "B/C staging split");
 
   __shared__ __align__(16) float2 s_du[DU_COPY + CPW * DU_STRIDE];
-  __shared__ __align__(16) float2 s_bc[NPAD * BC_STRIDE];
+  __shared__ __align__(16) float s_bcf[BC_FLOATS];
+  float2* const s_bc = reinterpret_cast<float2*>(s_bcf);
+  __shared__ __align__(16) float s_dy[CKPT ? CPW * DY_STRIDE : 4];
   __shared__ __align__(16) float s_y[FULL ? CPW * RPC * RING : 4];  // finished slice sums per step
   __shared__ float s_sum[FULL ? 1 : CPW];                              // aggregate pass: sum of delta
 
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     const bool ok = dvalid && n < N;
     A2[j] = ok ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = 0.0f;
-    if (FULL && ok) {
+    if ((FULL || CKPT) && ok) {
       const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + n;
       float hv = a.h0 ? a.h0[hi] : 0.0f;
       // Fold the aggregates of the preceding pieces: h <- P h + H.
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   // Empty rings: steps before the start (read by lagging lanes) are identity
   // steps (delta = 0, delta*u = 0, B = C = 0).
   for (int i = tid; i < DU_COPY + CPW * DU_STRIDE; i += THREADS) s_du[i] = make_float2(0.f, 0.f);
-  for (int i = tid; i < NPAD * BC_STRIDE; i += THREADS) s_bc[i] = make_float2(0.f, 0.f);
+  for (int i = tid; i < BC_FLOATS; i += THREADS) s_bcf[i] = 0.0f;
 
   // Full pass: lane 15 finishes step L-1 by iteration L+17. The aggregate pass
   // needs no cross-lane sum, so its lanes run in lockstep without the skew.
@@ -223,6 +240,15 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   // one of them resets (then the piece's decay product is 0).
   float sum_delta = 0.0f;
   bool cleared = false;
+  // Checkpoint sweep: running decay product and adjoint sum of the current
+  // backward segment.
+  float segP[NPL], segG[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    segP[j] = 1.0f;
+    segG[j] = 0.0f;
+  }
+  const InT* __restrict__ go_wg = CKPT ? static_cast<const InT*>(a.dout) + row0 : nullptr;
 
   // Row-staging items of this thread: RI consecutive steps of one channel.
   const bool row_thread = tid < ROW_THREADS;
@@ -241,7 +267,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   // Raw inputs of one chunk (loaded two chunks ahead of their use) and the
   // per-step output factors D*u and silu(z) kept until the chunk is finished.
   struct Raw {
-    InT b[BC_ITEMS], c[BC_ITEMS], u[RI], dt[RI], z[RI];
+    InT b[BC_ITEMS], c[BC_ITEMS], u[RI], dt[RI], z[RI], go[RI];
     uint8_t rs[RI];
   };
   struct Out {
@@ -258,6 +284,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     const InT* __restrict__ uj = u_wg + tau0;
     const InT* __restrict__ dtj = dt_wg + tau0;
     const InT* __restrict__ zj = z_wg ? z_wg + tau0 : nullptr;
+    const InT* __restrict__ goj = CKPT ? go_wg + tau0 : nullptr;
     const uint8_t* __restrict__ rsj = HAS_RESET ? rs_wg + tau0 : nullptr;
     if (group_full && tau0 + T <= Lseg) {
 #pragma unroll
@@ -265,13 +292,14 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         const bool ok = bc_n(q) < N;
         const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
         r.b[q] = ok ? Bj[off] : InT{};
-        r.c[q] = FULL && ok ? Cj[off] : InT{};
+        r.c[q] = (FULL || CKPT) && ok ? Cj[off] : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         r.u[i] = row_thread ? uj[srow + i] : InT{};
         r.dt[i] = row_thread ? dtj[srow + i] : InT{};
-        r.z[i] = FULL && zj && row_thread ? zj[srow + i] : InT{};
+        r.z[i] = (FULL || CKPT) && zj && row_thread ? zj[srow + i] : InT{};
+        r.go[i] = CKPT && row_thread ? goj[srow + i] : InT{};
         r.rs[i] = HAS_RESET && row_thread ? rsj[stl + i] : 0;
       }
     } else {
@@ -280,14 +308,15 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         const bool ok = bc_n(q) < N && tau0 + bc_tl(q) < Lseg;
         const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
         r.b[q] = ok ? Bj[off] : InT{};
-        r.c[q] = FULL && ok ? Cj[off] : InT{};
+        r.c[q] = (FULL || CKPT) && ok ? Cj[off] : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         const bool ok = sc_valid && tau0 + stl + i < Lseg;
         r.u[i] = ok ? uj[srow + i] : InT{};
         r.dt[i] = ok ? dtj[srow + i] : InT{};
-        r.z[i] = FULL && zj && ok ? zj[srow + i] : InT{};
+        r.z[i] = (FULL || CKPT) && zj && ok ? zj[srow + i] : InT{};
+        r.go[i] = CKPT && ok ? goj[srow + i] : InT{};
         r.rs[i] = HAS_RESET && ok ? rsj[stl + i] : 0;
       }
     }
@@ -303,7 +332,8 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         s_bc[n * BC_STRIDE + ((par * T + bc_tl(q) + (n / NPL) % 16) & MASK)] =
             make_float2(load_elem(&r.b[q], 0), load_elem(&r.c[q], 0));
       else
-        reinterpret_cast<float*>(s_bc)[n * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.b[q], 0);
+        s_bcf[n * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.b[q], 0);
+      if (CKPT) s_bcf[(NPAD + n) * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.c[q], 0);
     }
     if (!row_thread) return;
     float dl[RI], dv[RI];
@@ -318,9 +348,15 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
         o.dsk[i] = s_dskip * uu;
         o.gate[i] = z_wg ? silu_f32(load_elem(&r.z[i], 0)) : 1.0f;
       }
-      if (!FULL) {
+      if (MODE == kAggregate) {
         sum_delta += dl[i];
         cleared = cleared || (HAS_RESET && r.rs[i]);
+      }
+      if (CKPT) {
+        // dy = dout * silu(z): the gradient reaching y (zero past the end,
+        // where dout was not loaded)
+        const float go = load_elem(&r.go[i], 0);
+        s_dy[sc * DY_STRIDE + par * T + stl + i] = z_wg ? go * silu_f32(load_elem(&r.z[i], 0)) : go;
       }
       if (HAS_RESET && r.rs[i]) dl[i] = -dl[i];  // sign bit: clear the state before this step
     }
@@ -416,13 +452,93 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   const float2* du_row = s_du + p * DU_COPY + c * DU_STRIDE;
   const float2* bc_row = s_bc + nbase * BC_STRIDE;
 
+  // ---- one step of the checkpoint sweep ----
+  // h as in the scan; segP = product of a_t since the segment start (0 after a
+  // reset, where a_t counts as 0); segG += segP dy C, the segment's adjoint
+  // from a zero start, accumulated in forward order.
+  auto step_ck = [&](float dl, const float dv, const float dy, const float (&Bv)[NPL],
+                     const float (&Cv)[NPL]) {
+    bool rs = false;
+    if (HAS_RESET) {
+      rs = __float_as_int(dl) < 0;
+      if (__builtin_amdgcn_ballot_w64(rs)) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) h[j] = rs ? 0.0f : h[j];
+      }
+      dl = fabsf(dl);
+    }
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const float abar = fast_exp2(dl * A2[j]);
+      h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
+      segP[j] = rs ? 0.0f : segP[j] * abar;
+      segG[j] = __builtin_fmaf(segP[j] * dy, Cv[j], segG[j]);
+    }
+  };
+
   // ---- the recurrence over chunk J (ring half `par`) ----
   // One lane-step reads one (delta, delta*u) pair and NPL (B, C) pairs. With
   // one state per lane and up to three waves per SIMD (the register budget
   // allows it), the reads of each 8-step half block are issued while the
   // previous half block computes (two register sets, alternating statically).
-  auto compute = [&](const int par) {
-    if constexpr (!FULL) {
+  auto compute = [&](const int J, const int par) {
+    if constexpr (CKPT) {
+      // Lockstep, like the aggregate pass, plus C and dy per step. The state
+      // entering every 16-step chunk is written out, and each backward
+      // segment's (segP, segG) at its last step.
+      const float* b_row = s_bcf + nbase * B_STRIDE;
+      const float* c_row = s_bcf + (NPAD + nbase) * B_STRIDE;
+      const float* dy_row = s_dy + c * DY_STRIDE;
+      const int64_t tchunk = t_seg + static_cast<int64_t>(J) * T;  // step held in slot par * T
+      const int64_t pend = t_seg + Lseg;
+#pragma unroll
+      for (int i = 0; i < T; i += 4) {
+        const int m = par * T + i;
+        if (i % 16 == 0 && tchunk + i < pend) {
+          const int64_t ci = (static_cast<int64_t>(b) * a.n_ck + (tchunk + i) / 16) * a.D + d;
+#pragma unroll
+          for (int j = 0; j < NPL; ++j)
+            if (dvalid && nbase + j < N) a.ckpt[ci * N + nbase + j] = h[j];
+        }
+        const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
+        const float4 d23 = *reinterpret_cast<const float4*>(du_row + m + 2);
+        const float4 dy4 = *reinterpret_cast<const float4*>(dy_row + m);
+        float B0[NPL], B1[NPL], B2[NPL], B3[NPL], C0[NPL], C1[NPL], C2[NPL], C3[NPL];
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const float4 vb = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
+          const float4 vc = *reinterpret_cast<const float4*>(c_row + j * B_STRIDE + m);
+          B0[j] = vb.x;
+          B1[j] = vb.y;
+          B2[j] = vb.z;
+          B3[j] = vb.w;
+          C0[j] = vc.x;
+          C1[j] = vc.y;
+          C2[j] = vc.z;
+          C3[j] = vc.w;
+        }
+        step_ck(d01.x, d01.y, dy4.x, B0, C0);
+        step_ck(d01.z, d01.w, dy4.y, B1, C1);
+        step_ck(d23.x, d23.y, dy4.z, B2, C2);
+        step_ck(d23.z, d23.w, dy4.w, B3, C3);
+        if (i % 16 == 12) {
+          const int64_t tend = tchunk + i + 4;  // end of this 16-step block
+          if (tend - 16 < pend && (tend % a.seg_steps == 0 || tend >= pend)) {
+            const int64_t sg = (min(tend, pend) - 1) / a.seg_steps;
+            const int64_t si = ((static_cast<int64_t>(b) * a.nsegb + sg) * a.D + d) * N;
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+              if (dvalid && nbase + j < N) {
+                a.seg_P[si + nbase + j] = segP[j];
+                a.seg_G[si + nbase + j] = segG[j];
+              }
+              segP[j] = 1.0f;
+              segG[j] = 0.0f;
+            }
+          }
+        }
+      }
+    } else if constexpr (!FULL) {
       // Lockstep: every lane is at step m. Per four steps a lane reads two
       // (delta, delta*u) float4s (broadcast within its DPP row) and one B
       // float4 per state (shared by the rows of a wave). Nothing is stored,
@@ -522,7 +638,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     store_chunk(J, 0, r0, o0);
     if (J + 2 < nchunks) load_chunk(J + 2, r0);
     __syncthreads();
-    compute(0);
+    compute(J, 0);
     __syncthreads();
     if (FULL && J >= 1) finalize(J - 1, 1, o1);
     if (J + 1 >= nchunks) break;
@@ -530,7 +646,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     store_chunk(J + 1, 1, r1, o1);
     if (J + 3 < nchunks) load_chunk(J + 3, r1);
     __syncthreads();
-    compute(1);
+    compute(J + 1, 1);
     __syncthreads();
     if (FULL) finalize(J, 0, o0);
   }
@@ -542,7 +658,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   }
 
   // ---- results that leave the workgroup ----
-  if (!FULL) {
+  if (MODE == kAggregate) {
     // Per-channel totals from the T / RI staging threads of each channel
     // (consecutive threads within one wave).
     constexpr int G = T / RI;
@@ -562,7 +678,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     if (!dvalid || n >= N) continue;
     if (FULL) {
       if (a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * N + n] = h[j];
-    } else {
+    } else if (MODE == kAggregate) {
       const int64_t wi = (static_cast<int64_t>(s) * a.B + b) * a.D * N + d * N + n;
       a.ws_H[wi] = h[j];
       a.ws_P[wi] = sum_delta < 0.0f ? 0.0f : fast_exp2(A2[j] * sum_delta);
@@ -571,7 +687,8 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
 }
 
 template <typename TL, typename InT, bool HAS_RESET>
-hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, hipStream_t stream) {
+hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, bool checkpoint,
+                       hipStream_t stream) {
   if (args.nseg > 1) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
@@ -582,8 +699,12 @@ hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, 
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
-  hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull>), dim3(nblocks_full), dim3(TL::THREADS), 0, stream,
-                     full);
+  if (checkpoint)
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint>), dim3(nblocks_full), dim3(TL::THREADS), 0,
+                       stream, full);
+  else
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull>), dim3(nblocks_full), dim3(TL::THREADS), 0,
+                       stream, full);
   return hipGetLastError();
 }
 
@@ -679,6 +800,14 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.reset = pl.reset;
   a.out = pl.out;
   a.h_last = pl.h_last;
+  a.dout = pl.dout;
+  a.ckpt = pl.ckpt;
+  a.seg_P = pl.seg_P;
+  a.seg_G = pl.seg_G;
+  a.seg_steps = pl.seg_steps;
+  a.n_ck = pl.n_ck;
+  a.nsegb = pl.nsegb;
+  const bool ck = pl.checkpoint != 0;
   const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
   a.ws_P = pl.ws;
   a.ws_H = pl.ws ? pl.ws + per : nullptr;
@@ -689,8 +818,10 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   return with_tile(pl.N, [&](auto tile) {
     using TL = decltype(tile);
     if (pl.in_bf16)
-      return reset ? launch_tile<TL, bf16_t, true>(a, nf, na, stream) : launch_tile<TL, bf16_t, false>(a, nf, na, stream);
-    return reset ? launch_tile<TL, float, true>(a, nf, na, stream) : launch_tile<TL, float, false>(a, nf, na, stream);
+      return reset ? launch_tile<TL, bf16_t, true>(a, nf, na, ck, stream)
+                   : launch_tile<TL, bf16_t, false>(a, nf, na, ck, stream);
+    return reset ? launch_tile<TL, float, true>(a, nf, na, ck, stream)
+                 : launch_tile<TL, float, false>(a, nf, na, ck, stream);
   });
 }
 

@@ -41,8 +41,9 @@ def test_exports_every_declared_function(lib):
 def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(0) == ctypes.sizeof(bd.ScanParams)
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
+    assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10000
+    assert lib.ssm_version() == 10100
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -209,3 +210,95 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bd, "_lib", None)
     with pytest.raises(ImportError):
         bd.load_library()
+
+
+def bwd_params(**kw):
+    """Valid-looking backward parameters over fake, disjoint, aligned addresses."""
+    p = bd.BwdParams()
+    p.batch, p.dim, p.seqlen, p.dstate = B, D, L, N
+    p.in_dtype, p.grad_dtype = bd.SSM_BF16, bd.SSM_F32
+    addr = [BASE]
+
+    def take(nbytes):
+        a = addr[0]
+        addr[0] += (nbytes + 4095) // 4096 * 4096
+        return a
+
+    p.u, p.dt_raw, p.z, p.dout = (take(B * D * L * 2) for _ in range(4))
+    p.Bm, p.Cm = take(B * L * N * 2), take(B * L * N * 2)
+    p.A, p.dt_bias, p.Dskip = take(D * N * 4), take(D * 4), take(D * 4)
+    p.du, p.d_dt_raw, p.dz = (take(B * D * L * 4) for _ in range(3))
+    p.dA, p.dBm, p.dCm = take(D * N * 4), take(B * L * N * 4), take(B * L * N * 4)
+    p.dDskip, p.d_dt_bias, p.dh0 = take(D * 4), take(D * 4), take(B * D * N * 4)
+    n = ctypes.c_size_t(0)
+    assert bd.load_library().ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    p.workspace, p.workspace_bytes = take(n.value), n.value
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def bwd_status(lib, p):
+    return lib.ssm_scan_bwd(ctypes.byref(p), None)
+
+
+def test_bwd_null_params(lib):
+    assert lib.ssm_scan_bwd(None, None) == 1
+    assert lib.ssm_scan_bwd_workspace_size(None, None) == 1
+
+
+@pytest.mark.parametrize("field", ["u", "dt_raw", "A", "Bm", "Cm", "dout", "du", "d_dt_raw", "dA", "dBm", "dCm",
+                                   "workspace", "dz"])
+def test_bwd_required_pointers(lib, field):
+    assert bwd_status(lib, bwd_params(**{field: None})) == 1
+    assert field.encode() in lib.ssm_last_error()
+
+
+def test_bwd_dz_only_with_z(lib):
+    assert bwd_status(lib, bwd_params(z=None)) == 2          # dz given without z
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(seqlen=0), dict(dstate=257), dict(seqlen=2 ** 40)])
+def test_bwd_bad_shape(lib, kw):
+    n = ctypes.c_size_t(0)
+    p = bwd_params()
+    for k, v in kw.items():
+        setattr(p, k, v)
+    assert bwd_status(lib, p) == 2
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(in_dtype=2), dict(grad_dtype=-1)])
+def test_bwd_bad_dtype(lib, kw):
+    assert bwd_status(lib, bwd_params(**kw)) == 3
+
+
+@pytest.mark.parametrize("field,off", [("u", 1), ("dout", 1), ("du", 2), ("dA", 2), ("dBm", 2), ("dh0", 2),
+                                       ("workspace", 4)])
+def test_bwd_misaligned(lib, field, off):
+    p = bwd_params()
+    setattr(p, field, getattr(p, field) + off)
+    assert bwd_status(lib, p) == 4
+    assert field.encode() in lib.ssm_last_error()
+
+
+def test_bwd_workspace_too_small(lib):
+    p = bwd_params()
+    p.workspace_bytes -= 4
+    assert bwd_status(lib, p) == 6
+
+
+@pytest.mark.parametrize("a,b_", [("du", "u"), ("dBm", "Cm"), ("dA", "dCm"), ("d_dt_raw", "du"),
+                                  ("workspace", "dout"), ("dh0", "workspace"), ("dz", "z")])
+def test_bwd_alias(lib, a, b_):
+    p = bwd_params()
+    setattr(p, a, getattr(p, b_) + 16)
+    assert bwd_status(lib, p) == 7
+
+
+def test_bwd_workspace_covers_checkpoints_and_partials(lib):
+    # 8 x 1536 x 2048, N = 16: states every 16 steps alone are 8*128*1536*16 floats
+    n = ctypes.c_size_t(0)
+    p = bwd_params(batch=8, dim=1536, seqlen=2048)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= 8 * 128 * 1536 * 16 * 4
