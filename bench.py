@@ -14,6 +14,8 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
                kernel source changed since they were taken)
   cold_cache   the same launch after a 1 GiB write that evicts L2 and MALL
   decode       the single-token decode step (batch 64, 2048 channels, N = 128)
+  backward     ssm_scan_bwd on the same workload with a random output gradient
+               (checkpoint sweep, reverse sweep and reduction, back to back)
   cpu_baseline the float64 oracle on the host cores over the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -45,6 +47,12 @@ ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 #                     + 2 ops; delta*u, D*u + y, gate (3)               = 18
 OPS_PER_ELEMENT = 6.0
 OPS_PER_ROW_STEP = 18.0
+# Backward, per (b, d, t, n): the forward step again (6) and the adjoint:
+# g FMA, a*h, g*(a*h), dA FMA, S1 FMA, S2 FMA, Y FMA, g*delta*u, dy*h,
+# a*g (10) = 16; per (b, d, t): softplus (9), sigmoid (4), silu and silu' (8),
+# du, d dt_raw, dz, dD and d dt_bias (8) = 29.
+BWD_OPS_PER_ELEMENT = 16.0
+BWD_OPS_PER_ROW_STEP = 29.0
 SCAN_SOURCES = ["selective_state_space_67_amd/csrc/scan_fwd.hip",
                 "selective_state_space_67_amd/csrc/device_math.h"]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
@@ -82,6 +90,14 @@ def algorithmic_bytes(B, D, L, N, s_in, s_out, reset=False, h0=False, h_last=Fal
     if h_last:
         b += 4 * B * D * N
     return b
+
+
+def backward_bytes(B, D, L, N, s_in, s_grad, reset=False):
+    """HBM bytes the backward must move: u, dt_raw, z, dout and B, C read once;
+    du, d dt_raw, dz and dB, dC written once; the small parameters and their
+    gradients."""
+    return (4 * B * D * L * s_in + 2 * B * L * N * s_in + 3 * B * D * L * s_grad + 2 * B * L * N * 4
+            + 2 * (4 * D * N + 8 * D) + (B * L if reset else 0))
 
 
 def decode_bytes(B, D, N, s_in, s_out):
@@ -200,6 +216,25 @@ def main():
     dbytes = decode_bytes(Bd, Dd, Nd, 2, 4)
     dsec = float(np.median(dms)) / 1e3
 
+    # Backward pass on the same workload.
+    rng = np.random.default_rng(1234)
+    dout = wl.to_torch(wl.store(rng.standard_normal((B, D, L)), cfg["dtype"]), dev)
+    bwd = binding.prepare_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dout, dt_bias=t["dt_bias"],
+                                   Dskip=t["Dskip"], z=t["z"], reset=t["reset"])
+    for _ in range(3):
+        bwd()
+    bsteps = max(5, min(args.steps, 20))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(bsteps):
+        bwd()
+    e1.record(stream)
+    e1.synchronize()
+    bsec = e0.elapsed_time(e1) / bsteps / 1e3
+    bbytes = backward_bytes(B, D, L, N, s_in, 4, reset=x["reset"] is not None)
+    bops = BWD_OPS_PER_ELEMENT * elements + BWD_OPS_PER_ROW_STEP * B * D * L
+    del bwd, dout
+
     result = {
         "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
         "value": elements / wall,
@@ -239,6 +274,11 @@ def main():
         "decode": {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
                    "launch_ms_mean": dsec * 1e3, "algorithmic_bytes": dbytes,
                    "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS},
+        "backward": {"workload": "ssm_scan_bwd on the same inputs, %s dout, fp32 gradients" % cfg["dtype"],
+                     "ms_per_call": bsec * 1e3, "elements_per_s": elements / bsec,
+                     "algorithmic_bytes": bbytes, "hbm_gbps": bbytes / bsec / 1e9,
+                     "algorithmic_ops": bops, "alu_frac": bops / bsec / 1e12 / ALU_PEAK_TOPS,
+                     "vs_forward": bsec / launch_s},
     }
 
     if not args.no_cpu:

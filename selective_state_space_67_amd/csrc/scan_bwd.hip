@@ -129,11 +129,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
   constexpr int BCI = kK * NPADC / kThreads;  // (step, state) staging items per thread
   static_assert(BCI >= 1 && (kK * NPADC) % kThreads == 0, "B/C staging split");
 
-  __shared__ __align__(16) float4 s_rec[CPW * kK];  // (delta, delta*u, dy, 0); delta negated on a reset
+  // (delta, delta*u, dy, 0) per (channel, step); delta negated on a reset.
+  // Channel rows are RS = 17 float4 apart (an odd number of 16-byte units),
+  // so the channels of a wave read their rows from different banks.
+  constexpr int RS = kK + 1;
+  __shared__ __align__(16) float4 s_rec[CPW * RS];
   __shared__ __align__(16) float s_B[kK * NPADC];
   __shared__ __align__(16) float s_C[kK * NPADC];
   __shared__ __align__(16) float s_w[kWaves * 2 * TS];
-  __shared__ float s_acc[kWaves * 2 * FP * NPADC];  // per-wave totals of the dB and dC terms
+  // Per-wave totals of the dB and dC terms: [wave][type][step][state], the
+  // type halves 32 floats apart in banks.
+  constexpr int AT = FP * NPADC + 32;   // floats per type
+  constexpr int AW = 2 * AT;            // floats per wave
+  __shared__ float s_acc[kWaves * AW];
 
   int idx = blockIdx.x;
   if ((a.nblocks & 7) == 0) idx = (idx & 7) * (a.nblocks >> 3) + (idx >> 3);
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       }
       const float dv = dl * uu;
       if (HAS_RESET && r.rs[G]) dl = -dl;  // sign bit: the state is cleared before this step
-      s_rec[c * kK + t] = make_float4(dl, dv, dy, 0.0f);
+      s_rec[c * RS + t] = make_float4(dl, dv, dy, 0.0f);
       o.u[G] = uu;
       o.sig[G] = fast_rcp(1.0f + fast_exp2(-x * kLog2e));
       o.gz[G] = gz;
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
   };
 
   float* const wbuf = s_w + w * 2 * TS;
-  float* const wacc = s_acc + w * 2 * FP * NPADC;
+  float* const wacc = s_acc + w * AW;
 
   // The workgroup's dB / dC terms of steps [t0, t0 + FP) of the chunk at tc:
   // the waves' totals added in order, one partial per channel group.
@@ -270,9 +278,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       const int n = i % NPADC;
       const int64_t tg = tc + t0 + tt;
       if (n < N && tg < pend) {
-        float sum = s_acc[i];
+        const int k = type * AT + tt * NPADC + n;
+        float sum = s_acc[k];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) sum += s_acc[ww * 2 * FP * NPADC + i];
+        for (int ww = 1; ww < kWaves; ++ww) sum += s_acc[ww * AW + k];
         float* dst = type ? a.partC : a.partB;
         dst[((static_cast<int64_t>(g) * a.B + b) * a.L + tg) * N + n] = sum;
       }
@@ -281,14 +290,20 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
 
   // Chunk J: recompute its states from the checkpoint, then the adjoint
   // backwards through it.
-  auto chunk = [&](int J, const Out& o) {
+  // The checkpoint (state entering chunk J), loaded one chunk ahead.
+  auto load_ckpt = [&](int J, float (&hs)[kNPL]) {
     const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
-    float hs[kNPL], hist[kK][kNPL];
-    {
-      const int64_t ci = ((static_cast<int64_t>(b) * a.n_ck + tc / kK) * a.D + d) * N;
+    const int64_t ci = ((static_cast<int64_t>(b) * a.n_ck + tc / kK) * a.D + d) * N;
 #pragma unroll
-      for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? a.ckpt[ci + n0 + j] : 0.0f;
-    }
+    for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? a.ckpt[ci + n0 + j] : 0.0f;
+  };
+
+  auto chunk = [&](int J, const Out& o, const float (&hs)[kNPL]) {
+    const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
+    // States of the chunk: the checkpoint hs, then h_t of every odd step in
+    // registers; an even step's state is rebuilt from its odd predecessor in
+    // the reverse pass (one FMA with the a_t that pass computes anyway).
+    float hist[kK / 2][kNPL];
     __syncthreads();  // this chunk's LDS parameters are complete
 
     float h[kNPL];
@@ -296,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
     for (int j = 0; j < kNPL; ++j) h[j] = hs[j];
 #pragma unroll
     for (int t = 0; t < kK; ++t) {
-      const float4 r = s_rec[c * kK + t];
+      const float4 r = s_rec[c * RS + t];
       const float4 bv = *reinterpret_cast<const float4*>(s_B + t * NPADC + n0);
       const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
       float dl = r.x;
@@ -311,34 +326,28 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
 #pragma unroll
       for (int j = 0; j < kNPL; ++j) {
         h[j] = __builtin_fmaf(fast_exp2(dl * A2[j]), h[j], bb[j] * r.y);
-        hist[t][j] = h[j];
+        if (t & 1) hist[t >> 1][j] = h[j];
       }
     }
 
     float F1 = 0.0f, F2 = 0.0f, FY = 0.0f;  // this lane's step sums in the current group of four
-#pragma unroll
-    for (int t = kK - 1; t >= 0; --t) {
-      const float4 r = s_rec[c * kK + t];
-      const float4 bv = *reinterpret_cast<const float4*>(s_B + t * NPADC + n0);
-      const float4 cv = *reinterpret_cast<const float4*>(s_C + t * NPADC + n0);
-      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-      const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
-      const bool rs = HAS_RESET && __float_as_int(r.x) < 0;
+
+    // One reverse step: av = a_t (0 on a reset), hp = h_{t-1}, ht = h_t.
+    auto rstep = [&](const int t, const float4 r, const float (&bb)[4], const float (&cc)[4],
+                     const float (&av)[kNPL], const float (&hp)[kNPL], const float (&ht)[kNPL]) {
       const float dl = fabsf(r.x), dv = r.y, dy = r.z;
       float s1 = 0.0f, s2 = 0.0f, yy = 0.0f, p3[kNPL], p4[kNPL];
 #pragma unroll
       for (int j = 0; j < kNPL; ++j) {
-        const float hp = t > 0 ? hist[t - 1][j] : hs[j];
-        const float av = rs ? 0.0f : fast_exp2(dl * A2[j]);
         gv[j] = __builtin_fmaf(dy, cc[j], gv[j]);  // adjoint of h_t
-        const float gq = gv[j] * (av * hp);
+        const float gq = gv[j] * (av[j] * hp[j]);
         s1 = __builtin_fmaf(gv[j], bb[j], s1);
         s2 = __builtin_fmaf(gq, Av[j], s2);
         dA[j] = __builtin_fmaf(gq, dl, dA[j]);
-        yy = __builtin_fmaf(cc[j], hist[t][j], yy);
+        yy = __builtin_fmaf(cc[j], ht[j], yy);
         p3[j] = gv[j] * dv;
-        p4[j] = dy * hist[t][j];
-        gv[j] = av * gv[j];  // carried to step t-1
+        p4[j] = dy * ht[j];
+        gv[j] = av[j] * gv[j];  // carried to step t-1
       }
       s1 = chan_sum<LPC>(s1);
       s2 = chan_sum<LPC>(s2);
@@ -366,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
           float sum = src[0];
 #pragma unroll
           for (int q = 1; q < CPWAVE; ++q) sum += src[q * QS];
-          wacc[(type * FP + (t + par) % FP) * NPADC + n] = sum;
+          wacc[type * AT + ((t + par) % FP) * NPADC + n] = sum;
         }
         __builtin_amdgcn_wave_barrier();
         if (t % FP == 0 && t > 0) {
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
         const int G = t / 4;
         const int tf = t + l;
         const int64_t tg = tc + tf;
-        const float4 rf = s_rec[c * kK + tf];
+        const float4 rf = s_rec[c * RS + tf];
         if (dvalid && tg < pend) {
           const float dlf = fabsf(rf.x), dyf = rf.z;
           const float du = __builtin_fmaf(dyf, dsk, dlf * F1);
@@ -394,6 +403,34 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
           dbias_acc += dx;
         }
       }
+    };
+
+    // Steps in pairs (t odd, t - 1 even), last pair first.
+#pragma unroll
+    for (int t = kK - 1; t >= 1; t -= 2) {
+      const float4 r1 = s_rec[c * RS + t], r0 = s_rec[c * RS + t - 1];
+      const float4 b1v = *reinterpret_cast<const float4*>(s_B + t * NPADC + n0);
+      const float4 b0v = *reinterpret_cast<const float4*>(s_B + (t - 1) * NPADC + n0);
+      const float4 c1v = *reinterpret_cast<const float4*>(s_C + t * NPADC + n0);
+      const float4 c0v = *reinterpret_cast<const float4*>(s_C + (t - 1) * NPADC + n0);
+      const float b1[4] = {b1v.x, b1v.y, b1v.z, b1v.w}, b0[4] = {b0v.x, b0v.y, b0v.z, b0v.w};
+      const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, c0[4] = {c0v.x, c0v.y, c0v.z, c0v.w};
+      const bool rs1 = HAS_RESET && __float_as_int(r1.x) < 0;
+      const bool rs0 = HAS_RESET && __float_as_int(r0.x) < 0;
+      float a1[kNPL], a0[kNPL], hodd[kNPL], hev[kNPL], hpp[kNPL];
+#pragma unroll
+      for (int j = 0; j < kNPL; ++j) {
+        a1[j] = rs1 ? 0.0f : fast_exp2(fabsf(r1.x) * A2[j]);
+        a0[j] = rs0 ? 0.0f : fast_exp2(fabsf(r0.x) * A2[j]);
+        hpp[j] = t >= 3 ? hist[(t - 2) >> 1][j] : hs[j];          // h_{t-2}
+        hev[j] = __builtin_fmaf(a0[j], hpp[j], b0[j] * r0.y);     // h_{t-1}, as the forward computed it
+        hodd[j] = hist[t >> 1][j];                                 // h_t
+      }
+      rstep(t, r1, b1, c1, a1, hev, hodd);
+      rstep(t - 1, r0, b0, c0, a0, hpp, hev);
+      // Keep the scheduler from hoisting later pairs' reads and exponentials
+      // above this one: that costs registers the wave needs for occupancy.
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // totals of the chunk's first period complete; LDS parameters free
     flush(tc, 0);
@@ -401,11 +438,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
 
   Raw r;
   Out o;
+  float hs[kNPL];
   load(nchunks - 1, r);
+  load_ckpt(nchunks - 1, hs);
   for (int J = nchunks - 1; J >= 0; --J) {
     store(J, r, o);
-    if (J > 0) load(J - 1, r);
-    chunk(J, o);
+    float hs_next[kNPL];
+    if (J > 0) {
+      load(J - 1, r);
+      load_ckpt(J - 1, hs_next);
+    }
+    chunk(J, o, hs);
+#pragma unroll
+    for (int j = 0; j < kNPL; ++j) hs[j] = hs_next[j];
   }
 
   // Per-(b, segment) partials of dA, dD and d dt_bias; dh0 from the first segment.
@@ -439,33 +484,62 @@ struct RedArgs {
   float* dbias;
 };
 
-// Shared gradients: sums of the partials in a fixed order.
+// Shared gradients: sums of the partials in a fixed order. One thread owns
+// four consecutive outputs (float4 loads and stores where the range allows).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const RedArgs r) {
-  const int64_t total = 2 * r.bln + r.dn + 2 * r.D;
+  const int64_t n4_bc = (r.bln + 3) / 4, n4_a = (r.dn + 3) / 4, n4_d = (r.D + 3) / 4;
+  const int64_t total = 2 * n4_bc + n4_a + 2 * n4_d;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    if (i < 2 * r.bln) {
-      const bool isC = i >= r.bln;
-      const int64_t e = isC ? i - r.bln : i;
-      const float* src = isC ? r.partC : r.partB;
-      float acc = 0.0f;
-      for (int64_t q = 0; q < r.groups; ++q) acc += src[q * r.bln + e];
-      (isC ? r.dC : r.dB)[e] = acc;
-    } else if (i < 2 * r.bln + r.dn) {
-      const int64_t e = i - 2 * r.bln;
-      float acc = 0.0f;
-      for (int64_t q = 0; q < r.bs; ++q) acc += r.partA[q * r.dn + e];
-      r.dA[e] = acc;
+    const float* src;
+    float* dst;
+    int64_t e, len, stride, count;
+    if (i < 2 * n4_bc) {
+      const bool isC = i >= n4_bc;
+      e = (isC ? i - n4_bc : i) * 4;
+      src = isC ? r.partC : r.partB;
+      dst = isC ? r.dC : r.dB;
+      len = r.bln;
+      stride = r.bln;
+      count = r.groups;
+    } else if (i < 2 * n4_bc + n4_a) {
+      e = (i - 2 * n4_bc) * 4;
+      src = r.partA;
+      dst = r.dA;
+      len = r.dn;
+      stride = r.dn;
+      count = r.bs;
     } else {
-      const int64_t e = i - 2 * r.bln - r.dn;
-      const bool isBias = e >= r.D;
-      const int64_t dd = isBias ? e - r.D : e;
-      float* dst = isBias ? r.dbias : r.dD;
+      const int64_t k = i - 2 * n4_bc - n4_a;
+      const bool isBias = k >= n4_d;
+      e = (isBias ? k - n4_d : k) * 4;
+      src = isBias ? r.partBias : r.partD;
+      dst = isBias ? r.dbias : r.dD;
+      len = r.D;
+      stride = r.D;
+      count = r.bs;
       if (!dst) continue;
-      const float* src = isBias ? r.partBias : r.partD;
-      float acc = 0.0f;
-      for (int64_t q = 0; q < r.bs; ++q) acc += src[q * r.D + dd];
-      dst[dd] = acc;
+    }
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // 16-byte accesses only where every row of src and dst is 16-byte aligned
+    const bool vec = e + 4 <= len && (stride % 4) == 0 && (reinterpret_cast<uintptr_t>(src) % 16) == 0 &&
+                     (reinterpret_cast<uintptr_t>(dst) % 16) == 0;
+    for (int64_t q = 0; q < count; ++q) {
+      const float* p = src + q * stride + e;
+      if (vec) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        acc[0] += v.x;
+        acc[1] += v.y;
+        acc[2] += v.z;
+        acc[3] += v.w;
+      } else {
+        for (int k = 0; k < 4 && e + k < len; ++k) acc[k] += p[k];
+      }
+    }
+    if (vec) {
+      *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      for (int k = 0; k < 4 && e + k < len; ++k) dst[e + k] = acc[k];
     }
   }
 }
@@ -493,17 +567,31 @@ hipError_t with_bwd_tile(int64_t N, Fn&& fn) {
 
 int bwd_channels_per_block(int64_t N) { return kWaves * 64 / bwd_lpc(N); }
 
+// Reverse-sweep workgroups resident on the whole chip: 256 CUs x workgroups
+// per CU. The kernels need 200-250 VGPRs (two waves per SIMD, two 4-wave
+// workgroups per CU); the N > 128 layout's 84 KB of LDS allows one.
+int64_t bwd_resident_blocks(int64_t N) { return 256 * (bwd_lpc(N) >= 64 ? 1 : 2); }
+
 void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps) {
-  // Enough segments that the reverse sweep launches about three resident
-  // workgroups per compute unit (256 CUs), each segment a whole number of
-  // 16-step chunks.
+  // Segments of whole 16-step chunks. Workgroups run in rounds of the
+  // resident count, each as long as its segment, so pick the count that
+  // minimises rounds x chunks per segment (the fewest segments on a tie).
   const int64_t groups = B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N));
   const int64_t chunks = (L + kK - 1) / kK;
-  int64_t want = (3 * 256 + groups - 1) / groups;
-  want = std::max<int64_t>(1, std::min<int64_t>(want, chunks));
-  const int64_t per = (chunks + want - 1) / want;  // chunks per segment
-  *seg_steps = per * kK;
-  *nsegb = static_cast<int>((chunks + per - 1) / per);
+  const int64_t resident = bwd_resident_blocks(N);
+  int64_t best = 1, best_cost = -1;
+  const int64_t max_seg = std::min<int64_t>(chunks, 4096);
+  for (int64_t ns = 1; ns <= max_seg; ++ns) {
+    const int64_t per = (chunks + ns - 1) / ns;
+    const int64_t used = (chunks + per - 1) / per;  // segments actually needed at this length
+    const int64_t cost = (groups * used + resident - 1) / resident * per;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = per;
+    }
+  }
+  *seg_steps = best * kK;
+  *nsegb = static_cast<int>((chunks + best - 1) / best);
 }
 
 size_t bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb) {
@@ -588,8 +676,8 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   r.dA = pl.dA;
   r.dD = pl.dD;
   r.dbias = pl.dbias;
-  const int64_t total = 2 * r.bln + r.dn + 2 * r.D;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 4096);
+  const int64_t total = 2 * ((r.bln + 3) / 4) + (r.dn + 3) / 4 + 2 * ((r.D + 3) / 4);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
   return hipGetLastError();
 }
