@@ -53,6 +53,10 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
+        lib.oracle_conv_silu_rows.argtypes = [i64, i64, i64] + [p] * 10 + [ctypes.c_int]
+        lib.oracle_conv_silu_rows.restype = None
+        lib.oracle_conv_silu_bwd_rows.argtypes = [i64, i64, i64, i64] + [p] * 12 + [ctypes.c_int]
+        lib.oracle_conv_silu_bwd_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -109,9 +113,75 @@ def scan_rows(rows_b, rows_d, u_rows, dt_rows, A, Bm, Cm, *, z_rows=None, dt_bia
     return (out, h_last) if want_h_last else out
 
 
+def conv_silu(x, w, *, bias=None, reset=None, state_in=None, want_pre=False, want_state=False, nthreads=0):
+    """Causal depthwise conv1d (width K = w.shape[1]) then SiLU over x (B, D, L).
+
+    w: (D, K); bias: (D,); reset: (B, L); state_in: (B, D, K-1), the inputs
+    before the sequence (oldest first). Returns u (B, D, L), plus the
+    pre-activation and the final conv state (B, D, K-1) when asked for.
+    """
+    lib = _load()
+    x, w, bias, state_in = _f64(x), _f64(w), _f64(bias), _f64(state_in)
+    Bt, D, L = x.shape
+    K = w.shape[1]
+    assert w.shape == (D, K) and K >= 1
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    u = np.empty((Bt, D, L))
+    pre = np.empty((Bt, D, L)) if want_pre else None
+    st = np.empty((Bt, D, max(K - 1, 0))) if want_state else None
+    if state_in is not None:
+        assert state_in.shape == (Bt, D, K - 1)
+    lib.oracle_conv_silu_rows(Bt * D, L, K, _ptr(rb), _ptr(rd), _ptr(x), _ptr(w), _ptr(bias), _ptr(reset),
+                              _ptr(state_in), _ptr(pre), _ptr(u), _ptr(st) if K > 1 else None, int(nthreads))
+    res = [u]
+    if want_pre:
+        res.append(pre)
+    if want_state:
+        res.append(st)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def conv_silu_bwd(x, w, du, pre, *, reset=None, state_in=None, nthreads=0):
+    """Gradients of sum(du * conv_silu(x)) for x, w, bias and state_in.
+
+    Returns dict dx (B, D, L), dw (D, K), dbias (D,), dstate_in (B, D, K-1).
+    """
+    lib = _load()
+    x, w, du, pre, state_in = _f64(x), _f64(w), _f64(du), _f64(pre), _f64(state_in)
+    Bt, D, L = x.shape
+    K = w.shape[1]
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    out = dict(dx=np.empty((Bt, D, L)), dw=np.empty((D, K)), dbias=np.empty(D),
+               dstate_in=np.empty((Bt, D, max(K - 1, 0))))
+    rc = lib.oracle_conv_silu_bwd_rows(Bt * D, L, K, D, _ptr(rb), _ptr(rd), _ptr(x), _ptr(w), _ptr(reset),
+                                       _ptr(state_in), _ptr(pre), _ptr(du), _ptr(out["dx"]), _ptr(out["dw"]),
+                                       _ptr(out["dbias"]), _ptr(out["dstate_in"]) if K > 1 else None,
+                                       int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle conv backward: scratch allocation failed")
+    return out
+
+
 def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-         want_h_last=False, nthreads=0):
-    """Full scan. u, dt_raw, z: (B, D, L); h0: (B, D, N). Returns out (B, D, L)."""
+         want_h_last=False, conv_w=None, conv_b=None, conv_state=None, want_conv_state=False, nthreads=0):
+    """Full scan. u, dt_raw, z: (B, D, L); h0: (B, D, N). Returns out (B, D, L).
+
+    With conv_w (D, K) the scan input is silu(causal_conv1d(u)) (see conv_silu);
+    conv_state (B, D, K-1) is the input before the sequence, and
+    want_conv_state also returns the final conv state (after h_last).
+    """
+    if conv_w is not None:
+        u, cst = conv_silu(u, conv_w, bias=conv_b, reset=reset, state_in=conv_state, want_state=True,
+                           nthreads=nthreads)
+        res = scan(u, dt_raw, A, Bm, Cm, z=z, dt_bias=dt_bias, Dskip=Dskip, reset=reset, h0=h0,
+                   want_h_last=want_h_last, nthreads=nthreads)
+        if not want_conv_state:
+            return res
+        return (res + (cst,)) if want_h_last else (res, cst)
     u = np.asarray(u)
     Bt, D, L = u.shape
     N = np.asarray(A).shape[1]
@@ -127,11 +197,27 @@ def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, 
     return res.reshape(Bt, D, L)
 
 
-def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, nthreads=0):
+def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, conv_w=None, conv_b=None,
+                 conv_state=None, nthreads=0):
     """Decode step. h: (B, D, N); u, dt_raw, z: (B, D); Bm, Cm: (B, N).
 
-    Returns (out (B, D), h_new (B, D, N)); the input h is not modified.
+    Returns (out (B, D), h_new (B, D, N)); the input h is not modified. With
+    conv_w (D, K), u is the conv input of this step and conv_state (B, D, K-1)
+    holds the previous K-1 inputs (oldest first, zeros when None): the step
+    input is silu(conv_b + sum_k conv_w[:, k] * window[k]) over the window
+    (state, u), and (out, h_new, new conv state) is returned.
     """
+    if conv_w is not None:
+        conv_w = _f64(conv_w)
+        x = _f64(u)
+        Bt, D = x.shape
+        K = conv_w.shape[1]
+        st = np.zeros((Bt, D, K - 1)) if conv_state is None else _f64(conv_state)
+        window = np.concatenate([st, x[:, :, None]], axis=2)
+        pre = np.einsum("bdk,dk->bd", window, conv_w) + (0.0 if conv_b is None else _f64(conv_b)[None, :])
+        uc = pre / (1.0 + np.exp(-pre))
+        out, h_new = state_update(h, uc, dt_raw, A, Bm, Cm, z=z, dt_bias=dt_bias, Dskip=Dskip, nthreads=nthreads)
+        return out, h_new, np.ascontiguousarray(window[:, :, 1:])
     lib = _load()
     h_new = np.array(h, dtype=np.float64, copy=True, order="C")
     u, dt_raw, z = _f64(u), _f64(dt_raw), _f64(z)
@@ -148,7 +234,7 @@ def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, n
 
 
 def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-             dh_last=None, nthreads=0):
+             dh_last=None, conv_w=None, conv_b=None, conv_state=None, nthreads=0):
     """Gradients of sum(dout * out) + sum(dh_last * h_last) for the full scan.
 
     u, dt_raw, z, dout: (B, D, L); A: (D, N); Bm, Cm: (B, L, N); dt_bias, Dskip: (D,);
@@ -156,7 +242,18 @@ def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, re
     du, d_dt_raw (B, D, L), dz (B, D, L) or None, dA (D, N), dD, d_dt_bias (D,),
     dB, dC (B, L, N) and dh0 (B, D, N). dD and d_dt_bias are the gradients with
     respect to those parameters whether or not they were given (None acts as 0).
+    With conv_w, u is the conv input: du is its gradient, and dconv_w (D, K),
+    dconv_b (D,) and dconv_state (B, D, K-1) are added.
     """
+    if conv_w is not None:
+        uc, pre = conv_silu(u, conv_w, bias=conv_b, reset=reset, state_in=conv_state, want_pre=True,
+                            nthreads=nthreads)
+        g = scan_bwd(uc, dt_raw, A, Bm, Cm, dout, z=z, dt_bias=dt_bias, Dskip=Dskip, reset=reset, h0=h0,
+                     dh_last=dh_last, nthreads=nthreads)
+        cg = conv_silu_bwd(u, conv_w, g["du"], pre, reset=reset, state_in=conv_state, nthreads=nthreads)
+        g["du"] = cg["dx"]
+        g["dconv_w"], g["dconv_b"], g["dconv_state"] = cg["dw"], cg["dbias"], cg["dstate_in"]
+        return g
     lib = _load()
     u, dt_raw, z, dout = _f64(u), _f64(dt_raw), _f64(z), _f64(dout)
     A, Bm, Cm = _f64(A), _f64(Bm), _f64(Cm)

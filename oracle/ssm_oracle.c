@@ -328,3 +328,124 @@ int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t 
   free(acc);
   return 0;
 }
+
+/*
+ * Causal depthwise convolution followed by SiLU, the input side of the Mamba
+ * block: a depthwise Conv1d of width K, padded by K-1 on the left so that the
+ * output at t sees inputs t-K+1 .. t, then silu ("Illustrated Mamba state
+ * space model", the SSM module's conv1d with kernel_size = d_conv and
+ * groups = d_model; "Mamba SSM core theory and Keras/TensorFlow
+ * implementation", block structure: causal Conv1D, then SiLU):
+ *
+ *   pre_t = bias[d] + sum_{k=0}^{K-1} w[d,k] * x_{t-K+1+k},    u_t = silu(pre_t)
+ *
+ * x_s for s < 0 comes from state_in (the K-1 inputs before the sequence,
+ * oldest first; zeros when NULL). Reading taken where the pages are silent:
+ * the convolution does not look across a reset, so inputs before the start of
+ * the current document (the last t' <= t with reset[b,t'] != 0) count as zero.
+ *
+ *   x : (R, L) rows; w : (Dtot, K); bias : (Dtot) or NULL; reset : (Btot, L) or NULL
+ *   state_in : (R, K-1) or NULL; pre : (R, L) or NULL (pre-activation, for the
+ *   backward); u : (R, L); state_out : (R, K-1) or NULL (the last K-1 inputs,
+ *   zeros for those before a reset, oldest first)
+ */
+void oracle_conv_silu_rows(int64_t R, int64_t L, int64_t K, const int64_t* row_b, const int64_t* row_d,
+                           const double* x, const double* w, const double* bias, const uint8_t* reset,
+                           const double* state_in, double* pre, double* u, double* state_out, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t b = row_b[r], d = row_d[r];
+    int64_t doc = -(K - 1);  /* first step whose input is visible */
+    for (int64_t t = 0; t < L; ++t) {
+      if (reset && reset[b * L + t]) doc = t;
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t s = t - K + 1 + k;
+        if (s < doc) continue;
+        const double xs = s >= 0 ? x[r * L + s] : (state_in ? state_in[r * (K - 1) + (s + K - 1)] : 0.0);
+        acc += w[d * K + k] * xs;
+      }
+      if (pre) pre[r * L + t] = acc;
+      u[r * L + t] = silu(acc);
+    }
+    if (state_out)
+      for (int64_t k = 0; k < K - 1; ++k) {
+        const int64_t s = L - (K - 1) + k;
+        state_out[r * (K - 1) + k] =
+            s < doc ? 0.0 : (s >= 0 ? x[r * L + s] : (state_in ? state_in[r * (K - 1) + (s + K - 1)] : 0.0));
+      }
+  }
+}
+
+/*
+ * Backward of oracle_conv_silu_rows: given du (the gradient reaching u) and the
+ * pre-activations, the gradients of x, w, bias and state_in, by the chain rule:
+ *   dpre_t = du_t * silu'(pre_t)
+ *   dx_s  += w[d,k] dpre_t  and  dw[d,k] += x_s dpre_t  for every (t, k) with s = t-K+1+k visible
+ *   dbias[d] += dpre_t;  d state_in[k] gets the terms of s < 0.
+ * dw and dbias are (Dtot, K) and (Dtot), overwritten and summed over rows in a
+ * fixed order for a given thread count; dstate_in (R, K-1) may be NULL.
+ * Returns 0, or -1 when scratch memory could not be allocated.
+ */
+int oracle_conv_silu_bwd_rows(int64_t R, int64_t L, int64_t K, int64_t Dtot, const int64_t* row_b,
+                              const int64_t* row_d, const double* x, const double* w, const uint8_t* reset,
+                              const double* state_in, const double* pre, const double* du, double* dx,
+                              double* dw, double* dbias, double* dstate_in, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int T = omp_get_max_threads();
+#else
+  (void)nthreads;
+  const int T = 1;
+#endif
+  const int64_t per = Dtot * K + Dtot;
+  double* acc = (double*)calloc((size_t)T * (size_t)per, sizeof(double));
+  if (!acc) return -1;
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+    double* my = acc + (int64_t)omp_get_thread_num() * per;
+#else
+    double* my = acc;
+#endif
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+      const int64_t b = row_b[r], d = row_d[r];
+      for (int64_t t = 0; t < L; ++t) dx[r * L + t] = 0.0;
+      if (dstate_in)
+        for (int64_t k = 0; k < K - 1; ++k) dstate_in[r * (K - 1) + k] = 0.0;
+      int64_t doc = -(K - 1);
+      for (int64_t t = 0; t < L; ++t) {
+        if (reset && reset[b * L + t]) doc = t;
+        const double p = pre[r * L + t], sg = sigmoid(p);
+        const double dp = du[r * L + t] * sg * (1.0 + p * (1.0 - sg));
+        my[Dtot * K + d] += dp;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t s = t - K + 1 + k;
+          if (s < doc) continue;
+          if (s >= 0) {
+            dx[r * L + s] += w[d * K + k] * dp;
+            my[d * K + k] += x[r * L + s] * dp;
+          } else {
+            if (dstate_in) dstate_in[r * (K - 1) + (s + K - 1)] += w[d * K + k] * dp;
+            if (state_in) my[d * K + k] += state_in[r * (K - 1) + (s + K - 1)] * dp;
+          }
+        }
+      }
+    }
+  }
+  for (int64_t i = 0; i < Dtot * K; ++i) dw[i] = 0.0;
+  for (int64_t i = 0; i < Dtot; ++i) dbias[i] = 0.0;
+  for (int t = 0; t < T; ++t) {
+    const double* my = acc + (int64_t)t * per;
+    for (int64_t i = 0; i < Dtot * K; ++i) dw[i] += my[i];
+    for (int64_t i = 0; i < Dtot; ++i) dbias[i] += my[Dtot * K + i];
+  }
+  free(acc);
+  return 0;
+}
