@@ -28,7 +28,12 @@
  *    section 1 (hardware-aware algorithm) and 2.2 (kernel fusion);
  *  - document isolation by resetting the hidden state: same page, 3.2;
  *  - the single-token recurrent (RNN-style) inference step: "Reproducing
- *    Mamba's SSM core in Python" (mhpn.cn), section 3.
+ *    Mamba's SSM core in Python" (mhpn.cn), section 3;
+ *  - the causal depthwise convolution (width d_conv = 4) and SiLU that produce
+ *    the scan input inside the Mamba block: "Illustrated Mamba state space
+ *    model", the SSM module's conv1d (kernel_size = d_conv, padding d_conv-1,
+ *    groups = d_model); "Mamba SSM core theory and Keras/TensorFlow
+ *    implementation", block structure (causal Conv1D, then SiLU).
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
@@ -99,6 +104,19 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *                     the same stream.
  *   num_segments : 0 = the library chooses how many pieces to split L into;
  *                  k >= 1 asks for k pieces (clamped to what L allows).
+ *
+ * Optional input stage (conv_w != NULL): u holds the input x of a causal
+ * depthwise convolution, and the scan runs on
+ *   u'_t = silu(conv_b[d] + sum_{k<K} conv_w[d,k] * x_{t-K+1+k}),  K = conv_width
+ * in place of u everywhere (delta*u' and D*u'). The convolution does not look
+ * across a reset: inputs before the start of the current document count as 0.
+ *   conv_w         (D,K)   float32; 1 <= conv_width <= 4
+ *   conv_b         (D)     float32, NULL => 0
+ *   conv_state_in  (B,D,K-1) float32, NULL => zeros; x_{-K+1} .. x_{-1}, oldest first
+ *   conv_state_out (B,D,K-1) float32, NULL => not written; the last K-1 inputs
+ *                  of the sequence (zeros for those hidden by a later reset),
+ *                  ready to be the next call's conv_state_in
+ * conv_width is ignored when conv_w is NULL.
  */
 typedef struct {
   int64_t batch, dim, seqlen, dstate;
@@ -119,6 +137,12 @@ typedef struct {
   size_t workspace_bytes;
   int32_t num_segments;
   int32_t reserved0;
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_state_in;
+  float* conv_state_out;
+  int32_t conv_width;
+  int32_t reserved1;
 } ssm_scan_params;
 
 /* Bytes of workspace ssm_scan_fwd needs for these parameters (0 when the scan

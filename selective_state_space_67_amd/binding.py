@@ -40,6 +40,8 @@ class ScanParams(ctypes.Structure):
         ("h0", ctypes.c_void_p), ("out", ctypes.c_void_p), ("h_last", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("num_segments", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
+        ("conv_state_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -152,7 +154,7 @@ def _stream(stream, device):
 
 
 def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                 num_segments):
+                 num_segments, conv_w=None, conv_b=None, conv_state_in=None, conv_state_out=None):
     import torch
 
     Bt, D, L = u.shape
@@ -185,6 +187,17 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
     p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     p.reset, p.h0, p.out, p.h_last = _ptr(reset), _ptr(h0), _ptr(out), _ptr(h_last)
     p.num_segments = int(num_segments)
+    if conv_w is not None:
+        K = conv_w.shape[1]
+        _need(conv_w, (D, K), "conv_w", torch.float32)
+        if conv_b is not None:
+            _need(conv_b, (D,), "conv_b", torch.float32)
+        for t, name in ((conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+            if t is not None:
+                _need(t, (Bt, D, K - 1), name, torch.float32)
+        p.conv_w, p.conv_b = _ptr(conv_w), _ptr(conv_b)
+        p.conv_state_in, p.conv_state_out = _ptr(conv_state_in), _ptr(conv_state_out)
+        p.conv_width = K
     return p
 
 
@@ -205,8 +218,13 @@ def ssm_scan_workspace_size(u, A, *, num_segments=0, out_dtype=None):
 
 
 def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
-                 out=None, h_last=None, out_dtype=None, workspace=None, num_segments=0, stream=None):
+                 out=None, h_last=None, out_dtype=None, workspace=None, num_segments=0, conv_w=None, conv_b=None,
+                 conv_state_in=None, conv_state_out=None, stream=None):
     """Selective scan over the whole sequence; returns ``out`` (B, D, L).
+
+    With conv_w (D, K <= 4) float32, u is the input of a causal depthwise
+    conv1d + SiLU stage whose output feeds the scan (conv_b (D,),
+    conv_state_in / conv_state_out (B, D, K-1) float32 optional).
 
     u, dt_raw, z: (B, D, L) float32 or bfloat16; A: (D, N) float32;
     Bm, Cm: (B, L, N) same dtype as u; dt_bias, Dskip: (D,) float32;
@@ -221,7 +239,7 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if n.value:
@@ -234,7 +252,8 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
 
 
 def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None, out=None,
-                 h_last=None, out_dtype=None, num_segments=0, stream=None):
+                 h_last=None, out_dtype=None, num_segments=0, conv_w=None, conv_b=None, conv_state_in=None,
+                 conv_state_out=None, stream=None):
     """Marshal the arguments of ssm_scan_fwd once; returns a no-argument callable
     that enqueues the same scan again (same tensors, same stream) each time it is
     called. The tensors must stay alive and unchanged in shape while it is used."""
@@ -244,10 +263,11 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
-    keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last]
+    keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, conv_w, conv_b, conv_state_in,
+            conv_state_out]
     if n.value:
         ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
         keep.append(ws)

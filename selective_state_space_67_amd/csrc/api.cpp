@@ -332,12 +332,19 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
     if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
 
   const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
+  const int64_t K = p->conv_w ? p->conv_width : 0;
+  if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
+  if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
+    return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
+  const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
   const Range inputs[] = {
       range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
       range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln, si, "Bm"),
       range(p->Cm, sz.bln, si, "Cm"),        range(p->A, sz.dn, 4, "A"),
       range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
       range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
+      range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
+      range(p->conv_state_in, bdk, 4, "conv_state_in"),
   };
   const struct {
     const void* ptr;
@@ -346,18 +353,23 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   } aligns[] = {{p->u, si, "u"},           {p->dt_raw, si, "dt_raw"}, {p->z, si, "z"},
                 {p->Bm, si, "Bm"},         {p->Cm, si, "Cm"},         {p->A, 4, "A"},
                 {p->dt_bias, 4, "dt_bias"}, {p->Dskip, 4, "Dskip"},   {p->h0, 4, "h0"},
-                {p->out, so, "out"},       {p->h_last, 4, "h_last"},  {p->workspace, 4, "workspace"}};
+                {p->out, so, "out"},       {p->h_last, 4, "h_last"},  {p->workspace, 4, "workspace"},
+                {p->conv_w, 4, "conv_w"},  {p->conv_b, 4, "conv_b"},  {p->conv_state_in, 4, "conv_state_in"},
+                {p->conv_state_out, 4, "conv_state_out"}};
   for (const auto& a : aligns)
     if (a.ptr && !aligned(a.ptr, a.align))
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
 
   const Range out = range(p->out, sz.bdl, so, "out");
   const Range hl = range(p->h_last, sz.bdn, 4, "h_last");
+  const Range cso = range(p->conv_state_out, bdk, 4, "conv_state_out");
   for (const Range& r : inputs) {
     if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
     if (overlaps(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps %s", r.name);
+    if (overlaps(cso, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
   }
   if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
+  if (overlaps(out, cso) || overlaps(hl, cso)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
 
   int nseg;
   int64_t seg_len;
@@ -370,7 +382,8 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
     const Range w{static_cast<const char*>(p->workspace), ws, "workspace"};
     for (const Range& r : inputs)
       if (overlaps(w, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
-    if (overlaps(w, out) || overlaps(w, hl)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+    if (overlaps(w, out) || overlaps(w, hl) || overlaps(w, cso))
+      return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
   }
 
   ssm::ScanPlan plan{};
@@ -395,6 +408,11 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
   plan.nseg = nseg;
   plan.seg_len = seg_len;
+  plan.conv_w = p->conv_w;
+  plan.conv_b = p->conv_b;
+  plan.conv_state_in = p->conv_state_in;
+  plan.conv_state_out = p->conv_state_out;
+  plan.conv_k = static_cast<int>(K);
   hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -40,6 +40,12 @@ struct ScanPlan {
   int64_t seg_steps;
   int64_t n_ck;
   int nsegb;
+  // Causal depthwise conv1d + SiLU applied to u before the scan (conv_w null: none).
+  const float* conv_w;         // (D, conv_k)
+  const float* conv_b;         // (D) or null
+  const float* conv_state_in;  // (B, D, conv_k - 1) or null
+  float* conv_state_out;       // (B, D, conv_k - 1) or null
+  int conv_k;
 };
 
 struct UpdatePlan {

@@ -119,9 +119,32 @@ struct ScanArgs {
   int64_t seg_steps;  // backward segment length (a multiple of 16 dividing seg_len)
   int64_t n_ck;
   int nsegb;
+  // causal conv1d + SiLU on u (CONV kernels only)
+  const float* conv_w;         // (D, conv_k)
+  const float* conv_b;         // (D) or null
+  const float* conv_state_in;  // (B, D, conv_k - 1) or null
+  float* conv_state_out;       // (B, D, conv_k - 1) or null
+  int conv_k;                  // 1 .. 4
 };
 
-template <typename TL, typename InT, bool HAS_RESET, int MODE>
+// Visibility of the conv window's inputs: the window of step Q covers
+// Q-3 .. Q (taps 0..3, widths below 4 have leading zero taps); an input is
+// hidden when a reset lies after it within the window (the document started
+// later). r0, r1, r2 are the reset flags of Q, Q-1 and Q-2.
+__device__ __forceinline__ float conv_pre(const float (&w)[4], float bias, float x0, float x1, float x2, float x3,
+                                          bool r0, bool r1, bool r2) {
+  float acc = __builtin_fmaf(w[3], x3, bias);
+  if (!r0) {
+    acc = __builtin_fmaf(w[2], x2, acc);
+    if (!r1) {
+      acc = __builtin_fmaf(w[1], x1, acc);
+      if (!r2) acc = __builtin_fmaf(w[0], x0, acc);
+    }
+  }
+  return acc;
+}
+
+template <typename TL, typename InT, bool HAS_RESET, int MODE, bool CONV>
 __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kernel(const ScanArgs a) {
   constexpr int NPL = TL::NPL, RPC = TL::RPC, CPW = TL::CPW, THREADS = TL::THREADS;
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
@@ -258,6 +281,13 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   const bool sc_valid = row_thread && d0 + sc < a.D;
   const float s_bias = sc_valid && a.dt_bias ? a.dt_bias[d0 + sc] : 0.0f;
   const float s_dskip = sc_valid && a.Dskip ? a.Dskip[d0 + sc] : 0.0f;
+  // Conv taps of this staging thread's channel, right-aligned in 4 slots.
+  float s_cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s_cb = 0.0f;
+  if (CONV && sc_valid) {
+    for (int k = 0; k < a.conv_k; ++k) s_cw[4 - a.conv_k + k] = a.conv_w[(d0 + sc) * a.conv_k + k];
+    s_cb = a.conv_b ? a.conv_b[d0 + sc] : 0.0f;
+  }
 
   // (step, state) staging item q of this thread: step q_tl within the chunk,
   // state q_n (NPAD is a power of two, so these are a shift and a mask).
@@ -269,6 +299,8 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   struct Raw {
     InT b[BC_ITEMS], c[BC_ITEMS], u[RI], dt[RI], z[RI], go[RI];
     uint8_t rs[RI];
+    float xh[CONV ? 3 : 1];    // conv inputs of the three steps before the thread's first step
+    uint8_t rh[CONV ? 2 : 1];  // reset flags of the two steps before it
   };
   struct Out {
     float dsk[RI], gate[RI];
@@ -286,6 +318,30 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     const InT* __restrict__ zj = z_wg ? z_wg + tau0 : nullptr;
     const InT* __restrict__ goj = CKPT ? go_wg + tau0 : nullptr;
     const uint8_t* __restrict__ rsj = HAS_RESET ? rs_wg + tau0 : nullptr;
+    // Conv halo: the conv inputs of steps T0-3 .. T0-1 (T0 = this thread's
+    // first step) and the reset flags of T0-2, T0-1. Steps before the sequence
+    // come from the initial conv state (zeros without one).
+    if constexpr (CONV) {
+      const int64_t T0 = t_seg + tau0 + stl;
+      const int64_t dch = d0 + sc;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int64_t pos = T0 - 3 + j;
+        float v = 0.0f;
+        if (sc_valid && pos < L) {
+          if (pos >= 0)
+            v = load_elem(uj, static_cast<int64_t>(srow) - 3 + j);
+          else if (a.conv_state_in && pos >= 1 - a.conv_k)
+            v = a.conv_state_in[(static_cast<int64_t>(b) * a.D + dch) * (a.conv_k - 1) + (pos + a.conv_k - 1)];
+        }
+        r.xh[j] = v;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t pos = T0 - 2 + j;
+        r.rh[j] = HAS_RESET && sc_valid && pos >= 0 && pos < L ? a.reset[static_cast<int64_t>(b) * L + pos] : 0;
+      }
+    }
     if (group_full && tau0 + T <= Lseg) {
 #pragma unroll
       for (int q = 0; q < BC_ITEMS; ++q) {
@@ -337,10 +393,25 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     }
     if (!row_thread) return;
     float dl[RI], dv[RI];
+    float xw[3 + RI];   // conv window inputs x_{T0-3} .. x_{T0+RI-1}
+    bool rr[2 + RI];    // reset flags of T0-2 .. T0+RI-1
+    if constexpr (CONV) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) xw[j] = r.xh[j];
+      rr[0] = r.rh[0];
+      rr[1] = r.rh[1];
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        xw[3 + i] = load_elem(&r.u[i], 0);
+        rr[2 + i] = r.rs[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       // Items past the end carry zeros, which make identity steps (delta = 0).
-      const float uu = load_elem(&r.u[i], 0);
+      float uu = load_elem(&r.u[i], 0);
+      if constexpr (CONV)  // the scan input is silu(causal conv of u) at step T0 + i
+        uu = silu_f32(conv_pre(s_cw, s_cb, xw[i], xw[i + 1], xw[i + 2], xw[i + 3], rr[i + 2], rr[i + 1], rr[i]));
       dl[i] = softplus_f32(load_elem(&r.dt[i], 0) + s_bias);
       if (!sc_valid || tau0 + stl + i >= Lseg) dl[i] = 0.0f;
       dv[i] = dl[i] * uu;
@@ -684,28 +755,57 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
       a.ws_P[wi] = sum_delta < 0.0f ? 0.0f : fast_exp2(A2[j] * sum_delta);
     }
   }
+
+  // Final conv state: the last conv_k - 1 inputs of the sequence, oldest
+  // first, zeros for those hidden by a later reset.
+  if constexpr (FULL && CONV) {
+    if (a.conv_state_out && s == a.nseg - 1 && tid < CPW * 3) {
+      const int cc = tid / 3, kk = tid % 3;
+      const int64_t dd = d0 + cc;
+      if (dd < a.D && kk < a.conv_k - 1) {
+        const int64_t pos = a.L - (a.conv_k - 1) + kk;
+        bool vis = true;  // no reset after pos (a reset at pos itself starts a document there)
+        if (HAS_RESET)
+          for (int64_t q = max(pos + 1, int64_t{0}); q < a.L; ++q) vis = vis && !a.reset[static_cast<int64_t>(b) * a.L + q];
+        float v = 0.0f;
+        if (vis) {
+          if (pos >= 0)
+            v = load_elem(static_cast<const InT*>(a.u), (static_cast<int64_t>(b) * a.D + dd) * a.L + pos);
+          else if (a.conv_state_in)
+            v = a.conv_state_in[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + (pos + a.conv_k - 1)];
+        }
+        a.conv_state_out[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + kk] = v;
+      }
+    }
+  }
 }
 
-template <typename TL, typename InT, bool HAS_RESET>
+template <typename TL, typename InT, bool HAS_RESET, bool CONV>
 hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, bool checkpoint,
                        hipStream_t stream) {
   if (args.nseg > 1) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate>), dim3(nblocks_agg), dim3(TL::THREADS), 0,
-                       stream, agg);
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate, CONV>), dim3(nblocks_agg), dim3(TL::THREADS),
+                       0, stream, agg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
   if (checkpoint)
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint>), dim3(nblocks_full), dim3(TL::THREADS), 0,
-                       stream, full);
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint, CONV>), dim3(nblocks_full),
+                       dim3(TL::THREADS), 0, stream, full);
   else
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull>), dim3(nblocks_full), dim3(TL::THREADS), 0,
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull, CONV>), dim3(nblocks_full), dim3(TL::THREADS), 0,
                        stream, full);
   return hipGetLastError();
+}
+
+template <typename TL, typename InT, bool HAS_RESET>
+hipError_t launch_conv(const ScanArgs& a, int nf, int na, bool ck, hipStream_t stream) {
+  return a.conv_w ? launch_tile<TL, InT, HAS_RESET, true>(a, nf, na, ck, stream)
+                  : launch_tile<TL, InT, HAS_RESET, false>(a, nf, na, ck, stream);
 }
 
 // Layout by state size: (states per lane, rows per channel).
@@ -807,6 +907,11 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.seg_steps = pl.seg_steps;
   a.n_ck = pl.n_ck;
   a.nsegb = pl.nsegb;
+  a.conv_w = pl.conv_w;
+  a.conv_b = pl.conv_b;
+  a.conv_state_in = pl.conv_state_in;
+  a.conv_state_out = pl.conv_state_out;
+  a.conv_k = pl.conv_k;
   const bool ck = pl.checkpoint != 0;
   const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
   a.ws_P = pl.ws;
@@ -818,10 +923,10 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   return with_tile(pl.N, [&](auto tile) {
     using TL = decltype(tile);
     if (pl.in_bf16)
-      return reset ? launch_tile<TL, bf16_t, true>(a, nf, na, ck, stream)
-                   : launch_tile<TL, bf16_t, false>(a, nf, na, ck, stream);
-    return reset ? launch_tile<TL, float, true>(a, nf, na, ck, stream)
-                 : launch_tile<TL, float, false>(a, nf, na, ck, stream);
+      return reset ? launch_conv<TL, bf16_t, true>(a, nf, na, ck, stream)
+                   : launch_conv<TL, bf16_t, false>(a, nf, na, ck, stream);
+    return reset ? launch_conv<TL, float, true>(a, nf, na, ck, stream)
+                 : launch_conv<TL, float, false>(a, nf, na, ck, stream);
   });
 }
 

@@ -302,3 +302,26 @@ def test_bwd_workspace_covers_checkpoints_and_partials(lib):
     p = bwd_params(batch=8, dim=1536, seqlen=2048)
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value >= 8 * 128 * 1536 * 16 * 4
+
+
+def test_scan_conv_arguments(lib):
+    p = scan_params(conv_width=4)
+    p.conv_w = BASE + 0x60000000
+    p.conv_width = 5
+    assert scan_status(lib, p) == 2                 # width out of range
+    p.conv_width = 0
+    assert scan_status(lib, p) == 2
+    p = scan_params()
+    p.conv_b = BASE + 0x60000000                    # conv_b without conv_w
+    assert scan_status(lib, p) == 1
+    p = scan_params()
+    p.conv_w, p.conv_width = BASE + 0x60000000 + 2, 4
+    assert scan_status(lib, p) == 4                 # misaligned weights
+    p = scan_params()
+    p.conv_w, p.conv_width = BASE + 0x60000000, 4
+    p.conv_state_out = p.u                          # final conv state over an input
+    assert scan_status(lib, p) == 7
+    p = scan_params()
+    p.conv_w, p.conv_width = BASE + 0x60000000, 4
+    p.conv_state_out = p.out + 64                   # ... or over out
+    assert scan_status(lib, p) == 7
