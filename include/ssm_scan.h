@@ -164,6 +164,14 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream);
  *   dt_bias  (D), Dskip (D) float32, NULL => 0 / no skip term; A (D,N) float32
  *   Bm, Cm   (B,N)    required
  *   out      (B,D)    required; must not overlap h or any input
+ *   conv_w   (D,K)    float32, NULL => no conv stage; with it, u is this step's
+ *                     conv input and the step input is
+ *                     silu(conv_b + sum_k conv_w[d,k] * window[k]) over the window
+ *                     (conv_state[b,d,0 .. K-2], u), K = conv_width in [1, 4]
+ *   conv_b   (D)      float32, NULL => 0
+ *   conv_state (B,D,K-1) float32, required with conv_w when K > 1: the previous
+ *                     K-1 inputs, oldest first; shifted in place by one input.
+ *                     Must not overlap h, out or any input.
  */
 typedef struct {
   int64_t batch, dim, dstate;
@@ -178,6 +186,11 @@ typedef struct {
   const void* Bm;
   const void* Cm;
   void* out;
+  float* conv_state;
+  const float* conv_w;
+  const float* conv_b;
+  int32_t conv_width;
+  int32_t reserved0;
 } ssm_update_params;
 
 /* Enqueue the decode step described by `p` on `hip_stream`. */

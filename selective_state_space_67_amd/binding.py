@@ -52,7 +52,8 @@ class UpdateParams(ctypes.Structure):
         ("h", ctypes.c_void_p), ("u", ctypes.c_void_p), ("dt_raw", ctypes.c_void_p),
         ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("A", ctypes.c_void_p),
         ("Dskip", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
-        ("out", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("conv_state", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+        ("conv_b", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -309,7 +310,7 @@ def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z
     return call
 
 
-def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out):
+def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None, conv_b=None, conv_state=None):
     import torch
 
     Bt, D, N = h.shape
@@ -332,19 +333,30 @@ def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out):
     p.h, p.u, p.dt_raw, p.z = _ptr(h), _ptr(u), _ptr(dt_raw), _ptr(z)
     p.dt_bias, p.A, p.Dskip = _ptr(dt_bias), _ptr(A), _ptr(Dskip)
     p.Bm, p.Cm, p.out = _ptr(Bm), _ptr(Cm), _ptr(out)
+    if conv_w is not None:
+        K = conv_w.shape[1]
+        _need(conv_w, (D, K), "conv_w", torch.float32)
+        if conv_b is not None:
+            _need(conv_b, (D,), "conv_b", torch.float32)
+        if K > 1:
+            _need(conv_state, (Bt, D, K - 1), "conv_state", torch.float32)
+        p.conv_w, p.conv_b, p.conv_state, p.conv_width = _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K
     return p
 
 
 def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                     out_dtype=None, stream=None):
-    """Decode step: updates h (B, D, N) float32 in place and returns out (B, D)."""
+                     out_dtype=None, conv_w=None, conv_b=None, conv_state=None, stream=None):
+    """Decode step: updates h (B, D, N) float32 in place and returns out (B, D).
+
+    With conv_w (D, K), u is this step's conv input and conv_state
+    (B, D, K-1) float32 is shifted in place."""
     import torch
 
     lib = load_library()
     Bt, D, N = h.shape
     if out is None:
         out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
-    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w, conv_b, conv_state)
     _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
     return out
 

@@ -456,13 +456,28 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
                           range(p->z, bd, si, "z"),         range(p->dt_bias, p->dim, 4, "dt_bias"),
                           range(p->A, dn, 4, "A"),          range(p->Dskip, p->dim, 4, "Dskip"),
                           range(p->Bm, bn, si, "Bm"),       range(p->Cm, bn, si, "Cm")};
+  const int64_t K = p->conv_w ? p->conv_width : 0;
+  if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
+  if (!p->conv_w && (p->conv_b || p->conv_state))
+    return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
+  if (K > 1 && !p->conv_state) return fail(SSM_ERR_NULL_POINTER, "conv_state is NULL although conv_width > 1");
+  for (const void* q : {static_cast<const void*>(p->conv_state), static_cast<const void*>(p->conv_w),
+                        static_cast<const void*>(p->conv_b)})
+    if (q && !aligned(q, 4)) return fail(SSM_ERR_MISALIGNED, "a conv pointer is not aligned to 4 bytes");
+  const Range cw = range(p->conv_w, p->dim * K, 4, "conv_w"), cb = range(p->conv_b, p->dim, 4, "conv_b");
+  const Range cs = range(K > 1 ? p->conv_state : nullptr, bd * (K - 1), 4, "conv_state");
   const Range h = range(p->h, bdn, 4, "h");
   const Range out = range(p->out, bd, so, "out");
   for (const Range& r : inputs) {
     if (overlaps(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps %s", r.name);
     if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+    if (overlaps(cs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps %s", r.name);
   }
   if (overlaps(out, h)) return fail(SSM_ERR_ALIAS, "out overlaps h");
+  for (const Range& r : {h, out, cw, cb})
+    if (overlaps(cs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps %s", r.name);
+  if (overlaps(h, cw) || overlaps(h, cb) || overlaps(out, cw) || overlaps(out, cb))
+    return fail(SSM_ERR_ALIAS, "h or out overlaps a conv parameter");
 
   ssm::UpdatePlan plan{};
   plan.B = p->batch;
@@ -480,6 +495,10 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   plan.Bm = p->Bm;
   plan.Cm = p->Cm;
   plan.out = p->out;
+  plan.conv_state = K > 1 ? p->conv_state : nullptr;
+  plan.conv_w = p->conv_w;
+  plan.conv_b = p->conv_b;
+  plan.conv_k = static_cast<int>(K);
   hipError_t e = ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "state update launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -61,6 +61,10 @@ struct UpdatePlan {
   const void* Bm;
   const void* Cm;
   void* out;
+  float* conv_state;    // (B, D, conv_k - 1), updated in place; null without conv
+  const float* conv_w;  // (D, conv_k) or null
+  const float* conv_b;  // (D) or null
+  int conv_k;
 };
 
 // Largest supported state size.

@@ -18,6 +18,11 @@
 // lane of the row, which is cheaper than broadcasting them; the dot product
 // over n is a butterfly of cross-lane adds. Shapes whose N is not a multiple
 // of four take a scalar variant (one state per lane per pass).
+//
+// With a conv stage the step input is silu(conv_b + sum_k conv_w[k] * window[k])
+// over the window (conv_state[0 .. K-2], u): the conv state holds the previous
+// K-1 inputs, oldest first, and is shifted in place (the row's lane 0 writes it
+// after every lane has read it).
 #include "device_math.h"
 #include "kernels.h"
 
@@ -39,7 +44,32 @@ struct UpdateArgs {
   const void* Bm;
   const void* Cm;
   void* out;
+  float* conv_state;     // (B, D, conv_k - 1) or null
+  const float* conv_w;   // (D, conv_k) or null (no conv stage)
+  const float* conv_b;   // (D) or null
+  int conv_k;
 };
+
+// The step input of row `row` (channel d) from its raw input x: x itself, or
+// the conv + SiLU over (conv state, x).
+__device__ __forceinline__ float step_input(const UpdateArgs& a, int64_t row, int64_t d, float x) {
+  if (!a.conv_w) return x;
+  const int K = a.conv_k;
+  const float* st = a.conv_state + row * (K - 1);
+  float pre = __builtin_fmaf(a.conv_w[d * K + K - 1], x, a.conv_b ? a.conv_b[d] : 0.0f);
+  for (int k = 0; k < K - 1; ++k) pre = __builtin_fmaf(a.conv_w[d * K + k], st[k], pre);
+  return silu_f32(pre);
+}
+
+// Shift the row's conv state by one input (called by one lane per row, after
+// the row's lanes have read the state).
+__device__ __forceinline__ void shift_conv_state(const UpdateArgs& a, int64_t row, float x) {
+  if (!a.conv_w || a.conv_k < 2) return;
+  const int K = a.conv_k;
+  float* st = a.conv_state + row * (K - 1);
+  for (int k = 0; k < K - 2; ++k) st[k] = st[k + 1];
+  st[K - 2] = x;
+}
 
 template <typename InT>
 __device__ __forceinline__ float4 load4(const InT* p, int64_t i);
@@ -106,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a
     if (row >= a.rows) continue;
     const int64_t d = row % a.D;
     const float delta = softplus_f32(xx[r]);
-    const float du = delta * uu[r];
+    const float ui = step_input(a, row, d, uu[r]);
+    const float du = delta * ui;
     float4 hn;
     hn.x = __builtin_fmaf(fast_exp2(delta * (Av[r].x * kLog2e)), hv[r].x, Bv[r].x * du);
     hn.y = __builtin_fmaf(fast_exp2(delta * (Av[r].y * kLog2e)), hv[r].y, Bv[r].y * du);
@@ -119,9 +150,10 @@ __global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a
     y = __builtin_fmaf(Cv[r].w, hn.w, y);
     y = row_sum<LR>(y);
     if (li == 0) {
-      float o = y + (a.Dskip ? a.Dskip[d] * uu[r] : 0.0f);
+      float o = y + (a.Dskip ? a.Dskip[d] * ui : 0.0f);
       if (z_in) o *= silu_f32(zz[r]);
       store_out(a, row, o);
+      shift_conv_state(a, row, uu[r]);
     }
   }
 }
@@ -135,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs
   const InT* B_in = static_cast<const InT*>(a.Bm);
   const InT* C_in = static_cast<const InT*>(a.Cm);
   const int64_t b = row / a.D, d = row % a.D;
-  const float uu = load_elem(static_cast<const InT*>(a.u), row);
+  const float ux = load_elem(static_cast<const InT*>(a.u), row);
+  const float uu = step_input(a, row, d, ux);
   const float delta =
       softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
   const float du = delta * uu;
@@ -152,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs
     float o = y + (a.Dskip ? a.Dskip[d] * uu : 0.0f);
     if (a.z) o *= silu_f32(load_elem(static_cast<const InT*>(a.z), row));
     store_out(a, row, o);
+    shift_conv_state(a, row, ux);
   }
 }
 
@@ -215,6 +249,10 @@ hipError_t launch_state_update(const UpdatePlan& pl, hipStream_t stream) {
   a.Bm = pl.Bm;
   a.Cm = pl.Cm;
   a.out = pl.out;
+  a.conv_state = pl.conv_state;
+  a.conv_w = pl.conv_w;
+  a.conv_b = pl.conv_b;
+  a.conv_k = pl.conv_k;
   return pl.in_bf16 ? launch_dtype<bf16_t>(a, stream) : launch_dtype<float>(a, stream);
 }
 

@@ -89,3 +89,39 @@ def test_conv_with_split_sequence(nseg):
 def test_conv_long_sequence_automatic_split():
     x = conv_case(1, 32, 40000, 16, 4, wl.BF16, 21, packed=True, dt_lo=1e-3, dt_hi=1e-2)
     assert_close(gpu_conv_scan(x), oracle_conv_scan(x), wl.BF16)
+
+
+@pytest.mark.parametrize("N,K", [(128, 4), (16, 3), (12, 4), (64, 1), (256, 2)])
+def test_decode_with_conv_state(N, K):
+    """Decode steps with a conv state against the oracle's decode step, step by step."""
+    import torch
+
+    from selective_state_space_67_amd import ssm_state_update
+
+    dev = device()
+    B, D, steps = 3, 24, 6
+    rng = np.random.default_rng(N + K)
+    y = wl.make_decode_inputs(B, D, N, dtype=wl.BF16, seed=N + K)
+    w = (rng.standard_normal((D, K)) * 0.5).astype(np.float32)
+    cb = (rng.standard_normal(D) * 0.2).astype(np.float32)
+    st = rng.standard_normal((B, D, K - 1)).astype(np.float32)
+    h_ref, st_ref = y["h"].astype(np.float64), st.astype(np.float64)
+    h = torch.from_numpy(y["h"]).to(dev)
+    st_t = torch.from_numpy(st).to(dev) if K > 1 else None
+    t = {k: to_dev(y[k], dev) for k in ("dt_bias", "A", "Dskip")}
+    for s in range(steps):
+        xs = {k: wl.store(rng.standard_normal(shape), wl.BF16)
+              for k, shape in (("u", (B, D)), ("dt_raw", (B, D)), ("z", (B, D)), ("Bm", (B, N)), ("Cm", (B, N)))}
+        tt = {k: to_dev(v, dev) for k, v in xs.items()}
+        o = ssm_state_update(h, tt["u"], tt["dt_raw"], t["A"], tt["Bm"], tt["Cm"], dt_bias=t["dt_bias"],
+                             Dskip=t["Dskip"], z=tt["z"], conv_w=torch.from_numpy(w).to(dev),
+                             conv_b=torch.from_numpy(cb).to(dev), conv_state=st_t)
+        torch.cuda.synchronize()
+        ww = wl.widen
+        ro, h_ref, st_ref = oracle.state_update(h_ref, ww(xs["u"]), ww(xs["dt_raw"]), y["A"], ww(xs["Bm"]),
+                                                ww(xs["Cm"]), z=ww(xs["z"]), dt_bias=y["dt_bias"], Dskip=y["Dskip"],
+                                                conv_w=w, conv_b=cb, conv_state=st_ref)
+        assert_close(o.cpu().numpy(), ro, wl.BF16, what="decode out step %d" % s)
+        assert_close(h.cpu().numpy(), h_ref, wl.BF16, what="decode h step %d" % s)
+        if K > 1:
+            np.testing.assert_array_equal(st_t.cpu().numpy().astype(np.float64), st_ref)
