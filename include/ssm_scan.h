@@ -232,9 +232,14 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *   dh0      (B,D,N)  float32 output, NULL => not written
  *   workspace, workspace_bytes : at least ssm_scan_bwd_workspace_size() bytes
  *                     (never 0 for the backward); contents on entry ignored.
+ * Conv input stage (conv_w != NULL, as in ssm_scan_params): u is the conv
+ * input x; du is the gradient of x, and
+ *   conv_w, conv_b, conv_state_in, conv_width : the forward's conv arguments
+ *   dconv_w (D,K), dconv_b (D), dconv_state_in (B,D,K-1) float32 outputs,
+ *                     NULL => not written
  * Outputs must not overlap each other, the inputs or the workspace. Shared
- * gradients (dA, dBm, dCm, dDskip, d_dt_bias) are sums in a fixed order, so
- * repeated calls give identical bits.
+ * gradients (dA, dBm, dCm, dDskip, d_dt_bias, dconv_w, dconv_b) are sums in a
+ * fixed order, so repeated calls give identical bits.
  */
 typedef struct {
   int64_t batch, dim, seqlen, dstate;
@@ -262,6 +267,14 @@ typedef struct {
   float* dh0;
   void* workspace;
   size_t workspace_bytes;
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_state_in;
+  float* dconv_w;
+  float* dconv_b;
+  float* dconv_state_in;
+  int32_t conv_width;
+  int32_t reserved0;
 } ssm_scan_bwd_params;
 
 /* Bytes of workspace ssm_scan_bwd needs (only sizes and dtypes of `p` are read). */

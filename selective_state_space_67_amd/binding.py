@@ -69,6 +69,9 @@ class BwdParams(ctypes.Structure):
         ("dA", ctypes.c_void_p), ("dBm", ctypes.c_void_p), ("dCm", ctypes.c_void_p),
         ("dDskip", ctypes.c_void_p), ("d_dt_bias", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
+        ("dconv_w", ctypes.c_void_p), ("dconv_b", ctypes.c_void_p), ("dconv_state_in", ctypes.c_void_p),
+        ("conv_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -361,7 +364,7 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return out
 
 
-def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads):
+def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads, conv=None):
     import torch
 
     Bt, D, L = u.shape
@@ -373,7 +376,7 @@ def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_las
     shapes = dict(du=(Bt, D, L), d_dt_raw=(Bt, D, L), dz=(Bt, D, L), dA=(D, N), dBm=(Bt, L, N), dCm=(Bt, L, N),
                   dDskip=(D,), d_dt_bias=(D,), dh0=(Bt, D, N))
     for k, t in grads.items():
-        if t is not None:
+        if t is not None and k in shapes:
             _need(t, shapes[k], k)
     p = BwdParams()
     p.batch, p.dim, p.seqlen, p.dstate = Bt, D, L, N
@@ -383,7 +386,20 @@ def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_las
     p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     p.reset, p.h0, p.dout, p.dh_last = _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last)
     for k, t in grads.items():
+        if k in ("dconv_w", "dconv_b", "dconv_state_in"):
+            continue
         setattr(p, k, _ptr(t))
+    if conv is not None and conv[0] is not None:
+        conv_w, conv_b, conv_state_in = conv
+        K = conv_w.shape[1]
+        _need(conv_w, (D, K), "conv_w", torch.float32)
+        if conv_b is not None:
+            _need(conv_b, (D,), "conv_b", torch.float32)
+        if conv_state_in is not None:
+            _need(conv_state_in, (Bt, D, K - 1), "conv_state_in", torch.float32)
+        p.conv_w, p.conv_b, p.conv_state_in, p.conv_width = _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in), K
+        p.dconv_w, p.dconv_b = _ptr(grads.get("dconv_w")), _ptr(grads.get("dconv_b"))
+        p.dconv_state_in = _ptr(grads.get("dconv_state_in"))
     return p
 
 
@@ -408,20 +424,29 @@ def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0):
 
 def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                  dh_last=None, grad_dtype=None, want_dDskip=True, want_d_dt_bias=True, want_dh0=True,
-                 workspace=None, stream=None):
+                 conv_w=None, conv_b=None, conv_state_in=None, workspace=None, stream=None):
     """Backward pass of ssm_scan_fwd for the same inputs and the output gradient dout.
 
     Returns a dict with du, d_dt_raw, dz (None without z) in ``grad_dtype``
     (float32 by default), and float32 dA, dBm, dCm, dDskip, d_dt_bias, dh0
     (the last three None when not asked for). dh_last (B, D, N) float32 is the
     gradient reaching h_last (None = 0). The workspace is allocated when not
-    given or too small.
+    given or too small. With conv_w (D, K), u is the conv input and the dict
+    also holds dconv_w (D, K), dconv_b (D,) and dconv_state_in (B, D, K-1).
     """
     import torch
 
     lib = load_library()
     grads = _bwd_grads(u, A, Bm, z, grad_dtype, want_dDskip, want_d_dt_bias, want_dh0)
-    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads)
+    if conv_w is not None:
+        Bt, D, _ = u.shape
+        K = conv_w.shape[1]
+        grads["dconv_w"] = torch.empty((D, K), dtype=torch.float32, device=u.device)
+        grads["dconv_b"] = torch.empty((D,), dtype=torch.float32, device=u.device)
+        grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
+                                   if K > 1 else None)
+    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
+                    (conv_w, conv_b, conv_state_in))
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if workspace is None or workspace.numel() * workspace.element_size() < n.value:

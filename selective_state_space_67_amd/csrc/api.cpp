@@ -102,7 +102,7 @@ struct BwdLayout {
   int nsegb;          // segments of the reverse sweep
   int64_t seg_steps;
   int64_t n_ck;       // 16-step checkpoints
-  size_t off_agg, off_ckpt, off_segP, off_segG, off_part, total;
+  size_t off_agg, off_ckpt, off_segP, off_segG, off_part, off_uconv, off_duconv, off_convpart, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -145,6 +145,15 @@ ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout
   off += align256(static_cast<size_t>(seg) * 4);
   lay->off_part = off;
   off += align256(ssm::bwd_partial_floats(B, D, L, N, lay->nsegb) * 4);
+  lay->off_uconv = lay->off_duconv = lay->off_convpart = off;
+  if (p->conv_w) {  // the conv stage's u' and its gradient, and the conv parameter partials
+    lay->off_uconv = off;
+    off += align256(static_cast<size_t>(sz.bdl) * 4);
+    lay->off_duconv = off;
+    off += align256(static_cast<size_t>(sz.bdl) * 4);
+    lay->off_convpart = off;
+    off += align256(ssm::bwd_conv_partial_floats(B, D, L) * 4);
+  }
   lay->total = off;
   return SSM_OK;
 }
@@ -183,6 +192,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
     if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
   if (p->z && !p->dz) return fail(SSM_ERR_NULL_POINTER, "dz is NULL although z is given");
   if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
+  const int64_t K = p->conv_w ? p->conv_width : 0;
+  if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
+  if (!p->conv_w && (p->conv_b || p->conv_state_in || p->dconv_w || p->dconv_b || p->dconv_state_in))
+    return fail(SSM_ERR_NULL_POINTER, "conv arguments given without conv_w");
+  const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);
 
   const size_t si = dtype_size(p->in_dtype), sg = dtype_size(p->grad_dtype);
   const struct {
@@ -195,7 +209,9 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
                 {p->h0, 4, "h0"},          {p->dh_last, 4, "dh_last"},  {p->du, sg, "du"},
                 {p->d_dt_raw, sg, "d_dt_raw"}, {p->dz, sg, "dz"},       {p->dA, 4, "dA"},
                 {p->dBm, 4, "dBm"},        {p->dCm, 4, "dCm"},          {p->dDskip, 4, "dDskip"},
-                {p->d_dt_bias, 4, "d_dt_bias"}, {p->dh0, 4, "dh0"},     {p->workspace, 16, "workspace"}};
+                {p->d_dt_bias, 4, "d_dt_bias"}, {p->dh0, 4, "dh0"},     {p->workspace, 16, "workspace"},
+                {p->conv_w, 4, "conv_w"},  {p->conv_b, 4, "conv_b"},    {p->conv_state_in, 4, "conv_state_in"},
+                {p->dconv_w, 4, "dconv_w"}, {p->dconv_b, 4, "dconv_b"}, {p->dconv_state_in, 4, "dconv_state_in"}};
   for (const auto& a : aligns)
     if (a.ptr && !aligned(a.ptr, a.align))
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
@@ -212,6 +228,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
       range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
       range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
       range(p->dout, sz.bdl, si, "dout"),    range(p->dh_last, sz.bdn, 4, "dh_last"),
+      range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
+      range(p->conv_state_in, bdk, 4, "conv_state_in"),
   };
   const Range outputs[] = {
       range(p->du, sz.bdl, sg, "du"),        range(p->d_dt_raw, sz.bdl, sg, "d_dt_raw"),
@@ -219,6 +237,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
       range(p->dBm, sz.bln, 4, "dBm"),       range(p->dCm, sz.bln, 4, "dCm"),
       range(p->dDskip, p->dim, 4, "dDskip"), range(p->d_dt_bias, p->dim, 4, "d_dt_bias"),
       range(p->dh0, sz.bdn, 4, "dh0"),
+      range(p->dconv_w, p->dim * K, 4, "dconv_w"), range(p->dconv_b, p->dim, 4, "dconv_b"),
+      range(p->dconv_state_in, bdk, 4, "dconv_state_in"),
       Range{static_cast<const char*>(p->workspace), lay.total, "workspace"},
   };
   constexpr int n_out = sizeof(outputs) / sizeof(outputs[0]);
@@ -259,6 +279,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   sp.seg_steps = lay.seg_steps;
   sp.n_ck = lay.n_ck;
   sp.nsegb = lay.nsegb;
+  sp.conv_w = p->conv_w;
+  sp.conv_b = p->conv_b;
+  sp.conv_state_in = p->conv_state_in;
+  sp.conv_k = static_cast<int>(K);
+  sp.uconv_out = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_uconv) : nullptr;
   hipError_t e = ssm::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint sweep launch failed: %s", hipGetErrorString(e));
 
@@ -296,6 +321,16 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   bp.seg_steps = lay.seg_steps;
   bp.n_ck = lay.n_ck;
   bp.nsegb = lay.nsegb;
+  bp.conv_w = p->conv_w;
+  bp.conv_b = p->conv_b;
+  bp.conv_state_in = p->conv_state_in;
+  bp.conv_k = static_cast<int>(K);
+  bp.uconv = sp.uconv_out;
+  bp.du_conv = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_duconv) : nullptr;
+  bp.conv_part = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_convpart) : nullptr;
+  bp.dconv_w = p->dconv_w;
+  bp.dconv_b = p->dconv_b;
+  bp.dconv_state = K > 1 ? p->dconv_state_in : nullptr;
   e = ssm::launch_scan_bwd(bp, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "reverse sweep launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -46,6 +46,7 @@ struct ScanPlan {
   const float* conv_state_in;  // (B, D, conv_k - 1) or null
   float* conv_state_out;       // (B, D, conv_k - 1) or null
   int conv_k;
+  float* uconv_out;            // checkpoint sweep with conv: writes the scan input u' (B, D, L)
 };
 
 struct UpdatePlan {
@@ -118,6 +119,20 @@ struct BwdPlan {
   int64_t seg_steps;
   int64_t n_ck;
   int nsegb;
+  // Conv stage (conv_w null: none). The reverse sweep then reads the scan
+  // input u' from uconv and writes its gradient to du_conv; a conv backward
+  // turns that into du (the conv input's gradient), dconv_w, dconv_b and
+  // dconv_state.
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_state_in;
+  int conv_k;
+  const float* uconv;
+  float* du_conv;
+  float* conv_part;  // bwd_conv_partial_floats() floats
+  float* dconv_w;
+  float* dconv_b;
+  float* dconv_state;
 };
 
 // Backward segments: how many pieces the reverse sweep splits L into and
@@ -129,6 +144,8 @@ int bwd_channels_per_block(int64_t N);
 size_t bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb);
 // Workgroups of the reverse sweep.
 int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb);
+// Floats of partial sums of the conv backward (per row tile: 4 taps + bias).
+size_t bwd_conv_partial_floats(int64_t B, int64_t D, int64_t L);
 hipError_t launch_scan_bwd(const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace ssm

@@ -94,6 +94,8 @@ struct BwdArgs {
   float* partA;     // (B, nsegb, D, N)
   float* partD;     // (B, nsegb, D)
   float* partBias;  // (B, nsegb, D)
+  const float* uconv;  // conv stage: the scan input u' (B, D, L), read in place of u
+  float* du_conv;      // conv stage: the gradient of u' (B, D, L), written in place of du
 };
 
 // DPP lane permutation within rows of 16 (control word CTRL).
@@ -200,7 +202,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
   float dD_acc = 0.0f, dbias_acc = 0.0f;
 
   struct Raw {
-    InT b[BCI], c[BCI], u[4], dt[4], z[4], go[4];
+    InT b[BCI], c[BCI], dt[4], z[4], go[4];
+    float u[4];
     uint8_t rs[4];
   };
   struct Out {
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       const int t = l + 4 * G;
       const bool ok = fin && dvalid && tc + t < pend;
       const int64_t off = rowbase + tc + t;
-      r.u[G] = ok ? u_in[off] : InT{};
+      r.u[G] = ok ? (a.uconv ? a.uconv[off] : load_elem(u_in, off)) : 0.0f;
       r.dt[G] = ok ? dt_in[off] : InT{};
       r.z[G] = ok && z_in ? z_in[off] : InT{};
       r.go[G] = ok ? go_in[off] : InT{};
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       const bool ok = dvalid && tc + t < pend;
       const float x = load_elem(&r.dt[G], 0) + bias;
       float dl = ok ? softplus_f32(x) : 0.0f;
-      const float uu = load_elem(&r.u[G], 0);
+      const float uu = r.u[G];
       const float go = load_elem(&r.go[G], 0);
       float dy = go, gz = 0.0f;
       if (z_in) {
@@ -396,7 +399,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
           const float du = __builtin_fmaf(dyf, dsk, dlf * F1);
           const float dx = __builtin_fmaf(o.u[G], F1, F2) * o.sig[G];
           const float dz = o.gz[G] * __builtin_fmaf(dsk, o.u[G], FY);
-          store_grad(a, a.du, rowbase + tg, du);
+          if (a.du_conv)
+            a.du_conv[rowbase + tg] = du;  // the conv backward takes it from here
+          else
+            store_grad(a, a.du, rowbase + tg, du);
           store_grad(a, a.ddt, rowbase + tg, dx);
           if (a.dz) store_grad(a, a.dz, rowbase + tg, dz);
           dD_acc = __builtin_fmaf(dyf, o.u[G], dD_acc);
@@ -544,6 +550,147 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const RedArgs r) {
   }
 }
 
+// ---- backward of the causal conv1d + SiLU input stage ----
+//
+// Given du' (the gradient of the scan input u' = silu(pre)), with
+//   pre_t = conv_b + sum_{k<4} w[k] x_{t-3+k}   (taps right-aligned: widths
+//           below 4 have leading zero taps; inputs hidden by a later reset
+//           within the window count as 0),
+// the chain rule gives dpre_t = du'_t silu'(pre_t) and
+//   dx_s      = sum_k w[k] dpre_{s+3-k}       (over taps that see x_s)
+//   dw[k]    += dpre_t x_{t-3+k};  dconv_b += dpre_t;  the terms of s < 0 go to
+//   the initial conv state.
+// One workgroup covers kConvTile steps of one (b, d) row; each thread owns four
+// consecutive steps and recomputes pre for them and the three that follow.
+constexpr int kConvTile = 1024;
+
+struct ConvBwdArgs {
+  int64_t B, D, L;
+  int K, ntiles, grad_bf16;
+  const void* x;
+  const uint8_t* reset;
+  const float* w;
+  const float* bias;
+  const float* state_in;
+  const float* du_conv;
+  void* dx;
+  float* dstate;
+  float* part;  // (B, D, ntiles, 5): four taps and the bias
+};
+
+template <typename InT>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(const ConvBwdArgs a) {
+  const int64_t row = blockIdx.x / a.ntiles;  // b * D + d
+  const int tile = blockIdx.x % a.ntiles;
+  const int64_t d = row % a.D, b = row / a.D;
+  const int K = a.K;
+  float wp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < K; ++k) wp[4 - K + k] = a.w[d * K + k];
+  const float cb = a.bias ? a.bias[d] : 0.0f;
+  const InT* xr = static_cast<const InT*>(a.x) + row * a.L;
+  const float* dur = a.du_conv + row * a.L;
+  const uint8_t* rs = a.reset ? a.reset + b * a.L : nullptr;
+  const int64_t t0 = static_cast<int64_t>(tile) * kConvTile + 4 * threadIdx.x;
+
+  // x_{t0-3} .. x_{t0+6} and the reset flags of t0-3 .. t0+6
+  float xv[10];
+  bool rv[10];
+#pragma unroll
+  for (int j = 0; j < 10; ++j) {
+    const int64_t pos = t0 - 3 + j;
+    float v = 0.0f;
+    if (pos >= 0 && pos < a.L)
+      v = load_elem(xr, pos);
+    else if (pos < 0 && a.state_in && pos >= 1 - K)
+      v = a.state_in[row * (K - 1) + (pos + K - 1)];
+    xv[j] = v;
+    rv[j] = rs && pos >= 0 && pos < a.L && rs[pos];
+  }
+  // tap k of step t0 + i reads x_{t0+i-3+k} = xv[i + k]; it is visible unless a
+  // reset lies in (that input, t0 + i], i.e. at xv indices i+k+1 .. i+3.
+  auto vis = [&](int i, int k) {
+    bool v = true;
+#pragma unroll
+    for (int q = 1; q <= 3; ++q)
+      if (q > k) v = v && !rv[i + q];  // reset flags of t0+i-3+q for q in k+1 .. 3
+    return v;
+  };
+  float dpre[7];
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const int64_t t = t0 + i;
+    float p = cb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (vis(i, k)) p = __builtin_fmaf(wp[k], xv[i + k], p);
+    const float sg = fast_rcp(1.0f + fast_exp2(-p * kLog2e));
+    const float g = t < a.L ? dur[t] : 0.0f;
+    dpre[i] = g * (sg * __builtin_fmaf(p, 1.0f - sg, 1.0f));
+  }
+  float dw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t s = t0 + i;  // the step this thread owns: dx_s and the sums of dpre_s
+    if (s >= a.L) break;
+    float acc = 0.0f;
+    // dpre_{s+3-k} reaches x_s through tap k when x_s is visible from s+3-k
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (vis(i + 3 - k, k)) acc = __builtin_fmaf(wp[k], dpre[i + 3 - k], acc);
+    if (a.grad_bf16)
+      store_elem(static_cast<bf16_t*>(a.dx) + row * a.L, s, acc);
+    else
+      store_elem(static_cast<float*>(a.dx) + row * a.L, s, acc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (vis(i, k)) dw[k] = __builtin_fmaf(dpre[i], xv[i + k], dw[k]);
+    db += dpre[i];
+  }
+  // the initial conv state: inputs x_{-3..-1} feed steps 0..2
+  if (t0 == 0 && a.dstate) {
+    for (int j = 0; j < K - 1; ++j) {
+      const int pos = j - (K - 1);  // -K+1 .. -1
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (i - 3 + k == pos && vis(i, k) && i < a.L) acc = __builtin_fmaf(wp[k], dpre[i], acc);
+      a.dstate[row * (K - 1) + j] = acc;
+    }
+  }
+  // workgroup sums of the tap and bias gradients, in a fixed order
+  __shared__ float red[5][256];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) red[k][threadIdx.x] = dw[k];
+  red[4][threadIdx.x] = db;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off)
+#pragma unroll
+      for (int j = 0; j < 5; ++j) red[j][threadIdx.x] += red[j][threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x < 5) a.part[(row * a.ntiles + tile) * 5 + threadIdx.x] = red[threadIdx.x][0];
+}
+
+// dconv_w[d, k] and dconv_b[d]: the tiles' sums over batch rows and tiles, in order.
+__global__ __launch_bounds__(256) void conv_param_reduce_kernel(int64_t B, int64_t D, int K, int ntiles,
+                                                                const float* part, float* dw, float* db) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= D * 5) return;
+  const int64_t d = i / 5;
+  const int j = static_cast<int>(i % 5);
+  float acc = 0.0f;
+  for (int64_t b = 0; b < B; ++b)
+    for (int t = 0; t < ntiles; ++t) acc += part[((b * D + d) * ntiles + t) * 5 + j];
+  if (j < 4) {
+    if (dw && j >= 4 - K) dw[d * K + (j - (4 - K))] = acc;
+  } else if (db) {
+    db[d] = acc;
+  }
+}
+
 int bwd_lpc(int64_t N) {
   if (N <= 16) return 4;
   if (N <= 32) return 8;
@@ -599,6 +746,10 @@ size_t bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb)
   return static_cast<size_t>(2 * groups * B * L * N + B * nsegb * D * N + 2 * B * nsegb * D);
 }
 
+size_t bwd_conv_partial_floats(int64_t B, int64_t D, int64_t L) {
+  return static_cast<size_t>(B * D * ((L + kConvTile - 1) / kConvTile) * 5);
+}
+
 int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb) {
   return B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N)) * nsegb;
 }
@@ -635,6 +786,8 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   a.ddt = pl.ddt;
   a.dz = pl.dz;
   a.dh0 = pl.dh0;
+  a.uconv = pl.conv_w ? pl.uconv : nullptr;
+  a.du_conv = pl.conv_w ? pl.du_conv : nullptr;
   const int64_t bln = pl.B * pl.L * pl.N;
   a.partB = pl.part;
   a.partC = pl.part + groups * bln;
@@ -679,6 +832,35 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   const int64_t total = 2 * ((r.bln + 3) / 4) + (r.dn + 3) / 4 + 2 * ((r.D + 3) / 4);
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
+  e = hipGetLastError();
+  if (e != hipSuccess || !pl.conv_w) return e;
+
+  ConvBwdArgs c{};
+  c.B = pl.B;
+  c.D = pl.D;
+  c.L = pl.L;
+  c.K = pl.conv_k;
+  c.ntiles = static_cast<int>((pl.L + kConvTile - 1) / kConvTile);
+  c.grad_bf16 = pl.grad_bf16;
+  c.x = pl.u;
+  c.reset = pl.reset;
+  c.w = pl.conv_w;
+  c.bias = pl.conv_b;
+  c.state_in = pl.conv_state_in;
+  c.du_conv = pl.du_conv;
+  c.dx = pl.du;
+  c.dstate = pl.dconv_state;
+  c.part = pl.conv_part;
+  const dim3 cgrid(static_cast<unsigned>(pl.B * pl.D * c.ntiles));
+  if (pl.in_bf16)
+    hipLaunchKernelGGL(conv_bwd_kernel<bf16_t>, cgrid, dim3(256), 0, stream, c);
+  else
+    hipLaunchKernelGGL(conv_bwd_kernel<float>, cgrid, dim3(256), 0, stream, c);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(conv_param_reduce_kernel, dim3(static_cast<unsigned>((pl.D * 5 + 255) / 256)), dim3(256), 0,
+                     stream, pl.B, pl.D, pl.conv_k, c.ntiles, static_cast<const float*>(pl.conv_part), pl.dconv_w,
+                     pl.dconv_b);
   return hipGetLastError();
 }
 

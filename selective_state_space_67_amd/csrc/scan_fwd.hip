@@ -125,6 +125,7 @@ struct ScanArgs {
   const float* conv_state_in;  // (B, D, conv_k - 1) or null
   float* conv_state_out;       // (B, D, conv_k - 1) or null
   int conv_k;                  // 1 .. 4
+  float* uconv_out;            // kCheckpoint with a conv stage: the scan input u' (B, D, L), f32
 };
 
 // Visibility of the conv window's inputs: the window of step Q covers
@@ -410,8 +411,10 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
     for (int i = 0; i < RI; ++i) {
       // Items past the end carry zeros, which make identity steps (delta = 0).
       float uu = load_elem(&r.u[i], 0);
-      if constexpr (CONV)  // the scan input is silu(causal conv of u) at step T0 + i
+      if constexpr (CONV) {  // the scan input is silu(causal conv of u) at step T0 + i
         uu = silu_f32(conv_pre(s_cw, s_cb, xw[i], xw[i + 1], xw[i + 2], xw[i + 3], rr[i + 2], rr[i + 1], rr[i]));
+        if (CKPT && a.uconv_out && sc_valid && tau0 + stl + i < Lseg) a.uconv_out[row0 + tau0 + srow + i] = uu;
+      }
       dl[i] = softplus_f32(load_elem(&r.dt[i], 0) + s_bias);
       if (!sc_valid || tau0 + stl + i >= Lseg) dl[i] = 0.0f;
       dv[i] = dl[i] * uu;
@@ -912,6 +915,7 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.conv_state_in = pl.conv_state_in;
   a.conv_state_out = pl.conv_state_out;
   a.conv_k = pl.conv_k;
+  a.uconv_out = pl.uconv_out;
   const bool ck = pl.checkpoint != 0;
   const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
   a.ws_P = pl.ws;

@@ -325,3 +325,28 @@ def test_scan_conv_arguments(lib):
     p.conv_w, p.conv_width = BASE + 0x60000000, 4
     p.conv_state_out = p.out + 64                   # ... or over out
     assert scan_status(lib, p) == 7
+
+
+def test_bwd_conv_arguments(lib):
+    p = bwd_params()
+    p.dconv_w = BASE + 0x70000000                   # conv gradient without conv_w
+    assert bwd_status(lib, p) == 1
+    p = bwd_params()
+    p.conv_w, p.conv_width = BASE + 0x70000000, 9   # width out of range
+    assert bwd_status(lib, p) == 2
+    p = bwd_params()
+    p.conv_w, p.conv_width = BASE + 0x70000000, 4
+    n = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    p.workspace_bytes = n.value                     # the workspace is the last fake range: it may grow
+    p.dconv_w = p.conv_w                            # gradient over its own weights
+    assert bwd_status(lib, p) == 7
+
+
+def test_bwd_conv_workspace_grows(lib):
+    n0, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p = bwd_params()
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n0)) == 0
+    p.conv_w, p.conv_width = BASE + 0x70000000, 4
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
+    assert n1.value >= n0.value + 2 * B * D * L * 4   # u' and its gradient

@@ -125,3 +125,58 @@ def test_decode_with_conv_state(N, K):
         assert_close(h.cpu().numpy(), h_ref, wl.BF16, what="decode h step %d" % s)
         if K > 1:
             np.testing.assert_array_equal(st_t.cpu().numpy().astype(np.float64), st_ref)
+
+
+def oracle_conv_bwd(x):
+    w = wl.widen
+    return oracle.scan_bwd(w(x["u"]), w(x["dt_raw"]), x["A"], w(x["Bm"]), w(x["Cm"]), w(x["dout"]), z=w(x["z"]),
+                           dt_bias=x["dt_bias"], Dskip=x["Dskip"], reset=x["reset"], h0=None, dh_last=None,
+                           conv_w=x["conv_w"], conv_b=x["conv_b"], conv_state=x["conv_state"])
+
+
+def gpu_conv_bwd(x):
+    import torch
+
+    from selective_state_space_67_amd import ssm_scan_bwd
+
+    dev = device()
+    t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset", "dout")}
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    g = ssm_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], t["dout"], dt_bias=t["dt_bias"],
+                     Dskip=t["Dskip"], z=t["z"], reset=t["reset"], conv_w=f32(x["conv_w"]), conv_b=f32(x["conv_b"]),
+                     conv_state_in=f32(x["conv_state"]))
+    torch.cuda.synchronize()
+    return {k: None if v is None else v.float().cpu().numpy().astype(np.float64) for k, v in g.items()}
+
+
+PAIRS = dict(du="du", d_dt_raw="d_dt_raw", dz="dz", dA="dA", dBm="dB", dCm="dC", dDskip="dD",
+             d_dt_bias="d_dt_bias", dh0="dh0", dconv_w="dconv_w", dconv_b="dconv_b", dconv_state_in="dconv_state")
+
+
+def assert_conv_grads(got, ref, what):
+    for gk, rk in PAIRS.items():
+        o, r = got.get(gk), ref.get(rk)
+        if o is None:
+            assert r is None or r.size == 0 or gk == "dconv_state_in", (what, gk)
+            continue
+        bound = 1e-4 * (np.sqrt(np.mean(r * r)) + np.abs(r)) + 1e-30
+        ratio = np.abs(o - r) / bound
+        if np.any(ratio > 1):
+            i = np.unravel_index(np.argmax(ratio), ratio.shape)
+            raise AssertionError("%s %s: %d outside; worst at %s got %.9g want %.9g" %
+                                 (what, gk, int((ratio > 1).sum()), i, o[i], r[i]))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("K,N,packed", [(4, 16, False), (4, 16, True), (3, 64, True), (1, 16, False),
+                                        (2, 128, True)])
+def test_conv_backward(dtype, K, N, packed):
+    x = conv_case(2, 24, 333, N, K, dtype, 40 + K + N, packed=packed)
+    x["dout"] = wl.store(np.random.default_rng(99).standard_normal(x["u"].shape), dtype)
+    assert_conv_grads(gpu_conv_bwd(x), oracle_conv_bwd(x), "K%d N%d %s" % (K, N, dtype))
+
+
+def test_conv_backward_long_split():
+    x = conv_case(1, 16, 20000, 16, 4, wl.BF16, 61, packed=True, dt_lo=1e-3, dt_hi=1e-2)
+    x["dout"] = wl.store(np.random.default_rng(98).standard_normal(x["u"].shape), wl.BF16)
+    assert_conv_grads(gpu_conv_bwd(x), oracle_conv_bwd(x), "long")
