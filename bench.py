@@ -16,6 +16,8 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
   decode       the single-token decode step (batch 64, 2048 channels, N = 128)
   backward     ssm_scan_bwd on the same workload with a random output gradient
                (checkpoint sweep, reverse sweep and reduction, back to back)
+  conv_stage   the same forward and backward with the fused causal conv1d
+               (width 4) + SiLU input stage, u being the conv input
   cpu_baseline the float64 oracle on the host cores over the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -233,7 +235,30 @@ def main():
     bsec = e0.elapsed_time(e1) / bsteps / 1e3
     bbytes = backward_bytes(B, D, L, N, s_in, 4, reset=x["reset"] is not None)
     bops = BWD_OPS_PER_ELEMENT * elements + BWD_OPS_PER_ROW_STEP * B * D * L
-    del bwd, dout
+
+    # Fused conv1d (width 4) + SiLU input stage, forward and backward.
+    rc = np.random.default_rng(4321)
+    cw = torch.from_numpy((rc.standard_normal((D, 4)) * 0.5).astype(np.float32)).to(dev)
+    cb = torch.from_numpy((rc.standard_normal(D) * 0.2).astype(np.float32)).to(dev)
+    fconv = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                                 Dskip=t["Dskip"], z=t["z"], reset=t["reset"], conv_w=cw, conv_b=cb)
+    bconv = binding.prepare_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dout, dt_bias=t["dt_bias"],
+                                     Dskip=t["Dskip"], z=t["z"], reset=t["reset"], conv_w=cw, conv_b=cb)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(n):
+            fn()
+        s1.record(stream)
+        s1.synchronize()
+        return s0.elapsed_time(s1) / n / 1e3
+
+    csec_f = timed(fconv, max(5, min(args.steps, 50)))
+    csec_b = timed(bconv, bsteps)
+    del bwd, dout, fconv, bconv
 
     result = {
         "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
@@ -279,6 +304,11 @@ def main():
                      "algorithmic_bytes": bbytes, "hbm_gbps": bbytes / bsec / 1e9,
                      "algorithmic_ops": bops, "alu_frac": bops / bsec / 1e12 / ALU_PEAK_TOPS,
                      "vs_forward": bsec / launch_s},
+        "conv_stage": {"workload": "the same scan with u = silu(causal depthwise conv1d of width 4 + bias)",
+                       "fwd_ms": csec_f * 1e3, "fwd_vs_plain_forward": csec_f / launch_s,
+                       "fwd_elements_per_s": elements / csec_f, "bwd_ms": csec_b * 1e3,
+                       "bwd_vs_plain_backward": csec_b / bsec,
+                       "hbm_bytes_saved_by_fusion": B * D * L * (s_in + 4)},
     }
 
     if not args.no_cpu:

@@ -458,7 +458,7 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
 
 
 def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
-                     dh_last=None, grad_dtype=None, stream=None):
+                     dh_last=None, grad_dtype=None, conv_w=None, conv_b=None, conv_state_in=None, stream=None):
     """Marshal the arguments of ssm_scan_bwd once; returns a no-argument callable
     that enqueues the same backward pass again each time it is called and
     returns the gradient dict (the same tensors every time)."""
@@ -466,7 +466,15 @@ def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=
 
     lib = load_library()
     grads = _bwd_grads(u, A, Bm, z, grad_dtype, True, True, True)
-    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads)
+    if conv_w is not None:
+        Bt, D, _ = u.shape
+        K = conv_w.shape[1]
+        grads["dconv_w"] = torch.empty((D, K), dtype=torch.float32, device=u.device)
+        grads["dconv_b"] = torch.empty((D,), dtype=torch.float32, device=u.device)
+        grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
+                                   if K > 1 else None)
+    p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
+                    (conv_w, conv_b, conv_state_in))
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
@@ -480,5 +488,6 @@ def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=
         _check(fn(pref, st))
         return grads
 
-    call.keep = ((u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, ws), p)
+    call.keep = ((u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, conv_w, conv_b, conv_state_in,
+                  ws), p)
     return call
