@@ -55,7 +55,8 @@ OPS_PER_ROW_STEP = 18.0
 # du, d dt_raw, dz, dD and d dt_bias (8) = 29.
 BWD_OPS_PER_ELEMENT = 16.0
 BWD_OPS_PER_ROW_STEP = 29.0
-SCAN_SOURCES = ["selective_state_space_67_amd/csrc/scan_fwd.hip",
+SCAN_SOURCES = ["selective_state_space_67_amd/csrc/scan_fwd_kernel.h",
+                "selective_state_space_67_amd/csrc/scan_fwd.hip",
                 "selective_state_space_67_amd/csrc/device_math.h"]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
