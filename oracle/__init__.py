@@ -45,13 +45,13 @@ def _load():
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_scan_rows.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p, p,
-                                         ctypes.c_int]
+                                         ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_rows.restype = None
         lib.oracle_state_update.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p,
-                                            ctypes.c_int]
+                                            ctypes.c_int, ctypes.c_int]
         lib.oracle_state_update.restype = None
         lib.oracle_max_threads.restype = ctypes.c_int
-        lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
+        lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
         lib.oracle_conv_silu_rows.argtypes = [i64, i64, i64] + [p] * 10 + [ctypes.c_int]
         lib.oracle_conv_silu_rows.restype = None
@@ -76,7 +76,7 @@ def _ptr(x):
 
 
 def scan_rows(rows_b, rows_d, u_rows, dt_rows, A, Bm, Cm, *, z_rows=None, dt_bias=None,
-              Dskip=None, reset=None, h0_rows=None, want_h_last=False, nthreads=0):
+              Dskip=None, reset=None, h0_rows=None, want_h_last=False, zoh=False, nthreads=0):
     """Run the recurrence on selected (b, d) rows over the full sequence.
 
     rows_b, rows_d : (R,) int   batch and channel of each row
@@ -109,7 +109,7 @@ def scan_rows(rows_b, rows_d, u_rows, dt_rows, A, Bm, Cm, *, z_rows=None, dt_bia
     h_last = np.empty((R, N), dtype=np.float64) if want_h_last else None
     lib.oracle_scan_rows(R, L, N, _ptr(rows_b), _ptr(rows_d), _ptr(u_rows), _ptr(dt_rows),
                          _ptr(z_rows), _ptr(dt_bias), _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm),
-                         _ptr(reset), _ptr(h0_rows), _ptr(out), _ptr(h_last), int(nthreads))
+                         _ptr(reset), _ptr(h0_rows), _ptr(out), _ptr(h_last), int(bool(zoh)), int(nthreads))
     return (out, h_last) if want_h_last else out
 
 
@@ -167,7 +167,8 @@ def conv_silu_bwd(x, w, du, pre, *, reset=None, state_in=None, nthreads=0):
 
 
 def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-         want_h_last=False, conv_w=None, conv_b=None, conv_state=None, want_conv_state=False, nthreads=0):
+         want_h_last=False, conv_w=None, conv_b=None, conv_state=None, want_conv_state=False, zoh=False,
+         nthreads=0):
     """Full scan. u, dt_raw, z: (B, D, L); h0: (B, D, N). Returns out (B, D, L).
 
     With conv_w (D, K) the scan input is silu(causal_conv1d(u)) (see conv_silu);
@@ -178,7 +179,7 @@ def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, 
         u, cst = conv_silu(u, conv_w, bias=conv_b, reset=reset, state_in=conv_state, want_state=True,
                            nthreads=nthreads)
         res = scan(u, dt_raw, A, Bm, Cm, z=z, dt_bias=dt_bias, Dskip=Dskip, reset=reset, h0=h0,
-                   want_h_last=want_h_last, nthreads=nthreads)
+                   want_h_last=want_h_last, zoh=zoh, nthreads=nthreads)
         if not want_conv_state:
             return res
         return (res + (cst,)) if want_h_last else (res, cst)
@@ -190,7 +191,7 @@ def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, 
                     z_rows=None if z is None else np.asarray(z).reshape(Bt * D, L),
                     dt_bias=dt_bias, Dskip=Dskip, reset=reset,
                     h0_rows=None if h0 is None else np.asarray(h0).reshape(Bt * D, N),
-                    want_h_last=want_h_last, nthreads=nthreads)
+                    want_h_last=want_h_last, zoh=zoh, nthreads=nthreads)
     if want_h_last:
         out, hl = res
         return out.reshape(Bt, D, L), hl.reshape(Bt, D, N)
@@ -198,7 +199,7 @@ def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, 
 
 
 def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, conv_w=None, conv_b=None,
-                 conv_state=None, nthreads=0):
+                 conv_state=None, zoh=False, nthreads=0):
     """Decode step. h: (B, D, N); u, dt_raw, z: (B, D); Bm, Cm: (B, N).
 
     Returns (out (B, D), h_new (B, D, N)); the input h is not modified. With
@@ -216,7 +217,8 @@ def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, c
         window = np.concatenate([st, x[:, :, None]], axis=2)
         pre = np.einsum("bdk,dk->bd", window, conv_w) + (0.0 if conv_b is None else _f64(conv_b)[None, :])
         uc = pre / (1.0 + np.exp(-pre))
-        out, h_new = state_update(h, uc, dt_raw, A, Bm, Cm, z=z, dt_bias=dt_bias, Dskip=Dskip, nthreads=nthreads)
+        out, h_new = state_update(h, uc, dt_raw, A, Bm, Cm, z=z, dt_bias=dt_bias, Dskip=Dskip, zoh=zoh,
+                                  nthreads=nthreads)
         return out, h_new, np.ascontiguousarray(window[:, :, 1:])
     lib = _load()
     h_new = np.array(h, dtype=np.float64, copy=True, order="C")
@@ -229,12 +231,12 @@ def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, c
     assert Bm.shape == (Bt, N) and Cm.shape == (Bt, N)
     out = np.empty((Bt, D), dtype=np.float64)
     lib.oracle_state_update(Bt, D, N, _ptr(h_new), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
-                            _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(out), int(nthreads))
+                            _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(out), int(bool(zoh)), int(nthreads))
     return out, h_new
 
 
 def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-             dh_last=None, conv_w=None, conv_b=None, conv_state=None, nthreads=0):
+             dh_last=None, conv_w=None, conv_b=None, conv_state=None, zoh=False, nthreads=0):
     """Gradients of sum(dout * out) + sum(dh_last * h_last) for the full scan.
 
     u, dt_raw, z, dout: (B, D, L); A: (D, N); Bm, Cm: (B, L, N); dt_bias, Dskip: (D,);
@@ -249,7 +251,7 @@ def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, re
         uc, pre = conv_silu(u, conv_w, bias=conv_b, reset=reset, state_in=conv_state, want_pre=True,
                             nthreads=nthreads)
         g = scan_bwd(uc, dt_raw, A, Bm, Cm, dout, z=z, dt_bias=dt_bias, Dskip=Dskip, reset=reset, h0=h0,
-                     dh_last=dh_last, nthreads=nthreads)
+                     dh_last=dh_last, zoh=zoh, nthreads=nthreads)
         cg = conv_silu_bwd(u, conv_w, g["du"], pre, reset=reset, state_in=conv_state, nthreads=nthreads)
         g["du"] = cg["dx"]
         g["dconv_w"], g["dconv_b"], g["dconv_state"] = cg["dw"], cg["dbias"], cg["dstate_in"]
@@ -278,7 +280,7 @@ def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, re
         Bt * D, L, N, Bt, D, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
         _ptr(A), _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last),
         _ptr(out["du"]), _ptr(out["d_dt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dD"]),
-        _ptr(out["d_dt_bias"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(nthreads))
+        _ptr(out["d_dt_bias"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(bool(zoh)), int(nthreads))
     if rc != 0:
         raise MemoryError("oracle backward: scratch allocation failed")
     return out

@@ -60,11 +60,21 @@ static double silu(double x) {
   return x / (1.0 + exp(-x));
 }
 
+/* Coefficient of B*u in the discretised input: delta (the small-delta form,
+ * zoh = 0) or the exact zero-order hold (e^{delta A} - 1) / A (zoh = 1), whose
+ * limit at A = 0 is delta ("Illustrated Mamba state space model", section
+ * "Mathematical basis: structured SSM": Bbar = (delta A)^-1 (exp(delta A) - I) delta B,
+ * which for a diagonal A is (exp(delta A) - 1) / A * B per state). */
+static double bcoef(double delta, double A, int zoh) {
+  if (!zoh || A == 0.0) return delta;
+  return expm1(delta * A) / A;
+}
+
 /* One step of the recurrence for one (b, d) row. h has N entries and is
  * updated in place; returns the gated output for this step. */
 static double step(int64_t N, double dt_raw, double bias, const double* A_row,
                    const double* B_t, const double* C_t, double Dskip, double u,
-                   int has_z, double z, int reset, double* h) {
+                   int has_z, double z, int reset, int zoh, double* h) {
   double delta = softplus(dt_raw + bias);
   double y = 0.0;
   if (reset) {
@@ -72,7 +82,7 @@ static double step(int64_t N, double dt_raw, double bias, const double* A_row,
   }
   for (int64_t n = 0; n < N; ++n) {
     double abar = exp(delta * A_row[n]);
-    double bbar = delta * B_t[n];
+    double bbar = bcoef(delta, A_row[n], zoh) * B_t[n];
     h[n] = abar * h[n] + bbar * u;
     y += C_t[n] * h[n];
   }
@@ -101,7 +111,7 @@ void oracle_scan_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b,
                       const double* z, const double* dt_bias, const double* A,
                       const double* Dskip, const double* Bm, const double* Cm,
                       const uint8_t* reset, const double* h0, double* out,
-                      double* h_last, int nthreads) {
+                      double* h_last, int zoh, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -119,7 +129,7 @@ void oracle_scan_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b,
       const int64_t bt = b * L + t;
       out[r * L + t] = step(N, dt_raw[r * L + t], bias, A + d * N, Bm + bt * N,
                             Cm + bt * N, dsk, u[r * L + t], z != NULL,
-                            z ? z[r * L + t] : 0.0, reset ? reset[bt] != 0 : 0, h);
+                            z ? z[r * L + t] : 0.0, reset ? reset[bt] != 0 : 0, zoh, h);
     }
     if (h_last)
       for (int64_t n = 0; n < N; ++n) h_last[r * N + n] = h[n];
@@ -139,7 +149,7 @@ void oracle_scan_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b,
 void oracle_state_update(int64_t Bt, int64_t Dt, int64_t N, double* h,
                          const double* u, const double* dt_raw, const double* z,
                          const double* dt_bias, const double* A, const double* Dskip,
-                         const double* Bm, const double* Cm, double* out, int nthreads) {
+                         const double* Bm, const double* Cm, double* out, int zoh, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -150,7 +160,7 @@ void oracle_state_update(int64_t Bt, int64_t Dt, int64_t N, double* h,
     const int64_t b = r / Dt, d = r % Dt;
     out[r] = step(N, dt_raw[r], dt_bias ? dt_bias[d] : 0.0, A + d * N, Bm + b * N,
                   Cm + b * N, Dskip ? Dskip[d] : 0.0, u[r], z != NULL, z ? z[r] : 0.0,
-                  0, h + r * N);
+                  0, zoh, h + r * N);
   }
 }
 
@@ -209,7 +219,7 @@ int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t 
                          const uint8_t* reset, const double* h0, const double* dout,
                          const double* dh_last, double* du, double* d_dt_raw, double* dz,
                          double* dA, double* dD, double* d_dt_bias, double* dB, double* dC,
-                         double* dh0, int nthreads) {
+                         double* dh0, int zoh, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
   const int T = omp_get_max_threads();
@@ -259,7 +269,7 @@ int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t 
           double y = 0.0;
           for (int64_t n = 0; n < N; ++n) {
             const double hp = rs ? 0.0 : hist[t * N + n];
-            const double h = exp(delta * Ad[n]) * hp + delta * Bm[bt * N + n] * uu;
+            const double h = exp(delta * Ad[n]) * hp + bcoef(delta, Ad[n], zoh) * Bm[bt * N + n] * uu;
             hist[(t + 1) * N + n] = h;
             y += Cm[bt * N + n] * h;
           }
@@ -285,12 +295,23 @@ int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t 
             const double Bn = Bm[bt * N + n], Cn = Cm[bt * N + n];
             const double hp = rs ? 0.0 : hist[t * N + n];
             const double a = exp(delta * Ad[n]);
+            /* input coefficient phi and its derivatives: phi = delta (d/d delta = 1)
+             * or (e^{delta A} - 1)/A (d/d delta = a; d/dA = (delta a A - expm1(delta A))/A^2,
+             * evaluated by its series delta^2 (1/2 + x/3 + x^2/8 + x^3/30) for |x| < 1e-3) */
+            const double phi = bcoef(delta, Ad[n], zoh);
+            double dphi_dd = 1.0, dphi_dA = 0.0;
+            if (zoh) {
+              const double x = delta * Ad[n];
+              dphi_dd = a;
+              dphi_dA = fabs(x) < 1e-3 ? delta * delta * (0.5 + x * (1.0 / 3.0 + x * (0.125 + x / 30.0)))
+                                       : (delta * a * Ad[n] - expm1(x)) / (Ad[n] * Ad[n]);
+            }
             g[n] += dy * Cn;
             mC[bt * N + n] += dy * hist[(t + 1) * N + n];
-            mB[bt * N + n] += g[n] * delta * uu;
-            mA[d * N + n] += g[n] * hp * a * delta;
-            ddelta += g[n] * (hp * a * Ad[n] + Bn * uu);
-            du_t += g[n] * delta * Bn;
+            mB[bt * N + n] += g[n] * phi * uu;
+            mA[d * N + n] += g[n] * (hp * a * delta + Bn * uu * dphi_dA);
+            ddelta += g[n] * (hp * a * Ad[n] + Bn * uu * dphi_dd);
+            du_t += g[n] * phi * Bn;
             g[n] = rs ? 0.0 : g[n] * a;
           }
           du[r * L + t] = du_t;
