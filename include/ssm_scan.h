@@ -79,6 +79,16 @@ typedef enum {
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
+/* How the input matrix is discretised (the `discretization` field):
+ *  SSM_DISC_DELTA_B  Bbar = delta * B, the small-delta form ("Illustrated Mamba
+ *                    state space model", step 1; "Mamba SSM core theory and
+ *                    Keras/TensorFlow implementation", scan step). Default.
+ *  SSM_DISC_ZOH      Bbar = (exp(delta A) - 1) / A * B, the exact zero-order hold
+ *                    of the diagonal continuous system (first page, "Mathematical
+ *                    basis: structured SSM"); delta * B where A = 0.
+ * Abar = exp(delta A) in both. Other values return SSM_ERR_UNSUPPORTED. */
+typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
+
 /*
  * Full-sequence scan (prefill / training forward).
  *
@@ -136,7 +146,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int32_t num_segments;
-  int32_t reserved0;
+  int32_t discretization; /* ssm_discretization */
   const float* conv_w;
   const float* conv_b;
   const float* conv_state_in;
@@ -190,7 +200,7 @@ typedef struct {
   const float* conv_w;
   const float* conv_b;
   int32_t conv_width;
-  int32_t reserved0;
+  int32_t discretization; /* ssm_discretization */
 } ssm_update_params;
 
 /* Enqueue the decode step described by `p` on `hip_stream`. */
@@ -274,7 +284,7 @@ typedef struct {
   float* dconv_b;
   float* dconv_state_in;
   int32_t conv_width;
-  int32_t reserved0;
+  int32_t discretization; /* ssm_discretization */
 } ssm_scan_bwd_params;
 
 /* Bytes of workspace ssm_scan_bwd needs (only sizes and dtypes of `p` are read). */

@@ -16,6 +16,8 @@ _LIB_NAME = "libssmscan.so"
 
 SSM_F32 = 0
 SSM_BF16 = 1
+SSM_DISC_DELTA_B = 0
+SSM_DISC_ZOH = 1
 
 STATUS_NAMES = {
     0: "SSM_OK", 1: "SSM_ERR_NULL_POINTER", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
@@ -39,7 +41,7 @@ class ScanParams(ctypes.Structure):
         ("Dskip", ctypes.c_void_p), ("z", ctypes.c_void_p), ("reset", ctypes.c_void_p),
         ("h0", ctypes.c_void_p), ("out", ctypes.c_void_p), ("h_last", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("num_segments", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32), ("discretization", ctypes.c_int32),
         ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
         ("conv_state_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ]
@@ -53,7 +55,7 @@ class UpdateParams(ctypes.Structure):
         ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("A", ctypes.c_void_p),
         ("Dskip", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("conv_state", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
-        ("conv_b", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("conv_b", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("discretization", ctypes.c_int32),
     ]
 
 
@@ -71,7 +73,7 @@ class BwdParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
         ("dconv_w", ctypes.c_void_p), ("dconv_b", ctypes.c_void_p), ("dconv_state_in", ctypes.c_void_p),
-        ("conv_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32), ("discretization", ctypes.c_int32),
     ]
 
 
@@ -158,7 +160,7 @@ def _stream(stream, device):
 
 
 def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                 num_segments, conv_w=None, conv_b=None, conv_state_in=None, conv_state_out=None):
+                 num_segments, conv_w=None, conv_b=None, conv_state_in=None, conv_state_out=None, zoh=False):
     import torch
 
     Bt, D, L = u.shape
@@ -191,6 +193,7 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
     p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     p.reset, p.h0, p.out, p.h_last = _ptr(reset), _ptr(h0), _ptr(out), _ptr(h_last)
     p.num_segments = int(num_segments)
+    p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
     if conv_w is not None:
         K = conv_w.shape[1]
         _need(conv_w, (D, K), "conv_w", torch.float32)
@@ -223,12 +226,13 @@ def ssm_scan_workspace_size(u, A, *, num_segments=0, out_dtype=None):
 
 def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                  out=None, h_last=None, out_dtype=None, workspace=None, num_segments=0, conv_w=None, conv_b=None,
-                 conv_state_in=None, conv_state_out=None, stream=None):
+                 conv_state_in=None, conv_state_out=None, zoh=False, stream=None):
     """Selective scan over the whole sequence; returns ``out`` (B, D, L).
 
     With conv_w (D, K <= 4) float32, u is the input of a causal depthwise
     conv1d + SiLU stage whose output feeds the scan (conv_b (D,),
-    conv_state_in / conv_state_out (B, D, K-1) float32 optional).
+    conv_state_in / conv_state_out (B, D, K-1) float32 optional). zoh=True
+    selects the exact zero-order-hold input coefficient (e^{delta A} - 1) / A.
 
     u, dt_raw, z: (B, D, L) float32 or bfloat16; A: (D, N) float32;
     Bm, Cm: (B, L, N) same dtype as u; dt_bias, Dskip: (D,) float32;
@@ -243,7 +247,7 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if n.value:
@@ -257,7 +261,7 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
 
 def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None, out=None,
                  h_last=None, out_dtype=None, num_segments=0, conv_w=None, conv_b=None, conv_state_in=None,
-                 conv_state_out=None, stream=None):
+                 conv_state_out=None, zoh=False, stream=None):
     """Marshal the arguments of ssm_scan_fwd once; returns a no-argument callable
     that enqueues the same scan again (same tensors, same stream) each time it is
     called. The tensors must stay alive and unchanged in shape while it is used."""
@@ -267,7 +271,7 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, conv_w, conv_b, conv_state_in,
@@ -290,7 +294,7 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
 
 
 def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                         out_dtype=None, stream=None):
+                         out_dtype=None, zoh=False, stream=None):
     """Marshal the arguments of ssm_state_update once; returns a no-argument
     callable that enqueues the same decode step again each time it is called
     (updating h in place every time)."""
@@ -300,7 +304,7 @@ def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z
     Bt, D, N = h.shape
     if out is None:
         out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
-    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, zoh=zoh)
     st = _stream(stream, u.device)
     fn = lib.ssm_state_update
     pref = ctypes.byref(p)
@@ -313,7 +317,8 @@ def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z
     return call
 
 
-def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None, conv_b=None, conv_state=None):
+def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None, conv_b=None, conv_state=None,
+                   zoh=False):
     import torch
 
     Bt, D, N = h.shape
@@ -336,6 +341,7 @@ def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None,
     p.h, p.u, p.dt_raw, p.z = _ptr(h), _ptr(u), _ptr(dt_raw), _ptr(z)
     p.dt_bias, p.A, p.Dskip = _ptr(dt_bias), _ptr(A), _ptr(Dskip)
     p.Bm, p.Cm, p.out = _ptr(Bm), _ptr(Cm), _ptr(out)
+    p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
     if conv_w is not None:
         K = conv_w.shape[1]
         _need(conv_w, (D, K), "conv_w", torch.float32)
@@ -348,7 +354,7 @@ def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None,
 
 
 def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                     out_dtype=None, conv_w=None, conv_b=None, conv_state=None, stream=None):
+                     out_dtype=None, conv_w=None, conv_b=None, conv_state=None, zoh=False, stream=None):
     """Decode step: updates h (B, D, N) float32 in place and returns out (B, D).
 
     With conv_w (D, K), u is this step's conv input and conv_state
@@ -359,12 +365,12 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     Bt, D, N = h.shape
     if out is None:
         out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
-    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w, conv_b, conv_state)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w, conv_b, conv_state, zoh)
     _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
     return out
 
 
-def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads, conv=None):
+def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads, conv=None, zoh=False):
     import torch
 
     Bt, D, L = u.shape
@@ -385,6 +391,7 @@ def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_las
     p.u, p.dt_raw, p.dt_bias, p.A = _ptr(u), _ptr(dt_raw), _ptr(dt_bias), _ptr(A)
     p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     p.reset, p.h0, p.dout, p.dh_last = _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last)
+    p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
     for k, t in grads.items():
         if k in ("dconv_w", "dconv_b", "dconv_state_in"):
             continue
@@ -424,7 +431,7 @@ def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0):
 
 def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                  dh_last=None, grad_dtype=None, want_dDskip=True, want_d_dt_bias=True, want_dh0=True,
-                 conv_w=None, conv_b=None, conv_state_in=None, workspace=None, stream=None):
+                 conv_w=None, conv_b=None, conv_state_in=None, zoh=False, workspace=None, stream=None):
     """Backward pass of ssm_scan_fwd for the same inputs and the output gradient dout.
 
     Returns a dict with du, d_dt_raw, dz (None without z) in ``grad_dtype``
@@ -446,7 +453,7 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
         grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
                                    if K > 1 else None)
     p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
-                    (conv_w, conv_b, conv_state_in))
+                    (conv_w, conv_b, conv_state_in), zoh)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if workspace is None or workspace.numel() * workspace.element_size() < n.value:
@@ -458,7 +465,8 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
 
 
 def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
-                     dh_last=None, grad_dtype=None, conv_w=None, conv_b=None, conv_state_in=None, stream=None):
+                     dh_last=None, grad_dtype=None, conv_w=None, conv_b=None, conv_state_in=None, zoh=False,
+                     stream=None):
     """Marshal the arguments of ssm_scan_bwd once; returns a no-argument callable
     that enqueues the same backward pass again each time it is called and
     returns the gradient dict (the same tensors every time)."""
@@ -474,7 +482,7 @@ def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=
         grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
                                    if K > 1 else None)
     p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
-                    (conv_w, conv_b, conv_state_in))
+                    (conv_w, conv_b, conv_state_in), zoh)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)

@@ -35,6 +35,7 @@ ssm_status ok() {
 }
 
 bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
+bool valid_disc(int32_t t) { return t == SSM_DISC_DELTA_B || t == SSM_DISC_ZOH; }
 size_t dtype_size(int32_t t) { return t == SSM_BF16 ? 2 : 4; }
 
 // a * b without overflow for non-negative operands.
@@ -118,7 +119,7 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_params* p, ScanSizes* sz) {
 
 ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout* lay) {
   const int64_t B = p->batch, D = p->dim, L = p->seqlen, N = p->dstate;
-  ssm::plan_bwd_segments(B, D, L, N, &lay->nsegb, &lay->seg_steps);
+  ssm::plan_bwd_segments(B, D, L, N, p->discretization == SSM_DISC_ZOH, &lay->nsegb, &lay->seg_steps);
   int nseg;
   int64_t seg_len;
   ssm::plan_segments(B, D, L, N, 0, &nseg, &seg_len);
@@ -169,6 +170,8 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params* p, size_t* byt
   if (s != SSM_OK) return s;
   if (!valid_dtype(p->in_dtype) || !valid_dtype(p->grad_dtype))
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
+  if (!valid_disc(p->discretization))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
   BwdLayout lay;
   if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
   *bytes = lay.total;
@@ -192,6 +195,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
     if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
   if (p->z && !p->dz) return fail(SSM_ERR_NULL_POINTER, "dz is NULL although z is given");
   if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
+  if (!valid_disc(p->discretization))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->dconv_w || p->dconv_b || p->dconv_state_in))
@@ -284,6 +289,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   sp.conv_state_in = p->conv_state_in;
   sp.conv_k = static_cast<int>(K);
   sp.uconv_out = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_uconv) : nullptr;
+  sp.zoh = p->discretization == SSM_DISC_ZOH;
   hipError_t e = ssm::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint sweep launch failed: %s", hipGetErrorString(e));
 
@@ -331,6 +337,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   bp.dconv_w = p->dconv_w;
   bp.dconv_b = p->dconv_b;
   bp.dconv_state = K > 1 ? p->dconv_state_in : nullptr;
+  bp.zoh = p->discretization == SSM_DISC_ZOH;
   e = ssm::launch_scan_bwd(bp, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "reverse sweep launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -367,6 +374,8 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
     if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
 
   const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
+  if (!valid_disc(p->discretization))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
@@ -448,6 +457,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.conv_state_in = p->conv_state_in;
   plan.conv_state_out = p->conv_state_out;
   plan.conv_k = static_cast<int>(K);
+  plan.zoh = p->discretization == SSM_DISC_ZOH;
   hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -491,6 +501,8 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
                           range(p->z, bd, si, "z"),         range(p->dt_bias, p->dim, 4, "dt_bias"),
                           range(p->A, dn, 4, "A"),          range(p->Dskip, p->dim, 4, "Dskip"),
                           range(p->Bm, bn, si, "Bm"),       range(p->Cm, bn, si, "Cm")};
+  if (!valid_disc(p->discretization))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state))
@@ -534,6 +546,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   plan.conv_w = p->conv_w;
   plan.conv_b = p->conv_b;
   plan.conv_k = static_cast<int>(K);
+  plan.zoh = p->discretization == SSM_DISC_ZOH;
   hipError_t e = ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "state update launch failed: %s", hipGetErrorString(e));
   return ok();

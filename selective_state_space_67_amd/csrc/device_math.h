@@ -54,6 +54,36 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
 }
 
+// Input coefficient of the exact zero-order hold: Bbar = (e^{delta A} - 1) / A * B
+// for a diagonal A ("Illustrated Mamba state space model", "Mathematical
+// basis: structured SSM"). With x = delta A and abar = e^x already computed:
+// for |x| >= 1/16 it is (abar - 1) / A (one FMA with the precomputed 1/A; the
+// relative error of abar - 1 is at most ~2e-6 there); below that, where
+// abar - 1 would cancel, the series delta (1 + x/2 + x^2/6 + x^3/24), whose
+// truncation is below 1.3e-7 relative. A = 0 gives x = 0 and the series' delta.
+__device__ __forceinline__ float zoh_coef(float delta, float x, float abar, float invA) {
+  const float series = delta * __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f),
+                                              1.0f);
+  const float direct = __builtin_fmaf(abar, invA, -invA);
+  return fabsf(x) < 0.0625f ? series : direct;
+}
+
+// Derivative of the zero-order-hold coefficient with respect to A, divided by
+// delta^2: psi(x) = (x e^x - e^x + 1) / x^2 with x = delta A and abar = e^x.
+// For |x| < 1/2 the series sum_k (k+1)/(k+2)! x^k through x^7 (truncation
+// below 1e-8); above, the closed form, whose numerator no longer cancels.
+__device__ __forceinline__ float zoh_psi(float x, float abar) {
+  float s = __builtin_fmaf(x, 1.0f / 45360.0f, 1.0f / 5760.0f);
+  s = __builtin_fmaf(x, s, 1.0f / 840.0f);
+  s = __builtin_fmaf(x, s, 1.0f / 144.0f);
+  s = __builtin_fmaf(x, s, 1.0f / 30.0f);
+  s = __builtin_fmaf(x, s, 0.125f);
+  s = __builtin_fmaf(x, s, 1.0f / 3.0f);
+  s = __builtin_fmaf(x, s, 0.5f);
+  const float direct = __builtin_fmaf(x, abar, 1.0f - abar) * fast_rcp(x * x);
+  return fabsf(x) < 0.5f ? s : direct;
+}
+
 // Value of the lane one below within the same row of 16 lanes (DPP
 // row_shr:1); lane 0 of each row reads 0.
 __device__ __forceinline__ float row_shr1(float v) {

@@ -47,6 +47,7 @@ struct ScanPlan {
   float* conv_state_out;       // (B, D, conv_k - 1) or null
   int conv_k;
   float* uconv_out;            // checkpoint sweep with conv: writes the scan input u' (B, D, L)
+  int zoh;                     // 1: exact zero-order-hold Bbar; 0: delta * B
 };
 
 struct UpdatePlan {
@@ -66,6 +67,7 @@ struct UpdatePlan {
   const float* conv_w;  // (D, conv_k) or null
   const float* conv_b;  // (D) or null
   int conv_k;
+  int zoh;              // 1: exact zero-order-hold Bbar; 0: delta * B
 };
 
 // Largest supported state size.
@@ -133,11 +135,12 @@ struct BwdPlan {
   float* dconv_w;
   float* dconv_b;
   float* dconv_state;
+  int zoh;  // 1: exact zero-order-hold Bbar; 0: delta * B
 };
 
 // Backward segments: how many pieces the reverse sweep splits L into and
 // their length (a multiple of 16). Pure host arithmetic.
-void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps);
+void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, bool zoh, int* nsegb, int64_t* seg_steps);
 // Channels one reverse-sweep workgroup covers.
 int bwd_channels_per_block(int64_t N);
 // Floats of partial sums the reverse sweep writes and the reduction reads.

@@ -98,6 +98,13 @@ struct BwdArgs {
   float* du_conv;      // conv stage: the gradient of u' (B, D, L), written in place of du
 };
 
+// Zero-order hold (ZOH kernels): the input term is phi B u with
+// phi = (e^{delta A} - 1) / A in place of delta, so
+//   d phi / d delta = abar (the decay before any reset masking),
+//   d phi / d A     = delta^2 psi(delta A),
+// du = dy D + sum_n g phi B, d delta = S2 + u sum_n g B abar, and dA gains
+// g B u delta^2 psi; dB is g u phi.
+
 // DPP lane permutation within rows of 16 (control word CTRL).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -123,8 +130,10 @@ __device__ __forceinline__ void store_grad(const BwdArgs& a, void* p, int64_t i,
     store_elem(static_cast<float*>(p), i, v);
 }
 
-template <typename TL, typename InT, bool HAS_RESET>
-__global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) {
+// Two waves per SIMD; the zero-order-hold variant's extra per-state terms need
+// more registers than that allows without spilling, so it runs at one.
+template <typename TL, typename InT, bool HAS_RESET, bool ZOH>
+__global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const BwdArgs a) {
   constexpr int LPC = TL::LPC, NPADC = TL::NPADC, CPWAVE = TL::CPWAVE, CPW = TL::CPW;
   constexpr int QS = TL::QS, TS = TL::TS, FP = TL::FP;
   static_assert(kK % FP == 0 && FP % 2 == 0, "flush period");
@@ -180,13 +189,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
   // Per-lane parameters, gradient accumulators and the adjoint entering this
   // segment: dh_last folded through the aggregates of every later segment,
   // g <- P g + G (the later segments' affine maps, last one first).
-  float Av[kNPL], A2[kNPL], gv[kNPL], dA[kNPL];
+  float Av[kNPL], A2[kNPL], gv[kNPL], dA[kNPL], invA[ZOH ? kNPL : 1];
 #pragma unroll
   for (int j = 0; j < kNPL; ++j) {
     const int n = n0 + j;
     const bool ok = dvalid && n < N;
     Av[j] = ok ? a.A[d * N + n] : 0.0f;
     A2[j] = Av[j] * kLog2e;
+    if constexpr (ZOH) invA[j] = Av[j] != 0.0f ? 1.0f / Av[j] : 0.0f;
     dA[j] = 0.0f;
     float gg = ok && a.dh_last ? a.dh_last[bdn + n] : 0.0f;
     if (ok) {
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
         dy = go * (zz * sg);
         gz = go * (sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
       }
-      const float dv = dl * uu;
+      const float dv = ZOH ? uu : dl * uu;  // ZOH keeps u: its coefficient depends on the state's A
       if (HAS_RESET && r.rs[G]) dl = -dl;  // sign bit: the state is cleared before this step
       s_rec[c * RS + t] = make_float4(dl, dv, dy, 0.0f);
       o.u[G] = uu;
@@ -328,37 +338,56 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       }
 #pragma unroll
       for (int j = 0; j < kNPL; ++j) {
-        h[j] = __builtin_fmaf(fast_exp2(dl * A2[j]), h[j], bb[j] * r.y);
+        const float abar = fast_exp2(dl * A2[j]);
+        if constexpr (ZOH)
+          h[j] = __builtin_fmaf(abar, h[j], (bb[j] * r.y) * zoh_coef(dl, dl * Av[j], abar, invA[j]));
+        else
+          h[j] = __builtin_fmaf(abar, h[j], bb[j] * r.y);
         if (t & 1) hist[t >> 1][j] = h[j];
       }
     }
 
-    float F1 = 0.0f, F2 = 0.0f, FY = 0.0f;  // this lane's step sums in the current group of four
+    float F1 = 0.0f, F2 = 0.0f, FY = 0.0f, F3 = 0.0f;  // this lane's step sums in the current group of four
 
     // One reverse step: av = a_t (0 on a reset), hp = h_{t-1}, ht = h_t.
+    // av = a_t masked by a reset, au = e^{delta A} unmasked (ZOH's d phi / d delta).
     auto rstep = [&](const int t, const float4 r, const float (&bb)[4], const float (&cc)[4],
-                     const float (&av)[kNPL], const float (&hp)[kNPL], const float (&ht)[kNPL]) {
+                     const float (&av)[kNPL], const float (&au)[kNPL], const float (&hp)[kNPL],
+                     const float (&ht)[kNPL]) {
       const float dl = fabsf(r.x), dv = r.y, dy = r.z;
-      float s1 = 0.0f, s2 = 0.0f, yy = 0.0f, p3[kNPL], p4[kNPL];
+      float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f, yy = 0.0f, p3[kNPL], p4[kNPL];
 #pragma unroll
       for (int j = 0; j < kNPL; ++j) {
         gv[j] = __builtin_fmaf(dy, cc[j], gv[j]);  // adjoint of h_t
         const float gq = gv[j] * (av[j] * hp[j]);
-        s1 = __builtin_fmaf(gv[j], bb[j], s1);
+        if constexpr (ZOH) {
+          const float x = dl * Av[j];
+          const float phi = zoh_coef(dl, x, au[j], invA[j]);
+          const float gb = gv[j] * bb[j];
+          s1 = __builtin_fmaf(gb, phi, s1);    // for du
+          s3 = __builtin_fmaf(gb, au[j], s3);  // for d delta
+          dA[j] = __builtin_fmaf(gq, dl, dA[j]);
+          dA[j] = __builtin_fmaf(gb * dv, (dl * dl) * zoh_psi(x, au[j]), dA[j]);
+          p3[j] = (gv[j] * dv) * phi;
+        } else {
+          s1 = __builtin_fmaf(gv[j], bb[j], s1);
+          dA[j] = __builtin_fmaf(gq, dl, dA[j]);
+          p3[j] = gv[j] * dv;
+        }
         s2 = __builtin_fmaf(gq, Av[j], s2);
-        dA[j] = __builtin_fmaf(gq, dl, dA[j]);
         yy = __builtin_fmaf(cc[j], ht[j], yy);
-        p3[j] = gv[j] * dv;
         p4[j] = dy * ht[j];
         gv[j] = av[j] * gv[j];  // carried to step t-1
       }
       s1 = chan_sum<LPC>(s1);
       s2 = chan_sum<LPC>(s2);
       yy = chan_sum<LPC>(yy);
+      if constexpr (ZOH) s3 = chan_sum<LPC>(s3);
       const bool mine = (l & 3) == (t & 3);
       F1 = mine ? s1 : F1;
       F2 = mine ? s2 : F2;
       FY = mine ? yy : FY;
+      if constexpr (ZOH) F3 = mine ? s3 : F3;
 
       // dB / dC terms of this step into the wave buffer (slot t & 1).
       *reinterpret_cast<float4*>(wbuf + cw * QS + (t & 1) * NPADC + n0) = make_float4(p3[0], p3[1], p3[2], p3[3]);
@@ -396,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
         const float4 rf = s_rec[c * RS + tf];
         if (dvalid && tg < pend) {
           const float dlf = fabsf(rf.x), dyf = rf.z;
-          const float du = __builtin_fmaf(dyf, dsk, dlf * F1);
-          const float dx = __builtin_fmaf(o.u[G], F1, F2) * o.sig[G];
+          const float du = __builtin_fmaf(dyf, dsk, ZOH ? F1 : dlf * F1);
+          const float dx = __builtin_fmaf(o.u[G], ZOH ? F3 : F1, F2) * o.sig[G];
           const float dz = o.gz[G] * __builtin_fmaf(dsk, o.u[G], FY);
           if (a.du_conv)
             a.du_conv[rowbase + tg] = du;  // the conv backward takes it from here
@@ -423,17 +452,24 @@ __global__ __launch_bounds__(kThreads, 2) void scan_bwd_kernel(const BwdArgs a) 
       const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, c0[4] = {c0v.x, c0v.y, c0v.z, c0v.w};
       const bool rs1 = HAS_RESET && __float_as_int(r1.x) < 0;
       const bool rs0 = HAS_RESET && __float_as_int(r0.x) < 0;
-      float a1[kNPL], a0[kNPL], hodd[kNPL], hev[kNPL], hpp[kNPL];
+      float a1[kNPL], a0[kNPL], u1[kNPL], u0[kNPL], hodd[kNPL], hev[kNPL], hpp[kNPL];
 #pragma unroll
       for (int j = 0; j < kNPL; ++j) {
-        a1[j] = rs1 ? 0.0f : fast_exp2(fabsf(r1.x) * A2[j]);
-        a0[j] = rs0 ? 0.0f : fast_exp2(fabsf(r0.x) * A2[j]);
-        hpp[j] = t >= 3 ? hist[(t - 2) >> 1][j] : hs[j];          // h_{t-2}
-        hev[j] = __builtin_fmaf(a0[j], hpp[j], b0[j] * r0.y);     // h_{t-1}, as the forward computed it
-        hodd[j] = hist[t >> 1][j];                                 // h_t
+        u1[j] = fast_exp2(fabsf(r1.x) * A2[j]);
+        u0[j] = fast_exp2(fabsf(r0.x) * A2[j]);
+        a1[j] = rs1 ? 0.0f : u1[j];
+        a0[j] = rs0 ? 0.0f : u0[j];
+        hpp[j] = t >= 3 ? hist[(t - 2) >> 1][j] : hs[j];  // h_{t-2}
+        // h_{t-1}, as the forward computed it
+        if constexpr (ZOH)
+          hev[j] = __builtin_fmaf(a0[j], hpp[j],
+                                  (b0[j] * r0.y) * zoh_coef(fabsf(r0.x), fabsf(r0.x) * Av[j], u0[j], invA[j]));
+        else
+          hev[j] = __builtin_fmaf(a0[j], hpp[j], b0[j] * r0.y);
+        hodd[j] = hist[t >> 1][j];  // h_t
       }
-      rstep(t, r1, b1, c1, a1, hev, hodd);
-      rstep(t - 1, r0, b0, c0, a0, hpp, hev);
+      rstep(t, r1, b1, c1, a1, u1, hev, hodd);
+      rstep(t - 1, r0, b0, c0, a0, u0, hpp, hev);
       // Keep the scheduler from hoisting later pairs' reads and exponentials
       // above this one: that costs registers the wave needs for occupancy.
       __builtin_amdgcn_sched_barrier(0);
@@ -716,16 +752,17 @@ int bwd_channels_per_block(int64_t N) { return kWaves * 64 / bwd_lpc(N); }
 
 // Reverse-sweep workgroups resident on the whole chip: 256 CUs x workgroups
 // per CU. The kernels need 200-250 VGPRs (two waves per SIMD, two 4-wave
-// workgroups per CU); the N > 128 layout's 84 KB of LDS allows one.
-int64_t bwd_resident_blocks(int64_t N) { return 256 * (bwd_lpc(N) >= 64 ? 1 : 2); }
+// workgroups per CU); the N > 128 layout's 84 KB of LDS allows one, and so
+// does the zero-order-hold variant's register budget.
+int64_t bwd_resident_blocks(int64_t N, bool zoh) { return 256 * (bwd_lpc(N) >= 64 || zoh ? 1 : 2); }
 
-void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps) {
+void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, bool zoh, int* nsegb, int64_t* seg_steps) {
   // Segments of whole 16-step chunks. Workgroups run in rounds of the
   // resident count, each as long as its segment, so pick the count that
   // minimises rounds x chunks per segment (the fewest segments on a tie).
   const int64_t groups = B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N));
   const int64_t chunks = (L + kK - 1) / kK;
-  const int64_t resident = bwd_resident_blocks(N);
+  const int64_t resident = bwd_resident_blocks(N, zoh);
   int64_t best = 1, best_cost = -1;
   const int64_t max_seg = std::min<int64_t>(chunks, 4096);
   for (int64_t ns = 1; ns <= max_seg; ++ns) {
@@ -798,16 +835,28 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   hipError_t e = with_bwd_tile(pl.N, [&](auto tile) {
     using TL = decltype(tile);
     const dim3 grid(static_cast<unsigned>(a.nblocks)), block(kThreads);
-    if (pl.in_bf16) {
+    if (pl.zoh) {
+      if (pl.in_bf16) {
+        if (reset)
+          hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, true, true>), grid, block, 0, stream, a);
+        else
+          hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, false, true>), grid, block, 0, stream, a);
+      } else {
+        if (reset)
+          hipLaunchKernelGGL((scan_bwd_kernel<TL, float, true, true>), grid, block, 0, stream, a);
+        else
+          hipLaunchKernelGGL((scan_bwd_kernel<TL, float, false, true>), grid, block, 0, stream, a);
+      }
+    } else if (pl.in_bf16) {
       if (reset)
-        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, true, false>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, bf16_t, false, false>), grid, block, 0, stream, a);
     } else {
       if (reset)
-        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, true, false>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<TL, float, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
   });

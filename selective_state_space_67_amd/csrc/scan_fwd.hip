@@ -78,6 +78,7 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.conv_state_out = pl.conv_state_out;
   a.conv_k = pl.conv_k;
   a.uconv_out = pl.uconv_out;
+  a.zoh = pl.zoh;
   const bool ck = pl.checkpoint != 0;
   const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
   a.ws_P = pl.ws;

@@ -128,6 +128,7 @@ struct ScanArgs {
   float* conv_state_out;       // (B, D, conv_k - 1) or null
   int conv_k;                  // 1 .. 4
   float* uconv_out;            // kCheckpoint with a conv stage: the scan input u' (B, D, L), f32
+  int zoh;                     // exact zero-order hold input coefficient (ZOH kernels)
 };
 
 // Visibility of the conv window's inputs: the window of step Q covers
@@ -147,7 +148,7 @@ __device__ __forceinline__ float conv_pre(const float (&w)[4], float bias, float
   return acc;
 }
 
-template <typename TL, typename InT, bool HAS_RESET, int MODE, bool CONV>
+template <typename TL, typename InT, bool HAS_RESET, int MODE, bool CONV, bool ZOH>
 __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kernel(const ScanArgs a) {
   constexpr int NPL = TL::NPL, RPC = TL::RPC, CPW = TL::CPW, THREADS = TL::THREADS;
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
@@ -229,13 +230,17 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   const bool dvalid = d < a.D;
   const int nbase = (slice * 16 + k) * NPL;         // first state of this lane
 
-  // Per-lane parameters and state.
-  float A2[NPL], h[NPL];
+  // Per-lane parameters and state. With ZOH also A and 1/A (0 for A = 0).
+  float A2[NPL], h[NPL], Aj[ZOH ? NPL : 1], invA[ZOH ? NPL : 1];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = nbase + j;
     const bool ok = dvalid && n < N;
     A2[j] = ok ? a.A[d * N + n] * kLog2e : 0.0f;
+    if constexpr (ZOH) {
+      Aj[j] = ok ? a.A[d * N + n] : 0.0f;
+      invA[j] = Aj[j] != 0.0f ? 1.0f / Aj[j] : 0.0f;
+    }
     h[j] = 0.0f;
     if ((FULL || CKPT) && ok) {
       const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + n;
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
       }
       dl[i] = softplus_f32(load_elem(&r.dt[i], 0) + s_bias);
       if (!sc_valid || tau0 + stl + i >= Lseg) dl[i] = 0.0f;
-      dv[i] = dl[i] * uu;
+      dv[i] = ZOH ? uu : dl[i] * uu;  // ZOH keeps u: its coefficient depends on the state's A
       if (FULL) {
         o.dsk[i] = s_dskip * uu;
         o.gate[i] = z_wg ? silu_f32(load_elem(&r.z[i], 0)) : 1.0f;
@@ -512,7 +517,10 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const float abar = fast_exp2(dl * A2[j]);
-      h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
+      if constexpr (ZOH)
+        h[j] = __builtin_fmaf(abar, h[j], (Bv[j] * dv) * zoh_coef(dl, dl * Aj[j], abar, invA[j]));
+      else
+        h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
       if (FULL) part = j == 0 ? Cv[j] * h[j] : __builtin_fmaf(Cv[j], h[j], part);
     }
     if (FULL) {
@@ -546,7 +554,10 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const float abar = fast_exp2(dl * A2[j]);
-      h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
+      if constexpr (ZOH)
+        h[j] = __builtin_fmaf(abar, h[j], (Bv[j] * dv) * zoh_coef(dl, dl * Aj[j], abar, invA[j]));
+      else
+        h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
       segP[j] = rs ? 0.0f : segP[j] * abar;
       segG[j] = __builtin_fmaf(segP[j] * dy, Cv[j], segG[j]);
     }
@@ -785,32 +796,35 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
   }
 }
 
-template <typename TL, typename InT, bool HAS_RESET, bool CONV>
+template <typename TL, typename InT, bool HAS_RESET, bool CONV, bool ZOH>
 hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, bool checkpoint,
                        hipStream_t stream) {
   if (args.nseg > 1) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate, CONV>), dim3(nblocks_agg), dim3(TL::THREADS),
-                       0, stream, agg);
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate, CONV, ZOH>), dim3(nblocks_agg),
+                       dim3(TL::THREADS), 0, stream, agg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
   if (checkpoint)
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint, CONV>), dim3(nblocks_full),
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint, CONV, ZOH>), dim3(nblocks_full),
                        dim3(TL::THREADS), 0, stream, full);
   else
-    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull, CONV>), dim3(nblocks_full), dim3(TL::THREADS), 0,
-                       stream, full);
+    hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kFull, CONV, ZOH>), dim3(nblocks_full), dim3(TL::THREADS),
+                       0, stream, full);
   return hipGetLastError();
 }
 
 template <typename TL, typename InT, bool HAS_RESET>
 hipError_t launch_conv(const ScanArgs& a, int nf, int na, bool ck, hipStream_t stream) {
-  return a.conv_w ? launch_tile<TL, InT, HAS_RESET, true>(a, nf, na, ck, stream)
-                  : launch_tile<TL, InT, HAS_RESET, false>(a, nf, na, ck, stream);
+  if (a.zoh)
+    return a.conv_w ? launch_tile<TL, InT, HAS_RESET, true, true>(a, nf, na, ck, stream)
+                    : launch_tile<TL, InT, HAS_RESET, false, true>(a, nf, na, ck, stream);
+  return a.conv_w ? launch_tile<TL, InT, HAS_RESET, true, false>(a, nf, na, ck, stream)
+                  : launch_tile<TL, InT, HAS_RESET, false, false>(a, nf, na, ck, stream);
 }
 
 // Layout by state size: (states per lane, rows per channel).

@@ -48,7 +48,17 @@ struct UpdateArgs {
   const float* conv_w;   // (D, conv_k) or null (no conv stage)
   const float* conv_b;   // (D) or null
   int conv_k;
+  int zoh;               // exact zero-order-hold input coefficient
 };
+
+// One state's update: h <- e^{delta A} h + coef * B * u, coef = delta or the
+// exact zero-order hold (e^{delta A} - 1) / A.
+__device__ __forceinline__ float update_state(const UpdateArgs& a, float delta, float A, float h, float B, float u) {
+  const float abar = fast_exp2(delta * (A * kLog2e));
+  if (!a.zoh) return __builtin_fmaf(abar, h, B * (delta * u));
+  const float coef = zoh_coef(delta, delta * A, abar, A != 0.0f ? 1.0f / A : 0.0f);
+  return __builtin_fmaf(abar, h, B * (u * coef));
+}
 
 // The step input of row `row` (channel d) from its raw input x: x itself, or
 // the conv + SiLU over (conv state, x).
@@ -137,12 +147,11 @@ __global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a
     const int64_t d = row % a.D;
     const float delta = softplus_f32(xx[r]);
     const float ui = step_input(a, row, d, uu[r]);
-    const float du = delta * ui;
     float4 hn;
-    hn.x = __builtin_fmaf(fast_exp2(delta * (Av[r].x * kLog2e)), hv[r].x, Bv[r].x * du);
-    hn.y = __builtin_fmaf(fast_exp2(delta * (Av[r].y * kLog2e)), hv[r].y, Bv[r].y * du);
-    hn.z = __builtin_fmaf(fast_exp2(delta * (Av[r].z * kLog2e)), hv[r].z, Bv[r].z * du);
-    hn.w = __builtin_fmaf(fast_exp2(delta * (Av[r].w * kLog2e)), hv[r].w, Bv[r].w * du);
+    hn.x = update_state(a, delta, Av[r].x, hv[r].x, Bv[r].x, ui);
+    hn.y = update_state(a, delta, Av[r].y, hv[r].y, Bv[r].y, ui);
+    hn.z = update_state(a, delta, Av[r].z, hv[r].z, Bv[r].z, ui);
+    hn.w = update_state(a, delta, Av[r].w, hv[r].w, Bv[r].w, ui);
     *reinterpret_cast<float4*>(a.h + row * a.N + n0) = hn;
     float y = Cv[r].x * hn.x;
     y = __builtin_fmaf(Cv[r].y, hn.y, y);
@@ -171,12 +180,10 @@ __global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs
   const float uu = step_input(a, row, d, ux);
   const float delta =
       softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
-  const float du = delta * uu;
   float y = 0.0f;
   float* hrow = a.h + row * a.N;
   for (int64_t n = li; n < a.N; n += LR) {
-    const float abar = fast_exp2(delta * (a.A[d * a.N + n] * kLog2e));
-    const float hn = __builtin_fmaf(abar, hrow[n], load_elem(B_in, b * a.N + n) * du);
+    const float hn = update_state(a, delta, a.A[d * a.N + n], hrow[n], load_elem(B_in, b * a.N + n), uu);
     hrow[n] = hn;
     y = __builtin_fmaf(load_elem(C_in, b * a.N + n), hn, y);
   }
@@ -253,6 +260,7 @@ hipError_t launch_state_update(const UpdatePlan& pl, hipStream_t stream) {
   a.conv_w = pl.conv_w;
   a.conv_b = pl.conv_b;
   a.conv_k = pl.conv_k;
+  a.zoh = pl.zoh;
   return pl.in_bf16 ? launch_dtype<bf16_t>(a, stream) : launch_dtype<float>(a, stream);
 }
 

@@ -350,3 +350,11 @@ def test_bwd_conv_workspace_grows(lib):
     p.conv_w, p.conv_width = BASE + 0x70000000, 4
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
     assert n1.value >= n0.value + 2 * B * D * L * 4   # u' and its gradient
+
+
+def test_unknown_discretization(lib):
+    assert scan_status(lib, scan_params(discretization=2)) == 5
+    assert update_status(lib, update_params(discretization=-1)) == 5
+    assert bwd_status(lib, bwd_params(discretization=7)) == 5
+    n = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(bwd_params(discretization=7)), ctypes.byref(n)) == 5
