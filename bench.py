@@ -18,6 +18,8 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
                (checkpoint sweep, reverse sweep and reduction, back to back)
   conv_stage   the same forward and backward with the fused causal conv1d
                (width 4) + SiLU input stage, u being the conv input
+  zoh          the same forward and backward with the exact zero-order-hold
+               input coefficient (e^{delta A} - 1) / A in place of delta
   cpu_baseline the float64 oracle on the host cores over the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -259,7 +261,16 @@ def main():
 
     csec_f = timed(fconv, max(5, min(args.steps, 50)))
     csec_b = timed(bconv, bsteps)
-    del bwd, dout, fconv, bconv
+    del fconv, bconv
+
+    # Exact zero-order hold.
+    fzoh = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                                Dskip=t["Dskip"], z=t["z"], reset=t["reset"], zoh=True)
+    bzoh = binding.prepare_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dout, dt_bias=t["dt_bias"],
+                                    Dskip=t["Dskip"], z=t["z"], reset=t["reset"], zoh=True)
+    zsec_f = timed(fzoh, max(5, min(args.steps, 50)))
+    zsec_b = timed(bzoh, bsteps)
+    del bwd, dout, fzoh, bzoh
 
     result = {
         "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
@@ -310,6 +321,10 @@ def main():
                        "fwd_elements_per_s": elements / csec_f, "bwd_ms": csec_b * 1e3,
                        "bwd_vs_plain_backward": csec_b / bsec,
                        "hbm_bytes_saved_by_fusion": B * D * L * (s_in + 4)},
+        "zoh": {"workload": "the same scan with Bbar = (e^{delta A} - 1) / A * B",
+                "fwd_ms": zsec_f * 1e3, "fwd_vs_plain_forward": zsec_f / launch_s,
+                "fwd_elements_per_s": elements / zsec_f, "bwd_ms": zsec_b * 1e3,
+                "bwd_vs_plain_backward": zsec_b / bsec},
     }
 
     if not args.no_cpu:
