@@ -53,6 +53,8 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
+        lib.oracle_scan_cplx_rows.argtypes = [i64, i64, i64] + [p] * 14 + [ctypes.c_int]
+        lib.oracle_scan_cplx_rows.restype = None
         lib.oracle_conv_silu_rows.argtypes = [i64, i64, i64] + [p] * 10 + [ctypes.c_int]
         lib.oracle_conv_silu_rows.restype = None
         lib.oracle_conv_silu_bwd_rows.argtypes = [i64, i64, i64, i64] + [p] * 12 + [ctypes.c_int]
@@ -284,3 +286,59 @@ def scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, re
     if rc != 0:
         raise MemoryError("oracle backward: scratch allocation failed")
     return out
+
+
+def _interleave(x):
+    """complex array -> float64 array with a trailing (re, im) axis."""
+    if x is None:
+        return None
+    x = np.asarray(x, dtype=np.complex128)
+    return np.ascontiguousarray(np.stack([x.real, x.imag], axis=-1))
+
+
+def scan_cplx(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
+              want_h_last=False, nthreads=0):
+    """Full scan with a complex diagonal state (the S4D-Lin variant).
+
+    u, dt_raw, z: (B, D, L) real; A: (D, N) complex; Bm, Cm: (B, L, N) complex;
+    h0: (B, D, N) complex or None. Returns out (B, D, L) float64 (the gated real
+    part of the read-out) and, if asked, h_last (B, D, N) complex128.
+    """
+    lib = _load()
+    u, dt_raw, z = _f64(u), _f64(dt_raw), _f64(z)
+    dt_bias, Dskip = _f64(dt_bias), _f64(Dskip)
+    Ai, Bi, Ci, h0i = _interleave(A), _interleave(Bm), _interleave(Cm), _interleave(h0)
+    Bt, D, L = u.shape
+    N = Ai.shape[1]
+    if N > MAX_N:
+        raise ValueError("oracle supports N <= %d" % MAX_N)
+    assert dt_raw.shape == (Bt, D, L) and Ai.shape == (D, N, 2)
+    assert Bi.shape == (Bt, L, N, 2) and Ci.shape == (Bt, L, N, 2)
+    assert z is None or z.shape == (Bt, D, L)
+    assert h0i is None or h0i.shape == (Bt, D, N, 2)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+        assert reset.shape == (Bt, L)
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    out = np.empty((Bt, D, L))
+    hl = np.empty((Bt, D, N, 2)) if want_h_last else None
+    lib.oracle_scan_cplx_rows(Bt * D, L, N, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
+                              _ptr(Ai), _ptr(Dskip), _ptr(Bi), _ptr(Ci), _ptr(reset), _ptr(h0i), _ptr(out),
+                              _ptr(hl), int(nthreads))
+    if want_h_last:
+        return out, hl[..., 0] + 1j * hl[..., 1]
+    return out
+
+
+def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, nthreads=0):
+    """Decode step with a complex state: one step of scan_cplx from h.
+
+    h: (B, D, N) complex; u, dt_raw, z: (B, D); A: (D, N) complex; Bm, Cm: (B, N)
+    complex. Returns (out (B, D), h_new (B, D, N) complex128).
+    """
+    u = _f64(u)
+    Bt, D = u.shape
+    out, h_new = scan_cplx(u[:, :, None], _f64(dt_raw)[:, :, None], A, np.asarray(Bm)[:, None, :],
+                           np.asarray(Cm)[:, None, :], z=None if z is None else _f64(z)[:, :, None],
+                           dt_bias=dt_bias, Dskip=Dskip, h0=h, want_h_last=True, nthreads=nthreads)
+    return out[:, :, 0], h_new

@@ -40,6 +40,7 @@
  * All arithmetic is IEEE double with libm exp/log1p. Inputs arrive already
  * widened to double by the caller (bf16 and fp32 widen exactly).
  */
+#include <complex.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -161,6 +162,67 @@ void oracle_state_update(int64_t Bt, int64_t Dt, int64_t N, double* h,
     out[r] = step(N, dt_raw[r], dt_bias ? dt_bias[d] : 0.0, A + d * N, Bm + b * N,
                   Cm + b * N, Dskip ? Dskip[d] : 0.0, u[r], z != NULL, z ? z[r] : 0.0,
                   0, zoh, h + r * N);
+  }
+}
+
+/*
+ * Complex diagonal state (the S4D-Lin variant). The pages give its
+ * initialisation, A = -1/2 + i n ("Technical analysis: Mamba selective state
+ * spaces", section 4.1), and say that a complex state keeps phase information
+ * (section 5.3); they say nothing more, so the plain reading is taken: the
+ * same recurrence with A[d,n], B[b,t,n], C[b,t,n] and h[n] complex, delta and
+ * u real, and the real part of the read-out:
+ *
+ *   h[n] = h0[b,d,n]  (zeros when absent)
+ *   for t: delta = softplus(dt_raw + dt_bias); h = 0 on a reset;
+ *          h[n] = exp(delta A[d,n]) h[n] + delta B[b,t,n] u
+ *          y = Re(sum_n C[b,t,n] h[n]) + D[d] u;  out = y silu(z)
+ *
+ * Complex arrays are interleaved (re, im) doubles with the shapes of the real
+ * scan plus a trailing 2: A (Dtot, N, 2), Bm, Cm (Btot, L, N, 2), h0 and
+ * h_last (R, N, 2). Everything else is as in oracle_scan_rows.
+ */
+void oracle_scan_cplx_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b,
+                           const int64_t* row_d, const double* u, const double* dt_raw,
+                           const double* z, const double* dt_bias, const double* A,
+                           const double* Dskip, const double* Bm, const double* Cm,
+                           const uint8_t* reset, const double* h0, double* out,
+                           double* h_last, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t b = row_b[r], d = row_d[r];
+    double complex h[1024];
+    for (int64_t n = 0; n < N; ++n)
+      h[n] = h0 ? h0[2 * (r * N + n)] + I * h0[2 * (r * N + n) + 1] : 0.0;
+    const double bias = dt_bias ? dt_bias[d] : 0.0;
+    const double dsk = Dskip ? Dskip[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      const int64_t bt = b * L + t;
+      const double delta = softplus(dt_raw[r * L + t] + bias);
+      const double x = u[r * L + t];
+      if (reset && reset[bt])
+        for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+      double complex acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double complex An = A[2 * (d * N + n)] + I * A[2 * (d * N + n) + 1];
+        const double complex Bn = Bm[2 * (bt * N + n)] + I * Bm[2 * (bt * N + n) + 1];
+        const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
+        h[n] = cexp(delta * An) * h[n] + delta * Bn * x;
+        acc += Cn * h[n];
+      }
+      const double y = creal(acc) + dsk * x;
+      out[r * L + t] = z ? y * silu(z[r * L + t]) : y;
+    }
+    if (h_last)
+      for (int64_t n = 0; n < N; ++n) {
+        h_last[2 * (r * N + n)] = creal(h[n]);
+        h_last[2 * (r * N + n) + 1] = cimag(h[n]);
+      }
   }
 }
 

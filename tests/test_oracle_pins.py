@@ -373,5 +373,5 @@ def test_oracle_is_independent_of_the_product():
             assert not re.search(r"^\s*(import|from)\s+selective_state_space_67_amd", text, re.M), name
         if name.endswith(".c"):
             includes = set(re.findall(r"#include\s*<([^>]+)>", open(path).read()))
-            assert includes <= {"math.h", "stddef.h", "stdint.h", "stdlib.h", "omp.h"}, includes
+            assert includes <= {"complex.h", "math.h", "stddef.h", "stdint.h", "stdlib.h", "omp.h"}, includes
             assert '#include "' not in open(path).read()
