@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10200 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -88,6 +88,27 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *                    basis: structured SSM"); delta * B where A = 0.
  * Abar = exp(delta A) in both. Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
+
+/* Kind of the diagonal state (the `state_kind` field):
+ *  SSM_STATE_REAL     real A, B, C and h, as above. Default.
+ *  SSM_STATE_COMPLEX  the complex-diagonal variant whose initialisation the
+ *                     pages give as A = -1/2 + i n (S4D-Lin) and whose complex
+ *                     state keeps phase information ("Technical analysis: Mamba
+ *                     selective state spaces", sections 4.1 and 5.3). A, B, C,
+ *                     h0, h_last and the decode state h are complex, stored as
+ *                     interleaved (re, im) pairs: every such tensor gains a
+ *                     trailing dimension of 2 (A (D,N,2) float32, Bm and Cm
+ *                     (B,L,N,2) or (B,N,2) in in_dtype, states (B,D,N,2) float32).
+ *                     delta, u, z and out stay real; the recurrence is
+ *                       h_t[n] = exp(delta_t A[d,n]) h_{t-1}[n] + delta_t B[b,t,n] u
+ *                       y_t    = Re(sum_n C[b,t,n] h_t[n]) + D[d] u
+ *                     with the same gate and resets. This build supports it
+ *                     with SSM_DISC_DELTA_B and no conv stage, in ssm_scan_fwd
+ *                     (which then never splits the sequence and needs no
+ *                     workspace) and ssm_state_update; other combinations, and
+ *                     the backward, return SSM_ERR_UNSUPPORTED.
+ * Other values return SSM_ERR_UNSUPPORTED. */
+typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 
 /*
  * Full-sequence scan (prefill / training forward).
@@ -152,7 +173,7 @@ typedef struct {
   const float* conv_state_in;
   float* conv_state_out;
   int32_t conv_width;
-  int32_t reserved1;
+  int32_t state_kind; /* ssm_state_kind */
 } ssm_scan_params;
 
 /* Bytes of workspace ssm_scan_fwd needs for these parameters (0 when the scan
@@ -201,6 +222,8 @@ typedef struct {
   const float* conv_b;
   int32_t conv_width;
   int32_t discretization; /* ssm_discretization */
+  int32_t state_kind;     /* ssm_state_kind */
+  int32_t reserved1;      /* set to 0 */
 } ssm_update_params;
 
 /* Enqueue the decode step described by `p` on `hip_stream`. */
@@ -285,6 +308,8 @@ typedef struct {
   float* dconv_state_in;
   int32_t conv_width;
   int32_t discretization; /* ssm_discretization */
+  int32_t state_kind;     /* ssm_state_kind; only SSM_STATE_REAL is supported here */
+  int32_t reserved1;      /* set to 0 */
 } ssm_scan_bwd_params;
 
 /* Bytes of workspace ssm_scan_bwd needs (only sizes and dtypes of `p` are read). */

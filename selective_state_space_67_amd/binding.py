@@ -18,6 +18,8 @@ SSM_F32 = 0
 SSM_BF16 = 1
 SSM_DISC_DELTA_B = 0
 SSM_DISC_ZOH = 1
+SSM_STATE_REAL = 0
+SSM_STATE_COMPLEX = 1
 
 STATUS_NAMES = {
     0: "SSM_OK", 1: "SSM_ERR_NULL_POINTER", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
@@ -43,7 +45,7 @@ class ScanParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("num_segments", ctypes.c_int32), ("discretization", ctypes.c_int32),
         ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
-        ("conv_state_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+        ("conv_state_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("state_kind", ctypes.c_int32),
     ]
 
 
@@ -56,6 +58,7 @@ class UpdateParams(ctypes.Structure):
         ("Dskip", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("conv_state", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
         ("conv_b", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("discretization", ctypes.c_int32),
+        ("state_kind", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -74,6 +77,7 @@ class BwdParams(ctypes.Structure):
         ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
         ("dconv_w", ctypes.c_void_p), ("dconv_b", ctypes.c_void_p), ("dconv_state_in", ctypes.c_void_p),
         ("conv_width", ctypes.c_int32), ("discretization", ctypes.c_int32),
+        ("state_kind", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -160,16 +164,18 @@ def _stream(stream, device):
 
 
 def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                 num_segments, conv_w=None, conv_b=None, conv_state_in=None, conv_state_out=None, zoh=False):
+                 num_segments, conv_w=None, conv_b=None, conv_state_in=None, conv_state_out=None, zoh=False,
+                 cplx=False):
     import torch
 
     Bt, D, L = u.shape
     N = A.shape[1]
+    c2 = (2,) if cplx else ()  # complex tensors carry a trailing (re, im) axis
     _need(u, (Bt, D, L), "u")
     _need(dt_raw, (Bt, D, L), "dt_raw", u.dtype)
-    _need(A, (D, N), "A", torch.float32)
-    _need(Bm, (Bt, L, N), "Bm", u.dtype)
-    _need(Cm, (Bt, L, N), "Cm", u.dtype)
+    _need(A, (D, N) + c2, "A", torch.float32)
+    _need(Bm, (Bt, L, N) + c2, "Bm", u.dtype)
+    _need(Cm, (Bt, L, N) + c2, "Cm", u.dtype)
     if dt_bias is not None:
         _need(dt_bias, (D,), "dt_bias", torch.float32)
     if Dskip is not None:
@@ -179,11 +185,11 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
     if reset is not None:
         _need(reset, (Bt, L), "reset", torch.uint8)
     if h0 is not None:
-        _need(h0, (Bt, D, N), "h0", torch.float32)
+        _need(h0, (Bt, D, N) + c2, "h0", torch.float32)
     if out is not None:
         _need(out, (Bt, D, L), "out")
     if h_last is not None:
-        _need(h_last, (Bt, D, N), "h_last", torch.float32)
+        _need(h_last, (Bt, D, N) + c2, "h_last", torch.float32)
     p = ScanParams()
     p.batch, p.dim, p.seqlen, p.dstate = Bt, D, L, N
     p.in_dtype = _dtype_code(u)
@@ -194,6 +200,7 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
     p.reset, p.h0, p.out, p.h_last = _ptr(reset), _ptr(h0), _ptr(out), _ptr(h_last)
     p.num_segments = int(num_segments)
     p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    p.state_kind = SSM_STATE_COMPLEX if cplx else SSM_STATE_REAL
     if conv_w is not None:
         K = conv_w.shape[1]
         _need(conv_w, (D, K), "conv_w", torch.float32)
@@ -226,13 +233,15 @@ def ssm_scan_workspace_size(u, A, *, num_segments=0, out_dtype=None):
 
 def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                  out=None, h_last=None, out_dtype=None, workspace=None, num_segments=0, conv_w=None, conv_b=None,
-                 conv_state_in=None, conv_state_out=None, zoh=False, stream=None):
+                 conv_state_in=None, conv_state_out=None, zoh=False, complex_state=False, stream=None):
     """Selective scan over the whole sequence; returns ``out`` (B, D, L).
 
     With conv_w (D, K <= 4) float32, u is the input of a causal depthwise
     conv1d + SiLU stage whose output feeds the scan (conv_b (D,),
     conv_state_in / conv_state_out (B, D, K-1) float32 optional). zoh=True
     selects the exact zero-order-hold input coefficient (e^{delta A} - 1) / A.
+    complex_state=True selects the complex diagonal state: A (D, N, 2),
+    Bm, Cm (B, L, N, 2) and h0, h_last (B, D, N, 2) then hold (re, im) pairs.
 
     u, dt_raw, z: (B, D, L) float32 or bfloat16; A: (D, N) float32;
     Bm, Cm: (B, L, N) same dtype as u; dt_bias, Dskip: (D,) float32;
@@ -247,7 +256,7 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh, complex_state)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if n.value:
@@ -261,7 +270,7 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
 
 def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None, out=None,
                  h_last=None, out_dtype=None, num_segments=0, conv_w=None, conv_b=None, conv_state_in=None,
-                 conv_state_out=None, zoh=False, stream=None):
+                 conv_state_out=None, zoh=False, complex_state=False, stream=None):
     """Marshal the arguments of ssm_scan_fwd once; returns a no-argument callable
     that enqueues the same scan again (same tensors, same stream) each time it is
     called. The tensors must stay alive and unchanged in shape while it is used."""
@@ -271,7 +280,7 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     if out is None:
         out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
-                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh)
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh, complex_state)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, conv_w, conv_b, conv_state_in,
@@ -294,17 +303,17 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
 
 
 def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                         out_dtype=None, zoh=False, stream=None):
+                         out_dtype=None, zoh=False, complex_state=False, stream=None):
     """Marshal the arguments of ssm_state_update once; returns a no-argument
     callable that enqueues the same decode step again each time it is called
     (updating h in place every time)."""
     import torch
 
     lib = load_library()
-    Bt, D, N = h.shape
+    Bt, D, N = h.shape[:3]
     if out is None:
         out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
-    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, zoh=zoh)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, zoh=zoh, cplx=complex_state)
     st = _stream(stream, u.device)
     fn = lib.ssm_state_update
     pref = ctypes.byref(p)
@@ -318,16 +327,17 @@ def prepare_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z
 
 
 def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None, conv_b=None, conv_state=None,
-                   zoh=False):
+                   zoh=False, cplx=False):
     import torch
 
-    Bt, D, N = h.shape
-    _need(h, (Bt, D, N), "h", torch.float32)
+    Bt, D, N = h.shape[:3]
+    c2 = (2,) if cplx else ()  # complex tensors carry a trailing (re, im) axis
+    _need(h, (Bt, D, N) + c2, "h", torch.float32)
     _need(u, (Bt, D), "u")
     _need(dt_raw, (Bt, D), "dt_raw", u.dtype)
-    _need(A, (D, N), "A", torch.float32)
-    _need(Bm, (Bt, N), "Bm", u.dtype)
-    _need(Cm, (Bt, N), "Cm", u.dtype)
+    _need(A, (D, N) + c2, "A", torch.float32)
+    _need(Bm, (Bt, N) + c2, "Bm", u.dtype)
+    _need(Cm, (Bt, N) + c2, "Cm", u.dtype)
     if z is not None:
         _need(z, (Bt, D), "z", u.dtype)
     if dt_bias is not None:
@@ -342,6 +352,7 @@ def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None,
     p.dt_bias, p.A, p.Dskip = _ptr(dt_bias), _ptr(A), _ptr(Dskip)
     p.Bm, p.Cm, p.out = _ptr(Bm), _ptr(Cm), _ptr(out)
     p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    p.state_kind = SSM_STATE_COMPLEX if cplx else SSM_STATE_REAL
     if conv_w is not None:
         K = conv_w.shape[1]
         _need(conv_w, (D, K), "conv_w", torch.float32)
@@ -354,18 +365,21 @@ def _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w=None,
 
 
 def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, out=None,
-                     out_dtype=None, conv_w=None, conv_b=None, conv_state=None, zoh=False, stream=None):
+                     out_dtype=None, conv_w=None, conv_b=None, conv_state=None, zoh=False, complex_state=False,
+                     stream=None):
     """Decode step: updates h (B, D, N) float32 in place and returns out (B, D).
 
     With conv_w (D, K), u is this step's conv input and conv_state
-    (B, D, K-1) float32 is shifted in place."""
+    (B, D, K-1) float32 is shifted in place. complex_state=True: h (B, D, N, 2),
+    A (D, N, 2) and Bm, Cm (B, N, 2) hold (re, im) pairs."""
     import torch
 
     lib = load_library()
-    Bt, D, N = h.shape
+    Bt, D, N = h.shape[:3]
     if out is None:
         out = torch.empty((Bt, D), dtype=out_dtype or torch.float32, device=u.device)
-    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w, conv_b, conv_state, zoh)
+    p = _update_params(h, u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, out, conv_w, conv_b, conv_state, zoh,
+                       complex_state)
     _check(lib.ssm_state_update(ctypes.byref(p), _stream(stream, u.device)))
     return out
 

@@ -36,6 +36,16 @@ ssm_status ok() {
 
 bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
 bool valid_disc(int32_t t) { return t == SSM_DISC_DELTA_B || t == SSM_DISC_ZOH; }
+bool valid_kind(int32_t k) { return k == SSM_STATE_REAL || k == SSM_STATE_COMPLEX; }
+
+// The complex state is built for the small-delta input matrix without a conv stage.
+ssm_status check_kind(int32_t kind, int32_t disc, bool conv) {
+  if (!valid_kind(kind)) return fail(SSM_ERR_UNSUPPORTED, "unknown state_kind %d", kind);
+  if (kind == SSM_STATE_COMPLEX && disc != SSM_DISC_DELTA_B)
+    return fail(SSM_ERR_UNSUPPORTED, "the complex state supports only SSM_DISC_DELTA_B");
+  if (kind == SSM_STATE_COMPLEX && conv) return fail(SSM_ERR_UNSUPPORTED, "the complex state has no conv stage");
+  return SSM_OK;
+}
 size_t dtype_size(int32_t t) { return t == SSM_BF16 ? 2 : 4; }
 
 // a * b without overflow for non-negative operands.
@@ -172,6 +182,8 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params* p, size_t* byt
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
+  if (p->state_kind != SSM_STATE_REAL)
+    return fail(SSM_ERR_UNSUPPORTED, "the backward supports only SSM_STATE_REAL (got state_kind %d)", p->state_kind);
   BwdLayout lay;
   if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
   *bytes = lay.total;
@@ -197,6 +209,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
+  if (p->state_kind != SSM_STATE_REAL)
+    return fail(SSM_ERR_UNSUPPORTED, "the backward supports only SSM_STATE_REAL (got state_kind %d)", p->state_kind);
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->dconv_w || p->dconv_b || p->dconv_state_in))
@@ -350,6 +364,11 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   if (s != SSM_OK) return s;
   if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
+  if (!valid_kind(p->state_kind)) return fail(SSM_ERR_UNSUPPORTED, "unknown state_kind %d", p->state_kind);
+  if (p->state_kind == SSM_STATE_COMPLEX) {  // never splits the sequence
+    *bytes = 0;
+    return ok();
+  }
   int nseg;
   int64_t seg_len;
   size_t ws;
@@ -380,13 +399,16 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
     return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
+  if ((s = check_kind(p->state_kind, p->discretization, p->conv_w != nullptr)) != SSM_OK) return s;
+  const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
+  const int64_t cw = cplx ? 2 : 1;  // scalars per A, B, C and state entry
   const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
   const Range inputs[] = {
       range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
-      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln, si, "Bm"),
-      range(p->Cm, sz.bln, si, "Cm"),        range(p->A, sz.dn, 4, "A"),
+      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln * cw, si, "Bm"),
+      range(p->Cm, sz.bln * cw, si, "Cm"),   range(p->A, sz.dn * cw, 4, "A"),
       range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
-      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
+      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn * cw, 4, "h0"),
       range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
       range(p->conv_state_in, bdk, 4, "conv_state_in"),
   };
@@ -405,7 +427,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
 
   const Range out = range(p->out, sz.bdl, so, "out");
-  const Range hl = range(p->h_last, sz.bdn, 4, "h_last");
+  const Range hl = range(p->h_last, sz.bdn * cw, 4, "h_last");
   const Range cso = range(p->conv_state_out, bdk, 4, "conv_state_out");
   for (const Range& r : inputs) {
     if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
@@ -414,6 +436,35 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   }
   if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
   if (overlaps(out, cso) || overlaps(hl, cso)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
+
+  if (cplx) {
+    if (ssm::cplx_scan_grid_blocks(p->batch, p->dim) > std::numeric_limits<int32_t>::max())
+      return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+    ssm::ScanPlan plan{};
+    plan.B = p->batch;
+    plan.D = p->dim;
+    plan.L = p->seqlen;
+    plan.N = p->dstate;
+    plan.in_bf16 = p->in_dtype == SSM_BF16;
+    plan.out_bf16 = p->out_dtype == SSM_BF16;
+    plan.u = p->u;
+    plan.dt = p->dt_raw;
+    plan.z = p->z;
+    plan.Bm = p->Bm;
+    plan.Cm = p->Cm;
+    plan.dt_bias = p->dt_bias;
+    plan.A = p->A;
+    plan.Dskip = p->Dskip;
+    plan.h0 = p->h0;
+    plan.reset = p->reset;
+    plan.out = p->out;
+    plan.h_last = p->h_last;
+    plan.nseg = 1;
+    plan.seg_len = p->seqlen;
+    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
 
   int nseg;
   int64_t seg_len;
@@ -497,12 +548,16 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   for (const auto& a : aligns)
     if (a.ptr && !aligned(a.ptr, a.align))
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
-  const Range inputs[] = {range(p->u, bd, si, "u"),         range(p->dt_raw, bd, si, "dt_raw"),
-                          range(p->z, bd, si, "z"),         range(p->dt_bias, p->dim, 4, "dt_bias"),
-                          range(p->A, dn, 4, "A"),          range(p->Dskip, p->dim, 4, "Dskip"),
-                          range(p->Bm, bn, si, "Bm"),       range(p->Cm, bn, si, "Cm")};
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
+  ssm_status s = check_kind(p->state_kind, p->discretization, p->conv_w != nullptr);
+  if (s != SSM_OK) return s;
+  const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
+  const int64_t ce = cplx ? 2 : 1;  // scalars per A, B, C and state entry
+  const Range inputs[] = {range(p->u, bd, si, "u"),         range(p->dt_raw, bd, si, "dt_raw"),
+                          range(p->z, bd, si, "z"),         range(p->dt_bias, p->dim, 4, "dt_bias"),
+                          range(p->A, dn * ce, 4, "A"),     range(p->Dskip, p->dim, 4, "Dskip"),
+                          range(p->Bm, bn * ce, si, "Bm"),  range(p->Cm, bn * ce, si, "Cm")};
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state))
@@ -513,7 +568,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
     if (q && !aligned(q, 4)) return fail(SSM_ERR_MISALIGNED, "a conv pointer is not aligned to 4 bytes");
   const Range cw = range(p->conv_w, p->dim * K, 4, "conv_w"), cb = range(p->conv_b, p->dim, 4, "conv_b");
   const Range cs = range(K > 1 ? p->conv_state : nullptr, bd * (K - 1), 4, "conv_state");
-  const Range h = range(p->h, bdn, 4, "h");
+  const Range h = range(p->h, bdn * ce, 4, "h");
   const Range out = range(p->out, bd, so, "out");
   for (const Range& r : inputs) {
     if (overlaps(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps %s", r.name);
@@ -547,7 +602,8 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   plan.conv_b = p->conv_b;
   plan.conv_k = static_cast<int>(K);
   plan.zoh = p->discretization == SSM_DISC_ZOH;
-  hipError_t e = ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
+  hipError_t e = cplx ? ssm::launch_state_update_cplx(plan, static_cast<hipStream_t>(hip_stream))
+                      : ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "state update launch failed: %s", hipGetErrorString(e));
   return ok();
 }

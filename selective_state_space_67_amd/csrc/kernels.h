@@ -1,5 +1,5 @@
 // Host-side interface between the C-ABI front end (api.cpp) and the HIP
-// kernels (scan_fwd.hip, state_update.hip). Not installed; not part of the ABI.
+// kernels (scan_fwd.hip, scan_bwd.hip, scan_cplx.hip, state_update.hip). Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -87,6 +87,13 @@ int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg);
 
 hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
 hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);
+
+// Complex diagonal state (scan_cplx.hip): A, B, C and the states hold
+// interleaved (re, im) pairs; the sequence is never split (nseg = 1) and the
+// conv, zero-order-hold and checkpoint fields are unused.
+int64_t cplx_scan_grid_blocks(int64_t B, int64_t D);
+hipError_t launch_scan_cplx(const ScanPlan& plan, hipStream_t stream);
+hipError_t launch_state_update_cplx(const UpdatePlan& plan, hipStream_t stream);
 
 // Backward pass (scan_bwd.hip). The checkpoint sweep runs through launch_scan
 // with ScanPlan::checkpoint set; BwdPlan describes the reverse sweep and the

@@ -1,0 +1,389 @@
+// Selective scan with a complex diagonal state (the S4D-Lin variant) for
+// gfx950: the full-sequence forward and the single-token decode step.
+//
+// The pages give this variant's initialisation, A = -1/2 + i n, and say a
+// complex state keeps phase information ("Technical analysis: Mamba selective
+// state spaces", sections 4.1 and 5.3). The recurrence is the real one with
+// complex A, B, C and h, real delta and u, and the real part of the read-out:
+//
+//   h[n] = exp(delta A[d,n]) h[n] + delta B[t,n] u
+//   out  = (Re sum_n C[t,n] h[n] + D[d] u) * silu(z)
+//
+// exp(delta A) = exp(delta Re A) (cos(delta Im A) + i sin(delta Im A)). The
+// angle is kept in revolutions: Im A / (2 pi) is held as an unevaluated sum
+// of two floats and its product with delta is formed with an exact FMA
+// remainder, so the angle reduced to [-1/2, 1/2] carries no rounding of the
+// product or of 1/(2 pi), only delta's own. Sine and cosine come from Taylor
+// polynomials on the quarter-turn-reduced angle (|theta| <= pi/4), accurate to
+// about an ulp and without bias. The hardware v_sin_f32 / v_cos_f32 are not
+// used: measured on gfx950, the cosine of small angles is low by about one
+// ulp on average and the sine of small angles is off by up to 1e-6 relative
+// (4.5e-5 for negative ones), and a biased decay compounds over the thousands
+// of steps a slowly decaying state remembers. What is left grows with the
+// angle: a relative error of a few float32 ulps in delta turns into a phase
+// error of that size times |delta Im A|.
+//
+// Mapping. A DPP row of 16 lanes owns one channel (b, d) and lane k holds the
+// NPL consecutive states k NPL .. k NPL + NPL - 1, so each lane reads its B
+// and C values as contiguous (re, im) pairs. All lanes of a row run the same
+// step together; the read-out is summed over the row with four DPP steps,
+// after which every lane holds it. A workgroup of 4 waves covers 16 channels
+// of one batch row, and B and C of each 16-step chunk are staged in LDS once
+// for all of them.
+//
+// Chunk items. Thread (channel c, lane k) stages step k of its channel's chunk
+// (delta with a reset flag in its sign bit, delta u) and keeps D u and
+// silu(z); after the chunk the same lane holds the read-out of that step
+// (selected while the steps go by) and writes the output. Lanes run their
+// recurrences in lockstep, so the row needs no skew.
+#include <algorithm>
+
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCPW = 16;  // channels per workgroup (one per DPP row)
+constexpr int kT = 16;    // steps per chunk (one per lane of a row)
+// 1 / (2 pi) as the sum of two floats (the second is the rounding error of the first).
+constexpr float kInv2PiHi = 0.15915494f;
+constexpr float kInv2PiLo = 0.15915494309189535 - static_cast<double>(0.15915494f);
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane gets the total.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
+// sin and cos of the angle delta (ai + ai_lo) revolutions. The product
+// p = delta ai is split into p and its exact rounding error; p - rint(p) is
+// exact and lies in [-1/2, 1/2]; q quarter turns are taken off exactly, and
+// the small parts are added to the remainder r, |r| <= 1/8 revolution. Then
+// theta = 2 pi r, sin and cos by their Taylor series through theta^9 and
+// theta^10 (truncation below 2e-9 and 1.2e-10 on |theta| <= pi/4), and a
+// rotation by q quarter turns.
+__device__ __forceinline__ void sincos_rev(float delta, float ai, float ai_lo, float& s, float& c) {
+  const float p = delta * ai;
+  const float lo = __builtin_fmaf(delta, ai, -p) + delta * ai_lo;
+  const float f = p - __builtin_rintf(p);
+  const float q = __builtin_rintf(4.0f * f);  // -2 .. 2
+  const float r = __builtin_fmaf(-0.25f, q, f) + lo;
+  const float th = r * 6.28318530717958648f;
+  const float t2 = th * th;
+  float sp = __builtin_fmaf(t2, 2.75573192e-6f, -1.98412698e-4f);
+  sp = __builtin_fmaf(t2, sp, 8.33333333e-3f);
+  sp = __builtin_fmaf(t2, sp, -1.66666667e-1f);
+  const float sn = __builtin_fmaf(th * t2, sp, th);
+  float cp = __builtin_fmaf(t2, -2.75573192e-7f, 2.48015873e-5f);
+  cp = __builtin_fmaf(t2, cp, -1.38888889e-3f);
+  cp = __builtin_fmaf(t2, cp, 4.16666667e-2f);
+  cp = __builtin_fmaf(t2, cp, -0.5f);
+  const float cs = __builtin_fmaf(t2, cp, 1.0f);
+  // (sin, cos) of theta + q pi/2: q = 1 -> (c, -s), 2 -> (-s, -c), 3 (= -1) -> (-c, s)
+  const int qi = static_cast<int>(q) & 3;
+  const float s2 = (qi & 1) ? cs : sn;
+  const float c2 = (qi & 1) ? sn : cs;
+  s = (qi & 2) ? -s2 : s2;
+  c = ((qi + 1) & 2) ? -c2 : c2;
+}
+
+struct CplxArgs {
+  int64_t B, D, L, N;
+  int out_bf16;
+  const void* u;
+  const void* dt;
+  const void* z;
+  const void* Bm;  // (B, L, N, 2)
+  const void* Cm;  // (B, L, N, 2)
+  const float* dt_bias;
+  const float* A;  // (D, N, 2)
+  const float* Dskip;
+  const float* h0;  // (B, D, N, 2) or null
+  const uint8_t* reset;
+  void* out;
+  float* h_last;  // (B, D, N, 2) or null
+  int n_dgroups;
+};
+
+// Per-lane constants of state n: Re A log2(e), and Im A / (2 pi) as ai + ai_lo
+// (ai rounded, ai_lo the rest to within float32 rounding); zero past N.
+template <int NPL>
+__device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0, bool dvalid, float (&ar)[NPL],
+                                       float (&ai)[NPL], float (&ai_lo)[NPL]) {
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int n = n0 + j;
+    const bool ok = dvalid && n < N;
+    const float im = ok ? A[2 * (d * N + n) + 1] : 0.0f;
+    ar[j] = ok ? A[2 * (d * N + n)] * kLog2e : 0.0f;
+    ai[j] = im * kInv2PiHi;
+    ai_lo[j] = __builtin_fmaf(im, kInv2PiHi, -ai[j]) + im * kInv2PiLo;
+  }
+}
+
+// One step of state j: h = exp(delta A) h + delta u B; returns Re(C h).
+__device__ __forceinline__ float cplx_step(float dl, float dv, float ar, float ai, float ai_lo, float2 Bv, float2 Cv,
+                                           float& hr, float& hi) {
+  const float e = fast_exp2(dl * ar);
+  float s, c;
+  sincos_rev(dl, ai, ai_lo, s, c);
+  const float are = e * c, aim = e * s;
+  const float nr = __builtin_fmaf(are, hr, __builtin_fmaf(-aim, hi, Bv.x * dv));
+  const float ni = __builtin_fmaf(are, hi, __builtin_fmaf(aim, hr, Bv.y * dv));
+  hr = nr;
+  hi = ni;
+  return __builtin_fmaf(Cv.x, nr, -Cv.y * ni);
+}
+
+template <int NPL, typename InT, bool HAS_RESET>
+__global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
+  constexpr int NPAD = 16 * NPL;
+  const int g = blockIdx.x % a.n_dgroups;
+  const int b = blockIdx.x / a.n_dgroups;
+  const int L = static_cast<int>(a.L);
+  const int N = static_cast<int>(a.N);
+  const int tid = threadIdx.x;
+  const int k = tid & 15;
+  const int c = tid >> 4;  // channel within the workgroup = DPP row
+  const int64_t d = static_cast<int64_t>(g) * kCPW + c;
+  const bool dvalid = d < a.D;
+  const int n0 = k * NPL;
+
+  // (B, C) of the chunk's steps per state, as (B.re, B.im, C.re, C.im); states
+  // past N stay zero.
+  __shared__ __align__(16) float4 s_bc[kT * NPAD];
+  __shared__ __align__(8) float2 s_du[kCPW * kT];  // (delta, delta u); delta negated on a reset step
+
+  float ar[NPL], ai[NPL], ai_lo[NPL], hr[NPL], hi[NPL];
+  load_A<NPL>(a.A, d, N, n0, dvalid, ar, ai, ai_lo);
+  const int64_t row = static_cast<int64_t>(b) * a.D + d;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const bool ok = dvalid && n0 + j < N && a.h0;
+    hr[j] = ok ? a.h0[2 * (row * N + n0 + j)] : 0.0f;
+    hi[j] = ok ? a.h0[2 * (row * N + n0 + j) + 1] : 0.0f;
+  }
+  for (int i = tid; i < kT * NPAD; i += kThreads) s_bc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  const InT* __restrict__ u = static_cast<const InT*>(a.u) + row * a.L;
+  const InT* __restrict__ dt = static_cast<const InT*>(a.dt) + row * a.L;
+  const InT* __restrict__ z = a.z ? static_cast<const InT*>(a.z) + row * a.L : nullptr;
+  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + static_cast<int64_t>(b) * a.L * N * 2;
+  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + static_cast<int64_t>(b) * a.L * N * 2;
+  const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
+  const float dsk = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
+
+  for (int t0 = 0; t0 < L; t0 += kT) {
+    const int steps = min(kT, L - t0);
+    __syncthreads();  // the previous chunk's readers are done
+    // B and C of steps t0 .. t0+steps-1: contiguous (steps, N, 2) blocks
+    for (int i = tid; i < steps * N; i += kThreads) {
+      const int tl = i / N, n = i - tl * N;
+      const int64_t e = (static_cast<int64_t>(t0 + tl) * N + n) * 2;
+      s_bc[tl * NPAD + n] = make_float4(load_elem(Bb, e), load_elem(Bb, e + 1), load_elem(Cb, e), load_elem(Cb, e + 1));
+    }
+    // this lane's row item: step t0 + k of channel d
+    const int t = t0 + k;
+    const bool live = dvalid && k < steps;
+    float dl = 0.0f, uu = 0.0f, gate = 1.0f;
+    if (live) {
+      uu = load_elem(u, t);
+      dl = softplus_f32(load_elem(dt, t) + bias);
+      if (z) gate = silu_f32(load_elem(z, t));
+      if (HAS_RESET && a.reset[static_cast<int64_t>(b) * a.L + t]) dl = -dl;
+    }
+    s_du[c * kT + k] = make_float2(dl, fabsf(dl) * uu);
+    __syncthreads();
+
+    float ymine = 0.0f;
+#pragma unroll 4
+    for (int tl = 0; tl < kT; ++tl) {
+      const float2 du = s_du[c * kT + tl];
+      float dlt = du.x;
+      if (HAS_RESET) {
+        const bool rs = __float_as_int(dlt) < 0;
+        if (__builtin_amdgcn_ballot_w64(rs)) {
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) {
+            hr[j] = rs ? 0.0f : hr[j];
+            hi[j] = rs ? 0.0f : hi[j];
+          }
+        }
+        dlt = fabsf(dlt);
+      }
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const float4 bc = s_bc[tl * NPAD + n0 + j];
+        p += cplx_step(dlt, du.y, ar[j], ai[j], ai_lo[j], make_float2(bc.x, bc.y), make_float2(bc.z, bc.w), hr[j],
+                       hi[j]);
+      }
+      p = row_sum16(p);
+      ymine = k == tl ? p : ymine;
+    }
+    if (live) {
+      const float v = (ymine + dsk * uu) * gate;
+      const int64_t o = row * a.L + t;
+      if (a.out_bf16)
+        store_elem(static_cast<bf16_t*>(a.out), o, v);
+      else
+        store_elem(static_cast<float*>(a.out), o, v);
+    }
+  }
+  if (a.h_last && dvalid) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      if (n0 + j < N) {
+        a.h_last[2 * (row * N + n0 + j)] = hr[j];
+        a.h_last[2 * (row * N + n0 + j) + 1] = hi[j];
+      }
+    }
+  }
+}
+
+struct CplxUpdateArgs {
+  int64_t B, D, N;
+  int out_bf16;
+  float* h;  // (B, D, N, 2), in place
+  const void* u;
+  const void* dt;
+  const void* z;
+  const float* dt_bias;
+  const float* A;  // (D, N, 2)
+  const float* Dskip;
+  const void* Bm;  // (B, N, 2)
+  const void* Cm;
+  void* out;
+};
+
+// Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup.
+template <int NPL, typename InT>
+__global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateArgs a) {
+  const int tid = threadIdx.x;
+  const int k = tid & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kCPW + (tid >> 4);
+  if (row >= a.B * a.D) return;  // whole DPP rows leave together
+  const int64_t b = row / a.D, d = row % a.D;
+  const int N = static_cast<int>(a.N);
+  const int n0 = k * NPL;
+  float ar[NPL], ai[NPL], ai_lo[NPL];
+  load_A<NPL>(a.A, d, N, n0, true, ar, ai, ai_lo);
+  const float uu = load_elem(static_cast<const InT*>(a.u), row);
+  const float dl = softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
+  const float dv = dl * uu;
+  const InT* Bb = static_cast<const InT*>(a.Bm) + b * N * 2;
+  const InT* Cb = static_cast<const InT*>(a.Cm) + b * N * 2;
+  float* h = a.h + row * N * 2;
+  float p = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int n = n0 + j;
+    if (n < N) {
+      float hr = h[2 * n], hi = h[2 * n + 1];
+      p += cplx_step(dl, dv, ar[j], ai[j], ai_lo[j], make_float2(load_elem(Bb, 2 * n), load_elem(Bb, 2 * n + 1)),
+                     make_float2(load_elem(Cb, 2 * n), load_elem(Cb, 2 * n + 1)), hr, hi);
+      h[2 * n] = hr;
+      h[2 * n + 1] = hi;
+    }
+  }
+  p = row_sum16(p);
+  if (k == 0) {
+    float v = p + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
+    if (a.z) v *= silu_f32(load_elem(static_cast<const InT*>(a.z), row));
+    if (a.out_bf16)
+      store_elem(static_cast<bf16_t*>(a.out), row, v);
+    else
+      store_elem(static_cast<float*>(a.out), row, v);
+  }
+}
+
+// States per lane: the smallest power of two with 16 NPL >= N.
+template <typename Fn>
+hipError_t with_npl(int64_t N, Fn&& fn) {
+  if (N <= 16) return fn(std::integral_constant<int, 1>{});
+  if (N <= 32) return fn(std::integral_constant<int, 2>{});
+  if (N <= 64) return fn(std::integral_constant<int, 4>{});
+  if (N <= 128) return fn(std::integral_constant<int, 8>{});
+  return fn(std::integral_constant<int, 16>{});
+}
+
+}  // namespace
+
+int64_t cplx_scan_grid_blocks(int64_t B, int64_t D) { return B * ((D + kCPW - 1) / kCPW); }
+
+hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
+  CplxArgs a{};
+  a.B = p.B;
+  a.D = p.D;
+  a.L = p.L;
+  a.N = p.N;
+  a.out_bf16 = p.out_bf16;
+  a.u = p.u;
+  a.dt = p.dt;
+  a.z = p.z;
+  a.Bm = p.Bm;
+  a.Cm = p.Cm;
+  a.dt_bias = p.dt_bias;
+  a.A = p.A;
+  a.Dskip = p.Dskip;
+  a.h0 = p.h0;
+  a.reset = p.reset;
+  a.out = p.out;
+  a.h_last = p.h_last;
+  a.n_dgroups = static_cast<int>((p.D + kCPW - 1) / kCPW);
+  const dim3 grid(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D)));
+  return with_npl(p.N, [&](auto npl) {
+    constexpr int NPL = decltype(npl)::value;
+    if (p.in_bf16) {
+      if (p.reset)
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, bf16_t, true>), grid, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, bf16_t, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (p.reset)
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, float, true>), grid, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, float, false>), grid, dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
+  CplxUpdateArgs a{};
+  a.B = p.B;
+  a.D = p.D;
+  a.N = p.N;
+  a.out_bf16 = p.out_bf16;
+  a.h = p.h;
+  a.u = p.u;
+  a.dt = p.dt;
+  a.z = p.z;
+  a.dt_bias = p.dt_bias;
+  a.A = p.A;
+  a.Dskip = p.Dskip;
+  a.Bm = p.Bm;
+  a.Cm = p.Cm;
+  a.out = p.out;
+  const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
+  return with_npl(p.N, [&](auto npl) {
+    constexpr int NPL = decltype(npl)::value;
+    if (p.in_bf16)
+      hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((cplx_update_kernel<NPL, float>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace ssm

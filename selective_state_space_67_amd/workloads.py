@@ -19,6 +19,12 @@ draws in this order, all in float64 before the cast to the storage dtype:
 
 The decode workload uses the same draws at (B, D) / (B, N) plus an initial
 state h ~ N(0, 1) in float32, drawn last.
+
+Complex-state workloads (the S4D-Lin variant) draw u, dt_raw, z as above, then
+the real and the imaginary parts of Bm and of Cm, each N(0, 1) with shape
+(B, L, N) (order: Bm.re, Bm.im, Cm.re, Cm.im), then dt_bias and resets as
+above; A[d, n] = -1/2 + i n (S4D-Lin) and Dskip = 1. Complex values are stored
+as a trailing (re, im) axis. Decode adds h (re, im) ~ N(0, 1), drawn last.
 """
 from __future__ import annotations
 
@@ -130,6 +136,51 @@ def config_inputs(index: int, **overrides):
     return make_scan_inputs(c["B"], c["D"], c["L"], c["N"], dtype=c["dtype"],
                             seed=c.get("seed", index), dt_lo=c["dt_lo"], dt_hi=c["dt_hi"],
                             packed=c["packed"])
+
+
+def s4d_lin_A(D, N):
+    """A[d, n] = -1/2 + i n as (D, N, 2) float32 (re, im) pairs."""
+    A = np.empty((D, N, 2), dtype=np.float32)
+    A[..., 0] = -0.5
+    A[..., 1] = np.arange(N, dtype=np.float32)[None, :]
+    return A
+
+
+def make_cplx_inputs(B, D, L, N, dtype=F32, seed=0, dt_lo=1e-3, dt_hi=1e-1, packed=False, with_z=True):
+    """Inputs of one complex-state scan workload in storage format (numpy, host)."""
+    rng = np.random.default_rng(seed)
+    u = store(rng.standard_normal((B, D, L)), dtype)
+    dt_raw = store(rng.standard_normal((B, D, L)), dtype)
+    z = store(rng.standard_normal((B, D, L)), dtype)
+    parts = [rng.standard_normal((B, L, N)) for _ in range(4)]
+    Bm = store(np.stack(parts[:2], axis=-1), dtype)
+    Cm = store(np.stack(parts[2:], axis=-1), dtype)
+    dt_bias = dt_bias_draw(rng, D, dt_lo, dt_hi)
+    reset = doc_resets(rng, B, L) if packed else None
+    return dict(u=u, dt_raw=dt_raw, z=z if with_z else None, Bm=Bm, Cm=Cm, dt_bias=dt_bias,
+                A=s4d_lin_A(D, N), Dskip=np.ones(D, dtype=np.float32), reset=reset, dtype=dtype)
+
+
+def make_cplx_decode_inputs(B, D, N, dtype=BF16, seed=5, dt_lo=1e-3, dt_hi=1e-1, with_z=True):
+    rng = np.random.default_rng(seed)
+    u = store(rng.standard_normal((B, D)), dtype)
+    dt_raw = store(rng.standard_normal((B, D)), dtype)
+    z = store(rng.standard_normal((B, D)), dtype)
+    parts = [rng.standard_normal((B, N)) for _ in range(4)]
+    Bm = store(np.stack(parts[:2], axis=-1), dtype)
+    Cm = store(np.stack(parts[2:], axis=-1), dtype)
+    dt_bias = dt_bias_draw(rng, D, dt_lo, dt_hi)
+    h = rng.standard_normal((B, D, N, 2)).astype(np.float32)
+    return dict(u=u, dt_raw=dt_raw, z=z if with_z else None, Bm=Bm, Cm=Cm, dt_bias=dt_bias,
+                A=s4d_lin_A(D, N), Dskip=np.ones(D, dtype=np.float32), h=h, dtype=dtype)
+
+
+def as_complex(x):
+    """A (..., 2) (re, im) array (float32 or bf16 bits) as complex128, exactly."""
+    if x is None:
+        return None
+    w = widen(x)
+    return w[..., 0] + 1j * w[..., 1]
 
 
 def make_decode_inputs(B, D, N, dtype=BF16, seed=5, dt_lo=1e-3, dt_hi=1e-1, with_z=True):

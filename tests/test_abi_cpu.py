@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10100
+    assert lib.ssm_version() == 10200
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -358,3 +358,39 @@ def test_unknown_discretization(lib):
     assert bwd_status(lib, bwd_params(discretization=7)) == 5
     n = ctypes.c_size_t(0)
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(bwd_params(discretization=7)), ctypes.byref(n)) == 5
+
+
+def test_unknown_state_kind(lib):
+    assert scan_status(lib, scan_params(state_kind=2)) == 5
+    assert update_status(lib, update_params(state_kind=-1)) == 5
+    n = ctypes.c_size_t(0)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(scan_params(state_kind=3)), ctypes.byref(n)) == 5
+
+
+def test_complex_state_unsupported_combinations(lib):
+    cplx = bd.SSM_STATE_COMPLEX
+    assert scan_status(lib, scan_params(state_kind=cplx, discretization=bd.SSM_DISC_ZOH)) == 5
+    assert scan_status(lib, scan_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=4)) == 5
+    assert update_status(lib, update_params(state_kind=cplx, discretization=bd.SSM_DISC_ZOH)) == 5
+    assert update_status(lib, update_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=1)) == 5
+    assert bwd_status(lib, bwd_params(state_kind=cplx)) == 5        # no complex backward
+    n = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(bwd_params(state_kind=cplx)), ctypes.byref(n)) == 5
+
+
+def test_complex_state_needs_no_workspace(lib):
+    n = ctypes.c_size_t(123)
+    p = scan_params(state_kind=bd.SSM_STATE_COMPLEX, num_segments=8)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_complex_state_extents_are_doubled(lib):
+    # out starts inside the second (imaginary) half of A's complex extent: an
+    # alias only when A holds (re, im) pairs. Both calls fail validation.
+    p = scan_params(state_kind=bd.SSM_STATE_COMPLEX, dt_bias=None, Dskip=None)
+    p.out = p.A + D * N * 4
+    assert scan_status(lib, p) == 7
+    q = update_params(state_kind=bd.SSM_STATE_COMPLEX)
+    q.out = q.h + B * D * N * 4
+    assert update_status(lib, q) == 7
