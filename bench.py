@@ -272,6 +272,24 @@ def main():
     zsec_b = timed(bzoh, bsteps)
     del bwd, dout, fzoh, bzoh
 
+    # Complex diagonal state (S4D-Lin A = -1/2 + i n) at the same shape, and its decode step.
+    xc = wl.make_cplx_inputs(B, D, L, N, cfg["dtype"], seed=cfg.get("seed", args.config), dt_lo=cfg["dt_lo"],
+                             dt_hi=cfg["dt_hi"], packed=cfg["packed"])
+    tc = {k: wl.to_torch(xc[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
+    fcx = binding.prepare_scan(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], dt_bias=tc["dt_bias"],
+                               Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True)
+    xsec_f = timed(fcx, max(5, min(args.steps, 30)))
+    del fcx, tc, xc
+    yc = wl.make_cplx_decode_inputs(Bd, Dd, Nd, wl.BF16, seed=5)
+    tdc = {k: wl.to_torch(yc[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    hdc = torch.from_numpy(yc["h"]).to(dev)
+    dcx = binding.prepare_state_update(hdc, tdc["u"], tdc["dt_raw"], tdc["A"], tdc["Bm"], tdc["Cm"],
+                                       dt_bias=tdc["dt_bias"], Dskip=tdc["Dskip"], z=tdc["z"], complex_state=True)
+    xsec_d = timed(dcx, 50)
+    # state (B, D, N, 2) read and written, plus the per-row inputs, complex B, C and A
+    xdbytes = 16 * Bd * Dd * Nd + 3 * Bd * Dd * 2 + 2 * Bd * Nd * 2 * 2 + 8 * Dd * Nd + 8 * Dd + Bd * Dd * 4
+    del dcx, tdc, hdc, yc
+
     result = {
         "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
         "value": elements / wall,
@@ -325,6 +343,13 @@ def main():
                 "fwd_ms": zsec_f * 1e3, "fwd_vs_plain_forward": zsec_f / launch_s,
                 "fwd_elements_per_s": elements / zsec_f, "bwd_ms": zsec_b * 1e3,
                 "bwd_vs_plain_backward": zsec_b / bsec},
+        "complex_state": {"workload": "the same shape with a complex diagonal state: A = -1/2 + i n (S4D-Lin), "
+                                      "complex B, C (re, im pairs), y = Re(C h)",
+                          "fwd_ms": xsec_f * 1e3, "fwd_vs_plain_forward": xsec_f / launch_s,
+                          "fwd_elements_per_s": elements / xsec_f,
+                          "decode_workload": "state update B=64 D=2048 N=128 complex, bf16 inputs, fp32 state",
+                          "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes,
+                          "decode_hbm_gbps": xdbytes / xsec_d / 1e9},
     }
 
     if not args.no_cpu:

@@ -266,7 +266,19 @@ struct CplxUpdateArgs {
   void* out;
 };
 
-// Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup.
+// One complex value stored as an (re, im) pair of the input type, widened.
+__device__ __forceinline__ float2 load_cpair(const float* p, int64_t n) {
+  return *reinterpret_cast<const float2*>(p + 2 * n);
+}
+__device__ __forceinline__ float2 load_cpair(const bf16_t* p, int64_t n) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2 * n);
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+}
+
+// Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup. Lane
+// k holds states k, k + 16, k + 32, ..., so for each j the 16 lanes of a row
+// read 16 consecutive (re, im) pairs of h, A, B and C: coalesced accesses to
+// the state, which is what the step moves.
 template <int NPL, typename InT>
 __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateArgs a) {
   const int tid = threadIdx.x;
@@ -275,26 +287,33 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
   if (row >= a.B * a.D) return;  // whole DPP rows leave together
   const int64_t b = row / a.D, d = row % a.D;
   const int N = static_cast<int>(a.N);
-  const int n0 = k * NPL;
-  float ar[NPL], ai[NPL], ai_lo[NPL];
-  load_A<NPL>(a.A, d, N, n0, true, ar, ai, ai_lo);
+  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + b * N * 2;
+  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + b * N * 2;
+  const float* __restrict__ Ad = a.A + d * N * 2;
+  float* __restrict__ h = a.h + row * N * 2;
+  float2 hv[NPL], av[NPL], bv[NPL], cv[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int n = k + 16 * j;
+    const bool ok = n < N;
+    const float2 zero = make_float2(0.0f, 0.0f);
+    hv[j] = ok ? *reinterpret_cast<const float2*>(h + 2 * n) : zero;
+    av[j] = ok ? *reinterpret_cast<const float2*>(Ad + 2 * n) : zero;
+    bv[j] = ok ? load_cpair(Bb, n) : zero;
+    cv[j] = ok ? load_cpair(Cb, n) : zero;
+  }
   const float uu = load_elem(static_cast<const InT*>(a.u), row);
   const float dl = softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
   const float dv = dl * uu;
-  const InT* Bb = static_cast<const InT*>(a.Bm) + b * N * 2;
-  const InT* Cb = static_cast<const InT*>(a.Cm) + b * N * 2;
-  float* h = a.h + row * N * 2;
   float p = 0.0f;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const int n = n0 + j;
-    if (n < N) {
-      float hr = h[2 * n], hi = h[2 * n + 1];
-      p += cplx_step(dl, dv, ar[j], ai[j], ai_lo[j], make_float2(load_elem(Bb, 2 * n), load_elem(Bb, 2 * n + 1)),
-                     make_float2(load_elem(Cb, 2 * n), load_elem(Cb, 2 * n + 1)), hr, hi);
-      h[2 * n] = hr;
-      h[2 * n + 1] = hi;
-    }
+    const int n = k + 16 * j;
+    const float ai = av[j].y * kInv2PiHi;
+    const float ai_lo = __builtin_fmaf(av[j].y, kInv2PiHi, -ai) + av[j].y * kInv2PiLo;
+    float hr = hv[j].x, hi = hv[j].y;
+    p += cplx_step(dl, dv, av[j].x * kLog2e, ai, ai_lo, bv[j], cv[j], hr, hi);
+    if (n < N) *reinterpret_cast<float2*>(h + 2 * n) = make_float2(hr, hi);
   }
   p = row_sum16(p);
   if (k == 0) {
