@@ -104,9 +104,10 @@ typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
  *                       y_t    = Re(sum_n C[b,t,n] h_t[n]) + D[d] u
  *                     with the same gate and resets. This build supports it
  *                     with SSM_DISC_DELTA_B and no conv stage, in ssm_scan_fwd
- *                     (which then never splits the sequence and needs no
- *                     workspace) and ssm_state_update; other combinations, and
- *                     the backward, return SSM_ERR_UNSUPPORTED.
+ *                     (whose workspace then holds complex aggregates; ask
+ *                     ssm_scan_workspace_size with state_kind set) and
+ *                     ssm_state_update; other combinations, and the backward,
+ *                     return SSM_ERR_UNSUPPORTED.
  * Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 
@@ -177,8 +178,8 @@ typedef struct {
 } ssm_scan_params;
 
 /* Bytes of workspace ssm_scan_fwd needs for these parameters (0 when the scan
- * does not split the sequence). Only the sizes, dtypes and num_segments of
- * `p` are read. */
+ * does not split the sequence). Only the sizes, dtypes, num_segments and
+ * state_kind of `p` are read. */
 ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes);
 
 /* Enqueue the scan described by `p` on `hip_stream`. */

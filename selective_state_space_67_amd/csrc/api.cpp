@@ -99,6 +99,13 @@ ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
 
 ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
   if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
+  if (p->state_kind == SSM_STATE_COMPLEX) {
+    ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+    if (ssm::cplx_scan_grid_blocks(p->batch, p->dim, *nseg) > std::numeric_limits<int32_t>::max())
+      return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+    *ws = ssm::cplx_workspace_bytes(p->batch, p->dim, p->dstate, *nseg);
+    return SSM_OK;
+  }
   ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
   if (ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg) > std::numeric_limits<int32_t>::max())
     return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
@@ -365,10 +372,6 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
   if (!valid_kind(p->state_kind)) return fail(SSM_ERR_UNSUPPORTED, "unknown state_kind %d", p->state_kind);
-  if (p->state_kind == SSM_STATE_COMPLEX) {  // never splits the sequence
-    *bytes = 0;
-    return ok();
-  }
   int nseg;
   int64_t seg_len;
   size_t ws;
@@ -437,35 +440,6 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
   if (overlaps(out, cso) || overlaps(hl, cso)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
 
-  if (cplx) {
-    if (ssm::cplx_scan_grid_blocks(p->batch, p->dim) > std::numeric_limits<int32_t>::max())
-      return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
-    ssm::ScanPlan plan{};
-    plan.B = p->batch;
-    plan.D = p->dim;
-    plan.L = p->seqlen;
-    plan.N = p->dstate;
-    plan.in_bf16 = p->in_dtype == SSM_BF16;
-    plan.out_bf16 = p->out_dtype == SSM_BF16;
-    plan.u = p->u;
-    plan.dt = p->dt_raw;
-    plan.z = p->z;
-    plan.Bm = p->Bm;
-    plan.Cm = p->Cm;
-    plan.dt_bias = p->dt_bias;
-    plan.A = p->A;
-    plan.Dskip = p->Dskip;
-    plan.h0 = p->h0;
-    plan.reset = p->reset;
-    plan.out = p->out;
-    plan.h_last = p->h_last;
-    plan.nseg = 1;
-    plan.seg_len = p->seqlen;
-    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
-    return ok();
-  }
-
   int nseg;
   int64_t seg_len;
   size_t ws;
@@ -503,6 +477,11 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
   plan.nseg = nseg;
   plan.seg_len = seg_len;
+  if (cplx) {
+    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   plan.conv_w = p->conv_w;
   plan.conv_b = p->conv_b;
   plan.conv_state_in = p->conv_state_in;

@@ -89,9 +89,12 @@ hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
 hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);
 
 // Complex diagonal state (scan_cplx.hip): A, B, C and the states hold
-// interleaved (re, im) pairs; the sequence is never split (nseg = 1) and the
-// conv, zero-order-hold and checkpoint fields are unused.
-int64_t cplx_scan_grid_blocks(int64_t B, int64_t D);
+// interleaved (re, im) pairs; `ws` holds the complex per-piece aggregates when
+// nseg > 1 (P then H, each (nseg - 1, B, D, N, 2)); the conv, zero-order-hold
+// and checkpoint fields are unused.
+void plan_cplx_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg, int64_t* seg_len);
+size_t cplx_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg);
+int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg);
 hipError_t launch_scan_cplx(const ScanPlan& plan, hipStream_t stream);
 hipError_t launch_state_update_cplx(const UpdatePlan& plan, hipStream_t stream);
 

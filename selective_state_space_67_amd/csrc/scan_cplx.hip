@@ -113,6 +113,10 @@ struct CplxArgs {
   void* out;
   float* h_last;  // (B, D, N, 2) or null
   int n_dgroups;
+  int64_t seg_len;  // steps per piece when the sequence is split (the last may be shorter)
+  int nseg;
+  float* ws_P;  // (nseg - 1, B, D, N, 2): the decay product of pieces 0 .. nseg-2
+  float* ws_H;  // (nseg - 1, B, D, N, 2): their end states from a zero start
 };
 
 // Per-lane constants of state n: Re A log2(e), and Im A / (2 pi) as ai + ai_lo
@@ -145,12 +149,20 @@ __device__ __forceinline__ float cplx_step(float dl, float dv, float ar, float a
   return __builtin_fmaf(Cv.x, nr, -Cv.y * ni);
 }
 
-template <int NPL, typename InT, bool HAS_RESET>
+// Long sequences with few channels are split into pieces like the real scan:
+// a first launch (AGG) runs each piece from a zero state and keeps only its
+// affine aggregate, the decay product P = exp(A sum delta) (0 after a reset)
+// and the end state H; the full launch folds the aggregates of the preceding
+// pieces into its starting state, h <- P h + H, and runs its piece.
+template <int NPL, typename InT, bool HAS_RESET, bool AGG>
 __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   constexpr int NPAD = 16 * NPL;
   const int g = blockIdx.x % a.n_dgroups;
-  const int b = blockIdx.x / a.n_dgroups;
-  const int L = static_cast<int>(a.L);
+  const int rest = blockIdx.x / a.n_dgroups;
+  const int b = rest % static_cast<int>(a.B);
+  const int sp = rest / static_cast<int>(a.B);  // piece
+  const int64_t t_seg = static_cast<int64_t>(sp) * a.seg_len;
+  const int Lseg = static_cast<int>(min(a.seg_len, a.L - t_seg));
   const int N = static_cast<int>(a.N);
   const int tid = threadIdx.x;
   const int k = tid & 15;
@@ -169,22 +181,37 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   const int64_t row = static_cast<int64_t>(b) * a.D + d;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const bool ok = dvalid && n0 + j < N && a.h0;
-    hr[j] = ok ? a.h0[2 * (row * N + n0 + j)] : 0.0f;
-    hi[j] = ok ? a.h0[2 * (row * N + n0 + j) + 1] : 0.0f;
+    const int64_t e = 2 * (row * N + n0 + j);
+    const bool ok = !AGG && dvalid && n0 + j < N;
+    hr[j] = ok && a.h0 ? a.h0[e] : 0.0f;
+    hi[j] = ok && a.h0 ? a.h0[e + 1] : 0.0f;
+    if (ok) {
+      for (int q = 0; q < sp; ++q) {  // h <- P h + H for the preceding pieces
+        const int64_t w = static_cast<int64_t>(q) * a.B * a.D * N * 2 + e;
+        const float pr = a.ws_P[w], pi = a.ws_P[w + 1];
+        const float nr = __builtin_fmaf(pr, hr[j], __builtin_fmaf(-pi, hi[j], a.ws_H[w]));
+        const float ni = __builtin_fmaf(pr, hi[j], __builtin_fmaf(pi, hr[j], a.ws_H[w + 1]));
+        hr[j] = nr;
+        hi[j] = ni;
+      }
+    }
   }
   for (int i = tid; i < kT * NPAD; i += kThreads) s_bc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  const InT* __restrict__ u = static_cast<const InT*>(a.u) + row * a.L;
-  const InT* __restrict__ dt = static_cast<const InT*>(a.dt) + row * a.L;
-  const InT* __restrict__ z = a.z ? static_cast<const InT*>(a.z) + row * a.L : nullptr;
-  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + static_cast<int64_t>(b) * a.L * N * 2;
-  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + static_cast<int64_t>(b) * a.L * N * 2;
+  const InT* __restrict__ u = static_cast<const InT*>(a.u) + row * a.L + t_seg;
+  const InT* __restrict__ dt = static_cast<const InT*>(a.dt) + row * a.L + t_seg;
+  const InT* __restrict__ z = a.z ? static_cast<const InT*>(a.z) + row * a.L + t_seg : nullptr;
+  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + (static_cast<int64_t>(b) * a.L + t_seg) * N * 2;
+  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + (static_cast<int64_t>(b) * a.L + t_seg) * N * 2;
+  const uint8_t* __restrict__ rs = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L + t_seg : nullptr;
+  // AGG: this lane's compensated (Kahan) sum of delta over its steps, and whether one of them resets
+  float dsum = 0.0f, dcomp = 0.0f;
+  bool cleared = false;
   const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
   const float dsk = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
 
-  for (int t0 = 0; t0 < L; t0 += kT) {
-    const int steps = min(kT, L - t0);
+  for (int t0 = 0; t0 < Lseg; t0 += kT) {
+    const int steps = min(kT, Lseg - t0);
     __syncthreads();  // the previous chunk's readers are done
     // B and C of steps t0 .. t0+steps-1: contiguous (steps, N, 2) blocks
     for (int i = tid; i < steps * N; i += kThreads) {
@@ -199,8 +226,17 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
     if (live) {
       uu = load_elem(u, t);
       dl = softplus_f32(load_elem(dt, t) + bias);
-      if (z) gate = silu_f32(load_elem(z, t));
-      if (HAS_RESET && a.reset[static_cast<int64_t>(b) * a.L + t]) dl = -dl;
+      if (!AGG && z) gate = silu_f32(load_elem(z, t));
+      if constexpr (AGG) {
+        const float yk = dl - dcomp;
+        const float tk = dsum + yk;
+        dcomp = (tk - dsum) - yk;
+        dsum = tk;
+      }
+      if (HAS_RESET && rs[t]) {
+        dl = -dl;
+        cleared = true;
+      }
     }
     s_du[c * kT + k] = make_float2(dl, fabsf(dl) * uu);
     __syncthreads();
@@ -228,19 +264,41 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
         p += cplx_step(dlt, du.y, ar[j], ai[j], ai_lo[j], make_float2(bc.x, bc.y), make_float2(bc.z, bc.w), hr[j],
                        hi[j]);
       }
-      p = row_sum16(p);
-      ymine = k == tl ? p : ymine;
+      if constexpr (!AGG) {
+        p = row_sum16(p);
+        ymine = k == tl ? p : ymine;
+      }
     }
-    if (live) {
+    if (!AGG && live) {
       const float v = (ymine + dsk * uu) * gate;
-      const int64_t o = row * a.L + t;
+      const int64_t o = row * a.L + t_seg + t;
       if (a.out_bf16)
         store_elem(static_cast<bf16_t*>(a.out), o, v);
       else
         store_elem(static_cast<float*>(a.out), o, v);
     }
   }
-  if (a.h_last && dvalid) {
+  if constexpr (AGG) {
+    // The piece's decay product exp(A S), S = its sum of delta (0 after a reset).
+    const float S = row_sum16(dsum) - row_sum16(dcomp);
+    const bool any_reset = __builtin_amdgcn_ballot_w64(cleared) & (0xFFFFull << (16 * ((tid >> 4) & 3)));
+    if (dvalid) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        if (n0 + j >= N) continue;
+        const int64_t w = static_cast<int64_t>(sp) * a.B * a.D * N * 2 + 2 * (row * N + n0 + j);
+        float sn, cs;
+        sincos_rev(S, ai[j], ai_lo[j], sn, cs);
+        const float e = any_reset ? 0.0f : fast_exp2(S * ar[j]);
+        a.ws_P[w] = e * cs;
+        a.ws_P[w + 1] = e * sn;
+        a.ws_H[w] = hr[j];
+        a.ws_H[w + 1] = hi[j];
+      }
+    }
+    return;
+  }
+  if (a.h_last && dvalid && sp == a.nseg - 1) {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       if (n0 + j < N) {
@@ -338,7 +396,38 @@ hipError_t with_npl(int64_t N, Fn&& fn) {
 
 }  // namespace
 
-int64_t cplx_scan_grid_blocks(int64_t B, int64_t D) { return B * ((D + kCPW - 1) / kCPW); }
+// Pieces of the sequence. Splitting costs an aggregate pass nearly as long
+// as the scan itself (the rotation dominates both), so it pays only where the
+// channels leave CUs idle or short of the waves that hide latency: aim for
+// about 4 / NPL workgroups per CU (at least one), split only when the
+// channels fill less than half of that, and keep pieces >= 512 steps and a
+// multiple of 16. With several states per lane (N > 32) one workgroup per CU
+// already has the independent work it needs.
+void plan_cplx_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg, int64_t* seg_len) {
+  int64_t want;
+  if (requested > 0) {
+    want = requested;
+  } else {
+    const int64_t npl = N <= 16 ? 1 : N <= 32 ? 2 : 4;
+    const int64_t blocks = B * ((D + kCPW - 1) / kCPW);
+    const int64_t round = 256 * std::max<int64_t>(1, 4 / npl);
+    want = 2 * blocks >= round ? 1 : round / blocks;
+    want = std::min<int64_t>(want, std::max<int64_t>(1, L / 512));
+  }
+  want = std::max<int64_t>(1, std::min<int64_t>(want, (L + 15) / 16));
+  int64_t len = (L + want - 1) / want;
+  len = (len + 15) / 16 * 16;
+  *seg_len = len;
+  *nseg = static_cast<int>((L + len - 1) / len);
+}
+
+size_t cplx_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg) {
+  if (nseg <= 1) return 0;
+  return static_cast<size_t>(2) * static_cast<size_t>(nseg - 1) * static_cast<size_t>(B) * static_cast<size_t>(D) *
+         static_cast<size_t>(N) * 2 * sizeof(float);
+}
+
+int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg) { return B * ((D + kCPW - 1) / kCPW) * nseg; }
 
 hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
   CplxArgs a{};
@@ -360,21 +449,31 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
   a.out = p.out;
   a.h_last = p.h_last;
   a.n_dgroups = static_cast<int>((p.D + kCPW - 1) / kCPW);
-  const dim3 grid(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D)));
+  a.nseg = p.nseg;
+  a.seg_len = p.seg_len;
+  if (p.nseg > 1) {
+    const size_t half = cplx_workspace_bytes(p.B, p.D, p.N, p.nseg) / 2 / sizeof(float);
+    a.ws_P = p.ws;
+    a.ws_H = p.ws + half;
+  }
+  const dim3 grid(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg)));
+  const dim3 grid_agg(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg - 1)));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
-    if (p.in_bf16) {
-      if (p.reset)
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, bf16_t, true>), grid, dim3(kThreads), 0, stream, a);
-      else
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, bf16_t, false>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-      if (p.reset)
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, float, true>), grid, dim3(kThreads), 0, stream, a);
-      else
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, float, false>), grid, dim3(kThreads), 0, stream, a);
-    }
-    return hipGetLastError();
+    auto run = [&](auto in_t, auto has_reset) {
+      using InT = decltype(in_t);
+      constexpr bool R = decltype(has_reset)::value;
+      if (p.nseg > 1) {  // the last piece's aggregate is never needed
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true>), grid_agg, dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false>), grid, dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    };
+    if (p.in_bf16)
+      return p.reset ? run(bf16_t{}, std::true_type{}) : run(bf16_t{}, std::false_type{});
+    return p.reset ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
   });
 }
 

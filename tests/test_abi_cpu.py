@@ -378,10 +378,16 @@ def test_complex_state_unsupported_combinations(lib):
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(bwd_params(state_kind=cplx)), ctypes.byref(n)) == 5
 
 
-def test_complex_state_needs_no_workspace(lib):
-    n = ctypes.c_size_t(123)
-    p = scan_params(state_kind=bd.SSM_STATE_COMPLEX, num_segments=8)
+def test_complex_state_workspace(lib):
+    # a split complex scan keeps complex aggregates: P and H for all pieces but the last
+    n = ctypes.c_size_t(0)
+    p = scan_params(state_kind=bd.SSM_STATE_COMPLEX, num_segments=4)   # L = 64: four 16-step pieces
     assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * B * D * N * 2 * 4
+    p.workspace, p.workspace_bytes = BASE + 0x40000000, n.value - 4
+    assert scan_status(lib, p) == 6                 # too small: rejected before any launch
+    q = scan_params(state_kind=bd.SSM_STATE_COMPLEX, num_segments=1)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == 0
     assert n.value == 0
 
 
