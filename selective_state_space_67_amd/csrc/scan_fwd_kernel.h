@@ -148,8 +148,16 @@ __device__ __forceinline__ float conv_pre(const float (&w)[4], float bias, float
   return acc;
 }
 
+// The checkpoint sweep keeps more per-state values live (the segment's decay
+// product and adjoint sum), so with several states per lane it gets the
+// register budget of two waves per SIMD.
+template <typename TL, int MODE>
+constexpr int kernel_waves_per_simd() {
+  return MODE == kCheckpoint && TL::NPL >= 2 ? 2 : TL::MIN_WAVES_PER_SIMD;
+}
+
 template <typename TL, typename InT, bool HAS_RESET, int MODE, bool CONV, bool ZOH>
-__global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kernel(const ScanArgs a) {
+__global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE>())) void scan_kernel(const ScanArgs a) {
   constexpr int NPL = TL::NPL, RPC = TL::RPC, CPW = TL::CPW, THREADS = TL::THREADS;
   constexpr int T = TL::T, RING = TL::RING, NPAD = TL::NPAD;
   constexpr int MASK = RING - 1;
@@ -587,27 +595,52 @@ __global__ __launch_bounds__(TL::THREADS, TL::MIN_WAVES_PER_SIMD) void scan_kern
           for (int j = 0; j < NPL; ++j)
             if (dvalid && nbase + j < N) a.ckpt[ci * N + nbase + j] = h[j];
         }
-        const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
-        const float4 d23 = *reinterpret_cast<const float4*>(du_row + m + 2);
-        const float4 dy4 = *reinterpret_cast<const float4*>(dy_row + m);
-        float B0[NPL], B1[NPL], B2[NPL], B3[NPL], C0[NPL], C1[NPL], C2[NPL], C3[NPL];
+        if constexpr (NPL == 1) {
+          const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
+          const float4 d23 = *reinterpret_cast<const float4*>(du_row + m + 2);
+          const float4 dy4 = *reinterpret_cast<const float4*>(dy_row + m);
+          float B0[NPL], B1[NPL], B2[NPL], B3[NPL], C0[NPL], C1[NPL], C2[NPL], C3[NPL];
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-          const float4 vb = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
-          const float4 vc = *reinterpret_cast<const float4*>(c_row + j * B_STRIDE + m);
-          B0[j] = vb.x;
-          B1[j] = vb.y;
-          B2[j] = vb.z;
-          B3[j] = vb.w;
-          C0[j] = vc.x;
-          C1[j] = vc.y;
-          C2[j] = vc.z;
-          C3[j] = vc.w;
+          for (int j = 0; j < NPL; ++j) {
+            const float4 vb = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
+            const float4 vc = *reinterpret_cast<const float4*>(c_row + j * B_STRIDE + m);
+            B0[j] = vb.x;
+            B1[j] = vb.y;
+            B2[j] = vb.z;
+            B3[j] = vb.w;
+            C0[j] = vc.x;
+            C1[j] = vc.y;
+            C2[j] = vc.z;
+            C3[j] = vc.w;
+          }
+          step_ck(d01.x, d01.y, dy4.x, B0, C0);
+          step_ck(d01.z, d01.w, dy4.y, B1, C1);
+          step_ck(d23.x, d23.y, dy4.z, B2, C2);
+          step_ck(d23.z, d23.w, dy4.w, B3, C3);
+        } else {
+          // Several states per lane: two steps per group of reads, so that
+          // fewer B and C values are live at once (no spills at the register
+          // budget of two waves per SIMD).
+#pragma unroll
+          for (int i2 = 0; i2 < 4; i2 += 2) {
+            const float4 d01 = *reinterpret_cast<const float4*>(du_row + m + i2);
+            const float2 dy2 = *reinterpret_cast<const float2*>(dy_row + m + i2);
+            float B0[NPL], B1[NPL], C0[NPL], C1[NPL];
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+              const float2 vb = *reinterpret_cast<const float2*>(b_row + j * B_STRIDE + m + i2);
+              const float2 vc = *reinterpret_cast<const float2*>(c_row + j * B_STRIDE + m + i2);
+              B0[j] = vb.x;
+              B1[j] = vb.y;
+              C0[j] = vc.x;
+              C1[j] = vc.y;
+            }
+            step_ck(d01.x, d01.y, dy2.x, B0, C0);
+            step_ck(d01.z, d01.w, dy2.y, B1, C1);
+            // keep the next group's reads from being hoisted above this one
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        step_ck(d01.x, d01.y, dy4.x, B0, C0);
-        step_ck(d01.z, d01.w, dy4.y, B1, C1);
-        step_ck(d23.x, d23.y, dy4.z, B2, C2);
-        step_ck(d23.z, d23.w, dy4.w, B3, C3);
         if (i % 16 == 12) {
           const int64_t tend = tchunk + i + 4;  // end of this 16-step block
           if (tend - 16 < pend && (tend % a.seg_steps == 0 || tend >= pend)) {
