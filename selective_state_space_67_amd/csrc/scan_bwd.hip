@@ -118,8 +118,18 @@ __device__ __forceinline__ float chan_sum(float v) {
   if constexpr (LPC >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
   if constexpr (LPC >= 8) v += dpp_f<0x141>(v);   // row_half_mirror: the other quad of each 8
   if constexpr (LPC >= 16) v += dpp_f<0x140>(v);  // row_mirror: the other 8 of each row
-  if constexpr (LPC >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (LPC >= 64) v += __shfl_xor(v, 32, 64);
+  // Across rows: v_permlane16_swap / v_permlane32_swap exchange rows between
+  // the two operands (a VALU operation, where a shuffle would go through the
+  // LDS); with both operands v, the two results are this row's value and the
+  // partner row's, so their sum is the pair's total in every lane.
+  if constexpr (LPC >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (LPC >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return v;
 }
 
