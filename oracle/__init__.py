@@ -55,6 +55,8 @@ def _load():
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
         lib.oracle_scan_cplx_rows.argtypes = [i64, i64, i64] + [p] * 14 + [ctypes.c_int]
         lib.oracle_scan_cplx_rows.restype = None
+        lib.oracle_scan_cplx_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
+        lib.oracle_scan_cplx_bwd_rows.restype = ctypes.c_int
         lib.oracle_conv_silu_rows.argtypes = [i64, i64, i64] + [p] * 10 + [ctypes.c_int]
         lib.oracle_conv_silu_rows.restype = None
         lib.oracle_conv_silu_bwd_rows.argtypes = [i64, i64, i64, i64] + [p] * 12 + [ctypes.c_int]
@@ -342,3 +344,41 @@ def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=No
                            np.asarray(Cm)[:, None, :], z=None if z is None else _f64(z)[:, :, None],
                            dt_bias=dt_bias, Dskip=Dskip, h0=h, want_h_last=True, nthreads=nthreads)
     return out[:, :, 0], h_new
+
+
+def scan_cplx_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
+                  dh_last=None, nthreads=0):
+    """Gradients of sum(dout * out) + sum(Re dh_last Re h_last + Im dh_last Im h_last)
+    for the complex-state scan (scan_cplx). Gradients of complex inputs are
+    dL/dRe + i dL/dIm. Returns a dict: du, d_dt_raw, dz (B, D, L) (dz None
+    without z), dA (D, N) complex, dD, d_dt_bias (D,), dB, dC (B, L, N) complex
+    and dh0 (B, D, N) complex."""
+    lib = _load()
+    u, dt_raw, z, dout = _f64(u), _f64(dt_raw), _f64(z), _f64(dout)
+    dt_bias, Dskip = _f64(dt_bias), _f64(Dskip)
+    Ai, Bi, Ci, h0i, dhi = (_interleave(v) for v in (A, Bm, Cm, h0, dh_last))
+    Bt, D, L = u.shape
+    N = Ai.shape[1]
+    assert dt_raw.shape == (Bt, D, L) and dout.shape == (Bt, D, L) and Ai.shape == (D, N, 2)
+    assert Bi.shape == (Bt, L, N, 2) and Ci.shape == (Bt, L, N, 2)
+    assert z is None or z.shape == (Bt, D, L)
+    for v in (h0i, dhi):
+        assert v is None or v.shape == (Bt, D, N, 2)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+        assert reset.shape == (Bt, L)
+    rb, rd = np.divmod(np.arange(Bt * D, dtype=np.int64), D)
+    out = dict(du=np.empty((Bt, D, L)), d_dt_raw=np.empty((Bt, D, L)),
+               dz=None if z is None else np.empty((Bt, D, L)), dA=np.empty((D, N, 2)), dD=np.empty(D),
+               d_dt_bias=np.empty(D), dB=np.empty((Bt, L, N, 2)), dC=np.empty((Bt, L, N, 2)),
+               dh0=np.empty((Bt, D, N, 2)))
+    rc = lib.oracle_scan_cplx_bwd_rows(
+        Bt * D, L, N, Bt, D, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias), _ptr(Ai),
+        _ptr(Dskip), _ptr(Bi), _ptr(Ci), _ptr(reset), _ptr(h0i), _ptr(dout), _ptr(dhi), _ptr(out["du"]),
+        _ptr(out["d_dt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dD"]), _ptr(out["d_dt_bias"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle complex backward: scratch allocation failed")
+    for k in ("dA", "dB", "dC", "dh0"):
+        out[k] = out[k][..., 0] + 1j * out[k][..., 1]
+    return out

@@ -413,6 +413,176 @@ int oracle_scan_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t 
 }
 
 /*
+ * Backward pass of the complex-state scan (oracle_scan_cplx_rows): gradients
+ * of the real scalar
+ *
+ *   loss = sum dout[b,d,t] out[b,d,t] + sum_{b,d,n} (Re dh_last Re h_last + Im dh_last Im h_last)
+ *
+ * A gradient with respect to a complex quantity w is reported as the complex
+ * number dL/d(Re w) + i dL/d(Im w). With that convention, for w = a h with
+ * complex a and h, the gradient of h is conj(a) times that of w, and the
+ * gradient of a is that of w times conj(h); Re(c w) has gradient conj(c) in w.
+ * The chain rule through the recurrence, step by step in reverse (g = the
+ * gradient of h_t, a_t = exp(delta_t A), hp_t = h_{t-1}, 0 after a reset):
+ *
+ *   g[n]      = dh_last[n]
+ *   for t = L-1 .. 0:
+ *     dy      = dout_t silu(z_t) (dout_t without a gate);  dz_t, dD as in the real case
+ *     for n:  g[n]     += dy conj(C_t[n])
+ *             dC[b,t,n] += dy conj(h_t[n]);        dB[b,t,n] += delta_t u_t g[n]
+ *             dA[d,n]   += delta_t g[n] conj(a hp_t[n])
+ *             ddelta    += Re(conj(g[n]) (A[n] a hp_t[n] + B_t[n] u_t))
+ *             du_t      += delta_t Re(conj(g[n]) B_t[n])
+ *             g[n]       = reset[b,t] ? 0 : conj(a) g[n]
+ *     d dt_raw_t = ddelta sigmoid(x_t);  d dt_bias += the same
+ *   dh0 = g
+ *
+ * Complex arrays are interleaved (re, im): A, dA (Dtot, N, 2); Bm, Cm, dB, dC
+ * (Btot, L, N, 2); h0, dh_last, dh0 (R, N, 2). Real arrays as in
+ * oracle_scan_bwd_rows. Returns 0, or -1 when scratch memory could not be
+ * allocated.
+ */
+int oracle_scan_cplx_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int64_t Dtot,
+                              const int64_t* row_b, const int64_t* row_d, const double* u,
+                              const double* dt_raw, const double* z, const double* dt_bias,
+                              const double* A, const double* Dskip, const double* Bm, const double* Cm,
+                              const uint8_t* reset, const double* h0, const double* dout,
+                              const double* dh_last, double* du, double* d_dt_raw, double* dz,
+                              double* dA, double* dD, double* d_dt_bias, double* dB, double* dC,
+                              double* dh0, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int T = omp_get_max_threads();
+#else
+  (void)nthreads;
+  const int T = 1;
+#endif
+  const int64_t nA = 2 * Dtot * N, nBC = 2 * Btot * L * N;
+  const int64_t per = nA + 2 * Dtot + 2 * nBC;
+  double* acc = (double*)calloc((size_t)T * (size_t)per, sizeof(double));
+  if (!acc) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+    const int tid = omp_get_thread_num();
+#else
+    const int tid = 0;
+#endif
+    double* my = acc + (int64_t)tid * per;
+    double *mA = my, *mD = my + nA, *mbias = my + nA + Dtot, *mB = my + nA + 2 * Dtot,
+           *mC = mB + nBC;
+    double complex* hist = (double complex*)malloc((size_t)(L + 1) * (size_t)N * sizeof(double complex));
+    double* dl = (double*)malloc((size_t)L * 3 * sizeof(double));
+    double complex* g = (double complex*)malloc((size_t)N * sizeof(double complex));
+    if (!hist || !dl || !g) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t b = row_b[r], d = row_d[r];
+        const double bias = dt_bias ? dt_bias[d] : 0.0;
+        const double dsk = Dskip ? Dskip[d] : 0.0;
+        double *xs = dl + L, *ys = dl + 2 * L;
+        for (int64_t n = 0; n < N; ++n)
+          hist[n] = h0 ? h0[2 * (r * N + n)] + I * h0[2 * (r * N + n) + 1] : 0.0;
+        /* forward, keeping every state */
+        for (int64_t t = 0; t < L; ++t) {
+          const int64_t bt = b * L + t;
+          const double x = dt_raw[r * L + t] + bias;
+          const double delta = softplus(x);
+          const int rs = reset ? reset[bt] != 0 : 0;
+          const double uu = u[r * L + t];
+          double complex acc_y = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double complex An = A[2 * (d * N + n)] + I * A[2 * (d * N + n) + 1];
+            const double complex Bn = Bm[2 * (bt * N + n)] + I * Bm[2 * (bt * N + n) + 1];
+            const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
+            const double complex hp = rs ? 0.0 : hist[t * N + n];
+            const double complex h = cexp(delta * An) * hp + delta * Bn * uu;
+            hist[(t + 1) * N + n] = h;
+            acc_y += Cn * h;
+          }
+          dl[t] = delta;
+          xs[t] = x;
+          ys[t] = creal(acc_y) + dsk * uu;
+        }
+        /* reverse */
+        for (int64_t n = 0; n < N; ++n)
+          g[n] = dh_last ? dh_last[2 * (r * N + n)] + I * dh_last[2 * (r * N + n) + 1] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          const int64_t bt = b * L + t;
+          const double delta = dl[t], uu = u[r * L + t], go = dout[r * L + t];
+          const int rs = reset ? reset[bt] != 0 : 0;
+          double dy = go;
+          if (z) {
+            const double zz = z[r * L + t], sg = sigmoid(zz);
+            dy = go * zz * sg;
+            dz[r * L + t] = go * ys[t] * sg * (1.0 + zz * (1.0 - sg));
+          }
+          mD[d] += dy * uu;
+          double du_t = dy * dsk, ddelta = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double complex An = A[2 * (d * N + n)] + I * A[2 * (d * N + n) + 1];
+            const double complex Bn = Bm[2 * (bt * N + n)] + I * Bm[2 * (bt * N + n) + 1];
+            const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
+            const double complex hp = rs ? 0.0 : hist[t * N + n];
+            const double complex a = cexp(delta * An);
+            g[n] += dy * conj(Cn);
+            const double complex gC = dy * conj(hist[(t + 1) * N + n]);
+            const double complex gB = delta * uu * g[n];
+            const double complex gA = delta * g[n] * conj(a * hp);
+            mC[2 * (bt * N + n)] += creal(gC);
+            mC[2 * (bt * N + n) + 1] += cimag(gC);
+            mB[2 * (bt * N + n)] += creal(gB);
+            mB[2 * (bt * N + n) + 1] += cimag(gB);
+            mA[2 * (d * N + n)] += creal(gA);
+            mA[2 * (d * N + n) + 1] += cimag(gA);
+            ddelta += creal(conj(g[n]) * (An * a * hp + Bn * uu));
+            du_t += delta * creal(conj(g[n]) * Bn);
+            g[n] = rs ? 0.0 : conj(a) * g[n];
+          }
+          du[r * L + t] = du_t;
+          const double dx = ddelta * sigmoid(xs[t]);
+          d_dt_raw[r * L + t] = dx;
+          mbias[d] += dx;
+        }
+        if (dh0)
+          for (int64_t n = 0; n < N; ++n) {
+            dh0[2 * (r * N + n)] = creal(g[n]);
+            dh0[2 * (r * N + n) + 1] = cimag(g[n]);
+          }
+      }
+    }
+    free(hist);
+    free(dl);
+    free(g);
+  }
+  if (failed) {
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < nA; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < Dtot; ++i) dD[i] = d_dt_bias[i] = 0.0;
+  for (int64_t i = 0; i < nBC; ++i) dB[i] = dC[i] = 0.0;
+  for (int t = 0; t < T; ++t) {
+    const double* my = acc + (int64_t)t * per;
+    for (int64_t i = 0; i < nA; ++i) dA[i] += my[i];
+    for (int64_t i = 0; i < Dtot; ++i) {
+      dD[i] += my[nA + i];
+      d_dt_bias[i] += my[nA + Dtot + i];
+    }
+    for (int64_t i = 0; i < nBC; ++i) {
+      dB[i] += my[nA + 2 * Dtot + i];
+      dC[i] += my[nA + 2 * Dtot + nBC + i];
+    }
+  }
+  free(acc);
+  return 0;
+}
+
+/*
  * Causal depthwise convolution followed by SiLU, the input side of the Mamba
  * block: a depthwise Conv1d of width K, padded by K-1 on the left so that the
  * output at t sees inputs t-K+1 .. t, then silu ("Illustrated Mamba state
