@@ -53,7 +53,7 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_scan_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
-        lib.oracle_scan_cplx_rows.argtypes = [i64, i64, i64] + [p] * 14 + [ctypes.c_int]
+        lib.oracle_scan_cplx_rows.argtypes = [i64, i64, i64] + [p] * 14 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_cplx_rows.restype = None
         lib.oracle_scan_cplx_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
         lib.oracle_scan_cplx_bwd_rows.restype = ctypes.c_int
@@ -299,12 +299,13 @@ def _interleave(x):
 
 
 def scan_cplx(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-              want_h_last=False, nthreads=0):
+              want_h_last=False, zoh=False, nthreads=0):
     """Full scan with a complex diagonal state (the S4D-Lin variant).
 
     u, dt_raw, z: (B, D, L) real; A: (D, N) complex; Bm, Cm: (B, L, N) complex;
     h0: (B, D, N) complex or None. Returns out (B, D, L) float64 (the gated real
-    part of the read-out) and, if asked, h_last (B, D, N) complex128.
+    part of the read-out) and, if asked, h_last (B, D, N) complex128. zoh=True:
+    the input coefficient is (e^{delta A} - 1) / A instead of delta.
     """
     lib = _load()
     u, dt_raw, z = _f64(u), _f64(dt_raw), _f64(z)
@@ -326,13 +327,13 @@ def scan_cplx(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=N
     hl = np.empty((Bt, D, N, 2)) if want_h_last else None
     lib.oracle_scan_cplx_rows(Bt * D, L, N, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias),
                               _ptr(Ai), _ptr(Dskip), _ptr(Bi), _ptr(Ci), _ptr(reset), _ptr(h0i), _ptr(out),
-                              _ptr(hl), int(nthreads))
+                              _ptr(hl), int(bool(zoh)), int(nthreads))
     if want_h_last:
         return out, hl[..., 0] + 1j * hl[..., 1]
     return out
 
 
-def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, nthreads=0):
+def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, zoh=False, nthreads=0):
     """Decode step with a complex state: one step of scan_cplx from h.
 
     h: (B, D, N) complex; u, dt_raw, z: (B, D); A: (D, N) complex; Bm, Cm: (B, N)
@@ -342,7 +343,7 @@ def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=No
     Bt, D = u.shape
     out, h_new = scan_cplx(u[:, :, None], _f64(dt_raw)[:, :, None], A, np.asarray(Bm)[:, None, :],
                            np.asarray(Cm)[:, None, :], z=None if z is None else _f64(z)[:, :, None],
-                           dt_bias=dt_bias, Dskip=Dskip, h0=h, want_h_last=True, nthreads=nthreads)
+                           dt_bias=dt_bias, Dskip=Dskip, h0=h, want_h_last=True, zoh=zoh, nthreads=nthreads)
     return out[:, :, 0], h_new
 
 

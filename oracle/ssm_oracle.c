@@ -180,14 +180,27 @@ void oracle_state_update(int64_t Bt, int64_t Dt, int64_t N, double* h,
  *
  * Complex arrays are interleaved (re, im) doubles with the shapes of the real
  * scan plus a trailing 2: A (Dtot, N, 2), Bm, Cm (Btot, L, N, 2), h0 and
- * h_last (R, N, 2). Everything else is as in oracle_scan_rows.
+ * h_last (R, N, 2). Everything else is as in oracle_scan_rows. With zoh = 1
+ * the input coefficient delta becomes the exact zero-order hold (see bcoef_c).
  */
+
+/* The zero-order-hold coefficient (e^{delta A} - 1) / A for a complex A, with
+ * e^{x + iy} - 1 written as expm1(x) cos y - 2 sin^2(y/2) + i e^x sin y, which
+ * does not cancel for small delta A; its limit at A = 0 is delta. */
+static double complex bcoef_c(double delta, double complex A, int zoh) {
+  if (!zoh || A == 0.0) return delta;
+  const double re = delta * creal(A), im = delta * cimag(A);
+  const double sh = sin(0.5 * im);
+  const double complex em1 = expm1(re) * cos(im) - 2.0 * sh * sh + I * (exp(re) * sin(im));
+  return em1 / A;
+}
+
 void oracle_scan_cplx_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b,
                            const int64_t* row_d, const double* u, const double* dt_raw,
                            const double* z, const double* dt_bias, const double* A,
                            const double* Dskip, const double* Bm, const double* Cm,
                            const uint8_t* reset, const double* h0, double* out,
-                           double* h_last, int nthreads) {
+                           double* h_last, int zoh, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -212,7 +225,7 @@ void oracle_scan_cplx_rows(int64_t R, int64_t L, int64_t N, const int64_t* row_b
         const double complex An = A[2 * (d * N + n)] + I * A[2 * (d * N + n) + 1];
         const double complex Bn = Bm[2 * (bt * N + n)] + I * Bm[2 * (bt * N + n) + 1];
         const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
-        h[n] = cexp(delta * An) * h[n] + delta * Bn * x;
+        h[n] = cexp(delta * An) * h[n] + bcoef_c(delta, An, zoh) * Bn * x;
         acc += Cn * h[n];
       }
       const double y = creal(acc) + dsk * x;

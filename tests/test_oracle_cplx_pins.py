@@ -16,6 +16,12 @@ oracle's header. What pins it here:
 - pure rotation (Re A = 0, B = 0): h_t = exp(i w S_t) h0 with S_t the running
   sum of delta, which fixes the sign of the phase;
 - a conjugate pair of states reads out twice the real part of one of them.
+
+With the exact zero-order hold (input coefficient (e^{delta A} - 1) / A), each
+step equals a DOP853 integration of the complex system h' = A h + B u over the
+step; constant inputs reach the continuous fixed point -B u / A exactly; A = 0
+gives the delta B form bit for bit, a real A the real ZOH oracle, and a tiny
+delta A the delta B form to 1e-10 (no cancellation in e^{delta A} - 1).
 """
 import numpy as np
 import pytest
@@ -157,3 +163,55 @@ def test_decode_steps_reproduce_the_scan(with_z):
                                         z=None if zz is None else zz[:, :, t], dt_bias=dt_bias, Dskip=Dskip)
         np.testing.assert_allclose(o, ref[:, :, t], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(h, rhl, rtol=1e-12, atol=1e-12)
+
+
+# ---- exact zero-order hold with a complex state ----
+
+def test_zoh_steps_equal_ode_integration():
+    """Each step is the exact solution of h' = A h + B u over delta with B, u held."""
+    import scipy.integrate
+
+    rng = np.random.default_rng(21)
+    D, L, N = 2, 6, 3
+    u = rng.standard_normal((1, D, L))
+    dt = rng.standard_normal((1, D, L))
+    A = -rng.uniform(0.2, 2.0, (D, N)) + 1j * rng.uniform(-6, 6, (D, N))
+    Bm, Cm, h0 = cplx(rng, 1, L, N), cplx(rng, 1, L, N), cplx(rng, 1, D, N)
+    out, hl = oracle.scan_cplx(u, dt, A, Bm, Cm, h0=h0, want_h_last=True, zoh=True)
+    for d in range(D):
+        h = h0[0, d].copy()
+        for t in range(L):
+            delta = softplus(dt[0, d, t])
+            rhs = lambda s, y, t=t: A[d] * y + Bm[0, t] * u[0, d, t]
+            h = scipy.integrate.solve_ivp(rhs, (0.0, delta), h, method="DOP853", rtol=1e-12, atol=1e-14).y[:, -1]
+            np.testing.assert_allclose(out[0, d, t], np.sum(Cm[0, t] * h).real, rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(hl[0, d], h, rtol=1e-9, atol=1e-11)
+
+
+def test_zoh_steady_state_and_limits():
+    # constant inputs: h -> -B u / A exactly, whatever the step
+    D, L, N = 3, 4000, 3
+    A = np.array([[-0.5 + 2j, -1.0 - 0.5j, -2.0 + 7j]] * D)
+    Bv = np.array([0.3 - 1j, -1.2, 0.7 + 0.4j])
+    u = np.full((1, D, L), 1.7)
+    dt = np.broadcast_to(np.array([-2.0, 0.0, 1.5])[None, :, None], (1, D, L)).copy()
+    _, hl = oracle.scan_cplx(u, dt, A, np.broadcast_to(Bv, (1, L, N)), np.zeros((1, L, N), complex),
+                             want_h_last=True, zoh=True)
+    np.testing.assert_allclose(hl[0], np.broadcast_to(-Bv * 1.7 / A[0], (D, N)), rtol=1e-11)
+    # A = 0 gives the delta B form exactly; a real A gives the real ZOH oracle
+    rng = np.random.default_rng(22)
+    u, dt = rng.standard_normal((2, 3, 40)), rng.standard_normal((2, 3, 40))
+    Bm, Cm = rng.standard_normal((2, 40, 4)), rng.standard_normal((2, 40, 4))
+    A0 = np.zeros((3, 4), complex)
+    np.testing.assert_array_equal(oracle.scan_cplx(u, dt, A0, Bm + 0j, Cm + 0j, zoh=True),
+                                  oracle.scan_cplx(u, dt, A0, Bm + 0j, Cm + 0j, zoh=False))
+    Ar = -rng.uniform(0.1, 3, (3, 4))
+    np.testing.assert_allclose(oracle.scan_cplx(u, dt, Ar + 0j, Bm + 0j, Cm + 0j, zoh=True),
+                               oracle.scan(u, dt, Ar, Bm, Cm, zoh=True), rtol=1e-12, atol=1e-13)
+    # small delta A: the coefficient stays accurate (no cancellation in e^{delta A} - 1)
+    A_small = np.full((1, 1), -1e-12 + 3e-12j)
+    o1 = oracle.scan_cplx(np.ones((1, 1, 3)), np.zeros((1, 1, 3)), A_small, np.ones((1, 3, 1), complex),
+                          np.ones((1, 3, 1), complex), zoh=True)
+    o0 = oracle.scan_cplx(np.ones((1, 1, 3)), np.zeros((1, 1, 3)), A_small, np.ones((1, 3, 1), complex),
+                          np.ones((1, 3, 1), complex), zoh=False)
+    np.testing.assert_allclose(o1, o0, rtol=1e-10)
