@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10300 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -102,12 +102,13 @@ typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
  *                     delta, u, z and out stay real; the recurrence is
  *                       h_t[n] = exp(delta_t A[d,n]) h_{t-1}[n] + delta_t B[b,t,n] u
  *                       y_t    = Re(sum_n C[b,t,n] h_t[n]) + D[d] u
- *                     with the same gate and resets. This build supports it
- *                     with SSM_DISC_DELTA_B and no conv stage, in ssm_scan_fwd
- *                     (whose workspace then holds complex aggregates; ask
- *                     ssm_scan_workspace_size with state_kind set) and
- *                     ssm_state_update; other combinations, and the backward,
- *                     return SSM_ERR_UNSUPPORTED.
+ *                     (with SSM_DISC_ZOH the input coefficient is the complex
+ *                     (exp(delta A) - 1) / A in place of delta), with the same
+ *                     gate and resets. It is supported without a conv stage,
+ *                     in ssm_scan_fwd (whose workspace then holds complex
+ *                     aggregates; ask ssm_scan_workspace_size with state_kind
+ *                     set) and ssm_state_update; a conv stage with it, and the
+ *                     backward, return SSM_ERR_UNSUPPORTED.
  * Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 

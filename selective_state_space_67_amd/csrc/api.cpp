@@ -38,11 +38,9 @@ bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
 bool valid_disc(int32_t t) { return t == SSM_DISC_DELTA_B || t == SSM_DISC_ZOH; }
 bool valid_kind(int32_t k) { return k == SSM_STATE_REAL || k == SSM_STATE_COMPLEX; }
 
-// The complex state is built for the small-delta input matrix without a conv stage.
-ssm_status check_kind(int32_t kind, int32_t disc, bool conv) {
+// The complex state is built without a conv stage.
+ssm_status check_kind(int32_t kind, bool conv) {
   if (!valid_kind(kind)) return fail(SSM_ERR_UNSUPPORTED, "unknown state_kind %d", kind);
-  if (kind == SSM_STATE_COMPLEX && disc != SSM_DISC_DELTA_B)
-    return fail(SSM_ERR_UNSUPPORTED, "the complex state supports only SSM_DISC_DELTA_B");
   if (kind == SSM_STATE_COMPLEX && conv) return fail(SSM_ERR_UNSUPPORTED, "the complex state has no conv stage");
   return SSM_OK;
 }
@@ -402,7 +400,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
     return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
-  if ((s = check_kind(p->state_kind, p->discretization, p->conv_w != nullptr)) != SSM_OK) return s;
+  if ((s = check_kind(p->state_kind, p->conv_w != nullptr)) != SSM_OK) return s;
   const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
   const int64_t cw = cplx ? 2 : 1;  // scalars per A, B, C and state entry
   const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
@@ -477,6 +475,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
   plan.nseg = nseg;
   plan.seg_len = seg_len;
+  plan.zoh = p->discretization == SSM_DISC_ZOH;
   if (cplx) {
     hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
@@ -487,7 +486,6 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.conv_state_in = p->conv_state_in;
   plan.conv_state_out = p->conv_state_out;
   plan.conv_k = static_cast<int>(K);
-  plan.zoh = p->discretization == SSM_DISC_ZOH;
   hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -529,7 +527,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
-  ssm_status s = check_kind(p->state_kind, p->discretization, p->conv_w != nullptr);
+  ssm_status s = check_kind(p->state_kind, p->conv_w != nullptr);
   if (s != SSM_OK) return s;
   const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
   const int64_t ce = cplx ? 2 : 1;  // scalars per A, B, C and state entry

@@ -119,31 +119,69 @@ struct CplxArgs {
   float* ws_H;  // (nseg - 1, B, D, N, 2): their end states from a zero start
 };
 
-// Per-lane constants of state n: Re A log2(e), and Im A / (2 pi) as ai + ai_lo
-// (ai rounded, ai_lo the rest to within float32 rounding); zero past N.
+// Per-lane constants of one state: Re A log2(e) for the decay's magnitude,
+// Im A / (2 pi) as ai + ai_lo (ai rounded, ai_lo the rest to within float32
+// rounding) for its angle, and for the zero-order hold A and 1/A.
+struct CState {
+  float ar, ai, ai_lo;
+  float re, im, ir, ii;
+};
+
+__device__ __forceinline__ CState make_cstate(float re, float im) {
+  CState q;
+  q.ar = re * kLog2e;
+  q.ai = im * kInv2PiHi;
+  q.ai_lo = __builtin_fmaf(im, kInv2PiHi, -q.ai) + im * kInv2PiLo;
+  q.re = re;
+  q.im = im;
+  const float m = re * re + im * im;
+  const float r = m > 0.0f ? 1.0f / m : 0.0f;  // 1/A = conj(A) / |A|^2; 0 for A = 0
+  q.ir = re * r;
+  q.ii = -im * r;
+  return q;
+}
+
+// Constants of this lane's states n0 .. n0+NPL-1 (zero past N).
 template <int NPL>
-__device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0, bool dvalid, float (&ar)[NPL],
-                                       float (&ai)[NPL], float (&ai_lo)[NPL]) {
+__device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0, bool dvalid, CState (&q)[NPL]) {
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = n0 + j;
     const bool ok = dvalid && n < N;
-    const float im = ok ? A[2 * (d * N + n) + 1] : 0.0f;
-    ar[j] = ok ? A[2 * (d * N + n)] * kLog2e : 0.0f;
-    ai[j] = im * kInv2PiHi;
-    ai_lo[j] = __builtin_fmaf(im, kInv2PiHi, -ai[j]) + im * kInv2PiLo;
+    q[j] = make_cstate(ok ? A[2 * (d * N + n)] : 0.0f, ok ? A[2 * (d * N + n) + 1] : 0.0f);
   }
 }
 
-// One step of state j: h = exp(delta A) h + delta u B; returns Re(C h).
-__device__ __forceinline__ float cplx_step(float dl, float dv, float ar, float ai, float ai_lo, float2 Bv, float2 Cv,
-                                           float& hr, float& hi) {
-  const float e = fast_exp2(dl * ar);
+// One step of a state: h = exp(delta A) h + q u B with the input coefficient
+// q = delta, or with the zero-order hold q = (exp(delta A) - 1) / A; returns
+// Re(C h). dv is delta u (or u with the zero-order hold). The zero-order hold
+// forms q from exp(delta A) - 1 times the precomputed 1/A where |delta A| >=
+// 1/16, and below that, where the difference would cancel, from the series
+// delta (1 + x/2 + x^2/6 + x^3/24), x = delta A (truncation below 1.3e-7).
+template <bool ZOH>
+__device__ __forceinline__ float cplx_step(float dl, float dv, const CState& q, float2 Bv, float2 Cv, float& hr,
+                                           float& hi) {
+  const float e = fast_exp2(dl * q.ar);
   float s, c;
-  sincos_rev(dl, ai, ai_lo, s, c);
+  sincos_rev(dl, q.ai, q.ai_lo, s, c);
   const float are = e * c, aim = e * s;
-  const float nr = __builtin_fmaf(are, hr, __builtin_fmaf(-aim, hi, Bv.x * dv));
-  const float ni = __builtin_fmaf(are, hi, __builtin_fmaf(aim, hr, Bv.y * dv));
+  float br = Bv.x * dv, bi = Bv.y * dv;
+  if constexpr (ZOH) {
+    const float xr = dl * q.re, xi = dl * q.im;
+    // series: p = ((x/24 + 1/6) x + 1/2) x + 1, complex Horner
+    float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
+    float tr = __builtin_fmaf(pr, xr, -pi * xi) + 0.5f, ti = __builtin_fmaf(pr, xi, pi * xr);
+    pr = __builtin_fmaf(tr, xr, -ti * xi) + 1.0f;
+    pi = __builtin_fmaf(tr, xi, ti * xr);
+    const float mr = are - 1.0f, mi = aim;  // exp(delta A) - 1
+    const bool small = xr * xr + xi * xi < 1.0f / 256.0f;
+    const float qr = small ? dl * pr : __builtin_fmaf(mr, q.ir, -mi * q.ii);
+    const float qi = small ? dl * pi : __builtin_fmaf(mr, q.ii, mi * q.ir);
+    br = dv * __builtin_fmaf(qr, Bv.x, -qi * Bv.y);
+    bi = dv * __builtin_fmaf(qr, Bv.y, qi * Bv.x);
+  }
+  const float nr = __builtin_fmaf(are, hr, __builtin_fmaf(-aim, hi, br));
+  const float ni = __builtin_fmaf(are, hi, __builtin_fmaf(aim, hr, bi));
   hr = nr;
   hi = ni;
   return __builtin_fmaf(Cv.x, nr, -Cv.y * ni);
@@ -154,7 +192,7 @@ __device__ __forceinline__ float cplx_step(float dl, float dv, float ar, float a
 // affine aggregate, the decay product P = exp(A sum delta) (0 after a reset)
 // and the end state H; the full launch folds the aggregates of the preceding
 // pieces into its starting state, h <- P h + H, and runs its piece.
-template <int NPL, typename InT, bool HAS_RESET, bool AGG>
+template <int NPL, typename InT, bool HAS_RESET, bool AGG, bool ZOH>
 __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   constexpr int NPAD = 16 * NPL;
   const int g = blockIdx.x % a.n_dgroups;
@@ -174,10 +212,12 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   // (B, C) of the chunk's steps per state, as (B.re, B.im, C.re, C.im); states
   // past N stay zero.
   __shared__ __align__(16) float4 s_bc[kT * NPAD];
-  __shared__ __align__(8) float2 s_du[kCPW * kT];  // (delta, delta u); delta negated on a reset step
+  // (delta, delta u), or (delta, u) with the zero-order hold; delta negated on a reset step
+  __shared__ __align__(8) float2 s_du[kCPW * kT];
 
-  float ar[NPL], ai[NPL], ai_lo[NPL], hr[NPL], hi[NPL];
-  load_A<NPL>(a.A, d, N, n0, dvalid, ar, ai, ai_lo);
+  CState cq[NPL];
+  float hr[NPL], hi[NPL];
+  load_A<NPL>(a.A, d, N, n0, dvalid, cq);
   const int64_t row = static_cast<int64_t>(b) * a.D + d;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
@@ -238,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
         cleared = true;
       }
     }
-    s_du[c * kT + k] = make_float2(dl, fabsf(dl) * uu);
+    s_du[c * kT + k] = make_float2(dl, ZOH ? uu : fabsf(dl) * uu);
     __syncthreads();
 
     float ymine = 0.0f;
@@ -261,8 +301,7 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const float4 bc = s_bc[tl * NPAD + n0 + j];
-        p += cplx_step(dlt, du.y, ar[j], ai[j], ai_lo[j], make_float2(bc.x, bc.y), make_float2(bc.z, bc.w), hr[j],
-                       hi[j]);
+        p += cplx_step<ZOH>(dlt, du.y, cq[j], make_float2(bc.x, bc.y), make_float2(bc.z, bc.w), hr[j], hi[j]);
       }
       if constexpr (!AGG) {
         p = row_sum16(p);
@@ -288,8 +327,8 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
         if (n0 + j >= N) continue;
         const int64_t w = static_cast<int64_t>(sp) * a.B * a.D * N * 2 + 2 * (row * N + n0 + j);
         float sn, cs;
-        sincos_rev(S, ai[j], ai_lo[j], sn, cs);
-        const float e = any_reset ? 0.0f : fast_exp2(S * ar[j]);
+        sincos_rev(S, cq[j].ai, cq[j].ai_lo, sn, cs);
+        const float e = any_reset ? 0.0f : fast_exp2(S * cq[j].ar);
         a.ws_P[w] = e * cs;
         a.ws_P[w + 1] = e * sn;
         a.ws_H[w] = hr[j];
@@ -337,7 +376,7 @@ __device__ __forceinline__ float2 load_cpair(const bf16_t* p, int64_t n) {
 // k holds states k, k + 16, k + 32, ..., so for each j the 16 lanes of a row
 // read 16 consecutive (re, im) pairs of h, A, B and C: coalesced accesses to
 // the state, which is what the step moves.
-template <int NPL, typename InT>
+template <int NPL, typename InT, bool ZOH>
 __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateArgs a) {
   const int tid = threadIdx.x;
   const int k = tid & 15;
@@ -362,15 +401,13 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
   }
   const float uu = load_elem(static_cast<const InT*>(a.u), row);
   const float dl = softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
-  const float dv = dl * uu;
+  const float dv = ZOH ? uu : dl * uu;
   float p = 0.0f;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = k + 16 * j;
-    const float ai = av[j].y * kInv2PiHi;
-    const float ai_lo = __builtin_fmaf(av[j].y, kInv2PiHi, -ai) + av[j].y * kInv2PiLo;
     float hr = hv[j].x, hi = hv[j].y;
-    p += cplx_step(dl, dv, av[j].x * kLog2e, ai, ai_lo, bv[j], cv[j], hr, hi);
+    p += cplx_step<ZOH>(dl, dv, make_cstate(av[j].x, av[j].y), bv[j], cv[j], hr, hi);
     if (n < N) *reinterpret_cast<float2*>(h + 2 * n) = make_float2(hr, hi);
   }
   p = row_sum16(p);
@@ -460,20 +497,23 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
   const dim3 grid_agg(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg - 1)));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
-    auto run = [&](auto in_t, auto has_reset) {
+    auto run = [&](auto in_t, auto has_reset, auto zoh) {
       using InT = decltype(in_t);
-      constexpr bool R = decltype(has_reset)::value;
+      constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
       if (p.nseg > 1) {  // the last piece's aggregate is never needed
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true>), grid_agg, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z>), grid_agg, dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z>), grid, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };
+    auto with_zoh = [&](auto in_t, auto has_reset) {
+      return p.zoh ? run(in_t, has_reset, std::true_type{}) : run(in_t, has_reset, std::false_type{});
+    };
     if (p.in_bf16)
-      return p.reset ? run(bf16_t{}, std::true_type{}) : run(bf16_t{}, std::false_type{});
-    return p.reset ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
+      return p.reset ? with_zoh(bf16_t{}, std::true_type{}) : with_zoh(bf16_t{}, std::false_type{});
+    return p.reset ? with_zoh(float{}, std::true_type{}) : with_zoh(float{}, std::false_type{});
   });
 }
 
@@ -496,10 +536,17 @@ hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
-    if (p.in_bf16)
-      hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((cplx_update_kernel<NPL, float>), grid, dim3(kThreads), 0, stream, a);
+    if (p.in_bf16) {
+      if (p.zoh)
+        hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, true>), grid, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (p.zoh)
+        hipLaunchKernelGGL((cplx_update_kernel<NPL, float, true>), grid, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_update_kernel<NPL, float, false>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
   });
 }

@@ -18,6 +18,14 @@ bound on h_last), with E and M run in float64 from the stored inputs; a reset
 zeroes both, as it zeroes the state. For |theta| of order 1 or below the
 extra term is negligible; it matters for large states (Im A up to N - 1)
 with large steps.
+
+With the zero-order hold the input coefficient q = (e^{delta A} - 1) / A
+adds its own error. Where the kernel forms it as (abar - 1) * (1/A), with
+|delta A| >= 1/16, the absolute error of abar (the phase term above plus a
+couple of ulps) divided by |A| is at most (K |theta| + 2) u / |A|
+<= (K + 32) u delta; the series branch below 1/16 is within a few ulps of
+delta. So each step adds K_ZOH u |delta u| |B| (K_ZOH = 40) to E before the
+next decay; |q| <= delta (Re A <= 0), so M still bounds the state.
 """
 import numpy as np
 import pytest
@@ -30,7 +38,7 @@ from gpu_helpers import TOL, assert_close, bf16_half_ulp, device, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_scan(x, h0=None, out_bf16=False, num_segments=0):
+def run_scan(x, h0=None, out_bf16=False, num_segments=0, zoh=False):
     import torch
 
     from selective_state_space_67_amd import ssm_scan_fwd
@@ -43,23 +51,25 @@ def run_scan(x, h0=None, out_bf16=False, num_segments=0):
     h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, np.float32)).to(dev)
     out = ssm_scan_fwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"], Dskip=t["Dskip"],
                        z=t["z"], reset=t["reset"], h0=h0t, h_last=hl, complex_state=True,
-                       out_dtype=torch.bfloat16 if out_bf16 else torch.float32, num_segments=num_segments)
+                       out_dtype=torch.bfloat16 if out_bf16 else torch.float32, num_segments=num_segments,
+                       zoh=zoh)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), hl.cpu().numpy().astype(np.float64)
 
 
-def ref_scan(x, h0=None):
+def ref_scan(x, h0=None, zoh=False):
     w = wl.widen
     return oracle.scan_cplx(w(x["u"]), w(x["dt_raw"]), wl.as_complex(x["A"]), wl.as_complex(x["Bm"]),
                             wl.as_complex(x["Cm"]), z=w(x["z"]), dt_bias=x["dt_bias"], Dskip=x["Dskip"],
-                            reset=x["reset"], h0=wl.as_complex(h0), want_h_last=True)
+                            reset=x["reset"], h0=wl.as_complex(h0), want_h_last=True, zoh=zoh)
 
 
 K_PHASE = 4.0
+K_ZOH = 40.0
 U32 = 2.0 ** -24
 
 
-def phase_bound(x, h0=None):
+def phase_bound(x, h0=None, zoh=False):
     """First-order bound of the phase error (see the module docstring).
 
     Returns (bound on out (B, D, L), bound on h_last (B, D, N))."""
@@ -85,7 +95,10 @@ def phase_bound(x, h0=None):
         amag = np.exp(dl * A.real[None])
         dlt = K_PHASE * U32 * np.abs(dl * A.imag[None])
         E = amag * (E + dlt * M)
-        M = amag * M + np.abs(dl * u[:, :, t][:, :, None]) * Bmag[:, None, t, :]
+        inflow = np.abs(dl * u[:, :, t][:, :, None]) * Bmag[:, None, t, :]
+        if zoh:
+            E = E + K_ZOH * U32 * inflow
+        M = amag * M + inflow
         out_b[:, :, t] = gate[:, :, t] * np.sum(Cmag[:, None, t, :] * E, axis=2)
     return out_b, E
 
@@ -105,9 +118,9 @@ def assert_within(out, ref, extra, dtype, out_bf16=False, what="out"):
     print(what, "worst err/bound %.3f" % float((err / bound).max()), flush=True)
 
 
-def check(x, got, hl, ref, rhl, what, out_bf16=False, h0=None):
+def check(x, got, hl, ref, rhl, what, out_bf16=False, h0=None, zoh=False):
     dtype = x["dtype"]
-    eo, eh = phase_bound(x, h0)
+    eo, eh = phase_bound(x, h0, zoh)
     assert_within(got, ref, eo, dtype, out_bf16=out_bf16, what="out " + what)
     assert_within(hl[..., 0], rhl.real, eh, dtype, what="h_last.re " + what)
     assert_within(hl[..., 1], rhl.imag, eh, dtype, what="h_last.im " + what)
@@ -181,7 +194,7 @@ def test_complex_real_case_matches_real_kernel():
     assert_close(c, r, wl.F32, what="complex kernel vs real kernel")
 
 
-def run_update(y, h, steps=1):
+def run_update(y, h, zoh=False):
     import torch
 
     from selective_state_space_67_amd import ssm_state_update
@@ -190,21 +203,21 @@ def run_update(y, h, steps=1):
     t = {k: to_dev(y[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
     ht = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dev)
     out = ssm_state_update(ht, t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
-                           Dskip=t["Dskip"], z=t["z"], complex_state=True)
+                           Dskip=t["Dskip"], z=t["z"], complex_state=True, zoh=zoh)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), ht.cpu().numpy().astype(np.float64)
 
 
-def check_decode(y, out, h, what):
+def check_decode(y, out, h, what, zoh=False):
     w = wl.widen
     ro, rh = oracle.state_update_cplx(wl.as_complex(y["h"]), w(y["u"]), w(y["dt_raw"]), wl.as_complex(y["A"]),
                                       wl.as_complex(y["Bm"]), wl.as_complex(y["Cm"]), z=w(y["z"]),
-                                      dt_bias=y["dt_bias"], Dskip=y["Dskip"])
+                                      dt_bias=y["dt_bias"], Dskip=y["Dskip"], zoh=zoh)
     # the decode step is one scan step from h: the same phase term with L = 1
     one = dict(u=y["u"][:, :, None], dt_raw=y["dt_raw"][:, :, None],
                z=None if y["z"] is None else y["z"][:, :, None], Bm=y["Bm"][:, None], Cm=y["Cm"][:, None],
                A=y["A"], dt_bias=y["dt_bias"], reset=None)
-    eo, eh = phase_bound(one, h0=y["h"])
+    eo, eh = phase_bound(one, h0=y["h"], zoh=zoh)
     dtype = y["dtype"]
     assert_within(out, ro, eo[:, :, 0], dtype, what="decode out " + what)
     assert_within(h[..., 0], rh.real, eh, dtype, what="decode h.re " + what)
@@ -259,3 +272,84 @@ def test_complex_scan_at_workload_sizes_sampled_channels(index, per_row):
                    dtype=x["dtype"])
         ref, rhl = ref_scan(sub)
         check(sub, got[b:b + 1, ds], hl[b:b + 1, ds], ref, rhl, "%s b=%d" % (cfg["name"], b))
+
+
+# ---- zero-order hold: q = (e^{delta A} - 1) / A ----
+
+def zoh_A(D, N, rng):
+    """S4D-Lin A with a few entries replaced: A = 0 (the coefficient is delta),
+    purely imaginary, and |A| near 1/(16 delta) where the kernel switches
+    from the series to the direct form."""
+    A = wl.s4d_lin_A(D, N)
+    if N >= 4:
+        A[0, 0] = 0.0
+        A[1, 1, 0] = 0.0
+        A[2, :4, 0] = -rng.uniform(0.3, 0.9, 4).astype(np.float32)
+        A[2, :4, 1] = rng.uniform(0.3, 0.9, 4).astype(np.float32)
+    return A
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("N", [1, 16, 64, 256])
+def test_complex_scan_zoh(dtype, N):
+    rng = np.random.default_rng(70 + N)
+    x = wl.make_cplx_inputs(2, 20, 260, N, dtype, seed=700 + N, packed=True, dt_lo=1e-3, dt_hi=3e-1)
+    x["reset"] = wl.doc_resets(rng, 2, 260, lo=20, hi=90)
+    x["A"] = zoh_A(20, N, rng)
+    h0 = rng.standard_normal((2, 20, N, 2)).astype(np.float32)
+    got, hl = run_scan(x, h0=h0, zoh=True)
+    ref, rhl = ref_scan(x, h0=h0, zoh=True)
+    check(x, got, hl, ref, rhl, "zoh N=%d %s" % (N, dtype), h0=h0, zoh=True)
+
+
+@pytest.mark.parametrize("nseg", [2, 5])
+def test_complex_scan_zoh_split_into_pieces(nseg):
+    rng = np.random.default_rng(80 + nseg)
+    x = wl.make_cplx_inputs(2, 24, 1000, 16, wl.F32, seed=800 + nseg, packed=True, dt_lo=1e-3, dt_hi=3e-1)
+    x["reset"] = wl.doc_resets(rng, 2, 1000, lo=100, hi=600)
+    x["A"] = zoh_A(24, 16, rng)
+    got, hl = run_scan(x, num_segments=nseg, zoh=True)
+    ref, rhl = ref_scan(x, zoh=True)
+    check(x, got, hl, ref, rhl, "zoh pieces=%d" % nseg, zoh=True)
+
+
+def test_complex_zoh_real_case_matches_real_kernel():
+    """Zero imaginary parts: the complex zero-order hold reproduces the real one."""
+    import torch
+
+    from selective_state_space_67_amd import ssm_scan_fwd
+
+    x = wl.make_scan_inputs(2, 48, 400, 16, wl.F32, seed=78, packed=True)
+    dev = device()
+    t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
+    real = ssm_scan_fwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"], Dskip=t["Dskip"],
+                        z=t["z"], reset=t["reset"], zoh=True)
+    cz = lambda v: torch.stack([v, torch.zeros_like(v)], dim=-1).contiguous()
+    cplx = ssm_scan_fwd(t["u"], t["dt_raw"], cz(t["A"]), cz(t["Bm"]), cz(t["Cm"]), dt_bias=t["dt_bias"],
+                        Dskip=t["Dskip"], z=t["z"], reset=t["reset"], complex_state=True, zoh=True)
+    torch.cuda.synchronize()
+    r, c = real.cpu().numpy().astype(np.float64), cplx.cpu().numpy().astype(np.float64)
+    assert_close(c, r, wl.F32, what="complex zoh kernel vs real zoh kernel")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("N", [1, 16, 128])
+def test_complex_decode_zoh(dtype, N):
+    y = wl.make_cplx_decode_inputs(5, 37, N, dtype, seed=60 + N, dt_lo=1e-3, dt_hi=3e-1)
+    y["A"] = zoh_A(37, N, np.random.default_rng(N))
+    out, h = run_update(y, y["h"], zoh=True)
+    check_decode(y, out, h, "zoh N=%d %s" % (N, dtype), zoh=True)
+
+
+def test_complex_scan_zoh_at_layer_size_sampled_channels():
+    """The 8 x 1536 x 2048, N = 16 layer shape with the zero-order hold."""
+    x = wl.make_cplx_inputs(8, 1536, 2048, 16, wl.BF16, seed=2)
+    got, hl = run_scan(x, zoh=True)
+    rng = np.random.default_rng(4)
+    for b in (0, 5):
+        ds = np.sort(rng.choice(1536, 48, replace=False))
+        sub = dict(u=x["u"][b:b + 1, ds], dt_raw=x["dt_raw"][b:b + 1, ds], z=x["z"][b:b + 1, ds],
+                   Bm=x["Bm"][b:b + 1], Cm=x["Cm"][b:b + 1], A=x["A"][ds], dt_bias=x["dt_bias"][ds],
+                   Dskip=x["Dskip"][ds], reset=None, dtype=x["dtype"])
+        ref, rhl = ref_scan(sub, zoh=True)
+        check(sub, got[b:b + 1, ds], hl[b:b + 1, ds], ref, rhl, "zoh layer b=%d" % b, zoh=True)
