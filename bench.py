@@ -279,7 +279,14 @@ def main():
     fcx = binding.prepare_scan(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], dt_bias=tc["dt_bias"],
                                Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True)
     xsec_f = timed(fcx, max(5, min(args.steps, 30)))
-    del fcx, tc, xc
+    fcz = binding.prepare_scan(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], dt_bias=tc["dt_bias"],
+                               Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True, zoh=True)
+    xsec_z = timed(fcz, max(5, min(args.steps, 30)))
+    doutc = wl.to_torch(wl.store(np.random.default_rng(4242).standard_normal((B, D, L)), cfg["dtype"]), dev)
+    bcx = binding.prepare_scan_bwd(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], doutc, dt_bias=tc["dt_bias"],
+                                   Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True)
+    xsec_b = timed(bcx, bsteps)
+    del fcx, fcz, bcx, doutc, tc, xc
     yc = wl.make_cplx_decode_inputs(Bd, Dd, Nd, wl.BF16, seed=5)
     tdc = {k: wl.to_torch(yc[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
     hdc = torch.from_numpy(yc["h"]).to(dev)
@@ -347,6 +354,9 @@ def main():
                                       "complex B, C (re, im pairs), y = Re(C h)",
                           "fwd_ms": xsec_f * 1e3, "fwd_vs_plain_forward": xsec_f / launch_s,
                           "fwd_elements_per_s": elements / xsec_f,
+                          "zoh_fwd_ms": xsec_z * 1e3,
+                          "bwd_ms": xsec_b * 1e3, "bwd_vs_complex_forward": xsec_b / xsec_f,
+                          "bwd_elements_per_s": elements / xsec_b,
                           "decode_workload": "state update B=64 D=2048 N=128 complex, bf16 inputs, fp32 state",
                           "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes,
                           "decode_hbm_gbps": xdbytes / xsec_d / 1e9},

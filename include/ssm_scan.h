@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10300 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10400 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -107,8 +107,9 @@ typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
  *                     gate and resets. It is supported without a conv stage,
  *                     in ssm_scan_fwd (whose workspace then holds complex
  *                     aggregates; ask ssm_scan_workspace_size with state_kind
- *                     set) and ssm_state_update; a conv stage with it, and the
- *                     backward, return SSM_ERR_UNSUPPORTED.
+ *                     set), ssm_state_update and, with SSM_DISC_DELTA_B,
+ *                     ssm_scan_bwd; a conv stage with it, and its backward
+ *                     with SSM_DISC_ZOH, return SSM_ERR_UNSUPPORTED.
  * Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 
@@ -272,6 +273,18 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *   conv_w, conv_b, conv_state_in, conv_width : the forward's conv arguments
  *   dconv_w (D,K), dconv_b (D), dconv_state_in (B,D,K-1) float32 outputs,
  *                     NULL => not written
+ * Complex state (state_kind = SSM_STATE_COMPLEX, SSM_DISC_DELTA_B, no conv):
+ * A, Bm, Cm, h0, dh_last and dA, dBm, dCm, dh0 gain a trailing (re, im)
+ * dimension of 2, as in the forward. The loss's h_last term is
+ * sum (Re dh_last Re h_last + Im dh_last Im h_last), and the gradient of a
+ * complex input x is stored as (dL/dRe x, dL/dIm x). With G_t that form of
+ * the adjoint of h_t, the formulas above become
+ *   G_t = conj(a_{t+1}) G_{t+1} + dy_t conj(C_t),   dC = sum_d dy_t conj(h_t),
+ *   dB = sum_d delta_t u_t G_t,   dA = sum_{b,t} delta_t G_t conj(a_t h_{t-1}),
+ *   du_t = dy_t D + delta_t Re sum_n conj(G_t) B_t,
+ *   d dt_raw_t = Re(sum_n conj(G_t) (A a_t h_{t-1} + B_t u_t)) sigmoid(..),
+ *   dh0 = conj(a_0) G_0,
+ * and y_t in dz_t is the real read-out Re sum_n C_t h_t + D u_t.
  * Outputs must not overlap each other, the inputs or the workspace. Shared
  * gradients (dA, dBm, dCm, dDskip, d_dt_bias, dconv_w, dconv_b) are sums in a
  * fixed order, so repeated calls give identical bits.
@@ -310,7 +323,7 @@ typedef struct {
   float* dconv_state_in;
   int32_t conv_width;
   int32_t discretization; /* ssm_discretization */
-  int32_t state_kind;     /* ssm_state_kind; only SSM_STATE_REAL is supported here */
+  int32_t state_kind;     /* ssm_state_kind (complex: SSM_DISC_DELTA_B, no conv stage) */
   int32_t reserved1;      /* set to 0 */
 } ssm_scan_bwd_params;
 

@@ -384,17 +384,20 @@ def ssm_state_update(h, u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return out
 
 
-def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads, conv=None, zoh=False):
+def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads, conv=None, zoh=False,
+                cplx=False):
     import torch
 
     Bt, D, L = u.shape
     N = A.shape[1]
-    _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, None, None, None, 0)  # input checks
+    _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, None, None, None, 0,
+                 cplx=cplx)  # input checks
     _need(dout, (Bt, D, L), "dout", u.dtype)
+    c2 = (2,) if cplx else ()  # complex tensors carry a trailing (re, im) axis
     if dh_last is not None:
-        _need(dh_last, (Bt, D, N), "dh_last", torch.float32)
-    shapes = dict(du=(Bt, D, L), d_dt_raw=(Bt, D, L), dz=(Bt, D, L), dA=(D, N), dBm=(Bt, L, N), dCm=(Bt, L, N),
-                  dDskip=(D,), d_dt_bias=(D,), dh0=(Bt, D, N))
+        _need(dh_last, (Bt, D, N) + c2, "dh_last", torch.float32)
+    shapes = dict(du=(Bt, D, L), d_dt_raw=(Bt, D, L), dz=(Bt, D, L), dA=(D, N) + c2, dBm=(Bt, L, N) + c2,
+                  dCm=(Bt, L, N) + c2, dDskip=(D,), d_dt_bias=(D,), dh0=(Bt, D, N) + c2)
     for k, t in grads.items():
         if t is not None and k in shapes:
             _need(t, shapes[k], k)
@@ -406,6 +409,7 @@ def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_las
     p.Bm, p.Cm, p.Dskip, p.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     p.reset, p.h0, p.dout, p.dh_last = _ptr(reset), _ptr(h0), _ptr(dout), _ptr(dh_last)
     p.discretization = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    p.state_kind = SSM_STATE_COMPLEX if cplx else SSM_STATE_REAL
     for k, t in grads.items():
         if k in ("dconv_w", "dconv_b", "dconv_state_in"):
             continue
@@ -424,7 +428,7 @@ def _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_las
     return p
 
 
-def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0):
+def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0, cplx=False):
     import torch
 
     Bt, D, L = u.shape
@@ -432,20 +436,22 @@ def _bwd_grads(u, A, Bm, z, grad_dtype, want_dD, want_dbias, want_dh0):
     dev = u.device
     gd = grad_dtype or torch.float32
     f32 = torch.float32
+    c2 = (2,) if cplx else ()
     return dict(du=torch.empty((Bt, D, L), dtype=gd, device=dev),
                 d_dt_raw=torch.empty((Bt, D, L), dtype=gd, device=dev),
                 dz=torch.empty((Bt, D, L), dtype=gd, device=dev) if z is not None else None,
-                dA=torch.empty((D, N), dtype=f32, device=dev),
-                dBm=torch.empty((Bt, L, N), dtype=f32, device=dev),
-                dCm=torch.empty((Bt, L, N), dtype=f32, device=dev),
+                dA=torch.empty((D, N) + c2, dtype=f32, device=dev),
+                dBm=torch.empty((Bt, L, N) + c2, dtype=f32, device=dev),
+                dCm=torch.empty((Bt, L, N) + c2, dtype=f32, device=dev),
                 dDskip=torch.empty((D,), dtype=f32, device=dev) if want_dD else None,
                 d_dt_bias=torch.empty((D,), dtype=f32, device=dev) if want_dbias else None,
-                dh0=torch.empty((Bt, D, N), dtype=f32, device=dev) if want_dh0 else None)
+                dh0=torch.empty((Bt, D, N) + c2, dtype=f32, device=dev) if want_dh0 else None)
 
 
 def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                  dh_last=None, grad_dtype=None, want_dDskip=True, want_d_dt_bias=True, want_dh0=True,
-                 conv_w=None, conv_b=None, conv_state_in=None, zoh=False, workspace=None, stream=None):
+                 conv_w=None, conv_b=None, conv_state_in=None, zoh=False, complex_state=False, workspace=None,
+                 stream=None):
     """Backward pass of ssm_scan_fwd for the same inputs and the output gradient dout.
 
     Returns a dict with du, d_dt_raw, dz (None without z) in ``grad_dtype``
@@ -454,11 +460,14 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
     gradient reaching h_last (None = 0). The workspace is allocated when not
     given or too small. With conv_w (D, K), u is the conv input and the dict
     also holds dconv_w (D, K), dconv_b (D,) and dconv_state_in (B, D, K-1).
+    complex_state=True: the complex-state scan; A, Bm, Cm, h0, dh_last and
+    the gradients dA, dBm, dCm, dh0 carry a trailing (re, im) axis, each
+    gradient holding dL/dRe and dL/dIm.
     """
     import torch
 
     lib = load_library()
-    grads = _bwd_grads(u, A, Bm, z, grad_dtype, want_dDskip, want_d_dt_bias, want_dh0)
+    grads = _bwd_grads(u, A, Bm, z, grad_dtype, want_dDskip, want_d_dt_bias, want_dh0, complex_state)
     if conv_w is not None:
         Bt, D, _ = u.shape
         K = conv_w.shape[1]
@@ -467,7 +476,7 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
         grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
                                    if K > 1 else None)
     p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
-                    (conv_w, conv_b, conv_state_in), zoh)
+                    (conv_w, conv_b, conv_state_in), zoh, complex_state)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     if workspace is None or workspace.numel() * workspace.element_size() < n.value:
@@ -480,14 +489,14 @@ def ssm_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None
 
 def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
                      dh_last=None, grad_dtype=None, conv_w=None, conv_b=None, conv_state_in=None, zoh=False,
-                     stream=None):
+                     complex_state=False, stream=None):
     """Marshal the arguments of ssm_scan_bwd once; returns a no-argument callable
     that enqueues the same backward pass again each time it is called and
     returns the gradient dict (the same tensors every time)."""
     import torch
 
     lib = load_library()
-    grads = _bwd_grads(u, A, Bm, z, grad_dtype, True, True, True)
+    grads = _bwd_grads(u, A, Bm, z, grad_dtype, True, True, True, complex_state)
     if conv_w is not None:
         Bt, D, _ = u.shape
         K = conv_w.shape[1]
@@ -496,7 +505,7 @@ def prepare_scan_bwd(u, dt_raw, A, Bm, Cm, dout, *, dt_bias=None, Dskip=None, z=
         grads["dconv_state_in"] = (torch.empty((Bt, D, K - 1), dtype=torch.float32, device=u.device)
                                    if K > 1 else None)
     p = _bwd_params(u, dt_raw, A, Bm, Cm, dout, dt_bias, Dskip, z, reset, h0, dh_last, grads,
-                    (conv_w, conv_b, conv_state_in), zoh)
+                    (conv_w, conv_b, conv_state_in), zoh, complex_state)
     n = ctypes.c_size_t(0)
     _check(lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     ws = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)

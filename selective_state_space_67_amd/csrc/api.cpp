@@ -132,7 +132,47 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_params* p, ScanSizes* sz) {
   return check_scan_sizes(&f, sz);
 }
 
+// The complex-state backward: no conv stage (as in the forward) and only the delta B form.
+ssm_status check_bwd_kind(const ssm_scan_bwd_params* p) {
+  const ssm_status s = check_kind(p->state_kind, p->conv_w != nullptr);
+  if (s != SSM_OK) return s;
+  if (p->state_kind == SSM_STATE_COMPLEX && p->discretization != SSM_DISC_DELTA_B)
+    return fail(SSM_ERR_UNSUPPORTED, "the complex-state backward supports only SSM_DISC_DELTA_B");
+  return SSM_OK;
+}
+
+// Complex state: checkpoints every 16 / NPL steps and complex aggregates,
+// checkpoints and partials (two floats per value).
+ssm_status plan_bwd_cplx(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout* lay) {
+  const int64_t B = p->batch, D = p->dim, L = p->seqlen, N = p->dstate;
+  ssm::plan_cplx_bwd(B, D, L, N, &lay->nsegb, &lay->seg_steps, &lay->nseg, &lay->seg_len, &lay->n_ck);
+  if (ssm::cplx_scan_grid_blocks(B, D, lay->nseg) > std::numeric_limits<int32_t>::max() ||
+      ssm::cplx_bwd_grid_blocks(B, D, lay->nsegb) > std::numeric_limits<int32_t>::max())
+    return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  int64_t ck, seg, part;
+  const int64_t groups = (D + 15) / 16;
+  if (!mul_ok(2 * sz.bdn, lay->n_ck, &ck) || !mul_ok(2 * sz.bdn, lay->nsegb, &seg) ||
+      !mul_ok(2 * sz.bln, 2 * groups, &part) || ck > (int64_t{1} << 58) || seg > (int64_t{1} << 58) ||
+      part > (int64_t{1} << 58))
+    return fail(SSM_ERR_BAD_SHAPE, "backward workspace size overflows");
+  size_t off = 0;
+  lay->off_agg = off;
+  off += align256(ssm::cplx_workspace_bytes(B, D, N, lay->nseg));
+  lay->off_ckpt = off;
+  off += align256(static_cast<size_t>(ck) * 4);
+  lay->off_segP = off;
+  off += align256(static_cast<size_t>(seg) * 4);
+  lay->off_segG = off;
+  off += align256(static_cast<size_t>(seg) * 4);
+  lay->off_part = off;
+  off += align256(ssm::cplx_bwd_partial_floats(B, D, L, N, lay->nsegb) * 4);
+  lay->off_uconv = lay->off_duconv = lay->off_convpart = off;
+  lay->total = off;
+  return SSM_OK;
+}
+
 ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout* lay) {
+  if (p->state_kind == SSM_STATE_COMPLEX) return plan_bwd_cplx(p, sz, lay);
   const int64_t B = p->batch, D = p->dim, L = p->seqlen, N = p->dstate;
   ssm::plan_bwd_segments(B, D, L, N, p->discretization == SSM_DISC_ZOH, &lay->nsegb, &lay->seg_steps);
   int nseg;
@@ -187,8 +227,7 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params* p, size_t* byt
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
-  if (p->state_kind != SSM_STATE_REAL)
-    return fail(SSM_ERR_UNSUPPORTED, "the backward supports only SSM_STATE_REAL (got state_kind %d)", p->state_kind);
+  if ((s = check_bwd_kind(p)) != SSM_OK) return s;
   BwdLayout lay;
   if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
   *bytes = lay.total;
@@ -214,8 +253,9 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
-  if (p->state_kind != SSM_STATE_REAL)
-    return fail(SSM_ERR_UNSUPPORTED, "the backward supports only SSM_STATE_REAL (got state_kind %d)", p->state_kind);
+  if ((s = check_bwd_kind(p)) != SSM_OK) return s;
+  const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
+  const int64_t cw = cplx ? 2 : 1;  // scalars per A, B, C and state entry
   const int64_t K = p->conv_w ? p->conv_width : 0;
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->dconv_w || p->dconv_b || p->dconv_state_in))
@@ -247,20 +287,20 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
 
   const Range inputs[] = {
       range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
-      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln, si, "Bm"),
-      range(p->Cm, sz.bln, si, "Cm"),        range(p->A, sz.dn, 4, "A"),
+      range(p->z, sz.bdl, si, "z"),          range(p->Bm, cw * sz.bln, si, "Bm"),
+      range(p->Cm, cw * sz.bln, si, "Cm"),   range(p->A, cw * sz.dn, 4, "A"),
       range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
-      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn, 4, "h0"),
-      range(p->dout, sz.bdl, si, "dout"),    range(p->dh_last, sz.bdn, 4, "dh_last"),
+      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, cw * sz.bdn, 4, "h0"),
+      range(p->dout, sz.bdl, si, "dout"),    range(p->dh_last, cw * sz.bdn, 4, "dh_last"),
       range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
       range(p->conv_state_in, bdk, 4, "conv_state_in"),
   };
   const Range outputs[] = {
       range(p->du, sz.bdl, sg, "du"),        range(p->d_dt_raw, sz.bdl, sg, "d_dt_raw"),
-      range(p->dz, sz.bdl, sg, "dz"),        range(p->dA, sz.dn, 4, "dA"),
-      range(p->dBm, sz.bln, 4, "dBm"),       range(p->dCm, sz.bln, 4, "dCm"),
+      range(p->dz, sz.bdl, sg, "dz"),        range(p->dA, cw * sz.dn, 4, "dA"),
+      range(p->dBm, cw * sz.bln, 4, "dBm"),  range(p->dCm, cw * sz.bln, 4, "dCm"),
       range(p->dDskip, p->dim, 4, "dDskip"), range(p->d_dt_bias, p->dim, 4, "d_dt_bias"),
-      range(p->dh0, sz.bdn, 4, "dh0"),
+      range(p->dh0, cw * sz.bdn, 4, "dh0"),
       range(p->dconv_w, p->dim * K, 4, "dconv_w"), range(p->dconv_b, p->dim, 4, "dconv_b"),
       range(p->dconv_state_in, bdk, 4, "dconv_state_in"),
       Range{static_cast<const char*>(p->workspace), lay.total, "workspace"},
@@ -309,8 +349,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   sp.conv_k = static_cast<int>(K);
   sp.uconv_out = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_uconv) : nullptr;
   sp.zoh = p->discretization == SSM_DISC_ZOH;
-  hipError_t e = ssm::launch_scan(sp, stream);
-  if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint sweep launch failed: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  if (!cplx) {
+    e = ssm::launch_scan(sp, stream);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint sweep launch failed: %s", hipGetErrorString(e));
+  }
 
   ssm::BwdPlan bp{};
   bp.B = p->batch;
@@ -357,6 +400,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   bp.dconv_b = p->dconv_b;
   bp.dconv_state = K > 1 ? p->dconv_state_in : nullptr;
   bp.zoh = p->discretization == SSM_DISC_ZOH;
+  if (cplx) {
+    e = ssm::launch_scan_cplx_bwd(sp, bp, stream);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   e = ssm::launch_scan_bwd(bp, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "reverse sweep launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -1,5 +1,5 @@
 // Host-side interface between the C-ABI front end (api.cpp) and the HIP
-// kernels (scan_fwd.hip, scan_bwd.hip, scan_cplx.hip, state_update.hip). Not installed; not part of the ABI.
+// kernels (scan_fwd.hip, scan_bwd.hip, scan_cplx.hip, scan_cplx_bwd.hip, state_update.hip). Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -95,7 +95,8 @@ hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);
 void plan_cplx_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg, int64_t* seg_len);
 size_t cplx_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg);
 int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg);
-hipError_t launch_scan_cplx(const ScanPlan& plan, hipStream_t stream);
+// aggregates_only: just the piece aggregates of a split scan (nothing when nseg == 1).
+hipError_t launch_scan_cplx(const ScanPlan& plan, hipStream_t stream, bool aggregates_only = false);
 hipError_t launch_state_update_cplx(const UpdatePlan& plan, hipStream_t stream);
 
 // Backward pass (scan_bwd.hip). The checkpoint sweep runs through launch_scan
@@ -160,5 +161,23 @@ int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb);
 // Floats of partial sums of the conv backward (per row tile: 4 taps + bias).
 size_t bwd_conv_partial_floats(int64_t B, int64_t D, int64_t L);
 hipError_t launch_scan_bwd(const BwdPlan& plan, hipStream_t stream);
+// Sums of the backward's partials in a fixed order: dB and dC (bln floats
+// each) over `groups` channel groups, dA (dn floats), dD and d dt_bias (D
+// floats, null: skipped) over `bs` batch-row segments.
+hipError_t launch_bwd_reduce(const float* partB, const float* partC, const float* partA, const float* partD,
+                             const float* partBias, float* dB, float* dC, float* dA, float* dD, float* dbias,
+                             int64_t bln, int64_t dn, int64_t D, int64_t groups, int64_t bs, hipStream_t stream);
+
+// Backward of the complex-state scan (scan_cplx_bwd.hip): the checkpoint
+// sweep writes the state entering every 16 / NPL steps (NPL = states per lane,
+// 1 for N <= 16 up to 16 for N = 256) to ckpt (B, n_ck, D, N, 2) and the
+// segments' adjoint aggregates to seg_P / seg_G (B, nsegb, D, N, 2); the
+// forward pieces come from `sp` (nseg, seg_len, ws), the reverse sweep and
+// reduction from `bp` (part: cplx_bwd_partial_floats floats).
+void plan_cplx_bwd(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps, int* nseg,
+                   int64_t* seg_len, int64_t* n_ck);
+size_t cplx_bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb);
+int64_t cplx_bwd_grid_blocks(int64_t B, int64_t D, int nsegb);
+hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream_t stream);
 
 }  // namespace ssm

@@ -801,6 +801,31 @@ int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb) {
   return B * ((D + bwd_channels_per_block(N) - 1) / bwd_channels_per_block(N)) * nsegb;
 }
 
+hipError_t launch_bwd_reduce(const float* partB, const float* partC, const float* partA, const float* partD,
+                             const float* partBias, float* dB, float* dC, float* dA, float* dD, float* dbias,
+                             int64_t bln, int64_t dn, int64_t D, int64_t groups, int64_t bs, hipStream_t stream) {
+  RedArgs r{};
+  r.bln = bln;
+  r.dn = dn;
+  r.D = D;
+  r.groups = groups;
+  r.bs = bs;
+  r.partB = partB;
+  r.partC = partC;
+  r.partA = partA;
+  r.partD = partD;
+  r.partBias = partBias;
+  r.dB = dB;
+  r.dC = dC;
+  r.dA = dA;
+  r.dD = dD;
+  r.dbias = dbias;
+  const int64_t total = 2 * ((r.bln + 3) / 4) + (r.dn + 3) / 4 + 2 * ((r.D + 3) / 4);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   const int cpw = bwd_channels_per_block(pl.N);
   const int64_t groups = (pl.D + cpw - 1) / cpw;
@@ -872,26 +897,8 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   });
   if (e != hipSuccess) return e;
 
-  RedArgs r{};
-  r.bln = bln;
-  r.dn = pl.D * pl.N;
-  r.D = pl.D;
-  r.groups = groups;
-  r.bs = pl.B * pl.nsegb;
-  r.partB = a.partB;
-  r.partC = a.partC;
-  r.partA = a.partA;
-  r.partD = a.partD;
-  r.partBias = a.partBias;
-  r.dB = pl.dB;
-  r.dC = pl.dC;
-  r.dA = pl.dA;
-  r.dD = pl.dD;
-  r.dbias = pl.dbias;
-  const int64_t total = 2 * ((r.bln + 3) / 4) + (r.dn + 3) / 4 + 2 * ((r.D + 3) / 4);
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
-  e = hipGetLastError();
+  e = launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, pl.dB, pl.dC, pl.dA, pl.dD, pl.dbias, bln,
+                        pl.D * pl.N, pl.D, groups, pl.B * pl.nsegb, stream);
   if (e != hipSuccess || !pl.conv_w) return e;
 
   ConvBwdArgs c{};

@@ -38,64 +38,17 @@
 // recurrences in lockstep, so the row needs no skew.
 #include <algorithm>
 
-#include "device_math.h"
+#include "cplx_device.h"
 #include "kernels.h"
 
 namespace ssm {
 namespace {
 
+using namespace cplx;
+
 constexpr int kThreads = 256;
 constexpr int kCPW = 16;  // channels per workgroup (one per DPP row)
 constexpr int kT = 16;    // steps per chunk (one per lane of a row)
-// 1 / (2 pi) as the sum of two floats (the second is the rounding error of the first).
-constexpr float kInv2PiHi = 0.15915494f;
-constexpr float kInv2PiLo = 0.15915494309189535 - static_cast<double>(0.15915494f);
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane gets the total.
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
-}
-
-// sin and cos of the angle delta (ai + ai_lo) revolutions. The product
-// p = delta ai is split into p and its exact rounding error; p - rint(p) is
-// exact and lies in [-1/2, 1/2]; q quarter turns are taken off exactly, and
-// the small parts are added to the remainder r, |r| <= 1/8 revolution. Then
-// theta = 2 pi r, sin and cos by their Taylor series through theta^9 and
-// theta^10 (truncation below 2e-9 and 1.2e-10 on |theta| <= pi/4), and a
-// rotation by q quarter turns.
-__device__ __forceinline__ void sincos_rev(float delta, float ai, float ai_lo, float& s, float& c) {
-  const float p = delta * ai;
-  const float lo = __builtin_fmaf(delta, ai, -p) + delta * ai_lo;
-  const float f = p - __builtin_rintf(p);
-  const float q = __builtin_rintf(4.0f * f);  // -2 .. 2
-  const float r = __builtin_fmaf(-0.25f, q, f) + lo;
-  const float th = r * 6.28318530717958648f;
-  const float t2 = th * th;
-  float sp = __builtin_fmaf(t2, 2.75573192e-6f, -1.98412698e-4f);
-  sp = __builtin_fmaf(t2, sp, 8.33333333e-3f);
-  sp = __builtin_fmaf(t2, sp, -1.66666667e-1f);
-  const float sn = __builtin_fmaf(th * t2, sp, th);
-  float cp = __builtin_fmaf(t2, -2.75573192e-7f, 2.48015873e-5f);
-  cp = __builtin_fmaf(t2, cp, -1.38888889e-3f);
-  cp = __builtin_fmaf(t2, cp, 4.16666667e-2f);
-  cp = __builtin_fmaf(t2, cp, -0.5f);
-  const float cs = __builtin_fmaf(t2, cp, 1.0f);
-  // (sin, cos) of theta + q pi/2: q = 1 -> (c, -s), 2 -> (-s, -c), 3 (= -1) -> (-c, s)
-  const int qi = static_cast<int>(q) & 3;
-  const float s2 = (qi & 1) ? cs : sn;
-  const float c2 = (qi & 1) ? sn : cs;
-  s = (qi & 2) ? -s2 : s2;
-  c = ((qi + 1) & 2) ? -c2 : c2;
-}
 
 struct CplxArgs {
   int64_t B, D, L, N;
@@ -119,39 +72,6 @@ struct CplxArgs {
   float* ws_H;  // (nseg - 1, B, D, N, 2): their end states from a zero start
 };
 
-// Per-lane constants of one state: Re A log2(e) for the decay's magnitude,
-// Im A / (2 pi) as ai + ai_lo (ai rounded, ai_lo the rest to within float32
-// rounding) for its angle, and for the zero-order hold A and 1/A.
-struct CState {
-  float ar, ai, ai_lo;
-  float re, im, ir, ii;
-};
-
-__device__ __forceinline__ CState make_cstate(float re, float im) {
-  CState q;
-  q.ar = re * kLog2e;
-  q.ai = im * kInv2PiHi;
-  q.ai_lo = __builtin_fmaf(im, kInv2PiHi, -q.ai) + im * kInv2PiLo;
-  q.re = re;
-  q.im = im;
-  const float m = re * re + im * im;
-  const float r = m > 0.0f ? 1.0f / m : 0.0f;  // 1/A = conj(A) / |A|^2; 0 for A = 0
-  q.ir = re * r;
-  q.ii = -im * r;
-  return q;
-}
-
-// Constants of this lane's states n0 .. n0+NPL-1 (zero past N).
-template <int NPL>
-__device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0, bool dvalid, CState (&q)[NPL]) {
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int n = n0 + j;
-    const bool ok = dvalid && n < N;
-    q[j] = make_cstate(ok ? A[2 * (d * N + n)] : 0.0f, ok ? A[2 * (d * N + n) + 1] : 0.0f);
-  }
-}
-
 // One step of a state: h = exp(delta A) h + q u B with the input coefficient
 // q = delta, or with the zero-order hold q = (exp(delta A) - 1) / A; returns
 // Re(C h). dv is delta u (or u with the zero-order hold). The zero-order hold
@@ -161,10 +81,8 @@ __device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0,
 template <bool ZOH>
 __device__ __forceinline__ float cplx_step(float dl, float dv, const CState& q, float2 Bv, float2 Cv, float& hr,
                                            float& hi) {
-  const float e = fast_exp2(dl * q.ar);
-  float s, c;
-  sincos_rev(dl, q.ai, q.ai_lo, s, c);
-  const float are = e * c, aim = e * s;
+  float are, aim;
+  decay(dl, q, are, aim);
   float br = Bv.x * dv, bi = Bv.y * dv;
   if constexpr (ZOH) {
     const float xr = dl * q.re, xi = dl * q.im;
@@ -363,15 +281,6 @@ struct CplxUpdateArgs {
   void* out;
 };
 
-// One complex value stored as an (re, im) pair of the input type, widened.
-__device__ __forceinline__ float2 load_cpair(const float* p, int64_t n) {
-  return *reinterpret_cast<const float2*>(p + 2 * n);
-}
-__device__ __forceinline__ float2 load_cpair(const bf16_t* p, int64_t n) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2 * n);
-  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
-}
-
 // Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup. Lane
 // k holds states k, k + 16, k + 32, ..., so for each j the 16 lanes of a row
 // read 16 consecutive (re, im) pairs of h, A, B and C: coalesced accesses to
@@ -466,7 +375,7 @@ size_t cplx_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg) {
 
 int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg) { return B * ((D + kCPW - 1) / kCPW) * nseg; }
 
-hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
+hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregates_only) {
   CplxArgs a{};
   a.B = p.B;
   a.D = p.D;
@@ -503,8 +412,9 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream) {
       if (p.nseg > 1) {  // the last piece's aggregate is never needed
         hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z>), grid_agg, dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || aggregates_only) return e;
       }
+      if (aggregates_only) return hipSuccess;
       hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z>), grid, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };

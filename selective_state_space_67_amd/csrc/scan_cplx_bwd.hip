@@ -1,0 +1,588 @@
+// Backward pass of the complex-state selective scan (gfx950).
+//
+// The gradients of loss = sum dout out + sum (Re dh_last Re h_last +
+// Im dh_last Im h_last) with respect to every input of the complex-state
+// forward: the real u, delta (through dt_raw and dt_bias), z and D, and the
+// complex A, B, C and h0, whose gradients are given as dL/dRe + i dL/dIm.
+// With G_t that form of the adjoint of h_t, the chain rule through
+// h_t = a_t h_{t-1} + delta_t u_t B_t, a_t = exp(delta_t A), gives
+//
+//   G_t         = conj(a_{t+1}) G_{t+1} + dy_t conj(C_t),  dy_t = dout_t silu(z_t)
+//   dC_t[n]    += dy_t conj(h_t[n])       dB_t[n] += delta_t u_t G_t[n]   (sums over d)
+//   dA[n]      += delta_t G_t[n] conj(a_t[n] h_{t-1}[n])                 (sum over b, t)
+//   du_t        = delta_t Re sum_n conj(G_t[n]) B_t[n] + D dy_t
+//   d delta_t   = Re sum_n conj(G_t[n]) (A[n] a_t[n] h_{t-1}[n] + B_t[n] u_t)
+//   d dt_raw_t  = d delta_t sigmoid(dt_raw_t + dt_bias)
+//   dz_t        = dout_t y_t silu'(z_t),  y_t = Re sum_n C_t[n] h_t[n] + D u_t
+//   dh0         = conj(a_0) G_0
+//
+// where a reset at t makes a_t = 0. The states are recomputed, not stored
+// ("Technical analysis: Mamba selective state spaces", section 2.2, item 3).
+//
+// Launches (after the forward's aggregate pass when the sequence is split
+// into pieces):
+// 1. Checkpoint sweep (cplx_ckpt_kernel): the forward recurrence in the
+//    layout of the complex scan (a DPP row of 16 lanes per channel, lane k
+//    holding the NPL consecutive states k NPL ..), writing the state entering
+//    every KC = 16 / NPL steps. For every reverse segment it also writes
+//    P = prod_t a_t and G = conj(sum_t (prod_{r <= t} a_r) dy_t C_t), both
+//    over the segment's steps, so that the adjoint reaching the end of the
+//    preceding segment is conj(P) X + G for the adjoint X arriving from the
+//    right, accumulated in forward order.
+// 2. Reverse sweep (cplx_bwd_kernel): one workgroup per (segment, batch row,
+//    16 channels). It folds the later segments' (P, G) into the adjoint
+//    arriving at its end, then walks its 16-step chunks backwards. For every
+//    KC-step block it recomputes the states from the checkpoint, keeping each
+//    step's a_t and a_t h_{t-1} in registers, and runs the adjoint back
+//    through the block. The three sums over n per step are DPP row sums; the
+//    sums of dB and dC over the workgroup's 16 channels go through LDS and
+//    are written as one partial per channel group.
+// 3. Reduction (shared with the real backward): dB and dC over channel
+//    groups, dA, dD and d dt_bias over batch rows and segments, in a fixed
+//    order, so repeated calls give identical bits.
+#include <algorithm>
+
+#include "cplx_device.h"
+#include "kernels.h"
+
+namespace ssm {
+namespace {
+
+using namespace cplx;
+
+constexpr int kThreads = 256;
+constexpr int kCPW = 16;  // channels per workgroup (one per DPP row)
+constexpr int kT = 16;    // steps per chunk (one per lane of a row)
+
+struct CplxBwdArgs {
+  int64_t B, D, L, N;
+  int n_dgroups;
+  int grad_bf16;
+  // forward pieces of the checkpoint sweep
+  int nseg;
+  int64_t seg_len;
+  const float* ws_P;  // (nseg - 1, B, D, N, 2) piece decay products (nseg > 1)
+  const float* ws_H;  // (nseg - 1, B, D, N, 2) piece end states from a zero start
+  // reverse segments and checkpoints
+  int nsegb;
+  int64_t seg_steps;  // multiple of 16; seg_len is a multiple of it
+  int64_t n_ck;       // checkpoints, one per KC steps
+  const void* u;
+  const void* dt;
+  const void* z;
+  const void* Bm;    // (B, L, N, 2)
+  const void* Cm;    // (B, L, N, 2)
+  const void* dout;  // (B, D, L)
+  const float* dt_bias;
+  const float* A;  // (D, N, 2)
+  const float* Dskip;
+  const float* h0;       // (B, D, N, 2) or null
+  const float* dh_last;  // (B, D, N, 2) or null
+  const uint8_t* reset;
+  float* ckpt;   // (B, n_ck, D, N, 2)
+  float* seg_P;  // (B, nsegb, D, N, 2)
+  float* seg_G;  // (B, nsegb, D, N, 2)
+  void* du;
+  void* ddt;
+  void* dz;
+  float* dh0;       // (B, D, N, 2) or null
+  float* partB;     // (groups, B, L, N, 2)
+  float* partC;     // (groups, B, L, N, 2)
+  float* partA;     // (B, nsegb, D, N, 2)
+  float* partD;     // (B, nsegb, D)
+  float* partBias;  // (B, nsegb, D)
+};
+
+// Stages step t0 + k of this lane's channel: loads u, dt_raw, z and dout and
+// forms delta (negated on a reset step), delta u and dy = dout silu(z).
+template <typename InT, bool HAS_RESET>
+struct StepInputs {
+  float dl = 0.0f, uu = 0.0f, sgx = 0.0f, go = 0.0f, zz = 0.0f, dy = 0.0f;
+  bool reset = false;
+  __device__ __forceinline__ void load(const InT* u, const InT* dt, const InT* z, const InT* dout,
+                                       const uint8_t* rs, int t, float bias) {
+    uu = load_elem(u, t);
+    const float x = load_elem(dt, t) + bias;
+    dl = softplus_f32(x);
+    sgx = fast_rcp(1.0f + fast_exp2(-x * kLog2e));  // d softplus / dx
+    go = load_elem(dout, t);
+    dy = go;
+    if (z) {
+      zz = load_elem(z, t);
+      dy = go * silu_f32(zz);
+    }
+    if (HAS_RESET) reset = rs[t] != 0;
+  }
+  __device__ __forceinline__ float4 staged() const {
+    return make_float4(reset ? -dl : dl, dl * uu, dy, 0.0f);
+  }
+};
+
+// Stages B and C of steps t0 .. t0+steps-1 as (B.re, B.im, C.re, C.im) per
+// (step, state); entries past N keep their zeros, steps past `steps` keep
+// what they held (finite; their delta, u and dy are zero).
+template <int NPAD, typename InT>
+__device__ __forceinline__ void stage_bc(float4* s_bc, const InT* Bb, const InT* Cb, int steps, int N, int tid) {
+  for (int i = tid; i < steps * N; i += kThreads) {
+    const int tl = i / N, n = i - tl * N;
+    const int64_t e = static_cast<int64_t>(tl) * N + n;
+    const float2 bv = load_cpair(Bb, e), cv = load_cpair(Cb, e);
+    s_bc[tl * NPAD + n] = make_float4(bv.x, bv.y, cv.x, cv.y);
+  }
+}
+
+template <int NPL, typename InT, bool HAS_RESET>
+__global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a) {
+  constexpr int NPAD = 16 * NPL;
+  constexpr int KC = 16 / NPL;
+  const int g = blockIdx.x % a.n_dgroups;
+  const int rest = blockIdx.x / a.n_dgroups;
+  const int b = rest % static_cast<int>(a.B);
+  const int sp = rest / static_cast<int>(a.B);  // forward piece
+  const int64_t t_seg = static_cast<int64_t>(sp) * a.seg_len;
+  const int Lseg = static_cast<int>(min(a.seg_len, a.L - t_seg));
+  const int N = static_cast<int>(a.N);
+  const int tid = threadIdx.x;
+  const int k = tid & 15;
+  const int c = tid >> 4;
+  const int64_t d = static_cast<int64_t>(g) * kCPW + c;
+  const bool dvalid = d < a.D;
+  const int n0 = k * NPL;
+
+  __shared__ __align__(16) float4 s_bc[kT * NPAD];
+  __shared__ __align__(16) float4 s_st[kCPW * kT];  // (delta, delta u, dy, 0); delta negated on a reset step
+
+  CState cq[NPL];
+  load_A<NPL>(a.A, d, N, n0, dvalid, cq);
+  const int64_t row = static_cast<int64_t>(b) * a.D + d;
+  // state h, the segment's running decay product q and adjoint sum s
+  float hr[NPL], hi[NPL], qr[NPL], qi[NPL], sr[NPL], si[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int64_t e = 2 * (row * N + n0 + j);
+    const bool ok = dvalid && n0 + j < N;
+    hr[j] = ok && a.h0 ? a.h0[e] : 0.0f;
+    hi[j] = ok && a.h0 ? a.h0[e + 1] : 0.0f;
+    if (ok) {
+      for (int q = 0; q < sp; ++q) {  // h <- P h + H for the preceding pieces
+        const int64_t w = static_cast<int64_t>(q) * a.B * a.D * N * 2 + e;
+        const float pr = a.ws_P[w], pi = a.ws_P[w + 1];
+        const float nr = __builtin_fmaf(pr, hr[j], __builtin_fmaf(-pi, hi[j], a.ws_H[w]));
+        const float ni = __builtin_fmaf(pr, hi[j], __builtin_fmaf(pi, hr[j], a.ws_H[w + 1]));
+        hr[j] = nr;
+        hi[j] = ni;
+      }
+    }
+    qr[j] = 1.0f;
+    qi[j] = 0.0f;
+    sr[j] = 0.0f;
+    si[j] = 0.0f;
+  }
+  for (int i = tid; i < kT * NPAD; i += kThreads) s_bc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  const InT* __restrict__ u = static_cast<const InT*>(a.u) + row * a.L + t_seg;
+  const InT* __restrict__ dt = static_cast<const InT*>(a.dt) + row * a.L + t_seg;
+  const InT* __restrict__ z = a.z ? static_cast<const InT*>(a.z) + row * a.L + t_seg : nullptr;
+  const InT* __restrict__ go = static_cast<const InT*>(a.dout) + row * a.L + t_seg;
+  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + (static_cast<int64_t>(b) * a.L + t_seg) * N * 2;
+  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + (static_cast<int64_t>(b) * a.L + t_seg) * N * 2;
+  const uint8_t* __restrict__ rs = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L + t_seg : nullptr;
+  const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
+
+  for (int t0 = 0; t0 < Lseg; t0 += kT) {
+    const int steps = min(kT, Lseg - t0);
+    __syncthreads();  // the previous chunk's readers are done
+    stage_bc<NPAD>(s_bc, Bb + static_cast<int64_t>(t0) * N * 2, Cb + static_cast<int64_t>(t0) * N * 2, steps, N, tid);
+    StepInputs<InT, HAS_RESET> in;
+    if (dvalid && k < steps) in.load(u, dt, z, go, rs, t0 + k, bias);
+    s_st[c * kT + k] = in.staged();
+    __syncthreads();
+
+#pragma unroll 4
+    for (int tl = 0; tl < kT; ++tl) {
+      const int64_t tg = t_seg + t0 + tl;
+      if (tl % KC == 0 && dvalid && tl < steps) {  // the state entering step tg
+        float* ck = a.ckpt + ((static_cast<int64_t>(b) * a.n_ck + tg / KC) * a.D + d) * N * 2;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+          if (n0 + j < N) *reinterpret_cast<float2*>(ck + 2 * (n0 + j)) = make_float2(hr[j], hi[j]);
+      }
+      const float4 st = s_st[c * kT + tl];
+      float dl = st.x;
+      if (HAS_RESET) {
+        const bool r = __float_as_int(dl) < 0;
+        if (__builtin_amdgcn_ballot_w64(r)) {
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) {
+            hr[j] = r ? 0.0f : hr[j];
+            hi[j] = r ? 0.0f : hi[j];
+            qr[j] = r ? 0.0f : qr[j];
+            qi[j] = r ? 0.0f : qi[j];
+          }
+        }
+        dl = fabsf(dl);
+      }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const float4 bc = s_bc[tl * NPAD + n0 + j];
+        float ar, ai;
+        decay(dl, cq[j], ar, ai);
+        const float nr = __builtin_fmaf(ar, hr[j], __builtin_fmaf(-ai, hi[j], st.y * bc.x));
+        const float ni = __builtin_fmaf(ar, hi[j], __builtin_fmaf(ai, hr[j], st.y * bc.y));
+        hr[j] = nr;
+        hi[j] = ni;
+        const float pr = __builtin_fmaf(ar, qr[j], -ai * qi[j]);
+        const float pi = __builtin_fmaf(ar, qi[j], ai * qr[j]);
+        qr[j] = pr;
+        qi[j] = pi;
+        const float cr = st.z * bc.z, ci = st.z * bc.w;  // dy C
+        sr[j] = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, sr[j]));
+        si[j] = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, si[j]));
+      }
+    }
+    const int64_t tend = t_seg + t0 + kT;
+    if (tend % a.seg_steps == 0 || tend >= a.L) {  // end of a reverse segment
+      const int64_t sg = (t_seg + t0) / a.seg_steps;
+      if (dvalid) {
+        const int64_t w = ((static_cast<int64_t>(b) * a.nsegb + sg) * a.D + d) * N * 2;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          if (n0 + j < N) {
+            *reinterpret_cast<float2*>(a.seg_P + w + 2 * (n0 + j)) = make_float2(qr[j], qi[j]);
+            *reinterpret_cast<float2*>(a.seg_G + w + 2 * (n0 + j)) = make_float2(sr[j], -si[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        qr[j] = 1.0f;
+        qi[j] = 0.0f;
+        sr[j] = 0.0f;
+        si[j] = 0.0f;
+      }
+    }
+  }
+}
+
+template <int NPL, typename InT, bool HAS_RESET>
+__global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs a) {
+  constexpr int NPAD = 16 * NPL;
+  constexpr int KC = 16 / NPL;                     // steps per checkpoint block
+  constexpr int F = NPAD >= 64 ? 1 : 64 / NPAD;    // steps per flush of the channel sums
+  const int g = blockIdx.x % a.n_dgroups;
+  const int rest = blockIdx.x / a.n_dgroups;
+  const int b = rest % static_cast<int>(a.B);
+  const int sg = rest / static_cast<int>(a.B);  // reverse segment
+  const int64_t s_t0 = static_cast<int64_t>(sg) * a.seg_steps;
+  const int64_t s_t1 = min(s_t0 + a.seg_steps, a.L);
+  const int N = static_cast<int>(a.N);
+  const int tid = threadIdx.x;
+  const int k = tid & 15;
+  const int c = tid >> 4;
+  const int64_t d = static_cast<int64_t>(g) * kCPW + c;
+  const bool dvalid = d < a.D;
+  const int n0 = k * NPL;
+
+  __shared__ __align__(16) float4 s_bc[kT * NPAD];
+  __shared__ __align__(16) float4 s_st[kCPW * kT];
+  // per (flush slot, channel, state): (dB.re, dB.im, dC.re, dC.im) of one step
+  __shared__ __align__(16) float4 s_dbc[F * kCPW * NPAD];
+
+  CState cq[NPL];
+  load_A<NPL>(a.A, d, N, n0, dvalid, cq);
+  const int64_t row = static_cast<int64_t>(b) * a.D + d;
+  // adjoint arriving from the right: dh_last, folded through the later segments
+  float xr[NPL], xi[NPL], dar[NPL], dai[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int64_t e = 2 * (row * N + n0 + j);
+    const bool ok = dvalid && n0 + j < N;
+    xr[j] = ok && a.dh_last ? a.dh_last[e] : 0.0f;
+    xi[j] = ok && a.dh_last ? a.dh_last[e + 1] : 0.0f;
+    if (ok) {
+      for (int q = a.nsegb - 1; q > sg; --q) {  // X <- conj(P) X + G
+        const int64_t w = ((static_cast<int64_t>(b) * a.nsegb + q) * a.D + d) * N * 2 + 2 * (n0 + j);
+        const float pr = a.seg_P[w], pi = a.seg_P[w + 1];
+        const float nr = __builtin_fmaf(pr, xr[j], __builtin_fmaf(pi, xi[j], a.seg_G[w]));
+        const float ni = __builtin_fmaf(pr, xi[j], __builtin_fmaf(-pi, xr[j], a.seg_G[w + 1]));
+        xr[j] = nr;
+        xi[j] = ni;
+      }
+    }
+    dar[j] = 0.0f;
+    dai[j] = 0.0f;
+  }
+  for (int i = tid; i < kT * NPAD; i += kThreads) s_bc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  const InT* __restrict__ u = static_cast<const InT*>(a.u) + row * a.L;
+  const InT* __restrict__ dt = static_cast<const InT*>(a.dt) + row * a.L;
+  const InT* __restrict__ z = a.z ? static_cast<const InT*>(a.z) + row * a.L : nullptr;
+  const InT* __restrict__ go = static_cast<const InT*>(a.dout) + row * a.L;
+  const InT* __restrict__ Bb = static_cast<const InT*>(a.Bm) + static_cast<int64_t>(b) * a.L * N * 2;
+  const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + static_cast<int64_t>(b) * a.L * N * 2;
+  const uint8_t* __restrict__ rs = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L : nullptr;
+  const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
+  const float dsk = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
+  const int64_t gbl = (static_cast<int64_t>(g) * a.B + b) * a.L;  // partial row of this group and batch row
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+
+  for (int64_t t0 = s_t0 + (s_t1 - s_t0 - 1) / kT * kT; t0 >= s_t0; t0 -= kT) {
+    const int steps = static_cast<int>(min<int64_t>(kT, a.L - t0));
+    __syncthreads();  // the previous chunk's readers are done
+    stage_bc<NPAD>(s_bc, Bb + t0 * N * 2, Cb + t0 * N * 2, steps, N, tid);
+    StepInputs<InT, HAS_RESET> in;
+    const bool live = dvalid && k < steps;
+    if (live) in.load(u, dt, z, go, rs, static_cast<int>(t0) + k, bias);
+    s_st[c * kT + k] = in.staged();
+    __syncthreads();
+
+    float m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;  // the row sums of this lane's step
+#pragma unroll 1
+    for (int tb = kT - KC; tb >= 0; tb -= KC) {
+      if (tb >= steps) continue;  // the whole block lies past L: the adjoint passes unchanged
+      // recompute the block's states from its checkpoint
+      float hr[NPL], hi[NPL];
+      {
+        const float* ck = a.ckpt + ((static_cast<int64_t>(b) * a.n_ck + (t0 + tb) / KC) * a.D + d) * N * 2;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const bool ok = dvalid && n0 + j < N;
+          const float2 v = ok ? *reinterpret_cast<const float2*>(ck + 2 * (n0 + j)) : make_float2(0.0f, 0.0f);
+          hr[j] = v.x;
+          hi[j] = v.y;
+        }
+      }
+      float2 ha[KC][NPL], hw[KC][NPL];  // a_t and a_t h_{t-1} of the block's steps
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const float4 st = s_st[c * kT + tb + i];
+        float dl = st.x;
+        if (HAS_RESET) {
+          const bool r = __float_as_int(dl) < 0;
+          if (__builtin_amdgcn_ballot_w64(r)) {
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+              hr[j] = r ? 0.0f : hr[j];
+              hi[j] = r ? 0.0f : hi[j];
+            }
+          }
+          dl = fabsf(dl);
+        }
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const float4 bc = s_bc[(tb + i) * NPAD + n0 + j];
+          float ar, ai;
+          decay(dl, cq[j], ar, ai);
+          const float wr = __builtin_fmaf(ar, hr[j], -ai * hi[j]);
+          const float wi = __builtin_fmaf(ar, hi[j], ai * hr[j]);
+          ha[i][j] = make_float2(ar, ai);
+          hw[i][j] = make_float2(wr, wi);
+          hr[j] = __builtin_fmaf(st.y, bc.x, wr);
+          hi[j] = __builtin_fmaf(st.y, bc.y, wi);
+        }
+      }
+      // the adjoint back through the block
+#pragma unroll
+      for (int i = KC - 1; i >= 0; --i) {
+        const float4 st = s_st[c * kT + tb + i];
+        const float dl = fabsf(st.x), dv = st.y, dy = st.z;
+        float p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const float4 bc = s_bc[(tb + i) * NPAD + n0 + j];
+          const float gr = __builtin_fmaf(dy, bc.z, xr[j]);  // G = X + dy conj(C)
+          const float gi = __builtin_fmaf(-dy, bc.w, xi[j]);
+          const float2 w = hw[i][j];
+          const float hr2 = __builtin_fmaf(dv, bc.x, w.x);  // h_t
+          const float hi2 = __builtin_fmaf(dv, bc.y, w.y);
+          const float er = __builtin_fmaf(gr, w.x, gi * w.y);  // E = G conj(a h_{t-1})
+          const float ei = __builtin_fmaf(gi, w.x, -gr * w.y);
+          dar[j] = __builtin_fmaf(dl, er, dar[j]);
+          dai[j] = __builtin_fmaf(dl, ei, dai[j]);
+          p1 = __builtin_fmaf(gr, bc.x, __builtin_fmaf(gi, bc.y, p1));        // Re conj(G) B
+          p2 = __builtin_fmaf(cq[j].re, er, __builtin_fmaf(cq[j].im, ei, p2));  // Re conj(G) A a h_{t-1}
+          p3 = __builtin_fmaf(bc.z, hr2, __builtin_fmaf(-bc.w, hi2, p3));     // Re C h
+          s_dbc[((i % F) * kCPW + c) * NPAD + n0 + j] = make_float4(dv * gr, dv * gi, dy * hr2, -dy * hi2);
+          const float2 av = ha[i][j];  // X <- conj(a) G; 0 across a reset
+          const float nr = __builtin_fmaf(av.x, gr, av.y * gi);
+          const float ni = __builtin_fmaf(av.x, gi, -av.y * gr);
+          const bool r = HAS_RESET && __float_as_int(st.x) < 0;
+          xr[j] = r ? 0.0f : nr;
+          xi[j] = r ? 0.0f : ni;
+        }
+        p1 = row_sum16(p1);
+        p2 = row_sum16(p2);
+        p3 = row_sum16(p3);
+        if (k == tb + i) {
+          m1 = p1;
+          m2 = p2;
+          m3 = p3;
+        }
+        if (i % F == 0) {  // add the F steps' dB and dC over the 16 channels
+          __syncthreads();
+          const float* sd = reinterpret_cast<const float*>(s_dbc);
+          for (int e = tid; e < F * NPAD * 4; e += kThreads) {
+            const int comp = e & 3, n = (e >> 2) % NPAD, fs = (e >> 2) / NPAD;
+            const int64_t t = t0 + tb + i + fs;
+            if (n < N && t < a.L) {
+              float acc = 0.0f;
+#pragma unroll
+              for (int cc = 0; cc < kCPW; ++cc) acc += sd[((fs * kCPW + cc) * NPAD + n) * 4 + comp];
+              float* dst = comp < 2 ? a.partB : a.partC;
+              dst[((gbl + t) * N + n) * 2 + (comp & 1)] = acc;
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+    if (live) {
+      const float du = __builtin_fmaf(in.dl, m1, dsk * in.dy);
+      const float ddt = __builtin_fmaf(in.uu, m1, m2) * in.sgx;
+      const int64_t o = row * a.L + t0 + k;
+      if (a.grad_bf16) {
+        store_elem(static_cast<bf16_t*>(a.du), o, du);
+        store_elem(static_cast<bf16_t*>(a.ddt), o, ddt);
+      } else {
+        store_elem(static_cast<float*>(a.du), o, du);
+        store_elem(static_cast<float*>(a.ddt), o, ddt);
+      }
+      if (z) {
+        const float y = __builtin_fmaf(dsk, in.uu, m3);
+        const float sz = fast_rcp(1.0f + fast_exp2(-in.zz * kLog2e));
+        const float dz = in.go * y * sz * __builtin_fmaf(in.zz, 1.0f - sz, 1.0f);
+        if (a.grad_bf16)
+          store_elem(static_cast<bf16_t*>(a.dz), o, dz);
+        else
+          store_elem(static_cast<float*>(a.dz), o, dz);
+      }
+      dD_acc = __builtin_fmaf(in.dy, in.uu, dD_acc);
+      dbias_acc += ddt;
+    }
+  }
+  dD_acc = row_sum16(dD_acc);
+  dbias_acc = row_sum16(dbias_acc);
+  if (!dvalid) return;
+  const int64_t pw = (static_cast<int64_t>(b) * a.nsegb + sg) * a.D + d;
+  if (k == 0) {
+    a.partD[pw] = dD_acc;
+    a.partBias[pw] = dbias_acc;
+  }
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    if (n0 + j >= N) continue;
+    *reinterpret_cast<float2*>(a.partA + pw * N * 2 + 2 * (n0 + j)) = make_float2(dar[j], dai[j]);
+    if (sg == 0 && a.dh0) *reinterpret_cast<float2*>(a.dh0 + 2 * (row * N + n0 + j)) = make_float2(xr[j], xi[j]);
+  }
+}
+
+template <typename Fn>
+hipError_t with_npl(int64_t N, Fn&& fn) {
+  if (N <= 16) return fn(std::integral_constant<int, 1>{});
+  if (N <= 32) return fn(std::integral_constant<int, 2>{});
+  if (N <= 64) return fn(std::integral_constant<int, 4>{});
+  if (N <= 128) return fn(std::integral_constant<int, 8>{});
+  return fn(std::integral_constant<int, 16>{});
+}
+
+int npl_of(int64_t N) { return N <= 16 ? 1 : N <= 32 ? 2 : N <= 64 ? 4 : N <= 128 ? 8 : 16; }
+
+}  // namespace
+
+// Reverse segments: enough workgroups to fill the GPU a few times over
+// (about 2048), each segment at least 256 steps. The checkpoint sweep's
+// forward pieces are the complex scan's, lengthened to whole segments.
+void plan_cplx_bwd(int64_t B, int64_t D, int64_t L, int64_t N, int* nsegb, int64_t* seg_steps, int* nseg,
+                   int64_t* seg_len, int64_t* n_ck) {
+  const int64_t chunks = (L + kT - 1) / kT;
+  const int64_t base = B * ((D + kCPW - 1) / kCPW);
+  int64_t want = (2048 + base - 1) / base;
+  want = std::max<int64_t>(1, std::min<int64_t>(want, chunks / 16));
+  const int64_t steps = (chunks + want - 1) / want * kT;
+  *seg_steps = steps;
+  *nsegb = static_cast<int>((L + steps - 1) / steps);
+  int ns;
+  int64_t len;
+  plan_cplx_segments(B, D, L, N, 0, &ns, &len);
+  len = (len + steps - 1) / steps * steps;
+  *seg_len = len;
+  *nseg = static_cast<int>((L + len - 1) / len);
+  const int64_t kc = kT / npl_of(N);
+  *n_ck = (L + kc - 1) / kc;
+}
+
+size_t cplx_bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int nsegb) {
+  const int64_t groups = (D + kCPW - 1) / kCPW;
+  return static_cast<size_t>(2 * groups * B * L * N * 2 + B * nsegb * D * N * 2 + 2 * B * nsegb * D);
+}
+
+int64_t cplx_bwd_grid_blocks(int64_t B, int64_t D, int nsegb) { return B * ((D + kCPW - 1) / kCPW) * nsegb; }
+
+hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream_t stream) {
+  hipError_t e = launch_scan_cplx(sp, stream, true);  // piece aggregates (nothing when not split)
+  if (e != hipSuccess) return e;
+  const int64_t groups = (bp.D + kCPW - 1) / kCPW;
+  CplxBwdArgs a{};
+  a.B = bp.B;
+  a.D = bp.D;
+  a.L = bp.L;
+  a.N = bp.N;
+  a.n_dgroups = static_cast<int>(groups);
+  a.grad_bf16 = bp.grad_bf16;
+  a.nseg = sp.nseg;
+  a.seg_len = sp.seg_len;
+  if (sp.nseg > 1) {
+    const size_t half = cplx_workspace_bytes(sp.B, sp.D, sp.N, sp.nseg) / 2 / sizeof(float);
+    a.ws_P = sp.ws;
+    a.ws_H = sp.ws + half;
+  }
+  a.nsegb = bp.nsegb;
+  a.seg_steps = bp.seg_steps;
+  a.n_ck = bp.n_ck;
+  a.u = bp.u;
+  a.dt = bp.dt;
+  a.z = bp.z;
+  a.Bm = bp.Bm;
+  a.Cm = bp.Cm;
+  a.dout = bp.dout;
+  a.dt_bias = bp.dt_bias;
+  a.A = bp.A;
+  a.Dskip = bp.Dskip;
+  a.h0 = sp.h0;
+  a.dh_last = bp.dh_last;
+  a.reset = bp.reset;
+  a.ckpt = sp.ckpt;
+  a.seg_P = sp.seg_P;
+  a.seg_G = sp.seg_G;
+  a.du = bp.du;
+  a.ddt = bp.ddt;
+  a.dz = bp.dz;
+  a.dh0 = bp.dh0;
+  const int64_t bln2 = bp.B * bp.L * bp.N * 2;
+  a.partB = bp.part;
+  a.partC = bp.part + groups * bln2;
+  a.partA = bp.part + 2 * groups * bln2;
+  a.partD = a.partA + bp.B * bp.nsegb * bp.D * bp.N * 2;
+  a.partBias = a.partD + bp.B * bp.nsegb * bp.D;
+  const dim3 grid_ck(static_cast<unsigned>(cplx_scan_grid_blocks(bp.B, bp.D, sp.nseg)));
+  const dim3 grid_bwd(static_cast<unsigned>(cplx_bwd_grid_blocks(bp.B, bp.D, bp.nsegb)));
+  e = with_npl(bp.N, [&](auto npl) {
+    constexpr int NPL = decltype(npl)::value;
+    auto run = [&](auto in_t, auto has_reset) {
+      using InT = decltype(in_t);
+      constexpr bool R = decltype(has_reset)::value;
+      hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R>), grid_ck, dim3(kThreads), 0, stream, a);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((cplx_bwd_kernel<NPL, InT, R>), grid_bwd, dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    };
+    if (bp.in_bf16) return bp.reset ? run(bf16_t{}, std::true_type{}) : run(bf16_t{}, std::false_type{});
+    return bp.reset ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
+  });
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, bp.dB, bp.dC, bp.dA, bp.dD, bp.dbias,
+                           bln2, bp.D * bp.N * 2, bp.D, groups, bp.B * bp.nsegb, stream);
+}
+
+}  // namespace ssm

@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10300
+    assert lib.ssm_version() == 10400
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -212,11 +212,14 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
         bd.load_library()
 
 
-def bwd_params(**kw):
-    """Valid-looking backward parameters over fake, disjoint, aligned addresses."""
+def bwd_params(cplx=False, **kw):
+    """Valid-looking backward parameters over fake, disjoint, aligned addresses
+    (complex-state extents with cplx=True)."""
     p = bd.BwdParams()
     p.batch, p.dim, p.seqlen, p.dstate = B, D, L, N
     p.in_dtype, p.grad_dtype = bd.SSM_BF16, bd.SSM_F32
+    c = 2 if cplx else 1
+    p.state_kind = bd.SSM_STATE_COMPLEX if cplx else bd.SSM_STATE_REAL
     addr = [BASE]
 
     def take(nbytes):
@@ -225,11 +228,11 @@ def bwd_params(**kw):
         return a
 
     p.u, p.dt_raw, p.z, p.dout = (take(B * D * L * 2) for _ in range(4))
-    p.Bm, p.Cm = take(B * L * N * 2), take(B * L * N * 2)
-    p.A, p.dt_bias, p.Dskip = take(D * N * 4), take(D * 4), take(D * 4)
+    p.Bm, p.Cm = take(c * B * L * N * 2), take(c * B * L * N * 2)
+    p.A, p.dt_bias, p.Dskip = take(c * D * N * 4), take(D * 4), take(D * 4)
     p.du, p.d_dt_raw, p.dz = (take(B * D * L * 4) for _ in range(3))
-    p.dA, p.dBm, p.dCm = take(D * N * 4), take(B * L * N * 4), take(B * L * N * 4)
-    p.dDskip, p.d_dt_bias, p.dh0 = take(D * 4), take(D * 4), take(B * D * N * 4)
+    p.dA, p.dBm, p.dCm = take(c * D * N * 4), take(c * B * L * N * 4), take(c * B * L * N * 4)
+    p.dDskip, p.d_dt_bias, p.dh0 = take(D * 4), take(D * 4), take(c * B * D * N * 4)
     n = ctypes.c_size_t(0)
     assert bd.load_library().ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     p.workspace, p.workspace_bytes = take(n.value), n.value
@@ -371,9 +374,41 @@ def test_complex_state_unsupported_combinations(lib):
     cplx = bd.SSM_STATE_COMPLEX
     assert scan_status(lib, scan_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=4)) == 5
     assert update_status(lib, update_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=1)) == 5
-    assert bwd_status(lib, bwd_params(state_kind=cplx)) == 5        # no complex backward
+    # the complex backward has no zero-order hold and no conv stage
+    assert bwd_status(lib, bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)) == 5
+    assert bwd_status(lib, bwd_params(cplx=True, conv_w=BASE + 0x70000000, conv_width=4)) == 5
     n = ctypes.c_size_t(0)
-    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(bwd_params(state_kind=cplx)), ctypes.byref(n)) == 5
+    q = bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(q), ctypes.byref(n)) == 5
+
+
+def test_complex_backward_workspace(lib):
+    # 8 x 1536 x 2048, N = 16: complex states every 16 steps (8*128*1536*16 pairs)
+    # and the dB / dC partials of 96 channel groups (2*96*8*2048*16 pairs)
+    n = ctypes.c_size_t(0)
+    p = bwd_params(cplx=True)
+    p.batch, p.dim, p.seqlen = 8, 1536, 2048
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= (8 * 128 * 1536 * 16 + 2 * 96 * 8 * 2048 * 16) * 2 * 4
+    # N = 128: eight states per lane, so a checkpoint every 2 steps
+    p.batch, p.dim, p.seqlen, p.dstate = 2, 2048, 4096, 128
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= 2 * 2048 * 2048 * 128 * 2 * 4
+    q = bwd_params(cplx=True)
+    q.workspace_bytes -= 4
+    assert bwd_status(lib, q) == 6                  # too small: rejected before any launch
+
+
+def test_complex_backward_extents_are_doubled(lib):
+    # du starts inside the imaginary half of A's complex extent, dBm's second
+    # half overlaps dh0: aliases only with (re, im) pairs. Both calls fail
+    # validation before any launch.
+    p = bwd_params(cplx=True, Dskip=None, dt_bias=None)
+    p.du = p.A + D * N * 4
+    assert bwd_status(lib, p) == 7
+    q = bwd_params(cplx=True)
+    q.dh0 = q.dBm + B * L * N * 4
+    assert bwd_status(lib, q) == 7
 
 
 def test_complex_state_workspace(lib):
