@@ -326,6 +326,8 @@ def main():
             "frac": achieved / ALU_PEAK_TOPS,
             "traffic": traffic,
             "launch_ms_mean": launch_s * 1e3,
+            "launch_ms_median": float(np.median(launch_ms)), "launch_ms_p10": percentile(launch_ms, 10),
+            "launch_ms_p90": percentile(launch_ms, 90),
             "algorithmic_bytes": abytes,
             "algorithmic_ops": ops,
             "hbm_gbps_at_launch_time": abytes / launch_s / 1e9,

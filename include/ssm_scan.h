@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10400 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10500 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -104,12 +104,12 @@ typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
  *                       y_t    = Re(sum_n C[b,t,n] h_t[n]) + D[d] u
  *                     (with SSM_DISC_ZOH the input coefficient is the complex
  *                     (exp(delta A) - 1) / A in place of delta), with the same
- *                     gate and resets. It is supported without a conv stage,
- *                     in ssm_scan_fwd (whose workspace then holds complex
+ *                     gate, resets and optional conv stage. It is supported in
+ *                     ssm_scan_fwd (whose workspace then holds complex
  *                     aggregates; ask ssm_scan_workspace_size with state_kind
  *                     set), ssm_state_update and, with SSM_DISC_DELTA_B,
- *                     ssm_scan_bwd; a conv stage with it, and its backward
- *                     with SSM_DISC_ZOH, return SSM_ERR_UNSUPPORTED.
+ *                     ssm_scan_bwd; its backward with SSM_DISC_ZOH returns
+ *                     SSM_ERR_UNSUPPORTED.
  * Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 
@@ -273,7 +273,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *   conv_w, conv_b, conv_state_in, conv_width : the forward's conv arguments
  *   dconv_w (D,K), dconv_b (D), dconv_state_in (B,D,K-1) float32 outputs,
  *                     NULL => not written
- * Complex state (state_kind = SSM_STATE_COMPLEX, SSM_DISC_DELTA_B, no conv):
+ * Complex state (state_kind = SSM_STATE_COMPLEX, SSM_DISC_DELTA_B):
  * A, Bm, Cm, h0, dh_last and dA, dBm, dCm, dh0 gain a trailing (re, im)
  * dimension of 2, as in the forward. The loss's h_last term is
  * sum (Re dh_last Re h_last + Im dh_last Im h_last), and the gradient of a
@@ -323,7 +323,7 @@ typedef struct {
   float* dconv_state_in;
   int32_t conv_width;
   int32_t discretization; /* ssm_discretization */
-  int32_t state_kind;     /* ssm_state_kind (complex: SSM_DISC_DELTA_B, no conv stage) */
+  int32_t state_kind;     /* ssm_state_kind (complex: SSM_DISC_DELTA_B only) */
   int32_t reserved1;      /* set to 0 */
 } ssm_scan_bwd_params;
 

@@ -38,10 +38,8 @@ bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
 bool valid_disc(int32_t t) { return t == SSM_DISC_DELTA_B || t == SSM_DISC_ZOH; }
 bool valid_kind(int32_t k) { return k == SSM_STATE_REAL || k == SSM_STATE_COMPLEX; }
 
-// The complex state is built without a conv stage.
-ssm_status check_kind(int32_t kind, bool conv) {
+ssm_status check_kind(int32_t kind) {
   if (!valid_kind(kind)) return fail(SSM_ERR_UNSUPPORTED, "unknown state_kind %d", kind);
-  if (kind == SSM_STATE_COMPLEX && conv) return fail(SSM_ERR_UNSUPPORTED, "the complex state has no conv stage");
   return SSM_OK;
 }
 size_t dtype_size(int32_t t) { return t == SSM_BF16 ? 2 : 4; }
@@ -132,9 +130,9 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_params* p, ScanSizes* sz) {
   return check_scan_sizes(&f, sz);
 }
 
-// The complex-state backward: no conv stage (as in the forward) and only the delta B form.
+// The complex-state backward is built for the delta B form only.
 ssm_status check_bwd_kind(const ssm_scan_bwd_params* p) {
-  const ssm_status s = check_kind(p->state_kind, p->conv_w != nullptr);
+  const ssm_status s = check_kind(p->state_kind);
   if (s != SSM_OK) return s;
   if (p->state_kind == SSM_STATE_COMPLEX && p->discretization != SSM_DISC_DELTA_B)
     return fail(SSM_ERR_UNSUPPORTED, "the complex-state backward supports only SSM_DISC_DELTA_B");
@@ -167,6 +165,14 @@ ssm_status plan_bwd_cplx(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdL
   lay->off_part = off;
   off += align256(ssm::cplx_bwd_partial_floats(B, D, L, N, lay->nsegb) * 4);
   lay->off_uconv = lay->off_duconv = lay->off_convpart = off;
+  if (p->conv_w) {  // the conv stage's u' and its gradient, and the conv parameter partials
+    lay->off_uconv = off;
+    off += align256(static_cast<size_t>(sz.bdl) * 4);
+    lay->off_duconv = off;
+    off += align256(static_cast<size_t>(sz.bdl) * 4);
+    lay->off_convpart = off;
+    off += align256(ssm::bwd_conv_partial_floats(B, D, L) * 4);
+  }
   lay->total = off;
   return SSM_OK;
 }
@@ -448,7 +454,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
     return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
-  if ((s = check_kind(p->state_kind, p->conv_w != nullptr)) != SSM_OK) return s;
+  if ((s = check_kind(p->state_kind)) != SSM_OK) return s;
   const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
   const int64_t cw = cplx ? 2 : 1;  // scalars per A, B, C and state entry
   const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
@@ -524,16 +530,16 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   plan.nseg = nseg;
   plan.seg_len = seg_len;
   plan.zoh = p->discretization == SSM_DISC_ZOH;
-  if (cplx) {
-    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
-    return ok();
-  }
   plan.conv_w = p->conv_w;
   plan.conv_b = p->conv_b;
   plan.conv_state_in = p->conv_state_in;
   plan.conv_state_out = p->conv_state_out;
   plan.conv_k = static_cast<int>(K);
+  if (cplx) {
+    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -575,7 +581,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
       return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
-  ssm_status s = check_kind(p->state_kind, p->conv_w != nullptr);
+  ssm_status s = check_kind(p->state_kind);
   if (s != SSM_OK) return s;
   const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
   const int64_t ce = cplx ? 2 : 1;  // scalars per A, B, C and state entry

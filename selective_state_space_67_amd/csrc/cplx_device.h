@@ -109,5 +109,46 @@ __device__ __forceinline__ float2 load_cpair(const bf16_t* p, int64_t n) {
   return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
 }
 
+// Conv taps of channel d right-aligned in four slots (widths below 4 have
+// leading zero taps) and its bias.
+__device__ __forceinline__ void conv_taps(const float* conv_w, const float* conv_b, int64_t d, int K, float (&w)[4],
+                                          float& cb) {
+  for (int k = 0; k < 4; ++k) w[k] = 0.0f;
+  for (int k = 0; k < K; ++k) w[4 - K + k] = conv_w[d * K + k];
+  cb = conv_b ? conv_b[d] : 0.0f;
+}
+
+// silu(causal depthwise conv) of a row's input at absolute step P: x_row and
+// rs_row point at the row's step 0; inputs before the sequence come from the
+// row's conv state st_row (K - 1 values, oldest first; zeros without one);
+// inputs hidden by a later reset within the window count as 0.
+template <typename InT, bool HAS_RESET>
+__device__ __forceinline__ float conv_silu_at(const float (&w)[4], float cb, const InT* x_row, const uint8_t* rs_row,
+                                              const float* st_row, int K, int64_t P) {
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t pos = P - 3 + j;
+    x[j] = pos >= 0 ? load_elem(x_row, pos) : (st_row && pos >= 1 - K ? st_row[pos + K - 1] : 0.0f);
+  }
+  const bool r0 = HAS_RESET && rs_row[P] != 0;
+  const bool r1 = HAS_RESET && P >= 1 && rs_row[P - 1] != 0;
+  const bool r2 = HAS_RESET && P >= 2 && rs_row[P - 2] != 0;
+  return silu_f32(conv_pre(w, cb, x[0], x[1], x[2], x[3], r0, r1, r2));
+}
+
+// Entry kk of a row's final conv state: input L - (K - 1) + kk, 0 when a
+// later reset hides it (a reset at that step itself starts a document there).
+template <typename InT, bool HAS_RESET>
+__device__ __forceinline__ float conv_state_at_end(const InT* x_row, const uint8_t* rs_row, const float* st_row, int K,
+                                                   int64_t L, int kk) {
+  const int64_t pos = L - (K - 1) + kk;
+  if (HAS_RESET)
+    for (int64_t q = pos + 1 > 0 ? pos + 1 : 0; q < L; ++q)
+      if (rs_row[q]) return 0.0f;
+  if (pos >= 0) return load_elem(x_row, pos);
+  return st_row ? st_row[pos + K - 1] : 0.0f;
+}
+
 }  // namespace cplx
 }  // namespace ssm

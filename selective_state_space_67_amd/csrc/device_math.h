@@ -1,8 +1,9 @@
 // Device-side helpers shared by the scan and decode kernels (gfx950).
 //
 // Element access for the two input formats (float32 and bfloat16 bit
-// patterns), the float32 step-size and gate functions, and the DPP lane shift
-// the scan's cross-lane accumulation uses.
+// patterns), the float32 step-size and gate functions, the conv window with
+// reset visibility, and the DPP lane shift the scan's cross-lane accumulation
+// uses.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,6 +83,23 @@ __device__ __forceinline__ float zoh_psi(float x, float abar) {
   s = __builtin_fmaf(x, s, 0.5f);
   const float direct = __builtin_fmaf(x, abar, 1.0f - abar) * fast_rcp(x * x);
   return fabsf(x) < 0.5f ? s : direct;
+}
+
+// Visibility of the conv window's inputs: the window of step Q covers
+// Q-3 .. Q (taps 0..3, widths below 4 have leading zero taps); an input is
+// hidden when a reset lies after it within the window (the document started
+// later). r0, r1, r2 are the reset flags of Q, Q-1 and Q-2.
+__device__ __forceinline__ float conv_pre(const float (&w)[4], float bias, float x0, float x1, float x2, float x3,
+                                          bool r0, bool r1, bool r2) {
+  float acc = __builtin_fmaf(w[3], x3, bias);
+  if (!r0) {
+    acc = __builtin_fmaf(w[2], x2, acc);
+    if (!r1) {
+      acc = __builtin_fmaf(w[1], x1, acc);
+      if (!r2) acc = __builtin_fmaf(w[0], x0, acc);
+    }
+  }
+  return acc;
 }
 
 // Value of the lane one below within the same row of 16 lanes (DPP

@@ -161,6 +161,9 @@ int64_t bwd_grid_blocks(int64_t B, int64_t D, int64_t N, int nsegb);
 // Floats of partial sums of the conv backward (per row tile: 4 taps + bias).
 size_t bwd_conv_partial_floats(int64_t B, int64_t D, int64_t L);
 hipError_t launch_scan_bwd(const BwdPlan& plan, hipStream_t stream);
+// The conv stage's backward: du_conv (the gradient of the scan input u') to
+// du, dconv_w, dconv_b and dconv_state (launched by launch_scan_bwd itself).
+hipError_t launch_conv_bwd(const BwdPlan& plan, hipStream_t stream);
 // Sums of the backward's partials in a fixed order: dB and dC (bln floats
 // each) over `groups` channel groups, dA (dn floats), dD and d dt_bias (D
 // floats, null: skipped) over `bs` batch-row segments.

@@ -900,7 +900,10 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   e = launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, pl.dB, pl.dC, pl.dA, pl.dD, pl.dbias, bln,
                         pl.D * pl.N, pl.D, groups, pl.B * pl.nsegb, stream);
   if (e != hipSuccess || !pl.conv_w) return e;
+  return launch_conv_bwd(pl, stream);
+}
 
+hipError_t launch_conv_bwd(const BwdPlan& pl, hipStream_t stream) {
   ConvBwdArgs c{};
   c.B = pl.B;
   c.D = pl.D;
@@ -922,7 +925,7 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
     hipLaunchKernelGGL(conv_bwd_kernel<bf16_t>, cgrid, dim3(256), 0, stream, c);
   else
     hipLaunchKernelGGL(conv_bwd_kernel<float>, cgrid, dim3(256), 0, stream, c);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(conv_param_reduce_kernel, dim3(static_cast<unsigned>((pl.D * 5 + 255) / 256)), dim3(256), 0,
                      stream, pl.B, pl.D, pl.conv_k, c.ntiles, static_cast<const float*>(pl.conv_part), pl.dconv_w,

@@ -70,6 +70,12 @@ struct CplxArgs {
   int nseg;
   float* ws_P;  // (nseg - 1, B, D, N, 2): the decay product of pieces 0 .. nseg-2
   float* ws_H;  // (nseg - 1, B, D, N, 2): their end states from a zero start
+  // causal conv1d + SiLU on u (CONV kernels only)
+  const float* conv_w;         // (D, conv_k)
+  const float* conv_b;         // (D) or null
+  const float* conv_state_in;  // (B, D, conv_k - 1) or null
+  float* conv_state_out;       // (B, D, conv_k - 1) or null
+  int conv_k;
 };
 
 // One step of a state: h = exp(delta A) h + q u B with the input coefficient
@@ -110,7 +116,7 @@ __device__ __forceinline__ float cplx_step(float dl, float dv, const CState& q, 
 // affine aggregate, the decay product P = exp(A sum delta) (0 after a reset)
 // and the end state H; the full launch folds the aggregates of the preceding
 // pieces into its starting state, h <- P h + H, and runs its piece.
-template <int NPL, typename InT, bool HAS_RESET, bool AGG, bool ZOH>
+template <int NPL, typename InT, bool HAS_RESET, bool AGG, bool ZOH, bool CONV>
 __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   constexpr int NPAD = 16 * NPL;
   const int g = blockIdx.x % a.n_dgroups;
@@ -167,6 +173,12 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   bool cleared = false;
   const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
   const float dsk = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
+  // conv stage: taps, and the row's input, resets and initial conv state from step 0
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f;
+  if (CONV && dvalid) conv_taps(a.conv_w, a.conv_b, d, a.conv_k, cw, cb);
+  const InT* __restrict__ u_row = u - t_seg;
+  const uint8_t* __restrict__ rs_row = HAS_RESET ? rs - t_seg : nullptr;
+  const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     const int steps = min(kT, Lseg - t0);
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
     const bool live = dvalid && k < steps;
     float dl = 0.0f, uu = 0.0f, gate = 1.0f;
     if (live) {
-      uu = load_elem(u, t);
+      uu = CONV ? conv_silu_at<InT, HAS_RESET>(cw, cb, u_row, rs_row, cst, a.conv_k, t_seg + t) : load_elem(u, t);
       dl = softplus_f32(load_elem(dt, t) + bias);
       if (!AGG && z) gate = silu_f32(load_elem(z, t));
       if constexpr (AGG) {
@@ -200,7 +212,8 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
     __syncthreads();
 
     float ymine = 0.0f;
-#pragma unroll 4
+    // (one step at a time for 16 states per lane: their registers leave no room to unroll)
+#pragma unroll (NPL >= 16 ? 1 : 4)
     for (int tl = 0; tl < kT; ++tl) {
       const float2 du = s_du[c * kT + tl];
       float dlt = du.x;
@@ -255,6 +268,16 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
     }
     return;
   }
+  if (CONV && a.conv_state_out && sp == a.nseg - 1 && tid < kCPW * 3) {  // final conv state
+    const int cc = tid / 3, kk = tid % 3;
+    const int64_t dd = static_cast<int64_t>(g) * kCPW + cc;
+    if (dd < a.D && kk < a.conv_k - 1) {
+      const int64_t rr = static_cast<int64_t>(b) * a.D + dd;
+      a.conv_state_out[rr * (a.conv_k - 1) + kk] = conv_state_at_end<InT, HAS_RESET>(
+          static_cast<const InT*>(a.u) + rr * a.L, HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L : nullptr,
+          a.conv_state_in ? a.conv_state_in + rr * (a.conv_k - 1) : nullptr, a.conv_k, a.L, kk);
+    }
+  }
   if (a.h_last && dvalid && sp == a.nseg - 1) {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
@@ -279,6 +302,10 @@ struct CplxUpdateArgs {
   const void* Bm;  // (B, N, 2)
   const void* Cm;
   void* out;
+  float* conv_state;    // (B, D, conv_k - 1), updated in place; null without a conv stage
+  const float* conv_w;  // (D, conv_k)
+  const float* conv_b;  // (D) or null
+  int conv_k;
 };
 
 // Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup. Lane
@@ -297,18 +324,35 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
   const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + b * N * 2;
   const float* __restrict__ Ad = a.A + d * N * 2;
   float* __restrict__ h = a.h + row * N * 2;
+  // States past N read state N - 1 (always in bounds) and are zeroed after
+  // the load, so every load is an unconditional global load.
   float2 hv[NPL], av[NPL], bv[NPL], cv[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = k + 16 * j;
     const bool ok = n < N;
-    const float2 zero = make_float2(0.0f, 0.0f);
-    hv[j] = ok ? *reinterpret_cast<const float2*>(h + 2 * n) : zero;
-    av[j] = ok ? *reinterpret_cast<const float2*>(Ad + 2 * n) : zero;
-    bv[j] = ok ? load_cpair(Bb, n) : zero;
-    cv[j] = ok ? load_cpair(Cb, n) : zero;
+    const int nc = ok ? n : N - 1;
+    hv[j] = *reinterpret_cast<const float2*>(h + 2 * nc);
+    av[j] = *reinterpret_cast<const float2*>(Ad + 2 * nc);
+    bv[j] = load_cpair(Bb, nc);
+    cv[j] = load_cpair(Cb, nc);
+    if (!ok) {
+      hv[j] = make_float2(0.0f, 0.0f);
+      av[j] = hv[j];
+      bv[j] = hv[j];
+      cv[j] = hv[j];
+    }
   }
-  const float uu = load_elem(static_cast<const InT*>(a.u), row);
+  const float x = load_elem(static_cast<const InT*>(a.u), row);
+  float uu = x;
+  float* cst = nullptr;
+  if (a.conv_w) {  // u' = silu(conv over the row's conv state and this input)
+    const int K = a.conv_k;
+    cst = a.conv_state + row * (K - 1);
+    float pre = __builtin_fmaf(a.conv_w[d * K + K - 1], x, a.conv_b ? a.conv_b[d] : 0.0f);
+    for (int q = 0; q < K - 1; ++q) pre = __builtin_fmaf(a.conv_w[d * K + q], cst[q], pre);
+    uu = silu_f32(pre);
+  }
   const float dl = softplus_f32(load_elem(static_cast<const InT*>(a.dt), row) + (a.dt_bias ? a.dt_bias[d] : 0.0f));
   const float dv = ZOH ? uu : dl * uu;
   float p = 0.0f;
@@ -321,6 +365,10 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
   }
   p = row_sum16(p);
   if (k == 0) {
+    if (cst) {  // shift the conv state by this input (the row's lanes have all read it)
+      for (int q = 0; q + 1 < a.conv_k - 1; ++q) cst[q] = cst[q + 1];
+      if (a.conv_k > 1) cst[a.conv_k - 2] = x;
+    }
     float v = p + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
     if (a.z) v *= silu_f32(load_elem(static_cast<const InT*>(a.z), row));
     if (a.out_bf16)
@@ -402,24 +450,32 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregat
     a.ws_P = p.ws;
     a.ws_H = p.ws + half;
   }
+  a.conv_w = p.conv_w;
+  a.conv_b = p.conv_b;
+  a.conv_state_in = p.conv_state_in;
+  a.conv_state_out = p.conv_state_out;
+  a.conv_k = p.conv_k;
   const dim3 grid(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg)));
   const dim3 grid_agg(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg - 1)));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
-    auto run = [&](auto in_t, auto has_reset, auto zoh) {
+    auto run = [&](auto in_t, auto has_reset, auto zoh, auto conv) {
       using InT = decltype(in_t);
-      constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
+      constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value, C = decltype(conv)::value;
       if (p.nseg > 1) {  // the last piece's aggregate is never needed
-        hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z>), grid_agg, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z, C>), grid_agg, dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || aggregates_only) return e;
       }
       if (aggregates_only) return hipSuccess;
-      hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z, C>), grid, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };
+    auto with_conv = [&](auto in_t, auto has_reset, auto zoh) {
+      return p.conv_w ? run(in_t, has_reset, zoh, std::true_type{}) : run(in_t, has_reset, zoh, std::false_type{});
+    };
     auto with_zoh = [&](auto in_t, auto has_reset) {
-      return p.zoh ? run(in_t, has_reset, std::true_type{}) : run(in_t, has_reset, std::false_type{});
+      return p.zoh ? with_conv(in_t, has_reset, std::true_type{}) : with_conv(in_t, has_reset, std::false_type{});
     };
     if (p.in_bf16)
       return p.reset ? with_zoh(bf16_t{}, std::true_type{}) : with_zoh(bf16_t{}, std::false_type{});
@@ -443,6 +499,10 @@ hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
   a.Bm = p.Bm;
   a.Cm = p.Cm;
   a.out = p.out;
+  a.conv_state = p.conv_state;
+  a.conv_w = p.conv_w;
+  a.conv_b = p.conv_b;
+  a.conv_k = p.conv_k;
   const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;

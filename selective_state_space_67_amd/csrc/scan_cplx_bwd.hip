@@ -40,6 +40,10 @@
 // 3. Reduction (shared with the real backward): dB and dC over channel
 //    groups, dA, dD and d dt_bias over batch rows and segments, in a fixed
 //    order, so repeated calls give identical bits.
+// With the conv input stage, u is the conv input and the scan's input is
+// u' = silu(conv(u)): the checkpoint sweep writes u' for the reverse sweep,
+// which writes the gradient of u', and the real backward's conv backward
+// turns that into du and the conv parameters' gradients.
 #include <algorithm>
 
 #include "cplx_device.h"
@@ -91,17 +95,27 @@ struct CplxBwdArgs {
   float* partA;     // (B, nsegb, D, N, 2)
   float* partD;     // (B, nsegb, D)
   float* partBias;  // (B, nsegb, D)
+  // conv stage: the checkpoint sweep writes the scan input u' = silu(conv(u))
+  // to uconv, the reverse sweep reads it there and writes its gradient to
+  // du_conv (both (B, D, L) float32); null without a conv stage
+  const float* conv_w;         // (D, conv_k)
+  const float* conv_b;         // (D) or null
+  const float* conv_state_in;  // (B, D, conv_k - 1) or null
+  int conv_k;
+  float* uconv;
+  float* du_conv;
 };
 
-// Stages step t0 + k of this lane's channel: loads u, dt_raw, z and dout and
-// forms delta (negated on a reset step), delta u and dy = dout silu(z).
+// Stages step t of this lane's channel: takes the scan input u_t, loads
+// dt_raw, z and dout and forms delta (negated on a reset step), delta u and
+// dy = dout silu(z).
 template <typename InT, bool HAS_RESET>
 struct StepInputs {
   float dl = 0.0f, uu = 0.0f, sgx = 0.0f, go = 0.0f, zz = 0.0f, dy = 0.0f;
   bool reset = false;
-  __device__ __forceinline__ void load(const InT* u, const InT* dt, const InT* z, const InT* dout,
-                                       const uint8_t* rs, int t, float bias) {
-    uu = load_elem(u, t);
+  __device__ __forceinline__ void load(float u_t, const InT* dt, const InT* z, const InT* dout, const uint8_t* rs,
+                                       int t, float bias) {
+    uu = u_t;
     const float x = load_elem(dt, t) + bias;
     dl = softplus_f32(x);
     sgx = fast_rcp(1.0f + fast_exp2(-x * kLog2e));  // d softplus / dx
@@ -131,7 +145,7 @@ __device__ __forceinline__ void stage_bc(float4* s_bc, const InT* Bb, const InT*
   }
 }
 
-template <int NPL, typename InT, bool HAS_RESET>
+template <int NPL, typename InT, bool HAS_RESET, bool CONV>
 __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a) {
   constexpr int NPAD = 16 * NPL;
   constexpr int KC = 16 / NPL;
@@ -188,13 +202,26 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
   const InT* __restrict__ Cb = static_cast<const InT*>(a.Cm) + (static_cast<int64_t>(b) * a.L + t_seg) * N * 2;
   const uint8_t* __restrict__ rs = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L + t_seg : nullptr;
   const float bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f;
+  if (CONV && dvalid) conv_taps(a.conv_w, a.conv_b, d, a.conv_k, cw, cb);
+  const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     const int steps = min(kT, Lseg - t0);
     __syncthreads();  // the previous chunk's readers are done
     stage_bc<NPAD>(s_bc, Bb + static_cast<int64_t>(t0) * N * 2, Cb + static_cast<int64_t>(t0) * N * 2, steps, N, tid);
     StepInputs<InT, HAS_RESET> in;
-    if (dvalid && k < steps) in.load(u, dt, z, go, rs, t0 + k, bias);
+    if (dvalid && k < steps) {
+      float ut;
+      if constexpr (CONV) {  // the scan input u' = silu(conv(u)), kept for the reverse sweep
+        ut = conv_silu_at<InT, HAS_RESET>(cw, cb, u - t_seg, HAS_RESET ? rs - t_seg : nullptr, cst, a.conv_k,
+                                          t_seg + t0 + k);
+        a.uconv[row * a.L + t_seg + t0 + k] = ut;
+      } else {
+        ut = load_elem(u, t0 + k);
+      }
+      in.load(ut, dt, z, go, rs, t0 + k, bias);
+    }
     s_st[c * kT + k] = in.staged();
     __syncthreads();
 
@@ -332,7 +359,10 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
     stage_bc<NPAD>(s_bc, Bb + t0 * N * 2, Cb + t0 * N * 2, steps, N, tid);
     StepInputs<InT, HAS_RESET> in;
     const bool live = dvalid && k < steps;
-    if (live) in.load(u, dt, z, go, rs, static_cast<int>(t0) + k, bias);
+    if (live) {
+      const int t = static_cast<int>(t0) + k;
+      in.load(a.uconv ? a.uconv[row * a.L + t] : load_elem(u, t), dt, z, go, rs, t, bias);
+    }
     s_st[c * kT + k] = in.staged();
     __syncthreads();
 
@@ -440,13 +470,16 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
       const float du = __builtin_fmaf(in.dl, m1, dsk * in.dy);
       const float ddt = __builtin_fmaf(in.uu, m1, m2) * in.sgx;
       const int64_t o = row * a.L + t0 + k;
-      if (a.grad_bf16) {
+      if (a.du_conv)  // the gradient of u', which the conv backward turns into du
+        a.du_conv[o] = du;
+      else if (a.grad_bf16)
         store_elem(static_cast<bf16_t*>(a.du), o, du);
-        store_elem(static_cast<bf16_t*>(a.ddt), o, ddt);
-      } else {
+      else
         store_elem(static_cast<float*>(a.du), o, du);
+      if (a.grad_bf16)
+        store_elem(static_cast<bf16_t*>(a.ddt), o, ddt);
+      else
         store_elem(static_cast<float*>(a.ddt), o, ddt);
-      }
       if (z) {
         const float y = __builtin_fmaf(dsk, in.uu, m3);
         const float sz = fast_rcp(1.0f + fast_exp2(-in.zz * kLog2e));
@@ -564,6 +597,14 @@ hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream
   a.partA = bp.part + 2 * groups * bln2;
   a.partD = a.partA + bp.B * bp.nsegb * bp.D * bp.N * 2;
   a.partBias = a.partD + bp.B * bp.nsegb * bp.D;
+  if (bp.conv_w) {
+    a.conv_w = bp.conv_w;
+    a.conv_b = bp.conv_b;
+    a.conv_state_in = bp.conv_state_in;
+    a.conv_k = bp.conv_k;
+    a.uconv = sp.uconv_out;
+    a.du_conv = bp.du_conv;
+  }
   const dim3 grid_ck(static_cast<unsigned>(cplx_scan_grid_blocks(bp.B, bp.D, sp.nseg)));
   const dim3 grid_bwd(static_cast<unsigned>(cplx_bwd_grid_blocks(bp.B, bp.D, bp.nsegb)));
   e = with_npl(bp.N, [&](auto npl) {
@@ -571,7 +612,10 @@ hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream
     auto run = [&](auto in_t, auto has_reset) {
       using InT = decltype(in_t);
       constexpr bool R = decltype(has_reset)::value;
-      hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R>), grid_ck, dim3(kThreads), 0, stream, a);
+      if (bp.conv_w)
+        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, true>), grid_ck, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, false>), grid_ck, dim3(kThreads), 0, stream, a);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL((cplx_bwd_kernel<NPL, InT, R>), grid_bwd, dim3(kThreads), 0, stream, a);
@@ -581,8 +625,10 @@ hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream
     return bp.reset ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
   });
   if (e != hipSuccess) return e;
-  return launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, bp.dB, bp.dC, bp.dA, bp.dD, bp.dbias,
-                           bln2, bp.D * bp.N * 2, bp.D, groups, bp.B * bp.nsegb, stream);
+  e = launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, bp.dB, bp.dC, bp.dA, bp.dD, bp.dbias, bln2,
+                        bp.D * bp.N * 2, bp.D, groups, bp.B * bp.nsegb, stream);
+  if (e != hipSuccess || !bp.conv_w) return e;
+  return launch_conv_bwd(bp, stream);
 }
 
 }  // namespace ssm

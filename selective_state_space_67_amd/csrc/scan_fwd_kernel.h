@@ -131,23 +131,6 @@ struct ScanArgs {
   int zoh;                     // exact zero-order hold input coefficient (ZOH kernels)
 };
 
-// Visibility of the conv window's inputs: the window of step Q covers
-// Q-3 .. Q (taps 0..3, widths below 4 have leading zero taps); an input is
-// hidden when a reset lies after it within the window (the document started
-// later). r0, r1, r2 are the reset flags of Q, Q-1 and Q-2.
-__device__ __forceinline__ float conv_pre(const float (&w)[4], float bias, float x0, float x1, float x2, float x3,
-                                          bool r0, bool r1, bool r2) {
-  float acc = __builtin_fmaf(w[3], x3, bias);
-  if (!r0) {
-    acc = __builtin_fmaf(w[2], x2, acc);
-    if (!r1) {
-      acc = __builtin_fmaf(w[1], x1, acc);
-      if (!r2) acc = __builtin_fmaf(w[0], x0, acc);
-    }
-  }
-  return acc;
-}
-
 // The checkpoint sweep keeps more per-state values live (the segment's decay
 // product and adjoint sum), so with several states per lane it gets the
 // register budget of two waves per SIMD.

@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10400
+    assert lib.ssm_version() == 10500
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -371,15 +371,28 @@ def test_unknown_state_kind(lib):
 
 
 def test_complex_state_unsupported_combinations(lib):
-    cplx = bd.SSM_STATE_COMPLEX
-    assert scan_status(lib, scan_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=4)) == 5
-    assert update_status(lib, update_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=1)) == 5
-    # the complex backward has no zero-order hold and no conv stage
+    # the complex backward has no zero-order hold
     assert bwd_status(lib, bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)) == 5
-    assert bwd_status(lib, bwd_params(cplx=True, conv_w=BASE + 0x70000000, conv_width=4)) == 5
     n = ctypes.c_size_t(0)
     q = bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(q), ctypes.byref(n)) == 5
+
+
+def test_complex_state_conv_arguments_checked(lib):
+    # the conv stage with the complex state goes through the same checks
+    # (each call fails validation before any launch)
+    cplx = bd.SSM_STATE_COMPLEX
+    assert scan_status(lib, scan_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=5)) == 2
+    assert scan_status(lib, scan_params(state_kind=cplx, conv_w=BASE + 0x70000000 + 2, conv_width=4)) == 4
+    assert update_status(lib, update_params(state_kind=cplx, conv_w=BASE + 0x70000000, conv_width=0)) == 2
+    assert bwd_status(lib, bwd_params(cplx=True, conv_w=BASE + 0x70000000, conv_width=5)) == 2
+    # the complex backward's workspace grows by u', its gradient and the conv partials
+    n0, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p = bwd_params(cplx=True)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n0)) == 0
+    p.conv_w, p.conv_width = BASE + 0x70000000, 4
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
+    assert n1.value >= n0.value + 2 * B * D * L * 4
 
 
 def test_complex_backward_workspace(lib):

@@ -209,3 +209,54 @@ def test_workload_full_size(index):
     x["h0"] = None
     x["dh_last"] = None
     assert_grads(gpu_bwd(x), reference(x), what=cfg["name"])
+
+
+# ---- conv1d + SiLU input stage: u is the conv input, the scan reads u' = silu(conv(u)) ----
+
+def conv_reference(x, w, cb, st):
+    """The oracle's complex backward at u' (with its phase term), carried
+    through the oracle's conv backward to the conv input and parameters."""
+    uc, pre = oracle.conv_silu(wl.widen(x["u"]), w, bias=cb, reset=x["reset"], state_in=st, want_pre=True)
+    xs = dict(x)
+    xs["u"] = uc
+    ref, phase = reference(xs)
+    du_p = ref["du"] + phase["du"]  # the phase term carried through the (linear) conv backward
+    cref = oracle.conv_silu_bwd(wl.widen(x["u"]), w, ref["du"], pre, reset=x["reset"], state_in=st)
+    cper = oracle.conv_silu_bwd(wl.widen(x["u"]), w, du_p, pre, reset=x["reset"], state_in=st)
+    ref = dict(ref)
+    phase = dict(phase)
+    for k, ck in (("du", "dx"), ("dconv_w", "dw"), ("dconv_b", "dbias"), ("dconv_state", "dstate_in")):
+        ref[k] = cref[ck]
+        phase[k] = np.abs(cper[ck] - cref[ck])
+    return ref, phase
+
+
+@pytest.mark.parametrize("K,N,packed", [(4, 16, True), (3, 64, False), (1, 16, True), (2, 128, True)])
+def test_conv_backward(K, N, packed):
+    import torch
+
+    from selective_state_space_67_amd import ssm_scan_bwd
+
+    x = make_case(2, 24, 333, N, wl.BF16, 40 + K + N, packed=packed, h0=True, dh_last=True)
+    rng = np.random.default_rng(90 + K)
+    w = (rng.standard_normal((24, K)) * 0.5).astype(np.float32)
+    cb = (rng.standard_normal(24) * 0.2).astype(np.float32)
+    st = rng.standard_normal((2, 24, K - 1)).astype(np.float32) if K > 1 else None
+    dev = device()
+    t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset", "dout")}
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    g = ssm_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], t["dout"], dt_bias=t["dt_bias"],
+                     Dskip=t["Dskip"], z=t["z"], reset=t["reset"], h0=f32(x["h0"]), dh_last=f32(x["dh_last"]),
+                     conv_w=f32(w), conv_b=f32(cb), conv_state_in=f32(st), complex_state=True)
+    torch.cuda.synchronize()
+    got = {k: (None if g[GPU_KEY[k]] is None else g[GPU_KEY[k]].float().cpu().numpy().astype(np.float64))
+           for k in KEYS}
+    ref, phase = conv_reference(x, w, cb, st)
+    assert_grads(got, (ref, phase), what="conv K%d N%d" % (K, N))
+    for gk, rk in (("dconv_w", "dconv_w"), ("dconv_b", "dconv_b"), ("dconv_state_in", "dconv_state")):
+        if g.get(gk) is None:
+            assert K == 1 and gk == "dconv_state_in", gk
+            continue
+        o, r = g[gk].cpu().numpy().astype(np.float64), ref[rk]
+        bound = TOL * (np.sqrt(np.mean(r * r)) + np.abs(r)) + phase[rk] + 1e-30
+        assert np.all(np.abs(o - r) <= bound), (gk, float(np.max(np.abs(o - r) / bound)))

@@ -353,3 +353,122 @@ def test_complex_scan_zoh_at_layer_size_sampled_channels():
                    Dskip=x["Dskip"][ds], reset=None, dtype=x["dtype"])
         ref, rhl = ref_scan(sub, zoh=True)
         check(sub, got[b:b + 1, ds], hl[b:b + 1, ds], ref, rhl, "zoh layer b=%d" % b, zoh=True)
+
+
+# ---- conv1d + SiLU input stage with the complex state ----
+
+def conv_params(D, B, K, seed, with_bias=True, with_state=True):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((D, K)) * 0.5).astype(np.float32)
+    cb = (rng.standard_normal(D) * 0.2).astype(np.float32) if with_bias else None
+    st = rng.standard_normal((B, D, K - 1)).astype(np.float32) if with_state and K > 1 else None
+    return w, cb, st
+
+
+def run_conv_scan(x, w, cb, st, h0=None, num_segments=0, zoh=False):
+    import torch
+
+    from selective_state_space_67_amd import ssm_scan_fwd
+
+    dev = device()
+    t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    Bt, D, L = x["u"].shape
+    N, K = x["A"].shape[1], w.shape[1]
+    hl = torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev)
+    cs = torch.full((Bt, D, K - 1), float("nan"), device=dev)
+    out = ssm_scan_fwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"], Dskip=t["Dskip"],
+                       z=t["z"], reset=t["reset"], h0=f32(h0), h_last=hl, complex_state=True, zoh=zoh,
+                       num_segments=num_segments, conv_w=f32(w), conv_b=f32(cb), conv_state_in=f32(st),
+                       conv_state_out=cs if K > 1 else None)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy().astype(np.float64), hl.cpu().numpy().astype(np.float64),
+            cs.cpu().numpy().astype(np.float64))
+
+
+def ref_conv_scan(x, w, cb, st, h0=None, zoh=False):
+    """The oracle's conv stage composed with its complex scan; returns
+    (out, h_last, final conv state, inputs with u replaced by the scan input)."""
+    uc, st_out = oracle.conv_silu(wl.widen(x["u"]), w, bias=cb, reset=x["reset"], state_in=st, want_state=True)
+    xs = dict(x)
+    xs["u"] = uc
+    ref, rhl = ref_scan(xs, h0=h0, zoh=zoh)
+    return ref, rhl, st_out, xs
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_complex_conv_widths(dtype, K):
+    x = wl.make_cplx_inputs(2, 24, 300, 16, dtype, seed=500 + K, packed=True, dt_lo=1e-3, dt_hi=3e-1)
+    x["reset"] = wl.doc_resets(np.random.default_rng(K), 2, 300, lo=20, hi=90)
+    x["reset"][0, 0] = 1                 # row 0 discards its initial conv state
+    w, cb, st = conv_params(24, 2, K, 50 + K)
+    h0 = np.random.default_rng(K).standard_normal((2, 24, 16, 2)).astype(np.float32)
+    got, hl, cs = run_conv_scan(x, w, cb, st, h0=h0)
+    ref, rhl, rcs, xs = ref_conv_scan(x, w, cb, st, h0=h0)
+    check(xs, got, hl, ref, rhl, "conv K=%d %s" % (K, dtype), h0=h0)
+    if K > 1:
+        np.testing.assert_array_equal(cs, rcs)
+
+
+@pytest.mark.parametrize("N", [1, 64, 128])
+def test_complex_conv_state_sizes(N):
+    x = wl.make_cplx_inputs(2, 19, 150, N, wl.BF16, seed=520 + N, packed=True)
+    x["reset"][1, :] = 0
+    x["reset"][1, 149] = 1               # a reset at the very last step hides the final conv state
+    w, cb, st = conv_params(19, 2, 4, 60 + N, with_bias=N != 64, with_state=N != 1)
+    got, hl, cs = run_conv_scan(x, w, cb, st)
+    ref, rhl, rcs, xs = ref_conv_scan(x, w, cb, st)
+    check(xs, got, hl, ref, rhl, "conv N=%d" % N)
+    np.testing.assert_array_equal(cs, rcs)
+
+
+@pytest.mark.parametrize("nseg,zoh", [(3, False), (5, True)])
+def test_complex_conv_split_into_pieces(nseg, zoh):
+    # pieces start mid-sequence: their conv windows read the previous piece's inputs
+    x = wl.make_cplx_inputs(2, 20, 1000, 16, wl.F32, seed=540 + nseg, packed=True, dt_lo=1e-3, dt_hi=3e-1)
+    x["reset"] = wl.doc_resets(np.random.default_rng(nseg), 2, 1000, lo=100, hi=600)
+    w, cb, st = conv_params(20, 2, 4, 70 + nseg)
+    got, hl, cs = run_conv_scan(x, w, cb, st, num_segments=nseg, zoh=zoh)
+    ref, rhl, rcs, xs = ref_conv_scan(x, w, cb, st, zoh=zoh)
+    check(xs, got, hl, ref, rhl, "conv pieces=%d zoh=%s" % (nseg, zoh), zoh=zoh)
+    np.testing.assert_array_equal(cs, rcs)
+
+
+@pytest.mark.parametrize("N,K,zoh", [(128, 4, False), (16, 3, True), (33, 1, False)])
+def test_complex_decode_with_conv_state(N, K, zoh):
+    """Decode steps with a conv state against the oracle, step by step."""
+    import torch
+
+    from selective_state_space_67_amd import ssm_state_update
+
+    dev = device()
+    Bt, D, steps = 3, 24, 5
+    rng = np.random.default_rng(N + K)
+    y = wl.make_cplx_decode_inputs(Bt, D, N, wl.BF16, seed=N + K)
+    w, cb, st = conv_params(D, Bt, K, 80 + N + K)
+    h = torch.from_numpy(y["h"]).to(dev)
+    st_t = torch.from_numpy(st).to(dev) if K > 1 else None
+    h_ref, st_ref = y["h"].copy(), st
+    t = {k: to_dev(y[k], dev) for k in ("dt_bias", "A", "Dskip")}
+    for s in range(steps):
+        ys = dict(y)
+        for k, shape in (("u", (Bt, D)), ("dt_raw", (Bt, D)), ("z", (Bt, D)), ("Bm", (Bt, N, 2)),
+                         ("Cm", (Bt, N, 2))):
+            ys[k] = wl.store(rng.standard_normal(shape), wl.BF16)
+        tt = {k: to_dev(ys[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm")}
+        o = ssm_state_update(h, tt["u"], tt["dt_raw"], t["A"], tt["Bm"], tt["Cm"], dt_bias=t["dt_bias"],
+                             Dskip=t["Dskip"], z=tt["z"], complex_state=True, zoh=zoh,
+                             conv_w=torch.from_numpy(w).to(dev), conv_b=torch.from_numpy(cb).to(dev),
+                             conv_state=st_t)
+        torch.cuda.synchronize()
+        # the oracle: u' from the conv over (state, u), then one complex step from h
+        uc, st_new = oracle.conv_silu(wl.widen(ys["u"])[:, :, None], w, bias=cb, state_in=st_ref, want_state=True)
+        ys["u"] = uc[:, :, 0]
+        ys["h"] = h_ref
+        got_h = h.cpu().numpy().astype(np.float64)
+        check_decode(ys, o.cpu().numpy().astype(np.float64), got_h, "conv step %d" % s, zoh=zoh)
+        h_ref = got_h.astype(np.float32)  # the next step starts from the GPU's state
+        if K > 1:
+            np.testing.assert_array_equal(st_t.cpu().numpy().astype(np.float64), st_new)
+            st_ref = st_new.astype(np.float32)
