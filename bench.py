@@ -297,6 +297,23 @@ def main():
     xdbytes = 16 * Bd * Dd * Nd + 3 * Bd * Dd * 2 + 2 * Bd * Nd * 2 * 2 + 8 * Dd * Nd + 8 * Dd + Bd * Dd * 4
     del dcx, tdc, hdc, yc
 
+    # One GPU's share of the long-genomics sequence split 8 ways: the shard's
+    # aggregate (what the other shards need) and its scan from a carried state.
+    c3 = wl.CONFIGS[3]
+    Ls = c3["L"] // 8
+    xs = wl.make_scan_inputs(c3["B"], c3["D"], Ls, c3["N"], c3["dtype"], seed=3, dt_lo=c3["dt_lo"], dt_hi=c3["dt_hi"])
+    ts = {k: wl.to_torch(xs[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    h0s = torch.zeros((c3["B"], c3["D"], c3["N"]), dtype=torch.float32, device=dev)
+    fsh = binding.prepare_scan(ts["u"], ts["dt_raw"], ts["A"], ts["Bm"], ts["Cm"], dt_bias=ts["dt_bias"],
+                               Dskip=ts["Dskip"], z=ts["z"], h0=h0s)
+    Pa = torch.empty_like(h0s)
+    Ha = torch.empty_like(h0s)
+    agg = binding.prepare_aggregate(ts["u"], ts["dt_raw"], ts["A"], ts["Bm"], dt_bias=ts["dt_bias"], P=Pa, H=Ha)
+    ssec_a = timed(agg, 20)
+    ssec_f = timed(fsh, 20)
+    shard_elems = c3["B"] * c3["D"] * Ls * c3["N"]
+    del fsh, agg, ts, xs, h0s, Pa, Ha
+
     result = {
         "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
         "value": elements / wall,
@@ -362,6 +379,11 @@ def main():
                           "decode_workload": "state update B=64 D=2048 N=128 complex, bf16 inputs, fp32 state",
                           "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes,
                           "decode_hbm_gbps": xdbytes / xsec_d / 1e9},
+        "sequence_shard": {"workload": "one of 8 shards of the long-genomics sequence: B=1 D=256 L=%d N=16, "
+                                       "bf16; the all-gather and fold of the aggregates between devices is "
+                                       "not built" % Ls,
+                           "aggregate_ms": ssec_a * 1e3, "scan_from_carried_state_ms": ssec_f * 1e3,
+                           "elements_per_s": shard_elems / (ssec_a + ssec_f)},
     }
 
     if not args.no_cpu:

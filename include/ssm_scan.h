@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10500 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10600 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -186,6 +186,34 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes);
 
 /* Enqueue the scan described by `p` on `hip_stream`. */
 ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream);
+
+/*
+ * Affine aggregate of a whole sequence, for scanning one sequence in shards
+ * (the pages advise processing extremely long sequences in chunks: "Technical
+ * analysis: Mamba selective state spaces", section 7), for instance one shard
+ * per device. For the inputs of ssm_scan_fwd the sequence maps the state h
+ * entering it to P h + H, per (b, d, n), with
+ *   P = prod_t exp(delta_t A[d,n])   (0 when a reset lies in the sequence)
+ *   H = the state after the sequence from a zero state (same input
+ *       coefficient, resets and conv stage as the forward).
+ * Scanning consecutive shards s = 0, 1, ...: each computes (P_s, H_s); the
+ * state entering shard s is h_s = P_{s-1} h_{s-1} + H_{s-1} (h_0: the
+ * sequence's h0); ssm_scan_fwd of shard s with h0 = h_s gives its outputs.
+ * With the conv stage, a shard's conv_state_in is the preceding shard's last
+ * K-1 inputs.
+ *   p    : read as for ssm_scan_fwd: batch .. dstate, in_dtype, u, dt_raw,
+ *          dt_bias, A, Bm, reset, conv_w, conv_b, conv_state_in, conv_width,
+ *          discretization, state_kind, num_segments, workspace; out_dtype,
+ *          z, Cm, Dskip, h0, out, h_last and conv_state_out are not read.
+ *   P, H : (B,D,N) float32 outputs ((B,D,N,2) with the complex state),
+ *          4-byte aligned, overlapping neither the inputs, each other nor the
+ *          workspace. Errors as for ssm_scan_fwd, all detected before any launch.
+ */
+ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void* hip_stream);
+
+/* Bytes of workspace ssm_scan_aggregate needs (0 unless the library splits
+ * the sequence into pieces); sizes, dtypes, flags and num_segments are read. */
+ssm_status ssm_scan_aggregate_workspace_size(const ssm_scan_params* p, size_t* bytes);
 
 /*
  * Single-token decode step: one application of the recurrence to a stored

@@ -202,6 +202,27 @@ def scan(u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, reset=None, 
     return res.reshape(Bt, D, L)
 
 
+def scan_aggregate(u, dt_raw, A, Bm, *, dt_bias=None, reset=None, conv_w=None, conv_b=None, conv_state=None,
+                   zoh=False, complex_state=False, nthreads=0):
+    """Affine aggregate (P, H) of a whole sequence: the scan maps the entering
+    state h to P h + H per (b, d, n). By that definition, H is the final
+    state from h0 = 0 and P is the final state from h0 = 1 minus H (C plays
+    no part in the state, so it is zero here). A is (D, N) real or complex;
+    returns float64 (or complex128) arrays (B, D, N)."""
+    if conv_w is not None:
+        u = conv_silu(u, conv_w, bias=conv_b, reset=reset, state_in=conv_state, nthreads=nthreads)
+    u = np.asarray(u)
+    Bt, D, L = u.shape
+    N = np.asarray(A).shape[1]
+    Cz = np.zeros((Bt, L, N), dtype=np.complex128 if complex_state else np.float64)
+    run = scan_cplx if complex_state else scan
+    one = np.ones((Bt, D, N), dtype=np.complex128 if complex_state else np.float64)
+    _, H = run(u, dt_raw, A, Bm, Cz, dt_bias=dt_bias, reset=reset, want_h_last=True, zoh=zoh, nthreads=nthreads)
+    _, H1 = run(u, dt_raw, A, Bm, Cz, dt_bias=dt_bias, reset=reset, h0=one, want_h_last=True, zoh=zoh,
+                nthreads=nthreads)
+    return H1 - H, H
+
+
 def state_update(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=None, conv_w=None, conv_b=None,
                  conv_state=None, zoh=False, nthreads=0):
     """Decode step. h: (B, D, N); u, dt_raw, z: (B, D); Bm, Cm: (B, N).

@@ -81,8 +81,9 @@ class BwdParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_scan_bwd_workspace_size",
-           "ssm_scan_bwd", "ssm_status_string", "ssm_last_error", "ssm_version", "ssm_abi_struct_size")
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_aggregate_workspace_size", "ssm_scan_aggregate",
+           "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string", "ssm_last_error",
+           "ssm_version", "ssm_abi_struct_size")
 
 _lib = None
 
@@ -105,6 +106,10 @@ def load_library():
     lib.ssm_scan_workspace_size.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_aggregate_workspace_size.argtypes = [ctypes.POINTER(ScanParams), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssm_scan_aggregate_workspace_size.restype = ctypes.c_int
+    lib.ssm_scan_aggregate.argtypes = [ctypes.POINTER(ScanParams), vp, vp, vp]
+    lib.ssm_scan_aggregate.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [ctypes.POINTER(UpdateParams), vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(ctypes.c_size_t)]
@@ -175,7 +180,8 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
     _need(dt_raw, (Bt, D, L), "dt_raw", u.dtype)
     _need(A, (D, N) + c2, "A", torch.float32)
     _need(Bm, (Bt, L, N) + c2, "Bm", u.dtype)
-    _need(Cm, (Bt, L, N) + c2, "Cm", u.dtype)
+    if Cm is not None:
+        _need(Cm, (Bt, L, N) + c2, "Cm", u.dtype)
     if dt_bias is not None:
         _need(dt_bias, (D,), "dt_bias", torch.float32)
     if Dskip is not None:
@@ -213,6 +219,69 @@ def _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last
         p.conv_state_in, p.conv_state_out = _ptr(conv_state_in), _ptr(conv_state_out)
         p.conv_width = K
     return p
+
+
+def ssm_scan_aggregate(u, dt_raw, A, Bm, *, dt_bias=None, reset=None, conv_w=None, conv_b=None, conv_state_in=None,
+                       zoh=False, complex_state=False, num_segments=0, P=None, H=None, workspace=None, stream=None):
+    """Affine aggregate of the sequence: returns (P, H), (B, D, N) float32
+    ((B, D, N, 2) with complex_state), such that the scan maps an entering
+    state h to P h + H. Shards of one long sequence are scanned by folding the
+    preceding shards' aggregates into h0 (see include/ssm_scan.h)."""
+    import torch
+
+    lib = load_library()
+    Bt, D, _ = u.shape
+    N = A.shape[1]
+    shape = (Bt, D, N, 2) if complex_state else (Bt, D, N)
+    P = torch.empty(shape, dtype=torch.float32, device=u.device) if P is None else P
+    H = torch.empty(shape, dtype=torch.float32, device=u.device) if H is None else H
+    _need(P, shape, "P", torch.float32)
+    _need(H, shape, "H", torch.float32)
+    p = _scan_params(u, dt_raw, A, Bm, None, dt_bias, None, None, reset, None, None, None, None, num_segments,
+                     conv_w, conv_b, conv_state_in, None, zoh, complex_state)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_aggregate_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    if n.value and (workspace is None or workspace.numel() * workspace.element_size() < n.value):
+        workspace = torch.empty(int(n.value), dtype=torch.uint8, device=u.device)
+    if n.value:
+        p.workspace = _ptr(workspace)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssm_scan_aggregate(ctypes.byref(p), _ptr(P), _ptr(H), _stream(stream, u.device)))
+    return P, H
+
+
+def prepare_aggregate(u, dt_raw, A, Bm, *, dt_bias=None, reset=None, conv_w=None, conv_b=None, conv_state_in=None,
+                      zoh=False, complex_state=False, num_segments=0, P=None, H=None, stream=None):
+    """Marshal the arguments of ssm_scan_aggregate once; returns a no-argument
+    callable that enqueues the same call again and returns (P, H)."""
+    import torch
+
+    lib = load_library()
+    Bt, D, _ = u.shape
+    N = A.shape[1]
+    shape = (Bt, D, N, 2) if complex_state else (Bt, D, N)
+    P = torch.empty(shape, dtype=torch.float32, device=u.device) if P is None else P
+    H = torch.empty(shape, dtype=torch.float32, device=u.device) if H is None else H
+    _need(P, shape, "P", torch.float32)
+    _need(H, shape, "H", torch.float32)
+    p = _scan_params(u, dt_raw, A, Bm, None, dt_bias, None, None, reset, None, None, None, None, num_segments,
+                     conv_w, conv_b, conv_state_in, None, zoh, complex_state)
+    n = ctypes.c_size_t(0)
+    _check(lib.ssm_scan_aggregate_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=u.device)
+    if n.value:
+        p.workspace = _ptr(ws)
+        p.workspace_bytes = int(n.value)
+    st = _stream(stream, u.device)
+    fn = lib.ssm_scan_aggregate
+    pref, pp, hp = ctypes.byref(p), _ptr(P), _ptr(H)
+
+    def call():
+        _check(fn(pref, pp, hp, st))
+        return P, H
+
+    call.keep = ((u, dt_raw, A, Bm, dt_bias, reset, conv_w, conv_b, conv_state_in, ws), p)
+    return call
 
 
 def ssm_scan_workspace_size(u, A, *, num_segments=0, out_dtype=None):

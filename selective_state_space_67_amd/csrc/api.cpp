@@ -109,6 +109,141 @@ ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size
   return SSM_OK;
 }
 
+// Checks of a scan call's inputs shared by ssm_scan_fwd (aggregate = false)
+// and ssm_scan_aggregate (aggregate = true: C, z, D, h0 and the outputs of
+// the forward are not read). With pointers = false only sizes, types and
+// flags are checked (the workspace-size queries).
+constexpr int kScanInputs = 13;
+
+struct ScanCheck {
+  ScanSizes sz;
+  int64_t K = 0, cw = 1, bdk = 0;
+  size_t si = 4, so = 4;
+  bool cplx = false;
+};
+
+ssm_status check_scan_inputs(const ssm_scan_params* p, bool aggregate, ScanCheck* c, Range (&inputs)[kScanInputs],
+                             bool pointers = true) {
+  ssm_status s = check_scan_sizes(p, &c->sz);
+  if (s != SSM_OK) return s;
+  const ScanSizes& sz = c->sz;
+  if (!valid_dtype(p->in_dtype) || (!aggregate && !valid_dtype(p->out_dtype)))
+    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
+  if (!valid_disc(p->discretization))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
+  if ((s = check_kind(p->state_kind)) != SSM_OK) return s;
+  c->cplx = p->state_kind == SSM_STATE_COMPLEX;
+  c->cw = c->cplx ? 2 : 1;
+  c->K = p->conv_w ? p->conv_width : 0;
+  if (p->conv_w && (c->K < 1 || c->K > 4))
+    return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
+  if (!pointers) return SSM_OK;
+  const struct {
+    const void* ptr;
+    const char* name;
+  } required[] = {{p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"}, {p->Bm, "Bm"},
+                  {aggregate ? p->u : p->Cm, "Cm"}, {aggregate ? p->u : p->out, "out"}};
+  for (const auto& r : required)
+    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+  c->si = dtype_size(p->in_dtype);
+  c->so = aggregate ? 4 : dtype_size(p->out_dtype);
+  if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
+    return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
+  const int64_t K = c->K, cw = c->cw;
+  const size_t si = c->si;
+  c->bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
+  const void* z = aggregate ? nullptr : p->z;
+  const void* Cm = aggregate ? nullptr : p->Cm;
+  const void* Dskip = aggregate ? nullptr : p->Dskip;
+  const void* h0 = aggregate ? nullptr : p->h0;
+  const Range in[kScanInputs] = {
+      range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
+      range(z, sz.bdl, si, "z"),             range(p->Bm, sz.bln * cw, si, "Bm"),
+      range(Cm, sz.bln * cw, si, "Cm"),      range(p->A, sz.dn * cw, 4, "A"),
+      range(p->dt_bias, p->dim, 4, "dt_bias"), range(Dskip, p->dim, 4, "Dskip"),
+      range(p->reset, sz.bl, 1, "reset"),    range(h0, sz.bdn * cw, 4, "h0"),
+      range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
+      range(p->conv_state_in, c->bdk, 4, "conv_state_in"),
+  };
+  for (int i = 0; i < kScanInputs; ++i) inputs[i] = in[i];
+  const struct {
+    const void* ptr;
+    size_t align;
+    const char* name;
+  } aligns[] = {{p->u, si, "u"},           {p->dt_raw, si, "dt_raw"}, {z, si, "z"},
+                {p->Bm, si, "Bm"},         {Cm, si, "Cm"},            {p->A, 4, "A"},
+                {p->dt_bias, 4, "dt_bias"}, {Dskip, 4, "Dskip"},      {h0, 4, "h0"},
+                {aggregate ? nullptr : p->out, c->so, "out"},
+                {aggregate ? nullptr : p->h_last, 4, "h_last"},       {p->workspace, 4, "workspace"},
+                {p->conv_w, 4, "conv_w"},  {p->conv_b, 4, "conv_b"},  {p->conv_state_in, 4, "conv_state_in"},
+                {aggregate ? nullptr : p->conv_state_out, 4, "conv_state_out"}};
+  for (const auto& a : aligns)
+    if (a.ptr && !aligned(a.ptr, a.align))
+      return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
+  return SSM_OK;
+}
+
+// The caller's workspace: large enough and clear of the inputs and outputs.
+ssm_status check_workspace(const ssm_scan_params* p, size_t ws, const Range (&inputs)[kScanInputs],
+                           const Range* outs, int n_outs) {
+  if (ws == 0) return SSM_OK;
+  if (!p->workspace || p->workspace_bytes < ws)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws,
+                p->workspace ? p->workspace_bytes : static_cast<size_t>(0));
+  const Range w{static_cast<const char*>(p->workspace), ws, "workspace"};
+  for (const Range& r : inputs)
+    if (overlaps(w, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+  for (int i = 0; i < n_outs; ++i)
+    if (overlaps(w, outs[i])) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+  return SSM_OK;
+}
+
+// The aggregate pass: every piece's aggregate goes to the workspace (then one
+// fold into P and H) unless the sequence stays in one piece.
+ssm_status plan_aggregate(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
+  if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
+  const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
+  if (cplx)
+    ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+  else
+    ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+  const int64_t blocks = cplx ? ssm::cplx_scan_grid_blocks(p->batch, p->dim, *nseg)
+                              : ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg);
+  if (blocks > std::numeric_limits<int32_t>::max())
+    return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  *ws = *nseg > 1 ? static_cast<size_t>(2) * static_cast<size_t>(*nseg) * static_cast<size_t>(p->batch) *
+                        static_cast<size_t>(p->dim) * static_cast<size_t>(p->dstate) * (cplx ? 2 : 1) *
+                        sizeof(float)
+                  : 0;
+  return SSM_OK;
+}
+
+// The launch description common to the forward and the aggregate pass.
+ssm::ScanPlan scan_plan(const ssm_scan_params* p, const ScanCheck& c, int nseg, int64_t seg_len, size_t ws) {
+  ssm::ScanPlan plan{};
+  plan.B = p->batch;
+  plan.D = p->dim;
+  plan.L = p->seqlen;
+  plan.N = p->dstate;
+  plan.in_bf16 = p->in_dtype == SSM_BF16;
+  plan.out_bf16 = p->out_dtype == SSM_BF16;
+  plan.u = p->u;
+  plan.dt = p->dt_raw;
+  plan.Bm = p->Bm;
+  plan.dt_bias = p->dt_bias;
+  plan.A = p->A;
+  plan.reset = p->reset;
+  plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  plan.nseg = nseg;
+  plan.seg_len = seg_len;
+  plan.zoh = p->discretization == SSM_DISC_ZOH;
+  plan.conv_w = p->conv_w;
+  plan.conv_b = p->conv_b;
+  plan.conv_state_in = p->conv_state_in;
+  plan.conv_k = static_cast<int>(c.K);
+  return plan;
+}
+
 // Workspace layout of the backward pass (byte offsets, each 256-aligned).
 struct BwdLayout {
   int nseg;           // pieces of the checkpoint sweep (forward split)
@@ -434,56 +569,14 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
 
 ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
-  ScanSizes sz;
-  ssm_status s = check_scan_sizes(p, &sz);
+  ScanCheck c;
+  Range inputs[kScanInputs];
+  ssm_status s = check_scan_inputs(p, false, &c, inputs);
   if (s != SSM_OK) return s;
-  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
-    return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
-  const struct {
-    const void* ptr;
-    const char* name;
-  } required[] = {{p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"}, {p->Bm, "Bm"}, {p->Cm, "Cm"},
-                  {p->out, "out"}};
-  for (const auto& r : required)
-    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
-
-  const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
-  if (!valid_disc(p->discretization))
-    return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
-  const int64_t K = p->conv_w ? p->conv_width : 0;
-  if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
-  if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
-    return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
-  if ((s = check_kind(p->state_kind)) != SSM_OK) return s;
-  const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
-  const int64_t cw = cplx ? 2 : 1;  // scalars per A, B, C and state entry
-  const int64_t bdk = sz.bdn / p->dstate * (K > 0 ? K - 1 : 0);  // B*D*(K-1)
-  const Range inputs[] = {
-      range(p->u, sz.bdl, si, "u"),          range(p->dt_raw, sz.bdl, si, "dt_raw"),
-      range(p->z, sz.bdl, si, "z"),          range(p->Bm, sz.bln * cw, si, "Bm"),
-      range(p->Cm, sz.bln * cw, si, "Cm"),   range(p->A, sz.dn * cw, 4, "A"),
-      range(p->dt_bias, p->dim, 4, "dt_bias"), range(p->Dskip, p->dim, 4, "Dskip"),
-      range(p->reset, sz.bl, 1, "reset"),    range(p->h0, sz.bdn * cw, 4, "h0"),
-      range(p->conv_w, p->dim * K, 4, "conv_w"), range(p->conv_b, p->dim, 4, "conv_b"),
-      range(p->conv_state_in, bdk, 4, "conv_state_in"),
-  };
-  const struct {
-    const void* ptr;
-    size_t align;
-    const char* name;
-  } aligns[] = {{p->u, si, "u"},           {p->dt_raw, si, "dt_raw"}, {p->z, si, "z"},
-                {p->Bm, si, "Bm"},         {p->Cm, si, "Cm"},         {p->A, 4, "A"},
-                {p->dt_bias, 4, "dt_bias"}, {p->Dskip, 4, "Dskip"},   {p->h0, 4, "h0"},
-                {p->out, so, "out"},       {p->h_last, 4, "h_last"},  {p->workspace, 4, "workspace"},
-                {p->conv_w, 4, "conv_w"},  {p->conv_b, 4, "conv_b"},  {p->conv_state_in, 4, "conv_state_in"},
-                {p->conv_state_out, 4, "conv_state_out"}};
-  for (const auto& a : aligns)
-    if (a.ptr && !aligned(a.ptr, a.align))
-      return fail(SSM_ERR_MISALIGNED, "%s is not aligned to %zu bytes", a.name, a.align);
-
-  const Range out = range(p->out, sz.bdl, so, "out");
-  const Range hl = range(p->h_last, sz.bdn * cw, 4, "h_last");
-  const Range cso = range(p->conv_state_out, bdk, 4, "conv_state_out");
+  const ScanSizes& sz = c.sz;
+  const Range out = range(p->out, sz.bdl, c.so, "out");
+  const Range hl = range(p->h_last, sz.bdn * c.cw, 4, "h_last");
+  const Range cso = range(p->conv_state_out, c.bdk, 4, "conv_state_out");
   for (const Range& r : inputs) {
     if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
     if (overlaps(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps %s", r.name);
@@ -496,52 +589,62 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   int64_t seg_len;
   size_t ws;
   if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
-  if (ws > 0) {
-    if (!p->workspace || p->workspace_bytes < ws)
-      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws,
-                  p->workspace ? p->workspace_bytes : static_cast<size_t>(0));
-    const Range w{static_cast<const char*>(p->workspace), ws, "workspace"};
-    for (const Range& r : inputs)
-      if (overlaps(w, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
-    if (overlaps(w, out) || overlaps(w, hl) || overlaps(w, cso))
-      return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
-  }
+  const Range outs[] = {out, hl, cso};
+  if ((s = check_workspace(p, ws, inputs, outs, 3)) != SSM_OK) return s;
 
-  ssm::ScanPlan plan{};
-  plan.B = p->batch;
-  plan.D = p->dim;
-  plan.L = p->seqlen;
-  plan.N = p->dstate;
-  plan.in_bf16 = p->in_dtype == SSM_BF16;
-  plan.out_bf16 = p->out_dtype == SSM_BF16;
-  plan.u = p->u;
-  plan.dt = p->dt_raw;
-  plan.z = p->z;
-  plan.Bm = p->Bm;
-  plan.Cm = p->Cm;
-  plan.dt_bias = p->dt_bias;
-  plan.A = p->A;
-  plan.Dskip = p->Dskip;
-  plan.h0 = p->h0;
-  plan.reset = p->reset;
+  ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
   plan.out = p->out;
   plan.h_last = p->h_last;
-  plan.ws = ws > 0 ? static_cast<float*>(p->workspace) : nullptr;
-  plan.nseg = nseg;
-  plan.seg_len = seg_len;
-  plan.zoh = p->discretization == SSM_DISC_ZOH;
-  plan.conv_w = p->conv_w;
-  plan.conv_b = p->conv_b;
-  plan.conv_state_in = p->conv_state_in;
   plan.conv_state_out = p->conv_state_out;
-  plan.conv_k = static_cast<int>(K);
-  if (cplx) {
-    hipError_t e = ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "complex scan launch failed: %s", hipGetErrorString(e));
-    return ok();
-  }
-  hipError_t e = ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
+  plan.Cm = p->Cm;
+  plan.z = p->z;
+  plan.Dskip = p->Dskip;
+  plan.h0 = p->h0;
+  const hipError_t e = c.cplx ? ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream))
+                              : ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_scan_aggregate_workspace_size(const ssm_scan_params* p, size_t* bytes) {
+  if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");
+  ScanCheck c;
+  Range inputs[kScanInputs];
+  ssm_status s = check_scan_inputs(p, true, &c, inputs, false);
+  if (s != SSM_OK) return s;
+  int nseg;
+  int64_t seg_len;
+  size_t ws;
+  if ((s = plan_aggregate(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  *bytes = ws;
+  return ok();
+}
+
+ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void* hip_stream) {
+  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
+  ScanCheck c;
+  Range inputs[kScanInputs];
+  ssm_status s = check_scan_inputs(p, true, &c, inputs);
+  if (s != SSM_OK) return s;
+  if (!P || !H) return fail(SSM_ERR_NULL_POINTER, "P or H is NULL");
+  if (!aligned(P, 4) || !aligned(H, 4)) return fail(SSM_ERR_MISALIGNED, "P and H must be 4-byte aligned");
+  const Range rp = range(P, c.sz.bdn * c.cw, 4, "P"), rh = range(H, c.sz.bdn * c.cw, 4, "H");
+  for (const Range& r : inputs) {
+    if (overlaps(rp, r)) return fail(SSM_ERR_ALIAS, "P overlaps %s", r.name);
+    if (overlaps(rh, r)) return fail(SSM_ERR_ALIAS, "H overlaps %s", r.name);
+  }
+  if (overlaps(rp, rh)) return fail(SSM_ERR_ALIAS, "P overlaps H");
+  int nseg;
+  int64_t seg_len;
+  size_t ws;
+  if ((s = plan_aggregate(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  const Range outs[] = {rp, rh};
+  if ((s = check_workspace(p, ws, inputs, outs, 2)) != SSM_OK) return s;
+
+  ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
+  const hipError_t e = c.cplx ? ssm::launch_aggregate_cplx(plan, P, H, static_cast<hipStream_t>(hip_stream))
+                              : ssm::launch_aggregate(plan, P, H, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "aggregate launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -86,6 +86,9 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg);
 int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg);
 
 hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
+// Affine aggregate of the whole sequence into P and H (B, D, N): the pieces'
+// aggregates (in `ws`, nseg of each when nseg > 1) folded in order.
+hipError_t launch_aggregate(const ScanPlan& plan, float* P, float* H, hipStream_t stream);
 hipError_t launch_state_update(const UpdatePlan& plan, hipStream_t stream);
 
 // Complex diagonal state (scan_cplx.hip): A, B, C and the states hold
@@ -98,6 +101,7 @@ int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg);
 // aggregates_only: just the piece aggregates of a split scan (nothing when nseg == 1).
 hipError_t launch_scan_cplx(const ScanPlan& plan, hipStream_t stream, bool aggregates_only = false);
 hipError_t launch_state_update_cplx(const UpdatePlan& plan, hipStream_t stream);
+hipError_t launch_aggregate_cplx(const ScanPlan& plan, float* P, float* H, hipStream_t stream);
 
 // Backward pass (scan_bwd.hip). The checkpoint sweep runs through launch_scan
 // with ScanPlan::checkpoint set; BwdPlan describes the reverse sweep and the

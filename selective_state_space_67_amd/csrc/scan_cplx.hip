@@ -183,11 +183,13 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     const int steps = min(kT, Lseg - t0);
     __syncthreads();  // the previous chunk's readers are done
-    // B and C of steps t0 .. t0+steps-1: contiguous (steps, N, 2) blocks
+    // B and C of steps t0 .. t0+steps-1: contiguous (steps, N, 2) blocks (the
+    // aggregate pass reads no C: Cm may be null there)
     for (int i = tid; i < steps * N; i += kThreads) {
       const int tl = i / N, n = i - tl * N;
       const int64_t e = (static_cast<int64_t>(t0 + tl) * N + n) * 2;
-      s_bc[tl * NPAD + n] = make_float4(load_elem(Bb, e), load_elem(Bb, e + 1), load_elem(Cb, e), load_elem(Cb, e + 1));
+      s_bc[tl * NPAD + n] = make_float4(load_elem(Bb, e), load_elem(Bb, e + 1), AGG ? 0.0f : load_elem(Cb, e),
+                                        AGG ? 0.0f : load_elem(Cb, e + 1));
     }
     // this lane's row item: step t0 + k of channel d
     const int t = t0 + k;
@@ -423,7 +425,9 @@ size_t cplx_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg) {
 
 int64_t cplx_scan_grid_blocks(int64_t B, int64_t D, int nseg) { return B * ((D + kCPW - 1) / kCPW) * nseg; }
 
-hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregates_only) {
+namespace {
+
+CplxArgs cplx_args(const ScanPlan& p) {
   CplxArgs a{};
   a.B = p.B;
   a.D = p.D;
@@ -445,29 +449,30 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregat
   a.n_dgroups = static_cast<int>((p.D + kCPW - 1) / kCPW);
   a.nseg = p.nseg;
   a.seg_len = p.seg_len;
-  if (p.nseg > 1) {
-    const size_t half = cplx_workspace_bytes(p.B, p.D, p.N, p.nseg) / 2 / sizeof(float);
-    a.ws_P = p.ws;
-    a.ws_H = p.ws + half;
-  }
   a.conv_w = p.conv_w;
   a.conv_b = p.conv_b;
   a.conv_state_in = p.conv_state_in;
   a.conv_state_out = p.conv_state_out;
   a.conv_k = p.conv_k;
+  return a;
+}
+
+// Aggregates of pieces 0 .. agg_pieces-1 into a.ws_P / a.ws_H, then (when
+// full) the full pass over every piece.
+hipError_t launch_cplx(const ScanPlan& p, const CplxArgs& a, int agg_pieces, bool full, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg)));
-  const dim3 grid_agg(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, p.nseg - 1)));
+  const dim3 grid_agg(static_cast<unsigned>(cplx_scan_grid_blocks(p.B, p.D, agg_pieces)));
   return with_npl(p.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
     auto run = [&](auto in_t, auto has_reset, auto zoh, auto conv) {
       using InT = decltype(in_t);
       constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value, C = decltype(conv)::value;
-      if (p.nseg > 1) {  // the last piece's aggregate is never needed
+      if (agg_pieces > 0) {
         hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z, C>), grid_agg, dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
-        if (e != hipSuccess || aggregates_only) return e;
+        if (e != hipSuccess || !full) return e;
       }
-      if (aggregates_only) return hipSuccess;
+      if (!full) return hipSuccess;
       hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z, C>), grid, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };
@@ -481,6 +486,53 @@ hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregat
       return p.reset ? with_zoh(bf16_t{}, std::true_type{}) : with_zoh(bf16_t{}, std::false_type{});
     return p.reset ? with_zoh(float{}, std::true_type{}) : with_zoh(float{}, std::false_type{});
   });
+}
+
+// Folds the pieces' complex aggregates in order: P = prod_s P_s, H <- P_s H + H_s.
+__global__ __launch_bounds__(256) void cplx_aggregate_fold_kernel(const float2* wsP, const float2* wsH, int nseg,
+                                                                  int64_t count, float2* P, float2* H) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  float pr = 1.0f, pi = 0.0f, hr = 0.0f, hi = 0.0f;
+  for (int s = 0; s < nseg; ++s) {
+    const float2 q = wsP[s * count + i], g = wsH[s * count + i];
+    const float nr = __builtin_fmaf(q.x, hr, __builtin_fmaf(-q.y, hi, g.x));
+    const float ni = __builtin_fmaf(q.x, hi, __builtin_fmaf(q.y, hr, g.y));
+    hr = nr;
+    hi = ni;
+    const float mr = __builtin_fmaf(q.x, pr, -q.y * pi);
+    const float mi = __builtin_fmaf(q.x, pi, q.y * pr);
+    pr = mr;
+    pi = mi;
+  }
+  P[i] = make_float2(pr, pi);
+  H[i] = make_float2(hr, hi);
+}
+
+}  // namespace
+
+hipError_t launch_scan_cplx(const ScanPlan& p, hipStream_t stream, bool aggregates_only) {
+  CplxArgs a = cplx_args(p);
+  if (p.nseg > 1) {
+    const size_t half = cplx_workspace_bytes(p.B, p.D, p.N, p.nseg) / 2 / sizeof(float);
+    a.ws_P = p.ws;
+    a.ws_H = p.ws + half;
+  }
+  // the last piece's aggregate is never needed
+  return launch_cplx(p, a, p.nseg - 1, !aggregates_only, stream);
+}
+
+hipError_t launch_aggregate_cplx(const ScanPlan& p, float* P, float* H, hipStream_t stream) {
+  CplxArgs a = cplx_args(p);
+  const int64_t count = p.B * p.D * p.N;  // complex values
+  a.ws_P = p.nseg > 1 ? p.ws : P;
+  a.ws_H = p.nseg > 1 ? p.ws + 2 * static_cast<size_t>(p.nseg) * count : H;
+  hipError_t e = launch_cplx(p, a, p.nseg, false, stream);
+  if (e != hipSuccess || p.nseg == 1) return e;
+  hipLaunchKernelGGL(cplx_aggregate_fold_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<const float2*>(a.ws_P), reinterpret_cast<const float2*>(a.ws_H),
+                     p.nseg, count, reinterpret_cast<float2*>(P), reinterpret_cast<float2*>(H));
+  return hipGetLastError();
 }
 
 hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {

@@ -41,7 +41,9 @@ int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg) {
   return static_cast<int64_t>(nseg) * B * ((D + cpw - 1) / cpw);
 }
 
-hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
+namespace {
+
+fwd::ScanArgs scan_args(const ScanPlan& pl) {
   fwd::ScanArgs a{};
   a.B = pl.B;
   a.D = pl.D;
@@ -79,19 +81,55 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.conv_k = pl.conv_k;
   a.uconv_out = pl.uconv_out;
   a.zoh = pl.zoh;
-  const bool ck = pl.checkpoint != 0;
-  const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
-  a.ws_P = pl.ws;
-  a.ws_H = pl.ws ? pl.ws + per : nullptr;
-  const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
-  const int nf = per_piece * pl.nseg;
-  const int na = per_piece * (pl.nseg - 1);
+  return a;
+}
+
+hipError_t launch(const ScanPlan& pl, const fwd::ScanArgs& a, int nf, int na, bool ck, hipStream_t stream) {
   const bool reset = pl.reset != nullptr;
   if (pl.in_bf16)
     return reset ? fwd::launch_variant<bf16_t, true>(a, nf, na, ck, stream)
                  : fwd::launch_variant<bf16_t, false>(a, nf, na, ck, stream);
   return reset ? fwd::launch_variant<float, true>(a, nf, na, ck, stream)
                : fwd::launch_variant<float, false>(a, nf, na, ck, stream);
+}
+
+// Folds the pieces' aggregates in order: P = prod_s P_s, H <- P_s H + H_s.
+__global__ __launch_bounds__(256) void aggregate_fold_kernel(const float* wsP, const float* wsH, int nseg,
+                                                             int64_t count, float* P, float* H) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  float p = 1.0f, h = 0.0f;
+  for (int s = 0; s < nseg; ++s) {
+    const float ps = wsP[s * count + i];
+    h = __builtin_fmaf(ps, h, wsH[s * count + i]);
+    p *= ps;
+  }
+  P[i] = p;
+  H[i] = h;
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
+  fwd::ScanArgs a = scan_args(pl);
+  const size_t per = static_cast<size_t>(pl.nseg > 1 ? pl.nseg - 1 : 0) * pl.B * pl.D * pl.N;
+  a.ws_P = pl.ws;
+  a.ws_H = pl.ws ? pl.ws + per : nullptr;
+  const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
+  return launch(pl, a, per_piece * pl.nseg, per_piece * (pl.nseg - 1), pl.checkpoint != 0, stream);
+}
+
+hipError_t launch_aggregate(const ScanPlan& pl, float* P, float* H, hipStream_t stream) {
+  fwd::ScanArgs a = scan_args(pl);
+  const int64_t count = pl.B * pl.D * pl.N;
+  a.ws_P = pl.nseg > 1 ? pl.ws : P;
+  a.ws_H = pl.nseg > 1 ? pl.ws + static_cast<size_t>(pl.nseg) * count : H;
+  const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
+  hipError_t e = launch(pl, a, 0, per_piece * pl.nseg, false, stream);
+  if (e != hipSuccess || pl.nseg == 1) return e;
+  hipLaunchKernelGGL(aggregate_fold_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream,
+                     a.ws_P, a.ws_H, pl.nseg, count, P, H);
+  return hipGetLastError();
 }
 
 }  // namespace ssm

@@ -815,7 +815,9 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE>())) v
 template <typename TL, typename InT, bool HAS_RESET, bool CONV, bool ZOH>
 hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, bool checkpoint,
                        hipStream_t stream) {
-  if (args.nseg > 1) {
+  // nblocks_agg workgroups of piece aggregates (none when the sequence is one
+  // piece), then nblocks_full of the full pass (none for aggregates only)
+  if (nblocks_agg > 0) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
     hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate, CONV, ZOH>), dim3(nblocks_agg),
@@ -823,6 +825,7 @@ hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (nblocks_full == 0) return hipSuccess;
   ScanArgs full = args;
   full.nblocks = nblocks_full;
   if (checkpoint)

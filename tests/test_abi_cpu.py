@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10500
+    assert lib.ssm_version() == 10600
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -446,3 +446,40 @@ def test_complex_state_extents_are_doubled(lib):
     q = update_params(state_kind=bd.SSM_STATE_COMPLEX)
     q.out = q.h + B * D * N * 4
     assert update_status(lib, q) == 7
+
+
+def agg_status(lib, p, P, H):
+    return lib.ssm_scan_aggregate(ctypes.byref(p) if p is not None else None, P, H, None)
+
+
+def test_aggregate_arguments(lib):
+    # every call fails validation before any launch
+    P, H = BASE + 0x50000000, BASE + 0x51000000
+    assert agg_status(lib, None, P, H) == 1
+    # C, z, D, h0 and out are not read: with them absent the missing P is the error
+    assert agg_status(lib, scan_params(Cm=None, out=None, z=None), None, H) == 1
+    assert b"P or H" in lib.ssm_last_error()
+    assert agg_status(lib, scan_params(u=None), P, H) == 1
+    assert agg_status(lib, scan_params(), P + 2, H) == 4          # misaligned
+    assert agg_status(lib, scan_params(), P, P + 8) == 7          # P overlaps H
+    p = scan_params()
+    assert agg_status(lib, p, p.u, H) == 7                         # P over an input
+    assert agg_status(lib, scan_params(state_kind=7), P, H) == 5
+    assert agg_status(lib, scan_params(conv_w=BASE + 0x70000000, conv_width=5), P, H) == 2
+    assert agg_status(lib, scan_params(discretization=9), P, H) == 5
+
+
+def test_aggregate_workspace(lib):
+    # pieces: every piece's aggregate, P and H, then one fold
+    n = ctypes.c_size_t(0)
+    p = scan_params(num_segments=4)                                # L = 64: four 16-step pieces
+    assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * B * D * N * 4
+    p.workspace, p.workspace_bytes = BASE + 0x40000000, n.value - 4
+    assert agg_status(lib, p, BASE + 0x50000000, BASE + 0x51000000) == 6
+    q = scan_params(num_segments=4, state_kind=bd.SSM_STATE_COMPLEX)
+    assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(q), ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * B * D * N * 2 * 4
+    r = scan_params(num_segments=1)
+    assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(r), ctypes.byref(n)) == 0
+    assert n.value == 0
