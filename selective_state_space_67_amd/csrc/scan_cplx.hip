@@ -138,6 +138,11 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   __shared__ __align__(16) float4 s_bc[kT * NPAD];
   // (delta, delta u), or (delta, u) with the zero-order hold; delta negated on a reset step
   __shared__ __align__(8) float2 s_du[kCPW * kT];
+  // Read-out partials of a chunk, [channel][step][lane]; the lane that owns a
+  // step adds its row's 16 partials after the chunk. Channels are kYS floats
+  // apart so that the four rows of a wave write to different banks.
+  constexpr int kYS = kT * 16 + 16;
+  __shared__ __align__(16) float s_y[AGG ? 4 : kCPW * kYS];
 
   CState cq[NPL];
   float hr[NPL], hi[NPL];
@@ -236,10 +241,16 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
         const float4 bc = s_bc[tl * NPAD + n0 + j];
         p += cplx_step<ZOH>(dlt, du.y, cq[j], make_float2(bc.x, bc.y), make_float2(bc.z, bc.w), hr[j], hi[j]);
       }
-      if constexpr (!AGG) {
-        p = row_sum16(p);
-        ymine = k == tl ? p : ymine;
-      }
+      if constexpr (!AGG) s_y[c * kYS + tl * 16 + k] = p;
+    }
+    if constexpr (!AGG) {
+      // the row's lanes wrote the partials; lane k adds those of step k
+      __builtin_amdgcn_wave_barrier();
+      const float4* yr = reinterpret_cast<const float4*>(s_y + c * kYS + k * 16);
+      const float4 y0 = yr[0], y1 = yr[1], y2 = yr[2], y3 = yr[3];
+      ymine = ((y0.x + y0.y) + (y0.z + y0.w)) + ((y1.x + y1.y) + (y1.z + y1.w)) +
+              (((y2.x + y2.y) + (y2.z + y2.w)) + ((y3.x + y3.y) + (y3.z + y3.w)));
+      __builtin_amdgcn_wave_barrier();
     }
     if (!AGG && live) {
       const float v = (ymine + dsk * uu) * gate;

@@ -34,7 +34,8 @@
 //    arriving at its end, then walks its 16-step chunks backwards. For every
 //    KC-step block it recomputes the states from the checkpoint, keeping each
 //    step's a_t and a_t h_{t-1} in registers, and runs the adjoint back
-//    through the block. The three sums over n per step are DPP row sums; the
+//    through the block. The three sums over n per step go through LDS (each
+//    lane adds its row's partials of the step it owns after the block); the
 //    sums of dB and dC over the workgroup's 16 channels go through LDS and
 //    are written as one partial per channel group.
 // 3. Reduction (shared with the real backward): dB and dC over channel
@@ -314,6 +315,12 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
   __shared__ __align__(16) float4 s_st[kCPW * kT];
   // per (flush slot, channel, state): (dB.re, dB.im, dC.re, dC.im) of one step
   __shared__ __align__(16) float4 s_dbc[F * kCPW * NPAD];
+  // The three per-step partial sums over a lane's states, [sum][channel][step
+  // of the block][lane]; the lane that owns a step adds its row's 16 partials
+  // after the block. Channels are PS floats apart (the rows of a wave write
+  // to different banks).
+  constexpr int PS = KC * 16 + 16;
+  __shared__ __align__(16) float s_p[3 * kCPW * PS];
 
   CState cq[NPL];
   load_A<NPL>(a.A, d, N, n0, dvalid, cq);
@@ -440,14 +447,10 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
           xr[j] = r ? 0.0f : nr;
           xi[j] = r ? 0.0f : ni;
         }
-        p1 = row_sum16(p1);
-        p2 = row_sum16(p2);
-        p3 = row_sum16(p3);
-        if (k == tb + i) {
-          m1 = p1;
-          m2 = p2;
-          m3 = p3;
-        }
+        float* pp = s_p + c * PS + i * 16 + k;
+        pp[0] = p1;
+        pp[kCPW * PS] = p2;
+        pp[2 * kCPW * PS] = p3;
         if (i % F == 0) {  // add the F steps' dB and dC over the 16 channels
           __syncthreads();
           const float* sd = reinterpret_cast<const float*>(s_dbc);
@@ -465,6 +468,23 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
           __syncthreads();
         }
       }
+      // the row's lanes wrote the block's partials; the lane of each step adds them
+      __builtin_amdgcn_wave_barrier();
+      const int mi = k - tb;
+      if (mi >= 0 && mi < KC) {
+        float m[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const float4* r = reinterpret_cast<const float4*>(s_p + q * kCPW * PS + c * PS + mi * 16);
+          const float4 y0 = r[0], y1 = r[1], y2 = r[2], y3 = r[3];
+          m[q] = ((y0.x + y0.y) + (y0.z + y0.w)) + ((y1.x + y1.y) + (y1.z + y1.w)) +
+                 (((y2.x + y2.y) + (y2.z + y2.w)) + ((y3.x + y3.y) + (y3.z + y3.w)));
+        }
+        m1 = m[0];
+        m2 = m[1];
+        m3 = m[2];
+      }
+      __builtin_amdgcn_wave_barrier();
     }
     if (live) {
       const float du = __builtin_fmaf(in.dl, m1, dsk * in.dy);
