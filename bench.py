@@ -7,11 +7,13 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
   value        whole-job throughput in scan elements (B*D*L*N) per second over
                the K timed steps (wall clock, synchronised on both sides)
   hbm_gbps     algorithmic HBM bytes per step / time per step
-  roofline     the scan kernel against the bound that limits it (the vector
-               ALU; see the design doc for the peak), measured with HIP events on
-               the launch stream; `traffic` is the HBM byte count from the
-               rocprofv3 counter runs recorded under profiles/ (null when the
-               kernel source changed since they were taken)
+  roofline     the scan kernel against the bound that limits it: the vector
+               ALU, whose peak is 256 CUs x 64 lanes x 2.4 GHz = 39.3e12 float32
+               lane-operations per second (no packed float32; a transcendental
+               counts twice), measured with HIP events on the launch stream;
+               `traffic` is the HBM byte count from the rocprofv3 counter runs
+               recorded under profiles/ (null when the kernel source changed
+               since they were taken)
   cold_cache   the same launch after a 1 GiB write that evicts L2 and MALL
   decode       the single-token decode step (batch 64, 2048 channels, N = 128)
   backward     ssm_scan_bwd on the same workload with a random output gradient
@@ -20,9 +22,13 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
                (width 4) + SiLU input stage, u being the conv input
   zoh          the same forward and backward with the exact zero-order-hold
                input coefficient (e^{delta A} - 1) / A in place of delta
+  complex_state the complex diagonal state (S4D-Lin A) at the same shape:
+               forward, forward with the zero-order hold, backward, decode
+  sequence_shard one of 8 shards of the long-genomics sequence: its aggregate
+               and its scan from a carried state
   cpu_baseline the float64 oracle on the host cores over the same workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -119,9 +125,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--config", type=int, default=1,
-                    help="workload index (1 = Mamba-130M layer, the default and the headline; 0, 2, 3, 4 "
-                         "print their own line for reference)")
+    ap.add_argument("--workload", default="mamba130m-layer",
+                    help="workload name: mamba130m-layer (the default and the headline); tiny-fp32, "
+                         "mamba2.8b-layer, long-genomics and packed-docs-n128 print their own line for reference")
     ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL-evicting write")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (for counter calibration runs)")
@@ -139,9 +145,9 @@ def main():
 
     load_library()
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS[args.config]
+    cfg = wl.workload(args.workload)
     B, D, L, N = cfg["B"], cfg["D"], cfg["L"], cfg["N"]
-    x = wl.config_inputs(args.config)
+    x = wl.workload_inputs(args.workload)
     t = {k: wl.to_torch(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
     out = torch.empty((B, D, L), dtype=torch.float32, device=dev)
     call = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
@@ -273,7 +279,7 @@ def main():
     del bwd, dout, fzoh, bzoh
 
     # Complex diagonal state (S4D-Lin A = -1/2 + i n) at the same shape, and its decode step.
-    xc = wl.make_cplx_inputs(B, D, L, N, cfg["dtype"], seed=cfg.get("seed", args.config), dt_lo=cfg["dt_lo"],
+    xc = wl.make_cplx_inputs(B, D, L, N, cfg["dtype"], seed=cfg["seed"], dt_lo=cfg["dt_lo"],
                              dt_hi=cfg["dt_hi"], packed=cfg["packed"])
     tc = {k: wl.to_torch(xc[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset")}
     fcx = binding.prepare_scan(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], dt_bias=tc["dt_bias"],
@@ -299,7 +305,7 @@ def main():
 
     # One GPU's share of the long-genomics sequence split 8 ways: the shard's
     # aggregate (what the other shards need) and its scan from a carried state.
-    c3 = wl.CONFIGS[3]
+    c3 = wl.workload("long-genomics")
     Ls = c3["L"] // 8
     xs = wl.make_scan_inputs(c3["B"], c3["D"], Ls, c3["N"], c3["dtype"], seed=3, dt_lo=c3["dt_lo"], dt_hi=c3["dt_hi"])
     ts = {k: wl.to_torch(xs[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}

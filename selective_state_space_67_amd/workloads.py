@@ -70,17 +70,17 @@ def widen(x) -> np.ndarray:
     return x.astype(np.float64)
 
 
-# The five workloads: shapes, dtypes and the dt_bias range.
-CONFIGS = [
-    dict(name="tiny-fp32", B=1, D=64, L=256, N=16, dtype=F32, dt_lo=1e-3, dt_hi=1e-1, packed=False),
+# The five workloads: shapes, dtypes, the dt_bias range and the seed of each.
+WORKLOADS = [
+    dict(name="tiny-fp32", B=1, D=64, L=256, N=16, dtype=F32, dt_lo=1e-3, dt_hi=1e-1, packed=False, seed=0),
     dict(name="mamba130m-layer", B=8, D=1536, L=2048, N=16, dtype=BF16, dt_lo=1e-3, dt_hi=1e-1,
-         packed=False),
+         packed=False, seed=1),
     dict(name="mamba2.8b-layer", B=4, D=5120, L=2048, N=16, dtype=BF16, dt_lo=1e-3, dt_hi=1e-1,
-         packed=False),
+         packed=False, seed=2),
     dict(name="long-genomics", B=1, D=256, L=131072, N=16, dtype=BF16, dt_lo=1e-3, dt_hi=1e-2,
-         packed=False),
+         packed=False, seed=3),
     dict(name="packed-docs-n128", B=2, D=2048, L=4096, N=128, dtype=BF16, dt_lo=1e-3, dt_hi=1e-1,
-         packed=True),
+         packed=True, seed=4),
 ]
 DECODE = dict(name="decode-n128", B=64, D=2048, N=128, dtype=BF16, dt_lo=1e-3, dt_hi=1e-1, seed=5)
 
@@ -130,12 +130,20 @@ def make_scan_inputs(B, D, L, N, dtype=F32, seed=0, dt_lo=1e-3, dt_hi=1e-1, pack
                 A=s4d_real_A(D, N), Dskip=Dskip, reset=reset, dtype=dtype)
 
 
-def config_inputs(index: int, **overrides):
-    c = dict(CONFIGS[index])
+def workload(name: str) -> dict:
+    """The workload called ``name`` (shapes, dtype, dt_bias range, seed)."""
+    for w in WORKLOADS:
+        if w["name"] == name:
+            return dict(w)
+    raise KeyError(name)
+
+
+def workload_inputs(name: str, **overrides):
+    """Stored inputs of the workload called ``name`` (its own seed)."""
+    c = workload(name)
     c.update(overrides)
-    return make_scan_inputs(c["B"], c["D"], c["L"], c["N"], dtype=c["dtype"],
-                            seed=c.get("seed", index), dt_lo=c["dt_lo"], dt_hi=c["dt_hi"],
-                            packed=c["packed"])
+    return make_scan_inputs(c["B"], c["D"], c["L"], c["N"], dtype=c["dtype"], seed=c["seed"], dt_lo=c["dt_lo"],
+                            dt_hi=c["dt_hi"], packed=c["packed"])
 
 
 def s4d_lin_A(D, N):

@@ -118,8 +118,8 @@ def test_sharded_scan_at_the_long_genomics_shard():
 
     from selective_state_space_67_amd import ssm_scan_aggregate, ssm_scan_fwd
 
-    cfg = wl.CONFIGS[3]
-    x = wl.config_inputs(3)
+    cfg = wl.workload("long-genomics")
+    x = wl.workload_inputs("long-genomics")
     dev = device()
     t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
     B, D, L, N = cfg["B"], cfg["D"], cfg["L"], cfg["N"]

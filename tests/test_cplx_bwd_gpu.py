@@ -197,14 +197,14 @@ def test_real_case_matches_real_backward():
         assert np.all(np.abs(c - r) <= bound), k
 
 
-@pytest.mark.parametrize("index", [1, 3, 4])
-def test_workload_full_size(index):
+@pytest.mark.parametrize("name", ["mamba130m-layer", "long-genomics", "packed-docs-n128"])
+def test_workload_full_size(name):
     """The workload shapes with S4D-Lin A at their full sizes, every gradient
     element against the oracle."""
-    cfg = wl.CONFIGS[index]
-    x = wl.make_cplx_inputs(cfg["B"], cfg["D"], cfg["L"], cfg["N"], cfg["dtype"], seed=index, dt_lo=cfg["dt_lo"],
-                            dt_hi=cfg["dt_hi"], packed=cfg["packed"])
-    rng = np.random.default_rng(600 + index)
+    cfg = wl.workload(name)
+    x = wl.make_cplx_inputs(cfg["B"], cfg["D"], cfg["L"], cfg["N"], cfg["dtype"], seed=cfg["seed"],
+                            dt_lo=cfg["dt_lo"], dt_hi=cfg["dt_hi"], packed=cfg["packed"])
+    rng = np.random.default_rng(600 + cfg["seed"])
     x["dout"] = wl.store(rng.standard_normal(x["u"].shape), cfg["dtype"])
     x["h0"] = None
     x["dh_last"] = None

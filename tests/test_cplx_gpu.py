@@ -254,16 +254,16 @@ def test_complex_scan_at_layer_size_sampled_channels():
         check(sub, got[b:b + 1, ds], hl[b:b + 1, ds], ref, rhl, "layer b=%d" % b)
 
 
-@pytest.mark.parametrize("index,per_row", [(3, 16), (4, 24)])
-def test_complex_scan_at_workload_sizes_sampled_channels(index, per_row):
+@pytest.mark.parametrize("name,per_row", [("long-genomics", 16), ("packed-docs-n128", 24)])
+def test_complex_scan_at_workload_sizes_sampled_channels(name, per_row):
     """The long-genomics (split into pieces) and packed N = 128 (resets)
     shapes with S4D-Lin A, in the launch the bench times; sampled channels of
     every batch row against the oracle."""
-    cfg = wl.CONFIGS[index]
-    x = wl.make_cplx_inputs(cfg["B"], cfg["D"], cfg["L"], cfg["N"], cfg["dtype"], seed=index, dt_lo=cfg["dt_lo"],
-                            dt_hi=cfg["dt_hi"], packed=cfg["packed"])
+    cfg = wl.workload(name)
+    x = wl.make_cplx_inputs(cfg["B"], cfg["D"], cfg["L"], cfg["N"], cfg["dtype"], seed=cfg["seed"],
+                            dt_lo=cfg["dt_lo"], dt_hi=cfg["dt_hi"], packed=cfg["packed"])
     got, hl = run_scan(x)
-    rng = np.random.default_rng(10 + index)
+    rng = np.random.default_rng(10 + cfg["seed"])
     for b in range(cfg["B"]):
         ds = np.sort(rng.choice(cfg["D"], per_row, replace=False))
         sub = dict(u=x["u"][b:b + 1, ds], dt_raw=x["dt_raw"][b:b + 1, ds], z=x["z"][b:b + 1, ds],

@@ -143,12 +143,12 @@ def test_deterministic():
             np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
-@pytest.mark.parametrize("index", [1, 3, 4])
-def test_config_full_size(index):
+@pytest.mark.parametrize("name", ["mamba130m-layer", "long-genomics", "packed-docs-n128"])
+def test_workload_full_size(name):
     """The workloads at their full sizes, every gradient element against the oracle."""
-    cfg = wl.CONFIGS[index]
-    x = wl.config_inputs(index)
-    rng = np.random.default_rng(500 + index)
+    cfg = wl.workload(name)
+    x = wl.workload_inputs(name)
+    rng = np.random.default_rng(500 + cfg["seed"])
     x["dout"] = wl.store(rng.standard_normal(x["u"].shape), cfg["dtype"])
     x["h0"] = None
     x["dh_last"] = None

@@ -45,9 +45,9 @@ def small(B, D, L, N, dtype, seed=0, packed=False, with_z=True, dskip="ones", do
 
 # ---------------------------------------------------------------------------- small, every element
 
-def test_config0_tiny_fp32_every_element():
-    x = wl.config_inputs(0)
-    log("config 0 %s" % (x["u"].shape,))
+def test_tiny_fp32_every_element():
+    x = wl.workload_inputs("tiny-fp32")
+    log("tiny-fp32 %s" % (x["u"].shape,))
     assert_close(gpu_scan(x), oracle_full(x), wl.F32)
 
 
@@ -216,9 +216,9 @@ def test_decode_unaligned_state_takes_scalar_path():
     assert big[0].item() == 0.0
 
 
-def test_decode_config_full_size():
+def test_decode_full_size():
     x = wl.decode_inputs()
-    log("decode config %s" % (x["h"].shape,))
+    log("decode %s" % (x["h"].shape,))
     out, h = gpu_update(x, x["h"])
     ro, rh = oracle_update(x, x["h"])
     assert_close(out, ro, wl.BF16)
@@ -248,16 +248,17 @@ def sampled_rows(B, D, count, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4])
-def test_config_full_size_sampled_rows(index):
-    c = wl.CONFIGS[index]
-    log("config %d %s generating inputs" % (index, c["name"]))
-    x = wl.config_inputs(index)
+@pytest.mark.parametrize("name", ["mamba130m-layer", "mamba2.8b-layer", "long-genomics", "packed-docs-n128"])
+def test_workload_full_size_sampled_rows(name):
+    c = wl.workload(name)
+    index = c["seed"]
+    log("%s: generating inputs" % name)
+    x = wl.workload_inputs(name)
     out = gpu_scan(x)
     B, D, L = x["u"].shape
     assert np.all(np.isfinite(out))
     rows = sampled_rows(B, D, 40, seed=index)
-    log("config %d: oracle on %d rows" % (index, len(rows)))
+    log("%s: oracle on %d rows" % (name, len(rows)))
     ref = oracle_rows(x, rows)
     margin = assert_close(out.reshape(B * D, L)[rows], ref, wl.BF16)
-    log("config %d: max err/bound %.3g" % (index, margin))
+    log("%s: max err/bound %.3g" % (name, margin))
