@@ -227,6 +227,55 @@ def main():
     dbytes = decode_bytes(Bd, Dd, Nd, 2, 4)
     dsec = float(np.median(dms)) / 1e3
 
+    # A launch-bound decode loop (one sequence of the Mamba-130M layer shape,
+    # 32 tokens): prepared launches one by one, against the same 32 steps
+    # captured once in a HIP graph and replayed.
+    y1 = wl.make_decode_inputs(1, 1536, 16, dtype=wl.BF16, seed=5)
+    t1 = {k: wl.to_torch(y1[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    h1 = torch.from_numpy(y1["h"]).to(dev)
+    loop = binding.prepare_state_update(h1, t1["u"], t1["dt_raw"], t1["A"], t1["Bm"], t1["Cm"], dt_bias=t1["dt_bias"],
+                                        Dskip=t1["Dskip"], z=t1["z"])
+    tokens = 32
+
+    def eager_loop():
+        for _ in range(tokens):
+            loop()
+
+    for _ in range(3):
+        eager_loop()
+    torch.cuda.synchronize()
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    l0.record(stream)
+    for _ in range(10):
+        eager_loop()
+    l1.record(stream)
+    l1.synchronize()
+    eager_tok = l0.elapsed_time(l1) / (10 * tokens) / 1e3
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        gl = binding.prepare_state_update(h1, t1["u"], t1["dt_raw"], t1["A"], t1["Bm"], t1["Cm"],
+                                          dt_bias=t1["dt_bias"], Dskip=t1["Dskip"], z=t1["z"])
+        gl()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gcap = binding.prepare_state_update(h1, t1["u"], t1["dt_raw"], t1["A"], t1["Bm"], t1["Cm"],
+                                            dt_bias=t1["dt_bias"], Dskip=t1["Dskip"], z=t1["z"])
+        for _ in range(tokens):
+            gcap()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    l0.record(stream)
+    for _ in range(10):
+        graph.replay()
+    l1.record(stream)
+    l1.synchronize()
+    graph_tok = l0.elapsed_time(l1) / (10 * tokens) / 1e3
+    del graph, gcap, gl, loop, t1, h1, y1
+
     # Backward pass on the same workload.
     rng = np.random.default_rng(1234)
     dout = wl.to_torch(wl.store(rng.standard_normal((B, D, L)), cfg["dtype"]), dev)
@@ -361,6 +410,8 @@ def main():
         "decode": {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
                    "launch_ms_mean": dsec * 1e3, "algorithmic_bytes": dbytes,
                    "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS},
+        "decode_loop": {"workload": "32 decode steps of one sequence, B=1 D=1536 N=16, bf16 inputs",
+                        "eager_us_per_token": eager_tok * 1e6, "hip_graph_us_per_token": graph_tok * 1e6},
         "backward": {"workload": "ssm_scan_bwd on the same inputs, %s dout, fp32 gradients" % cfg["dtype"],
                      "ms_per_call": bsec * 1e3, "elements_per_s": elements / bsec,
                      "algorithmic_bytes": bbytes, "hbm_gbps": bbytes / bsec / 1e9,
