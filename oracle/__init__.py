@@ -55,7 +55,7 @@ def _load():
         lib.oracle_scan_bwd_rows.restype = ctypes.c_int
         lib.oracle_scan_cplx_rows.argtypes = [i64, i64, i64] + [p] * 14 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_cplx_rows.restype = None
-        lib.oracle_scan_cplx_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int]
+        lib.oracle_scan_cplx_bwd_rows.argtypes = [i64, i64, i64, i64, i64] + [p] * 23 + [ctypes.c_int] * 2
         lib.oracle_scan_cplx_bwd_rows.restype = ctypes.c_int
         lib.oracle_conv_silu_rows.argtypes = [i64, i64, i64] + [p] * 10 + [ctypes.c_int]
         lib.oracle_conv_silu_rows.restype = None
@@ -369,12 +369,12 @@ def state_update_cplx(h, u, dt_raw, A, Bm, Cm, *, z=None, dt_bias=None, Dskip=No
 
 
 def scan_cplx_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=None, reset=None, h0=None,
-                  dh_last=None, nthreads=0):
+                  dh_last=None, zoh=False, nthreads=0):
     """Gradients of sum(dout * out) + sum(Re dh_last Re h_last + Im dh_last Im h_last)
-    for the complex-state scan (scan_cplx). Gradients of complex inputs are
-    dL/dRe + i dL/dIm. Returns a dict: du, d_dt_raw, dz (B, D, L) (dz None
-    without z), dA (D, N) complex, dD, d_dt_bias (D,), dB, dC (B, L, N) complex
-    and dh0 (B, D, N) complex."""
+    for the complex-state scan (scan_cplx, zoh as there). Gradients of complex
+    inputs are dL/dRe + i dL/dIm. Returns a dict: du, d_dt_raw, dz (B, D, L)
+    (dz None without z), dA (D, N) complex, dD, d_dt_bias (D,), dB, dC
+    (B, L, N) complex and dh0 (B, D, N) complex."""
     lib = _load()
     u, dt_raw, z, dout = _f64(u), _f64(dt_raw), _f64(z), _f64(dout)
     dt_bias, Dskip = _f64(dt_bias), _f64(Dskip)
@@ -398,7 +398,7 @@ def scan_cplx_bwd(u, dt_raw, A, Bm, Cm, dout, *, z=None, dt_bias=None, Dskip=Non
         Bt * D, L, N, Bt, D, _ptr(rb), _ptr(rd), _ptr(u), _ptr(dt_raw), _ptr(z), _ptr(dt_bias), _ptr(Ai),
         _ptr(Dskip), _ptr(Bi), _ptr(Ci), _ptr(reset), _ptr(h0i), _ptr(dout), _ptr(dhi), _ptr(out["du"]),
         _ptr(out["d_dt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dD"]), _ptr(out["d_dt_bias"]),
-        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(nthreads))
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dh0"]), int(bool(zoh)), int(nthreads))
     if rc != 0:
         raise MemoryError("oracle complex backward: scratch allocation failed")
     for k in ("dA", "dB", "dC", "dh0"):

@@ -462,7 +462,7 @@ int oracle_scan_cplx_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int
                               const uint8_t* reset, const double* h0, const double* dout,
                               const double* dh_last, double* du, double* d_dt_raw, double* dz,
                               double* dA, double* dD, double* d_dt_bias, double* dB, double* dC,
-                              double* dh0, int nthreads) {
+                              double* dh0, int zoh, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
   const int T = omp_get_max_threads();
@@ -513,7 +513,7 @@ int oracle_scan_cplx_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int
             const double complex Bn = Bm[2 * (bt * N + n)] + I * Bm[2 * (bt * N + n) + 1];
             const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
             const double complex hp = rs ? 0.0 : hist[t * N + n];
-            const double complex h = cexp(delta * An) * hp + delta * Bn * uu;
+            const double complex h = cexp(delta * An) * hp + bcoef_c(delta, An, zoh) * Bn * uu;
             hist[(t + 1) * N + n] = h;
             acc_y += Cn * h;
           }
@@ -542,18 +542,31 @@ int oracle_scan_cplx_bwd_rows(int64_t R, int64_t L, int64_t N, int64_t Btot, int
             const double complex Cn = Cm[2 * (bt * N + n)] + I * Cm[2 * (bt * N + n) + 1];
             const double complex hp = rs ? 0.0 : hist[t * N + n];
             const double complex a = cexp(delta * An);
+            /* input coefficient phi (delta, or (e^{delta A} - 1)/A with the
+             * zero-order hold) and its derivatives: d phi/d delta = 1 or a;
+             * d phi/dA = (delta a A - (e^{delta A} - 1))/A^2 = (delta a - phi)/A,
+             * by its series delta^2 (1/2 + x/3 + x^2/8 + x^3/30) for
+             * |x| < 1e-3, x = delta A */
+            const double complex phi = bcoef_c(delta, An, zoh);
+            double complex dphi_dd = 1.0, dphi_dA = 0.0;
+            if (zoh) {
+              const double complex x = delta * An;
+              dphi_dd = a;
+              dphi_dA = cabs(x) < 1e-3 ? delta * delta * (0.5 + x * (1.0 / 3.0 + x * (0.125 + x / 30.0)))
+                                       : (delta * a - phi) / An;
+            }
             g[n] += dy * conj(Cn);
             const double complex gC = dy * conj(hist[(t + 1) * N + n]);
-            const double complex gB = delta * uu * g[n];
-            const double complex gA = delta * g[n] * conj(a * hp);
+            const double complex gB = uu * conj(phi) * g[n];
+            const double complex gA = g[n] * conj(delta * a * hp + dphi_dA * Bn * uu);
             mC[2 * (bt * N + n)] += creal(gC);
             mC[2 * (bt * N + n) + 1] += cimag(gC);
             mB[2 * (bt * N + n)] += creal(gB);
             mB[2 * (bt * N + n) + 1] += cimag(gB);
             mA[2 * (d * N + n)] += creal(gA);
             mA[2 * (d * N + n) + 1] += cimag(gA);
-            ddelta += creal(conj(g[n]) * (An * a * hp + Bn * uu));
-            du_t += delta * creal(conj(g[n]) * Bn);
+            ddelta += creal(conj(g[n]) * (An * a * hp + Bn * uu * dphi_dd));
+            du_t += creal(conj(g[n]) * phi * Bn);
             g[n] = rs ? 0.0 : conj(a) * g[n];
           }
           du[r * L + t] = du_t;
