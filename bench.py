@@ -341,7 +341,10 @@ def main():
     bcx = binding.prepare_scan_bwd(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], doutc, dt_bias=tc["dt_bias"],
                                    Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True)
     xsec_b = timed(bcx, bsteps)
-    del fcx, fcz, bcx, doutc, tc, xc
+    bcz = binding.prepare_scan_bwd(tc["u"], tc["dt_raw"], tc["A"], tc["Bm"], tc["Cm"], doutc, dt_bias=tc["dt_bias"],
+                                   Dskip=tc["Dskip"], z=tc["z"], reset=tc["reset"], complex_state=True, zoh=True)
+    xsec_bz = timed(bcz, bsteps)
+    del fcx, fcz, bcx, bcz, doutc, tc, xc
     yc = wl.make_cplx_decode_inputs(Bd, Dd, Nd, wl.BF16, seed=5)
     tdc = {k: wl.to_torch(yc[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
     hdc = torch.from_numpy(yc["h"]).to(dev)
@@ -432,7 +435,7 @@ def main():
                           "fwd_elements_per_s": elements / xsec_f,
                           "zoh_fwd_ms": xsec_z * 1e3,
                           "bwd_ms": xsec_b * 1e3, "bwd_vs_complex_forward": xsec_b / xsec_f,
-                          "bwd_elements_per_s": elements / xsec_b,
+                          "bwd_elements_per_s": elements / xsec_b, "zoh_bwd_ms": xsec_bz * 1e3,
                           "decode_workload": "state update B=64 D=2048 N=128 complex, bf16 inputs, fp32 state",
                           "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes,
                           "decode_hbm_gbps": xdbytes / xsec_d / 1e9},

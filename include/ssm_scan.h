@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10600 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10700 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -107,9 +107,8 @@ typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
  *                     gate, resets and optional conv stage. It is supported in
  *                     ssm_scan_fwd (whose workspace then holds complex
  *                     aggregates; ask ssm_scan_workspace_size with state_kind
- *                     set), ssm_state_update and, with SSM_DISC_DELTA_B,
- *                     ssm_scan_bwd; its backward with SSM_DISC_ZOH returns
- *                     SSM_ERR_UNSUPPORTED.
+ *                     set), ssm_scan_aggregate, ssm_state_update and
+ *                     ssm_scan_bwd.
  * Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 
@@ -301,7 +300,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *   conv_w, conv_b, conv_state_in, conv_width : the forward's conv arguments
  *   dconv_w (D,K), dconv_b (D), dconv_state_in (B,D,K-1) float32 outputs,
  *                     NULL => not written
- * Complex state (state_kind = SSM_STATE_COMPLEX, SSM_DISC_DELTA_B):
+ * Complex state (state_kind = SSM_STATE_COMPLEX):
  * A, Bm, Cm, h0, dh_last and dA, dBm, dCm, dh0 gain a trailing (re, im)
  * dimension of 2, as in the forward. The loss's h_last term is
  * sum (Re dh_last Re h_last + Im dh_last Im h_last), and the gradient of a
@@ -312,7 +311,12 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *   du_t = dy_t D + delta_t Re sum_n conj(G_t) B_t,
  *   d dt_raw_t = Re(sum_n conj(G_t) (A a_t h_{t-1} + B_t u_t)) sigmoid(..),
  *   dh0 = conj(a_0) G_0,
- * and y_t in dz_t is the real read-out Re sum_n C_t h_t + D u_t.
+ * and y_t in dz_t is the real read-out Re sum_n C_t h_t + D u_t. With
+ * SSM_DISC_ZOH the input coefficient delta becomes q = (e^{delta A} - 1)/A:
+ *   dB = sum_d u_t conj(q_t) G_t,   du_t = dy_t D + Re sum_n conj(G_t) q_t B_t,
+ *   d dt_raw_t gains Re sum_n conj(G_t) a_t B_t u_t in place of the B_t u_t
+ *   term (d q/d delta = a), and dA gains u_t G_t conj(dq/dA B_t),
+ *   dq/dA = (delta a_t - q_t)/A.
  * Outputs must not overlap each other, the inputs or the workspace. Shared
  * gradients (dA, dBm, dCm, dDskip, d_dt_bias, dconv_w, dconv_b) are sums in a
  * fixed order, so repeated calls give identical bits.
@@ -351,7 +355,7 @@ typedef struct {
   float* dconv_state_in;
   int32_t conv_width;
   int32_t discretization; /* ssm_discretization */
-  int32_t state_kind;     /* ssm_state_kind (complex: SSM_DISC_DELTA_B only) */
+  int32_t state_kind;     /* ssm_state_kind */
   int32_t reserved1;      /* set to 0 */
 } ssm_scan_bwd_params;
 

@@ -265,14 +265,7 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_params* p, ScanSizes* sz) {
   return check_scan_sizes(&f, sz);
 }
 
-// The complex-state backward is built for the delta B form only.
-ssm_status check_bwd_kind(const ssm_scan_bwd_params* p) {
-  const ssm_status s = check_kind(p->state_kind);
-  if (s != SSM_OK) return s;
-  if (p->state_kind == SSM_STATE_COMPLEX && p->discretization != SSM_DISC_DELTA_B)
-    return fail(SSM_ERR_UNSUPPORTED, "the complex-state backward supports only SSM_DISC_DELTA_B");
-  return SSM_OK;
-}
+ssm_status check_bwd_kind(const ssm_scan_bwd_params* p) { return check_kind(p->state_kind); }
 
 // Complex state: checkpoints every 16 / NPL steps and complex aggregates,
 // checkpoints and partials (two floats per value).

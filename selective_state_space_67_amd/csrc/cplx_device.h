@@ -100,6 +100,46 @@ __device__ __forceinline__ void decay(float dl, const CState& q, float& are, flo
   aim = e * s;
 }
 
+// The exact zero-order-hold input coefficient q = (e^{delta A} - 1)/A of one
+// state, from its decay a = e^{delta A} = (are, aim): (a - 1) times the
+// precomputed 1/A where |delta A| >= 1/16, and below that, where a - 1 would
+// cancel, the series delta (1 + x/2 + x^2/6 + x^3/24), x = delta A
+// (truncation below 1.3e-7). A = 0 gives delta.
+__device__ __forceinline__ void zoh_coef_c(float dl, const CState& q, float are, float aim, float& qr, float& qi) {
+  const float xr = dl * q.re, xi = dl * q.im;
+  float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
+  const float tr = __builtin_fmaf(pr, xr, -pi * xi) + 0.5f, ti = __builtin_fmaf(pr, xi, pi * xr);
+  pr = __builtin_fmaf(tr, xr, -ti * xi) + 1.0f;
+  pi = __builtin_fmaf(tr, xi, ti * xr);
+  const float mr = are - 1.0f, mi = aim;
+  const bool small = xr * xr + xi * xi < 1.0f / 256.0f;
+  qr = small ? dl * pr : __builtin_fmaf(mr, q.ir, -mi * q.ii);
+  qi = small ? dl * pi : __builtin_fmaf(mr, q.ii, mi * q.ir);
+}
+
+// d q / dA for the zero-order hold, q as above: (delta a - q)/A for
+// |delta A| >= 1/2, below that delta^2 sum_k (k+1)/(k+2)! x^k through x^7
+// (truncation below 1e-8), x = delta A.
+__device__ __forceinline__ void zoh_dq_dA(float dl, const CState& q, float are, float aim, float qr, float qi,
+                                          float& kr, float& ki) {
+  const float xr = dl * q.re, xi = dl * q.im;
+  constexpr float c[8] = {0.5f, 1.0f / 3.0f, 0.125f, 1.0f / 30.0f, 1.0f / 144.0f, 1.0f / 840.0f, 1.0f / 5760.0f,
+                          1.0f / 45360.0f};
+  float sr = c[7], si = 0.0f;
+#pragma unroll
+  for (int k = 6; k >= 0; --k) {  // s <- s x + c_k
+    const float nr = __builtin_fmaf(sr, xr, __builtin_fmaf(-si, xi, c[k]));
+    const float ni = __builtin_fmaf(sr, xi, si * xr);
+    sr = nr;
+    si = ni;
+  }
+  const float d2 = dl * dl;
+  const float er = __builtin_fmaf(dl, are, -qr), ei = __builtin_fmaf(dl, aim, -qi);  // delta a - q
+  const bool small = xr * xr + xi * xi < 0.25f;
+  kr = small ? d2 * sr : __builtin_fmaf(er, q.ir, -ei * q.ii);
+  ki = small ? d2 * si : __builtin_fmaf(er, q.ii, ei * q.ir);
+}
+
 // One complex value stored as an (re, im) pair of the input type, widened.
 __device__ __forceinline__ float2 load_cpair(const float* p, int64_t n) {
   return *reinterpret_cast<const float2*>(p + 2 * n);

@@ -79,11 +79,8 @@ struct CplxArgs {
 };
 
 // One step of a state: h = exp(delta A) h + q u B with the input coefficient
-// q = delta, or with the zero-order hold q = (exp(delta A) - 1) / A; returns
-// Re(C h). dv is delta u (or u with the zero-order hold). The zero-order hold
-// forms q from exp(delta A) - 1 times the precomputed 1/A where |delta A| >=
-// 1/16, and below that, where the difference would cancel, from the series
-// delta (1 + x/2 + x^2/6 + x^3/24), x = delta A (truncation below 1.3e-7).
+// q = delta, or with the zero-order hold q = (exp(delta A) - 1) / A
+// (zoh_coef_c); returns Re(C h). dv is delta u (or u with the zero-order hold).
 template <bool ZOH>
 __device__ __forceinline__ float cplx_step(float dl, float dv, const CState& q, float2 Bv, float2 Cv, float& hr,
                                            float& hi) {
@@ -91,16 +88,8 @@ __device__ __forceinline__ float cplx_step(float dl, float dv, const CState& q, 
   decay(dl, q, are, aim);
   float br = Bv.x * dv, bi = Bv.y * dv;
   if constexpr (ZOH) {
-    const float xr = dl * q.re, xi = dl * q.im;
-    // series: p = ((x/24 + 1/6) x + 1/2) x + 1, complex Horner
-    float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
-    float tr = __builtin_fmaf(pr, xr, -pi * xi) + 0.5f, ti = __builtin_fmaf(pr, xi, pi * xr);
-    pr = __builtin_fmaf(tr, xr, -ti * xi) + 1.0f;
-    pi = __builtin_fmaf(tr, xi, ti * xr);
-    const float mr = are - 1.0f, mi = aim;  // exp(delta A) - 1
-    const bool small = xr * xr + xi * xi < 1.0f / 256.0f;
-    const float qr = small ? dl * pr : __builtin_fmaf(mr, q.ir, -mi * q.ii);
-    const float qi = small ? dl * pi : __builtin_fmaf(mr, q.ii, mi * q.ir);
+    float qr, qi;
+    zoh_coef_c(dl, q, are, aim, qr, qi);
     br = dv * __builtin_fmaf(qr, Bv.x, -qi * Bv.y);
     bi = dv * __builtin_fmaf(qr, Bv.y, qi * Bv.x);
   }

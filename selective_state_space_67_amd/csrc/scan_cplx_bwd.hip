@@ -108,9 +108,10 @@ struct CplxBwdArgs {
 };
 
 // Stages step t of this lane's channel: takes the scan input u_t, loads
-// dt_raw, z and dout and forms delta (negated on a reset step), delta u and
+// dt_raw, z and dout and forms delta (negated on a reset step), delta u (u
+// with the zero-order hold, whose coefficient depends on the state) and
 // dy = dout silu(z).
-template <typename InT, bool HAS_RESET>
+template <typename InT, bool HAS_RESET, bool ZOH>
 struct StepInputs {
   float dl = 0.0f, uu = 0.0f, sgx = 0.0f, go = 0.0f, zz = 0.0f, dy = 0.0f;
   bool reset = false;
@@ -129,7 +130,7 @@ struct StepInputs {
     if (HAS_RESET) reset = rs[t] != 0;
   }
   __device__ __forceinline__ float4 staged() const {
-    return make_float4(reset ? -dl : dl, dl * uu, dy, 0.0f);
+    return make_float4(reset ? -dl : dl, ZOH ? uu : dl * uu, dy, 0.0f);
   }
 };
 
@@ -146,7 +147,7 @@ __device__ __forceinline__ void stage_bc(float4* s_bc, const InT* Bb, const InT*
   }
 }
 
-template <int NPL, typename InT, bool HAS_RESET, bool CONV>
+template <int NPL, typename InT, bool HAS_RESET, bool CONV, bool ZOH>
 __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a) {
   constexpr int NPAD = 16 * NPL;
   constexpr int KC = 16 / NPL;
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
     const int steps = min(kT, Lseg - t0);
     __syncthreads();  // the previous chunk's readers are done
     stage_bc<NPAD>(s_bc, Bb + static_cast<int64_t>(t0) * N * 2, Cb + static_cast<int64_t>(t0) * N * 2, steps, N, tid);
-    StepInputs<InT, HAS_RESET> in;
+    StepInputs<InT, HAS_RESET, ZOH> in;
     if (dvalid && k < steps) {
       float ut;
       if constexpr (CONV) {  // the scan input u' = silu(conv(u)), kept for the reverse sweep
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
     s_st[c * kT + k] = in.staged();
     __syncthreads();
 
-#pragma unroll 4
+    // (one step at a time for 16 states per lane: their registers leave no room to unroll)
+#pragma unroll (NPL >= 16 ? 1 : 4)
     for (int tl = 0; tl < kT; ++tl) {
       const int64_t tg = t_seg + t0 + tl;
       if (tl % KC == 0 && dvalid && tl < steps) {  // the state entering step tg
@@ -255,8 +257,15 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
         const float4 bc = s_bc[tl * NPAD + n0 + j];
         float ar, ai;
         decay(dl, cq[j], ar, ai);
-        const float nr = __builtin_fmaf(ar, hr[j], __builtin_fmaf(-ai, hi[j], st.y * bc.x));
-        const float ni = __builtin_fmaf(ar, hi[j], __builtin_fmaf(ai, hr[j], st.y * bc.y));
+        float br = st.y * bc.x, bi = st.y * bc.y;  // the input term (delta u B, or u q B)
+        if constexpr (ZOH) {
+          float qr, qi;
+          zoh_coef_c(dl, cq[j], ar, ai, qr, qi);
+          br = st.y * __builtin_fmaf(qr, bc.x, -qi * bc.y);
+          bi = st.y * __builtin_fmaf(qr, bc.y, qi * bc.x);
+        }
+        const float nr = __builtin_fmaf(ar, hr[j], __builtin_fmaf(-ai, hi[j], br));
+        const float ni = __builtin_fmaf(ar, hi[j], __builtin_fmaf(ai, hr[j], bi));
         hr[j] = nr;
         hi[j] = ni;
         const float pr = __builtin_fmaf(ar, qr[j], -ai * qi[j]);
@@ -292,8 +301,9 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
   }
 }
 
-template <int NPL, typename InT, bool HAS_RESET>
-__global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs a) {
+// Two waves per SIMD; the zero-order hold's extra per-state terms run at one.
+template <int NPL, typename InT, bool HAS_RESET, bool ZOH>
+__global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const CplxBwdArgs a) {
   constexpr int NPAD = 16 * NPL;
   constexpr int KC = 16 / NPL;                     // steps per checkpoint block
   constexpr int F = NPAD >= 64 ? 1 : 64 / NPAD;    // steps per flush of the channel sums
@@ -315,12 +325,13 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
   __shared__ __align__(16) float4 s_st[kCPW * kT];
   // per (flush slot, channel, state): (dB.re, dB.im, dC.re, dC.im) of one step
   __shared__ __align__(16) float4 s_dbc[F * kCPW * NPAD];
-  // The three per-step partial sums over a lane's states, [sum][channel][step
-  // of the block][lane]; the lane that owns a step adds its row's 16 partials
-  // after the block. Channels are PS floats apart (the rows of a wave write
-  // to different banks).
+  // The per-step partial sums over a lane's states (three, four with the
+  // zero-order hold), [sum][channel][step of the block][lane]; the lane that
+  // owns a step adds its row's 16 partials after the block. Channels are PS
+  // floats apart (the rows of a wave write to different banks).
   constexpr int PS = KC * 16 + 16;
-  __shared__ __align__(16) float s_p[3 * kCPW * PS];
+  constexpr int NS = ZOH ? 4 : 3;
+  __shared__ __align__(16) float s_p[NS * kCPW * PS];
 
   CState cq[NPL];
   load_A<NPL>(a.A, d, N, n0, dvalid, cq);
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
     const int steps = static_cast<int>(min<int64_t>(kT, a.L - t0));
     __syncthreads();  // the previous chunk's readers are done
     stage_bc<NPAD>(s_bc, Bb + t0 * N * 2, Cb + t0 * N * 2, steps, N, tid);
-    StepInputs<InT, HAS_RESET> in;
+    StepInputs<InT, HAS_RESET, ZOH> in;
     const bool live = dvalid && k < steps;
     if (live) {
       const int t = static_cast<int>(t0) + k;
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
     s_st[c * kT + k] = in.staged();
     __syncthreads();
 
-    float m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;  // the row sums of this lane's step
+    float m1 = 0.0f, m2 = 0.0f, m3 = 0.0f, m4 = 0.0f;  // the row sums of this lane's step
 #pragma unroll 1
     for (int tb = kT - KC; tb >= 0; tb -= KC) {
       if (tb >= steps) continue;  // the whole block lies past L: the adjoint passes unchanged
@@ -414,8 +425,15 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
           const float wi = __builtin_fmaf(ar, hi[j], ai * hr[j]);
           ha[i][j] = make_float2(ar, ai);
           hw[i][j] = make_float2(wr, wi);
-          hr[j] = __builtin_fmaf(st.y, bc.x, wr);
-          hi[j] = __builtin_fmaf(st.y, bc.y, wi);
+          float br = bc.x, bi = bc.y;  // B, or q B with the zero-order hold
+          if constexpr (ZOH) {
+            float qr, qi;
+            zoh_coef_c(dl, cq[j], ar, ai, qr, qi);
+            br = __builtin_fmaf(qr, bc.x, -qi * bc.y);
+            bi = __builtin_fmaf(qr, bc.y, qi * bc.x);
+          }
+          hr[j] = __builtin_fmaf(st.y, br, wr);
+          hi[j] = __builtin_fmaf(st.y, bi, wi);
         }
       }
       // the adjoint back through the block
@@ -423,24 +441,48 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
       for (int i = KC - 1; i >= 0; --i) {
         const float4 st = s_st[c * kT + tb + i];
         const float dl = fabsf(st.x), dv = st.y, dy = st.z;
-        float p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+        float p1 = 0.0f, p2 = 0.0f, p3 = 0.0f, p4 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           const float4 bc = s_bc[(tb + i) * NPAD + n0 + j];
           const float gr = __builtin_fmaf(dy, bc.z, xr[j]);  // G = X + dy conj(C)
           const float gi = __builtin_fmaf(-dy, bc.w, xi[j]);
           const float2 w = hw[i][j];
-          const float hr2 = __builtin_fmaf(dv, bc.x, w.x);  // h_t
-          const float hi2 = __builtin_fmaf(dv, bc.y, w.y);
+          const float2 av = ha[i][j];
+          float dbr, dbi;  // dB term
+          float hr2, hi2;  // h_t
+          if constexpr (ZOH) {
+            // input term u q B: d/d delta through q is a, d/dA is dq/dA
+            float qr, qi, kr, ki;
+            zoh_coef_c(dl, cq[j], av.x, av.y, qr, qi);
+            zoh_dq_dA(dl, cq[j], av.x, av.y, qr, qi, kr, ki);
+            const float qbr = __builtin_fmaf(qr, bc.x, -qi * bc.y), qbi = __builtin_fmaf(qr, bc.y, qi * bc.x);
+            hr2 = __builtin_fmaf(dv, qbr, w.x);
+            hi2 = __builtin_fmaf(dv, qbi, w.y);
+            p1 = __builtin_fmaf(gr, qbr, __builtin_fmaf(gi, qbi, p1));  // Re conj(G) q B
+            const float abr = __builtin_fmaf(av.x, bc.x, -av.y * bc.y), abi = __builtin_fmaf(av.x, bc.y, av.y * bc.x);
+            p4 = __builtin_fmaf(gr, abr, __builtin_fmaf(gi, abi, p4));  // Re conj(G) a B
+            const float mr = dv * __builtin_fmaf(kr, bc.x, -ki * bc.y);  // M = u (dq/dA) B
+            const float mi = dv * __builtin_fmaf(kr, bc.y, ki * bc.x);
+            dar[j] = __builtin_fmaf(gr, mr, __builtin_fmaf(gi, mi, dar[j]));  // += G conj(M)
+            dai[j] = __builtin_fmaf(gi, mr, __builtin_fmaf(-gr, mi, dai[j]));
+            dbr = dv * __builtin_fmaf(qr, gr, qi * gi);  // u conj(q) G
+            dbi = dv * __builtin_fmaf(qr, gi, -qi * gr);
+          } else {
+            hr2 = __builtin_fmaf(dv, bc.x, w.x);
+            hi2 = __builtin_fmaf(dv, bc.y, w.y);
+            p1 = __builtin_fmaf(gr, bc.x, __builtin_fmaf(gi, bc.y, p1));  // Re conj(G) B
+            dbr = dv * gr;
+            dbi = dv * gi;
+          }
           const float er = __builtin_fmaf(gr, w.x, gi * w.y);  // E = G conj(a h_{t-1})
           const float ei = __builtin_fmaf(gi, w.x, -gr * w.y);
           dar[j] = __builtin_fmaf(dl, er, dar[j]);
           dai[j] = __builtin_fmaf(dl, ei, dai[j]);
-          p1 = __builtin_fmaf(gr, bc.x, __builtin_fmaf(gi, bc.y, p1));        // Re conj(G) B
           p2 = __builtin_fmaf(cq[j].re, er, __builtin_fmaf(cq[j].im, ei, p2));  // Re conj(G) A a h_{t-1}
           p3 = __builtin_fmaf(bc.z, hr2, __builtin_fmaf(-bc.w, hi2, p3));     // Re C h
-          s_dbc[((i % F) * kCPW + c) * NPAD + n0 + j] = make_float4(dv * gr, dv * gi, dy * hr2, -dy * hi2);
-          const float2 av = ha[i][j];  // X <- conj(a) G; 0 across a reset
+          s_dbc[((i % F) * kCPW + c) * NPAD + n0 + j] = make_float4(dbr, dbi, dy * hr2, -dy * hi2);
+          // X <- conj(a) G; 0 across a reset
           const float nr = __builtin_fmaf(av.x, gr, av.y * gi);
           const float ni = __builtin_fmaf(av.x, gi, -av.y * gr);
           const bool r = HAS_RESET && __float_as_int(st.x) < 0;
@@ -451,6 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
         pp[0] = p1;
         pp[kCPW * PS] = p2;
         pp[2 * kCPW * PS] = p3;
+        if constexpr (ZOH) pp[3 * kCPW * PS] = p4;
         if (i % F == 0) {  // add the F steps' dB and dC over the 16 channels
           __syncthreads();
           const float* sd = reinterpret_cast<const float*>(s_dbc);
@@ -472,9 +515,9 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
       __builtin_amdgcn_wave_barrier();
       const int mi = k - tb;
       if (mi >= 0 && mi < KC) {
-        float m[3];
+        float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
+        for (int q = 0; q < NS; ++q) {
           const float4* r = reinterpret_cast<const float4*>(s_p + q * kCPW * PS + c * PS + mi * 16);
           const float4 y0 = r[0], y1 = r[1], y2 = r[2], y3 = r[3];
           m[q] = ((y0.x + y0.y) + (y0.z + y0.w)) + ((y1.x + y1.y) + (y1.z + y1.w)) +
@@ -483,12 +526,15 @@ __global__ __launch_bounds__(kThreads, 2) void cplx_bwd_kernel(const CplxBwdArgs
         m1 = m[0];
         m2 = m[1];
         m3 = m[2];
+        m4 = m[3];
       }
       __builtin_amdgcn_wave_barrier();
     }
     if (live) {
-      const float du = __builtin_fmaf(in.dl, m1, dsk * in.dy);
-      const float ddt = __builtin_fmaf(in.uu, m1, m2) * in.sgx;
+      // du = Re sum conj(G) (q B, or delta B); d delta = Re sum conj(G) A a h_{t-1}
+      // + u Re sum conj(G) (a B, or B)
+      const float du = __builtin_fmaf(ZOH ? 1.0f : in.dl, m1, dsk * in.dy);
+      const float ddt = __builtin_fmaf(in.uu, ZOH ? m4 : m1, m2) * in.sgx;
       const int64_t o = row * a.L + t0 + k;
       if (a.du_conv)  // the gradient of u', which the conv backward turns into du
         a.du_conv[o] = du;
@@ -629,20 +675,23 @@ hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream
   const dim3 grid_bwd(static_cast<unsigned>(cplx_bwd_grid_blocks(bp.B, bp.D, bp.nsegb)));
   e = with_npl(bp.N, [&](auto npl) {
     constexpr int NPL = decltype(npl)::value;
-    auto run = [&](auto in_t, auto has_reset) {
+    auto run = [&](auto in_t, auto has_reset, auto zoh) {
       using InT = decltype(in_t);
-      constexpr bool R = decltype(has_reset)::value;
+      constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
       if (bp.conv_w)
-        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, true>), grid_ck, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, true, Z>), grid_ck, dim3(kThreads), 0, stream, a);
       else
-        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, false>), grid_ck, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, false, Z>), grid_ck, dim3(kThreads), 0, stream, a);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((cplx_bwd_kernel<NPL, InT, R>), grid_bwd, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((cplx_bwd_kernel<NPL, InT, R, Z>), grid_bwd, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };
-    if (bp.in_bf16) return bp.reset ? run(bf16_t{}, std::true_type{}) : run(bf16_t{}, std::false_type{});
-    return bp.reset ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
+    auto with_zoh = [&](auto in_t, auto has_reset) {
+      return bp.zoh ? run(in_t, has_reset, std::true_type{}) : run(in_t, has_reset, std::false_type{});
+    };
+    if (bp.in_bf16) return bp.reset ? with_zoh(bf16_t{}, std::true_type{}) : with_zoh(bf16_t{}, std::false_type{});
+    return bp.reset ? with_zoh(float{}, std::true_type{}) : with_zoh(float{}, std::false_type{});
   });
   if (e != hipSuccess) return e;
   e = launch_bwd_reduce(a.partB, a.partC, a.partA, a.partD, a.partBias, bp.dB, bp.dC, bp.dA, bp.dD, bp.dbias, bln2,

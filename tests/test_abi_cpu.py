@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10600
+    assert lib.ssm_version() == 10700
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -368,14 +368,6 @@ def test_unknown_state_kind(lib):
     assert update_status(lib, update_params(state_kind=-1)) == 5
     n = ctypes.c_size_t(0)
     assert lib.ssm_scan_workspace_size(ctypes.byref(scan_params(state_kind=3)), ctypes.byref(n)) == 5
-
-
-def test_complex_state_unsupported_combinations(lib):
-    # the complex backward has no zero-order hold
-    assert bwd_status(lib, bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)) == 5
-    n = ctypes.c_size_t(0)
-    q = bwd_params(cplx=True, discretization=bd.SSM_DISC_ZOH)
-    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(q), ctypes.byref(n)) == 5
 
 
 def test_complex_state_conv_arguments_checked(lib):

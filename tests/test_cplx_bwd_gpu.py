@@ -58,7 +58,7 @@ def make_case(B, D, L, N, dtype, seed, *, with_z=True, with_bias=True, with_D=Tr
     return x
 
 
-def gpu_bwd(x, grad_bf16=False):
+def gpu_bwd(x, grad_bf16=False, zoh=False):
     import torch
 
     from selective_state_space_67_amd import ssm_scan_bwd
@@ -68,33 +68,33 @@ def gpu_bwd(x, grad_bf16=False):
     f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
     g = ssm_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], t["dout"], dt_bias=t["dt_bias"],
                      Dskip=t["Dskip"], z=t["z"], reset=t["reset"], h0=f32(x["h0"]), dh_last=f32(x["dh_last"]),
-                     grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32, complex_state=True)
+                     grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32, complex_state=True, zoh=zoh)
     torch.cuda.synchronize()
     return {k: (None if g[GPU_KEY[k]] is None else g[GPU_KEY[k]].float().cpu().numpy().astype(np.float64))
             for k in KEYS}
 
 
-def oracle_bwd(x, dt_raw=None):
+def oracle_bwd(x, dt_raw=None, zoh=False):
     w = wl.widen
     return oracle.scan_cplx_bwd(w(x["u"]), w(x["dt_raw"]) if dt_raw is None else dt_raw, wl.as_complex(x["A"]),
                                 wl.as_complex(x["Bm"]), wl.as_complex(x["Cm"]), w(x["dout"]), z=w(x["z"]),
                                 dt_bias=x["dt_bias"], Dskip=x["Dskip"], reset=x["reset"],
-                                h0=wl.as_complex(x["h0"]), dh_last=wl.as_complex(x["dh_last"]))
+                                h0=wl.as_complex(x["h0"]), dh_last=wl.as_complex(x["dh_last"]), zoh=zoh)
 
 
 def as_real(k, v):
     return np.stack([v.real, v.imag], axis=-1) if k in CPLX else v
 
 
-def reference(x):
+def reference(x, zoh=False):
     """The oracle's gradients and the phase term of each (see the module docstring)."""
-    ref = oracle_bwd(x)
+    ref = oracle_bwd(x, zoh=zoh)
     dt = wl.widen(x["dt_raw"])
     D = dt.shape[1]
     xx = dt + (np.zeros(D) if x["dt_bias"] is None else x["dt_bias"].astype(np.float64))[None, :, None]
     delta = np.maximum(xx, 0) + np.log1p(np.exp(-np.abs(xx)))
     sig = 1.0 / (1.0 + np.exp(-xx))
-    per = oracle_bwd(x, dt_raw=dt + EPS_DELTA * delta / sig)
+    per = oracle_bwd(x, dt_raw=dt + EPS_DELTA * delta / sig, zoh=zoh)
     phase = {k: None if ref[k] is None else 2.0 * np.abs(as_real(k, per[k]) - as_real(k, ref[k])) for k in KEYS}
     return ref, phase
 
@@ -260,3 +260,70 @@ def test_conv_backward(K, N, packed):
         o, r = g[gk].cpu().numpy().astype(np.float64), ref[rk]
         bound = TOL * (np.sqrt(np.mean(r * r)) + np.abs(r)) + phase[rk] + 1e-30
         assert np.all(np.abs(o - r) <= bound), (gk, float(np.max(np.abs(o - r) / bound)))
+
+
+# ---- exact zero-order hold: q = (e^{delta A} - 1)/A in place of delta ----
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("B,D,L,N", [(1, 1, 1, 1), (2, 3, 17, 4), (1, 40, 300, 17), (1, 7, 150, 64),
+                                     (2, 9, 80, 128), (1, 4, 50, 256)])
+def test_zoh_shapes(dtype, B, D, L, N):
+    x = make_case(B, D, L, N, dtype, 7000 + B * 1000 + D * 10 + N, h0=True, dh_last=True, dt_hi=3e-1)
+    if N >= 4:  # A = 0 (coefficient delta), purely imaginary, and |A| near the series switches
+        rng = np.random.default_rng(N)
+        x["A"][0, 0] = 0.0
+        if D > 1:
+            x["A"][1, 1, 0] = 0.0
+        if D > 2:
+            x["A"][2, :4, 0] = -rng.uniform(0.3, 0.9, 4)
+            x["A"][2, :4, 1] = rng.uniform(0.3, 0.9, 4)
+    assert_grads(gpu_bwd(x, zoh=True), reference(x, zoh=True), what="zoh B%d D%d L%d N%d %s" % (B, D, L, N, dtype))
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_zoh_resets(N):
+    x = make_case(2, 24, 700, N, wl.BF16, 7070 + N, packed=True, h0=True, dh_last=True)
+    assert_grads(gpu_bwd(x, zoh=True), reference(x, zoh=True), what="zoh resets N%d" % N)
+
+
+def test_zoh_long_sequence_many_segments():
+    x = make_case(1, 16, 40000, 16, wl.BF16, 7013, dt_lo=1e-3, dt_hi=1e-2, h0=True, dh_last=True)
+    assert_grads(gpu_bwd(x, zoh=True), reference(x, zoh=True), what="zoh long")
+
+
+def test_zoh_real_case_matches_real_backward():
+    """Zero imaginary parts: the complex zero-order-hold backward reproduces the real one."""
+    import torch
+
+    from selective_state_space_67_amd import ssm_scan_bwd
+
+    x = wl.make_scan_inputs(2, 48, 400, 16, wl.F32, seed=81, packed=True)
+    x["dout"] = wl.store(np.random.default_rng(82).standard_normal(x["u"].shape), wl.F32)
+    dev = device()
+    t = {k: to_dev(x[k], dev) for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip", "reset", "dout")}
+    real = ssm_scan_bwd(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], t["dout"], dt_bias=t["dt_bias"],
+                        Dskip=t["Dskip"], z=t["z"], reset=t["reset"], zoh=True)
+    cz = lambda v: torch.stack([v, torch.zeros_like(v)], dim=-1).contiguous()
+    cplx = ssm_scan_bwd(t["u"], t["dt_raw"], cz(t["A"]), cz(t["Bm"]), cz(t["Cm"]), t["dout"], dt_bias=t["dt_bias"],
+                        Dskip=t["Dskip"], z=t["z"], reset=t["reset"], complex_state=True, zoh=True)
+    torch.cuda.synchronize()
+    for k in ("du", "d_dt_raw", "dz", "dA", "dBm", "dCm", "dDskip", "d_dt_bias", "dh0"):
+        r = real[k].cpu().numpy().astype(np.float64)
+        c = cplx[k].cpu().numpy().astype(np.float64)
+        if k in ("dA", "dBm", "dCm", "dh0"):
+            assert np.all(c[..., 1] == 0), k
+            c = c[..., 0]
+        bound = TOL * (np.sqrt(np.mean(r * r)) + np.abs(r)) + 1e-30
+        assert np.all(np.abs(c - r) <= bound), (k, float(np.max(np.abs(c - r) / bound)))
+
+
+def test_zoh_workload_full_size():
+    """The mamba130m-layer shape with S4D-Lin A and the zero-order hold, every
+    gradient element against the oracle."""
+    cfg = wl.workload("mamba130m-layer")
+    x = wl.make_cplx_inputs(cfg["B"], cfg["D"], cfg["L"], cfg["N"], cfg["dtype"], seed=cfg["seed"],
+                            dt_lo=cfg["dt_lo"], dt_hi=cfg["dt_hi"])
+    x["dout"] = wl.store(np.random.default_rng(701).standard_normal(x["u"].shape), cfg["dtype"])
+    x["h0"] = None
+    x["dh_last"] = None
+    assert_grads(gpu_bwd(x, zoh=True), reference(x, zoh=True), what="zoh " + cfg["name"])
