@@ -128,7 +128,8 @@ def main():
     ap.add_argument("--workload", default="mamba130m-layer",
                     help="workload name: mamba130m-layer (the default and the headline); tiny-fp32, "
                          "mamba2.8b-layer, long-genomics and packed-docs-n128 print their own line for reference")
-    ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL-evicting write")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the launches timed after an L2/MALL-evicting write")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (for counter calibration runs)")
     args = ap.parse_args()
@@ -179,7 +180,7 @@ def main():
 
     # Cold caches: a 1 GiB write before each launch, outside the timed events.
     cold = []
-    if args.cold:
+    if not args.no_cold:
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         for i in range(min(args.steps, 50)):
             scratch.fill_(float(i))
