@@ -26,19 +26,21 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// sin and cos of the angle delta (ai + ai_lo) revolutions. The product
+// e (cos + i sin) of the angle delta (ai + ai_lo) revolutions. The product
 // p = delta ai is split into p and its exact rounding error; p - rint(p) is
-// exact and lies in [-1/2, 1/2]; q quarter turns are taken off exactly, and
+// exact and lies in [-1/2, 1/2]; k quarter turns are taken off exactly, and
 // the small parts are added to the remainder r, |r| <= 1/8 revolution. Then
 // theta = 2 pi r, sin and cos by their Taylor series through theta^9 and
-// theta^10 (truncation below 2e-9 and 1.2e-10 on |theta| <= pi/4), and a
-// rotation by q quarter turns.
-__device__ __forceinline__ void sincos_rev(float delta, float ai, float ai_lo, float& s, float& c) {
+// theta^10 (truncation below 2e-9 and 1.2e-10 on |theta| <= pi/4), and the
+// k quarter turns as a product with i^k = (1 - |k|) + i k (2 - |k|), k in
+// -2 .. 2, whose parts are 0 or +-1 (so the rotation is exact; e is folded
+// into them first).
+__device__ __forceinline__ void rotate_rev(float e, float delta, float ai, float ai_lo, float& re, float& im) {
   const float p = delta * ai;
   const float lo = __builtin_fmaf(delta, ai, -p) + delta * ai_lo;
   const float f = p - __builtin_rintf(p);
-  const float q = __builtin_rintf(4.0f * f);  // -2 .. 2
-  const float r = __builtin_fmaf(-0.25f, q, f) + lo;
+  const float k = __builtin_rintf(4.0f * f);  // -2 .. 2
+  const float r = __builtin_fmaf(-0.25f, k, f) + lo;
   const float th = r * 6.28318530717958648f;
   const float t2 = th * th;
   float sp = __builtin_fmaf(t2, 2.75573192e-6f, -1.98412698e-4f);
@@ -50,12 +52,10 @@ __device__ __forceinline__ void sincos_rev(float delta, float ai, float ai_lo, f
   cp = __builtin_fmaf(t2, cp, 4.16666667e-2f);
   cp = __builtin_fmaf(t2, cp, -0.5f);
   const float cs = __builtin_fmaf(t2, cp, 1.0f);
-  // (sin, cos) of theta + q pi/2: q = 1 -> (c, -s), 2 -> (-s, -c), 3 (= -1) -> (-c, s)
-  const int qi = static_cast<int>(q) & 3;
-  const float s2 = (qi & 1) ? cs : sn;
-  const float c2 = (qi & 1) ? sn : cs;
-  s = (qi & 2) ? -s2 : s2;
-  c = ((qi + 1) & 2) ? -c2 : c2;
+  const float ak = fabsf(k);
+  const float ec = e * (1.0f - ak), es = e * (k * (2.0f - ak));  // e i^k
+  re = __builtin_fmaf(cs, ec, -sn * es);
+  im = __builtin_fmaf(sn, ec, cs * es);
 }
 
 // Per-lane constants of one state: Re A log2(e) for the decay's magnitude,
@@ -93,11 +93,7 @@ __device__ __forceinline__ void load_A(const float* A, int64_t d, int N, int n0,
 
 // exp(delta A) = 2^(delta Re A log2 e) (cos theta + i sin theta), theta = delta Im A.
 __device__ __forceinline__ void decay(float dl, const CState& q, float& are, float& aim) {
-  const float e = fast_exp2(dl * q.ar);
-  float s, c;
-  sincos_rev(dl, q.ai, q.ai_lo, s, c);
-  are = e * c;
-  aim = e * s;
+  rotate_rev(fast_exp2(dl * q.ar), dl, q.ai, q.ai_lo, are, aim);
 }
 
 // The exact zero-order-hold input coefficient q = (e^{delta A} - 1)/A of one

@@ -259,11 +259,10 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
       for (int j = 0; j < NPL; ++j) {
         if (n0 + j >= N) continue;
         const int64_t w = static_cast<int64_t>(sp) * a.B * a.D * N * 2 + 2 * (row * N + n0 + j);
-        float sn, cs;
-        sincos_rev(S, cq[j].ai, cq[j].ai_lo, sn, cs);
-        const float e = any_reset ? 0.0f : fast_exp2(S * cq[j].ar);
-        a.ws_P[w] = e * cs;
-        a.ws_P[w + 1] = e * sn;
+        float pr, pi;
+        rotate_rev(any_reset ? 0.0f : fast_exp2(S * cq[j].ar), S, cq[j].ai, cq[j].ai_lo, pr, pi);
+        a.ws_P[w] = pr;
+        a.ws_P[w + 1] = pi;
         a.ws_H[w] = hr[j];
         a.ws_H[w + 1] = hi[j];
       }
