@@ -47,6 +47,13 @@
  *    the HIP error text. Faults during execution surface at the caller's next
  *    synchronisation of the stream.
  *  - NaN/Inf inputs propagate by IEEE rules; they are not trapped.
+ *  - Empty problems (B, D or L = 0) are valid: a pointer to an empty tensor
+ *    may be NULL, nothing is scanned, and the outputs that still hold values
+ *    get the empty sequence's: the state passes through it (h_last = h0, or
+ *    0 without h0; conv_state_out = conv_state_in, or 0), its aggregate is
+ *    the identity (P = 1, H = 0), empty sums are 0 (dA, dDskip, d_dt_bias,
+ *    dconv_w, dconv_b over no (b, t); dBm, dCm over no channel), the adjoint passes through (dh0 = dh_last,
+ *    or 0) and dconv_state_in is 0. No workspace is needed.
  *  - The library is re-entrant; its only global mutable state is the
  *    thread-local text returned by ssm_last_error().
  */
@@ -60,14 +67,14 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10700 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10800 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL_POINTER = 1, /* a required pointer (or params itself) is NULL   */
-  SSM_ERR_BAD_SHAPE = 2,    /* a size is < 1, N > SSM_MAX_DSTATE, L >= 2^27, or
-                               an element count overflows int64                */
+  SSM_ERR_BAD_SHAPE = 2,    /* a size is < 0, N < 1, N > SSM_MAX_DSTATE,
+                               L >= 2^27, or an element count overflows int64  */
   SSM_ERR_BAD_DTYPE = 3,    /* in_dtype / out_dtype is not an ssm_dtype         */
   SSM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size    */
   SSM_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement   */
@@ -115,7 +122,7 @@ typedef enum { SSM_STATE_REAL = 0, SSM_STATE_COMPLEX = 1 } ssm_state_kind;
 /*
  * Full-sequence scan (prefill / training forward).
  *
- *   batch, dim, seqlen, dstate : B, D, L, N;  B, D >= 1, 1 <= L < 2^27, 1 <= N <= 256
+ *   batch, dim, seqlen, dstate : B, D, L, N;  B, D >= 0, 0 <= L < 2^27, 1 <= N <= 256
  *   in_dtype  : element type of u, dt_raw, z, Bm, Cm (SSM_F32 or SSM_BF16)
  *   out_dtype : element type of out (SSM_F32 or SSM_BF16)
  *   u        (B,D,L)  required; the SSM input x (L contiguous)
@@ -218,7 +225,7 @@ ssm_status ssm_scan_aggregate_workspace_size(const ssm_scan_params* p, size_t* b
  * Single-token decode step: one application of the recurrence to a stored
  * state, in place.
  *
- *   batch, dim, dstate : B, D, N;  B, D >= 1, 1 <= N <= 256
+ *   batch, dim, dstate : B, D, N;  B, D >= 0, 1 <= N <= 256
  *   h        (B,D,N)  float32, required; read as h_{t-1}, overwritten with h_t.
  *                     To start a new sequence the caller zeroes that row.
  *   u, dt_raw (B,D)   required; z (B,D) NULL => no gate
@@ -294,7 +301,7 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream);
  *                     those inputs are given (an absent input acts as 0).
  *   dh0      (B,D,N)  float32 output, NULL => not written
  *   workspace, workspace_bytes : at least ssm_scan_bwd_workspace_size() bytes
- *                     (never 0 for the backward); contents on entry ignored.
+ *                     (0 only for an empty problem); contents on entry ignored.
  * Conv input stage (conv_w != NULL, as in ssm_scan_params): u is the conv
  * input x; du is the gradient of x, and
  *   conv_w, conv_b, conv_state_in, conv_width : the forward's conv arguments

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_fwd_f32_plain.hip", "scan_fwd_f32_reset.hip", "scan_fwd_bf16_plain.hip",
            "scan_fwd_bf16_reset.hip", "scan_bwd.hip", "state_update.hip", "scan_cplx.hip",
-           "scan_cplx_bwd.hip"]
+           "scan_cplx_bwd.hip", "fill.hip"]
 OUT = os.path.join(HERE, "libssmscan.so")
 OBJ = os.path.join(ROOT, "_build")
 ARCH = "gfx950"

@@ -72,11 +72,12 @@ Range range(const void* p, int64_t count, size_t esize, const char* name) {
 // Sizes of a scan, checked for range and overflow.
 struct ScanSizes {
   int64_t bdl, bln, dn, bdn, bl;
+  bool empty() const { return bdl == 0; }  // no (b, d, t): nothing is scanned
 };
 
 ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
-  if (p->batch < 1 || p->dim < 1 || p->seqlen < 1)
-    return fail(SSM_ERR_BAD_SHAPE, "batch, dim and seqlen must be >= 1 (got %lld, %lld, %lld)",
+  if (p->batch < 0 || p->dim < 0 || p->seqlen < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "batch, dim and seqlen must be >= 0 (got %lld, %lld, %lld)",
                 (long long)p->batch, (long long)p->dim, (long long)p->seqlen);
   if (p->dstate < 1 || p->dstate > SSM_MAX_DSTATE)
     return fail(SSM_ERR_BAD_SHAPE, "dstate must be in [1, %d] (got %lld)", SSM_MAX_DSTATE,
@@ -95,6 +96,12 @@ ssm_status check_scan_sizes(const ssm_scan_params* p, ScanSizes* sz) {
 
 ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
   if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
+  if (p->batch == 0 || p->dim == 0 || p->seqlen == 0) {  // empty: no launch, no workspace
+    *nseg = 1;
+    *seg_len = p->seqlen;
+    *ws = 0;
+    return SSM_OK;
+  }
   if (p->state_kind == SSM_STATE_COMPLEX) {
     ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
     if (ssm::cplx_scan_grid_blocks(p->batch, p->dim, *nseg) > std::numeric_limits<int32_t>::max())
@@ -138,13 +145,15 @@ ssm_status check_scan_inputs(const ssm_scan_params* p, bool aggregate, ScanCheck
   if (p->conv_w && (c->K < 1 || c->K > 4))
     return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!pointers) return SSM_OK;
+  // A pointer to an empty tensor may be NULL.
   const struct {
     const void* ptr;
+    int64_t count;
     const char* name;
-  } required[] = {{p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"}, {p->Bm, "Bm"},
-                  {aggregate ? p->u : p->Cm, "Cm"}, {aggregate ? p->u : p->out, "out"}};
+  } required[] = {{p->u, sz.bdl, "u"}, {p->dt_raw, sz.bdl, "dt_raw"}, {p->A, sz.dn, "A"}, {p->Bm, sz.bln, "Bm"},
+                  {p->Cm, aggregate ? 0 : sz.bln, "Cm"}, {p->out, aggregate ? 0 : sz.bdl, "out"}};
   for (const auto& r : required)
-    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+    if (!r.ptr && r.count > 0) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
   c->si = dtype_size(p->in_dtype);
   c->so = aggregate ? 4 : dtype_size(p->out_dtype);
   if (!p->conv_w && (p->conv_b || p->conv_state_in || p->conv_state_out))
@@ -202,6 +211,12 @@ ssm_status check_workspace(const ssm_scan_params* p, size_t ws, const Range (&in
 // fold into P and H) unless the sequence stays in one piece.
 ssm_status plan_aggregate(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size_t* ws) {
   if (p->num_segments < 0) return fail(SSM_ERR_BAD_SHAPE, "num_segments must be >= 0");
+  if (p->batch == 0 || p->dim == 0 || p->seqlen == 0) {  // empty: no launch, no workspace
+    *nseg = 1;
+    *seg_len = p->seqlen;
+    *ws = 0;
+    return SSM_OK;
+  }
   const bool cplx = p->state_kind == SSM_STATE_COMPLEX;
   if (cplx)
     ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
@@ -306,6 +321,11 @@ ssm_status plan_bwd_cplx(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdL
 }
 
 ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout* lay) {
+  if (sz.empty()) {  // nothing to sweep: no launch plan, no workspace
+    *lay = BwdLayout{};
+    lay->nseg = lay->nsegb = 1;
+    return SSM_OK;
+  }
   if (p->state_kind == SSM_STATE_COMPLEX) return plan_bwd_cplx(p, sz, lay);
   const int64_t B = p->batch, D = p->dim, L = p->seqlen, N = p->dstate;
   ssm::plan_bwd_segments(B, D, L, N, p->discretization == SSM_DISC_ZOH, &lay->nsegb, &lay->seg_steps);
@@ -375,15 +395,17 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   if (s != SSM_OK) return s;
   if (!valid_dtype(p->in_dtype) || !valid_dtype(p->grad_dtype))
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/grad_dtype must be SSM_F32 or SSM_BF16");
-  const struct {
+  const struct {  // a pointer to an empty tensor may be NULL; the workspace is checked below
     const void* ptr;
+    int64_t count;
     const char* name;
-  } required[] = {{p->u, "u"},     {p->dt_raw, "dt_raw"},     {p->A, "A"},        {p->Bm, "Bm"},
-                  {p->Cm, "Cm"},   {p->dout, "dout"},         {p->du, "du"},      {p->d_dt_raw, "d_dt_raw"},
-                  {p->dA, "dA"},   {p->dBm, "dBm"},           {p->dCm, "dCm"},    {p->workspace, "workspace"}};
+  } required[] = {{p->u, sz.bdl, "u"},   {p->dt_raw, sz.bdl, "dt_raw"}, {p->A, sz.dn, "A"},
+                  {p->Bm, sz.bln, "Bm"}, {p->Cm, sz.bln, "Cm"},         {p->dout, sz.bdl, "dout"},
+                  {p->du, sz.bdl, "du"}, {p->d_dt_raw, sz.bdl, "d_dt_raw"}, {p->dA, sz.dn, "dA"},
+                  {p->dBm, sz.bln, "dBm"}, {p->dCm, sz.bln, "dCm"}};
   for (const auto& r : required)
-    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
-  if (p->z && !p->dz) return fail(SSM_ERR_NULL_POINTER, "dz is NULL although z is given");
+    if (!r.ptr && r.count > 0) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+  if (p->z && !p->dz && sz.bdl > 0) return fail(SSM_ERR_NULL_POINTER, "dz is NULL although z is given");
   if (!p->z && p->dz) return fail(SSM_ERR_BAD_SHAPE, "dz is given although z is NULL");
   if (!valid_disc(p->discretization))
     return fail(SSM_ERR_UNSUPPORTED, "unknown discretization %d", p->discretization);
@@ -416,6 +438,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
 
   BwdLayout lay;
   if ((s = plan_bwd(p, sz, &lay)) != SSM_OK) return s;
+  if (lay.total > 0 && !p->workspace) return fail(SSM_ERR_NULL_POINTER, "workspace is NULL");
   if (p->workspace_bytes < lay.total)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, p->workspace_bytes);
 
@@ -437,7 +460,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
       range(p->dh0, cw * sz.bdn, 4, "dh0"),
       range(p->dconv_w, p->dim * K, 4, "dconv_w"), range(p->dconv_b, p->dim, 4, "dconv_b"),
       range(p->dconv_state_in, bdk, 4, "dconv_state_in"),
-      Range{static_cast<const char*>(p->workspace), lay.total, "workspace"},
+      Range{lay.total ? static_cast<const char*>(p->workspace) : nullptr, lay.total, "workspace"},
   };
   constexpr int n_out = sizeof(outputs) / sizeof(outputs[0]);
   for (int i = 0; i < n_out; ++i) {
@@ -450,6 +473,24 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
 
   char* ws = static_cast<char*>(p->workspace);
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (sz.empty()) {
+    // Sums over no (b, t) or no channel are 0; the adjoint passes through an
+    // empty sequence (h_last = h0); the outputs do not depend on the initial
+    // conv state.
+    hipError_t e = ssm::launch_fill(p->dA, nullptr, 0.0f, 0.0f, cw * sz.dn, stream);
+    if (e == hipSuccess) e = ssm::launch_fill(p->dBm, nullptr, 0.0f, 0.0f, cw * sz.bln, stream);
+    if (e == hipSuccess) e = ssm::launch_fill(p->dCm, nullptr, 0.0f, 0.0f, cw * sz.bln, stream);
+    const struct {
+      float* dst;
+      const float* src;
+      int64_t n;
+    } fills[] = {{p->dDskip, nullptr, p->dim}, {p->d_dt_bias, nullptr, p->dim}, {p->dconv_w, nullptr, p->dim * K},
+                 {p->dconv_b, nullptr, p->dim}, {p->dconv_state_in, nullptr, bdk}, {p->dh0, p->dh_last, cw * sz.bdn}};
+    for (const auto& f : fills)
+      if (e == hipSuccess) e = ssm::launch_fill(f.dst, f.src, 0.0f, 0.0f, f.n, stream);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   ssm::ScanPlan sp{};
   sp.B = p->batch;
   sp.D = p->dim;
@@ -584,6 +625,13 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
   if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
   const Range outs[] = {out, hl, cso};
   if ((s = check_workspace(p, ws, inputs, outs, 3)) != SSM_OK) return s;
+  if (sz.empty()) {  // the states pass through an empty sequence
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ssm::launch_fill(p->h_last, p->h0, 0.0f, 0.0f, sz.bdn * c.cw, st);
+    if (e == hipSuccess) e = ssm::launch_fill(p->conv_state_out, p->conv_state_in, 0.0f, 0.0f, c.bdk, st);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
 
   ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
   plan.out = p->out;
@@ -619,7 +667,7 @@ ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void
   Range inputs[kScanInputs];
   ssm_status s = check_scan_inputs(p, true, &c, inputs);
   if (s != SSM_OK) return s;
-  if (!P || !H) return fail(SSM_ERR_NULL_POINTER, "P or H is NULL");
+  if ((!P || !H) && c.sz.bdn > 0) return fail(SSM_ERR_NULL_POINTER, "P or H is NULL");
   if (!aligned(P, 4) || !aligned(H, 4)) return fail(SSM_ERR_MISALIGNED, "P and H must be 4-byte aligned");
   const Range rp = range(P, c.sz.bdn * c.cw, 4, "P"), rh = range(H, c.sz.bdn * c.cw, 4, "H");
   for (const Range& r : inputs) {
@@ -633,6 +681,13 @@ ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void
   if ((s = plan_aggregate(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
   const Range outs[] = {rp, rh};
   if ((s = check_workspace(p, ws, inputs, outs, 2)) != SSM_OK) return s;
+  if (c.sz.empty()) {  // an empty sequence is the identity map: P = 1, H = 0
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ssm::launch_fill(P, nullptr, 1.0f, c.cplx ? 0.0f : 1.0f, c.sz.bdn * c.cw, st);
+    if (e == hipSuccess) e = ssm::launch_fill(H, nullptr, 0.0f, 0.0f, c.sz.bdn * c.cw, st);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
 
   ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
   const hipError_t e = c.cplx ? ssm::launch_aggregate_cplx(plan, P, H, static_cast<hipStream_t>(hip_stream))
@@ -643,8 +698,8 @@ ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void
 
 ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
-  if (p->batch < 1 || p->dim < 1)
-    return fail(SSM_ERR_BAD_SHAPE, "batch and dim must be >= 1 (got %lld, %lld)", (long long)p->batch,
+  if (p->batch < 0 || p->dim < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "batch and dim must be >= 0 (got %lld, %lld)", (long long)p->batch,
                 (long long)p->dim);
   if (p->dstate < 1 || p->dstate > SSM_MAX_DSTATE)
     return fail(SSM_ERR_BAD_SHAPE, "dstate must be in [1, %d] (got %lld)", SSM_MAX_DSTATE,
@@ -657,13 +712,14 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
     return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
   if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
     return fail(SSM_ERR_BAD_DTYPE, "in_dtype/out_dtype must be SSM_F32 or SSM_BF16");
-  const struct {
+  const struct {  // a pointer to an empty tensor may be NULL
     const void* ptr;
+    int64_t count;
     const char* name;
-  } required[] = {{p->h, "h"}, {p->u, "u"}, {p->dt_raw, "dt_raw"}, {p->A, "A"},
-                  {p->Bm, "Bm"}, {p->Cm, "Cm"}, {p->out, "out"}};
+  } required[] = {{p->h, bdn, "h"}, {p->u, bd, "u"}, {p->dt_raw, bd, "dt_raw"}, {p->A, dn, "A"},
+                  {p->Bm, bn, "Bm"}, {p->Cm, bn, "Cm"}, {p->out, bd, "out"}};
   for (const auto& r : required)
-    if (!r.ptr) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
+    if (!r.ptr && r.count > 0) return fail(SSM_ERR_NULL_POINTER, "%s is NULL", r.name);
   const size_t si = dtype_size(p->in_dtype), so = dtype_size(p->out_dtype);
   const struct {
     const void* ptr;
@@ -689,7 +745,8 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   if (p->conv_w && (K < 1 || K > 4)) return fail(SSM_ERR_BAD_SHAPE, "conv_width must be in [1, 4] (got %d)", p->conv_width);
   if (!p->conv_w && (p->conv_b || p->conv_state))
     return fail(SSM_ERR_NULL_POINTER, "conv_b / conv_state given without conv_w");
-  if (K > 1 && !p->conv_state) return fail(SSM_ERR_NULL_POINTER, "conv_state is NULL although conv_width > 1");
+  if (K > 1 && !p->conv_state && bd > 0)
+    return fail(SSM_ERR_NULL_POINTER, "conv_state is NULL although conv_width > 1");
   for (const void* q : {static_cast<const void*>(p->conv_state), static_cast<const void*>(p->conv_w),
                         static_cast<const void*>(p->conv_b)})
     if (q && !aligned(q, 4)) return fail(SSM_ERR_MISALIGNED, "a conv pointer is not aligned to 4 bytes");
@@ -707,6 +764,8 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
     if (overlaps(cs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps %s", r.name);
   if (overlaps(h, cw) || overlaps(h, cb) || overlaps(out, cw) || overlaps(out, cb))
     return fail(SSM_ERR_ALIAS, "h or out overlaps a conv parameter");
+
+  if (bd == 0) return ok();  // no rows: nothing to update
 
   ssm::UpdatePlan plan{};
   plan.B = p->batch;

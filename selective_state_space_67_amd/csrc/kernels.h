@@ -187,4 +187,8 @@ size_t cplx_bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int n
 int64_t cplx_bwd_grid_blocks(int64_t B, int64_t D, int nsegb);
 hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream_t stream);
 
+// Outputs of empty problems: dst[i] = src[i] (src given) or v0 / v1 at even /
+// odd i, for n floats (nothing for dst = null or n = 0).
+hipError_t launch_fill(float* dst, const float* src, float v0, float v1, int64_t n, hipStream_t stream);
+
 }  // namespace ssm

@@ -146,6 +146,28 @@ def workload_inputs(name: str, **overrides):
                             dt_hi=c["dt_hi"], packed=c["packed"])
 
 
+def make_scan_inputs_device(B, D, L, N, device, seed=0, dt_lo=1e-3, dt_hi=1e-1):
+    """Bfloat16 scan inputs drawn on ``device``, for sizes too large to draw on
+    the host. u, dt_raw, z (B, D, L), then Bm, Cm (B, L, N), each N(0, 1) from
+    torch's generator on that device seeded with ``seed``, in that order, and
+    rounded to bfloat16 (nearest even); dt_bias is the host draw of
+    make_scan_inputs (numpy stream ``seed``); A is S4D-Real and Dskip = 1.
+    Returns a dict of device tensors (u, dt_raw, z, Bm, Cm) and numpy arrays
+    (dt_bias, A, Dskip)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+    x = dict(u=draw((B, D, L)), dt_raw=draw((B, D, L)), z=draw((B, D, L)), Bm=draw((B, L, N)), Cm=draw((B, L, N)))
+    x.update(dt_bias=dt_bias_draw(np.random.default_rng(seed), D, dt_lo, dt_hi), A=s4d_real_A(D, N),
+             Dskip=np.ones(D, dtype=np.float32), dtype=BF16)
+    return x
+
+
 def s4d_lin_A(D, N):
     """A[d, n] = -1/2 + i n as (D, N, 2) float32 (re, im) pairs."""
     A = np.empty((D, N, 2), dtype=np.float32)

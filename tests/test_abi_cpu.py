@@ -43,7 +43,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10700
+    assert lib.ssm_version() == 10800
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -113,7 +113,7 @@ def test_update_required_pointers(lib, field):
     assert update_status(lib, update_params(**{field: None})) == 1
 
 
-@pytest.mark.parametrize("kw", [dict(batch=0), dict(dim=0), dict(seqlen=0), dict(dstate=0), dict(dstate=257),
+@pytest.mark.parametrize("kw", [dict(dim=-1), dict(seqlen=-5), dict(dstate=0), dict(dstate=257),
                                 dict(batch=-3), dict(seqlen=2 ** 40), dict(batch=2 ** 40, dim=2 ** 40),
                                 dict(num_segments=-1)])
 def test_scan_bad_shape(lib, kw):
@@ -123,7 +123,7 @@ def test_scan_bad_shape(lib, kw):
         assert lib.ssm_scan_workspace_size(ctypes.byref(scan_params(**kw)), ctypes.byref(n)) == 2
 
 
-@pytest.mark.parametrize("kw", [dict(batch=0), dict(dim=0), dict(dstate=0), dict(dstate=300)])
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(dim=-2), dict(dstate=0), dict(dstate=300)])
 def test_update_bad_shape(lib, kw):
     assert update_status(lib, update_params(**kw)) == 2
 
@@ -261,7 +261,7 @@ def test_bwd_dz_only_with_z(lib):
     assert bwd_status(lib, bwd_params(z=None)) == 2          # dz given without z
 
 
-@pytest.mark.parametrize("kw", [dict(batch=0), dict(seqlen=0), dict(dstate=257), dict(seqlen=2 ** 40)])
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(seqlen=-1), dict(dstate=257), dict(seqlen=2 ** 40)])
 def test_bwd_bad_shape(lib, kw):
     n = ctypes.c_size_t(0)
     p = bwd_params()
@@ -475,3 +475,61 @@ def test_aggregate_workspace(lib):
     r = scan_params(num_segments=1)
     assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(r), ctypes.byref(n)) == 0
     assert n.value == 0
+
+
+# ---------------------------------------------------------------- empty problems
+# Valid and issue no device work when no output holds a value: the calls below
+# pass NULL for every empty tensor and for the outputs that would be written
+# (h_last, conv_state_out, dh0, ...), so they return SSM_OK without launching.
+
+@pytest.mark.parametrize("cplx", [False, True])
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(dim=0), dict(seqlen=0), dict(batch=0, seqlen=0)])
+def test_empty_scan_is_valid(lib, kw, cplx):
+    empty = dict(u=None, dt_raw=None, z=None, out=None, reset=None)
+    if kw.get("batch") == 0 or kw.get("seqlen") == 0:
+        empty.update(Bm=None, Cm=None)
+    if kw.get("dim") == 0:
+        empty.update(A=None, dt_bias=None, Dskip=None)
+    p = scan_params(**kw, **empty, state_kind=int(cplx))
+    n = ctypes.c_size_t(99)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value == 0
+    assert scan_status(lib, p) == 0, lib.ssm_last_error()
+    n = ctypes.c_size_t(99)
+    assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value == 0
+    if "dim" in kw or "batch" in kw:  # (B, D, N) P and H are empty too
+        assert lib.ssm_scan_aggregate(ctypes.byref(p), None, None, None) == 0, lib.ssm_last_error()
+    else:                             # an empty sequence still has an aggregate: P, H required
+        assert lib.ssm_scan_aggregate(ctypes.byref(p), None, None, None) == 1
+
+
+def test_empty_scan_keeps_other_checks(lib):
+    assert scan_status(lib, scan_params(seqlen=0, u=None, out=None, A=None)) == 1            # A is not empty
+    assert scan_status(lib, scan_params(seqlen=0, in_dtype=9)) == 3
+    assert scan_status(lib, scan_params(seqlen=0, h0=BASE + 0x7000002, h_last=BASE + 0x7100000)) == 4
+    assert scan_status(lib, scan_params(seqlen=0, h0=BASE + 0x7000000, h_last=BASE + 0x7000000)) == 7
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(dim=0)])
+def test_empty_update_is_valid(lib, kw):
+    empty = dict(h=None, u=None, dt_raw=None, z=None, out=None)
+    if "batch" in kw:
+        empty.update(Bm=None, Cm=None)
+    else:
+        empty.update(A=None, dt_bias=None, Dskip=None)
+    assert update_status(lib, update_params(**kw, **empty)) == 0, lib.ssm_last_error()
+
+
+@pytest.mark.parametrize("cplx", [False, True])
+@pytest.mark.parametrize("kw", [dict(dim=0, seqlen=0), dict(dim=0, batch=0)])
+def test_empty_bwd_is_valid(lib, cplx, kw):
+    """No channel and no step (or no row): every gradient is empty, no workspace."""
+    p = bwd_params(cplx=cplx, **kw)
+    for f in ("u", "dt_raw", "z", "dout", "du", "d_dt_raw", "dz", "A", "dA", "Bm", "Cm", "dBm", "dCm", "dt_bias",
+              "Dskip", "dDskip", "d_dt_bias", "dh0", "workspace"):
+        setattr(p, f, None)
+    p.workspace_bytes = 0
+    n = ctypes.c_size_t(99)
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value == 0
+    assert bwd_status(lib, p) == 0, lib.ssm_last_error()
+    p.dim = 3                          # dA (D, N) is not empty: required
+    assert bwd_status(lib, p) == 1 and b"A" in lib.ssm_last_error()

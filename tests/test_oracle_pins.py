@@ -375,3 +375,30 @@ def test_oracle_is_independent_of_the_product():
             includes = set(re.findall(r"#include\s*<([^>]+)>", open(path).read()))
             assert includes <= {"complex.h", "math.h", "stddef.h", "stdint.h", "stdlib.h", "omp.h"}, includes
             assert '#include "' not in open(path).read()
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 0), (0, 3, 7), (2, 0, 7)])
+def test_empty_problems(shape):
+    """Empty sums and products: with no step the state passes through
+    (h_last = h0, the aggregate is P = 1, H = 0) and the adjoint too
+    (dh0 = dh_last); gradients summed over no (b, t) or no channel are 0."""
+    Bt, D, L = shape
+    N = 4
+    rng = np.random.default_rng(21)
+    u, dt, z, dout = (rng.standard_normal((Bt, D, L)) for _ in range(4))
+    A = -rng.uniform(0.5, 1.5, (D, N))
+    Bm, Cm = rng.standard_normal((Bt, L, N)), rng.standard_normal((Bt, L, N))
+    h0, dhl = rng.standard_normal((Bt, D, N)), rng.standard_normal((Bt, D, N))
+    out, hl = oracle.scan(u, dt, A, Bm, Cm, z=z, h0=h0, want_h_last=True)
+    assert out.shape == (Bt, D, L)
+    if L == 0:
+        np.testing.assert_array_equal(hl, h0)
+    P, H = oracle.scan_aggregate(u, dt, A, Bm)
+    if L == 0:
+        np.testing.assert_array_equal(P, np.ones((Bt, D, N)))
+        np.testing.assert_array_equal(H, np.zeros((Bt, D, N)))
+    g = oracle.scan_bwd(u, dt, A, Bm, Cm, dout, z=z, h0=h0, dh_last=dhl)
+    if L == 0:
+        np.testing.assert_array_equal(g["dh0"], dhl)
+    for k in ("dA", "dD", "d_dt_bias") if D else ("dB", "dC"):
+        np.testing.assert_array_equal(g[k], np.zeros_like(g[k]))
