@@ -109,7 +109,8 @@ ssm_status plan_scan(const ssm_scan_params* p, int* nseg, int64_t* seg_len, size
     *ws = ssm::cplx_workspace_bytes(p->batch, p->dim, p->dstate, *nseg);
     return SSM_OK;
   }
-  ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+  const bool plain = !p->conv_w && p->discretization != SSM_DISC_ZOH;
+  ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len, plain);
   if (ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg) > std::numeric_limits<int32_t>::max())
     return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
   *ws = ssm::scan_workspace_bytes(p->batch, p->dim, p->dstate, *nseg);
@@ -221,7 +222,7 @@ ssm_status plan_aggregate(const ssm_scan_params* p, int* nseg, int64_t* seg_len,
   if (cplx)
     ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
   else
-    ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
+    ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len, true);
   const int64_t blocks = cplx ? ssm::cplx_scan_grid_blocks(p->batch, p->dim, *nseg)
                               : ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg);
   if (blocks > std::numeric_limits<int32_t>::max())

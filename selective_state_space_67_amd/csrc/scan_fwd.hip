@@ -8,7 +8,7 @@ using fwd::channels_per_block;
 using fwd::resident_blocks;
 
 void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg,
-                   int64_t* seg_len) {
+                   int64_t* seg_len, bool plain) {
   int64_t want;
   if (requested > 0) {
     want = requested;
@@ -19,7 +19,7 @@ void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, in
     // pieces long enough (>= 512 steps) that per-piece overheads stay small.
     const int cpw = channels_per_block(N);
     const int64_t blocks = B * ((D + cpw - 1) / cpw);
-    const int64_t round = resident_blocks(N);
+    const int64_t round = resident_blocks(N, plain);
     want = 2 * blocks >= round ? 1 : round / blocks;
     want = std::min<int64_t>(want, std::max<int64_t>(1, L / 512));
   }
