@@ -26,32 +26,52 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Taylor coefficients of sin(w r) and cos(w r) in r (revolutions):
+// (-1)^j w^(2j+1) / (2j+1)! and (-1)^j w^(2j) / (2j)!, with w = 2 pi rounded
+// to float32 first. Sine and cosine are then taken of the same angle w r
+// (2.8e-8 relative above 2 pi r, a phase error like that of forming
+// theta = r * 2 pi in float32) instead of angles that differ by the rounding
+// of their leading coefficients, which would bias the decay's magnitude.
+constexpr double kTwoPi = static_cast<double>(static_cast<float>(6.283185307179586476925));
+constexpr double kP2 = kTwoPi * kTwoPi;
+constexpr float kS1 = static_cast<float>(kTwoPi);
+constexpr float kS3 = static_cast<float>(-kTwoPi * kP2 / 6.0);
+constexpr float kS5 = static_cast<float>(kTwoPi * kP2 * kP2 / 120.0);
+constexpr float kS7 = static_cast<float>(-kTwoPi * kP2 * kP2 * kP2 / 5040.0);
+constexpr float kS9 = static_cast<float>(kTwoPi * kP2 * kP2 * kP2 * kP2 / 362880.0);
+constexpr float kC2 = static_cast<float>(-kP2 / 2.0);
+constexpr float kC4 = static_cast<float>(kP2 * kP2 / 24.0);
+constexpr float kC6 = static_cast<float>(-kP2 * kP2 * kP2 / 720.0);
+constexpr float kC8 = static_cast<float>(kP2 * kP2 * kP2 * kP2 / 40320.0);
+constexpr float kC10 = static_cast<float>(-kP2 * kP2 * kP2 * kP2 * kP2 / 3628800.0);
+
 // e (cos + i sin) of the angle delta (ai + ai_lo) revolutions. The product
 // p = delta ai is split into p and its exact rounding error; p - rint(p) is
 // exact and lies in [-1/2, 1/2]; k quarter turns are taken off exactly, and
 // the small parts are added to the remainder r, |r| <= 1/8 revolution. Then
-// theta = 2 pi r, sin and cos by their Taylor series through theta^9 and
-// theta^10 (truncation below 2e-9 and 1.2e-10 on |theta| <= pi/4), and the
-// k quarter turns as a product with i^k = (1 - |k|) + i k (2 - |k|), k in
-// -2 .. 2, whose parts are 0 or +-1 (so the rotation is exact; e is folded
-// into them first).
+// sin and cos of 2 pi r by their Taylor series through the 9th and 10th
+// power (truncation below 2e-9 and 1.2e-10 for |r| <= 1/8), evaluated in r
+// with the powers of 2 pi folded into the coefficients, and the k quarter
+// turns as a product with i^k = (1 - |k|) + i k (2 - |k|), k in -2 .. 2,
+// whose parts are 0 or +-1 (so the rotation is exact; e is folded into them
+// first).
 __device__ __forceinline__ void rotate_rev(float e, float delta, float ai, float ai_lo, float& re, float& im) {
   const float p = delta * ai;
   const float lo = __builtin_fmaf(delta, ai, -p) + delta * ai_lo;
   const float f = p - __builtin_rintf(p);
   const float k = __builtin_rintf(4.0f * f);  // -2 .. 2
   const float r = __builtin_fmaf(-0.25f, k, f) + lo;
-  const float th = r * 6.28318530717958648f;
-  const float t2 = th * th;
-  float sp = __builtin_fmaf(t2, 2.75573192e-6f, -1.98412698e-4f);
-  sp = __builtin_fmaf(t2, sp, 8.33333333e-3f);
-  sp = __builtin_fmaf(t2, sp, -1.66666667e-1f);
-  const float sn = __builtin_fmaf(th * t2, sp, th);
-  float cp = __builtin_fmaf(t2, -2.75573192e-7f, 2.48015873e-5f);
-  cp = __builtin_fmaf(t2, cp, -1.38888889e-3f);
-  cp = __builtin_fmaf(t2, cp, 4.16666667e-2f);
-  cp = __builtin_fmaf(t2, cp, -0.5f);
-  const float cs = __builtin_fmaf(t2, cp, 1.0f);
+  const float x = r * r;
+  float sp = __builtin_fmaf(x, kS9, kS7);
+  sp = __builtin_fmaf(x, sp, kS5);
+  sp = __builtin_fmaf(x, sp, kS3);
+  sp = __builtin_fmaf(x, sp, kS1);
+  const float sn = r * sp;
+  float cp = __builtin_fmaf(x, kC10, kC8);
+  cp = __builtin_fmaf(x, cp, kC6);
+  cp = __builtin_fmaf(x, cp, kC4);
+  cp = __builtin_fmaf(x, cp, kC2);
+  const float cs = __builtin_fmaf(x, cp, 1.0f);
   const float ak = fabsf(k);
   const float ec = e * (1.0f - ak), es = e * (k * (2.0f - ak));  // e i^k
   re = __builtin_fmaf(cs, ec, -sn * es);
