@@ -375,7 +375,9 @@ def main():
     del fsh, agg, ts, xs, h0s, Pa, Ha
 
     result = {
-        "metric": "selective-scan elements/s (B*D*L*N), 1 GPU",
+        # value is the element rate; the achieved HBM rate and its fraction of
+        # peak are hbm_gbps and hbm_frac_of_peak below
+        "metric": "selective-scan elements/s (B\u00b7D\u00b7L\u00b7N) and achieved HBM GB/s vs peak, 1 GPU",
         "value": elements / wall,
         "unit": "elements/s",
         "n_gpus": 1,
