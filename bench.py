@@ -15,7 +15,8 @@ arithmetic and output), inputs resident in HBM. Prints one JSON line:
                recorded under profiles/ (null when the kernel source changed
                since they were taken)
   cold_cache   the same launch after a 1 GiB write that evicts L2 and MALL
-  decode       the single-token decode step (batch 64, 2048 channels, N = 128)
+  decode       the single-token decode step (batch 64, 2048 channels, N = 128),
+               warm (repeated steps) and with cold caches
   backward     ssm_scan_bwd on the same workload with a random output gradient
                (checkpoint sweep, reverse sweep and reduction, back to back)
   conv_stage   the same forward and backward with the fused causal conv1d
@@ -228,6 +229,20 @@ def main():
     Bd, Dd, Nd = y["h"].shape
     dbytes = decode_bytes(Bd, Dd, Nd, 2, 4)
     dsec = float(np.median(dms)) / 1e3
+    # Repeated steps keep the 67 MB state in the last-level cache; a decode
+    # loop over many layers would not. Cold: a 1 GiB write before each launch.
+    dcold = []
+    if not args.no_cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for i in range(min(args.steps, 50)):
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dec()
+            e1.record(stream)
+            e1.synchronize()
+            dcold.append(e0.elapsed_time(e1))
+        del scratch
 
     # A launch-bound decode loop (one sequence of the Mamba-130M layer shape,
     # 32 tokens): prepared launches one by one, against the same 32 steps
@@ -415,8 +430,15 @@ def main():
             "launch_ms_median": float(np.median(cold)), "launch_ms_p10": percentile(cold, 10),
             "launch_ms_p90": percentile(cold, 90), "hbm_gbps": abytes / (float(np.median(cold)) / 1e3) / 1e9},
         "decode": {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
+                   "note": "launch_ms_mean / hbm_gbps: steps repeated on one state, which can stay in the "
+                           "last-level cache; cold_cache: the state read from HBM, as in a model whose layers' "
+                           "states do not fit the caches",
                    "launch_ms_mean": dsec * 1e3, "algorithmic_bytes": dbytes,
-                   "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS},
+                   "hbm_gbps": dbytes / dsec / 1e9, "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBPS,
+                   "cold_cache": None if not dcold else {
+                       "launch_ms_median": float(np.median(dcold)),
+                       "hbm_gbps": dbytes / (float(np.median(dcold)) / 1e3) / 1e9,
+                       "hbm_frac": dbytes / (float(np.median(dcold)) / 1e3) / 1e9 / HBM_PEAK_GBPS}},
         "decode_loop": {"workload": "32 decode steps of one sequence, B=1 D=1536 N=16, bf16 inputs",
                         "eager_us_per_token": eager_tok * 1e6, "hip_graph_us_per_token": graph_tok * 1e6},
         "backward": {"workload": "ssm_scan_bwd on the same inputs, %s dout, fp32 gradients" % cfg["dtype"],

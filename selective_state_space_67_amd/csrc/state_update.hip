@@ -13,7 +13,8 @@
 // nearly all of its HBM traffic, so the kernel is built to keep many bytes of
 // state in flight: LR consecutive lanes own one (b, d) row, each lane holding
 // four consecutive states (one 16-byte load and store), and every thread
-// handles RPT rows whose loads are all issued before any arithmetic. The
+// handles RPT rows whose loads are all issued before any arithmetic; states
+// larger than the L2 are read with nontemporal loads (streamed). The
 // step size and gate (a few transcendentals per row) are recomputed by each
 // lane of the row, which is cheaper than broadcasting them; the dot product
 // over n is a butterfly of cross-lane adds. Shapes whose N is not a multiple
@@ -108,8 +109,21 @@ __device__ __forceinline__ void store_out(const UpdateArgs& a, int64_t row, floa
     store_elem(static_cast<float*>(a.out), row, v);
 }
 
+// One 16-byte group of states. STREAM: a nontemporal load (the state is
+// read once per step and, when larger than the caches, comes from HBM).
+template <bool STREAM>
+__device__ __forceinline__ float4 load_state4(const float* p) {
+  if constexpr (STREAM) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+
 // Vector variant: N % 4 == 0, LR = N / 4 lanes per row (a power of two <= 64).
-template <typename InT, int LR, int RPT>
+template <typename InT, int LR, int RPT, bool STREAM>
 __global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a) {
   constexpr int ROWS_PER_PASS = kThreads / LR;
   const int li = threadIdx.x % LR;
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a
     const int64_t row = first + static_cast<int64_t>(r) * ROWS_PER_PASS;
     if (row < a.rows) {
       const int64_t b = row / a.D, d = row - b * a.D;
-      hv[r] = *reinterpret_cast<const float4*>(a.h + row * a.N + n0);
+      hv[r] = load_state4<STREAM>(a.h + row * a.N + n0);
       Av[r] = *reinterpret_cast<const float4*>(a.A + d * a.N + n0);
       Bv[r] = load4(B_in, b * a.N + n0);
       Cv[r] = load4(C_in, b * a.N + n0);
@@ -196,13 +210,24 @@ __global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs
   }
 }
 
+// States larger than this are streamed (nontemporal loads): measured at
+// 64 x 2048 x 128 (67 MB), a step whose state comes from HBM takes 33.8 us
+// streamed against 38 us cached, while a step repeated on a state that stays
+// in the last-level cache takes 32.5 us against 28.6 us. A state larger than
+// the L2 (4 MB per XCD) does not stay in it across the layers of a model.
+constexpr int64_t kStreamStateBytes = int64_t{32} << 20;
+
 template <typename InT, int LR>
 hipError_t launch_vec(const UpdateArgs& a, hipStream_t stream) {
   constexpr int RPT = 2;  // measured best of 1, 2, 4, 8, 16 on the 64x2048x128 step
   const int64_t rows_per_block = static_cast<int64_t>(kThreads / LR) * RPT;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, a);
+  if (a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes)
+    hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 
