@@ -37,6 +37,7 @@
 // (selected while the steps go by) and writes the output. Lanes run their
 // recurrences in lockstep, so the row needs no skew.
 #include <algorithm>
+#include <type_traits>
 
 #include "cplx_device.h"
 #include "kernels.h"
@@ -313,7 +314,9 @@ struct CplxUpdateArgs {
 // k holds states k, k + 16, k + 32, ..., so for each j the 16 lanes of a row
 // read 16 consecutive (re, im) pairs of h, A, B and C: coalesced accesses to
 // the state, which is what the step moves.
-template <int NPL, typename InT, bool ZOH>
+// STREAM: the state is read with nontemporal loads (states larger than the
+// L2, which a model's decode reads from HBM; as in the real decode step).
+template <int NPL, typename InT, bool ZOH, bool STREAM>
 __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateArgs a) {
   const int tid = threadIdx.x;
   const int k = tid & 15;
@@ -333,7 +336,13 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
     const int n = k + 16 * j;
     const bool ok = n < N;
     const int nc = ok ? n : N - 1;
-    hv[j] = *reinterpret_cast<const float2*>(h + 2 * nc);
+    if constexpr (STREAM) {
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f t = __builtin_nontemporal_load(reinterpret_cast<const v2f*>(h + 2 * nc));
+      hv[j] = make_float2(t.x, t.y);
+    } else {
+      hv[j] = *reinterpret_cast<const float2*>(h + 2 * nc);
+    }
     av[j] = *reinterpret_cast<const float2*>(Ad + 2 * nc);
     bv[j] = load_cpair(Bb, nc);
     cv[j] = load_cpair(Cb, nc);
@@ -555,20 +564,21 @@ hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
   a.conv_b = p.conv_b;
   a.conv_k = p.conv_k;
   const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
-  return with_npl(p.N, [&](auto npl) {
+  const bool streamed = p.B * p.D * p.N * 2 * static_cast<int64_t>(sizeof(float)) > (int64_t{32} << 20);
+  auto go = [&](auto npl, auto zoh, auto st) {
     constexpr int NPL = decltype(npl)::value;
-    if (p.in_bf16) {
-      if (p.zoh)
-        hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, true>), grid, dim3(kThreads), 0, stream, a);
-      else
-        hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, false>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-      if (p.zoh)
-        hipLaunchKernelGGL((cplx_update_kernel<NPL, float, true>), grid, dim3(kThreads), 0, stream, a);
-      else
-        hipLaunchKernelGGL((cplx_update_kernel<NPL, float, false>), grid, dim3(kThreads), 0, stream, a);
-    }
+    constexpr bool Z = decltype(zoh)::value, S = decltype(st)::value;
+    if (p.in_bf16)
+      hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, Z, S>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((cplx_update_kernel<NPL, float, Z, S>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  return with_npl(p.N, [&](auto npl) {
+    if (p.zoh) return streamed ? go(npl, T{}, T{}) : go(npl, T{}, F{});
+    return streamed ? go(npl, F{}, T{}) : go(npl, F{}, F{});
   });
 }
 
