@@ -136,7 +136,7 @@ def main():
                     help="also run one plain 512 MiB device copy (for counter calibration runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)"
+        print("bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 

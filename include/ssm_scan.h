@@ -77,7 +77,7 @@ typedef enum {
                                L >= 2^27, or an element count overflows int64  */
   SSM_ERR_BAD_DTYPE = 3,    /* in_dtype / out_dtype is not an ssm_dtype         */
   SSM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size    */
-  SSM_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement   */
+  SSM_ERR_UNSUPPORTED = 5,  /* a valid request the library does not implement */
   SSM_ERR_WORKSPACE = 6,    /* workspace smaller than ssm_scan_workspace_size() */
   SSM_ERR_ALIAS = 7,        /* an output overlaps an input, another output or
                                the workspace                                   */
