@@ -3,8 +3,9 @@
 The library must load on a machine without a GPU, export every function
 include/ssm_scan.h declares, agree with the binding on the struct layouts, and
 reject every invalid call on the host before touching the HIP runtime. The
-pointers used here are fake (aligned integers); every call below fails
-validation, so nothing is ever dereferenced or launched.
+pointers used here are fake (aligned integers); every call below either fails
+validation or is an empty problem with no output to write, so nothing is ever
+dereferenced or launched.
 """
 import ctypes
 import os
