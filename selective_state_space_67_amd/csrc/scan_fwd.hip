@@ -116,6 +116,7 @@ hipError_t launch_scan(const ScanPlan& pl, hipStream_t stream) {
   a.ws_P = pl.ws;
   a.ws_H = pl.ws ? pl.ws + per : nullptr;
   const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
+  if (fwd::n16_eligible(a, pl.checkpoint != 0)) return fwd::launch_n16(a, per_piece * pl.nseg, per_piece * (pl.nseg - 1), stream);
   return launch(pl, a, per_piece * pl.nseg, per_piece * (pl.nseg - 1), pl.checkpoint != 0, stream);
 }
 

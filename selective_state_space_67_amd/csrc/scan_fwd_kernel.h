@@ -912,5 +912,10 @@ extern template hipError_t launch_variant<float, true>(const ScanArgs&, int, int
 extern template hipError_t launch_variant<bf16_t, false>(const ScanArgs&, int, int, bool, hipStream_t);
 extern template hipError_t launch_variant<bf16_t, true>(const ScanArgs&, int, int, bool, hipStream_t);
 
+// The 16-state full pass (scan_fwd_n16.hip): whether it takes a launch, and
+// the launch (the pieces' aggregates, when split, through launch_variant).
+bool n16_eligible(const ScanArgs& a, bool checkpoint);
+hipError_t launch_n16(const ScanArgs& a, int nblocks_full, int nblocks_agg, hipStream_t stream);
+
 }  // namespace fwd
 }  // namespace ssm
