@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_VERSION 10800 /* major*10000 + minor*100 + patch */
+#define SSM_SCAN_VERSION 10900 /* major*10000 + minor*100 + patch */
 #define SSM_MAX_DSTATE 256     /* largest supported N */
 
 typedef enum {
@@ -91,8 +91,9 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *                    state space model", step 1; "Mamba SSM core theory and
  *                    Keras/TensorFlow implementation", scan step). Default.
  *  SSM_DISC_ZOH      Bbar = (exp(delta A) - 1) / A * B, the exact zero-order hold
- *                    of the diagonal continuous system (first page, "Mathematical
- *                    basis: structured SSM"); delta * B where A = 0.
+ *                    of the diagonal continuous system ("Illustrated Mamba state
+ *                    space model", "Mathematical basis: structured SSM"; also
+ *                    "Reproducing Mamba's SSM core in Python", section 1); delta * B where A = 0.
  * Abar = exp(delta A) in both. Other values return SSM_ERR_UNSUPPORTED. */
 typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
 
@@ -192,6 +193,27 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes);
 
 /* Enqueue the scan described by `p` on `hip_stream`. */
 ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same scan
+ * as ssm_scan_fwd, with the same arguments, results and errors, except that
+ * workspace and workspace_bytes are ignored: a scan that splits the sequence
+ * keeps its pieces' aggregates in scratch memory the library owns, a fixed
+ * array of SSM_NOALLOC_SCRATCH_BYTES on every device it runs on (held until
+ * the process ends; its address is looked up on the first call per device).
+ * The call allocates and frees nothing. Nothing in the scratch needs to start
+ * at zero: every piece's aggregate is written before it is read.
+ *   - A split whose aggregates need more than SSM_NOALLOC_SCRATCH_BYTES
+ *     (ssm_scan_workspace_size() reports the need) returns SSM_ERR_WORKSPACE
+ *     before any launch.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents: calls that may overlap on one GPU (different streams,
+ *     no ordering between them) race and must be serialised by the caller.
+ *   - The scratch address lookup can fail with SSM_ERR_HIP.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (16u << 20)
+ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, void* hip_stream);
 
 /*
  * Affine aggregate of a whole sequence, for scanning one sequence in shards

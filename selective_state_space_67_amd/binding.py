@@ -81,7 +81,8 @@ class BwdParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_aggregate_workspace_size", "ssm_scan_aggregate",
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_aggregate_workspace_size",
+           "ssm_scan_aggregate",
            "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string", "ssm_last_error",
            "ssm_version", "ssm_abi_struct_size")
 
@@ -106,6 +107,8 @@ def load_library():
     lib.ssm_scan_workspace_size.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanParams), vp]
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_scan_aggregate_workspace_size.argtypes = [ctypes.POINTER(ScanParams), ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_aggregate_workspace_size.restype = ctypes.c_int
     lib.ssm_scan_aggregate.argtypes = [ctypes.POINTER(ScanParams), vp, vp, vp]
@@ -334,6 +337,20 @@ def ssm_scan_fwd(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
         p.workspace = _ptr(workspace)
         p.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib.ssm_scan_fwd(ctypes.byref(p), _stream(stream, u.device)))
+    return out
+
+
+def ssm_scan_fwd_noalloc(u, dt_raw, A, Bm, Cm, *, out, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
+                         h_last=None, num_segments=0, conv_w=None, conv_b=None, conv_state_in=None,
+                         conv_state_out=None, zoh=False, complex_state=False, stream=None):
+    """ssm_scan_fwd through the allocation-free entry point: the caller passes
+    every output (``out`` is required), nothing is allocated here, and a scan
+    that splits the sequence uses the library's own per-device scratch
+    (include/ssm_scan.h, ssm_scan_fwd_noalloc). Returns ``out``."""
+    lib = load_library()
+    p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, None,
+                     num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh, complex_state)
+    _check(lib.ssm_scan_fwd_noalloc(ctypes.byref(p), _stream(stream, u.device)))
     return out
 
 

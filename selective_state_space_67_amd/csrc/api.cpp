@@ -369,6 +369,68 @@ ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout
   return SSM_OK;
 }
 
+// The forward scan. With noalloc the split-scan buffer is the library's
+// scratch on the current device instead of the caller's workspace (whose
+// fields are then ignored); a split larger than the scratch is refused.
+ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
+  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
+  ScanCheck c;
+  Range inputs[kScanInputs];
+  ssm_status s = check_scan_inputs(p, false, &c, inputs);
+  if (s != SSM_OK) return s;
+  const ScanSizes& sz = c.sz;
+  const Range out = range(p->out, sz.bdl, c.so, "out");
+  const Range hl = range(p->h_last, sz.bdn * c.cw, 4, "h_last");
+  const Range cso = range(p->conv_state_out, c.bdk, 4, "conv_state_out");
+  for (const Range& r : inputs) {
+    if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+    if (overlaps(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps %s", r.name);
+    if (overlaps(cso, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
+  }
+  if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
+  if (overlaps(out, cso) || overlaps(hl, cso)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
+
+  int nseg;
+  int64_t seg_len;
+  size_t ws;
+  if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  const Range outs[] = {out, hl, cso};
+  if (noalloc) {
+    if (ws > ssm::noalloc_scratch_bytes())
+      return fail(SSM_ERR_WORKSPACE,
+                  "this split needs %zu bytes of scratch; the allocation-free entry point holds %zu per device",
+                  ws, ssm::noalloc_scratch_bytes());
+  } else if ((s = check_workspace(p, ws, inputs, outs, 3)) != SSM_OK) {
+    return s;
+  }
+  if (sz.empty()) {  // the states pass through an empty sequence
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ssm::launch_fill(p->h_last, p->h0, 0.0f, 0.0f, sz.bdn * c.cw, st);
+    if (e == hipSuccess) e = ssm::launch_fill(p->conv_state_out, p->conv_state_in, 0.0f, 0.0f, c.bdk, st);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+
+  ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
+  if (noalloc && ws > 0) {
+    void* scratch = nullptr;
+    const hipError_t e = ssm::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+    plan.ws = static_cast<float*>(scratch);
+  }
+  plan.out = p->out;
+  plan.h_last = p->h_last;
+  plan.conv_state_out = p->conv_state_out;
+  plan.Cm = p->Cm;
+  plan.z = p->z;
+  plan.Dskip = p->Dskip;
+  plan.h0 = p->h0;
+  const hipError_t e = c.cplx ? ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream))
+                              : ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -602,51 +664,9 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   return ok();
 }
 
-ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) {
-  if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
-  ScanCheck c;
-  Range inputs[kScanInputs];
-  ssm_status s = check_scan_inputs(p, false, &c, inputs);
-  if (s != SSM_OK) return s;
-  const ScanSizes& sz = c.sz;
-  const Range out = range(p->out, sz.bdl, c.so, "out");
-  const Range hl = range(p->h_last, sz.bdn * c.cw, 4, "h_last");
-  const Range cso = range(p->conv_state_out, c.bdk, 4, "conv_state_out");
-  for (const Range& r : inputs) {
-    if (overlaps(out, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
-    if (overlaps(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps %s", r.name);
-    if (overlaps(cso, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
-  }
-  if (overlaps(out, hl)) return fail(SSM_ERR_ALIAS, "out overlaps h_last");
-  if (overlaps(out, cso) || overlaps(hl, cso)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
+ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) { return scan_fwd(p, hip_stream, false); }
 
-  int nseg;
-  int64_t seg_len;
-  size_t ws;
-  if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
-  const Range outs[] = {out, hl, cso};
-  if ((s = check_workspace(p, ws, inputs, outs, 3)) != SSM_OK) return s;
-  if (sz.empty()) {  // the states pass through an empty sequence
-    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = ssm::launch_fill(p->h_last, p->h0, 0.0f, 0.0f, sz.bdn * c.cw, st);
-    if (e == hipSuccess) e = ssm::launch_fill(p->conv_state_out, p->conv_state_in, 0.0f, 0.0f, c.bdk, st);
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
-    return ok();
-  }
-
-  ssm::ScanPlan plan = scan_plan(p, c, nseg, seg_len, ws);
-  plan.out = p->out;
-  plan.h_last = p->h_last;
-  plan.conv_state_out = p->conv_state_out;
-  plan.Cm = p->Cm;
-  plan.z = p->z;
-  plan.Dskip = p->Dskip;
-  plan.h0 = p->h0;
-  const hipError_t e = c.cplx ? ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream))
-                              : ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
+ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, void* hip_stream) { return scan_fwd(p, hip_stream, true); }
 
 ssm_status ssm_scan_aggregate_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");

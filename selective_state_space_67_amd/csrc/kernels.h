@@ -189,6 +189,11 @@ size_t cplx_bwd_partial_floats(int64_t B, int64_t D, int64_t L, int64_t N, int n
 int64_t cplx_bwd_grid_blocks(int64_t B, int64_t D, int nsegb);
 hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream_t stream);
 
+// Scratch of the allocation-free forward (scan_noalloc.hip): its size, and its
+// address on the current device (looked up on the first call per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 // Outputs of empty problems: dst[i] = src[i] (src given) or v0 / v1 at even /
 // odd i, for n floats (nothing for dst = null or n = 0).
 hipError_t launch_fill(float* dst, const float* src, float v0, float v1, int64_t n, hipStream_t stream);

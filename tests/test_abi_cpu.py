@@ -44,7 +44,7 @@ def test_struct_layout_and_version(lib):
     assert lib.ssm_abi_struct_size(1) == ctypes.sizeof(bd.UpdateParams)
     assert lib.ssm_abi_struct_size(2) == ctypes.sizeof(bd.BwdParams)
     assert lib.ssm_abi_struct_size(7) == 0
-    assert lib.ssm_version() == 10800
+    assert lib.ssm_version() == 10900
     for code, name in bd.STATUS_NAMES.items():
         assert lib.ssm_status_string(code).decode() == name
     assert lib.ssm_status_string(99).decode() == "unknown status"
@@ -192,6 +192,46 @@ def test_workspace_size_and_requirement(lib):
     p.workspace_bytes = n.value
     p.workspace = p.u                                      # overlapping an input
     assert scan_status(lib, p) == 7
+
+
+def sized_scan_params(Bt, Dd, Lq, Nn, **kw):
+    """Scan parameters over fake, disjoint, aligned addresses sized for (Bt, Dd, Lq, Nn)."""
+    p = bd.ScanParams()
+    p.batch, p.dim, p.seqlen, p.dstate = Bt, Dd, Lq, Nn
+    p.in_dtype, p.out_dtype = bd.SSM_BF16, bd.SSM_F32
+    addr = [BASE]
+
+    def take(nbytes):
+        a = addr[0]
+        addr[0] += (nbytes + 4095) // 4096 * 4096
+        return a
+
+    p.u, p.dt_raw, p.z = take(Bt * Dd * Lq * 2), take(Bt * Dd * Lq * 2), take(Bt * Dd * Lq * 2)
+    p.Bm, p.Cm = take(Bt * Lq * Nn * 2), take(Bt * Lq * Nn * 2)
+    p.A, p.dt_bias, p.Dskip = take(Dd * Nn * 4), take(Dd * 4), take(Dd * 4)
+    p.out = take(Bt * Dd * Lq * 4)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_noalloc_checks_like_the_forward_and_refuses_large_splits(lib):
+    # the same host checks as ssm_scan_fwd, before any device work
+    assert lib.ssm_scan_fwd_noalloc(None, None) == 1
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(scan_params(u=0)), None) == 1
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(scan_params(dstate=0)), None) == 2
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(scan_params(out=BASE)), None) == 7
+    # a split whose aggregates exceed the library's scratch is refused
+    # (64 pieces x 4096 channels x 256 states: 2 x 63 x 4096 x 256 x 4 bytes)
+    p = sized_scan_params(1, 4096, 1024, 256, num_segments=64)
+    n = ctypes.c_size_t(0)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 63 * 4096 * 256 * 4 > 16 << 20
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(p), None) == 6
+    assert b"scratch" in lib.ssm_last_error()
+    # the caller's workspace fields are not consulted
+    p.workspace, p.workspace_bytes = BASE + 0x70000000, n.value
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(p), None) == 6
 
 
 def test_automatic_split_only_for_long_sequences_with_few_channels(lib):
