@@ -92,7 +92,7 @@ def scan_source_hash() -> str:
 def recorded_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary of this
     workload, if the kernel source is unchanged since it was taken."""
-    path = os.path.join(COUNTERS_DIR, "scan_counters_%s.md" % workload)
+    path = os.path.join(COUNTERS_DIR, "scan_forward_%s.md" % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
