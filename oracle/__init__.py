@@ -37,11 +37,18 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def library_path() -> str:
+    """liboracle.so, or the build named by SSM_ORACLE_LIBRARY (the sanitizer tier's instrumented copy)."""
+    return os.environ.get("SSM_ORACLE_LIBRARY", _LIB)
+
+
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        path = library_path()
+        if path == _LIB:
+            build()
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_scan_rows.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p, p,

@@ -403,6 +403,13 @@ ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
   } else if ((s = check_workspace(p, ws, inputs, outs, 3)) != SSM_OK) {
     return s;
   }
+  SSM_LOG("%s: B %lld D %lld L %lld N %lld, %s state, %s in, %s out, %s, conv width %lld, resets %d; %d pieces of "
+          "%lld steps, workspace %zu bytes%s",
+          noalloc ? "ssm_scan_fwd_noalloc" : "ssm_scan_fwd", (long long)p->batch, (long long)p->dim,
+          (long long)p->seqlen, (long long)p->dstate, c.cplx ? "complex" : "real",
+          p->in_dtype == SSM_BF16 ? "bf16" : "f32", p->out_dtype == SSM_BF16 ? "bf16" : "f32",
+          p->discretization == SSM_DISC_ZOH ? "zoh" : "delta B", (long long)c.K, p->reset != nullptr, nseg,
+          (long long)seg_len, ws, noalloc ? " (library scratch)" : "");
   if (sz.empty()) {  // the states pass through an empty sequence
     const hipStream_t st = static_cast<hipStream_t>(hip_stream);
     hipError_t e = ssm::launch_fill(p->h_last, p->h0, 0.0f, 0.0f, sz.bdn * c.cw, st);
@@ -587,6 +594,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_bwd_params* p, void* hip_stream) {
   sp.conv_k = static_cast<int>(K);
   sp.uconv_out = p->conv_w ? reinterpret_cast<float*>(ws + lay.off_uconv) : nullptr;
   sp.zoh = p->discretization == SSM_DISC_ZOH;
+  SSM_LOG("ssm_scan_bwd: B %lld D %lld L %lld N %lld, %s state; checkpoint sweep in %d pieces of %lld steps, "
+          "reverse sweep in %d segments of %lld steps, workspace %zu bytes",
+          (long long)p->batch, (long long)p->dim, (long long)p->seqlen, (long long)p->dstate,
+          cplx ? "complex" : "real", lay.nseg, (long long)lay.seg_len, lay.nsegb, (long long)lay.seg_steps,
+          lay.total);
   hipError_t e = hipSuccess;
   if (!cplx) {
     e = ssm::launch_scan(sp, stream);
@@ -702,6 +714,9 @@ ssm_status ssm_scan_aggregate(const ssm_scan_params* p, float* P, float* H, void
   if ((s = plan_aggregate(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
   const Range outs[] = {rp, rh};
   if ((s = check_workspace(p, ws, inputs, outs, 2)) != SSM_OK) return s;
+  SSM_LOG("ssm_scan_aggregate: B %lld D %lld L %lld N %lld, %s state; %d pieces of %lld steps, workspace %zu bytes",
+          (long long)p->batch, (long long)p->dim, (long long)p->seqlen, (long long)p->dstate,
+          c.cplx ? "complex" : "real", nseg, (long long)seg_len, ws);
   if (c.sz.empty()) {  // an empty sequence is the identity map: P = 1, H = 0
     const hipStream_t st = static_cast<hipStream_t>(hip_stream);
     hipError_t e = ssm::launch_fill(P, nullptr, 1.0f, c.cplx ? 0.0f : 1.0f, c.sz.bdn * c.cw, st);
@@ -809,6 +824,9 @@ ssm_status ssm_state_update(const ssm_update_params* p, void* hip_stream) {
   plan.conv_b = p->conv_b;
   plan.conv_k = static_cast<int>(K);
   plan.zoh = p->discretization == SSM_DISC_ZOH;
+  SSM_LOG("ssm_state_update: B %lld D %lld N %lld, %s state, %s in, conv width %lld", (long long)p->batch,
+          (long long)p->dim, (long long)p->dstate, cplx ? "complex" : "real", plan.in_bf16 ? "bf16" : "f32",
+          (long long)K);
   hipError_t e = cplx ? ssm::launch_state_update_cplx(plan, static_cast<hipStream_t>(hip_stream))
                       : ssm::launch_state_update(plan, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "state update launch failed: %s", hipGetErrorString(e));

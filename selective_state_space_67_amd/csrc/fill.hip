@@ -27,6 +27,8 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ dst, cons
 hipError_t launch_fill(float* dst, const float* src, float v0, float v1, int64_t n, hipStream_t stream) {
   if (!dst || n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  SSM_LOG("launch fill_kernel: %lld floats; grid %lld x 256 threads", static_cast<long long>(n),
+          static_cast<long long>(blocks));
   hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, dst, src, v0, v1, n);
   return hipGetLastError();
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "log.h"
+
 namespace ssm {
 
 // One scan launch after validation. Pointers are device pointers; optional

@@ -822,6 +822,10 @@ hipError_t launch_bwd_reduce(const float* partB, const float* partC, const float
   r.dbias = dbias;
   const int64_t total = 2 * ((r.bln + 3) / 4) + (r.dn + 3) / 4 + 2 * ((r.D + 3) / 4);
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  SSM_LOG("launch bwd_reduce_kernel: %lld partial sets of dB/dC over %lld (b, l, n), %lld of dA/dD/dbias; "
+          "grid %lld x 256 threads",
+          static_cast<long long>(groups), static_cast<long long>(bln), static_cast<long long>(bs),
+          static_cast<long long>(blocks));
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, r);
   return hipGetLastError();
 }
@@ -870,6 +874,10 @@ hipError_t launch_scan_bwd(const BwdPlan& pl, hipStream_t stream) {
   hipError_t e = with_bwd_tile(pl.N, [&](auto tile) {
     using TL = decltype(tile);
     const dim3 grid(static_cast<unsigned>(a.nblocks)), block(kThreads);
+    SSM_LOG("launch scan_bwd_kernel<BwdTile<%d>>: %s in, reset %d, zoh %d; grid %d x %d threads (%d channels x "
+            "%d states per workgroup), %d reverse segments of %lld steps",
+            TL::LPC, pl.in_bf16 ? "bf16" : "f32", reset, pl.zoh, a.nblocks, kThreads, TL::CPW, TL::NPADC,
+            pl.nsegb, static_cast<long long>(pl.seg_steps));
     if (pl.zoh) {
       if (pl.in_bf16) {
         if (reset)
@@ -921,12 +929,15 @@ hipError_t launch_conv_bwd(const BwdPlan& pl, hipStream_t stream) {
   c.dstate = pl.dconv_state;
   c.part = pl.conv_part;
   const dim3 cgrid(static_cast<unsigned>(pl.B * pl.D * c.ntiles));
+  SSM_LOG("launch conv_bwd_kernel: width %d, %d tiles of %d steps; grid %u x 256 threads", c.K, c.ntiles, kConvTile,
+          cgrid.x);
   if (pl.in_bf16)
     hipLaunchKernelGGL(conv_bwd_kernel<bf16_t>, cgrid, dim3(256), 0, stream, c);
   else
     hipLaunchKernelGGL(conv_bwd_kernel<float>, cgrid, dim3(256), 0, stream, c);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  SSM_LOG("launch conv_param_reduce_kernel: grid %lld x 256 threads", static_cast<long long>((pl.D * 5 + 255) / 256));
   hipLaunchKernelGGL(conv_param_reduce_kernel, dim3(static_cast<unsigned>((pl.D * 5 + 255) / 256)), dim3(256), 0,
                      stream, pl.B, pl.D, pl.conv_k, c.ntiles, static_cast<const float*>(pl.conv_part), pl.dconv_w,
                      pl.dconv_b);

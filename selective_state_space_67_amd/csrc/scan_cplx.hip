@@ -476,11 +476,19 @@ hipError_t launch_cplx(const ScanPlan& p, const CplxArgs& a, int agg_pieces, boo
       using InT = decltype(in_t);
       constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value, C = decltype(conv)::value;
       if (agg_pieces > 0) {
+        SSM_LOG("launch cplx_scan_kernel<%d> aggregate: %s in, reset %d, zoh %d, conv %d; grid %u x %d threads "
+                "(%d channels per workgroup), %d pieces of %lld steps",
+                NPL, sizeof(InT) == 2 ? "bf16" : "f32", R, Z, C, grid_agg.x, kThreads, kCPW, agg_pieces,
+                static_cast<long long>(p.seg_len));
         hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, true, Z, C>), grid_agg, dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || !full) return e;
       }
       if (!full) return hipSuccess;
+      SSM_LOG("launch cplx_scan_kernel<%d> full: %s in, reset %d, zoh %d, conv %d; grid %u x %d threads "
+              "(%d channels per workgroup), %d pieces of %lld steps",
+              NPL, sizeof(InT) == 2 ? "bf16" : "f32", R, Z, C, grid.x, kThreads, kCPW, p.nseg,
+              static_cast<long long>(p.seg_len));
       hipLaunchKernelGGL((cplx_scan_kernel<NPL, InT, R, false, Z, C>), grid, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };
@@ -537,6 +545,8 @@ hipError_t launch_aggregate_cplx(const ScanPlan& p, float* P, float* H, hipStrea
   a.ws_H = p.nseg > 1 ? p.ws + 2 * static_cast<size_t>(p.nseg) * count : H;
   hipError_t e = launch_cplx(p, a, p.nseg, false, stream);
   if (e != hipSuccess || p.nseg == 1) return e;
+  SSM_LOG("launch cplx_aggregate_fold_kernel: %lld states, %d pieces; grid %lld x 256 threads",
+          static_cast<long long>(count), p.nseg, static_cast<long long>((count + 255) / 256));
   hipLaunchKernelGGL(cplx_aggregate_fold_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
                      stream, reinterpret_cast<const float2*>(a.ws_P), reinterpret_cast<const float2*>(a.ws_H),
                      p.nseg, count, reinterpret_cast<float2*>(P), reinterpret_cast<float2*>(H));
@@ -568,6 +578,8 @@ hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
   auto go = [&](auto npl, auto zoh, auto st) {
     constexpr int NPL = decltype(npl)::value;
     constexpr bool Z = decltype(zoh)::value, S = decltype(st)::value;
+    SSM_LOG("launch cplx_update_kernel<%d>: %s in, zoh %d, streamed state %d; grid %u x %d threads", NPL,
+            p.in_bf16 ? "bf16" : "f32", Z, S, grid.x, kThreads);
     if (p.in_bf16)
       hipLaunchKernelGGL((cplx_update_kernel<NPL, bf16_t, Z, S>), grid, dim3(kThreads), 0, stream, a);
     else

@@ -678,12 +678,17 @@ hipError_t launch_scan_cplx_bwd(const ScanPlan& sp, const BwdPlan& bp, hipStream
     auto run = [&](auto in_t, auto has_reset, auto zoh) {
       using InT = decltype(in_t);
       constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
+      SSM_LOG("launch cplx_ckpt_kernel<%d>: %s in, reset %d, zoh %d, conv %d; grid %u x %d threads, %d pieces of "
+              "%lld steps", NPL, sizeof(InT) == 2 ? "bf16" : "f32", R, Z, bp.conv_w != nullptr, grid_ck.x, kThreads,
+              sp.nseg, static_cast<long long>(sp.seg_len));
       if (bp.conv_w)
         hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, true, Z>), grid_ck, dim3(kThreads), 0, stream, a);
       else
         hipLaunchKernelGGL((cplx_ckpt_kernel<NPL, InT, R, false, Z>), grid_ck, dim3(kThreads), 0, stream, a);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
+      SSM_LOG("launch cplx_bwd_kernel<%d>: grid %u x %d threads, %d reverse segments of %lld steps", NPL,
+              grid_bwd.x, kThreads, bp.nsegb, static_cast<long long>(bp.seg_steps));
       hipLaunchKernelGGL((cplx_bwd_kernel<NPL, InT, R, Z>), grid_bwd, dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     };

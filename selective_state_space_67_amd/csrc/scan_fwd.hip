@@ -128,6 +128,8 @@ hipError_t launch_aggregate(const ScanPlan& pl, float* P, float* H, hipStream_t 
   const int per_piece = static_cast<int>(pl.B) * a.n_dgroups;
   hipError_t e = launch(pl, a, 0, per_piece * pl.nseg, false, stream);
   if (e != hipSuccess || pl.nseg == 1) return e;
+  SSM_LOG("launch aggregate_fold_kernel: %lld states, %d pieces; grid %lld x 256 threads",
+          static_cast<long long>(count), pl.nseg, static_cast<long long>((count + 255) / 256));
   hipLaunchKernelGGL(aggregate_fold_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream,
                      a.ws_P, a.ws_H, pl.nseg, count, P, H);
   return hipGetLastError();

@@ -828,6 +828,14 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   }
 }
 
+template <typename TL, typename InT>
+void log_tile_launch(const char* mode, const ScanArgs& a, int nblocks, bool reset, bool conv, bool zoh) {
+  SSM_LOG("launch scan_kernel<Tile<%d,%d>> %s: %s in, reset %d, conv %d, zoh %d; grid %d x %d threads "
+          "(%d channels x %d states per workgroup, %d-step chunks), %d pieces of %lld steps",
+          TL::NPL, TL::RPC, mode, sizeof(InT) == 2 ? "bf16" : "f32", reset, conv, zoh, nblocks, TL::THREADS,
+          TL::CPW, TL::NPAD, TL::T, a.nseg, static_cast<long long>(a.seg_len));
+}
+
 template <typename TL, typename InT, bool HAS_RESET, bool CONV, bool ZOH>
 hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, bool checkpoint,
                        hipStream_t stream) {
@@ -836,6 +844,7 @@ hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, 
   if (nblocks_agg > 0) {
     ScanArgs agg = args;
     agg.nblocks = nblocks_agg;
+    log_tile_launch<TL, InT>("aggregate", agg, nblocks_agg, HAS_RESET, CONV, ZOH);
     hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kAggregate, CONV, ZOH>), dim3(nblocks_agg),
                        dim3(TL::THREADS), 0, stream, agg);
     hipError_t e = hipGetLastError();
@@ -844,6 +853,7 @@ hipError_t launch_tile(const ScanArgs& args, int nblocks_full, int nblocks_agg, 
   if (nblocks_full == 0) return hipSuccess;
   ScanArgs full = args;
   full.nblocks = nblocks_full;
+  log_tile_launch<TL, InT>(checkpoint ? "checkpoint" : "full", full, nblocks_full, HAS_RESET, CONV, ZOH);
   if (checkpoint)
     hipLaunchKernelGGL((scan_kernel<TL, InT, HAS_RESET, kCheckpoint, CONV, ZOH>), dim3(nblocks_full),
                        dim3(TL::THREADS), 0, stream, full);

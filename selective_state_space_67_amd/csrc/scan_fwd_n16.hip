@@ -366,6 +366,9 @@ hipError_t launch_n16(const ScanArgs& args, int nblocks_full, int nblocks_agg, h
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
+  SSM_LOG("launch scan16_kernel full: %s in, reset %d; grid %d x 256 threads (16 channels x 16 states per "
+          "workgroup, 32-step chunks), %d pieces of %lld steps",
+          args.in_bf16 ? "bf16" : "f32", reset, nblocks_full, args.nseg, static_cast<long long>(args.seg_len));
   if (args.in_bf16) {
     if (reset)
       hipLaunchKernelGGL((scan16_kernel<bf16_t, true>), dim3(nblocks_full), dim3(256), 0, stream, full);

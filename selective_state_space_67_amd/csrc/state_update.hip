@@ -246,6 +246,10 @@ hipError_t launch_vec(const UpdateArgs& a, hipStream_t stream) {
   constexpr int RPT = 2;
   const int64_t rows_per_block = static_cast<int64_t>(kThreads / LR) * RPT;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  SSM_LOG("launch state_update_vec4<%d lanes per row, %d rows per thread>: %s in, streamed state %d; grid %lld x "
+          "%d threads",
+          LR, RPT, sizeof(InT) == 2 ? "bf16" : "f32", a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes,
+          static_cast<long long>(blocks), kThreads);
   if (a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes)
     hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
                        0, stream, a);
@@ -259,6 +263,8 @@ template <typename InT, int LR>
 hipError_t launch_scalar(const UpdateArgs& a, hipStream_t stream) {
   const int64_t rows_per_block = kThreads / LR;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  SSM_LOG("launch state_update_scalar<%d lanes per row>: %s in; grid %lld x %d threads", LR,
+          sizeof(InT) == 2 ? "bf16" : "f32", static_cast<long long>(blocks), kThreads);
   hipLaunchKernelGGL((state_update_scalar<InT, LR>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();

@@ -574,3 +574,37 @@ def test_empty_bwd_is_valid(lib, cplx, kw):
     assert bwd_status(lib, p) == 0, lib.ssm_last_error()
     p.dim = 3                          # dA (D, N) is not empty: required
     assert bwd_status(lib, p) == 1 and b"A" in lib.ssm_last_error()
+
+
+# ---------------------------------------------------------------- launch log
+# SSM_LOG is read once per process, so each case runs in a fresh interpreter.
+LOG_CALL = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from selective_state_space_67_amd import binding as bd
+lib = bd.load_library()
+p = bd.ScanParams()
+p.batch, p.dim, p.seqlen, p.dstate = 2, 32, 0, 16
+p.in_dtype, p.out_dtype = bd.SSM_BF16, bd.SSM_F32
+p.A, p.dt_bias, p.Dskip = 0x10000000, 0x10010000, 0x10020000
+assert lib.ssm_scan_fwd(ctypes.byref(p), None) == 0, lib.ssm_last_error()
+"""
+
+
+@pytest.mark.parametrize("value,logged", [("1", True), ("0", False), (None, False)])
+def test_launch_log_follows_ssm_log(lib, value, logged):
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("SSM_LOG", None)
+    if value is not None:
+        env["SSM_LOG"] = value
+    res = subprocess.run([sys.executable, "-c", LOG_CALL, ROOT], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    lines = [ln for ln in res.stderr.splitlines() if ln.startswith("[ssm] ")]
+    if logged:
+        assert lines == ["[ssm] ssm_scan_fwd: B 2 D 32 L 0 N 16, real state, bf16 in, f32 out, delta B, conv width 0, "
+                         "resets 0; 1 pieces of 0 steps, workspace 0 bytes"], res.stderr
+    else:
+        assert lines == [], res.stderr

@@ -312,3 +312,44 @@ def test_longest_sequence_sampled_rows():
                            Dskip=x["Dskip"])
     margin = assert_close(got, ref, wl.BF16)
     log("longest sequence: max err/bound %.3g" % margin)
+
+
+# ---------------------------------------------------------------------------- launch log
+
+LOG_RUN = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import torch
+from selective_state_space_67_amd import ssm_scan_fwd
+dev = torch.device("cuda:0")
+g = torch.Generator(device="cpu").manual_seed(0)
+for (B, D, L, N) in ((2, 32, 64, 16), (1, 24, 50, 128)):
+    u = torch.randn(B, D, L, generator=g).to(dev)
+    dt = torch.randn(B, D, L, generator=g).to(dev)
+    A = -torch.rand(D, N, generator=g).to(dev)
+    Bm = torch.randn(B, L, N, generator=g).to(dev)
+    Cm = torch.randn(B, L, N, generator=g).to(dev)
+    out = ssm_scan_fwd(u, dt, A, Bm, Cm)
+torch.cuda.synchronize()
+"""
+
+
+def test_launch_log_names_kernels_and_grids():
+    """With SSM_LOG=1 each call prints its plan and each launch its kernel, tile and grid."""
+    import os
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SSM_LOG="1")
+    log("launch log: 2x32x64 N=16 and 1x24x50 N=128 in a child process")
+    res = subprocess.run([sys.executable, "-c", LOG_RUN, root], env=env, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = [ln for ln in res.stderr.splitlines() if ln.startswith("[ssm] ")]
+    assert len(lines) == 4, lines
+    assert lines[0].startswith("[ssm] ssm_scan_fwd: B 2 D 32 L 64 N 16, real state, f32 in, f32 out")
+    # 16 states, even length: the 16-state pass, 2 batches x 2 groups of 16 channels
+    assert lines[1].startswith("[ssm] launch scan16_kernel full: f32 in, reset 0; grid 4 x 256 threads"), lines[1]
+    assert lines[2].startswith("[ssm] ssm_scan_fwd: B 1 D 24 L 50 N 128")
+    # 128 states: two states per lane over four rows, 8 channels per workgroup -> 3 workgroups
+    assert lines[3].startswith("[ssm] launch scan_kernel<Tile<2,4>> full: f32 in, reset 0, conv 0, zoh 0; "
+                               "grid 3 x 512 threads (8 channels x 128 states per workgroup"), lines[3]
