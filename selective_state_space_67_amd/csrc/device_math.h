@@ -108,4 +108,29 @@ __device__ __forceinline__ float row_shr1(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
 }
 
+// Wave priority from the share of a workgroup's work already done. The
+// instruction arbiter of a SIMD favours its oldest waves, so of the
+// workgroups sharing a CU the first-placed ones race ahead and the last one
+// ends alone, with too few waves to hide latency. Dropping a wave's priority
+// each time it completes another quarter of its work lets the workgroups that
+// are behind catch up, so that they end closer together.
+class ProgressPriority {
+ public:
+  __device__ explicit ProgressPriority(int total) : q1_(total / 4), q2_(total / 2), q3_(total - total / 4) {}
+  // `done`: units of work (chunks) completed so far, the same for every wave of the workgroup
+  __device__ __forceinline__ void update(int done) const {
+    if (done < q1_)
+      __builtin_amdgcn_s_setprio(3);
+    else if (done < q2_)
+      __builtin_amdgcn_s_setprio(2);
+    else if (done < q3_)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  }
+
+ private:
+  int q1_, q2_, q3_;
+};
+
 }  // namespace ssm

@@ -208,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
   if (CONV && dvalid) conv_taps(a.conv_w, a.conv_b, d, a.conv_k, cw, cb);
   const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
+  const ProgressPriority prio((Lseg + kT - 1) / kT);
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
+    prio.update(t0 / kT);
     const int steps = min(kT, Lseg - t0);
     __syncthreads();  // the previous chunk's readers are done
     stage_bc<NPAD>(s_bc, Bb + static_cast<int64_t>(t0) * N * 2, Cb + static_cast<int64_t>(t0) * N * 2, steps, N, tid);
@@ -371,7 +373,10 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
   const int64_t gbl = (static_cast<int64_t>(g) * a.B + b) * a.L;  // partial row of this group and batch row
   float dD_acc = 0.0f, dbias_acc = 0.0f;
 
-  for (int64_t t0 = s_t0 + (s_t1 - s_t0 - 1) / kT * kT; t0 >= s_t0; t0 -= kT) {
+  const int64_t t_last = s_t0 + (s_t1 - s_t0 - 1) / kT * kT;
+  const ProgressPriority prio(static_cast<int>((t_last - s_t0) / kT) + 1);
+  for (int64_t t0 = t_last; t0 >= s_t0; t0 -= kT) {
+    prio.update(static_cast<int>((t_last - t0) / kT));
     const int steps = static_cast<int>(min<int64_t>(kT, a.L - t0));
     __syncthreads();  // the previous chunk's readers are done
     stage_bc<NPAD>(s_bc, Bb + t0 * N * 2, Cb + t0 * N * 2, steps, N, tid);

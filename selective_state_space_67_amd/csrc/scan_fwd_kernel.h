@@ -166,13 +166,18 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   constexpr int DU_COPY = CPW * DU_STRIDE + 16;
   //  (B, C): one row per state; windows start at multiples of 16 and never wrap.
   constexpr int BC_STRIDE = RING + 2;
-  //  The aggregate pass needs B only: one float per (state, step), row stride
-  //  RING + 4 floats, so that a 16-byte read covers four steps and the 16
-  //  rows read by a DPP row fall in different banks.
-  constexpr int B_STRIDE = RING + 4;
-  //  The checkpoint sweep stages B and C as two such float arrays, and dy (the
-  //  gate-weighted output gradient) per (channel, step) with the same stride.
-  constexpr int BC_FLOATS = CKPT ? 2 * NPAD * B_STRIDE : 2 * NPAD * BC_STRIDE;
+  //  The lockstep passes (aggregate, checkpoint) read B (and the checkpoint
+  //  sweep C) as floats: one row per lane, holding the NPL states of that
+  //  lane side by side for every step, row stride RING * NPL + 4 floats. A
+  //  lane's values of consecutive steps are then one contiguous 16-byte read,
+  //  and consecutive lanes' reads start 4 banks apart, so the 16 lanes of a
+  //  read pass cover the 64 banks once. (A row per state puts the rows of
+  //  lanes with two states 2 x (RING + 4) floats apart, all in 8 banks.)
+  constexpr int LS_STRIDE = RING * NPL + 4;
+  constexpr int C_OFF = (NPAD / NPL) * LS_STRIDE;  // the checkpoint sweep's C rows follow the B rows
+  constexpr int BC_FLOATS = CKPT ? 2 * C_OFF : 2 * NPAD * BC_STRIDE;
+  static_assert(CKPT || C_OFF <= 2 * NPAD * BC_STRIDE, "aggregate B rows fit the (B, C) buffer");
+  //  dy (the gate-weighted output gradient) per (channel, step).
   constexpr int DY_STRIDE = RING + 4;
   // Row staging: CPW x T (channel, step) items per chunk, RI consecutive steps
   // per thread, handled by the first ROW_THREADS threads.
@@ -394,8 +399,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
         s_bc[n * BC_STRIDE + ((par * T + bc_tl(q) + (n / NPL) % 16) & MASK)] =
             make_float2(load_elem(&r.b[q], 0), load_elem(&r.c[q], 0));
       else
-        s_bcf[n * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.b[q], 0);
-      if (CKPT) s_bcf[(NPAD + n) * B_STRIDE + par * T + bc_tl(q)] = load_elem(&r.c[q], 0);
+        s_bcf[(n / NPL) * LS_STRIDE + (par * T + bc_tl(q)) * NPL + n % NPL] = load_elem(&r.b[q], 0);
+      if (CKPT) s_bcf[C_OFF + (n / NPL) * LS_STRIDE + (par * T + bc_tl(q)) * NPL + n % NPL] = load_elem(&r.c[q], 0);
     }
     if (!row_thread) return;
     float dl[RI], dv[RI];
@@ -572,8 +577,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       // Lockstep, like the aggregate pass, plus C and dy per step. The state
       // entering every 16-step chunk is written out, and each backward
       // segment's (segP, segG) at its last step.
-      const float* b_row = s_bcf + nbase * B_STRIDE;
-      const float* c_row = s_bcf + (NPAD + nbase) * B_STRIDE;
+      const float* b_row = s_bcf + (nbase / NPL) * LS_STRIDE;
+      const float* c_row = b_row + C_OFF;
       const float* dy_row = s_dy + c * DY_STRIDE;
       const int64_t tchunk = t_seg + static_cast<int64_t>(J) * T;  // step held in slot par * T
       const int64_t pend = t_seg + Lseg;
@@ -593,8 +598,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
           float B0[NPL], B1[NPL], B2[NPL], B3[NPL], C0[NPL], C1[NPL], C2[NPL], C3[NPL];
 #pragma unroll
           for (int j = 0; j < NPL; ++j) {
-            const float4 vb = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
-            const float4 vc = *reinterpret_cast<const float4*>(c_row + j * B_STRIDE + m);
+            const float4 vb = *reinterpret_cast<const float4*>(b_row + m);
+            const float4 vc = *reinterpret_cast<const float4*>(c_row + m);
             B0[j] = vb.x;
             B1[j] = vb.y;
             B2[j] = vb.z;
@@ -616,15 +621,29 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
           for (int i2 = 0; i2 < 4; i2 += 2) {
             const float4 d01 = *reinterpret_cast<const float4*>(du_row + m + i2);
             const float2 dy2 = *reinterpret_cast<const float2*>(dy_row + m + i2);
+            // steps m + i2 and m + i2 + 1, the lane's NPL states each: 2 x NPL
+            // consecutive floats of B and of C
+            float bt[2 * NPL], ct[2 * NPL];
+#pragma unroll
+            for (int q = 0; q < 2 * NPL; q += 4) {
+              const float4 vb = *reinterpret_cast<const float4*>(b_row + (m + i2) * NPL + q);
+              const float4 vc = *reinterpret_cast<const float4*>(c_row + (m + i2) * NPL + q);
+              bt[q] = vb.x;
+              bt[q + 1] = vb.y;
+              bt[q + 2] = vb.z;
+              bt[q + 3] = vb.w;
+              ct[q] = vc.x;
+              ct[q + 1] = vc.y;
+              ct[q + 2] = vc.z;
+              ct[q + 3] = vc.w;
+            }
             float B0[NPL], B1[NPL], C0[NPL], C1[NPL];
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
-              const float2 vb = *reinterpret_cast<const float2*>(b_row + j * B_STRIDE + m + i2);
-              const float2 vc = *reinterpret_cast<const float2*>(c_row + j * B_STRIDE + m + i2);
-              B0[j] = vb.x;
-              B1[j] = vb.y;
-              C0[j] = vc.x;
-              C1[j] = vc.y;
+              B0[j] = bt[j];
+              B1[j] = bt[NPL + j];
+              C0[j] = ct[j];
+              C1[j] = ct[NPL + j];
             }
             step_ck(d01.x, d01.y, dy2.x, B0, C0);
             step_ck(d01.z, d01.w, dy2.y, B1, C1);
@@ -654,20 +673,29 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       // (delta, delta*u) float4s (broadcast within its DPP row) and one B
       // float4 per state (shared by the rows of a wave). Nothing is stored,
       // so the compiler may issue the reads of the whole chunk early.
-      const float* b_row = reinterpret_cast<const float*>(s_bc) + nbase * B_STRIDE;
+      const float* b_row = reinterpret_cast<const float*>(s_bc) + (nbase / NPL) * LS_STRIDE;
 #pragma unroll
       for (int i = 0; i < T; i += 4) {
         const int m = par * T + i;
         const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
         const float4 d23 = *reinterpret_cast<const float4*>(du_row + m + 2);
+        // steps m .. m + 3, the lane's NPL states each: 4 x NPL consecutive floats
+        float bt[4 * NPL];
+#pragma unroll
+        for (int q = 0; q < 4 * NPL; q += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(b_row + m * NPL + q);
+          bt[q] = v.x;
+          bt[q + 1] = v.y;
+          bt[q + 2] = v.z;
+          bt[q + 3] = v.w;
+        }
         float B0[NPL], B1[NPL], B2[NPL], B3[NPL];
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          const float4 v = *reinterpret_cast<const float4*>(b_row + j * B_STRIDE + m);
-          B0[j] = v.x;
-          B1[j] = v.y;
-          B2[j] = v.z;
-          B3[j] = v.w;
+          B0[j] = bt[j];
+          B1[j] = bt[NPL + j];
+          B2[j] = bt[2 * NPL + j];
+          B3[j] = bt[3 * NPL + j];
         }
         step(i, m, d01.x, d01.y, B0, B0);  // C is not used by the aggregate pass
         step(i + 1, m, d01.z, d01.w, B1, B1);
@@ -752,7 +780,9 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   load_chunk(0, r0);
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
+  const ProgressPriority prio(nchunks);
   for (int J = 0; J < nchunks; J += 2) {
+    prio.update(J);
     // even chunk: ring half 0, register sets r0 / o0
     store_chunk(J, 0, r0, o0);
     if (J + 2 < nchunks) load_chunk(J + 2, r0);

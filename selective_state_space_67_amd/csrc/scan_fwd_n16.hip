@@ -320,7 +320,9 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   load_chunk(0, r0);
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
+  const ProgressPriority prio(nchunks);
   for (int J = 0; J < nchunks; J += 2) {
+    prio.update(J);
     store_chunk(J, 0, r0, o0);
     if (J + 2 < nchunks) load_chunk(J + 2, r0);
     __syncthreads();
