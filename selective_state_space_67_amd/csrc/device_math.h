@@ -112,11 +112,18 @@ __device__ __forceinline__ float row_shr1(float v) {
 // instruction arbiter of a SIMD favours its oldest waves, so of the
 // workgroups sharing a CU the first-placed ones race ahead and the last one
 // ends alone, with too few waves to hide latency. Dropping a wave's priority
-// each time it completes another quarter of its work lets the workgroups that
-// are behind catch up, so that they end closer together.
+// each time it passes another mark of its work lets the workgroups that are
+// behind catch up, so that they end closer together. When the whole grid is
+// resident at once the marks are at 1/2, 3/4 and 7/8 of the work (the spread
+// at the end is what the last stretch lets accumulate); when later
+// workgroups start as earlier ones end, at every quarter (a newcomer at the
+// top priority would otherwise starve the workgroups about to finish).
 class ProgressPriority {
  public:
-  __device__ explicit ProgressPriority(int total) : q1_(total / 4), q2_(total / 2), q3_(total - total / 4) {}
+  __device__ ProgressPriority(int total, bool all_resident)
+      : q1_(all_resident ? total / 2 : total / 4),
+        q2_(all_resident ? total - total / 4 : total / 2),
+        q3_(all_resident ? total - total / 8 : total - total / 4) {}
   // `done`: units of work (chunks) completed so far, the same for every wave of the workgroup
   __device__ __forceinline__ void update(int done) const {
     if (done < q1_)

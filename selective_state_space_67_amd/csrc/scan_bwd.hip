@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
   float hs[kNPL];
   load(nchunks - 1, r);
   load_ckpt(nchunks - 1, hs);
-  const ProgressPriority prio(nchunks);
+  const ProgressPriority prio(nchunks, false);
   for (int J = nchunks - 1; J >= 0; --J) {
     prio.update(nchunks - 1 - J);
     store(J, r, o);

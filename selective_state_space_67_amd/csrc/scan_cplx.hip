@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
   const uint8_t* __restrict__ rs_row = HAS_RESET ? rs - t_seg : nullptr;
   const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
-  const ProgressPriority prio((Lseg + kT - 1) / kT);
+  const ProgressPriority prio((Lseg + kT - 1) / kT, false);
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     prio.update(t0 / kT);
     const int steps = min(kT, Lseg - t0);

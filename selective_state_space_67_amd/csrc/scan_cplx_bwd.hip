@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
   if (CONV && dvalid) conv_taps(a.conv_w, a.conv_b, d, a.conv_k, cw, cb);
   const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
-  const ProgressPriority prio((Lseg + kT - 1) / kT);
+  const ProgressPriority prio((Lseg + kT - 1) / kT, false);
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     prio.update(t0 / kT);
     const int steps = min(kT, Lseg - t0);
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
   float dD_acc = 0.0f, dbias_acc = 0.0f;
 
   const int64_t t_last = s_t0 + (s_t1 - s_t0 - 1) / kT * kT;
-  const ProgressPriority prio(static_cast<int>((t_last - s_t0) / kT) + 1);
+  const ProgressPriority prio(static_cast<int>((t_last - s_t0) / kT) + 1, false);
   for (int64_t t0 = t_last; t0 >= s_t0; t0 -= kT) {
     prio.update(static_cast<int>((t_last - t0) / kT));
     const int steps = static_cast<int>(min<int64_t>(kT, a.L - t0));

@@ -780,7 +780,9 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   load_chunk(0, r0);
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
-  const ProgressPriority prio(nchunks);
+  // workgroups resident per CU at the occupancy bound: 4 SIMDs x waves per SIMD / waves per workgroup
+  constexpr int kResidentPerCU = 4 * kernel_waves_per_simd<TL, MODE, CONV, ZOH>() / TL::WAVES;
+  const ProgressPriority prio(nchunks, a.nblocks <= 256 * kResidentPerCU);
   for (int J = 0; J < nchunks; J += 2) {
     prio.update(J);
     // even chunk: ring half 0, register sets r0 / o0

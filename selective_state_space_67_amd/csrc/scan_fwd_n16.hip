@@ -320,7 +320,8 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   load_chunk(0, r0);
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
-  const ProgressPriority prio(nchunks);
+  // workgroups resident per CU: one wave per SIMD each, as many as the occupancy bound allows
+  const ProgressPriority prio(nchunks, a.nblocks <= 256 * (sizeof(InT) == 2 ? 4 : 3));
   for (int J = 0; J < nchunks; J += 2) {
     prio.update(J);
     store_chunk(J, 0, r0, o0);
