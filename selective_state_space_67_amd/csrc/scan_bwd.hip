@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
 
   struct Raw {
     InT b[BCI], c[BCI], dt[4], z[4], go[4];
-    float u[4];
+    uint32_t u[4];  // raw bits: a float (f32 input or the conv stage's u'), or a bf16 in the low half
     uint8_t rs[4];
   };
   struct Out {
@@ -246,7 +246,11 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
       const int t = l + 4 * G;
       const bool ok = fin && dvalid && tc + t < pend;
       const int64_t off = rowbase + tc + t;
-      r.u[G] = ok ? (a.uconv ? a.uconv[off] : load_elem(u_in, off)) : 0.0f;
+      // kept as loaded and converted at staging: a conversion here would wait for the load
+      if constexpr (sizeof(InT) == 2)
+        r.u[G] = ok ? (a.uconv ? __float_as_uint(a.uconv[off]) : static_cast<uint32_t>(u_in[off].bits)) : 0u;
+      else
+        r.u[G] = ok ? __float_as_uint(a.uconv ? a.uconv[off] : load_elem(u_in, off)) : 0u;
       r.dt[G] = ok ? dt_in[off] : InT{};
       r.z[G] = ok && z_in ? z_in[off] : InT{};
       r.go[G] = ok ? go_in[off] : InT{};
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
       const bool ok = dvalid && tc + t < pend;
       const float x = load_elem(&r.dt[G], 0) + bias;
       float dl = ok ? softplus_f32(x) : 0.0f;
-      const float uu = r.u[G];
+      const float uu = __uint_as_float(sizeof(InT) == 2 && !a.uconv ? r.u[G] << 16 : r.u[G]);
       const float go = load_elem(&r.go[G], 0);
       float dy = go, gz = 0.0f;
       if (z_in) {
@@ -356,6 +360,11 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
         if (t & 1) hist[t >> 1][j] = h[j];
       }
     }
+
+    // The next chunk's loads (issued before this chunk) have landed by now:
+    // wait for them here, before this chunk issues its gradient stores, so
+    // that the loop does not wait at its end for those stores to complete.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     float F1 = 0.0f, F2 = 0.0f, FY = 0.0f, F3 = 0.0f;  // this lane's step sums in the current group of four
 
