@@ -31,6 +31,13 @@ __device__ __forceinline__ void store_elem(bf16_t* p, int64_t i, float v) {
   b += 0x7FFFu + ((b >> 16) & 1u);
   p[i].bits = static_cast<uint16_t>(b >> 16);
 }
+// Two floats as bfloat16 (same rounding as store_elem), lo in the low half.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
 
 // 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32); both
 // are within ~2 ulp of the correctly rounded value on gfx950.

@@ -133,6 +133,7 @@ __device__ __forceinline__ float chan_sum(float v) {
   return v;
 }
 
+
 __device__ __forceinline__ void store_grad(const BwdArgs& a, void* p, int64_t i, float v) {
   if (a.grad_bf16)
     store_elem(static_cast<bf16_t*>(p), i, v);
@@ -163,6 +164,16 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
   constexpr int AT = FP * NPADC + 32;   // floats per type
   constexpr int AW = 2 * AT;            // floats per wave
   __shared__ float s_acc[kWaves * AW];
+  // The input gradients (du or the conv stage's du', d dt_raw, dz) of a pair
+  // of chunks, [gradient][channel][step]: written out together once the pair
+  // is done, as whole rows of 32 steps (128 bytes in float32) rather than the
+  // 4 steps the finalizing lanes of a channel hold at a time, so that the L2
+  // does not write back partially filled lines. Layouts with few channels per
+  // workgroup (N > 64) store directly: there the dB/dC partials dominate the
+  // traffic, and staging measured slower (2x2048x4096x128: 4.70 -> 4.82 ms).
+  constexpr bool STAGE_OUT = LPC <= 16;
+  constexpr int OS = 2 * kK + 4;        // floats per (gradient, channel) row
+  __shared__ __align__(16) float s_out[STAGE_OUT ? 3 * CPW * OS : 4];
 
   int idx = blockIdx.x;
   if ((a.nblocks & 7) == 0) idx = (idx & 7) * (a.nblocks >> 3) + (idx >> 3);
@@ -325,6 +336,42 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
     for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? a.ckpt[ci + n0 + j] : 0.0f;
   };
 
+  // The chunk pair (J, J + 1) of input gradients from s_out to memory: one
+  // item per (gradient, channel, 4 steps), 16-byte stores (8-byte in bf16)
+  // where the 4 steps are complete and aligned.
+  auto flush_out = [&](int J) {
+    constexpr int GROUPS = 2 * kK / 4;
+    const int64_t t0 = t_seg + static_cast<int64_t>(J) * kK;
+    const int steps = static_cast<int>(min<int64_t>(2 * kK, pend - t0));
+    for (int i = tid; i < 3 * CPW * GROUPS; i += kThreads) {
+      const int q = i % GROUPS, cc = (i / GROUPS) % CPW, kind = i / (GROUPS * CPW);
+      const int64_t dd = d0 + cc;
+      const int s0 = 4 * q;
+      if (dd >= a.D || s0 >= steps || (kind == 2 && !a.dz)) continue;
+      const float4 v = *reinterpret_cast<const float4*>(s_out + (kind * CPW + cc) * OS + s0);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+      const int cnt = min(4, steps - s0);
+      const int64_t at = (static_cast<int64_t>(b) * a.D + dd) * a.L + t0 + s0;
+      const bool f32 = (kind == 0 && a.du_conv) || !a.grad_bf16;
+      void* const dst = kind == 0 ? (a.du_conv ? static_cast<void*>(a.du_conv) : a.du) : kind == 1 ? a.ddt : a.dz;
+      if (f32) {
+        float* p = static_cast<float*>(dst) + at;
+        if (cnt == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+          *reinterpret_cast<float4*>(p) = v;
+        } else {
+          for (int k = 0; k < cnt; ++k) p[k] = e[k];
+        }
+      } else {
+        bf16_t* p = static_cast<bf16_t*>(dst) + at;
+        if (cnt == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+          *reinterpret_cast<uint2*>(p) = make_uint2(bf16_pair(e[0], e[1]), bf16_pair(e[2], e[3]));
+        } else {
+          for (int k = 0; k < cnt; ++k) store_elem(p, k, e[k]);
+        }
+      }
+    }
+  };
+
   auto chunk = [&](int J, const Out& o, const float (&hs)[kNPL]) {
     const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
     // States of the chunk: the checkpoint hs, then h_t of every odd step in
@@ -447,12 +494,19 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
           const float du = __builtin_fmaf(dyf, dsk, ZOH ? F1 : dlf * F1);
           const float dx = __builtin_fmaf(o.u[G], ZOH ? F3 : F1, F2) * o.sig[G];
           const float dz = o.gz[G] * __builtin_fmaf(dsk, o.u[G], FY);
-          if (a.du_conv)
-            a.du_conv[rowbase + tg] = du;  // the conv backward takes it from here
-          else
-            store_grad(a, a.du, rowbase + tg, du);
-          store_grad(a, a.ddt, rowbase + tg, dx);
-          if (a.dz) store_grad(a, a.dz, rowbase + tg, dz);
+          if constexpr (STAGE_OUT) {
+            const int tl = (J & 1) * kK + tf;  // step within the chunk pair
+            s_out[c * OS + tl] = du;
+            s_out[(CPW + c) * OS + tl] = dx;
+            s_out[(2 * CPW + c) * OS + tl] = dz;
+          } else {
+            if (a.du_conv)
+              a.du_conv[rowbase + tg] = du;  // the conv backward takes it from here
+            else
+              store_grad(a, a.du, rowbase + tg, du);
+            store_grad(a, a.ddt, rowbase + tg, dx);
+            if (a.dz) store_grad(a, a.dz, rowbase + tg, dz);
+          }
           dD_acc = __builtin_fmaf(dyf, o.u[G], dD_acc);
           dbias_acc += dx;
         }
@@ -495,6 +549,9 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
     }
     __syncthreads();  // totals of the chunk's first period complete; LDS parameters free
     flush(tc, 0);
+    if constexpr (STAGE_OUT) {
+      if ((J & 1) == 0) flush_out(J);
+    }
   };
 
   Raw r;
@@ -787,7 +844,10 @@ void plan_bwd_segments(int64_t B, int64_t D, int64_t L, int64_t N, bool zoh, int
   int64_t best = 1, best_cost = -1;
   const int64_t max_seg = std::min<int64_t>(chunks, 4096);
   for (int64_t ns = 1; ns <= max_seg; ++ns) {
-    const int64_t per = (chunks + ns - 1) / ns;
+    // an even number of chunks per segment keeps the reverse sweep's chunk
+    // pairs (its 32-step output rows) aligned to 32 steps of the sequence
+    int64_t per = (chunks + ns - 1) / ns;
+    per = std::min(per + (per & 1), chunks);
     const int64_t used = (chunks + per - 1) / per;  // segments actually needed at this length
     const int64_t cost = (groups * used + resident - 1) / resident * per;
     if (best_cost < 0 || cost < best_cost) {
