@@ -208,6 +208,10 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
   if (CONV && dvalid) conv_taps(a.conv_w, a.conv_b, d, a.conv_k, cw, cb);
   const float* __restrict__ cst = CONV && a.conv_state_in ? a.conv_state_in + row * (a.conv_k - 1) : nullptr;
 
+  // The current reverse segment's index and end, tracked as the sweep advances
+  // (a piece starts on a segment boundary) instead of a 64-bit remainder per chunk.
+  int64_t seg_idx = t_seg / a.seg_steps;
+  int64_t seg_end = t_seg + a.seg_steps;
   const ProgressPriority prio((Lseg + kT - 1) / kT, false);
   for (int t0 = 0; t0 < Lseg; t0 += kT) {
     prio.update(t0 / kT);
@@ -280,8 +284,9 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
       }
     }
     const int64_t tend = t_seg + t0 + kT;
-    if (tend % a.seg_steps == 0 || tend >= a.L) {  // end of a reverse segment
-      const int64_t sg = (t_seg + t0) / a.seg_steps;
+    if (tend == seg_end || tend >= a.L) {  // end of a reverse segment
+      const int64_t sg = seg_idx++;
+      seg_end += a.seg_steps;
       if (dvalid) {
         const int64_t w = ((static_cast<int64_t>(b) * a.nsegb + sg) * a.D + d) * N * 2;
 #pragma unroll

@@ -282,6 +282,12 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
     segP[j] = 1.0f;
     segG[j] = 0.0f;
   }
+  // ... and where the current backward segment ends, and its index (a piece
+  // starts on a segment boundary: seg_steps divides seg_len). Tracked as the
+  // sweep advances: a 64-bit remainder every 16 steps cost more scalar and
+  // vector instructions than the step arithmetic between them.
+  int64_t seg_end = CKPT ? t_seg + a.seg_steps : 0;
+  int64_t seg_idx = CKPT ? t_seg / a.seg_steps : 0;
   const InT* __restrict__ go_wg = CKPT ? static_cast<const InT*>(a.dout) + row0 : nullptr;
 
   // Row-staging items of this thread: RI consecutive steps of one channel.
@@ -653,9 +659,10 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
         }
         if (i % 16 == 12) {
           const int64_t tend = tchunk + i + 4;  // end of this 16-step block
-          if (tend - 16 < pend && (tend % a.seg_steps == 0 || tend >= pend)) {
-            const int64_t sg = (min(tend, pend) - 1) / a.seg_steps;
-            const int64_t si = ((static_cast<int64_t>(b) * a.nsegb + sg) * a.D + d) * N;
+          if (tend - 16 < pend && (tend == seg_end || tend >= pend)) {
+            const int64_t si = ((static_cast<int64_t>(b) * a.nsegb + seg_idx) * a.D + d) * N;
+            seg_end += a.seg_steps;
+            ++seg_idx;
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
               if (dvalid && nbase + j < N) {
