@@ -309,19 +309,30 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
 
   // The workgroup's dB / dC terms of steps [t0, t0 + FP) of the chunk at tc:
   // the waves' totals added in order, one partial per channel group.
+  // Items (type, step, state) are spread over the threads in a fixed pattern
+  // (2 x FP x NPADC is a multiple of the thread count), and the address of
+  // each item is a 32-bit offset from one base per flush. The loop stays
+  // rolled: unrolled inside the unrolled steps it spilled (N = 128).
+  constexpr int FLUSH_ITEMS = 2 * FP * NPADC;
+  static_assert(FLUSH_ITEMS % kThreads == 0, "flush items per thread");
+  const int64_t part_row = (static_cast<int64_t>(g) * a.B + b) * a.L * N;  // this group's (b, 0, 0)
+  const int64_t part_type = static_cast<int64_t>(a.B) * a.L * N * a.n_dgroups;  // partC - partB
   auto flush = [&](int64_t tc, int t0) {
-    for (int i = tid; i < 2 * FP * NPADC; i += kThreads) {
+    const int64_t t_first = tc + t0;
+    float* const base = a.partB + part_row + t_first * N;
+    const int limit = static_cast<int>(min<int64_t>(FP, pend - t_first));  // steps of this period in the segment
+#pragma unroll 1
+    for (int q = 0; q < FLUSH_ITEMS / kThreads; ++q) {
+      const int i = tid + q * kThreads;
       const int type = i / (FP * NPADC);
       const int tt = (i / NPADC) % FP;
       const int n = i % NPADC;
-      const int64_t tg = tc + t0 + tt;
-      if (n < N && tg < pend) {
+      if (n < N && tt < limit) {
         const int k = type * AT + tt * NPADC + n;
         float sum = s_acc[k];
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) sum += s_acc[ww * AW + k];
-        float* dst = type ? a.partC : a.partB;
-        dst[((static_cast<int64_t>(g) * a.B + b) * a.L + tg) * N + n] = sum;
+        base[(type ? part_type : 0) + tt * N + n] = sum;
       }
     }
   };
