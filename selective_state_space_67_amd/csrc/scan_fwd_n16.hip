@@ -87,7 +87,13 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   //  column t + n; the finished read-out sums per channel and step (floats).
   constexpr int DU_STRIDE = RING + 16;
   constexpr int DU_COPY = CPW * DU_STRIDE + 16;
-  constexpr int BC_STRIDE = RING + 2;
+  //  The (B, C) ring has three chunk parts where the (delta, delta*u) ring has
+  //  two: a chunk's (B, C) spill over into the next part (the skewed columns
+  //  t + n run past the chunk), so with two parts store_chunk(J + 1) would
+  //  overwrite the part compute(J) reads. With three, the one barrier per
+  //  chunk (after store_chunk) orders every cross-wave use of the ring.
+  constexpr int BC_RING = 3 * T;
+  constexpr int BC_STRIDE = BC_RING + 2;
   __shared__ __align__(16) float2 s_du[DU_COPY + CPW * DU_STRIDE];
   __shared__ __align__(16) float2 s_bc[N * BC_STRIDE];
   __shared__ __align__(16) float s_y[CPW * RING];
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
     if (HAS_RESET) r.rs = __builtin_amdgcn_raw_buffer_load_b16(rsrc_rs, stl + tau0, 0, 0);
   };
 
-  auto store_chunk = [&](int J, const int par, const Raw& r, Out& o) {
+  auto store_chunk = [&](int J, const int par, const int bpart, const Raw& r, Out& o) {
     const int tau0 = J * T;
     float b0 = P::lo(r.bb), b1 = P::hi(r.bb), c0 = P::lo(r.cc), c1 = P::hi(r.cc);
     float u0 = P::lo(r.u), u1 = P::hi(r.u);
@@ -210,10 +216,11 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
       dl0 = r0 ? -dl0 : dl0;
       dl1 = r1 ? -dl1 : dl1;
     }
-    // (B, C) of states bn, bn + 1 at step bt: row n, column (slot + n) mod RING
-    const int col = par * T + bt;
-    s_bc[bn * BC_STRIDE + ((col + bn) & MASK)] = make_float2(b0, c0);
-    s_bc[(bn + 1) * BC_STRIDE + ((col + bn + 1) & MASK)] = make_float2(b1, c1);
+    // (B, C) of states bn, bn + 1 at step bt: row n, column (part slot + n) mod BC_RING
+    const int col = bpart * T + bt;
+    const int c0i = col + bn, c1i = col + bn + 1;
+    s_bc[bn * BC_STRIDE + (c0i >= BC_RING ? c0i - BC_RING : c0i)] = make_float2(b0, c0);
+    s_bc[(bn + 1) * BC_STRIDE + (c1i >= BC_RING ? c1i - BC_RING : c1i)] = make_float2(b1, c1);
     // (delta, delta*u): copy 0 at slots s0, s0 + 1 (one 16-byte store), copy 1 one slot later
     const int s0 = par * T + stl;
     float2* du0 = s_du + c * DU_STRIDE;
@@ -293,18 +300,18 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   // at a time between the steps' arithmetic: issued in bursts, they fill the
   // LDS command queue and the waves stall at issue.
   constexpr int PF = 4;
-  auto read_pair = [&](const int par, const int q, float4& dd, float4& bc) {
+  auto read_pair = [&](const int par, const int bpart, const int q, float4& dd, float4& bc) {
     const int m0 = par * T + (q >> 3) * 16;
     dd = *reinterpret_cast<const float4*>(du_row + ((m0 - k + p) & MASK) + (q & 7) * 2);
-    bc = *reinterpret_cast<const float4*>(bc_row + m0 + (q & 7) * 2);
+    bc = *reinterpret_cast<const float4*>(bc_row + bpart * T + (q >> 3) * 16 + (q & 7) * 2);
   };
-  auto compute = [&](const int par) __attribute__((always_inline)) {
+  auto compute = [&](const int par, const int bpart) __attribute__((always_inline)) {
     float4 dd[T / 2], bc[T / 2];
 #pragma unroll
-    for (int q = 0; q < PF; ++q) read_pair(par, q, dd[q], bc[q]);
+    for (int q = 0; q < PF; ++q) read_pair(par, bpart, q, dd[q], bc[q]);
 #pragma unroll
     for (int q = 0; q < T / 2; ++q) {
-      if (q + PF < T / 2) read_pair(par, q + PF, dd[q + PF], bc[q + PF]);
+      if (q + PF < T / 2) read_pair(par, bpart, q + PF, dd[q + PF], bc[q + PF]);
       const int m0 = par * T + (q >> 3) * 16;
       const int st = (q & 7) * 2;
       step(st, m0, dd[q].x, dd[q].y, bc[q].x, bc[q].y);
@@ -322,21 +329,30 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   __syncthreads();  // rings are empty before the first chunk is stored
   // workgroups resident per CU: one wave per SIMD each, as many as the occupancy bound allows
   const ProgressPriority prio(nchunks, a.nblocks <= 256 * (sizeof(InT) == 2 ? 4 : 3));
+  // One barrier per chunk. The (B, C) ring is the only LDS data shared across
+  // waves; the barrier after store_chunk(J) makes part J mod 3 visible, and a
+  // wave past it knows that every wave has finished compute(J - 1), whose
+  // part store_chunk(J + 2) is the next to write (into its first columns, by
+  // the spill-over). The (delta, delta*u) rows and the read-out slots of a
+  // channel are written and read only by the wave that owns the channel
+  // (channel = tid / 16 in staging, compute and finalize alike), in program
+  // order.
+  int bpart = 0;  // J mod 3
   for (int J = 0; J < nchunks; J += 2) {
     prio.update(J);
-    store_chunk(J, 0, r0, o0);
+    const int bpart1 = bpart == 2 ? 0 : bpart + 1;
+    store_chunk(J, 0, bpart, r0, o0);
     if (J + 2 < nchunks) load_chunk(J + 2, r0);
     __syncthreads();
-    compute(0);
-    __syncthreads();
+    compute(0, bpart);
     if (J >= 1) finalize(J - 1, 1, o1);
     if (J + 1 >= nchunks) break;
-    store_chunk(J + 1, 1, r1, o1);
+    store_chunk(J + 1, 1, bpart1, r1, o1);
     if (J + 3 < nchunks) load_chunk(J + 3, r1);
     __syncthreads();
-    compute(1);
-    __syncthreads();
+    compute(1, bpart1);
     finalize(J, 0, o0);
+    bpart = bpart1 == 2 ? 0 : bpart1 + 1;
   }
   if ((nchunks - 1) * T < Lseg) {
     if ((nchunks - 1) & 1)
