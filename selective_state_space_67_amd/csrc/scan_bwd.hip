@@ -60,7 +60,11 @@ struct BwdTile {
   static constexpr int CPW = kWaves * CPWAVE;    // channels per workgroup
   // Per-wave buffer for the channel sums: [type][channel][step parity][state],
   // padded so that the 16-byte writes and the 4-byte reads spread over banks.
-  static constexpr int QS = 2 * NPADC + 4;
+  // A write pass covers 16 lanes, 16 / LPC channels of LPC x 4 floats each:
+  // with fewer than 16 lanes per channel the channel stride QS is an odd
+  // multiple (3) of 4 x LPC, so those channels start in different bank
+  // groups (2 x NPADC + 4 put two of every four channels on the same banks).
+  static constexpr int QS = LPC >= 16 ? 2 * NPADC + 4 : 12 * LPC;
   static constexpr int TS = CPWAVE * QS + 32;
   // Steps per flush of the dB / dC totals: each wave keeps its own totals
   // (2 x FP x NPADC floats) and the flush adds the waves in a fixed order, so
