@@ -332,8 +332,9 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   // One barrier per chunk. The (B, C) ring is the only LDS data shared across
   // waves; the barrier after store_chunk(J) makes part J mod 3 visible, and a
   // wave past it knows that every wave has finished compute(J - 1), whose
-  // part store_chunk(J + 2) is the next to write (into its first columns, by
-  // the spill-over). The (delta, delta*u) rows and the read-out slots of a
+  // part the next staging, store_chunk(J + 1), starts to overwrite (its
+  // spill-over lands in that part's first columns; store_chunk(J + 2) fills
+  // the rest after the next barrier). The (delta, delta*u) rows and the read-out slots of a
   // channel are written and read only by the wave that owns the channel
   // (channel = tid / 16 in staging, compute and finalize alike), in program
   // order.
