@@ -261,6 +261,11 @@ def measure_decode(torch, binding, wl, timer, evict):
     Bd, Dd, Nd = y["h"].shape
     dbytes = decode_bytes(Bd, Dd, Nd, 2, 4)
     cold_s = float(np.median(cold)) / 1e3
+    # ceiling: torch's in-place add on a float32 tensor of the state's size
+    # (the same state bytes read and written), timed the same way
+    probe = torch.zeros_like(hd)
+    ceil_s = float(np.median(timer.launches(lambda: probe.add_(1.0), 50, evict=evict))) / 1e3
+    del probe
     return {"workload": "state update B=64 D=2048 N=128, bf16 inputs, fp32 state",
             "note": "cold_cache: the state read from HBM (a 1 GiB read before each launch), as in a model whose "
                     "layers' states do not fit the caches; warm: steps repeated on one state, which can stay in "
@@ -270,7 +275,11 @@ def measure_decode(torch, binding, wl, timer, evict):
                            "launch_ms_p90": percentile(cold, 90), "hbm_gbps": dbytes / cold_s / 1e9,
                            "hbm_frac": dbytes / cold_s / 1e9 / HBM_PEAK_GBPS},
             "warm": {"launch_ms_mean": warm_s * 1e3, "hbm_gbps": dbytes / warm_s / 1e9,
-                     "hbm_frac": dbytes / warm_s / 1e9 / HBM_PEAK_GBPS}}
+                     "hbm_frac": dbytes / warm_s / 1e9 / HBM_PEAK_GBPS},
+            "inplace_ceiling": {"what": "torch in-place add on a float32 tensor of the state's size, cold cache "
+                                        "like the step (state bytes read and written once)",
+                                "launch_ms_median": ceil_s * 1e3, "gbps": 2 * hd.numel() * 4 / ceil_s / 1e9,
+                                "step_over_ceiling": cold_s / ceil_s}}
 
 
 def decode_loop(torch, binding, wl, timer):

@@ -10,17 +10,20 @@
 //   out   = y * silu(z)
 //
 // The step reads and rewrites the whole (B, D, N) float32 state, which is
-// nearly all of its HBM traffic, so the kernel is built to keep many bytes of
-// state in flight: LR consecutive lanes own one (b, d) row, each lane holding
-// four consecutive states (one 16-byte load and store), and every thread
-// handles RPT rows whose loads are all issued before any arithmetic; states
-// larger than the L2 are read with nontemporal loads (streamed). The
-// step size and gate (a few transcendentals per row) are recomputed by each
-// lane of the row, which is cheaper than broadcasting them; the dot product
-// over n is a chain of DPP adds that completes in the row's last lane, and row
-// indices are split into (b, d) in 32-bit arithmetic (fewer than 2^31 rows).
-// Shapes whose N is not a multiple of four take a scalar variant (one state
-// per lane per pass).
+// nearly all of its HBM traffic. Per row it also needs A[d, :] (as many bytes
+// as the row's state) and B[b, :], C[b, :]; read per row, those cached reads
+// doubled the load instructions and cost about a tenth of the step. So a
+// thread owns one group of four consecutive states (one 16-byte load and
+// store; LR = N / 4 consecutive lanes cover a row) for a tile of RD
+// consecutive channels by RB batch rows: its A values serve RB rows, its B
+// and C values RD rows, and u, dt_raw, z, dt_bias and D come as runs of RD
+// elements. Every load of the tile is issued before any arithmetic; states
+// larger than the L2 are read with nontemporal loads (streamed). The step
+// size and gate (a few transcendentals per row) are recomputed by each lane
+// of the row, which is cheaper than broadcasting them; the dot product over n
+// is a chain of DPP adds that completes in the row's last lane. Shapes whose
+// N is not a multiple of four take a scalar variant (one state per lane per
+// pass).
 //
 // With a conv stage the step input is silu(conv_b + sum_k conv_w[k] * window[k])
 // over the window (conv_state[0 .. K-2], u): the conv state holds the previous
@@ -52,6 +55,7 @@ struct UpdateArgs {
   const float* conv_b;   // (D) or null
   int conv_k;
   int zoh;               // exact zero-order-hold input coefficient
+  int dtiles;            // channel tiles per batch-row tile (tiled variant)
 };
 
 // One state's update: h <- e^{delta A} h + coef * B * u, coef = delta or the
@@ -82,19 +86,6 @@ __device__ __forceinline__ void shift_conv_state(const UpdateArgs& a, int64_t ro
   float* st = a.conv_state + row * (K - 1);
   for (int k = 0; k < K - 2; ++k) st[k] = st[k + 1];
   st[K - 2] = x;
-}
-
-template <typename InT>
-__device__ __forceinline__ float4 load4(const InT* p, int64_t i);
-template <>
-__device__ __forceinline__ float4 load4<float>(const float* p, int64_t i) {
-  return *reinterpret_cast<const float4*>(p + i);
-}
-template <>
-__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p, int64_t i) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p + i);
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
 }
 
 template <int LR>
@@ -145,62 +136,158 @@ __device__ __forceinline__ float4 load_state4(const float* p) {
   }
 }
 
-// Vector variant: N % 4 == 0, LR = N / 4 lanes per row (a power of two <= 64).
-template <typename InT, int LR, int RPT, bool STREAM>
-__global__ __launch_bounds__(kThreads) void state_update_vec4(const UpdateArgs a) {
-  constexpr int ROWS_PER_PASS = kThreads / LR;
+// Raw words of a run of consecutive input elements, loaded with one vector
+// load and kept as loaded until the arithmetic (converting at the load would
+// make the load phase wait for each value in turn).
+template <int BYTES>
+struct Bits;
+template <>
+struct Bits<2> {
+  using T = uint16_t;
+};
+template <>
+struct Bits<4> {
+  using T = uint32_t;
+};
+template <>
+struct Bits<8> {
+  using T = uint2;
+};
+template <>
+struct Bits<16> {
+  using T = uint4;
+};
+
+__device__ __forceinline__ uint32_t word(uint16_t v, int) { return v; }
+__device__ __forceinline__ uint32_t word(uint32_t v, int) { return v; }
+__device__ __forceinline__ uint32_t word(uint2 v, int k) { return k ? v.y : v.x; }
+__device__ __forceinline__ uint32_t word(uint4 v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
+
+template <typename T, int R>
+struct Run {
+  using raw = typename Bits<R * static_cast<int>(sizeof(T))>::T;
+  // `p` aligned to the run's size
+  __device__ __forceinline__ static raw load(const T* p) { return *reinterpret_cast<const raw*>(p); }
+  // element i (a compile-time constant after unrolling) as float
+  __device__ __forceinline__ static float at(raw v, int i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w = word(v, i >> 1);
+      return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+      return __uint_as_float(word(v, i));
+    }
+  }
+};
+
+// R consecutive outputs, one store (the run is aligned to its size).
+template <int R>
+__device__ __forceinline__ void store_run(float* p, const float (&v)[R]) {
+  if constexpr (R == 4)
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  else if constexpr (R == 2)
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  else
+    *p = v[0];
+}
+template <int R>
+__device__ __forceinline__ void store_run(bf16_t* p, const float (&v)[R]) {
+  if constexpr (R == 4)
+    *reinterpret_cast<uint2*>(p) = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
+  else if constexpr (R == 2)
+    *reinterpret_cast<uint32_t*>(p) = bf16_pair(v[0], v[1]);
+  else
+    store_elem(p, 0, v[0]);
+}
+
+// Tiled vector variant: N % 4 == 0, LR = N / 4 lanes per row (a power of two
+// <= 64), D % RD == 0 and the (B, D) tensors aligned to runs of RD. A
+// workgroup covers RB batch rows by kThreads / LR * RD channels; its threads
+// are `slots` of LR lanes, slot s holding channels d0 .. d0 + RD - 1. Batch
+// rows past the end (a ragged last tile) repeat the last row's loads and skip
+// every store, so the loads stay unconditional.
+template <typename InT, int LR, int RD, int RB, bool STREAM>
+__global__ __launch_bounds__(kThreads) void state_update_tile(const UpdateArgs a) {
+  constexpr int SLOTS = kThreads / LR;
   const int li = threadIdx.x % LR;
-  const int64_t first = (static_cast<int64_t>(blockIdx.x) * RPT) * ROWS_PER_PASS + threadIdx.x / LR;
+  const int bt = blockIdx.x / a.dtiles;
+  const int d0 = ((blockIdx.x - bt * a.dtiles) * SLOTS + static_cast<int>(threadIdx.x) / LR) * RD;
+  // Whole slots only (LR divides 64, so a slot never straddles a wave): an
+  // inactive slot takes no part in the other slots' cross-lane adds.
+  if (d0 >= a.D) return;
+  const int D = static_cast<int>(a.D), N = static_cast<int>(a.N);
+  const int b0 = bt * RB;
+  const int nb = min(RB, static_cast<int>(a.B) - b0);
+  const int n0 = li * 4;
+  using RunIn = Run<InT, RD>;
+  using Run4 = Run<InT, 4>;
+  using RunF = Run<float, RD>;
   const InT* u_in = static_cast<const InT*>(a.u);
   const InT* dt_in = static_cast<const InT*>(a.dt);
   const InT* z_in = static_cast<const InT*>(a.z);
-  const InT* B_in = static_cast<const InT*>(a.Bm);
-  const InT* C_in = static_cast<const InT*>(a.Cm);
-  const int n0 = li * 4;
 
-  // Issue every load of this thread's rows first.
-  float4 hv[RPT], Av[RPT], Bv[RPT], Cv[RPT];
-  float uu[RPT], xx[RPT], zz[RPT];
+  // Issue every load of the tile first, the state (from HBM) ahead of the rest.
+  int bj[RB];        // batch row j of the tile (the last row repeated past the end)
+  int64_t rowj[RB];  // its (b, d0) row index
+  float4 hv[RB][RD];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int64_t row = first + static_cast<int64_t>(r) * ROWS_PER_PASS;
-    if (row < a.rows) {
-      const uint32_t row32 = static_cast<uint32_t>(row), D32 = static_cast<uint32_t>(a.D);
-      const int64_t b = row32 / D32, d = row32 - static_cast<uint32_t>(b) * D32;
-      hv[r] = load_state4<STREAM>(a.h + row * a.N + n0);
-      Av[r] = *reinterpret_cast<const float4*>(a.A + d * a.N + n0);
-      Bv[r] = load4(B_in, b * a.N + n0);
-      Cv[r] = load4(C_in, b * a.N + n0);
-      uu[r] = load_elem(u_in, row);
-      xx[r] = load_elem(dt_in, row) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
-      zz[r] = z_in ? load_elem(z_in, row) : 0.0f;
-    }
+  for (int j = 0; j < RB; ++j) {
+    bj[j] = min(b0 + j, static_cast<int>(a.B) - 1);
+    rowj[j] = static_cast<int64_t>(bj[j]) * D + d0;
+#pragma unroll
+    for (int i = 0; i < RD; ++i) hv[j][i] = load_state4<STREAM>(a.h + (rowj[j] + i) * N + n0);
   }
+  float4 Av[RD];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int64_t row = first + static_cast<int64_t>(r) * ROWS_PER_PASS;
-    // Rows never straddle a wave (LR divides 64), so a row past the end is
-    // inactive as a whole and its lanes take no part in the cross-lane adds.
-    if (row >= a.rows) continue;
-    const int64_t d = static_cast<uint32_t>(row) % static_cast<uint32_t>(a.D);
-    const float delta = softplus_f32(xx[r]);
-    const float ui = step_input(a, row, d, uu[r]);
-    float4 hn;
-    hn.x = update_state(a, delta, Av[r].x, hv[r].x, Bv[r].x, ui);
-    hn.y = update_state(a, delta, Av[r].y, hv[r].y, Bv[r].y, ui);
-    hn.z = update_state(a, delta, Av[r].z, hv[r].z, Bv[r].z, ui);
-    hn.w = update_state(a, delta, Av[r].w, hv[r].w, Bv[r].w, ui);
-    *reinterpret_cast<float4*>(a.h + row * a.N + n0) = hn;
-    float y = Cv[r].x * hn.x;
-    y = __builtin_fmaf(Cv[r].y, hn.y, y);
-    y = __builtin_fmaf(Cv[r].z, hn.z, y);
-    y = __builtin_fmaf(Cv[r].w, hn.w, y);
-    y = group_sum_last<LR>(y);
-    if (li == LR - 1) {
-      float o = y + (a.Dskip ? a.Dskip[d] * ui : 0.0f);
-      if (z_in) o *= silu_f32(zz[r]);
-      store_out(a, row, o);
-      shift_conv_state(a, row, uu[r]);
+  for (int i = 0; i < RD; ++i) Av[i] = *reinterpret_cast<const float4*>(a.A + static_cast<int64_t>(d0 + i) * N + n0);
+  typename Run4::raw Bv[RB], Cv[RB];
+  typename RunIn::raw uv[RB], xv[RB], zv[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int64_t bn = static_cast<int64_t>(bj[j]) * N + n0;
+    Bv[j] = Run4::load(static_cast<const InT*>(a.Bm) + bn);
+    Cv[j] = Run4::load(static_cast<const InT*>(a.Cm) + bn);
+    uv[j] = RunIn::load(u_in + rowj[j]);
+    xv[j] = RunIn::load(dt_in + rowj[j]);
+    zv[j] = z_in ? RunIn::load(z_in + rowj[j]) : typename RunIn::raw{};
+  }
+  const typename RunF::raw biasv = a.dt_bias ? RunF::load(a.dt_bias + d0) : typename RunF::raw{};
+  const typename RunF::raw dskv = a.Dskip ? RunF::load(a.Dskip + d0) : typename RunF::raw{};
+
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    float Bf[4], Cf[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      Bf[k] = Run4::at(Bv[j], k);
+      Cf[k] = Run4::at(Cv[j], k);
+    }
+    float o[RD];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) {
+      const int64_t row = rowj[j] + i;
+      const float delta = softplus_f32(RunIn::at(xv[j], i) + RunF::at(biasv, i));
+      const float ui = step_input(a, row, d0 + i, RunIn::at(uv[j], i));
+      float4 hn;
+      hn.x = update_state(a, delta, Av[i].x, hv[j][i].x, Bf[0], ui);
+      hn.y = update_state(a, delta, Av[i].y, hv[j][i].y, Bf[1], ui);
+      hn.z = update_state(a, delta, Av[i].z, hv[j][i].z, Bf[2], ui);
+      hn.w = update_state(a, delta, Av[i].w, hv[j][i].w, Bf[3], ui);
+      if (j < nb) *reinterpret_cast<float4*>(a.h + row * N + n0) = hn;
+      float y = Cf[0] * hn.x;
+      y = __builtin_fmaf(Cf[1], hn.y, y);
+      y = __builtin_fmaf(Cf[2], hn.z, y);
+      y = __builtin_fmaf(Cf[3], hn.w, y);
+      y = group_sum_last<LR>(y);
+      if (a.Dskip) y += RunF::at(dskv, i) * ui;
+      o[i] = z_in ? y * silu_f32(RunIn::at(zv[j], i)) : y;
+    }
+    if (li == LR - 1 && j < nb) {
+      if (a.out_bf16)
+        store_run<RD>(static_cast<bf16_t*>(a.out) + rowj[j], o);
+      else
+        store_run<RD>(static_cast<float*>(a.out) + rowj[j], o);
+#pragma unroll
+      for (int i = 0; i < RD; ++i) shift_conv_state(a, rowj[j] + i, RunIn::at(uv[j], i));
     }
   }
 }
@@ -241,22 +328,36 @@ __global__ __launch_bounds__(kThreads) void state_update_scalar(const UpdateArgs
 // the L2 (4 MB per XCD) does not stay in it across the layers of a model.
 constexpr int64_t kStreamStateBytes = int64_t{32} << 20;
 
-template <typename InT, int LR>
-hipError_t launch_vec(const UpdateArgs& a, hipStream_t stream) {
-  constexpr int RPT = 2;
-  const int64_t rows_per_block = static_cast<int64_t>(kThreads / LR) * RPT;
-  const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-  SSM_LOG("launch state_update_vec4<%d lanes per row, %d rows per thread>: %s in, streamed state %d; grid %lld x "
-          "%d threads",
-          LR, RPT, sizeof(InT) == 2 ? "bf16" : "f32", a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes,
-          static_cast<long long>(blocks), kThreads);
-  if (a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes)
-    hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, stream, a);
+template <typename InT, int LR, int RD, int RB>
+hipError_t launch_tile(UpdateArgs a, hipStream_t stream) {
+  constexpr int kChannels = kThreads / LR * RD;  // channels per workgroup
+  a.dtiles = static_cast<int>((a.D + kChannels - 1) / kChannels);
+  const int64_t blocks = a.dtiles * ((a.B + RB - 1) / RB);
+  const bool stream_state = a.rows * a.N * static_cast<int64_t>(sizeof(float)) > kStreamStateBytes;
+  SSM_LOG("launch state_update_tile<%d lanes per row, %d channels x %d batch rows per thread>: %s in, streamed "
+          "state %d; grid %lld x %d threads",
+          LR, RD, RB, sizeof(InT) == 2 ? "bf16" : "f32", stream_state, static_cast<long long>(blocks), kThreads);
+  if (stream_state)
+    hipLaunchKernelGGL((state_update_tile<InT, LR, RD, RB, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((state_update_vec4<InT, LR, RPT, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((state_update_tile<InT, LR, RD, RB, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// Tile of a thread (channels x batch rows). Measured cold (state from HBM)
+// at 64 x 2048 x 128, bf16 inputs, against 31.0 us for two rows per thread
+// without reuse and 25.5 us for torch's in-place add on a float32 tensor of
+// the state's size: 2 x 2 26.9 us, 2 x 1 27.3, 4 x 1 27.7, 2 x 3 28.2,
+// 4 x 2 27.9, 4 x 4 32.4 (197 registers, two waves per SIMD), 1 x 2 34.8,
+// 1 x 1 40.8. Channel runs matter more than batch rows: with RD = 1, u,
+// dt_raw and z are three 2-byte loads per row. `runs2`: the shape allows
+// channel runs of two.
+template <typename InT, int LR>
+hipError_t launch_lr(const UpdateArgs& a, bool runs2, hipStream_t stream) {
+  if (runs2) return a.B >= 2 ? launch_tile<InT, LR, 2, 2>(a, stream) : launch_tile<InT, LR, 2, 1>(a, stream);
+  return launch_tile<InT, LR, 1, 2>(a, stream);
 }
 
 template <typename InT, int LR>
@@ -278,12 +379,20 @@ hipError_t launch_dtype(const UpdateArgs& a, hipStream_t stream) {
   // base pointers aligned to a 4-state group and fewer than 2^31 rows.
   const bool vec_ok = aligned_to(a.h, 16) && aligned_to(a.A, 16) && aligned_to(a.Bm, 4 * sizeof(InT)) &&
                       aligned_to(a.Cm, 4 * sizeof(InT)) && a.rows < (int64_t{1} << 31);
+  // Channel runs of rd elements need D % rd == 0 and the (B, D) and (D)
+  // tensors aligned to a run.
+  const auto runs_ok = [&](int rd) {
+    return a.D % rd == 0 && aligned_to(a.u, rd * sizeof(InT)) && aligned_to(a.dt, rd * sizeof(InT)) &&
+           (!a.z || aligned_to(a.z, rd * sizeof(InT))) && aligned_to(a.out, rd * (a.out_bf16 ? 2 : 4)) &&
+           (!a.dt_bias || aligned_to(a.dt_bias, rd * 4)) && (!a.Dskip || aligned_to(a.Dskip, rd * 4));
+  };
+  const bool runs2 = runs_ok(2);
   if (vec_ok) switch (a.N) {
-    case 16: return launch_vec<InT, 4>(a, stream);
-    case 32: return launch_vec<InT, 8>(a, stream);
-    case 64: return launch_vec<InT, 16>(a, stream);
-    case 128: return launch_vec<InT, 32>(a, stream);
-    case 256: return launch_vec<InT, 64>(a, stream);
+    case 16: return launch_lr<InT, 4>(a, runs2, stream);
+    case 32: return launch_lr<InT, 8>(a, runs2, stream);
+    case 64: return launch_lr<InT, 16>(a, runs2, stream);
+    case 128: return launch_lr<InT, 32>(a, runs2, stream);
+    case 256: return launch_lr<InT, 64>(a, runs2, stream);
     default: break;
   }
   if (a.N <= 16) return launch_scalar<InT, 16>(a, stream);

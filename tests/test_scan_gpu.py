@@ -208,6 +208,41 @@ def test_decode_small(dtype, B, D, N):
     assert_close(h, rh, dtype, what="h")
 
 
+@pytest.mark.parametrize("B,D,N,opts", [
+    (5, 34, 128, "all"),        # 2 x 2 tiles: ragged last batch tile, channel tile partly past D
+    (1, 20, 64, "all"),         # one batch row: 2 x 1 tiles
+    (3, 7, 128, "all"),         # odd D: 1 x 2 tiles
+    (6, 18, 16, "none"),        # no z, D term or step bias
+    (3, 6, 32, "bf16_out"),
+])
+def test_decode_tiles(B, D, N, opts):
+    import torch
+
+    from selective_state_space_67_amd import ssm_state_update
+
+    x = wl.make_decode_inputs(B, D, N, dtype=wl.BF16, seed=B * 100 + D + N)
+    # A and D differ per channel here, so that a wrong channel index in a tile shows
+    rng = np.random.default_rng(D * 7 + N)
+    x["A"] = (-np.exp(rng.uniform(-1.0, 1.5, (D, N)))).astype(np.float32)
+    x["Dskip"] = rng.standard_normal(D).astype(np.float32)
+    if opts == "none":
+        x["z"], x["Dskip"], x["dt_bias"] = None, None, None
+    dev = torch.device("cuda:0")
+    t = {k: (wl.to_torch(x[k], dev) if x[k] is not None else None)
+         for k in ("u", "dt_raw", "z", "Bm", "Cm", "dt_bias", "A", "Dskip")}
+    ht = torch.from_numpy(np.ascontiguousarray(x["h"], np.float32)).to(dev)
+    out = ssm_state_update(ht, t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                           Dskip=t["Dskip"], z=t["z"],
+                           out_dtype=torch.bfloat16 if opts == "bf16_out" else None)
+    torch.cuda.synchronize()
+    w = wl.widen
+    ro, rh = oracle.state_update(x["h"], w(x["u"]), w(x["dt_raw"]), x["A"], w(x["Bm"]), w(x["Cm"]),
+                                 z=w(x["z"]) if x["z"] is not None else None, dt_bias=x["dt_bias"],
+                                 Dskip=x["Dskip"])
+    assert_close(out.float().cpu().numpy(), ro, wl.BF16, out_bf16=opts == "bf16_out")
+    assert_close(ht.cpu().numpy(), rh, wl.BF16, what="h")
+
+
 def test_decode_unaligned_state_takes_scalar_path():
     # h offset by one float inside a larger buffer: not 16-byte aligned
     import torch
