@@ -397,6 +397,9 @@ def measure_extras(torch, binding, wl, timer, f, dout, bsec, fwd_s, steps):
     dcx = binding.prepare_state_update(hdc, tdc["u"], tdc["dt_raw"], tdc["A"], tdc["Bm"], tdc["Cm"],
                                        dt_bias=tdc["dt_bias"], Dskip=tdc["Dskip"], z=tdc["z"], complex_state=True)
     xsec_d = timer.mean(dcx, 50)
+    evict = torch.ones(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
+    xcold_d = float(np.median(timer.launches(dcx, 30, evict=evict))) / 1e3
+    del evict
     Bd, Dd, Nd = 64, 2048, 128
     # state (B, D, N, 2) read and written, plus the per-row inputs, complex B, C and A
     xdbytes = 16 * Bd * Dd * Nd + 3 * Bd * Dd * 2 + 2 * Bd * Nd * 2 * 2 + 8 * Dd * Nd + 8 * Dd + Bd * Dd * 4
@@ -408,7 +411,8 @@ def measure_extras(torch, binding, wl, timer, f, dout, bsec, fwd_s, steps):
         "zoh_fwd_ms": xsec_z * 1e3, "bwd_ms": xsec_b * 1e3, "bwd_vs_complex_forward": xsec_b / xsec_f,
         "bwd_elements_per_s": elements / xsec_b, "zoh_bwd_ms": xsec_bz * 1e3,
         "decode_workload": "state update B=64 D=2048 N=128 complex, bf16 inputs, fp32 state",
-        "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes, "decode_hbm_gbps": xdbytes / xsec_d / 1e9}
+        "decode_ms": xsec_d * 1e3, "decode_algorithmic_bytes": xdbytes, "decode_hbm_gbps": xdbytes / xsec_d / 1e9,
+        "decode_cold_ms_median": xcold_d * 1e3, "decode_cold_hbm_gbps": xdbytes / xcold_d / 1e9}
     # one GPU's share of the long-genomics sequence split 8 ways: the shard's
     # aggregate (what the other shards need) and its scan from a carried state
     c3 = wl.workload("long-genomics")

@@ -310,6 +310,8 @@ struct CplxUpdateArgs {
   const float* conv_w;  // (D, conv_k)
   const float* conv_b;  // (D) or null
   int conv_k;
+  int dtiles;  // channel tiles per batch-row tile (cplx_update_tile)
+  int stream;  // cplx_update_tile: read the state with nontemporal loads
 };
 
 // Decode: one (b, d) row per DPP row of 16 lanes, 16 rows per workgroup. Lane
@@ -387,6 +389,123 @@ __global__ __launch_bounds__(kThreads) void cplx_update_kernel(const CplxUpdateA
       store_elem(static_cast<bf16_t*>(a.out), row, v);
     else
       store_elem(static_cast<float*>(a.out), row, v);
+  }
+}
+
+// Tiled decode for N = 8 .. 128, a power of two: LR = N / 2 lanes per row,
+// each lane two consecutive complex states, so every state access is 16
+// bytes. As in the real decode step, a thread holds a tile of RD consecutive
+// channels by RB batch rows of its state pair: its A values (and the
+// constants derived from them) serve RB rows, its B and C values RD rows, and
+// u, dt_raw, z, dt_bias and D come as runs of RD elements. Every load of the
+// tile is issued before any arithmetic; batch rows past the end of a ragged
+// last tile repeat the last row's loads and skip every store.
+template <typename InT, int LR, int RD, int RB, bool ZOH>
+__global__ __launch_bounds__(kThreads) void cplx_update_tile(const CplxUpdateArgs a) {
+  constexpr int SLOTS = kThreads / LR;
+  const int li = threadIdx.x % LR;
+  const int bt = blockIdx.x / a.dtiles;
+  const int d0 = ((blockIdx.x - bt * a.dtiles) * SLOTS + static_cast<int>(threadIdx.x) / LR) * RD;
+  // Whole slots only (LR divides 64): an inactive slot takes no part in the
+  // other slots' cross-lane adds.
+  if (d0 >= a.D) return;
+  const int D = static_cast<int>(a.D), N = static_cast<int>(a.N);
+  const int b0 = bt * RB;
+  const int nb = min(RB, static_cast<int>(a.B) - b0);
+  const int n0 = li * 2;
+  using RunIn = Run<InT, RD>;
+  using Run4 = Run<InT, 4>;
+  using RunF = Run<float, RD>;
+  const InT* u_in = static_cast<const InT*>(a.u);
+  const InT* dt_in = static_cast<const InT*>(a.dt);
+  const InT* z_in = static_cast<const InT*>(a.z);
+
+  int bj[RB];
+  int64_t rowj[RB];
+  float4 hv[RB][RD];  // (re, im) of states n0 and n0 + 1
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    bj[j] = min(b0 + j, static_cast<int>(a.B) - 1);
+    rowj[j] = static_cast<int64_t>(bj[j]) * D + d0;
+#pragma unroll
+    for (int i = 0; i < RD; ++i) {
+      const float* p = a.h + ((rowj[j] + i) * N + n0) * 2;
+      if (a.stream) {  // a state larger than the L2: nontemporal loads
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+        hv[j][i] = make_float4(t.x, t.y, t.z, t.w);
+      } else {
+        hv[j][i] = *reinterpret_cast<const float4*>(p);
+      }
+    }
+  }
+  float4 Av[RD];
+#pragma unroll
+  for (int i = 0; i < RD; ++i)
+    Av[i] = *reinterpret_cast<const float4*>(a.A + (static_cast<int64_t>(d0 + i) * N + n0) * 2);
+  typename Run4::raw Bv[RB], Cv[RB];
+  typename RunIn::raw uv[RB], xv[RB], zv[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int64_t bn = (static_cast<int64_t>(bj[j]) * N + n0) * 2;
+    Bv[j] = Run4::load(static_cast<const InT*>(a.Bm) + bn);
+    Cv[j] = Run4::load(static_cast<const InT*>(a.Cm) + bn);
+    uv[j] = RunIn::load(u_in + rowj[j]);
+    xv[j] = RunIn::load(dt_in + rowj[j]);
+    zv[j] = z_in ? RunIn::load(z_in + rowj[j]) : typename RunIn::raw{};
+  }
+  const typename RunF::raw biasv = a.dt_bias ? RunF::load(a.dt_bias + d0) : typename RunF::raw{};
+  const typename RunF::raw dskv = a.Dskip ? RunF::load(a.Dskip + d0) : typename RunF::raw{};
+
+  CState q0[RD], q1[RD];
+#pragma unroll
+  for (int i = 0; i < RD; ++i) {
+    q0[i] = make_cstate(Av[i].x, Av[i].y);
+    q1[i] = make_cstate(Av[i].z, Av[i].w);
+  }
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const float2 B0 = make_float2(Run4::at(Bv[j], 0), Run4::at(Bv[j], 1));
+    const float2 B1 = make_float2(Run4::at(Bv[j], 2), Run4::at(Bv[j], 3));
+    const float2 C0 = make_float2(Run4::at(Cv[j], 0), Run4::at(Cv[j], 1));
+    const float2 C1 = make_float2(Run4::at(Cv[j], 2), Run4::at(Cv[j], 3));
+    float o[RD];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) {
+      const int64_t row = rowj[j] + i;
+      const float x = RunIn::at(uv[j], i);
+      float uu = x;
+      if (a.conv_w) {  // u' = silu(conv over the row's conv state and this input)
+        const int K = a.conv_k, d = d0 + i;
+        const float* cst = a.conv_state + row * (K - 1);
+        float pre = __builtin_fmaf(a.conv_w[d * K + K - 1], x, a.conv_b ? a.conv_b[d] : 0.0f);
+        for (int q = 0; q < K - 1; ++q) pre = __builtin_fmaf(a.conv_w[d * K + q], cst[q], pre);
+        uu = silu_f32(pre);
+      }
+      const float dl = softplus_f32(RunIn::at(xv[j], i) + RunF::at(biasv, i));
+      const float dv = ZOH ? uu : dl * uu;
+      float4 h = hv[j][i];
+      float p = cplx_step<ZOH>(dl, dv, q0[i], B0, C0, h.x, h.y);
+      p += cplx_step<ZOH>(dl, dv, q1[i], B1, C1, h.z, h.w);
+      if (j < nb) *reinterpret_cast<float4*>(a.h + (row * N + n0) * 2) = h;
+      p = group_sum_last<LR>(p);
+      if (a.Dskip) p += RunF::at(dskv, i) * uu;
+      o[i] = z_in ? p * silu_f32(RunIn::at(zv[j], i)) : p;
+    }
+    if (li == LR - 1 && j < nb) {
+      if (a.out_bf16)
+        store_run<RD>(static_cast<bf16_t*>(a.out) + rowj[j], o);
+      else
+        store_run<RD>(static_cast<float*>(a.out) + rowj[j], o);
+      if (a.conv_w && a.conv_k > 1) {  // shift the conv states by this input (the row's lanes have all read them)
+#pragma unroll
+        for (int i = 0; i < RD; ++i) {
+          float* cst = a.conv_state + (rowj[j] + i) * (a.conv_k - 1);
+          for (int q = 0; q + 1 < a.conv_k - 1; ++q) cst[q] = cst[q + 1];
+          cst[a.conv_k - 2] = RunIn::at(uv[j], i);
+        }
+      }
+    }
   }
 }
 
@@ -575,8 +694,45 @@ hipError_t launch_state_update_cplx(const UpdatePlan& p, hipStream_t stream) {
   a.conv_w = p.conv_w;
   a.conv_b = p.conv_b;
   a.conv_k = p.conv_k;
-  const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
   const bool streamed = p.B * p.D * p.N * 2 * static_cast<int64_t>(sizeof(float)) > (int64_t{32} << 20);
+  // The tiled kernel: N = 8 .. 128 a power of two, 16-byte state and A rows,
+  // runs of two channels (D even, the (B, D) and (D) tensors aligned to them),
+  // two or more batch rows and fewer than 2^31 rows.
+  const auto al = [](const void* q, size_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
+  const size_t s_in = p.in_bf16 ? 2 : 4;
+  const bool tile_ok = p.N >= 8 && p.N <= 128 && (p.N & (p.N - 1)) == 0 && p.B >= 2 && p.D % 2 == 0 &&
+                       p.B * p.D < (int64_t{1} << 31) && al(p.h, 16) && al(p.A, 16) && al(p.Bm, 4 * s_in) &&
+                       al(p.Cm, 4 * s_in) && al(p.u, 2 * s_in) && al(p.dt, 2 * s_in) && (!p.z || al(p.z, 2 * s_in)) &&
+                       al(p.out, p.out_bf16 ? 4 : 8) && (!p.dt_bias || al(p.dt_bias, 8)) && (!p.Dskip || al(p.Dskip, 8));
+  if (tile_ok) {
+    a.stream = streamed;
+    auto tile = [&](auto lr, auto zoh) {
+      constexpr int LR = decltype(lr)::value;
+      constexpr bool Z = decltype(zoh)::value;
+      constexpr int kChannels = kThreads / LR * 2;
+      a.dtiles = static_cast<int>((p.D + kChannels - 1) / kChannels);
+      const dim3 grid(static_cast<unsigned>(a.dtiles * ((p.B + 1) / 2)));
+      SSM_LOG("launch cplx_update_tile<%d lanes per row, 2 channels x 2 batch rows per thread>: %s in, zoh %d, "
+              "streamed state %d; grid %u x %d threads",
+              LR, p.in_bf16 ? "bf16" : "f32", Z, static_cast<int>(streamed), grid.x, kThreads);
+      if (p.in_bf16)
+        hipLaunchKernelGGL((cplx_update_tile<bf16_t, LR, 2, 2, Z>), grid, dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((cplx_update_tile<float, LR, 2, 2, Z>), grid, dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    };
+    auto with_lr = [&](auto zoh) {
+      switch (p.N) {
+        case 8: return tile(std::integral_constant<int, 4>{}, zoh);
+        case 16: return tile(std::integral_constant<int, 8>{}, zoh);
+        case 32: return tile(std::integral_constant<int, 16>{}, zoh);
+        case 64: return tile(std::integral_constant<int, 32>{}, zoh);
+        default: return tile(std::integral_constant<int, 64>{}, zoh);
+      }
+    };
+    return p.zoh ? with_lr(std::true_type{}) : with_lr(std::false_type{});
+  }
+  const dim3 grid(static_cast<unsigned>((p.B * p.D + kCPW - 1) / kCPW));
   auto go = [&](auto npl, auto zoh, auto st) {
     constexpr int NPL = decltype(npl)::value;
     constexpr bool Z = decltype(zoh)::value, S = decltype(st)::value;

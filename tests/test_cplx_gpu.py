@@ -232,6 +232,27 @@ def test_complex_decode(dtype, N):
     check_decode(y, out, h, "N=%d %s" % (N, dtype))
 
 
+@pytest.mark.parametrize("B,D,N,dtype,zoh,opts", [
+    (5, 34, 128, wl.BF16, False, "all"),  # 2 x 2 tiles: ragged last batch tile, channel tile partly past D
+    (4, 18, 16, wl.F32, True, "all"),
+    (3, 40, 8, wl.BF16, True, "all"),
+    (6, 12, 64, wl.F32, False, "none"),   # no z, D term or step bias
+])
+def test_complex_decode_tiles(B, D, N, dtype, zoh, opts):
+    rng = np.random.default_rng(B * 1000 + D + N)
+    y = wl.make_cplx_decode_inputs(B, D, N, dtype, seed=B + D + N, dt_lo=1e-3, dt_hi=3e-1)
+    # A and D differ per channel here, so that a wrong channel index in a tile shows
+    A = np.empty((D, N, 2), np.float32)
+    A[..., 0] = -rng.uniform(0.1, 2.0, (D, N))
+    A[..., 1] = rng.uniform(-4.0, 4.0, (D, N))
+    y["A"] = A
+    y["Dskip"] = rng.standard_normal(D).astype(np.float32)
+    if opts == "none":
+        y["z"], y["Dskip"], y["dt_bias"] = None, None, None
+    out, h = run_update(y, y["h"], zoh=zoh)
+    check_decode(y, out, h, "tiles %s N=%d zoh=%s %s" % ((B, D), N, zoh, opts), zoh=zoh)
+
+
 def test_complex_decode_at_full_size():
     """The decode shape of the packed workload (64 x 2048, N = 128), every element."""
     y = wl.make_cplx_decode_inputs(64, 2048, 128, wl.BF16, seed=5)
