@@ -157,6 +157,37 @@ __device__ __forceinline__ void zoh_dq_dA(float dl, const CState& q, float are, 
 }
 
 // One complex value stored as an (re, im) pair of the input type, widened.
+// (hr, hi) <- P[i] (hr, hi) + H[i] (complex) for i = 0 .. count - 1 in
+// order: the aggregates of the pieces before this one, `stride` floats
+// apart, each an (re, im) pair. The loads go out eight pieces at a time.
+__device__ __forceinline__ void fold_aggregates_c(const float* P, const float* H, int count, int64_t stride,
+                                                  float& hr, float& hi) {
+  auto one = [&](float pr, float pi, float gr, float gi) {
+    const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, gr));
+    const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, gi));
+    hr = nr;
+    hi = ni;
+  };
+  int i = 0;
+  for (; i + 8 <= count; i += 8) {
+    float p[8][2], g[8][2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t w = (i + k) * stride;
+      p[k][0] = P[w];
+      p[k][1] = P[w + 1];
+      g[k][0] = H[w];
+      g[k][1] = H[w + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) one(p[k][0], p[k][1], g[k][0], g[k][1]);
+  }
+  for (; i < count; ++i) {
+    const int64_t w = i * stride;
+    one(P[w], P[w + 1], H[w], H[w + 1]);
+  }
+}
+
 __device__ __forceinline__ float2 load_cpair(const float* p, int64_t n) {
   return *reinterpret_cast<const float2*>(p + 2 * n);
 }

@@ -200,6 +200,26 @@ __device__ __forceinline__ void store_run(bf16_t* p, const float (&v)[R]) {
     store_elem(p, 0, v[0]);
 }
 
+// h <- P[i] h + H[i] for i = 0 .. count - 1 in order: the affine aggregates
+// of the pieces that precede a piece of a split sequence, `stride` elements
+// apart. The loads go out eight pieces at a time; one piece at a time, every
+// piece paid a full load latency before the next load was issued.
+__device__ __forceinline__ float fold_aggregates(const float* P, const float* H, int count, int64_t stride, float h) {
+  int i = 0;
+  for (; i + 8 <= count; i += 8) {
+    float p[8], q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = P[(i + k) * stride];
+      q[k] = H[(i + k) * stride];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h = __builtin_fmaf(p[k], h, q[k]);
+  }
+  for (; i < count; ++i) h = __builtin_fmaf(P[i * stride], h, H[i * stride]);
+  return h;
+}
+
 // Wave priority from the share of a workgroup's work already done. The
 // instruction arbiter of a SIMD favours its oldest waves, so of the
 // workgroups sharing a CU the first-placed ones race ahead and the last one

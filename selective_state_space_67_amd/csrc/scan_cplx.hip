@@ -144,16 +144,8 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
     const bool ok = !AGG && dvalid && n0 + j < N;
     hr[j] = ok && a.h0 ? a.h0[e] : 0.0f;
     hi[j] = ok && a.h0 ? a.h0[e + 1] : 0.0f;
-    if (ok) {
-      for (int q = 0; q < sp; ++q) {  // h <- P h + H for the preceding pieces
-        const int64_t w = static_cast<int64_t>(q) * a.B * a.D * N * 2 + e;
-        const float pr = a.ws_P[w], pi = a.ws_P[w + 1];
-        const float nr = __builtin_fmaf(pr, hr[j], __builtin_fmaf(-pi, hi[j], a.ws_H[w]));
-        const float ni = __builtin_fmaf(pr, hi[j], __builtin_fmaf(pi, hr[j], a.ws_H[w + 1]));
-        hr[j] = nr;
-        hi[j] = ni;
-      }
-    }
+    if (ok)  // h <- P h + H for the preceding pieces
+      fold_aggregates_c(a.ws_P + e, a.ws_H + e, sp, a.B * a.D * N * 2, hr[j], hi[j]);
   }
   for (int i = tid; i < kT * NPAD; i += kThreads) s_bc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 

@@ -249,11 +249,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + n;
       float hv = a.h0 ? a.h0[hi] : 0.0f;
       // Fold the aggregates of the preceding pieces: h <- P h + H.
-      for (int sp = 0; sp < s; ++sp) {
-        const int64_t wi = (static_cast<int64_t>(sp) * a.B + b) * a.D * N + d * N + n;
-        hv = __builtin_fmaf(a.ws_P[wi], hv, a.ws_H[wi]);
-      }
-      h[j] = hv;
+      const int64_t w0 = (static_cast<int64_t>(b) * a.D + d) * N + n;
+      h[j] = fold_aggregates(a.ws_P + w0, a.ws_H + w0, s, a.B * a.D * N, hv);
     }
   }
 

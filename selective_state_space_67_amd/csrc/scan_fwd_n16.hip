@@ -134,10 +134,8 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   if (dvalid) {
     const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + k;
     h = a.h0 ? a.h0[hi] : 0.0f;
-    for (int sp = 0; sp < s; ++sp) {
-      const int64_t wi = (static_cast<int64_t>(sp) * a.B + b) * a.D * N + d * N + k;
-      h = __builtin_fmaf(a.ws_P[wi], h, a.ws_H[wi]);
-    }
+    const int64_t w0 = (static_cast<int64_t>(b) * a.D + d) * N + k;
+    h = fold_aggregates(a.ws_P + w0, a.ws_H + w0, s, a.B * a.D * N, h);
   }
 
   // Steps before the start are identity steps (delta = 0, delta*u = 0, B = C = 0).
