@@ -285,6 +285,14 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   // vector instructions than the step arithmetic between them.
   int64_t seg_end = CKPT ? t_seg + a.seg_steps : 0;
   int64_t seg_idx = CKPT ? t_seg / a.seg_steps : 0;
+  // This lane's checkpoint slot for the piece's first 16-step block (the
+  // piece starts on a block boundary); block k of the piece is k x D x N
+  // floats further, a scalar offset, where the full index cost a chain of
+  // 64-bit multiplies per write.
+  float* const ck_lane =
+      CKPT ? a.ckpt + ((static_cast<int64_t>(b) * a.n_ck + t_seg / 16) * a.D + (dvalid ? d : 0)) * N + nbase
+           : nullptr;
+  const int64_t ck_block = a.D * N;
   const InT* __restrict__ go_wg = CKPT ? static_cast<const InT*>(a.dout) + row0 : nullptr;
 
   // Row-staging items of this thread: RI consecutive steps of one channel.
@@ -589,10 +597,10 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       for (int i = 0; i < T; i += 4) {
         const int m = par * T + i;
         if (i % 16 == 0 && tchunk + i < pend) {
-          const int64_t ci = (static_cast<int64_t>(b) * a.n_ck + (tchunk + i) / 16) * a.D + d;
+          float* const ck = ck_lane + static_cast<int64_t>((J * T + i) >> 4) * ck_block;
 #pragma unroll
           for (int j = 0; j < NPL; ++j)
-            if (dvalid && nbase + j < N) a.ckpt[ci * N + nbase + j] = h[j];
+            if (dvalid && nbase + j < N) ck[j] = h[j];
         }
         if constexpr (NPL == 1) {
           const float4 d01 = *reinterpret_cast<const float4*>(du_row + m);
