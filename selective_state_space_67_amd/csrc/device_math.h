@@ -220,6 +220,13 @@ __device__ __forceinline__ float fold_aggregates(const float* P, const float* H,
   return h;
 }
 
+// Placed in the body of a wave-uniform branch that is rarely taken (a reset
+// somewhere in the wave): the body then stays behind the branch. Without it
+// the compiler turns the branch and its selects into selects executed every
+// step (measured: four extra VALU operations per step for two states per
+// lane, two for one).
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 // Wave priority from the share of a workgroup's work already done. The
 // instruction arbiter of a SIMD favours its oldest waves, so of the
 // workgroups sharing a CU the first-placed ones race ahead and the last one

@@ -407,6 +407,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
       if (HAS_RESET) {
         const bool rs = __float_as_int(dl) < 0;
         if (__builtin_amdgcn_ballot_w64(rs)) {
+          keep_branch();
 #pragma unroll
           for (int j = 0; j < kNPL; ++j) h[j] = rs ? 0.0f : h[j];
         }
@@ -545,8 +546,20 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
       for (int j = 0; j < kNPL; ++j) {
         u1[j] = fast_exp2(fabsf(r1.x) * A2[j]);
         u0[j] = fast_exp2(fabsf(r0.x) * A2[j]);
-        a1[j] = rs1 ? 0.0f : u1[j];
-        a0[j] = rs0 ? 0.0f : u0[j];
+        a1[j] = u1[j];
+        a0[j] = u0[j];
+      }
+      // a_t = 0 at a reset (every lane of a workgroup sees its batch row's resets at the same step)
+      if (HAS_RESET && __builtin_amdgcn_ballot_w64(rs1 || rs0)) {
+        keep_branch();
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+          a1[j] = rs1 ? 0.0f : a1[j];
+          a0[j] = rs0 ? 0.0f : a0[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kNPL; ++j) {
         hpp[j] = t >= 3 ? hist[(t - 2) >> 1][j] : hs[j];  // h_{t-2}
         // h_{t-1}, as the forward computed it
         if constexpr (ZOH)

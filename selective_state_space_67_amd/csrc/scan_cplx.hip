@@ -211,6 +211,7 @@ __global__ __launch_bounds__(kThreads) void cplx_scan_kernel(const CplxArgs a) {
       if (HAS_RESET) {
         const bool rs = __float_as_int(dlt) < 0;
         if (__builtin_amdgcn_ballot_w64(rs)) {
+          keep_branch();
 #pragma unroll
           for (int j = 0; j < NPL; ++j) {
             hr[j] = rs ? 0.0f : hr[j];

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
       if (HAS_RESET) {
         const bool r = __float_as_int(dl) < 0;
         if (__builtin_amdgcn_ballot_w64(r)) {
+          keep_branch();
 #pragma unroll
           for (int j = 0; j < NPL; ++j) {
             hr[j] = r ? 0.0f : hr[j];
@@ -410,6 +411,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
         if (HAS_RESET) {
           const bool r = __float_as_int(dl) < 0;
           if (__builtin_amdgcn_ballot_w64(r)) {
+            keep_branch();
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
               hr[j] = r ? 0.0f : hr[j];

@@ -522,6 +522,7 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
     if (HAS_RESET) {
       const bool rs = __float_as_int(dl) < 0;
       if (__builtin_amdgcn_ballot_w64(rs)) {
+        keep_branch();
 #pragma unroll
         for (int j = 0; j < NPL; ++j) h[j] = rs ? 0.0f : h[j];
       }
@@ -560,6 +561,7 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
     if (HAS_RESET) {
       rs = __float_as_int(dl) < 0;
       if (__builtin_amdgcn_ballot_w64(rs)) {
+        keep_branch();
 #pragma unroll
         for (int j = 0; j < NPL; ++j) h[j] = rs ? 0.0f : h[j];
       }

@@ -275,7 +275,10 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   auto step = [&](const int i, const int m0, float dl, const float dv, const float Bv, const float Cv) {
     if (HAS_RESET) {
       const bool rs = __float_as_int(dl) < 0;
-      if (__builtin_amdgcn_ballot_w64(rs)) h = rs ? 0.0f : h;
+      if (__builtin_amdgcn_ballot_w64(rs)) {
+        keep_branch();
+        h = rs ? 0.0f : h;
+      }
       dl = fabsf(dl);
     }
     const float abar = fast_exp2(dl * A2);
