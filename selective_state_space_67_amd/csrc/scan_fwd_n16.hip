@@ -1,6 +1,8 @@
-// The plain full pass of the selective scan for 16 states per channel on
-// gfx950: delta B input coefficient, no conv stage, output written (the
-// "Mamba-130M/2.8B-shaped" layer scans and the long-sequence scan).
+// The full pass of the selective scan for 16 states per channel on gfx950:
+// no conv stage, output written (the "Mamba-130M/2.8B-shaped" layer scans and
+// the long-sequence scan), with the delta B input coefficient or (template
+// flag ZOH) the exact zero-order hold (e^{delta A} - 1) / A B of
+// "Illustrated Mamba state space model", "Mathematical basis: structured SSM".
 //
 // What is computed is the same as scan_kernel's kFull mode in
 // scan_fwd_kernel.h (the recurrence of "Illustrated Mamba state space model",
@@ -25,6 +27,8 @@
 //    outputs of those steps are written as one pair.
 // The per-chunk structure (LDS rings, skew, mirrors, finishing order) is
 // scan_kernel's; see the layout notes there.
+#include <type_traits>
+
 #include "scan_fwd_kernel.h"
 
 
@@ -76,7 +80,7 @@ struct Pair<float> {
 
 }  // namespace
 
-template <typename InT, bool HAS_RESET>
+template <typename InT, bool HAS_RESET, bool ZOH>
 __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(const ScanArgs a) {
   using P = Pair<InT>;
   constexpr int N = 16, T = 32, RING = 2 * T, MASK = RING - 1, CPW = 16, THREADS = 256;
@@ -130,6 +134,9 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
 
   // Per-lane parameter and starting state (h0, then the preceding pieces' aggregates folded in).
   const float A2 = dvalid ? a.A[d * N + k] * kLog2e : 0.0f;
+  // zero-order hold: A and 1/A of this lane's state (0 for A = 0)
+  const float Aj = ZOH && dvalid ? a.A[d * N + k] : 0.0f;
+  const float invA = ZOH && Aj != 0.0f ? 1.0f / Aj : 0.0f;
   float h = 0.0f;
   if (dvalid) {
     const int64_t hi = (static_cast<int64_t>(b) * a.D + d) * N + k;
@@ -202,7 +209,9 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
       if (!dvalid || tau0 + stl + 1 >= Lseg) dl1 = u1 = 0.0f;
       if (tau0 + bt >= Lseg) b0 = b1 = c0 = c1 = 0.0f;
     }
-    const float dv0 = dl0 * u0, dv1 = dl1 * u1;
+    // the input term's factor: delta u, or u itself with the zero-order hold
+    // (its coefficient depends on the state's A and is formed per state)
+    const float dv0 = ZOH ? u0 : dl0 * u0, dv1 = ZOH ? u1 : dl1 * u1;
     o.u0 = u0;
     o.u1 = u1;
     o.g0 = has_z ? silu_f32(P::lo(r.z)) : 1.0f;
@@ -282,7 +291,10 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
       dl = fabsf(dl);
     }
     const float abar = fast_exp2(dl * A2);
-    h = __builtin_fmaf(abar, h, Bv * dv);
+    if constexpr (ZOH)
+      h = __builtin_fmaf(abar, h, (Bv * dv) * zoh_coef(dl, dl * Aj, abar, invA));
+    else
+      h = __builtin_fmaf(abar, h, Bv * dv);
     yreg[i] = __builtin_fmaf(Cv, h, row_shr1(yreg[(i + 15) & 15]));
     if ((i & 3) == 2 && k == 15) {
       // steps m0+i-18 .. m0+i-15 are complete in this row: one aligned 16-byte store
@@ -366,12 +378,12 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   if (dvalid && a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * N + k] = h;
 }
 
-// Whether the 16-state full pass takes this launch: 16 states, delta B, no
-// conv stage, not the checkpoint sweep, an even L (element pairs stay aligned)
-// and buffer ranges within 31 bits (17 rows of L elements plus a chunk).
+// Whether the 16-state full pass takes this launch: 16 states, no conv
+// stage, not the checkpoint sweep, an even L (element pairs stay aligned) and
+// buffer ranges within 31 bits (17 rows of L elements plus a chunk).
 bool n16_eligible(const ScanArgs& a, bool checkpoint) {
   const int64_t s_in = a.in_bf16 ? 2 : 4;
-  return a.N == 16 && !checkpoint && a.conv_w == nullptr && !a.zoh && a.L % 2 == 0 &&
+  return a.N == 16 && !checkpoint && a.conv_w == nullptr && a.L % 2 == 0 &&
          (17 * a.L + 256) * s_in < (int64_t{1} << 31);
 }
 
@@ -387,19 +399,31 @@ hipError_t launch_n16(const ScanArgs& args, int nblocks_full, int nblocks_agg, h
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
-  SSM_LOG("launch scan16_kernel full: %s in, reset %d; grid %d x 256 threads (16 channels x 16 states per "
-          "workgroup, 32-step chunks), %d pieces of %lld steps",
-          args.in_bf16 ? "bf16" : "f32", reset, nblocks_full, args.nseg, static_cast<long long>(args.seg_len));
+  SSM_LOG("launch scan16_kernel full: %s in, reset %d, zoh %d; grid %d x 256 threads (16 channels x 16 states "
+          "per workgroup, 32-step chunks), %d pieces of %lld steps",
+          args.in_bf16 ? "bf16" : "f32", reset, args.zoh, nblocks_full, args.nseg,
+          static_cast<long long>(args.seg_len));
+  auto go = [&](auto in_t, auto has_reset, auto zoh) {
+    using InT = decltype(in_t);
+    constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
+    hipLaunchKernelGGL((scan16_kernel<InT, R, Z>), dim3(nblocks_full), dim3(256), 0, stream, full);
+  };
+  auto with_zoh = [&](auto in_t, auto has_reset) {
+    if (args.zoh)
+      go(in_t, has_reset, std::true_type{});
+    else
+      go(in_t, has_reset, std::false_type{});
+  };
   if (args.in_bf16) {
     if (reset)
-      hipLaunchKernelGGL((scan16_kernel<bf16_t, true>), dim3(nblocks_full), dim3(256), 0, stream, full);
+      with_zoh(bf16_t{}, std::true_type{});
     else
-      hipLaunchKernelGGL((scan16_kernel<bf16_t, false>), dim3(nblocks_full), dim3(256), 0, stream, full);
+      with_zoh(bf16_t{}, std::false_type{});
   } else {
     if (reset)
-      hipLaunchKernelGGL((scan16_kernel<float, true>), dim3(nblocks_full), dim3(256), 0, stream, full);
+      with_zoh(float{}, std::true_type{});
     else
-      hipLaunchKernelGGL((scan16_kernel<float, false>), dim3(nblocks_full), dim3(256), 0, stream, full);
+      with_zoh(float{}, std::false_type{});
   }
   return hipGetLastError();
 }

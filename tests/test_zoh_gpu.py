@@ -60,6 +60,22 @@ def test_zoh_forward(dtype, N):
     assert_close(hl, rhl, dtype, what="h_last N=%d" % N)
 
 
+@pytest.mark.parametrize("dtype,B,D,L,nseg", [(wl.F32, 2, 37, 1000, 0), (wl.BF16, 1, 16, 4000, 3)])
+def test_zoh_forward_sixteen_states(dtype, B, D, L, nseg):
+    # N = 16, even L, no resets: the 16-state kernel's zero-order-hold variant,
+    # with a partial channel group, and pieces joined by aggregates. Every
+    # state decays here (A = 0 would make state 0 a plain running sum over the
+    # whole sequence, whose float32 rounding outgrows the float32 tolerance
+    # after a few hundred steps in any kernel); small step sizes still put
+    # delta*A below 1/16, where the coefficient is the series.
+    x = case(B, D, L, 16, dtype, 900 + D)
+    x["A"][:, 0] = -1.0
+    got, hl = run_fwd(x, num_segments=nseg)
+    ref, rhl = ref_fwd(x)
+    assert_close(got, ref, dtype, what="out")
+    assert_close(hl, rhl, dtype, what="h_last")
+
+
 def test_zoh_forward_split_and_conv():
     x = case(1, 32, 5000, 16, wl.BF16, 9, dt_lo=1e-3, dt_hi=1e-2, conv=True)
     got, _ = run_fwd(x, num_segments=4)
