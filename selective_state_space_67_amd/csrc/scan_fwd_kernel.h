@@ -131,6 +131,30 @@ struct ScanArgs {
   int zoh;                     // exact zero-order hold input coefficient (ZOH kernels)
 };
 
+// Final conv state of a workgroup's channels d0 .. d0 + cpw - 1 of batch row
+// b: the last conv_k - 1 inputs of the sequence, oldest first, zeros for those
+// hidden by a later reset; threads tid < 3 cpw write one value each. Called
+// by the workgroups of the last piece.
+template <typename InT, bool HAS_RESET>
+__device__ __forceinline__ void write_final_conv_state(const ScanArgs& a, int b, int64_t d0, int cpw, int tid) {
+  if (tid >= cpw * 3) return;
+  const int cc = tid / 3, kk = tid % 3;
+  const int64_t dd = d0 + cc;
+  if (dd >= a.D || kk >= a.conv_k - 1) return;
+  const int64_t pos = a.L - (a.conv_k - 1) + kk;
+  bool vis = true;  // no reset after pos (a reset at pos itself starts a document there)
+  if (HAS_RESET)
+    for (int64_t q = max(pos + 1, int64_t{0}); q < a.L; ++q) vis = vis && !a.reset[static_cast<int64_t>(b) * a.L + q];
+  float v = 0.0f;
+  if (vis) {
+    if (pos >= 0)
+      v = load_elem(static_cast<const InT*>(a.u), (static_cast<int64_t>(b) * a.D + dd) * a.L + pos);
+    else if (a.conv_state_in)
+      v = a.conv_state_in[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + (pos + a.conv_k - 1)];
+  }
+  a.conv_state_out[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + kk] = v;
+}
+
 // Register budget (waves per SIMD) of one kernel instance. The checkpoint
 // sweep keeps more per-state values live (the segment's decay product and
 // adjoint sum), so with several states per lane it gets two waves. The plain
@@ -850,27 +874,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
     }
   }
 
-  // Final conv state: the last conv_k - 1 inputs of the sequence, oldest
-  // first, zeros for those hidden by a later reset.
   if constexpr (FULL && CONV) {
-    if (a.conv_state_out && s == a.nseg - 1 && tid < CPW * 3) {
-      const int cc = tid / 3, kk = tid % 3;
-      const int64_t dd = d0 + cc;
-      if (dd < a.D && kk < a.conv_k - 1) {
-        const int64_t pos = a.L - (a.conv_k - 1) + kk;
-        bool vis = true;  // no reset after pos (a reset at pos itself starts a document there)
-        if (HAS_RESET)
-          for (int64_t q = max(pos + 1, int64_t{0}); q < a.L; ++q) vis = vis && !a.reset[static_cast<int64_t>(b) * a.L + q];
-        float v = 0.0f;
-        if (vis) {
-          if (pos >= 0)
-            v = load_elem(static_cast<const InT*>(a.u), (static_cast<int64_t>(b) * a.D + dd) * a.L + pos);
-          else if (a.conv_state_in)
-            v = a.conv_state_in[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + (pos + a.conv_k - 1)];
-        }
-        a.conv_state_out[(static_cast<int64_t>(b) * a.D + dd) * (a.conv_k - 1) + kk] = v;
-      }
-    }
+    if (a.conv_state_out && s == a.nseg - 1) write_final_conv_state<InT, HAS_RESET>(a, b, d0, CPW, tid);
   }
 }
 

@@ -1,8 +1,9 @@
-// The full pass of the selective scan for 16 states per channel on gfx950:
-// no conv stage, output written (the "Mamba-130M/2.8B-shaped" layer scans and
-// the long-sequence scan), with the delta B input coefficient or (template
-// flag ZOH) the exact zero-order hold (e^{delta A} - 1) / A B of
-// "Illustrated Mamba state space model", "Mathematical basis: structured SSM".
+// The full pass of the selective scan for 16 states per channel on gfx950,
+// output written (the "Mamba-130M/2.8B-shaped" layer scans and the
+// long-sequence scan), with the delta B input coefficient or (template flag
+// ZOH) the exact zero-order hold (e^{delta A} - 1) / A B of "Illustrated Mamba
+// state space model", "Mathematical basis: structured SSM", and optionally
+// (template flag CONV) the causal depthwise conv1d + SiLU on u.
 //
 // What is computed is the same as scan_kernel's kFull mode in
 // scan_fwd_kernel.h (the recurrence of "Illustrated Mamba state space model",
@@ -80,8 +81,16 @@ struct Pair<float> {
 
 }  // namespace
 
-template <typename InT, bool HAS_RESET, bool ZOH>
-__global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(const ScanArgs a) {
+// Waves per SIMD the kernel is built for: four in bf16 (128 registers), three
+// in float32 and where the conv stage and the zero-order hold come together
+// (they would spill at 128).
+template <typename InT, bool ZOH, bool CONV>
+constexpr int n16_waves_per_simd() {
+  return sizeof(InT) == 2 && !(ZOH && CONV) ? 4 : 3;
+}
+
+template <typename InT, bool HAS_RESET, bool ZOH, bool CONV>
+__global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void scan16_kernel(const ScanArgs a) {
   using P = Pair<InT>;
   constexpr int N = 16, T = 32, RING = 2 * T, MASK = RING - 1, CPW = 16, THREADS = 256;
   constexpr int S_IN = sizeof(InT);
@@ -162,10 +171,22 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   const float s_bias = dvalid && a.dt_bias ? a.dt_bias[d] : 0.0f;
   const float s_dskip = dvalid && a.Dskip ? a.Dskip[d] : 0.0f;
   const bool has_z = a.z != nullptr;
+  // Conv stage: the taps of channel d right-aligned in four slots (widths
+  // below 4 have leading zero taps) and its bias.
+  float s_cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s_cb = 0.0f;
+  if (CONV && dvalid) {
+    for (int q = 0; q < a.conv_k; ++q) s_cw[4 - a.conv_k + q] = a.conv_w[d * a.conv_k + q];
+    s_cb = a.conv_b ? a.conv_b[d] : 0.0f;
+  }
 
+  // uh0, uh1: with the conv stage, the inputs of steps stl - 4 .. stl - 1 (two
+  // pairs) and rsh the reset flags of stl - 2, stl - 1: the conv window of the
+  // thread's two steps reaches three steps back.
   struct Raw {
     typename P::raw u, dt, z, bb, cc;
-    uint32_t rs;
+    typename P::raw uh0, uh1;
+    uint32_t rs, rsh;
   };
   struct Out {
     float u0, u1, g0, g1;
@@ -183,6 +204,22 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   const __amdgpu_buffer_rsrc_t rsrc_C = make_rsrc(C_g + bc0, left_bc);
   const __amdgpu_buffer_rsrc_t rsrc_rs =
       make_rsrc(HAS_RESET ? a.reset + rs0 : nullptr, HAS_RESET ? bytes_left(a.B * a.L, rs0, 1) : 0);
+  // The conv window's earlier inputs through descriptors based 4 elements (2
+  // reset bytes) before the workgroup's first one. Inputs before the sequence
+  // (the first chunk of the first piece) are never loaded: they come from the
+  // initial conv state. The base is formed as an integer, since it can lie
+  // before the tensor; every address read through it lies inside.
+  const __amdgpu_buffer_rsrc_t rsrc_uh =
+      CONV ? make_rsrc(reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(u_g + row0) - 4 * S_IN),
+                       static_cast<int>(min(int64_t{left_rows} + 4 * S_IN, int64_t{0x7FFFFFFF})))
+           : rsrc_u;
+  const __amdgpu_buffer_rsrc_t rsrc_rsh =
+      CONV && HAS_RESET ? make_rsrc(reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(a.reset + rs0) - 2),
+                                    static_cast<int>(min(int64_t{bytes_left(a.B * a.L, rs0, 1)} + 2,
+                                                         int64_t{0x7FFFFFFF})))
+                        : rsrc_rs;
+  // whether this thread's window reaches before the sequence in chunk 0
+  const bool head0 = CONV && t_seg == 0 && stl < 4;
 
   auto load_chunk = [&](int J, Raw& r) {
     const uint32_t tau0 = static_cast<uint32_t>(J * T);
@@ -194,12 +231,47 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
     r.bb = P::load(rsrc_B, bo);
     r.cc = P::load(rsrc_C, bo);
     if (HAS_RESET) r.rs = __builtin_amdgcn_raw_buffer_load_b16(rsrc_rs, stl + tau0, 0, 0);
+    if constexpr (CONV) {
+      r.uh0 = r.uh1 = P::zero();
+      r.rsh = 0;
+      if (J > 0 || !head0) {
+        r.uh0 = P::load(rsrc_uh, ro);
+        r.uh1 = P::load(rsrc_uh, ro + 2 * S_IN);
+        if (HAS_RESET) r.rsh = __builtin_amdgcn_raw_buffer_load_b16(rsrc_rsh, stl + tau0, 0, 0);
+      } else if (stl == 2) {
+        r.uh1 = P::load(rsrc_uh, ro + 2 * S_IN);  // steps 0, 1
+        if (HAS_RESET) r.rsh = __builtin_amdgcn_raw_buffer_load_b16(rsrc_rsh, stl + tau0, 0, 0);
+      }
+    }
   };
 
   auto store_chunk = [&](int J, const int par, const int bpart, const Raw& r, Out& o) {
     const int tau0 = J * T;
     float b0 = P::lo(r.bb), b1 = P::hi(r.bb), c0 = P::lo(r.cc), c1 = P::hi(r.cc);
     float u0 = P::lo(r.u), u1 = P::hi(r.u);
+    if constexpr (CONV) {
+      // the scan input is silu(causal conv of u) over steps stl - 3 .. stl + 1
+      float x3 = P::hi(r.uh0), x2 = P::lo(r.uh1), x1 = P::hi(r.uh1);  // steps stl - 3, stl - 2, stl - 1
+      if (J == 0 && head0) {
+        // steps before the sequence: the initial conv state (oldest first), or zeros
+        const int K = a.conv_k;
+        auto before = [&](int pos) {
+          return a.conv_state_in && pos >= 1 - K && dvalid
+                     ? a.conv_state_in[(static_cast<int64_t>(b) * a.D + d) * (K - 1) + (pos + K - 1)]
+                     : 0.0f;
+        };
+        x3 = before(stl - 3);
+        if (stl == 0) {
+          x2 = before(-2);
+          x1 = before(-1);
+        }
+      }
+      const bool rq0 = HAS_RESET && (r.rs & 0xFFu), rq1 = HAS_RESET && (r.rs & 0xFF00u);
+      const bool rm1 = HAS_RESET && (r.rsh & 0xFF00u), rm2 = HAS_RESET && (r.rsh & 0xFFu);
+      const float x0 = u0;
+      u0 = silu_f32(conv_pre(s_cw, s_cb, x3, x2, x1, x0, rq0, rm1, rm2));
+      u1 = silu_f32(conv_pre(s_cw, s_cb, x2, x1, x0, u1, rq1, rq0, rm1));
+    }
     float dl0 = softplus_f32(P::lo(r.dt) + s_bias);
     float dl1 = softplus_f32(P::hi(r.dt) + s_bias);
     if (!group_full || tau0 + T > Lseg) {
@@ -341,7 +413,7 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
   // workgroups resident per CU: one wave per SIMD each, as many as the occupancy bound allows
-  const ProgressPriority prio(nchunks, a.nblocks <= 256 * (sizeof(InT) == 2 ? 4 : 3));
+  const ProgressPriority prio(nchunks, a.nblocks <= 256 * n16_waves_per_simd<InT, ZOH, CONV>());
   // One barrier per chunk. The (B, C) ring is the only LDS data shared across
   // waves; the barrier after store_chunk(J) makes part J mod 3 visible, and a
   // wave past it knows that every wave has finished compute(J - 1), whose
@@ -376,15 +448,17 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 3) void scan16_kernel(c
   }
 
   if (dvalid && a.h_last && s == a.nseg - 1) a.h_last[(static_cast<int64_t>(b) * a.D + d) * N + k] = h;
+  if constexpr (CONV) {
+    if (a.conv_state_out && s == a.nseg - 1) write_final_conv_state<InT, HAS_RESET>(a, b, d0, CPW, tid);
+  }
 }
 
-// Whether the 16-state full pass takes this launch: 16 states, no conv
-// stage, not the checkpoint sweep, an even L (element pairs stay aligned) and
-// buffer ranges within 31 bits (17 rows of L elements plus a chunk).
+// Whether the 16-state full pass takes this launch: 16 states, not the
+// checkpoint sweep, an even L (element pairs stay aligned) and buffer ranges
+// within 31 bits (17 rows of L elements plus a chunk).
 bool n16_eligible(const ScanArgs& a, bool checkpoint) {
   const int64_t s_in = a.in_bf16 ? 2 : 4;
-  return a.N == 16 && !checkpoint && a.conv_w == nullptr && a.L % 2 == 0 &&
-         (17 * a.L + 256) * s_in < (int64_t{1} << 31);
+  return a.N == 16 && !checkpoint && a.L % 2 == 0 && (17 * a.L + 256) * s_in < (int64_t{1} << 31);
 }
 
 hipError_t launch_n16(const ScanArgs& args, int nblocks_full, int nblocks_agg, hipStream_t stream) {
@@ -399,20 +473,26 @@ hipError_t launch_n16(const ScanArgs& args, int nblocks_full, int nblocks_agg, h
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
-  SSM_LOG("launch scan16_kernel full: %s in, reset %d, zoh %d; grid %d x 256 threads (16 channels x 16 states "
-          "per workgroup, 32-step chunks), %d pieces of %lld steps",
-          args.in_bf16 ? "bf16" : "f32", reset, args.zoh, nblocks_full, args.nseg,
+  SSM_LOG("launch scan16_kernel full: %s in, reset %d, zoh %d, conv %d; grid %d x 256 threads (16 channels x 16 "
+          "states per workgroup, 32-step chunks), %d pieces of %lld steps",
+          args.in_bf16 ? "bf16" : "f32", reset, args.zoh, args.conv_w != nullptr, nblocks_full, args.nseg,
           static_cast<long long>(args.seg_len));
-  auto go = [&](auto in_t, auto has_reset, auto zoh) {
+  auto go = [&](auto in_t, auto has_reset, auto zoh, auto conv) {
     using InT = decltype(in_t);
-    constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value;
-    hipLaunchKernelGGL((scan16_kernel<InT, R, Z>), dim3(nblocks_full), dim3(256), 0, stream, full);
+    constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value, C = decltype(conv)::value;
+    hipLaunchKernelGGL((scan16_kernel<InT, R, Z, C>), dim3(nblocks_full), dim3(256), 0, stream, full);
+  };
+  auto with_conv = [&](auto in_t, auto has_reset, auto zoh) {
+    if (args.conv_w)
+      go(in_t, has_reset, zoh, std::true_type{});
+    else
+      go(in_t, has_reset, zoh, std::false_type{});
   };
   auto with_zoh = [&](auto in_t, auto has_reset) {
     if (args.zoh)
-      go(in_t, has_reset, std::true_type{});
+      with_conv(in_t, has_reset, std::true_type{});
     else
-      go(in_t, has_reset, std::false_type{});
+      with_conv(in_t, has_reset, std::false_type{});
   };
   if (args.in_bf16) {
     if (reset)

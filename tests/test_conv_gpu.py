@@ -86,6 +86,21 @@ def test_conv_with_split_sequence(nseg):
     assert_close(gpu_conv_scan(x, num_segments=nseg), oracle_conv_scan(x), wl.BF16)
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_conv_resets_near_piece_starts(dtype):
+    # pieces start mid-sequence: a piece's first conv windows read the previous
+    # piece's inputs and reset flags; resets around the likely piece starts
+    x = conv_case(2, 20, 3000, 16, 4, dtype, 17, dt_lo=1e-3, dt_hi=1e-2)
+    x["reset"] = np.zeros((2, 3000), np.uint8)
+    for t0 in (750, 752, 768, 1500, 1504, 1536, 2250, 2256, 2304):
+        x["reset"][0, t0 - 2: t0 + 2] = 1
+        x["reset"][1, t0 + 1] = 1
+    got, cs = gpu_conv_scan(x, num_segments=4, want_state=True)
+    ref, rcs = oracle_conv_scan(x, want_state=True)
+    assert_close(got, ref, dtype)
+    np.testing.assert_array_equal(cs, rcs)
+
+
 def test_conv_long_sequence_automatic_split():
     x = conv_case(1, 32, 40000, 16, 4, wl.BF16, 21, packed=True, dt_lo=1e-3, dt_hi=1e-2)
     assert_close(gpu_conv_scan(x), oracle_conv_scan(x), wl.BF16)

@@ -383,7 +383,7 @@ def test_launch_log_names_kernels_and_grids():
     assert len(lines) == 4, lines
     assert lines[0].startswith("[ssm] ssm_scan_fwd: B 2 D 32 L 64 N 16, real state, f32 in, f32 out")
     # 16 states, even length: the 16-state pass, 2 batches x 2 groups of 16 channels
-    assert lines[1].startswith("[ssm] launch scan16_kernel full: f32 in, reset 0, zoh 0; grid 4 x 256 threads"), lines[1]
+    assert lines[1].startswith("[ssm] launch scan16_kernel full: f32 in, reset 0, zoh 0, conv 0; grid 4 x 256 threads"), lines[1]
     assert lines[2].startswith("[ssm] ssm_scan_fwd: B 1 D 24 L 50 N 128")
     # 128 states: two states per lane over four rows, 8 channels per workgroup -> 3 workgroups
     assert lines[3].startswith("[ssm] launch scan_kernel<Tile<2,4>> full: f32 in, reset 0, conv 0, zoh 0; "
