@@ -160,9 +160,12 @@ __device__ __forceinline__ void zoh_dq_dA(float dl, const CState& q, float are, 
 // (hr, hi) <- P[i] (hr, hi) + H[i] (complex) for i = 0 .. count - 1 in
 // order: the aggregates of the pieces before this one, `stride` floats
 // apart, each an (re, im) pair. The loads go out eight pieces at a time.
+// CONJ: conj(P[i]) in place of P[i] (the adjoint's fold over later segments).
+template <bool CONJ = false>
 __device__ __forceinline__ void fold_aggregates_c(const float* P, const float* H, int count, int64_t stride,
                                                   float& hr, float& hi) {
   auto one = [&](float pr, float pi, float gr, float gi) {
+    if (CONJ) pi = -pi;
     const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, gr));
     const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, gi));
     hr = nr;

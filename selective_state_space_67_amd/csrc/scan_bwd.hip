@@ -225,10 +225,9 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
     dA[j] = 0.0f;
     float gg = ok && a.dh_last ? a.dh_last[bdn + n] : 0.0f;
     if (ok) {
-      for (int sp = a.nsegb - 1; sp > s; --sp) {
-        const int64_t wi = ((static_cast<int64_t>(b) * a.nsegb + sp) * a.D + d) * N + n;
-        gg = __builtin_fmaf(a.seg_P[wi], gg, a.seg_G[wi]);
-      }
+      // the later segments, last one first (stride back one segment)
+      const int64_t wl = ((static_cast<int64_t>(b) * a.nsegb + a.nsegb - 1) * a.D + d) * N + n;
+      gg = fold_aggregates(a.seg_P + wl, a.seg_G + wl, a.nsegb - 1 - s, -a.D * N, gg);
     }
     gv[j] = gg;
   }

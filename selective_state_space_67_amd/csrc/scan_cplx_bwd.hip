@@ -344,15 +344,9 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
     const bool ok = dvalid && n0 + j < N;
     xr[j] = ok && a.dh_last ? a.dh_last[e] : 0.0f;
     xi[j] = ok && a.dh_last ? a.dh_last[e + 1] : 0.0f;
-    if (ok) {
-      for (int q = a.nsegb - 1; q > sg; --q) {  // X <- conj(P) X + G
-        const int64_t w = ((static_cast<int64_t>(b) * a.nsegb + q) * a.D + d) * N * 2 + 2 * (n0 + j);
-        const float pr = a.seg_P[w], pi = a.seg_P[w + 1];
-        const float nr = __builtin_fmaf(pr, xr[j], __builtin_fmaf(pi, xi[j], a.seg_G[w]));
-        const float ni = __builtin_fmaf(pr, xi[j], __builtin_fmaf(-pi, xr[j], a.seg_G[w + 1]));
-        xr[j] = nr;
-        xi[j] = ni;
-      }
+    if (ok) {  // X <- conj(P) X + G over the later segments, last one first
+      const int64_t wl = ((static_cast<int64_t>(b) * a.nsegb + a.nsegb - 1) * a.D + d) * N * 2 + 2 * (n0 + j);
+      fold_aggregates_c<true>(a.seg_P + wl, a.seg_G + wl, a.nsegb - 1 - sg, -a.D * N * 2, xr[j], xi[j]);
     }
     dar[j] = 0.0f;
     dai[j] = 0.0f;
