@@ -211,6 +211,23 @@ def measure_forward(args, torch, binding, wl, timer, evict):
                 warm=warm, elements=elements)
 
 
+def measure_wavefront(torch, binding, timer, f, evict, steps):
+    """The same forward through ssm_scan_fwd_wavefront (a DPP wavefront scan of
+    the affine pairs inside each 64-step chunk, carry across chunks), timed
+    like the headline: cold launches, median."""
+    cfg, t = f["cfg"], f["t"]
+    if cfg["N"] != 16:
+        return None
+    out = torch.empty_like(f["out"])
+    call = binding.prepare_scan(t["u"], t["dt_raw"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                                Dskip=t["Dskip"], z=t["z"], reset=t["reset"], out=out, wavefront=True)
+    for _ in range(3):
+        call()
+    cold = timer.launches(call, steps, evict=evict)
+    torch.cuda.synchronize()
+    return dict(cold=cold, out=out)
+
+
 def hbm_ceiling(torch, timer):
     dev = torch.device("cuda:0")
     src = torch.ones(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
@@ -494,7 +511,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other entry points and options (backward, conv, zoh, complex, shard, sweep)")
-    ap.add_argument("--only", choices=("forward", "decode", "backward"), default=None,
+    ap.add_argument("--only", choices=("forward", "decode", "backward", "wavefront"), default=None,
                     help="run just this entry point's timed launches (for profiler runs); prints no JSON line")
     ap.add_argument("--workload", default="mamba130m-layer",
                     help="workload name: mamba130m-layer (the default and the headline); tiny-fp32, "
@@ -536,6 +553,10 @@ def main():
     if args.only == "backward":
         measure_backward(torch, binding, wl, timer, f, args.steps)
         print("backward timed", flush=True)
+        return
+    if args.only == "wavefront":
+        wf = measure_wavefront(torch, binding, timer, f, evict, args.steps)
+        print("wavefront timed: median %.1f us" % (np.median(wf["cold"]) * 1e3), flush=True)
         return
 
     cfg, elements = f["cfg"], f["elements"]
@@ -592,6 +613,17 @@ def main():
                  "elements_per_s": elements / warm_s, "hbm_gbps": abytes / warm_s / 1e9},
         "hbm_ceiling": ceiling,
     }
+    wf = measure_wavefront(torch, binding, timer, f, evict, min(args.steps, 50)) if not args.no_extras else None
+    if wf is not None:
+        wf_s = float(np.median(wf["cold"])) / 1e3
+        result["wavefront_scan"] = {
+            "workload": "the same forward through ssm_scan_fwd_wavefront: one wave per (b, d), one step per lane, "
+                        "a DPP scan of the affine pairs inside each 64-step chunk, carry across chunks",
+            "launch_ms_median": wf_s * 1e3, "elements_per_s": elements / wf_s,
+            "vs_forward": wf_s / cold_s,
+            "max_abs_diff_vs_forward": float((wf["out"] - f["out"]).abs().max().item()),
+        }
+        del wf
     result["decode"] = measure_decode(torch, binding, wl, timer, evict)
     del evict
     if not args.no_extras:

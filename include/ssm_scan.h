@@ -216,6 +216,26 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream);
 ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, void* hip_stream);
 
 /*
+ * The same forward computed as a chunked two-level associative scan, the
+ * parallel form of the recurrence ("Technical analysis: Mamba selective state
+ * spaces", 2.2, the parallel scan in place of the serial recursion): one wave
+ * per (b, d), one step per lane of a 64-step chunk; per state the affine
+ * pairs (exp(delta_t A[d,n]), delta_t B[b,t,n] u_t) are composed by a
+ * wavefront scan with DPP lane moves (six levels), and the state after each
+ * chunk carries into the next. It exists to measure that design against
+ * ssm_scan_fwd's sequential-in-lane kernels, which are faster on gfx950; the
+ * results agree with ssm_scan_fwd's within rounding (the products of the decays
+ * are formed in a different order).
+ *   p : as for ssm_scan_fwd, restricted to dstate = 16, state_kind
+ *       SSM_STATE_REAL, discretization SSM_DISC_DELTA_B and no conv stage
+ *       (others return SSM_ERR_UNSUPPORTED before any launch), with Bm and
+ *       Cm aligned to 16 bytes (else SSM_ERR_MISALIGNED). The sequence is
+ *       never split: workspace, workspace_bytes and num_segments are
+ *       ignored, and nothing is allocated. Other errors as for ssm_scan_fwd.
+ */
+ssm_status ssm_scan_fwd_wavefront(const ssm_scan_params* p, void* hip_stream);
+
+/*
  * Affine aggregate of a whole sequence, for scanning one sequence in shards
  * (the pages advise processing extremely long sequences in chunks: "Technical
  * analysis: Mamba selective state spaces", section 7), for instance one shard

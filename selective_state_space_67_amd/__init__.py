@@ -2,7 +2,8 @@
 
 The public entry points mirror the C functions of ``include/ssm_scan.h``:
 ``ssm_scan_fwd``, ``ssm_scan_fwd_noalloc`` (the same scan without any
-allocation), ``ssm_scan_workspace_size``, ``ssm_scan_aggregate`` (the
+allocation), ``ssm_scan_fwd_wavefront`` (the same scan as a chunked
+associative scan, for comparison), ``ssm_scan_workspace_size``, ``ssm_scan_aggregate`` (the
 affine aggregate of a sequence shard), ``ssm_state_update`` and the backward
 pass ``ssm_scan_bwd``. They
 take torch tensors only as carriers of device pointers and the current stream;
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     ssm_scan_bwd,
     ssm_scan_fwd,
     ssm_scan_fwd_noalloc,
+    ssm_scan_fwd_wavefront,
     ssm_scan_workspace_size,
     ssm_state_update,
 )

@@ -81,7 +81,8 @@ class BwdParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_aggregate_workspace_size",
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_wavefront",
+           "ssm_scan_aggregate_workspace_size",
            "ssm_scan_aggregate",
            "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string", "ssm_last_error",
            "ssm_version", "ssm_abi_struct_size")
@@ -109,6 +110,8 @@ def load_library():
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanParams), vp]
     lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssm_scan_fwd_wavefront.argtypes = [ctypes.POINTER(ScanParams), vp]
+    lib.ssm_scan_fwd_wavefront.restype = ctypes.c_int
     lib.ssm_scan_aggregate_workspace_size.argtypes = [ctypes.POINTER(ScanParams), ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_aggregate_workspace_size.restype = ctypes.c_int
     lib.ssm_scan_aggregate.argtypes = [ctypes.POINTER(ScanParams), vp, vp, vp]
@@ -354,12 +357,29 @@ def ssm_scan_fwd_noalloc(u, dt_raw, A, Bm, Cm, *, out, dt_bias=None, Dskip=None,
     return out
 
 
+def ssm_scan_fwd_wavefront(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None,
+                           out=None, h_last=None, out_dtype=None, stream=None):
+    """The same forward as a chunked associative scan with a DPP wavefront scan
+    inside each 64-step chunk (include/ssm_scan.h, ssm_scan_fwd_wavefront): N = 16,
+    real state, delta B coefficient, no conv stage. Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(u.shape, dtype=out_dtype or torch.float32, device=u.device)
+    p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
+                     0, None, None, None, None, False, False)
+    _check(lib.ssm_scan_fwd_wavefront(ctypes.byref(p), _stream(stream, u.device)))
+    return out
+
+
 def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, reset=None, h0=None, out=None,
                  h_last=None, out_dtype=None, num_segments=0, conv_w=None, conv_b=None, conv_state_in=None,
-                 conv_state_out=None, zoh=False, complex_state=False, stream=None):
+                 conv_state_out=None, zoh=False, complex_state=False, wavefront=False, stream=None):
     """Marshal the arguments of ssm_scan_fwd once; returns a no-argument callable
     that enqueues the same scan again (same tensors, same stream) each time it is
-    called. The tensors must stay alive and unchanged in shape while it is used."""
+    called. The tensors must stay alive and unchanged in shape while it is used.
+    wavefront=True calls ssm_scan_fwd_wavefront instead (no workspace)."""
     import torch
 
     lib = load_library()
@@ -368,7 +388,8 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
     p = _scan_params(u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, out_dtype,
                      num_segments, conv_w, conv_b, conv_state_in, conv_state_out, zoh, complex_state)
     n = ctypes.c_size_t(0)
-    _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    if not wavefront:
+        _check(lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
     keep = [u, dt_raw, A, Bm, Cm, dt_bias, Dskip, z, reset, h0, out, h_last, conv_w, conv_b, conv_state_in,
             conv_state_out]
     if n.value:
@@ -377,7 +398,7 @@ def prepare_scan(u, dt_raw, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, rese
         p.workspace = _ptr(ws)
         p.workspace_bytes = int(n.value)
     st = _stream(stream, u.device)
-    fn = lib.ssm_scan_fwd
+    fn = lib.ssm_scan_fwd_wavefront if wavefront else lib.ssm_scan_fwd
     pref = ctypes.byref(p)
 
     def call():

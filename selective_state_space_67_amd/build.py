@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_fwd_f32_plain.hip", "scan_fwd_f32_reset.hip", "scan_fwd_bf16_plain.hip",
-           "scan_fwd_bf16_reset.hip", "scan_fwd_n16.hip", "scan_bwd.hip", "state_update.hip", "scan_cplx.hip",
-           "scan_cplx_bwd.hip", "fill.hip", "scan_noalloc.hip", "log.cpp"]
+           "scan_fwd_bf16_reset.hip", "scan_fwd_n16.hip", "scan_fwd_wavefront.hip", "scan_bwd.hip", "state_update.hip",
+           "scan_cplx.hip", "scan_cplx_bwd.hip", "fill.hip", "scan_noalloc.hip", "log.cpp"]
 OUT = os.path.join(HERE, "libssmscan.so")
 OBJ = os.path.join(ROOT, "_build")
 ARCH = "gfx950"

@@ -372,12 +372,19 @@ ssm_status plan_bwd(const ssm_scan_bwd_params* p, const ScanSizes& sz, BwdLayout
 // The forward scan. With noalloc the split-scan buffer is the library's
 // scratch on the current device instead of the caller's workspace (whose
 // fields are then ignored); a split larger than the scratch is refused.
-ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
+// With wavefront the scan runs as the chunked associative scan of
+// scan_fwd_wavefront.hip (16 real states, delta B, no conv stage; never split).
+ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc, bool wavefront = false) {
   if (!p) return fail(SSM_ERR_NULL_POINTER, "params is NULL");
   ScanCheck c;
   Range inputs[kScanInputs];
   ssm_status s = check_scan_inputs(p, false, &c, inputs);
   if (s != SSM_OK) return s;
+  if (wavefront && (p->dstate != 16 || c.cplx || p->discretization != SSM_DISC_DELTA_B || p->conv_w))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "ssm_scan_fwd_wavefront supports dstate 16, real states, the delta B coefficient and no conv stage");
+  if (wavefront && (!aligned(p->Bm, 16) || !aligned(p->Cm, 16)))  // its lanes load whole 16-state rows
+    return fail(SSM_ERR_MISALIGNED, "ssm_scan_fwd_wavefront needs Bm and Cm aligned to 16 bytes");
   const ScanSizes& sz = c.sz;
   const Range out = range(p->out, sz.bdl, c.so, "out");
   const Range hl = range(p->h_last, sz.bdn * c.cw, 4, "h_last");
@@ -394,6 +401,13 @@ ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
   int64_t seg_len;
   size_t ws;
   if ((s = plan_scan(p, &nseg, &seg_len, &ws)) != SSM_OK) return s;
+  if (wavefront) {  // one wave per (b, d) over the whole sequence
+    nseg = 1;
+    seg_len = p->seqlen;
+    ws = 0;
+    if ((p->batch * p->dim + 3) / 4 > std::numeric_limits<int32_t>::max())
+      return fail(SSM_ERR_BAD_SHAPE, "problem needs more workgroups than one launch allows");
+  }
   const Range outs[] = {out, hl, cso};
   if (noalloc) {
     if (ws > ssm::noalloc_scratch_bytes())
@@ -405,7 +419,8 @@ ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
   }
   SSM_LOG("%s: B %lld D %lld L %lld N %lld, %s state, %s in, %s out, %s, conv width %lld, resets %d; %d pieces of "
           "%lld steps, workspace %zu bytes%s",
-          noalloc ? "ssm_scan_fwd_noalloc" : "ssm_scan_fwd", (long long)p->batch, (long long)p->dim,
+          noalloc ? "ssm_scan_fwd_noalloc" : wavefront ? "ssm_scan_fwd_wavefront" : "ssm_scan_fwd",
+          (long long)p->batch, (long long)p->dim,
           (long long)p->seqlen, (long long)p->dstate, c.cplx ? "complex" : "real",
           p->in_dtype == SSM_BF16 ? "bf16" : "f32", p->out_dtype == SSM_BF16 ? "bf16" : "f32",
           p->discretization == SSM_DISC_ZOH ? "zoh" : "delta B", (long long)c.K, p->reset != nullptr, nseg,
@@ -432,8 +447,10 @@ ssm_status scan_fwd(const ssm_scan_params* p, void* hip_stream, bool noalloc) {
   plan.z = p->z;
   plan.Dskip = p->Dskip;
   plan.h0 = p->h0;
-  const hipError_t e = c.cplx ? ssm::launch_scan_cplx(plan, static_cast<hipStream_t>(hip_stream))
-                              : ssm::launch_scan(plan, static_cast<hipStream_t>(hip_stream));
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = wavefront ? ssm::launch_scan_wavefront(plan, st)
+                       : c.cplx  ? ssm::launch_scan_cplx(plan, st)
+                                 : ssm::launch_scan(plan, st);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -679,6 +696,10 @@ ssm_status ssm_scan_workspace_size(const ssm_scan_params* p, size_t* bytes) {
 ssm_status ssm_scan_fwd(const ssm_scan_params* p, void* hip_stream) { return scan_fwd(p, hip_stream, false); }
 
 ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, void* hip_stream) { return scan_fwd(p, hip_stream, true); }
+
+ssm_status ssm_scan_fwd_wavefront(const ssm_scan_params* p, void* hip_stream) {
+  return scan_fwd(p, hip_stream, false, true);
+}
 
 ssm_status ssm_scan_aggregate_workspace_size(const ssm_scan_params* p, size_t* bytes) {
   if (!p || !bytes) return fail(SSM_ERR_NULL_POINTER, "params or bytes is NULL");

@@ -90,6 +90,9 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int nseg);
 int64_t scan_grid_blocks(int64_t B, int64_t D, int64_t N, int nseg);
 
 hipError_t launch_scan(const ScanPlan& plan, hipStream_t stream);
+// The forward as a chunked associative scan (scan_fwd_wavefront.hip): N = 16,
+// real states, delta B, no conv stage, one piece.
+hipError_t launch_scan_wavefront(const ScanPlan& plan, hipStream_t stream);
 // Affine aggregate of the whole sequence into P and H (B, D, N): the pieces'
 // aggregates (in `ws`, nseg of each when nseg > 1) folded in order.
 hipError_t launch_aggregate(const ScanPlan& plan, float* P, float* H, hipStream_t stream);

@@ -234,6 +234,25 @@ def test_noalloc_checks_like_the_forward_and_refuses_large_splits(lib):
     assert lib.ssm_scan_fwd_noalloc(ctypes.byref(p), None) == 6
 
 
+def test_wavefront_checks_like_the_forward_and_refuses_other_variants(lib):
+    # the same host checks as ssm_scan_fwd, before any device work
+    f = lib.ssm_scan_fwd_wavefront
+    assert f(None, None) == 1
+    assert f(ctypes.byref(scan_params(u=0)), None) == 1
+    assert f(ctypes.byref(scan_params(dstate=0)), None) == 2
+    assert f(ctypes.byref(scan_params(in_dtype=7)), None) == 3
+    assert f(ctypes.byref(scan_params(u=BASE + 1)), None) == 4
+    assert f(ctypes.byref(scan_params(out=BASE)), None) == 7
+    # only 16 real states with the delta B coefficient and no conv stage
+    for kw in (dict(dstate=8), dict(dstate=32), dict(discretization=1), dict(state_kind=1),
+               dict(conv_w=BASE + 0x7000000, conv_width=4)):
+        assert f(ctypes.byref(scan_params(**kw)), None) == 5, kw
+        assert b"wavefront" in lib.ssm_last_error()
+    # whole 16-state rows of B and C are loaded at once
+    assert f(ctypes.byref(scan_params(Bm=BASE + 0x7000008)), None) == 4
+    assert f(ctypes.byref(scan_params(Cm=BASE + 0x7000008)), None) == 4
+
+
 def test_automatic_split_only_for_long_sequences_with_few_channels(lib):
     n = ctypes.c_size_t(0)
     # 1 x 256 channels x 131072 steps: few workgroups, long sequence -> split
