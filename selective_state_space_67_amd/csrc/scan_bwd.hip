@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
         float sum = s_acc[k];
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) sum += s_acc[ww * AW + k];
-        base[(type ? part_type : 0) + tt * N + n] = sum;
+        __builtin_nontemporal_store(sum, base + (type ? part_type : 0) + tt * N + n);
       }
     }
   };
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
     const int64_t tc = t_seg + static_cast<int64_t>(J) * kK;
     const int64_t ci = ((static_cast<int64_t>(b) * a.n_ck + tc / kK) * a.D + d) * N;
 #pragma unroll
-    for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? a.ckpt[ci + n0 + j] : 0.0f;
+    for (int j = 0; j < kNPL; ++j) hs[j] = dvalid && n0 + j < N ? __builtin_nontemporal_load(a.ckpt + ci + n0 + j) : 0.0f;
   };
 
   // The chunk pair (J, J + 1) of input gradients from s_out to memory: one
@@ -371,14 +371,16 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void scan_bwd_kernel(const B
       if (f32) {
         float* p = static_cast<float*>(dst) + at;
         if (cnt == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-          *reinterpret_cast<float4*>(p) = v;
+          typedef float v4f __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
         } else {
           for (int k = 0; k < cnt; ++k) p[k] = e[k];
         }
       } else {
         bf16_t* p = static_cast<bf16_t*>(dst) + at;
         if (cnt == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
-          *reinterpret_cast<uint2*>(p) = make_uint2(bf16_pair(e[0], e[1]), bf16_pair(e[2], e[3]));
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(v2u{bf16_pair(e[0], e[1]), bf16_pair(e[2], e[3])}, reinterpret_cast<v2u*>(p));
         } else {
           for (int k = 0; k < cnt; ++k) store_elem(p, k, e[k]);
         }

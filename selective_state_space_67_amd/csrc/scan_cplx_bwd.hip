@@ -392,7 +392,9 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           const bool ok = dvalid && n0 + j < N;
-          const float2 v = ok ? *reinterpret_cast<const float2*>(ck + 2 * (n0 + j)) : make_float2(0.0f, 0.0f);
+          // read once: a nontemporal load keeps the checkpoints out of the L2
+          typedef float v2f __attribute__((ext_vector_type(2)));
+          const v2f v = ok ? __builtin_nontemporal_load(reinterpret_cast<const v2f*>(ck + 2 * (n0 + j))) : v2f{0.0f, 0.0f};
           hr[j] = v.x;
           hi[j] = v.y;
         }
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(kThreads, ZOH ? 1 : 2) void cplx_bwd_kernel(const C
 #pragma unroll
               for (int cc = 0; cc < kCPW; ++cc) acc += sd[((fs * kCPW + cc) * NPAD + n) * 4 + comp];
               float* dst = comp < 2 ? a.partB : a.partC;
-              dst[((gbl + t) * N + n) * 2 + (comp & 1)] = acc;
+              __builtin_nontemporal_store(acc, dst + ((gbl + t) * N + n) * 2 + (comp & 1));  // written once
             }
           }
           __syncthreads();
