@@ -60,27 +60,32 @@ struct WaveArgs {
 // bound_ctrl, lanes with no source lane and rows outside the mask are not
 // written: they keep their own pair, as if composed with the identity (1, 0).
 // The compiler folds no DPP move into a float multiply or FMA, so the level
-// is written out here; the leading s_nop gives the two wait states gfx9
-// requires between a VALU write of a register and a DPP read of it (inside
-// the block, a state's registers are read by DPP only in the next level's
-// block, 14 instructions or more after their last write).
+// is written out here, and the compiler's hazard checks do not see the DPP
+// inside the block: the leading s_nop gives the two wait states gfx9 requires
+// between a VALU write of a register and a DPP read of it, and the chunk's
+// first block waits five, the requirement after a write of EXEC (the
+// prefetch's per-lane branch precedes the scan). Inside the blocks a state's
+// registers are read by DPP only in the next level's block, 14 instructions
+// or more after their last write.
 #define SSM_WF_PAIR(A, B, CTRL) "v_fmac_f32_dpp " B ", " B ", " A " " CTRL "\n\tv_mul_f32_dpp " A ", " A ", " A " " CTRL "\n\t"
-#define SSM_WF_LEVEL8(CTRL)                                                                                        \
-  "s_nop 1\n\t" SSM_WF_PAIR("%0", "%8", CTRL) SSM_WF_PAIR("%1", "%9", CTRL) SSM_WF_PAIR("%2", "%10", CTRL)       \
+#define SSM_WF_LEVEL8(NOP, CTRL)                                                                                   \
+  NOP "\n\t" SSM_WF_PAIR("%0", "%8", CTRL) SSM_WF_PAIR("%1", "%9", CTRL) SSM_WF_PAIR("%2", "%10", CTRL)           \
       SSM_WF_PAIR("%3", "%11", CTRL) SSM_WF_PAIR("%4", "%12", CTRL) SSM_WF_PAIR("%5", "%13", CTRL)                  \
           SSM_WF_PAIR("%6", "%14", CTRL) SSM_WF_PAIR("%7", "%15", CTRL)
 
+// LEVEL 6 is level 0 as the chunk's first block (the longer wait).
 template <int LEVEL>
 __device__ __forceinline__ void scan_level8(float* a, float* b) {
 #define SSM_WF_OPERANDS                                                                                             \
   : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(b[0]),    \
     "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7])
-  if constexpr (LEVEL == 0) asm volatile(SSM_WF_LEVEL8("row_shr:1 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
-  if constexpr (LEVEL == 1) asm volatile(SSM_WF_LEVEL8("row_shr:2 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
-  if constexpr (LEVEL == 2) asm volatile(SSM_WF_LEVEL8("row_shr:4 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
-  if constexpr (LEVEL == 3) asm volatile(SSM_WF_LEVEL8("row_shr:8 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
-  if constexpr (LEVEL == 4) asm volatile(SSM_WF_LEVEL8("row_bcast:15 row_mask:0xa bank_mask:0xf") SSM_WF_OPERANDS);
-  if constexpr (LEVEL == 5) asm volatile(SSM_WF_LEVEL8("row_bcast:31 row_mask:0xc bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 6) asm volatile(SSM_WF_LEVEL8("s_nop 4", "row_shr:1 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 0) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_shr:1 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 1) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_shr:2 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 2) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_shr:4 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 3) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_shr:8 row_mask:0xf bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 4) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_bcast:15 row_mask:0xa bank_mask:0xf") SSM_WF_OPERANDS);
+  if constexpr (LEVEL == 5) asm volatile(SSM_WF_LEVEL8("s_nop 1", "row_bcast:31 row_mask:0xc bank_mask:0xf") SSM_WF_OPERANDS);
 #undef SSM_WF_OPERANDS
 }
 
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(kWaves * 64) void scan_wavefront_kernel(const WaveA
     // inclusive scan of the pairs over the chunk's 64 lanes: row_shr:1, 2, 4,
     // 8 inside rows of 16 lanes, then row_bcast:15 into rows 1 and 3 and
     // row_bcast:31 into rows 2 and 3
-    scan_level8<0>(av, bv);
+    scan_level8<6>(av, bv);
     scan_level8<0>(av + 8, bv + 8);
     scan_level8<1>(av, bv);
     scan_level8<1>(av + 8, bv + 8);
