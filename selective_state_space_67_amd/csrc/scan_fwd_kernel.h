@@ -357,8 +357,14 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   // stay zero).
   auto load_chunk = [&](int J, Raw& r) {
     const int tau0 = J * T;
-    const InT* __restrict__ Bj = B_wg + static_cast<int64_t>(tau0) * N;
-    const InT* __restrict__ Cj = C_wg + static_cast<int64_t>(tau0) * N;
+    // B and C of the chunk: a workgroup-uniform base and 32-bit byte offsets
+    // below T * N * sizeof(InT), which the loads take as a scalar base plus a
+    // vector offset (no 64-bit address arithmetic per load).
+    const char* __restrict__ Bj = reinterpret_cast<const char*>(B_wg + static_cast<int64_t>(tau0) * N);
+    const char* __restrict__ Cj = reinterpret_cast<const char*>(C_wg + static_cast<int64_t>(tau0) * N);
+    auto bc_at = [](const char* base, unsigned item) {
+      return *reinterpret_cast<const InT*>(base + item * static_cast<unsigned>(sizeof(InT)));
+    };
     const InT* __restrict__ uj = u_wg + tau0;
     const InT* __restrict__ dtj = dt_wg + tau0;
     const InT* __restrict__ zj = z_wg ? z_wg + tau0 : nullptr;
@@ -393,8 +399,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       for (int q = 0; q < BC_ITEMS; ++q) {
         const bool ok = bc_n(q) < N;
         const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
-        r.b[q] = ok ? Bj[off] : InT{};
-        r.c[q] = (FULL || CKPT) && ok ? Cj[off] : InT{};
+        r.b[q] = ok ? bc_at(Bj, off) : InT{};
+        r.c[q] = (FULL || CKPT) && ok ? bc_at(Cj, off) : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
@@ -409,8 +415,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       for (int q = 0; q < BC_ITEMS; ++q) {
         const bool ok = bc_n(q) < N && tau0 + bc_tl(q) < Lseg;
         const unsigned off = static_cast<unsigned>(bc_tl(q) * N + bc_n(q));
-        r.b[q] = ok ? Bj[off] : InT{};
-        r.c[q] = (FULL || CKPT) && ok ? Cj[off] : InT{};
+        r.b[q] = ok ? bc_at(Bj, off) : InT{};
+        r.c[q] = (FULL || CKPT) && ok ? bc_at(Cj, off) : InT{};
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
