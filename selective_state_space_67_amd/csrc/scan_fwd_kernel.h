@@ -169,6 +169,24 @@ constexpr int kernel_waves_per_simd() {
   return TL::MIN_WAVES_PER_SIMD;
 }
 
+// One chunk's B or C rows through a buffer descriptor: the base (the chunk's
+// first element) and the range move with the chunk in scalar registers, so a
+// staging item keeps one fixed 32-bit byte offset for the whole kernel. (With
+// plain pointers the compiler strength-reduces every item's address into its
+// own 64-bit pointer, advanced by a 64-bit vector add per chunk.) The range is
+// the bytes from the base to the end of the tensor, capped at 2^31 - 1; every
+// item a chunk loads lies inside it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(min(bytes, int64_t{0x7FFFFFFF})), 0x00020000);
+}
+__device__ __forceinline__ bf16_t buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t item, bf16_t) {
+  return bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, item * 2u, 0, 0)};
+}
+__device__ __forceinline__ float buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t item, float) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, item * 4u, 0, 0));
+}
+
 template <typename TL, typename InT, bool HAS_RESET, int MODE, bool CONV, bool ZOH>
 __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV, ZOH>())) void scan_kernel(
     const ScanArgs a) {
@@ -245,6 +263,7 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   const int64_t bc0 = (static_cast<int64_t>(b) * a.L + t_seg) * a.N;
   const InT* __restrict__ B_wg = static_cast<const InT*>(a.Bm) + bc0;
   const InT* __restrict__ C_wg = static_cast<const InT*>(a.Cm) + bc0;
+  const int64_t bc_total = a.B * a.L * a.N;  // elements of B (and of C)
   const uint8_t* __restrict__ rs_wg = HAS_RESET ? a.reset + static_cast<int64_t>(b) * a.L + t_seg : nullptr;
 
   const int tid = threadIdx.x;
@@ -357,13 +376,19 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   // stay zero).
   auto load_chunk = [&](int J, Raw& r) {
     const int tau0 = J * T;
-    // B and C of the chunk: a workgroup-uniform base and 32-bit byte offsets
-    // below T * N * sizeof(InT), which the loads take as a scalar base plus a
-    // vector offset (no 64-bit address arithmetic per load).
-    const char* __restrict__ Bj = reinterpret_cast<const char*>(B_wg + static_cast<int64_t>(tau0) * N);
-    const char* __restrict__ Cj = reinterpret_cast<const char*>(C_wg + static_cast<int64_t>(tau0) * N);
-    auto bc_at = [](const char* base, unsigned item) {
-      return *reinterpret_cast<const InT*>(base + item * static_cast<unsigned>(sizeof(InT)));
+    // B and C of the chunk: in the full pass and the checkpoint sweep through
+    // descriptors based at its first element (item offsets below T * N stay
+    // fixed; see chunk_rsrc). The aggregate pass, which loads only B, keeps
+    // plain loads: there the descriptors measured 2% slower (long-genomics).
+    const int64_t bc_left = (bc_total - bc0 - static_cast<int64_t>(tau0) * N) * static_cast<int64_t>(sizeof(InT));
+    const InT* __restrict__ Bp = B_wg + static_cast<int64_t>(tau0) * N;
+    const __amdgpu_buffer_rsrc_t Bj = chunk_rsrc(Bp, bc_left);
+    const __amdgpu_buffer_rsrc_t Cj = chunk_rsrc(C_wg + static_cast<int64_t>(tau0) * N, bc_left);
+    auto bc_at = [&](__amdgpu_buffer_rsrc_t r, unsigned item) {
+      if constexpr (MODE == kAggregate)
+        return Bp[item];  // only B is read in this mode
+      else
+        return buffer_elem(r, item, InT{});
     };
     const InT* __restrict__ uj = u_wg + tau0;
     const InT* __restrict__ dtj = dt_wg + tau0;
