@@ -83,14 +83,20 @@ struct Pair<float> {
 
 // Waves per SIMD the kernel is built for: four in bf16 (128 registers), three
 // in float32 and where the conv stage and the zero-order hold come together
-// (they would spill at 128).
-template <typename InT, bool ZOH, bool CONV>
+// (they would spill at 128); five for the compact-LDS layout below.
+template <typename InT, bool ZOH, bool CONV, bool FIVE>
 constexpr int n16_waves_per_simd() {
-  return sizeof(InT) == 2 && !(ZOH && CONV) ? 4 : 3;
+  return FIVE ? 5 : sizeof(InT) == 2 && !(ZOH && CONV) ? 4 : 3;
 }
 
-template <typename InT, bool HAS_RESET, bool ZOH, bool CONV>
-__global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void scan16_kernel(const ScanArgs a) {
+// FIVE: the compact-LDS layout (29 KB instead of 37 KB per workgroup, so that
+// five workgroups fit a CU where four do otherwise): a two-part (B, C) ring,
+// which costs a second barrier per chunk, and the read-out sums kept in the
+// (delta, delta*u) slots of copy 0 once no lane reads them any more. It is
+// used where five workgroups per CU save a round of the grid.
+template <typename InT, bool HAS_RESET, bool ZOH, bool CONV, bool FIVE>
+__global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV, FIVE>())) void scan16_kernel(
+    const ScanArgs a) {
   using P = Pair<InT>;
   constexpr int N = 16, T = 32, RING = 2 * T, MASK = RING - 1, CPW = 16, THREADS = 256;
   constexpr int S_IN = sizeof(InT);
@@ -104,12 +110,14 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
   //  two: a chunk's (B, C) spill over into the next part (the skewed columns
   //  t + n run past the chunk), so with two parts store_chunk(J + 1) would
   //  overwrite the part compute(J) reads. With three, the one barrier per
-  //  chunk (after store_chunk) orders every cross-wave use of the ring.
-  constexpr int BC_RING = 3 * T;
+  //  chunk (after store_chunk) orders every cross-wave use of the ring; the
+  //  compact layout has two parts and a second barrier before each staging.
+  constexpr int BC_PARTS = FIVE ? 2 : 3;
+  constexpr int BC_RING = BC_PARTS * T;
   constexpr int BC_STRIDE = BC_RING + 2;
   __shared__ __align__(16) float2 s_du[DU_COPY + CPW * DU_STRIDE];
   __shared__ __align__(16) float2 s_bc[N * BC_STRIDE];
-  __shared__ __align__(16) float s_y[CPW * RING];
+  __shared__ __align__(16) float s_y[FIVE ? 4 : CPW * RING];
 
   // Workgroup -> (piece, batch row, channel group), renumbered so that a batch
   // row's workgroups (which share B and C) run on one XCD.
@@ -319,9 +327,16 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
       make_rsrc(static_cast<char*>(a.out) + row0 * s_out, bytes_left(n_rows, row0, s_out));
   const uint32_t out_off = static_cast<uint32_t>(c * a.L + stl) * s_out;
 
+  // The compact layout keeps the read-out sum of step slot m in copy 0's
+  // (delta, delta*u) entry of slot m, float 2m of the channel's row: lane 15
+  // writes it at least 15 iterations after lane 14, the last lane that reads
+  // copy 0 there, and the wave that owns the channel does both, in order.
+  float* const yrow0 = reinterpret_cast<float*>(s_du + c * DU_STRIDE);
   auto finalize = [&](int J, const int par, const Out& o) {
     const int tau0 = J * T;
-    const float2 yy = *reinterpret_cast<const float2*>(s_y + c * RING + par * T + stl);
+    const int ys = par * T + stl;
+    const float2 yy = FIVE ? make_float2(yrow0[2 * ys], yrow0[2 * ys + 2])
+                           : *reinterpret_cast<const float2*>(s_y + c * RING + ys);
     const float o0 = __builtin_fmaf(s_dskip, o.u0, yy.x) * o.g0;
     const float o1 = __builtin_fmaf(s_dskip, o.u1, yy.y) * o.g1;
     const uint32_t off = out_off + static_cast<uint32_t>(tau0 * s_out);
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
   float yreg[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) yreg[i] = 0.0f;
-  float* const yslot = s_y + c * RING;
+  float* const yslot = s_y + (FIVE ? 0 : c * RING);
   auto step = [&](const int i, const int m0, float dl, const float dv, const float Bv, const float Cv) {
     if (HAS_RESET) {
       const bool rs = __float_as_int(dl) < 0;
@@ -370,8 +385,16 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
     yreg[i] = __builtin_fmaf(Cv, h, row_shr1(yreg[(i + 15) & 15]));
     if ((i & 3) == 2 && k == 15) {
       // steps m0+i-18 .. m0+i-15 are complete in this row: one aligned 16-byte store
-      *reinterpret_cast<float4*>(yslot + ((m0 + i - 18) & MASK)) =
-          make_float4(yreg[(i - 3) & 15], yreg[(i - 2) & 15], yreg[(i - 1) & 15], yreg[i]);
+      const int ym = (m0 + i - 18) & MASK;
+      if constexpr (FIVE) {
+        yrow0[2 * ym] = yreg[(i - 3) & 15];
+        yrow0[2 * ym + 2] = yreg[(i - 2) & 15];
+        yrow0[2 * ym + 4] = yreg[(i - 1) & 15];
+        yrow0[2 * ym + 6] = yreg[i];
+      } else {
+        *reinterpret_cast<float4*>(yslot + ym) =
+            make_float4(yreg[(i - 3) & 15], yreg[(i - 2) & 15], yreg[(i - 1) & 15], yreg[i]);
+      }
     }
   };
 
@@ -413,7 +436,7 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
   if (nchunks > 1) load_chunk(1, r1);
   __syncthreads();  // rings are empty before the first chunk is stored
   // workgroups resident per CU: one wave per SIMD each, as many as the occupancy bound allows
-  const ProgressPriority prio(nchunks, a.nblocks <= 256 * n16_waves_per_simd<InT, ZOH, CONV>());
+  const ProgressPriority prio(nchunks, a.nblocks <= 256 * n16_waves_per_simd<InT, ZOH, CONV, FIVE>());
   // One barrier per chunk. The (B, C) ring is the only LDS data shared across
   // waves; the barrier after store_chunk(J) makes part J mod 3 visible, and a
   // wave past it knows that every wave has finished compute(J - 1), whose
@@ -423,22 +446,26 @@ __global__ __launch_bounds__(256, (n16_waves_per_simd<InT, ZOH, CONV>())) void s
   // channel are written and read only by the wave that owns the channel
   // (channel = tid / 16 in staging, compute and finalize alike), in program
   // order.
-  int bpart = 0;  // J mod 3
+  // The compact layout's second barrier: before store_chunk(J + 1) every wave
+  // has finished compute(J), whose part the staging's spill-over reaches.
+  int bpart = 0;  // J mod BC_PARTS
   for (int J = 0; J < nchunks; J += 2) {
     prio.update(J);
-    const int bpart1 = bpart == 2 ? 0 : bpart + 1;
+    const int bpart1 = bpart == BC_PARTS - 1 ? 0 : bpart + 1;
+    if (FIVE && J > 0) __syncthreads();
     store_chunk(J, 0, bpart, r0, o0);
     if (J + 2 < nchunks) load_chunk(J + 2, r0);
     __syncthreads();
     compute(0, bpart);
     if (J >= 1) finalize(J - 1, 1, o1);
     if (J + 1 >= nchunks) break;
+    if (FIVE) __syncthreads();
     store_chunk(J + 1, 1, bpart1, r1, o1);
     if (J + 3 < nchunks) load_chunk(J + 3, r1);
     __syncthreads();
     compute(1, bpart1);
     finalize(J, 0, o0);
-    bpart = bpart1 == 2 ? 0 : bpart1 + 1;
+    bpart = bpart1 == BC_PARTS - 1 ? 0 : bpart1 + 1;
   }
   if ((nchunks - 1) * T < Lseg) {
     if ((nchunks - 1) & 1)
@@ -473,14 +500,26 @@ hipError_t launch_n16(const ScanArgs& args, int nblocks_full, int nblocks_agg, h
   }
   ScanArgs full = args;
   full.nblocks = nblocks_full;
+  // The compact-LDS layout (bf16 inputs without resets, conv stage or
+  // zero-order hold: the others would spill at five waves per SIMD) where five
+  // workgroups per CU need fewer rounds of the grid than four.
+  const int64_t per4 = 256 * 4, per5 = 256 * 5;
+  const bool five = args.in_bf16 && !reset && !args.zoh && !args.conv_w &&
+                    (nblocks_full + per5 - 1) / per5 < (nblocks_full + per4 - 1) / per4;
   SSM_LOG("launch scan16_kernel full: %s in, reset %d, zoh %d, conv %d; grid %d x 256 threads (16 channels x 16 "
-          "states per workgroup, 32-step chunks), %d pieces of %lld steps",
+          "states per workgroup, 32-step chunks), %d pieces of %lld steps, %s LDS layout",
           args.in_bf16 ? "bf16" : "f32", reset, args.zoh, args.conv_w != nullptr, nblocks_full, args.nseg,
-          static_cast<long long>(args.seg_len));
+          static_cast<long long>(args.seg_len), five ? "compact (five workgroups per CU)" : "standard");
   auto go = [&](auto in_t, auto has_reset, auto zoh, auto conv) {
     using InT = decltype(in_t);
     constexpr bool R = decltype(has_reset)::value, Z = decltype(zoh)::value, C = decltype(conv)::value;
-    hipLaunchKernelGGL((scan16_kernel<InT, R, Z, C>), dim3(nblocks_full), dim3(256), 0, stream, full);
+    if constexpr (sizeof(InT) == 2 && !R && !Z && !C) {
+      if (five) {
+        hipLaunchKernelGGL((scan16_kernel<InT, R, Z, C, true>), dim3(nblocks_full), dim3(256), 0, stream, full);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((scan16_kernel<InT, R, Z, C, false>), dim3(nblocks_full), dim3(256), 0, stream, full);
   };
   auto with_conv = [&](auto in_t, auto has_reset, auto zoh) {
     if (args.conv_w)

@@ -300,6 +300,23 @@ def test_workload_full_size_every_row(name):
     log("%s: max err/bound %.3g" % (name, margin))
 
 
+@pytest.mark.parametrize("L,nseg", [(301, 0), (1000, 2)])
+def test_compact_lds_layout_every_element(L, nseg):
+    """Grids that need more than four and at most five 16-state workgroups per
+    CU (1100 channel groups, or 2200 in two pieces) run the compact-LDS layout
+    (two-part (B, C) ring, read-out sums in the (delta, delta*u) slots): a
+    partial last channel group, a ragged last chunk, h0 and h_last, and with
+    two pieces the aggregate fold, every element against the oracle."""
+    D = 16 * 1100 - 5
+    x = wl.make_scan_inputs(1, D, L, 16, dtype=wl.BF16, seed=L + nseg)
+    h0 = np.random.default_rng(L).standard_normal((1, D, 16)).astype(np.float32)
+    log("compact layout: D %d L %d pieces %d" % (D, L, nseg))
+    out, hl = gpu_scan(x, h0=h0, want_h_last=True, num_segments=nseg)
+    ref, hl_ref = oracle_full(x, h0=h0, want_h_last=True)
+    assert_close(out, ref, wl.BF16)
+    assert_close(hl, hl_ref, wl.BF16, what="h_last")
+
+
 @pytest.mark.parametrize("dt", [(1e-3, 1e-1), (1e-3, 1e-2)])
 def test_long_float32_planner_split_every_element(dt):
     """A float32 sequence the library splits itself (num_segments = 0): 16
