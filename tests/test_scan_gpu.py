@@ -320,8 +320,8 @@ def test_compact_lds_layout_every_element(L, nseg):
 @pytest.mark.parametrize("dt", [(1e-3, 1e-1), (1e-3, 1e-2)])
 def test_long_float32_planner_split_every_element(dt):
     """A float32 sequence the library splits itself (num_segments = 0): 16
-    channels of 65 536 steps fill one workgroup, so the planner cuts 128
-    pieces of 512 steps joined by their aggregates (the decay product from
+    channels of 65 536 steps fill one workgroup, so the planner cuts 256
+    pieces of 256 steps joined by their aggregates (the decay product from
     the sum of delta over a piece, the end state from zero). Every element is
     held to the float32 bound."""
     x = wl.make_scan_inputs(1, 16, 65536, 16, dtype=wl.F32, seed=41, dt_lo=dt[0], dt_hi=dt[1])
