@@ -518,9 +518,11 @@ hipError_t with_npl(int64_t N, Fn&& fn) {
 // as the scan itself (the rotation dominates both), so it pays only where the
 // channels leave CUs idle or short of the waves that hide latency: aim for
 // about 4 / NPL workgroups per CU (at least one), split only when the
-// channels fill less than half of that, and keep pieces >= 512 steps and a
-// multiple of 16. With several states per lane (N > 32) one workgroup per CU
-// already has the independent work it needs.
+// channels fill less than half of that, and keep pieces >= 128 steps and a
+// multiple of 16 (the rotation makes every step costly enough that a piece's
+// start-up is small against it: with a 512-step floor 1 x 256 x 8192 took
+// 171 us in 16 pieces, 81 us in 64). With several states per lane (N > 32)
+// one workgroup per CU already has the independent work it needs.
 void plan_cplx_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg, int64_t* seg_len) {
   int64_t want;
   if (requested > 0) {
@@ -530,7 +532,7 @@ void plan_cplx_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requeste
     const int64_t blocks = B * ((D + kCPW - 1) / kCPW);
     const int64_t round = 256 * std::max<int64_t>(1, 4 / npl);
     want = 2 * blocks >= round ? 1 : round / blocks;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, L / 512));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, L / 128));
   }
   want = std::max<int64_t>(1, std::min<int64_t>(want, (L + 15) / 16));
   int64_t len = (L + want - 1) / want;
