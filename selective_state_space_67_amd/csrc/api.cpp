@@ -222,7 +222,7 @@ ssm_status plan_aggregate(const ssm_scan_params* p, int* nseg, int64_t* seg_len,
   if (cplx)
     ssm::plan_cplx_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len);
   else
-    ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len, true);
+    ssm::plan_segments(p->batch, p->dim, p->seqlen, p->dstate, p->num_segments, nseg, seg_len, true, 512);
   const int64_t blocks = cplx ? ssm::cplx_scan_grid_blocks(p->batch, p->dim, *nseg)
                               : ssm::scan_grid_blocks(p->batch, p->dim, p->dstate, *nseg);
   if (blocks > std::numeric_limits<int32_t>::max())

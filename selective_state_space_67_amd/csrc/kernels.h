@@ -78,9 +78,10 @@ constexpr int kMaxState = 256;
 // How many pieces the sequence is split into (requested = 0: automatic) and
 // the resulting piece length. `plain`: the pass that follows is the plain
 // full pass (no conv stage, delta B coefficient) or the aggregate pass, which
-// keep more waves resident than the other variants. Pure host arithmetic.
+// keep more waves resident than the other variants. `min_steps`: the shortest
+// automatic piece. Pure host arithmetic.
 void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg,
-                   int64_t* seg_len, bool plain = false);
+                   int64_t* seg_len, bool plain = false, int64_t min_steps = 256);
 
 // Workspace bytes for `nseg` pieces: the affine aggregate (decay product and
 // end state) of every piece but the last, per (b, d, n), in float32.

@@ -8,7 +8,7 @@ using fwd::channels_per_block;
 using fwd::resident_blocks;
 
 void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, int* nseg,
-                   int64_t* seg_len, bool plain) {
+                   int64_t* seg_len, bool plain, int64_t min_steps) {
   int64_t want;
   if (requested > 0) {
     want = requested;
@@ -16,14 +16,16 @@ void plan_segments(int64_t B, int64_t D, int64_t L, int64_t N, int requested, in
     // Split the sequence only when the channels alone fill less than half of
     // one resident round of workgroups (the aggregate pass costs about half a
     // full pass over the data it covers); then aim for exactly one round, with
-    // pieces long enough (>= 256 steps) that per-piece overheads stay small.
-    // (With a 512-step floor, short sequences on few channels stayed below a
-    // round: 1 x 256 x 16384 took 59.8 us in 32 pieces, 51.3 us in 64.)
+    // pieces long enough (>= min_steps) that per-piece overheads stay small:
+    // 256 steps for a scan (with 512, short sequences on few channels stayed
+    // below a round: 1 x 256 x 16384 took 59.8 us in 32 pieces, 51.3 us in
+    // 64), 512 for the aggregate entry point, whose passes do less work per
+    // step (the same shape: 32 us in 32 pieces, 37 us in 64).
     const int cpw = channels_per_block(N);
     const int64_t blocks = B * ((D + cpw - 1) / cpw);
     const int64_t round = resident_blocks(N, plain);
     want = 2 * blocks >= round ? 1 : round / blocks;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, L / 256));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, L / min_steps));
   }
   want = std::max<int64_t>(1, std::min<int64_t>(want, (L + 15) / 16));
   int64_t len = (L + want - 1) / want;
