@@ -265,6 +265,34 @@ def test_automatic_split_only_for_long_sequences_with_few_channels(lib):
     assert n.value == 0
 
 
+def test_automatic_piece_counts(lib):
+    """The planner's piece floors, read back through the workspace sizes (each
+    piece but the last keeps a (P, H) pair per (b, d, n); the aggregate entry
+    point keeps every piece's): a scan aims for one round of 1024 16-state
+    workgroups with pieces of at least 256 steps, the aggregate entry point
+    with pieces of at least 512, the complex scan with pieces of at least 128."""
+    n = ctypes.c_size_t(0)
+    # 1 x 256 x 16384, N = 16: 16 workgroups -> 64 pieces of 256 steps
+    p = scan_params(batch=1, dim=256, seqlen=16384)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 63 * 256 * 16 * 4
+    # the same for the aggregate entry point: 32 pieces of 512 steps
+    assert lib.ssm_scan_aggregate_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 32 * 256 * 16 * 4
+    # 2 x 2048 x 1024: 256 workgroups -> 4 pieces of 256 steps
+    p = scan_params(batch=2, dim=2048, seqlen=1024)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * 2 * 2048 * 16 * 4
+    # complex state, 1 x 256 x 8192: 64 pieces of 128 steps, (re, im) aggregates
+    p = scan_params(batch=1, dim=256, seqlen=8192, state_kind=bd.SSM_STATE_COMPLEX)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 2 * 63 * 256 * 16 * 2 * 4
+    # long enough channels: one round already, no split
+    p = scan_params(batch=4, dim=5120, seqlen=2048)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setenv("SSM_SCAN_LIBRARY", str(tmp_path / "missing.so"))
     monkeypatch.setattr(bd, "_lib", None)
