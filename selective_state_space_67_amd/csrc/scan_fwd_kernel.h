@@ -174,11 +174,13 @@ constexpr int kernel_waves_per_simd() {
 // staging item keeps one fixed 32-bit byte offset for the whole kernel. (With
 // plain pointers the compiler strength-reduces every item's address into its
 // own 64-bit pointer, advanced by a 64-bit vector add per chunk.) The range is
-// the bytes from the base to the end of the tensor, capped at 2^31 - 1; every
-// item a chunk loads lies inside it.
+// the bytes from the base to the end of the tensor, clamped to [0, 2^31 - 1]
+// (0 for the trailing chunks the full pass runs past a piece, whose items are
+// all masked off); every item a chunk loads lies inside it.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                           static_cast<int>(min(bytes, int64_t{0x7FFFFFFF})), 0x00020000);
+                                           static_cast<int>(max(int64_t{0}, min(bytes, int64_t{0x7FFFFFFF}))),
+                                           0x00020000);
 }
 __device__ __forceinline__ bf16_t buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t item, bf16_t) {
   return bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, item * 2u, 0, 0)};
