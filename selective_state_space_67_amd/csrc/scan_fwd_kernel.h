@@ -611,8 +611,10 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
   // ---- one step of the checkpoint sweep ----
   // h as in the scan; segP = product of a_t since the segment start (0 after a
   // reset, where a_t counts as 0); segG += segP dy C, the segment's adjoint
-  // from a zero start, accumulated in forward order.
-  auto step_ck = [&](float dl, const float dv, const float dy, const float (&Bv)[NPL],
+  // from a zero start, accumulated in forward order. `seg` (a std::bool_constant)
+  // false leaves out (segP, segG): the first backward segment's are never read,
+  // since the reverse sweep folds only the segments after its own.
+  auto step_ck = [&](auto seg, float dl, const float dv, const float dy, const float (&Bv)[NPL],
                      const float (&Cv)[NPL]) {
     bool rs = false;
     if (HAS_RESET) {
@@ -631,9 +633,13 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
         h[j] = __builtin_fmaf(abar, h[j], (Bv[j] * dv) * zoh_coef(dl, dl * Aj[j], abar, invA[j]));
       else
         h[j] = __builtin_fmaf(abar, h[j], Bv[j] * dv);
-      segP[j] = rs ? 0.0f : segP[j] * abar;
-      segG[j] = __builtin_fmaf(segP[j] * dy, Cv[j], segG[j]);
+      if constexpr (decltype(seg)::value) {
+        segP[j] = rs ? 0.0f : segP[j] * abar;
+        segG[j] = __builtin_fmaf(segP[j] * dy, Cv[j], segG[j]);
+      }
     }
+    (void)rs;
+    (void)dy;
   };
 
   // ---- the recurrence over chunk J (ring half `par`) ----
@@ -652,6 +658,7 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
       const float* dy_row = s_dy + c * DY_STRIDE;
       const int64_t tchunk = t_seg + static_cast<int64_t>(J) * T;  // step held in slot par * T
       const int64_t pend = t_seg + Lseg;
+      auto sweep = [&](auto seg) {
 #pragma unroll
       for (int i = 0; i < T; i += 4) {
         const int m = par * T + i;
@@ -679,10 +686,10 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
             C2[j] = vc.z;
             C3[j] = vc.w;
           }
-          step_ck(d01.x, d01.y, dy4.x, B0, C0);
-          step_ck(d01.z, d01.w, dy4.y, B1, C1);
-          step_ck(d23.x, d23.y, dy4.z, B2, C2);
-          step_ck(d23.z, d23.w, dy4.w, B3, C3);
+          step_ck(seg, d01.x, d01.y, dy4.x, B0, C0);
+          step_ck(seg, d01.z, d01.w, dy4.y, B1, C1);
+          step_ck(seg, d23.x, d23.y, dy4.z, B2, C2);
+          step_ck(seg, d23.z, d23.w, dy4.w, B3, C3);
         } else {
           // Several states per lane: two steps per group of reads, so that
           // fewer B and C values are live at once (no spills at the register
@@ -715,8 +722,8 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
               C0[j] = ct[j];
               C1[j] = ct[NPL + j];
             }
-            step_ck(d01.x, d01.y, dy2.x, B0, C0);
-            step_ck(d01.z, d01.w, dy2.y, B1, C1);
+            step_ck(seg, d01.x, d01.y, dy2.x, B0, C0);
+            step_ck(seg, d01.z, d01.w, dy2.y, B1, C1);
             // keep the next group's reads from being hoisted above this one
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -738,6 +745,22 @@ __global__ __launch_bounds__(TL::THREADS, (kernel_waves_per_simd<TL, MODE, CONV,
             }
           }
         }
+      }
+      };
+      // Chunks that end within the first backward segment skip (segP, segG):
+      // what the sweep writes for that segment (P = 1, G = 0) is never read.
+      // Only with two states per lane and no conv stage or zero-order hold:
+      // with four states, the conv stage or the zero-order hold the second copy
+      // of the loop spills, and with one state per lane the sweep gained nothing
+      // (its step is not held by VALU issue there; 1-2% slower from the extra
+      // registers), while packed N = 128 documents went from 4.56 to 4.38 ms.
+      if constexpr (NPL == 2 && !CONV && !ZOH) {
+        if (tchunk + T > a.seg_steps)
+          sweep(std::true_type{});
+        else
+          sweep(std::false_type{});
+      } else {
+        sweep(std::true_type{});
       }
     } else if constexpr (!FULL) {
       // Lockstep: every lane is at step m. Per four steps a lane reads two
