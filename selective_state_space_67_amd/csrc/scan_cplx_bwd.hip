@@ -225,6 +225,10 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
     s_st[c * kT + k] = in.staged();
     __syncthreads();
 
+    // Chunks that end inside the first reverse segment leave out (q, s): the
+    // reverse sweep folds only the segments after its own, so that segment's
+    // aggregates (written as P = 1, G = 0) are never read.
+    auto sweep = [&](auto seg) {
     // (one step at a time for 16 states per lane: their registers leave no room to unroll)
 #pragma unroll (NPL >= 16 ? 1 : 4)
     for (int tl = 0; tl < kT; ++tl) {
@@ -267,15 +271,22 @@ __global__ __launch_bounds__(kThreads) void cplx_ckpt_kernel(const CplxBwdArgs a
         const float ni = __builtin_fmaf(ar, hi[j], __builtin_fmaf(ai, hr[j], bi));
         hr[j] = nr;
         hi[j] = ni;
-        const float pr = __builtin_fmaf(ar, qr[j], -ai * qi[j]);
-        const float pi = __builtin_fmaf(ar, qi[j], ai * qr[j]);
-        qr[j] = pr;
-        qi[j] = pi;
-        const float cr = st.z * bc.z, ci = st.z * bc.w;  // dy C
-        sr[j] = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, sr[j]));
-        si[j] = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, si[j]));
+        if constexpr (decltype(seg)::value) {
+          const float pr = __builtin_fmaf(ar, qr[j], -ai * qi[j]);
+          const float pi = __builtin_fmaf(ar, qi[j], ai * qr[j]);
+          qr[j] = pr;
+          qi[j] = pi;
+          const float cr = st.z * bc.z, ci = st.z * bc.w;  // dy C
+          sr[j] = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, sr[j]));
+          si[j] = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, si[j]));
+        }
       }
     }
+    };
+    if (t_seg + t0 + kT > a.seg_steps)
+      sweep(std::true_type{});
+    else
+      sweep(std::false_type{});
     const int64_t tend = t_seg + t0 + kT;
     if (tend == seg_end || tend >= a.L) {  // end of a reverse segment
       const int64_t sg = seg_idx++;
