@@ -135,6 +135,14 @@ def test_long_sequence_many_segments():
     assert_grads(gpu_bwd(x), oracle_bwd(x), what="long")
 
 
+def test_long_sequence_many_segments_two_states_per_lane():
+    # N = 128 with few channels: the checkpoint sweep is split into pieces, and
+    # its chunks inside the first backward segment leave out that segment's
+    # (unread) aggregates while the later segments' are folded by the reverse sweep
+    x = make_case(1, 8, 12000, 128, wl.BF16, 29, dt_lo=1e-3, dt_hi=1e-2, h0=True, dh_last=True)
+    assert_grads(gpu_bwd(x), oracle_bwd(x), what="long N128")
+
+
 def test_deterministic():
     x = make_case(2, 100, 300, 16, wl.BF16, 17)
     a, b = gpu_bwd(x), gpu_bwd(x)
